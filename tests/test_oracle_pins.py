@@ -1,0 +1,561 @@
+"""Pins of the float64 oracle against what the pages and the mathematics fix.
+
+Nothing here compares the oracle with itself: every expected value is a closed
+form, a hand-worked fixture under tests/golden/, a brute-force search, a
+library routine solving the same problem another way, or an invariant.
+CPU only.
+"""
+import itertools
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import prism_oracle as orc
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _read_rows(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                rows.append(line)
+    return rows
+
+
+# ---------------------------------------------------------------- candidates
+
+def test_candidate_set_matches_hand_typed_table():
+    rows = [list(map(int, r.split())) for r in _read_rows("candidate_shapes.txt")]
+    want = [tuple(r[2:]) for r in rows]
+    got = orc.candidate_shapes()
+    assert len(got) == 16                                     # the pages' count
+    assert got == want
+    for (idx, B, bt, bh, bw), s in zip(rows, got):
+        assert bt * bh * bw == B and 8 % bt == 0 and 8 % bh == 0 and 8 % bw == 0
+
+
+def test_candidate_set_is_every_power_of_two_box_without_unit_edges():
+    boxes = {(2 ** a, 2 ** b, 2 ** c) for a, b, c in itertools.product(range(4), repeat=3)
+             if 2 ** (a + b + c) in (64, 128, 256)}
+    with_unit = {s for s in boxes if 1 in s}
+    assert len(boxes) == 19 and len(with_unit) == 3
+    assert set(orc.candidate_shapes()) == boxes - with_unit
+
+
+# ---------------------------------------------------------------- E3 optimum
+
+@pytest.mark.parametrize("seed", range(6))
+def test_optimum_solves_the_constrained_minimisation(seed):
+    """E3 is the minimiser of sum_d g_d (b_d^2 - 1) subject to prod_d b_d = B.
+    Solve that problem numerically (SLSQP) and compare."""
+    from scipy.optimize import minimize
+    rng = np.random.default_rng(seed)
+    g = np.exp(rng.uniform(-6, 3, size=3))
+    for B in (64, 128, 256):
+        S = math.log2(B)
+        obj = lambda x: float(np.sum(g * (np.exp2(2 * np.clip(x, -60, 60)) - 1)))
+        con = {"type": "eq", "fun": lambda x: float(np.sum(x) - S)}
+        res = minimize(obj, x0=np.full(3, S / 3), constraints=[con], method="SLSQP",
+                       options={"ftol": 1e-14, "maxiter": 500})
+        assert res.success
+        ls = orc.optimum_log2(g[None, :], np.array([B]))[0]
+        np.testing.assert_allclose(ls, res.x, atol=2e-5)
+        assert abs(ls.sum() - S) < 1e-12                      # the product constraint
+        # b*_d proportional to g_d^(-1/2)
+        ratio = np.exp2(ls) * np.sqrt(g)
+        np.testing.assert_allclose(ratio, ratio[0], rtol=1e-12)
+
+
+def test_optimum_is_scale_invariant():
+    rng = np.random.default_rng(7)
+    g = np.exp(rng.uniform(-5, 2, size=(50, 3)))
+    B = rng.choice([64, 128, 256], size=50)
+    a = orc.optimum_log2(g, B)
+    b = orc.optimum_log2(g * 37.5, B)
+    np.testing.assert_allclose(a, b, atol=1e-12)
+
+
+# ---------------------------------------------------------------- shape choice
+
+def _frac(s):
+    return Fraction(s)
+
+
+def test_hand_worked_shapes():
+    for row in _read_rows("hand_worked_shapes.txt"):
+        gpart, lpart, spart, dpart = [p.split() for p in row.split("|")]
+        g = np.array([float(x) for x in gpart[:3]])
+        B = int(gpart[3])
+        lstar_hand = [float(_frac(x)) for x in lpart]
+        shape_hand = tuple(int(x) for x in spart)
+        ls = orc.optimum_log2(g[None, :], np.array([B]))[0]
+        np.testing.assert_allclose(ls, lstar_hand, atol=1e-12)
+        idx, _ = orc.nearest_shape(ls, B)
+        assert orc.candidate_shapes()[idx] == shape_hand, row
+        D = sum((math.log2(shape_hand[d]) - lstar_hand[d]) ** 2 for d in range(3))
+        assert abs(D - float(_frac(dpart[0]))) < 1e-12
+
+
+def test_rounding_ties_fall_in_the_window():
+    """g = (1+1e-6, 1e-6, 1e-6), B = 64: (2,4,8) and (2,8,4) are equidistant in exact
+    arithmetic (l*_H = l*_W) but their float64 distances differ in the last bits;
+    the tie window must still pick the lower index."""
+    ls = orc.optimum_log2(np.array([[1 + 1e-6, 1e-6, 1e-6]]), np.array([64]))[0]
+    assert ls[1] == ls[2]
+    idx, _ = orc.nearest_shape(ls, 64)
+    assert orc.candidate_shapes()[idx] == (2, 4, 8)
+    ls = orc.optimum_log2(np.array([[1e-6, 1e-6, 1 + 1e-6]]), np.array([128]))[0]
+    idx, _ = orc.nearest_shape(ls, 128)
+    assert orc.candidate_shapes()[idx] == (8, 8, 2)
+
+
+def test_nearest_shape_brute_force():
+    """Over random optima: the pick is at the minimum distance over every box of
+    the volume (enumerated here as exponent triples), and no lower-index
+    candidate lies within the window."""
+    rng = np.random.default_rng(3)
+    cands = orc.candidate_shapes()
+    for _ in range(400):
+        B = int(rng.choice([64, 128, 256]))
+        S = int(math.log2(B))
+        ls = rng.normal(S / 3, 1.5, size=3)
+        trip = [(a, b, c) for a in (1, 2, 3) for b in (1, 2, 3) for c in (1, 2, 3) if a + b + c == S]
+        dist = {t: sum((t[d] - ls[d]) ** 2 for d in range(3)) for t in trip}
+        Dmin = min(dist.values())
+        idx, _ = orc.nearest_shape(ls, B)
+        pick = tuple(int(math.log2(x)) for x in cands[idx])
+        assert abs(dist[pick] - Dmin) <= 1e-9
+        for j in range(idx):
+            s = cands[j]
+            if s[0] * s[1] * s[2] == B:
+                t = tuple(int(math.log2(x)) for x in s)
+                assert dist[t] > Dmin + 1e-9
+
+
+@pytest.mark.parametrize("axis", [0, 1, 2])
+def test_fast_axis_gets_the_finest_edge(axis):
+    """A zone that varies only along one axis, with no audio coupling, gets the
+    smallest edge that its volume offers on that axis: 2 at volumes 64 and 128,
+    4 at 256 ([P3] core ideas: finer partition along fast-changing axes)."""
+    r = np.zeros((1, 3))
+    r[0, axis] = 1.0
+    g = orc.indicator(r, np.zeros(1), np.full((1, 3), 1 / 3))
+    for B, edge in ((64, 2), (128, 2), (256, 4)):
+        idx, _ = orc.nearest_shape(orc.optimum_log2(g, np.array([B]))[0], B)
+        assert orc.candidate_shapes()[idx][axis] == edge
+
+
+# ---------------------------------------------------------------- statistics (E1)
+
+def _grid_values(T, H, W, C, fn):
+    t, h, w = np.meshgrid(np.arange(T), np.arange(H), np.arange(W), indexing="ij")
+    vals = fn(t.reshape(-1), h.reshape(-1), w.reshape(-1))
+    return np.repeat(vals[:, None], C, axis=1) if vals.ndim == 1 else vals
+
+
+def test_variance_of_a_field_varying_only_along_T():
+    T, H, W, C = 16, 8, 16, 5
+    rng = np.random.default_rng(0)
+    f = rng.normal(size=T)
+    u = rng.normal(size=C)
+    t, h, w = np.meshgrid(np.arange(T), np.arange(H), np.arange(W), indexing="ij")
+    V = f[t.reshape(-1)][:, None] * u[None, :]
+    s2, r = orc.video_variance(orc.axis_profiles(V, T, H, W))
+    # the H and W slices hold identical values: only rounding of their mean remains
+    assert np.all(s2[:, 1] < 1e-28) and np.all(s2[:, 2] < 1e-28)
+    np.testing.assert_allclose(r, np.tile([1.0, 0.0, 0.0], (len(r), 1)), atol=1e-25)
+    # closed form of sigma2_T per zone: mean_c u_c^2 * population variance of f over the zone's 8 slices
+    for zt in range(T // 8):
+        fz = f[8 * zt:8 * zt + 8]
+        want = np.mean(u ** 2) * np.mean((fz - fz.mean()) ** 2)
+        for m in range(len(r)):
+            if m // ((H // 8) * (W // 8)) == zt:
+                assert abs(s2[m, 0] - want) < 1e-12 * max(1.0, want)
+
+
+def test_alternating_slices_have_unit_variance():
+    V = _grid_values(8, 8, 8, 3, lambda t, h, w: np.where(t % 2 == 0, 1.0, -1.0))
+    s2, r = orc.video_variance(orc.axis_profiles(V, 8, 8, 8))
+    assert s2[0, 0] == 1.0 and s2[0, 1] == 0.0 and s2[0, 2] == 0.0
+    assert tuple(r[0]) == (1.0, 0.0, 0.0)
+
+
+def test_ramp_along_H_has_the_variance_of_0_to_7():
+    V = _grid_values(8, 16, 8, 4, lambda t, h, w: (h % 8).astype(float))
+    s2, _ = orc.video_variance(orc.axis_profiles(V, 8, 16, 8))
+    np.testing.assert_allclose(s2[:, 1], 5.25, atol=1e-12)       # (8^2 - 1) / 12
+    assert np.all(s2[:, 0] < 1e-28) and np.all(s2[:, 2] < 1e-28)
+
+
+def test_variance_averages_over_channels():
+    """Half the channels alternate along T, half along W: each axis carries the
+    channel-average, 1/2 (the 1/D factor of E1)."""
+    t, h, w = np.meshgrid(np.arange(8), np.arange(8), np.arange(8), indexing="ij")
+    a = np.where(t.reshape(-1) % 2 == 0, 1.0, -1.0)
+    b = np.where(w.reshape(-1) % 2 == 0, 1.0, -1.0)
+    V = np.stack([a, a, b, b], axis=1)
+    s2, r = orc.video_variance(orc.axis_profiles(V, 8, 8, 8))
+    assert tuple(s2[0]) == (0.5, 0.0, 0.5)
+    assert tuple(r[0]) == (0.5, 0.0, 0.5)
+
+
+def test_constant_zone_falls_back_to_thirds():
+    V = np.full((512, 3), 2.5)
+    s2, r = orc.video_variance(orc.axis_profiles(V, 8, 8, 8))
+    assert np.all(s2 == 0) and np.all(r == 1.0 / 3.0)
+
+
+def test_iid_noise_is_isotropic():
+    rng = np.random.default_rng(5)
+    V = rng.normal(size=(8 * 8 * 8, 4096))
+    s2, r = orc.video_variance(orc.axis_profiles(V, 8, 8, 8))
+    np.testing.assert_allclose(r[0], 1 / 3, atol=0.02)
+    np.testing.assert_allclose(s2[0], 7 / 8 / 64, rtol=0.05)     # E[(1/8)sum(mean64 - mean)^2] = (7/8)/64
+
+
+def test_zone_mean_is_the_same_along_every_axis():
+    rng = np.random.default_rng(9)
+    V = rng.normal(size=(16 * 8 * 8, 7))
+    P = orc.axis_profiles(V, 16, 8, 8)
+    mu = P.mean(axis=2)                                           # [nZ, 3, C]
+    np.testing.assert_allclose(mu[:, 0], mu[:, 1], atol=1e-14)
+    np.testing.assert_allclose(mu[:, 0], mu[:, 2], atol=1e-14)
+    np.testing.assert_allclose(mu[0, 0], V[orc.permutation(16, 8, 8, [3, 3])[:512]].mean(axis=0), atol=1e-14)
+
+
+def test_zone_order_is_raster():
+    """Zone m = (zt*nH + zh)*nW + zw: mark each zone by a constant value."""
+    T, H, W = 16, 24, 8
+    t, h, w = np.meshgrid(np.arange(T), np.arange(H), np.arange(W), indexing="ij")
+    mark = ((t // 8) * 3 + (h // 8)) * 1 + (w // 8)
+    V = mark.reshape(-1, 1).astype(float)
+    P = orc.axis_profiles(V, T, H, W)
+    np.testing.assert_array_equal(P[:, 0, 0, 0], np.arange(6))
+
+
+# ---------------------------------------------------------------- audio terms (readings)
+
+def test_audio_constant_map():
+    a = np.full(512, 0.3)
+    abar, s2, vhat = orc.audio_terms(a, 8, 8, 8)
+    assert abs(abar[0] - 0.3) < 1e-15 and np.all(s2 == 0) and np.all(vhat == 1 / 3)
+
+
+def test_audio_ramp_along_W():
+    t, h, w = np.meshgrid(np.arange(8), np.arange(8), np.arange(8), indexing="ij")
+    a = (w.reshape(-1) / 7.0)
+    abar, s2, vhat = orc.audio_terms(a, 8, 8, 8)
+    assert abs(abar[0] - 0.5) < 1e-15
+    assert tuple(vhat[0]) == (0.0, 0.0, 1.0)
+    assert abs(s2[0, 2] - 5.25 / 49) < 1e-15
+
+
+def test_indicator_is_E2():
+    r = np.array([[0.2, 0.3, 0.5]])
+    vhat = np.array([[0.1, 0.6, 0.3]])
+    g = orc.indicator(r, np.array([0.5]), vhat, eps=1e-6)
+    np.testing.assert_allclose(g[0], [0.2 + 0.05 + 1e-6, 0.3 + 0.3 + 1e-6, 0.5 + 0.15 + 1e-6], atol=1e-15)
+
+
+# ---------------------------------------------------------------- volume and density
+
+def test_volume_thresholds():
+    rho = np.array([0.0, 0.2499999, 0.25, 0.3, 0.4999999, 0.5, 0.9, 1.0])
+    np.testing.assert_array_equal(orc.volume(rho), [256, 256, 128, 128, 128, 64, 64, 64])
+
+
+def test_density_properties():
+    """Static zone with weak coupling -> 256; strong coupling -> 64; the most
+    varying zone -> 64 ([P2] step 2, [P3] §2)."""
+    s2 = np.array([[1e-6, 1e-6, 1e-6], [1.0, 2.0, 0.5], [1e-6, 0.0, 0.0], [0.1, 0.1, 0.1]])
+    abar = np.array([0.1, 0.0, 0.7, 0.3])
+    rho, S = orc.density(s2, abar)
+    np.testing.assert_array_equal(orc.volume(rho), [256, 64, 64, 128])
+    assert rho[1] == 1.0
+
+
+# ---------------------------------------------------------------- layout and permutation
+
+def test_block_layout_counts():
+    offs, NB = orc.block_layout([3, 7, 13])          # volumes 64, 128, 256
+    assert NB == 8 + 4 + 2
+    np.testing.assert_array_equal(np.diff(offs), [64] * 8 + [128] * 4 + [256] * 2)
+    assert offs[8] == 512 and offs[12] == 1024 and offs[-1] == 1536
+
+
+def test_permutation_hand_worked_first_block():
+    """Zone 0 of an 8x8x8 grid with shape (2,4,8): the first block holds
+    t in {0,1}, h in 0..3, w in 0..7 in raster order; the second block starts at
+    h = 4."""
+    pi = orc.permutation(8, 8, 8, [0])
+    want = [(t * 8 + h) * 8 + w for t in range(2) for h in range(4) for w in range(8)]
+    np.testing.assert_array_equal(pi[:64], want)
+    np.testing.assert_array_equal(pi[64:72], [(0 * 8 + 4) * 8 + w for w in range(8)])
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_permutation_properties(seed):
+    rng = np.random.default_rng(seed)
+    T, H, W = 16, 24, 16
+    nZ = (T // 8) * (H // 8) * (W // 8)
+    shapes = rng.integers(0, 16, size=nZ)
+    pi = orc.permutation(T, H, W, shapes)
+    N = T * H * W
+    assert np.array_equal(np.sort(pi), np.arange(N))             # bijection
+    X = rng.normal(size=(N, 3))
+    np.testing.assert_array_equal(orc.to_raster(orc.to_block_major(X, pi), pi), X)
+    offs, NB = orc.block_layout(shapes)
+    cands = orc.candidate_shapes()
+    zone_of_block = np.repeat(np.arange(nZ), [512 // np.prod(cands[s]) for s in shapes])
+    for i in range(NB):
+        toks = pi[offs[i]:offs[i + 1]]
+        t, rem = np.divmod(toks, H * W)
+        h, w = np.divmod(rem, W)
+        bt, bh, bw = cands[shapes[zone_of_block[i]]]
+        # contiguous axis-aligned box of the zone's shape, tokens in raster order
+        assert (t.max() - t.min() + 1, h.max() - h.min() + 1, w.max() - w.min() + 1) == (bt, bh, bw)
+        assert t.min() % bt == 0 and h.min() % bh == 0 and w.min() % bw == 0
+        assert np.all(np.diff(toks) > 0)
+        assert offs[i] // 512 == zone_of_block[i]
+
+
+# ---------------------------------------------------------------- pooling and scores
+
+def test_pool_blocks_is_the_block_mean():
+    N, d = 1024, 3
+    offs = np.array([0, 64, 128, 256, 512, 1024])
+    X = np.arange(N * d, dtype=float).reshape(N, 1, d)
+    Pb = orc.pool_blocks(X, offs, 0)
+    for i in range(len(offs) - 1):
+        a, b = offs[i], offs[i + 1]
+        first = (a + b - 1) / 2 * d                               # mean row index * d
+        np.testing.assert_allclose(Pb[i], first + np.arange(d), atol=1e-12)
+
+
+def test_block_logits_round_once_to_float32():
+    Qb = np.array([[1.0, 2.0, 0.0], [0.5, -1.0, 3.0]])
+    Kb = np.array([[2.0, 1.0, 1.0], [0.0, 0.0, 4.0]])
+    s = 0.125
+    L = orc.block_logits(Qb, Kb, s)
+    assert L.dtype == np.float32
+    np.testing.assert_array_equal(L, np.array([[0.5, 0.0], [0.375, 1.5]], dtype=np.float32))
+    # a value that is not a float32: 1/3 must be the nearest float32
+    L = orc.block_logits(np.array([[1.0]]), np.array([[1.0 / 3.0]]), 1.0)
+    assert L[0, 0] == np.float32(1.0 / 3.0)
+
+
+# ---------------------------------------------------------------- selection (E4)
+
+def _brute_select(L, k, p):
+    """E4 by enumeration: Top-k = the k highest-probability blocks (lower index
+    first on ties); Top-p = among the smallest subsets whose probability reaches
+    p, the one of largest mass (lexicographically lowest indices on ties)."""
+    L = np.asarray(L, dtype=np.float64)
+    NB = len(L)
+    P = np.exp(L - L.max())
+    P /= P.sum()
+    rank = sorted(range(NB), key=lambda j: (-L[j], j))
+    topk = set(rank[:min(k, NB)])
+    topp = None
+    for n in range(1, NB + 1):
+        best = None
+        for sub in itertools.combinations(range(NB), n):
+            m = sum(P[j] for j in sub)
+            if m >= p - 1e-12:
+                key = (-m, sorted(rank.index(j) for j in sub))
+                if best is None or key < best[0]:
+                    best = (key, set(sub))
+        if best is not None:
+            topp = best[1]
+            break
+    if topp is None:
+        topp = set(range(NB))
+    return sorted(topk | topp)
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_selection_brute_force(seed):
+    rng = np.random.default_rng(seed)
+    NB = int(rng.integers(1, 10))
+    L = rng.normal(scale=rng.choice([0.1, 1.0, 3.0]), size=NB).astype(np.float32)
+    if seed % 5 == 0 and NB > 2:
+        L[1] = L[0]                                           # an exact tie
+    k = int(rng.integers(0, NB + 2))
+    p = float(rng.choice([0.0, 0.3, 0.5, 0.9, 0.95, 1.0]))
+    sel, flag = orc.select_row(L, k, p)
+    if flag and p < 1.0:
+        pytest.skip("row lies on a decision boundary")
+    assert list(sel) == _brute_select(L, k, p)
+
+
+def test_selection_invariants():
+    rng = np.random.default_rng(11)
+    for _ in range(200):
+        NB = int(rng.integers(1, 300))
+        L = rng.normal(scale=2.0, size=NB).astype(np.float32)
+        k = int(rng.integers(0, 20))
+        p = float(rng.uniform(0, 1))
+        sel, flag = orc.select_row(L, k, p)
+        P = np.exp(L.astype(float) - L.max())
+        P /= P.sum()
+        assert len(sel) >= min(k, NB)
+        assert P[sel].sum() >= p - 1e-12
+        if len(sel) > max(k, 1):
+            rank = sorted(sel, key=lambda j: (-L[j], j))
+            assert P[rank[:-1]].sum() < p + 1e-12
+        others = np.setdiff1d(np.arange(NB), sel)
+        if others.size:
+            assert L[sel].min() >= L[others].max()
+
+
+def test_selection_closed_forms():
+    L = np.zeros(16, dtype=np.float32)                         # uniform scores
+    sel, _ = orc.select_row(L, 0, 0.9)
+    np.testing.assert_array_equal(sel, np.arange(15))          # ceil(0.9 * 16) = 15, lowest indices
+    sel, _ = orc.select_row(L, 3, 0.0)
+    np.testing.assert_array_equal(sel, [0, 1, 2])
+    L = np.array([0.0, 5.0, 1.0, 5.0], dtype=np.float32)
+    sel, _ = orc.select_row(L, 0, 0.0)
+    np.testing.assert_array_equal(sel, [1])                    # argmax, lower index on the tie
+    sel, _ = orc.select_row(L, 10, 0.5)
+    np.testing.assert_array_equal(sel, [0, 1, 2, 3])           # k >= NB selects all
+
+
+# ---------------------------------------------------------------- attention
+
+def _tiny_case(seed=0, T=8, H=16, W=16, d=16, k=3, p=0.8):
+    rng = np.random.default_rng(seed)
+    N = T * H * W
+    nZ = (T // 8) * (H // 8) * (W // 8)
+    shapes = rng.integers(0, 16, size=nZ)
+    pi = orc.permutation(T, H, W, shapes)
+    offs, NB = orc.block_layout(shapes)
+    Q, K, V, dO = (rng.normal(size=(N, 1, d)) for _ in range(4))
+    Qp, Kp, Vp, dOp = (orc.to_block_major(X, pi) for X in (Q, K, V, dO))
+    sc = 1.0 / math.sqrt(d)
+    Lg = orc.block_logits(orc.pool_blocks(Qp, offs, 0), orc.pool_blocks(Kp, offs, 0), sc)
+    co, ci, _ = orc.select(Lg, k, p)
+    return dict(Q=Q, K=K, V=V, dO=dO, Qp=Qp, Kp=Kp, Vp=Vp, dOp=dOp, pi=pi, offs=offs,
+                NB=NB, co=co, ci=ci, scale=sc, N=N, d=d)
+
+
+def _mask(c):
+    """Dense boolean token mask in raster order from the block CSR."""
+    N, offs, pi = c["N"], c["offs"], c["pi"]
+    Mp = np.zeros((N, N), dtype=bool)
+    for i in range(c["NB"]):
+        for j in c["ci"][c["co"][i]:c["co"][i + 1]]:
+            Mp[offs[i]:offs[i + 1], offs[j]:offs[j + 1]] = True
+    M = np.zeros_like(Mp)
+    M[np.ix_(pi, pi)] = Mp
+    return M
+
+
+def test_forward_with_everything_selected_is_dense_sdpa():
+    c = _tiny_case(k=10 ** 6)
+    assert c["co"][-1] == c["NB"] ** 2
+    out = orc.attention(c["Qp"], c["Kp"], c["Vp"], c["offs"], c["co"], c["ci"], 0, c["scale"])
+    O = orc.to_raster(out["O"], c["pi"])
+    q, k, v = (torch.from_numpy(c[x][:, 0, :]).unsqueeze(0) for x in ("Q", "K", "V"))
+    ref = torch.nn.functional.scaled_dot_product_attention(q, k, v, scale=float(np.float32(c["scale"])))[0]
+    np.testing.assert_allclose(O, ref.numpy(), atol=1e-12)
+    s = float(np.float32(c["scale"])) * (q[0] @ k[0].T)
+    np.testing.assert_allclose(orc.to_raster(out["lse"], c["pi"]), torch.logsumexp(s, 1).numpy(), atol=1e-12)
+
+
+def test_forward_equals_masked_dense_sdpa():
+    c = _tiny_case(seed=1)
+    M = _mask(c)
+    assert 0 < M.mean() < 1
+    out = orc.attention(c["Qp"], c["Kp"], c["Vp"], c["offs"], c["co"], c["ci"], 0, c["scale"])
+    q, k, v = (torch.from_numpy(c[x][:, 0, :]).unsqueeze(0) for x in ("Q", "K", "V"))
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        q, k, v, attn_mask=torch.from_numpy(M).unsqueeze(0), scale=float(np.float32(c["scale"])))[0]
+    np.testing.assert_allclose(orc.to_raster(out["O"], c["pi"]), ref.numpy(), atol=1e-12)
+
+
+def test_backward_equals_autograd_of_masked_dense_attention():
+    c = _tiny_case(seed=2)
+    M = torch.from_numpy(_mask(c))
+    out = orc.attention(c["Qp"], c["Kp"], c["Vp"], c["offs"], c["co"], c["ci"], 0, c["scale"], dOp=c["dOp"])
+    q, k, v = (torch.from_numpy(c[x][:, 0, :]).clone().requires_grad_(True) for x in ("Q", "K", "V"))
+    s = float(np.float32(c["scale"])) * (q @ k.T)
+    s = s.masked_fill(~M, float("-inf"))
+    o = torch.softmax(s, dim=1) @ v
+    o.backward(torch.from_numpy(c["dO"][:, 0, :]))
+    for name, t in (("dQ", q), ("dK", k), ("dV", v)):
+        np.testing.assert_allclose(orc.to_raster(out[name], c["pi"]), t.grad.numpy(), atol=1e-11)
+
+
+def test_backward_by_finite_differences():
+    """Central differences of <O, dO> against the oracle's own forward."""
+    c = _tiny_case(seed=3, d=8)
+    out = orc.attention(c["Qp"], c["Kp"], c["Vp"], c["offs"], c["co"], c["ci"], 0, c["scale"], dOp=c["dOp"])
+
+    def loss(Qp, Kp, Vp):
+        o = orc.attention(Qp, Kp, Vp, c["offs"], c["co"], c["ci"], 0, c["scale"])["O"]
+        return float(np.sum(o * c["dOp"][:, 0, :]))
+
+    rng = np.random.default_rng(0)
+    h = 1e-6
+    for name, grad in (("Qp", "dQ"), ("Kp", "dK"), ("Vp", "dV")):
+        for _ in range(4):
+            r, col = int(rng.integers(0, c["N"])), int(rng.integers(0, c["d"]))
+            args = {x: c[x] for x in ("Qp", "Kp", "Vp")}
+            plus = args[name].copy()
+            plus[r, 0, col] += h
+            minus = args[name].copy()
+            minus[r, 0, col] -= h
+            fd = (loss(**{**args, name: plus}) - loss(**{**args, name: minus})) / (2 * h)
+            assert abs(fd - out[grad][r, col]) < 1e-6 * max(1.0, abs(fd))
+
+
+def test_key_block_grads_and_unselected_keys():
+    c = _tiny_case(seed=4, H=32, W=32, k=1, p=0.05)
+    out = orc.attention(c["Qp"], c["Kp"], c["Vp"], c["offs"], c["co"], c["ci"], 0, c["scale"], dOp=c["dOp"])
+    chosen = set(int(x) for x in c["ci"])
+    offs = c["offs"]
+    for j in range(c["NB"]):
+        dk, dv = orc.key_block_grads(c["Qp"], c["Kp"], c["Vp"], c["dOp"], offs, c["co"], c["ci"], j, 0, c["scale"])
+        np.testing.assert_allclose(dk, out["dK"][offs[j]:offs[j + 1]], atol=1e-12)
+        np.testing.assert_allclose(dv, out["dV"][offs[j]:offs[j + 1]], atol=1e-12)
+        if j not in chosen:
+            assert not np.any(out["dK"][offs[j]:offs[j + 1]]) and not np.any(out["dV"][offs[j]:offs[j + 1]])
+    assert len(chosen) < c["NB"]
+
+
+# ---------------------------------------------------------------- end to end
+
+def test_zone_shapes_on_a_designed_grid():
+    """Four zones built so that the decision is known: zone 0 alternates along W
+    only (finest W edge, full variance -> 64), zone 1 is constant with no audio
+    (-> 256), zone 2 is constant but sits under strong audio coupling (-> 64),
+    zone 3 alternates along T with a quarter of zone 0's variance and weak audio
+    (rho = 0.25 -> 128)."""
+    T, H, W = 8, 16, 16
+    t, h, w = np.meshgrid(np.arange(T), np.arange(H), np.arange(W), indexing="ij")
+    t, h, w = t.reshape(-1), h.reshape(-1), w.reshape(-1)
+    zone = (h // 8) * 2 + (w // 8)
+    V = np.zeros(T * H * W)
+    V[zone == 0] = np.where(w[zone == 0] % 2 == 0, 1.0, -1.0)
+    V[zone == 1] = 0.7
+    V[zone == 2] = -0.2
+    V[zone == 3] = np.where(t[zone == 3] % 2 == 0, 0.5, -0.5)
+    a = np.zeros(T * H * W)
+    a[zone == 2] = 0.8
+    a[zone == 3] = 0.1
+    res = orc.zone_shapes(V[:, None].repeat(2, axis=1), a, T, H, W)
+    np.testing.assert_array_equal(res["B"], [64, 256, 64, 128])
+    np.testing.assert_allclose(res["rho"], [1.0, 0.0, 0.8, 0.25], atol=1e-15)
+    cands = orc.candidate_shapes()
+    assert cands[res["shape"][0]][2] == 2
+    assert cands[res["shape"][3]][0] == 2
+    assert res["NB"] == 8 + 2 + 8 + 4
+    assert res["near_tie"][3]                              # rho sits exactly on tau256
