@@ -1,0 +1,65 @@
+// permute.hip - block-major gather and its inverse scatter.
+//
+// The pages reorganise the token sequence into zone-shaped blocks (news article
+// at ailog.hnlab.kr, "핵심 내용" steps 1-2) and pool and attend whole blocks
+// (Prism reading guide, "Phương pháp" §3); after this permutation every block
+// is one contiguous run of 64, 128 or 256 rows, which is what the selection and
+// attention kernels stream.  The order inside a zone is computed from the
+// zone's shape index in-kernel; no index array is read.
+//
+// One wave moves one token row at a time with 16-byte loads and stores; a
+// workgroup of 4 waves walks a contiguous range of block-major positions, so
+// the block-major side is written (gather) or read (scatter) sequentially.
+#include "prism_device.hpp"
+#include "prism_internal.hpp"
+
+namespace prism {
+
+constexpr int kPermThreads = 256;
+constexpr int kPermRowsPerWave = 8;
+
+template <typename V>
+__global__ void __launch_bounds__(kPermThreads)
+permute_rows_kernel(const V* __restrict__ x, V* __restrict__ y, const uint8_t* __restrict__ zone_shape, ZoneGrid g,
+                    int64_t N, int64_t vec_per_row, int64_t x_ld_vec, int64_t y_ld_vec, int inverse) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wid = threadIdx.x / kWave;
+    const int64_t first = (static_cast<int64_t>(blockIdx.x) * (kPermThreads / kWave) + wid) * kPermRowsPerWave;
+#pragma unroll 1
+    for (int r = 0; r < kPermRowsPerWave; ++r) {
+        const int64_t p = first + r;
+        if (p >= N) return;
+        const int64_t n = block_major_to_raster(p, zone_shape, g);
+        const int64_t src = inverse ? p : n;
+        const int64_t dst = inverse ? n : p;
+        const V* __restrict__ xs = x + src * x_ld_vec;
+        V* __restrict__ yd = y + dst * y_ld_vec;
+        for (int64_t c = lane; c < vec_per_row; c += kWave) yd[c] = xs[c];
+    }
+}
+
+hipError_t launch_block_permute(const void* x, void* y, int elem_bytes, int64_t row_elems, int64_t x_ld,
+                                int64_t y_ld, const uint8_t* zone_shape, ZoneGrid g, int64_t N, int inverse,
+                                hipStream_t s) {
+    const int64_t rows_per_block = (kPermThreads / kWave) * kPermRowsPerWave;
+    const dim3 grid(static_cast<unsigned>((N + rows_per_block - 1) / rows_per_block));
+    const int64_t row_bytes = row_elems * elem_bytes;
+    const int64_t xb = x_ld * elem_bytes, yb = y_ld * elem_bytes;
+    const uintptr_t align = reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(y);
+    if ((row_bytes % 16) == 0 && (xb % 16) == 0 && (yb % 16) == 0 && (align % 16) == 0) {
+        hipLaunchKernelGGL(permute_rows_kernel<uint4>, grid, dim3(kPermThreads), 0, s,
+                           static_cast<const uint4*>(x), static_cast<uint4*>(y), zone_shape, g, N, row_bytes / 16,
+                           xb / 16, yb / 16, inverse);
+    } else if ((row_bytes % 4) == 0 && (xb % 4) == 0 && (yb % 4) == 0 && (align % 4) == 0) {
+        hipLaunchKernelGGL(permute_rows_kernel<uint32_t>, grid, dim3(kPermThreads), 0, s,
+                           static_cast<const uint32_t*>(x), static_cast<uint32_t*>(y), zone_shape, g, N,
+                           row_bytes / 4, xb / 4, yb / 4, inverse);
+    } else {
+        hipLaunchKernelGGL(permute_rows_kernel<uint16_t>, grid, dim3(kPermThreads), 0, s,
+                           static_cast<const uint16_t*>(x), static_cast<uint16_t*>(y), zone_shape, g, N,
+                           row_bytes / 2, xb / 2, yb / 2, inverse);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace prism

@@ -1,0 +1,321 @@
+// prism_api.cpp - the C ABI declared in include/prism.h: argument checks,
+// workspace carving and kernel launches.  Nothing here allocates device memory
+// or keeps state between calls; errors are reported by status code plus a
+// thread-local message.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+
+#include "prism.h"
+#include "prism_device.hpp"
+#include "prism_internal.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+prism_status fail(prism_status st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+prism_status hip_status(hipError_t e, const char* what) {
+    if (e == hipSuccess) return PRISM_OK;
+    return fail(PRISM_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Carves consecutive aligned regions out of the caller's workspace.
+struct Carver {
+    char* base;
+    size_t off = 0;
+    explicit Carver(void* b) : base(static_cast<char*>(b)) {}
+    template <typename T>
+    T* take(size_t count) {
+        T* p = base ? reinterpret_cast<T*>(base + off) : nullptr;
+        off += align_up(count * sizeof(T));
+        return p;
+    }
+};
+
+struct SelectWs {
+    double* pooled;
+    float* logits;
+    int32_t* row_count;
+    uint32_t* row_thr;
+    int32_t* row_jlim;
+};
+SelectWs carve_select(Carver& c, int64_t heads, int64_t d, int64_t nb) {
+    SelectWs w;
+    w.pooled = c.take<double>(2 * heads * nb * d);
+    w.logits = c.take<float>(heads * nb * nb);
+    w.row_count = c.take<int32_t>(heads * nb);
+    w.row_thr = c.take<uint32_t>(heads * nb);
+    w.row_jlim = c.take<int32_t>(heads * nb);
+    return w;
+}
+
+struct BwdWs {
+    float* Dq;
+    int32_t* tcount;
+    int32_t* tr_offsets;
+    int32_t* tr_idx;
+    int32_t* scratch;
+};
+BwdWs carve_bwd(Carver& c, int64_t N, int64_t heads, int64_t nb, int64_t cap) {
+    BwdWs w;
+    w.Dq = c.take<float>(heads * N);
+    w.tcount = c.take<int32_t>(heads * nb);
+    w.tr_offsets = c.take<int32_t>(heads * (nb + 1));
+    w.tr_idx = c.take<int32_t>(heads * cap);
+    w.scratch = c.take<int32_t>(heads * cap);
+    return w;
+}
+
+size_t zone_ws(int64_t N, int64_t C) {
+    const int nZ = static_cast<int>(N / prism::kZoneTokens);
+    return align_up(prism::zone_partial_doubles(nZ, C) * sizeof(double)) +
+           align_up(static_cast<size_t>(nZ) * PRISM_ZS_STRIDE * sizeof(double));
+}
+
+bool use_simt_attention(prism_dtype dt) {
+    if (dt == PRISM_F32) return true;
+    const char* e = std::getenv("PRISM_ATTN_SIMT");
+    return e && e[0] == '1';
+}
+
+prism_status check_grid(int32_t T, int32_t H, int32_t W) {
+    if (T <= 0 || H <= 0 || W <= 0 || T % 8 || H % 8 || W % 8)
+        return fail(PRISM_E_GRID, "grid %d x %d x %d: sides must be positive multiples of 8", T, H, W);
+    const int64_t nZ = static_cast<int64_t>(T / 8) * (H / 8) * (W / 8);
+    if (nZ > (1 << 22)) return fail(PRISM_E_ARG, "grid too large (%lld zones)", static_cast<long long>(nZ));
+    return PRISM_OK;
+}
+
+int elem_bytes(prism_dtype dt) { return dt == PRISM_BF16 ? 2 : 4; }
+
+// shared checks of the token-tensor calls
+prism_status check_tokens(prism_dtype dt, int64_t N, int32_t heads, int32_t d, int64_t ld, int64_t hs, int32_t nb,
+                          int64_t cap) {
+    if (dt != PRISM_F32 && dt != PRISM_BF16) return fail(PRISM_E_DTYPE, "unknown dtype %d", static_cast<int>(dt));
+    if (N <= 0 || N % 64) return fail(PRISM_E_ARG, "N = %lld must be a positive multiple of 64", static_cast<long long>(N));
+    if (heads <= 0) return fail(PRISM_E_ARG, "heads = %d must be positive", heads);
+    if (d != 64 && d != 128) return fail(PRISM_E_UNSUPPORTED, "d = %d: supported head sizes are 64 and 128", d);
+    if (ld < d || hs < 0) return fail(PRISM_E_ARG, "bad strides ld = %lld, hs = %lld", static_cast<long long>(ld),
+                                      static_cast<long long>(hs));
+    const int64_t vec = 16 / elem_bytes(dt);
+    if (ld % vec || hs % vec)
+        return fail(PRISM_E_UNSUPPORTED, "strides must be multiples of %lld elements", static_cast<long long>(vec));
+    if (nb <= 0 || static_cast<int64_t>(nb) * 64 > N)
+        return fail(PRISM_E_ARG, "nb = %d out of range for N = %lld", nb, static_cast<long long>(N));
+    if (nb > 32768) return fail(PRISM_E_UNSUPPORTED, "nb = %d above the 32768-block limit", nb);
+    if (cap <= 0) return fail(PRISM_E_ARG, "cap must be positive");
+    return PRISM_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+prism::ZoneGrid grid_of(int32_t T, int32_t H, int32_t W) {
+    prism::ZoneGrid g;
+    g.T = T;
+    g.H = H;
+    g.W = W;
+    g.nH = H / 8;
+    g.nW = W / 8;
+    return g;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* prism_status_string(prism_status s) {
+    switch (s) {
+        case PRISM_OK: return "ok";
+        case PRISM_E_ARG: return "invalid argument";
+        case PRISM_E_GRID: return "grid sides must be positive multiples of 8";
+        case PRISM_E_DTYPE: return "unknown dtype";
+        case PRISM_E_UNSUPPORTED: return "unsupported size, stride or alignment";
+        case PRISM_E_WORKSPACE: return "workspace missing or too small";
+        case PRISM_E_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+const char* prism_last_error(void) { return g_last_error.c_str(); }
+
+void prism_candidate_shapes(int32_t out[16][3]) {
+    for (int i = 0; i < 16; ++i) {
+        int bt, bh, bw;
+        prism::shape_of(i, bt, bh, bw);
+        out[i][0] = bt;
+        out[i][1] = bh;
+        out[i][2] = bw;
+    }
+}
+
+size_t prism_workspace_size(int32_t op, int64_t N, int32_t heads, int32_t d, int32_t nb, int64_t cap) {
+    if (N <= 0) return 0;
+    switch (op) {
+        case PRISM_OP_ZONE_SHAPES: return zone_ws(N, d);
+        case PRISM_OP_SELECT: {
+            Carver c(nullptr);
+            carve_select(c, heads, d, nb);
+            return c.off;
+        }
+        case PRISM_OP_ATTN_FWD: return 0;
+        case PRISM_OP_ATTN_BWD: {
+            Carver c(nullptr);
+            carve_bwd(c, N, heads, nb, cap);
+            return c.off;
+        }
+    }
+    return 0;
+}
+
+prism_status prism_zone_shapes(int32_t T, int32_t H, int32_t W, const void* v, prism_dtype vdt, int64_t C,
+                               int64_t v_ld, const float* a_map, const prism_shape_params* prm, uint8_t* zone_shape,
+                               int32_t* block_offsets, int32_t* nb_dev, int32_t* nb_host, double* zone_stats, void* ws,
+                               size_t ws_bytes, hipStream_t stream) {
+    prism_status st = check_grid(T, H, W);
+    if (st != PRISM_OK) return st;
+    if (vdt != PRISM_F32 && vdt != PRISM_BF16) return fail(PRISM_E_DTYPE, "unknown dtype %d", static_cast<int>(vdt));
+    if (!v || !a_map || !zone_shape || !block_offsets || !nb_dev) return fail(PRISM_E_ARG, "null pointer argument");
+    if (C <= 0 || v_ld < C) return fail(PRISM_E_ARG, "bad channel count C = %lld or stride v_ld = %lld",
+                                        static_cast<long long>(C), static_cast<long long>(v_ld));
+    prism_shape_params p{0.5, 0.25, 1e-6};
+    if (prm) p = *prm;
+    if (!(p.tau256 >= 0.0 && p.tau256 <= p.tau128 && p.tau128 <= 1.0) || !(p.eps > 0.0) || !std::isfinite(p.eps))
+        return fail(PRISM_E_ARG, "thresholds must satisfy 0 <= tau256 <= tau128 <= 1 and eps > 0");
+    const int64_t N = static_cast<int64_t>(T) * H * W;
+    const size_t need = zone_ws(N, C);
+    if (!ws || ws_bytes < need)
+        return fail(PRISM_E_WORKSPACE, "zone_shapes needs %zu workspace bytes, got %zu", need, ws ? ws_bytes : 0);
+    Carver c(ws);
+    const int nZ = static_cast<int>(N / prism::kZoneTokens);
+    double* partial = c.take<double>(prism::zone_partial_doubles(nZ, C));
+    double* rec = c.take<double>(static_cast<size_t>(nZ) * PRISM_ZS_STRIDE);
+    st = hip_status(prism::launch_zone_shapes(v, vdt == PRISM_BF16, C, v_ld, a_map, grid_of(T, H, W), nZ, p.tau128,
+                                              p.tau256, p.eps, zone_shape, block_offsets, nb_dev, partial, rec, stream),
+                    "zone_shapes launch");
+    if (st != PRISM_OK) return st;
+    if (zone_stats) {
+        st = hip_status(hipMemcpyAsync(zone_stats, rec, static_cast<size_t>(nZ) * PRISM_ZS_STRIDE * sizeof(double),
+                                       hipMemcpyDeviceToDevice, stream),
+                        "zone_stats copy");
+        if (st != PRISM_OK) return st;
+    }
+    if (nb_host) {
+        st = hip_status(hipMemcpyAsync(nb_host, nb_dev, sizeof(int32_t), hipMemcpyDeviceToHost, stream), "NB copy");
+        if (st != PRISM_OK) return st;
+        st = hip_status(hipStreamSynchronize(stream), "stream synchronize");
+    }
+    return st;
+}
+
+prism_status prism_block_permute(int32_t T, int32_t H, int32_t W, const uint8_t* zone_shape, const void* x, void* y,
+                                 prism_dtype dt, int64_t row_elems, int64_t x_ld, int64_t y_ld, int32_t inverse,
+                                 hipStream_t stream) {
+    prism_status st = check_grid(T, H, W);
+    if (st != PRISM_OK) return st;
+    if (dt != PRISM_F32 && dt != PRISM_BF16) return fail(PRISM_E_DTYPE, "unknown dtype %d", static_cast<int>(dt));
+    if (!zone_shape || !x || !y) return fail(PRISM_E_ARG, "null pointer argument");
+    if (row_elems <= 0 || x_ld < row_elems || y_ld < row_elems)
+        return fail(PRISM_E_ARG, "bad row_elems = %lld or strides", static_cast<long long>(row_elems));
+    if (inverse != 0 && inverse != 1) return fail(PRISM_E_ARG, "inverse must be 0 or 1");
+    const int64_t N = static_cast<int64_t>(T) * H * W;
+    const int eb = elem_bytes(dt);
+    const char* xb = static_cast<const char*>(x);
+    const char* yb = static_cast<const char*>(y);
+    const int64_t xspan = ((N - 1) * x_ld + row_elems) * eb, yspan = ((N - 1) * y_ld + row_elems) * eb;
+    if (xb < yb + yspan && yb < xb + xspan) return fail(PRISM_E_ARG, "x and y overlap");
+    return hip_status(prism::launch_block_permute(x, y, eb, row_elems, x_ld, y_ld, zone_shape, grid_of(T, H, W), N,
+                                                  inverse, stream),
+                      "block_permute launch");
+}
+
+prism_status prism_select(const void* q, const void* k, prism_dtype dt, int64_t N, int32_t heads, int32_t d,
+                          int64_t ld, int64_t hs, const int32_t* block_offsets, int32_t nb, int32_t top_k, double top_p,
+                          float scale, int32_t* sel_offsets, int32_t* sel_idx, int64_t cap, int64_t* sel_total,
+                          float* logits, void* ws, size_t ws_bytes, hipStream_t stream) {
+    prism_status st = check_tokens(dt, N, heads, d, ld, hs, nb, cap);
+    if (st != PRISM_OK) return st;
+    if (!q || !k || !block_offsets || !sel_offsets || !sel_idx || !sel_total)
+        return fail(PRISM_E_ARG, "null pointer argument");
+    if (top_k < 0 || !(top_p >= 0.0 && top_p <= 1.0)) return fail(PRISM_E_ARG, "need k >= 0 and 0 <= p <= 1");
+    if (!std::isfinite(scale)) return fail(PRISM_E_ARG, "scale must be finite");
+    const size_t need = prism_workspace_size(PRISM_OP_SELECT, N, heads, d, nb, cap);
+    if (!ws || ws_bytes < need)
+        return fail(PRISM_E_WORKSPACE, "select needs %zu workspace bytes, got %zu", need, ws ? ws_bytes : 0);
+    Carver c(ws);
+    SelectWs w = carve_select(c, heads, d, nb);
+    float* L = logits ? logits : w.logits;
+    return hip_status(prism::launch_select(q, k, dt == PRISM_BF16, heads, d, ld, hs, block_offsets, nb, top_k, top_p,
+                                           scale, sel_offsets, sel_idx, cap, sel_total, L, w.pooled, w.row_count,
+                                           w.row_thr, w.row_jlim, stream),
+                      "select launch");
+}
+
+prism_status prism_sparse_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, prism_dtype dt,
+                                   int64_t N, int32_t heads, int32_t d, int64_t ld, int64_t hs,
+                                   const int32_t* block_offsets, int32_t nb, const int32_t* sel_offsets,
+                                   const int32_t* sel_idx, int64_t cap, float scale, void* ws, size_t ws_bytes,
+                                   hipStream_t stream) {
+    prism_status st = check_tokens(dt, N, heads, d, ld, hs, nb, cap);
+    if (st != PRISM_OK) return st;
+    if (!q || !k || !v || !o || !lse || !block_offsets || !sel_offsets || !sel_idx)
+        return fail(PRISM_E_ARG, "null pointer argument");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+        return fail(PRISM_E_UNSUPPORTED, "token tensors must be 16-byte aligned");
+    if (!std::isfinite(scale)) return fail(PRISM_E_ARG, "scale must be finite");
+    (void)ws;
+    (void)ws_bytes;
+    return hip_status(prism::launch_attn_fwd_simt(q, k, v, o, lse, dt == PRISM_BF16, N, heads, d, ld, hs,
+                                                  block_offsets, nb, sel_offsets, sel_idx, cap, scale, stream),
+                      "attention forward launch");
+}
+
+prism_status prism_sparse_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                                   const float* lse, void* dq, void* dk, void* dv, prism_dtype dt, int64_t N,
+                                   int32_t heads, int32_t d, int64_t ld, int64_t hs, const int32_t* block_offsets,
+                                   int32_t nb, const int32_t* sel_offsets, const int32_t* sel_idx, int64_t cap,
+                                   float scale, void* ws, size_t ws_bytes, hipStream_t stream) {
+    prism_status st = check_tokens(dt, N, heads, d, ld, hs, nb, cap);
+    if (st != PRISM_OK) return st;
+    if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !block_offsets || !sel_offsets || !sel_idx)
+        return fail(PRISM_E_ARG, "null pointer argument");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) || !aligned16(dq) ||
+        !aligned16(dk) || !aligned16(dv))
+        return fail(PRISM_E_UNSUPPORTED, "token tensors must be 16-byte aligned");
+    if (!std::isfinite(scale)) return fail(PRISM_E_ARG, "scale must be finite");
+    const size_t need = prism_workspace_size(PRISM_OP_ATTN_BWD, N, heads, d, nb, cap);
+    if (!ws || ws_bytes < need)
+        return fail(PRISM_E_WORKSPACE, "backward needs %zu workspace bytes, got %zu", need, ws ? ws_bytes : 0);
+    Carver c(ws);
+    BwdWs w = carve_bwd(c, N, heads, nb, cap);
+    const bool bf16 = dt == PRISM_BF16;
+    st = hip_status(prism::launch_bwd_dot(o, dout, bf16, N, heads, d, ld, hs, w.Dq, stream), "backward dot launch");
+    if (st != PRISM_OK) return st;
+    st = hip_status(prism::launch_transpose_csr(sel_offsets, sel_idx, nb, heads, cap, w.tcount, w.tr_offsets, w.tr_idx,
+                                                w.scratch, stream),
+                    "transposed selection launch");
+    if (st != PRISM_OK) return st;
+    return hip_status(prism::launch_attn_bwd_simt(q, k, v, dout, lse, w.Dq, dq, dk, dv, bf16, N, heads, d, ld, hs,
+                                                  block_offsets, nb, sel_offsets, sel_idx, w.tr_offsets, w.tr_idx, cap,
+                                                  scale, stream),
+                      "attention backward launch");
+}
+
+}  // extern "C"

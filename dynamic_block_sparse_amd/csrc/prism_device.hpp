@@ -1,0 +1,122 @@
+// prism_device.hpp - device-side helpers shared by the gfx950 kernels of the
+// Prism block-sparse attention library.  Wave size is 64 throughout.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace prism {
+
+constexpr int kWave = 64;
+constexpr int kZone = 8;
+constexpr int kZoneTokens = 512;
+
+// Candidate block shapes (b_T, b_H, b_W), 16 entries: every box with edges in
+// {2, 4, 8} and volume 64, 128 or 256, by volume then lexicographically.  The
+// index is what zone_shape stores and what breaks ties between equidistant
+// shapes.
+__host__ __device__ inline void shape_of(int idx, int& bt, int& bh, int& bw) {
+    // packed as 2-bit log2 edges: (lt << 4) | (lh << 2) | lw
+    constexpr uint8_t kPacked[16] = {
+        (1 << 4) | (2 << 2) | 3, (1 << 4) | (3 << 2) | 2, (2 << 4) | (1 << 2) | 3,
+        (2 << 4) | (2 << 2) | 2, (2 << 4) | (3 << 2) | 1, (3 << 4) | (1 << 2) | 2,
+        (3 << 4) | (2 << 2) | 1,                                      // volume 64
+        (1 << 4) | (3 << 2) | 3, (2 << 4) | (2 << 2) | 3, (2 << 4) | (3 << 2) | 2,
+        (3 << 4) | (1 << 2) | 3, (3 << 4) | (2 << 2) | 2, (3 << 4) | (3 << 2) | 1,   // 128
+        (2 << 4) | (3 << 2) | 3, (3 << 4) | (2 << 2) | 3, (3 << 4) | (3 << 2) | 2    // 256
+    };
+    const uint8_t p = kPacked[idx & 15];
+    bt = 1 << ((p >> 4) & 3);
+    bh = 1 << ((p >> 2) & 3);
+    bw = 1 << (p & 3);
+}
+
+// bf16 <-> fp32 (round to nearest even; inputs here are finite)
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+    return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return static_cast<uint16_t>(u >> 16);
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+}
+
+// wave-level reductions (fixed butterfly order, hence deterministic)
+template <typename T>
+__device__ __forceinline__ T wave_sum(T v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+    return v;
+}
+template <typename T>
+__device__ __forceinline__ T wave_max(T v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        T o = __shfl_xor(v, off, kWave);
+        v = o > v ? o : v;
+    }
+    return v;
+}
+
+// Block-wide sum in a fixed order: butterfly inside each wave, then the wave
+// totals in wave order.  `scratch` holds at least blockDim.x / 64 values.
+template <typename T>
+__device__ __forceinline__ T block_sum(T v, T* scratch) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wid = threadIdx.x / kWave;
+    const int nw = blockDim.x / kWave;
+    v = wave_sum(v);
+    __syncthreads();
+    if (lane == 0) scratch[wid] = v;
+    __syncthreads();
+    T t = scratch[0];
+    for (int w = 1; w < nw; ++w) t += scratch[w];
+    return t;
+}
+template <typename T>
+__device__ __forceinline__ T block_max(T v, T* scratch) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wid = threadIdx.x / kWave;
+    const int nw = blockDim.x / kWave;
+    v = wave_max(v);
+    __syncthreads();
+    if (lane == 0) scratch[wid] = v;
+    __syncthreads();
+    T t = scratch[0];
+    for (int w = 1; w < nw; ++w) t = scratch[w] > t ? scratch[w] : t;
+    return t;
+}
+
+// Map block-major position p to its raster token index for the zone shapes.
+struct ZoneGrid {
+    int T, H, W, nH, nW;
+};
+__device__ __forceinline__ int64_t block_major_to_raster(int64_t p, const uint8_t* __restrict__ zone_shape,
+                                                         const ZoneGrid g) {
+    const int64_t m = p >> 9;
+    const int q = static_cast<int>(p & 511);
+    int bt, bh, bw;
+    shape_of(zone_shape[m], bt, bh, bw);
+    const int vol = bt * bh * bw;
+    const int j = q / vol;
+    const int r = q - j * vol;
+    const int nbh = kZone / bh, nbw = kZone / bw;
+    const int jt = j / (nbh * nbw);
+    const int jh = (j / nbw) % nbh;
+    const int jw = j % nbw;
+    const int rt = r / (bh * bw);
+    const int rh = (r / bw) % bh;
+    const int rw = r % bw;
+    const int64_t zt = m / (g.nH * g.nW);
+    const int64_t zh = (m / g.nW) % g.nH;
+    const int64_t zw = m % g.nW;
+    const int64_t t = zt * kZone + jt * bt + rt;
+    const int64_t h = zh * kZone + jh * bh + rh;
+    const int64_t w = zw * kZone + jw * bw + rw;
+    return (t * g.H + h) * g.W + w;
+}
+
+}  // namespace prism

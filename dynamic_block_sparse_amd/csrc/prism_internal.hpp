@@ -1,0 +1,44 @@
+// prism_internal.hpp - launchers shared between the kernel files and the host
+// ABI layer.  Every launcher is asynchronous on `s` and returns the launch
+// status; argument checking is done by the caller (prism_api.cpp).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace prism {
+
+struct ZoneGrid;
+
+hipError_t launch_zone_shapes(const void* v, bool bf16, int64_t C, int64_t ld, const float* a, ZoneGrid g, int nZ,
+                              double tau128, double tau256, double eps, uint8_t* zone_shape, int32_t* block_offsets,
+                              int32_t* nb_dev, double* partial, double* rec, hipStream_t s);
+size_t zone_partial_doubles(int nZ, int64_t C);
+
+hipError_t launch_block_permute(const void* x, void* y, int elem_bytes, int64_t row_elems, int64_t x_ld,
+                                int64_t y_ld, const uint8_t* zone_shape, ZoneGrid g, int64_t N, int inverse,
+                                hipStream_t s);
+
+hipError_t launch_select(const void* q, const void* k, bool bf16, int heads, int d, int64_t ld, int64_t hs,
+                         const int32_t* offs, int nb, int top_k, double top_p, float scale, int32_t* sel_offsets,
+                         int32_t* sel_idx, int64_t cap, int64_t* sel_total, float* logits, double* pooled,
+                         int32_t* row_count, uint32_t* row_thr, int32_t* row_jlim, hipStream_t s);
+
+hipError_t launch_transpose_csr(const int32_t* sel_offsets, const int32_t* sel_idx, int nb, int heads, int64_t cap,
+                                int32_t* tcount, int32_t* tr_offsets, int32_t* tr_idx, int32_t* scratch,
+                                hipStream_t s);
+
+hipError_t launch_attn_fwd_simt(const void* q, const void* k, const void* v, void* o, float* lse, bool bf16, int64_t N,
+                                int heads, int d, int64_t ld, int64_t hs, const int32_t* offs, int nb,
+                                const int32_t* so, const int32_t* si, int64_t cap, float scale, hipStream_t s);
+
+hipError_t launch_bwd_dot(const void* o, const void* dout, bool bf16, int64_t N, int heads, int d, int64_t ld,
+                          int64_t hs, float* Dq, hipStream_t s);
+
+hipError_t launch_attn_bwd_simt(const void* q, const void* k, const void* v, const void* dout, const float* lse,
+                                const float* Dq, void* dq, void* dk, void* dv, bool bf16, int64_t N, int heads, int d,
+                                int64_t ld, int64_t hs, const int32_t* offs, int nb, const int32_t* so,
+                                const int32_t* si, const int32_t* to, const int32_t* ti, int64_t cap, float scale,
+                                hipStream_t s);
+
+}  // namespace prism

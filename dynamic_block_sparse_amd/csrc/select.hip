@@ -1,0 +1,473 @@
+// select.hip - pooled block scores and hybrid Top-k U Top-p key-block
+// selection (Prism reading guide, xyznot.com paper 2610.05416, "Phương pháp"
+// §3: key blocks are mean-pooled, scored against query blocks into block
+// probabilities P_i, and S_i = Top-k(P_i, k) U Top-p(P_i, p)).
+//
+// Kernels, in launch order:
+//   pool_kernel          float64 block means of Q and K per head (sums of at
+//                        most 256 bf16 values are exact in float64)
+//   logits_kernel        L[h][i][j] = fl32(scale * (Q_bar_i . K_bar_j)), the dot in
+//                        float64: the scores are rounded once, so they equal
+//                        the float64 definition's nearest float
+//   select_count_kernel  per row: max, float64 softmax mass, and a binary
+//                        search over the order-preserving 32-bit key of the
+//                        scores for the boundary of the first max(k, n_p)
+//                        ranked blocks; ties at the boundary are resolved by
+//                        index.  No sort: the union of the two prefixes is one
+//                        prefix of the ranking, so only its boundary matters.
+//   csr_scan_kernel      per head exclusive scan of the row counts
+//   select_write_kernel  per row: ordered compaction of the selected indices
+// and, for the backward, the transposed CSR (key block -> query blocks):
+//   tr_count_kernel, csr_scan_kernel, tr_fill_kernel, tr_sort_kernel.
+#include "prism_device.hpp"
+#include "prism_internal.hpp"
+
+namespace prism {
+
+// ---------------------------------------------------------------- pooling
+
+template <typename TIn>
+__device__ __forceinline__ double load_as_double(const TIn* p);
+template <>
+__device__ __forceinline__ double load_as_double<uint16_t>(const uint16_t* p) {
+    return static_cast<double>(bf16_to_f32(*p));
+}
+template <>
+__device__ __forceinline__ double load_as_double<float>(const float* p) {
+    return static_cast<double>(*p);
+}
+
+// grid (nb, heads, 2): z = 0 pools q, z = 1 pools k.  256 threads: channel
+// c = t % D, row phase t / D; the phases are combined in phase order.
+template <typename TIn, int D>
+__global__ void __launch_bounds__(256)
+pool_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, int64_t ld, int64_t hs,
+            const int32_t* __restrict__ offs, int nb, int heads, double* __restrict__ pooled) {
+    constexpr int G = 256 / D;
+    __shared__ double part[G][D];
+    const int i = blockIdx.x, h = blockIdx.y, which = blockIdx.z;
+    const TIn* __restrict__ x = (which == 0 ? q : k) + static_cast<int64_t>(h) * hs;
+    const int c = threadIdx.x % D;
+    const int ph = threadIdx.x / D;
+    const int r0 = offs[i], r1 = offs[i + 1];
+    double s = 0.0;
+    for (int r = r0 + ph; r < r1; r += G) s += load_as_double(x + static_cast<int64_t>(r) * ld + c);
+    part[ph][c] = s;
+    __syncthreads();
+    if (ph == 0) {
+        double t = part[0][c];
+        for (int g = 1; g < G; ++g) t += part[g][c];
+        pooled[((static_cast<int64_t>(which) * heads + h) * nb + i) * D + c] = t / static_cast<double>(r1 - r0);
+    }
+}
+
+// ---------------------------------------------------------------- scores
+
+constexpr int kLT = 64;   // output tile
+constexpr int kLK = 16;   // reduction chunk
+
+template <int D>
+__global__ void __launch_bounds__(256)
+logits_kernel(const double* __restrict__ pooled, int nb, int heads, double scale, float* __restrict__ logits) {
+    __shared__ double As[kLK][kLT + 1];
+    __shared__ double Bs[kLK][kLT + 1];
+    const int h = blockIdx.z;
+    const int i0 = blockIdx.y * kLT, j0 = blockIdx.x * kLT;
+    const double* __restrict__ Qb = pooled + static_cast<int64_t>(h) * nb * D;
+    const double* __restrict__ Kb = pooled + (static_cast<int64_t>(heads) + h) * nb * D;
+    const int tx = threadIdx.x % 16, ty = threadIdx.x / 16;
+    double acc[4][4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) acc[a][b] = 0.0;
+    for (int c0 = 0; c0 < D; c0 += kLK) {
+        // 64 rows x 16 columns of each operand: 1024 values, 4 per thread
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int idx = threadIdx.x + e * 256;
+            const int row = idx / kLK, col = idx % kLK;
+            const int gi = i0 + row, gj = j0 + row;
+            As[col][row] = gi < nb ? Qb[static_cast<int64_t>(gi) * D + c0 + col] : 0.0;
+            Bs[col][row] = gj < nb ? Kb[static_cast<int64_t>(gj) * D + c0 + col] : 0.0;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int kk = 0; kk < kLK; ++kk) {
+            double a[4], b[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                a[e] = As[kk][ty + 16 * e];
+                b[e] = Bs[kk][tx + 16 * e];
+            }
+#pragma unroll
+            for (int x = 0; x < 4; ++x)
+#pragma unroll
+                for (int y = 0; y < 4; ++y) acc[x][y] = fma(a[x], b[y], acc[x][y]);
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+        const int gi = i0 + ty + 16 * x;
+        if (gi >= nb) continue;
+#pragma unroll
+        for (int y = 0; y < 4; ++y) {
+            const int gj = j0 + tx + 16 * y;
+            if (gj < nb) logits[(static_cast<int64_t>(h) * nb + gi) * nb + gj] = static_cast<float>(scale * acc[x][y]);
+        }
+    }
+}
+
+// ---------------------------------------------------------------- selection
+
+// Order-preserving key of a finite float (-0 is folded onto +0 so that equal
+// scores compare equal); every finite value maps to a key >= 0x00800000.
+__device__ __forceinline__ uint32_t score_key(float x) {
+    uint32_t u = __float_as_uint(x == 0.0f ? 0.0f : x);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_score(uint32_t k) {
+    return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+struct CountMass {
+    int c;
+    double m;
+};
+
+template <int NW>
+__device__ __forceinline__ CountMass block_count_mass(int c, double m, int* sc, double* sm) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wid = threadIdx.x / kWave;
+    c = wave_sum(c);
+    m = wave_sum(m);
+    __syncthreads();
+    if (lane == 0) {
+        sc[wid] = c;
+        sm[wid] = m;
+    }
+    __syncthreads();
+    CountMass r{sc[0], sm[0]};
+#pragma unroll
+    for (int w = 1; w < NW; ++w) {
+        r.c += sc[w];
+        r.m += sm[w];
+    }
+    return r;
+}
+
+// One workgroup of NW waves per (row i, head h); element j of the row lives in
+// thread j % (64 NW), slot j / (64 NW).
+template <int NW, int E>
+__global__ void __launch_bounds__(NW * 64)
+select_count_kernel(const float* __restrict__ logits, int nb, int top_k, double top_p, int32_t* __restrict__ row_count,
+                    uint32_t* __restrict__ row_thr, int32_t* __restrict__ row_jlim) {
+    constexpr int NT = NW * 64;
+    __shared__ int sc[NW];
+    __shared__ double sm[NW];
+    __shared__ float sf[NW];
+    const int i = blockIdx.x, h = blockIdx.y;
+    const int64_t row = static_cast<int64_t>(h) * nb + i;
+    const float* __restrict__ L = logits + row * nb;
+    uint32_t key[E];
+    double ev[E];
+    float lmax = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        const int j = threadIdx.x + e * NT;
+        if (j < nb) {
+            const float x = L[j];
+            key[e] = score_key(x);
+            lmax = x > lmax ? x : lmax;
+        } else {
+            key[e] = 0u;
+        }
+    }
+    const float M = block_max(lmax, sf);
+    double zpart = 0.0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        ev[e] = key[e] ? exp(static_cast<double>(key_score(key[e])) - static_cast<double>(M)) : 0.0;
+        zpart += ev[e];
+    }
+    auto count_mass = [&](uint64_t u) -> CountMass {
+        int c = 0;
+        double m = 0.0;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const bool in = static_cast<uint64_t>(key[e]) >= u && key[e] != 0u;
+            c += in ? 1 : 0;
+            m += in ? ev[e] : 0.0;
+        }
+        return block_count_mass<NW>(c, m, sc, sm);
+    };
+    const CountMass all = count_mass(1);          // every block: the mass is Z
+    const double target = top_p * all.m;
+    // the Top-p prefix holds at least one block, so the kept prefix has at
+    // least max(k, 1) blocks
+    const int kk = top_k > 1 ? top_k : 1;
+    int count;
+    uint32_t thr;
+    int jlim;
+    if (!(all.c >= kk && all.m >= target)) {
+        count = nb;                               // no prefix qualifies: keep every block
+        thr = 0u;
+        jlim = -1;
+    } else {
+        uint64_t lo = 1, hi = 1ull << 32;         // pred(lo) holds, pred(hi) fails
+        while (hi - lo > 1) {
+            const uint64_t mid = lo + ((hi - lo) >> 1);
+            const CountMass cm = count_mass(mid);
+            if (cm.c >= kk && cm.m >= target) lo = mid;
+            else hi = mid;
+        }
+        thr = static_cast<uint32_t>(lo);
+        const CountMass gt = (lo == 0xFFFFFFFFull) ? CountMass{0, 0.0} : count_mass(lo + 1);
+        int ceq = 0;
+#pragma unroll
+        for (int e = 0; e < E; ++e) ceq += key[e] == thr ? 1 : 0;
+        ceq = block_sum(ceq, sc);
+        const double eb = exp(static_cast<double>(key_score(thr)) - static_cast<double>(M));
+        int m = 0;
+        double acc = gt.m;
+        do {
+            ++m;
+            acc += eb;
+        } while (m < ceq && !(gt.c + m >= kk && acc >= target));
+        count = gt.c + m;
+        if (m == ceq) {
+            jlim = nb;
+        } else {
+            // smallest index x with #(ties at index <= x) >= m
+            int a = -1, b = nb - 1;               // count(a) < m <= count(b)
+            while (b - a > 1) {
+                const int x = a + ((b - a) >> 1);
+                int c = 0;
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    const int j = threadIdx.x + e * NT;
+                    c += (key[e] == thr && j <= x) ? 1 : 0;
+                }
+                c = block_sum(c, sc);
+                if (c >= m) b = x;
+                else a = x;
+            }
+            jlim = b;
+        }
+    }
+    if (threadIdx.x == 0) {
+        row_count[row] = count;
+        row_thr[row] = thr;
+        row_jlim[row] = jlim;
+    }
+}
+
+// exclusive scan of counts[h][0..n) into offsets[h][0..n]; totals[h] = sum
+__global__ void __launch_bounds__(1024)
+csr_scan_kernel(const int32_t* __restrict__ counts, int n, int32_t* __restrict__ offsets, int64_t* __restrict__ totals) {
+    __shared__ int32_t buf[1024];
+    __shared__ int64_t carry;
+    const int h = blockIdx.x;
+    const int32_t* __restrict__ c = counts + static_cast<int64_t>(h) * n;
+    int32_t* __restrict__ o = offsets + static_cast<int64_t>(h) * (n + 1);
+    if (threadIdx.x == 0) carry = 0;
+    __syncthreads();
+    for (int base = 0; base < n; base += 1024) {
+        const int idx = base + threadIdx.x;
+        const int32_t v = idx < n ? c[idx] : 0;
+        buf[threadIdx.x] = v;
+        __syncthreads();
+        for (int off = 1; off < 1024; off <<= 1) {
+            const int32_t t = threadIdx.x >= off ? buf[threadIdx.x - off] : 0;
+            __syncthreads();
+            buf[threadIdx.x] += t;
+            __syncthreads();
+        }
+        if (idx < n) o[idx] = static_cast<int32_t>(carry + buf[threadIdx.x] - v);
+        __syncthreads();
+        if (threadIdx.x == 1023) carry += buf[1023];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) {
+        o[n] = static_cast<int32_t>(carry);
+        if (totals) totals[h] = carry;
+    }
+}
+
+template <int NW>
+__global__ void __launch_bounds__(NW * 64)
+select_write_kernel(const float* __restrict__ logits, int nb, const uint32_t* __restrict__ row_thr,
+                    const int32_t* __restrict__ row_jlim, const int32_t* __restrict__ sel_offsets,
+                    int32_t* __restrict__ sel_idx, int64_t cap) {
+    constexpr int NT = NW * 64;
+    __shared__ int sc[NW];
+    const int i = blockIdx.x, h = blockIdx.y;
+    const int64_t row = static_cast<int64_t>(h) * nb + i;
+    const float* __restrict__ L = logits + row * nb;
+    const uint32_t thr = row_thr[row];
+    const int jlim = row_jlim[row];
+    int64_t pos = sel_offsets[static_cast<int64_t>(h) * (nb + 1) + i];
+    int32_t* __restrict__ out = sel_idx + static_cast<int64_t>(h) * cap;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wid = threadIdx.x / kWave;
+    for (int base = 0; base < nb; base += NT) {
+        const int j = base + threadIdx.x;
+        bool f = false;
+        if (j < nb) {
+            const uint32_t kk = score_key(L[j]);
+            f = kk > thr || (kk == thr && j <= jlim);
+        }
+        const uint64_t bal = __ballot(f);
+        const int before = __popcll(bal & ((lane == 0) ? 0ull : (~0ull >> (64 - lane))));
+        __syncthreads();
+        if (lane == 0) sc[wid] = __popcll(bal);
+        __syncthreads();
+        int woff = 0, tot = 0;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            woff += w < wid ? sc[w] : 0;
+            tot += sc[w];
+        }
+        if (f) {
+            const int64_t p = pos + woff + before;
+            if (p < cap) out[p] = j;
+        }
+        pos += tot;
+    }
+}
+
+// ---------------------------------------------------------------- transposed CSR
+
+__global__ void __launch_bounds__(256)
+tr_count_kernel(const int32_t* __restrict__ sel_offsets, const int32_t* __restrict__ sel_idx, int nb, int64_t cap,
+                int32_t* __restrict__ tcount) {
+    const int i = blockIdx.x, h = blockIdx.y;
+    const int32_t* __restrict__ so = sel_offsets + static_cast<int64_t>(h) * (nb + 1);
+    const int32_t* __restrict__ si = sel_idx + static_cast<int64_t>(h) * cap;
+    for (int e = so[i] + threadIdx.x; e < so[i + 1]; e += blockDim.x)
+        atomicAdd(&tcount[static_cast<int64_t>(h) * nb + si[e]], 1);
+}
+
+__global__ void __launch_bounds__(256)
+tr_fill_kernel(const int32_t* __restrict__ sel_offsets, const int32_t* __restrict__ sel_idx, int nb, int64_t cap,
+               const int32_t* __restrict__ tr_offsets, int32_t* __restrict__ tcursor, int32_t* __restrict__ tr_idx) {
+    const int i = blockIdx.x, h = blockIdx.y;
+    const int32_t* __restrict__ so = sel_offsets + static_cast<int64_t>(h) * (nb + 1);
+    const int32_t* __restrict__ si = sel_idx + static_cast<int64_t>(h) * cap;
+    const int32_t* __restrict__ to = tr_offsets + static_cast<int64_t>(h) * (nb + 1);
+    for (int e = so[i] + threadIdx.x; e < so[i + 1]; e += blockDim.x) {
+        const int j = si[e];
+        const int slot = atomicAdd(&tcursor[static_cast<int64_t>(h) * nb + j], 1);
+        tr_idx[static_cast<int64_t>(h) * cap + to[j] + slot] = i;
+    }
+}
+
+// Sort one key block's list of query blocks ascending (the fill order depends
+// on atomics; the backward reads the lists in ascending order so that its
+// sums are deterministic).  Entries are distinct, so the rank of an entry is
+// the number of smaller entries.
+constexpr int kSortLds = 8192;
+__global__ void __launch_bounds__(256)
+tr_sort_kernel(const int32_t* __restrict__ tr_offsets, int nb, int64_t cap, int32_t* __restrict__ tr_idx,
+               int32_t* __restrict__ scratch) {
+    __shared__ int32_t seg[kSortLds];
+    const int j = blockIdx.x, h = blockIdx.y;
+    const int32_t* __restrict__ to = tr_offsets + static_cast<int64_t>(h) * (nb + 1);
+    const int64_t b = to[j], n = to[j + 1] - to[j];
+    if (n <= 1) return;
+    int32_t* __restrict__ list = tr_idx + static_cast<int64_t>(h) * cap + b;
+    if (n <= kSortLds) {
+        for (int64_t e = threadIdx.x; e < n; e += blockDim.x) seg[e] = list[e];
+        __syncthreads();
+        for (int64_t e = threadIdx.x; e < n; e += blockDim.x) {
+            const int32_t v = seg[e];
+            int r = 0;
+            for (int64_t f = 0; f < n; ++f) r += seg[f] < v ? 1 : 0;
+            list[r] = v;
+        }
+    } else {
+        // long list: rank against a copy in the scratch area (same offsets)
+        int32_t* __restrict__ cp = scratch + static_cast<int64_t>(h) * cap + b;
+        for (int64_t e = threadIdx.x; e < n; e += blockDim.x) cp[e] = list[e];
+        __syncthreads();
+        for (int64_t e = threadIdx.x; e < n; e += blockDim.x) {
+            const int32_t v = cp[e];
+            int r = 0;
+            for (int64_t f = 0; f < n; ++f) r += cp[f] < v ? 1 : 0;
+            list[r] = v;
+        }
+    }
+}
+
+// ---------------------------------------------------------------- launchers
+
+hipError_t launch_select(const void* q, const void* k, bool bf16, int heads, int d, int64_t ld, int64_t hs,
+                         const int32_t* offs, int nb, int top_k, double top_p, float scale, int32_t* sel_offsets,
+                         int32_t* sel_idx, int64_t cap, int64_t* sel_total, float* logits, double* pooled,
+                         int32_t* row_count, uint32_t* row_thr, int32_t* row_jlim, hipStream_t s) {
+    const dim3 pg(nb, heads, 2);
+    if (bf16) {
+        if (d == 128)
+            hipLaunchKernelGGL((pool_kernel<uint16_t, 128>), pg, dim3(256), 0, s, static_cast<const uint16_t*>(q),
+                               static_cast<const uint16_t*>(k), ld, hs, offs, nb, heads, pooled);
+        else
+            hipLaunchKernelGGL((pool_kernel<uint16_t, 64>), pg, dim3(256), 0, s, static_cast<const uint16_t*>(q),
+                               static_cast<const uint16_t*>(k), ld, hs, offs, nb, heads, pooled);
+    } else {
+        if (d == 128)
+            hipLaunchKernelGGL((pool_kernel<float, 128>), pg, dim3(256), 0, s, static_cast<const float*>(q),
+                               static_cast<const float*>(k), ld, hs, offs, nb, heads, pooled);
+        else
+            hipLaunchKernelGGL((pool_kernel<float, 64>), pg, dim3(256), 0, s, static_cast<const float*>(q),
+                               static_cast<const float*>(k), ld, hs, offs, nb, heads, pooled);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const dim3 lg((nb + kLT - 1) / kLT, (nb + kLT - 1) / kLT, heads);
+    if (d == 128)
+        hipLaunchKernelGGL(logits_kernel<128>, lg, dim3(256), 0, s, pooled, nb, heads, static_cast<double>(scale), logits);
+    else
+        hipLaunchKernelGGL(logits_kernel<64>, lg, dim3(256), 0, s, pooled, nb, heads, static_cast<double>(scale), logits);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const dim3 rg(nb, heads);
+    if (nb <= 256)
+        hipLaunchKernelGGL((select_count_kernel<1, 4>), rg, dim3(64), 0, s, logits, nb, top_k, top_p, row_count,
+                           row_thr, row_jlim);
+    else if (nb <= 4096)
+        hipLaunchKernelGGL((select_count_kernel<4, 16>), rg, dim3(256), 0, s, logits, nb, top_k, top_p, row_count,
+                           row_thr, row_jlim);
+    else
+        hipLaunchKernelGGL((select_count_kernel<16, 32>), rg, dim3(1024), 0, s, logits, nb, top_k, top_p, row_count,
+                           row_thr, row_jlim);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(csr_scan_kernel, dim3(heads), dim3(1024), 0, s, row_count, nb, sel_offsets, sel_total);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(select_write_kernel<4>, rg, dim3(256), 0, s, logits, nb, row_thr, row_jlim, sel_offsets,
+                       sel_idx, cap);
+    return hipGetLastError();
+}
+
+hipError_t launch_transpose_csr(const int32_t* sel_offsets, const int32_t* sel_idx, int nb, int heads, int64_t cap,
+                                int32_t* tcount, int32_t* tr_offsets, int32_t* tr_idx, int32_t* scratch,
+                                hipStream_t s) {
+    const size_t cbytes = static_cast<size_t>(heads) * nb * sizeof(int32_t);
+    hipError_t e = hipMemsetAsync(tcount, 0, cbytes, s);
+    if (e != hipSuccess) return e;
+    const dim3 rg(nb, heads);
+    hipLaunchKernelGGL(tr_count_kernel, rg, dim3(256), 0, s, sel_offsets, sel_idx, nb, cap, tcount);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(csr_scan_kernel, dim3(heads), dim3(1024), 0, s, tcount, nb, tr_offsets,
+                       static_cast<int64_t*>(nullptr));
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = hipMemsetAsync(tcount, 0, cbytes, s)) != hipSuccess) return e;
+    hipLaunchKernelGGL(tr_fill_kernel, rg, dim3(256), 0, s, sel_offsets, sel_idx, nb, cap, tr_offsets, tcount, tr_idx);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(tr_sort_kernel, rg, dim3(256), 0, s, tr_offsets, nb, cap, tr_idx, scratch);
+    return hipGetLastError();
+}
+
+}  // namespace prism

@@ -1,0 +1,127 @@
+"""The Prism hot path end to end on device tensors.
+
+This module only allocates device memory with torch and calls the C ABI in
+order (zone shapes -> block-major permutation -> selection -> attention
+forward/backward -> inverse permutation); every step runs in libprism's HIP
+kernels.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import torch
+
+from . import prism as P
+
+
+@dataclass
+class Selection:
+    offsets: torch.Tensor     # int32 [hc, nb+1] per head chunk
+    idx: torch.Tensor         # int32 [hc, cap]
+    total: torch.Tensor       # int64 [hc]
+    cap: int
+    logits: torch.Tensor | None
+
+
+class PrismPath:
+    """One attention layer's hot path for a fixed grid and head layout.
+
+    q, k, v, do are raster-order [N, heads, d] tensors (bf16 or fp32) with
+    d contiguous.  Heads are processed in chunks of `head_chunk` (all at once
+    by default; 1 processes heads one at a time).
+    """
+
+    def __init__(self, T, H, W, heads, d, top_k, top_p, scale, head_chunk=None, prm=None, device="cuda"):
+        self.T, self.H, self.W = T, H, W
+        self.N = T * H * W
+        self.nZ = self.N // 512
+        self.heads, self.d = heads, d
+        self.top_k, self.top_p, self.scale = top_k, top_p, scale
+        self.hc = head_chunk or heads
+        if heads % self.hc:
+            raise ValueError("head_chunk must divide heads")
+        self.prm = prm
+        self.device = torch.device(device)
+        self.zone_shape = torch.empty(self.nZ, dtype=torch.uint8, device=self.device)
+        self.block_offsets = torch.empty(8 * self.nZ + 1, dtype=torch.int32, device=self.device)
+        self.nb_dev = torch.empty(1, dtype=torch.int32, device=self.device)
+        self.zone_stats = torch.empty(self.nZ * P.ZS_STRIDE, dtype=torch.float64, device=self.device)
+        self.nb = None
+
+    # -------------------------------------------------------------- stages
+    def shapes(self, v, a):
+        """v: raster [N, heads', d] or [N, C]; all of its channels enter the
+        zone statistics (one shape per zone, shared by every head)."""
+        C = v.shape[1] * v.shape[2] if v.dim() == 3 else v.shape[1]
+        ws = torch.empty(P.prism_workspace_size(P.OP_ZONE_SHAPES, self.N, 1, C, 0, 0), dtype=torch.uint8,
+                         device=self.device)
+        self.nb = P.prism_zone_shapes(self.T, self.H, self.W, v, C, v.stride(0), a, self.zone_shape,
+                                      self.block_offsets, self.nb_dev, ws, prm=self.prm, zone_stats=self.zone_stats)
+        return self.nb
+
+    def permute(self, x, inverse=False, out=None):
+        y = torch.empty_like(x) if out is None else out
+        P.prism_block_permute(self.T, self.H, self.W, self.zone_shape, x, y, x.shape[1] * x.shape[2], x.stride(0),
+                              y.stride(0), 1 if inverse else 0)
+        return y
+
+    def _cap(self):
+        return self.nb * self.nb
+
+    def select(self, qp, kp, h0=0, want_logits=False):
+        nb, hc, cap = self.nb, self.hc, self._cap()
+        offsets = torch.empty((hc, nb + 1), dtype=torch.int32, device=self.device)
+        idx = torch.empty((hc, cap), dtype=torch.int32, device=self.device)
+        total = torch.empty(hc, dtype=torch.int64, device=self.device)
+        logits = torch.empty((hc, nb, nb), dtype=torch.float32, device=self.device) if want_logits else None
+        ws = torch.empty(P.prism_workspace_size(P.OP_SELECT, self.N, hc, self.d, nb, cap), dtype=torch.uint8,
+                         device=self.device)
+        q, k = qp[:, h0:h0 + hc], kp[:, h0:h0 + hc]
+        P.prism_select(q, k, self.N, hc, self.d, q.stride(0), q.stride(1), self.block_offsets, nb, self.top_k,
+                       self.top_p, self.scale, offsets, idx, cap, total, ws, logits=logits)
+        return Selection(offsets, idx, total, cap, logits)
+
+    def forward(self, qp, kp, vp, sel, op=None, lse=None, h0=0):
+        hc = self.hc
+        if op is None:
+            op = torch.empty_like(qp)
+        if lse is None:
+            lse = torch.empty((hc, self.N), dtype=torch.float32, device=self.device)
+        q, k, v, o = (x[:, h0:h0 + hc] for x in (qp, kp, vp, op))
+        P.prism_sparse_attn_fwd(q, k, v, o, lse, self.N, hc, self.d, q.stride(0), q.stride(1), self.block_offsets,
+                                self.nb, sel.offsets, sel.idx, sel.cap, self.scale)
+        return op, lse
+
+    def backward(self, qp, kp, vp, op, dop, lse, sel, grads=None, h0=0):
+        hc = self.hc
+        if grads is None:
+            grads = tuple(torch.empty_like(qp) for _ in range(3))
+        dq, dk, dv = grads
+        ws = torch.empty(P.prism_workspace_size(P.OP_ATTN_BWD, self.N, hc, self.d, self.nb, sel.cap),
+                         dtype=torch.uint8, device=self.device)
+        q, k, v, o, do, gq, gk, gv = (x[:, h0:h0 + hc] for x in (qp, kp, vp, op, dop, dq, dk, dv))
+        P.prism_sparse_attn_bwd(q, k, v, o, do, lse, gq, gk, gv, self.N, hc, self.d, q.stride(0), q.stride(1),
+                                self.block_offsets, self.nb, sel.offsets, sel.idx, sel.cap, self.scale, ws)
+        return dq, dk, dv
+
+    # -------------------------------------------------------------- whole step
+    def step(self, q, k, v, a, do=None):
+        """Shapes, permutation, selection, forward (and backward when `do` is
+        given), inverse permutation.  Returns raster-order results."""
+        self.shapes(v, a)
+        qp, kp, vp = self.permute(q), self.permute(k), self.permute(v)
+        dop = self.permute(do) if do is not None else None
+        op = torch.empty_like(qp)
+        grads = tuple(torch.empty_like(qp) for _ in range(3)) if do is not None else None
+        lses, sels = [], []
+        for h0 in range(0, self.heads, self.hc):
+            sel = self.select(qp, kp, h0)
+            _, lse = self.forward(qp, kp, vp, sel, op=op, h0=h0)
+            if do is not None:
+                self.backward(qp, kp, vp, op, dop, lse, sel, grads=grads, h0=h0)
+            lses.append(lse)
+            sels.append(sel)
+        out = {"o": self.permute(op, inverse=True), "lse_block_major": torch.cat(lses, 0), "selections": sels}
+        if do is not None:
+            out["dq"], out["dk"], out["dv"] = (self.permute(g, inverse=True) for g in grads)
+        return out

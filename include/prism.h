@@ -1,0 +1,225 @@
+/*
+ * prism.h - C ABI of the MI355X (gfx950) Prism dynamic block-sparse attention path.
+ *
+ * The path (Prism reading guide, xyznot.com paper 2610.05416, "Phương pháp" §1-§3;
+ * news article at ailog.hnlab.kr, "핵심 내용", three steps):
+ *   1. split the T x H x W latent token grid into 8 x 8 x 8 macro-zones;
+ *   2. per zone, the directional video variance of mean-pooled V and the audio
+ *      terms give the variation indicator g_d; a density gives the block volume
+ *      B in {64, 128, 256} and the log2 optimum picks the nearest of 16 shapes;
+ *   3. tokens are permuted into block-major order (each block contiguous);
+ *   4. Q and K blocks are mean-pooled and scored; per query block a hybrid
+ *      Top-k U Top-p set of key blocks is selected;
+ *   5. exact attention runs over the selected key blocks only (forward and
+ *      backward).
+ *
+ * Conventions shared by every call:
+ *   - Every pointer argument is device memory owned by the caller unless the
+ *     argument says "host".  The library allocates nothing, frees nothing and
+ *     keeps no pointer after a call returns; scratch comes from the caller's
+ *     workspace `ws` of at least prism_workspace_size(...) bytes (16-byte aligned).
+ *   - Every call is asynchronous on `stream` (0 = the null stream) unless it
+ *     says it synchronises.  The returned status comes from host-side checks
+ *     made before anything is launched: on any status other than PRISM_OK
+ *     nothing was launched and no output was touched.  A failing launch
+ *     returns PRISM_E_HIP (outputs then undefined).
+ *   - No C++ exception crosses this boundary.  prism_last_error() returns a
+ *     message for the calling thread's last failure.
+ *   - The library holds no mutable global state; calls on different streams
+ *     may run concurrently as long as their buffers do not overlap.
+ *   - Token tensors are [N, heads, d] with element strides `ld` (between tokens)
+ *     and `hs` (between heads), d contiguous; every tensor of one call has the
+ *     same dtype, ld and hs.  Supported d: 64 and 128.  Vector access needs the
+ *     pointers 16-byte aligned and ld, hs multiples of 8 elements (bf16) or 4
+ *     (f32).
+ *   - Block-major order: zones in raster order (m = (zt*nH + zh)*nW + zw, 512
+ *     positions each); inside a zone, its blocks in raster order over the block
+ *     grid; inside a block, tokens in raster (t, h, w) order.  Raster token
+ *     index n = (t*H + h)*W + w.
+ */
+#ifndef PRISM_H
+#define PRISM_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    PRISM_OK = 0,
+    PRISM_E_ARG = 1,          /* null pointer, negative or inconsistent size, bad k/p */
+    PRISM_E_GRID = 2,         /* T, H or W not a positive multiple of 8 */
+    PRISM_E_DTYPE = 3,        /* unknown dtype */
+    PRISM_E_UNSUPPORTED = 4,  /* d not in {64, 128}, misaligned pointer or stride */
+    PRISM_E_WORKSPACE = 5,    /* ws NULL or smaller than prism_workspace_size() */
+    PRISM_E_HIP = 6           /* a HIP runtime call or launch failed */
+} prism_status;
+
+typedef enum { PRISM_F32 = 0, PRISM_BF16 = 1 } prism_dtype;
+
+/* Thresholds of the volume rule and the indicator's epsilon.  The reading guide
+ * ("Phương pháp" §2) gives tau128 = 0.5 and tau256 = 0.25; §1 adds an epsilon
+ * without a value (1e-6 is the value used by the tests and benchmark). */
+typedef struct { double tau128, tau256, eps; } prism_shape_params;
+
+/* operation codes for prism_workspace_size */
+enum { PRISM_OP_ZONE_SHAPES = 0, PRISM_OP_SELECT = 1, PRISM_OP_ATTN_FWD = 2, PRISM_OP_ATTN_BWD = 3 };
+
+/* Per-zone record written by prism_zone_shapes when `zone_stats` is not NULL:
+ * 16 doubles per zone. */
+enum {
+    PRISM_ZS_SIGMA2_V = 0,    /* [3] directional video variance, axes T, H, W ("Phương pháp" §1, first display) */
+    PRISM_ZS_R = 3,           /* [3] its ratio r_{v,d} (1/3 each for a constant zone) */
+    PRISM_ZS_ABAR = 6,        /* audio coupling: zone mean of a */
+    PRISM_ZS_SIGMA2_A = 7,    /* [3] variance of a's axis slice means */
+    PRISM_ZS_VHAT = 10,       /* [3] its ratio (1/3 each when a is constant on the zone) */
+    PRISM_ZS_RHO = 13,        /* density: max(S_v / max over zones of S_v, abar) */
+    PRISM_ZS_SV = 14,         /* S_v = sum of the three video variances */
+    PRISM_ZS_B = 15,          /* block volume 64, 128 or 256 */
+    PRISM_ZS_STRIDE = 16
+};
+
+/*
+ * prism_zone_shapes - macro-zones, variation indicator, block volume and shape,
+ * block layout ("Phương pháp" §1 and §2 of the reading guide; "Các ý tưởng cốt
+ * lõi" for the 8x8x8 zones and the 16 candidate shapes).
+ *
+ *   T, H, W        grid sides (positive multiples of 8); N = T*H*W, nZ = N/512
+ *   v, vdt, C, v_ld  value tensor in raster order: C channels per token
+ *                  (all heads: one shape per zone, shared by every head),
+ *                  token stride v_ld elements (>= C)
+ *   a_map          [N] fp32 audio-to-video norm map in raster order, values in [0, 1]
+ *   prm            host pointer to thresholds and epsilon (NULL: 0.5, 0.25, 1e-6)
+ *   zone_shape     out [nZ] uint8: index into the candidate table of
+ *                  prism_candidate_shapes()
+ *   block_offsets  out [8*nZ + 1] int32: token offset of each block in
+ *                  block-major order; entries 0..NB are valid, entry NB = N
+ *   nb_dev         out device int32: NB, the number of blocks
+ *   nb_host        optional host int32*: when not NULL the call synchronises
+ *                  `stream` and stores NB there
+ *   zone_stats     optional out [nZ * PRISM_ZS_STRIDE] doubles (layout above)
+ *
+ * Statistics accumulate in float64.  Decisions: rho < tau256 -> 256, else
+ * rho < tau128 -> 128, else 64; the shape is the candidate of that volume
+ * nearest to l* (third display of the reading guide's method) in squared log2
+ * distance, distances within 1e-9 of the minimum counting as ties and going
+ * to the lowest candidate index.
+ */
+prism_status prism_zone_shapes(int32_t T, int32_t H, int32_t W,
+                               const void* v, prism_dtype vdt, int64_t C, int64_t v_ld,
+                               const float* a_map, const prism_shape_params* prm,
+                               uint8_t* zone_shape, int32_t* block_offsets, int32_t* nb_dev,
+                               int32_t* nb_host, double* zone_stats,
+                               void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * prism_block_permute - gather rows from raster into block-major order
+ * (inverse = 0: y[p] = x[pi(p)]) or scatter them back (inverse = 1:
+ * y[pi(p)] = x[p]), pi being the block-major order defined above for the zone
+ * shapes of prism_zone_shapes.  The pages reorganise the token sequence into
+ * zone-shaped blocks (news article, "핵심 내용" steps 1-2) and pool and attend
+ * whole blocks (reading guide §3); they give no order, so the order above is
+ * this library's reading.
+ *
+ *   row_elems      elements moved per token (e.g. heads*d)
+ *   x_ld, y_ld     token strides of x and y in elements (>= row_elems)
+ *   x, y           must not overlap
+ */
+prism_status prism_block_permute(int32_t T, int32_t H, int32_t W, const uint8_t* zone_shape,
+                                 const void* x, void* y, prism_dtype dt, int64_t row_elems,
+                                 int64_t x_ld, int64_t y_ld, int32_t inverse, hipStream_t stream);
+
+/*
+ * prism_select - pooled block scores and hybrid Top-k U Top-p key-block
+ * selection (reading guide, "Phương pháp" §3, the selected-set display).
+ *
+ *   q, k           block-major [N, heads, d] (output of prism_block_permute)
+ *   block_offsets, nb  as written by prism_zone_shapes (nb on the host)
+ *   top_k          k >= 0;  top_p  0 <= p <= 1
+ *   scale          score scale (1/sqrt(d) in the tests), a float32 value
+ *   sel_offsets    out [heads * (nb + 1)] int32: row i of head h holds
+ *                  sel_idx[h*cap + sel_offsets[h*(nb+1) + i] ...
+ *                  h*cap + sel_offsets[h*(nb+1) + i + 1] - 1]
+ *   sel_idx        out [heads * cap] int32 key-block indices, ascending per row
+ *   cap            capacity per head (nb*nb never truncates)
+ *   sel_total      out device [heads] int64: entries head h needed; a value
+ *                  above cap means that head's list was truncated at cap
+ *                  (its CSR must then not be used)
+ *   logits         optional out [heads * nb * nb] fp32: the pooled scores
+ *
+ * Each block is pooled by its float64 mean; its score with key block j is
+ * scale * (Q_bar_i . K_bar_j) evaluated in float64 and rounded once to fp32.
+ * Per row the blocks are ranked by score (ties: lower index first); the row
+ * keeps the first max(k, n_p) of them (at most nb), n_p being the shortest
+ * prefix whose softmax mass, summed in float64, reaches p.
+ */
+prism_status prism_select(const void* q, const void* k, prism_dtype dt,
+                          int64_t N, int32_t heads, int32_t d, int64_t ld, int64_t hs,
+                          const int32_t* block_offsets, int32_t nb,
+                          int32_t top_k, double top_p, float scale,
+                          int32_t* sel_offsets, int32_t* sel_idx, int64_t cap,
+                          int64_t* sel_total, float* logits,
+                          void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * prism_sparse_attn_fwd - exact attention restricted to the selected key blocks
+ * (reading guide, "Phương pháp" §3: online-softmax attention over S_i only).
+ * Non-causal, no dropout, no bias.
+ *
+ *   q, k, v        block-major [N, heads, d]
+ *   o              out block-major [N, heads, d], same dtype/strides
+ *   lse            out [heads, N] fp32 natural-log log-sum-exp of the scaled scores
+ *   sel_offsets, sel_idx, cap  the CSR written by prism_select
+ * bf16 runs on bf16 MFMA with fp32 accumulation and an fp32 online softmax;
+ * f32 runs on fp32 vector arithmetic.
+ */
+prism_status prism_sparse_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                                   prism_dtype dt, int64_t N, int32_t heads, int32_t d,
+                                   int64_t ld, int64_t hs,
+                                   const int32_t* block_offsets, int32_t nb,
+                                   const int32_t* sel_offsets, const int32_t* sel_idx, int64_t cap,
+                                   float scale, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * prism_sparse_attn_bwd - gradient of prism_sparse_attn_fwd with respect to
+ * q, k and v, the selection being a constant.  The pages train with the
+ * method but do not describe its backward; this is the chain rule of the
+ * masked softmax: P = exp(scale*q.k - lse), dV = P^T dO, dP = dO V^T,
+ * dS = P (dP - rowsum(dO * O)), dQ = scale dS K, dK = scale dS^T Q.
+ *
+ *   o, dout        forward output and upstream gradient (block-major)
+ *   lse            forward log-sum-exp
+ *   dq, dk, dv     out block-major, same dtype/strides (fully overwritten)
+ * Deterministic: every output element is accumulated in a fixed order.
+ */
+prism_status prism_sparse_attn_bwd(const void* q, const void* k, const void* v, const void* o,
+                                   const void* dout, const float* lse,
+                                   void* dq, void* dk, void* dv,
+                                   prism_dtype dt, int64_t N, int32_t heads, int32_t d,
+                                   int64_t ld, int64_t hs,
+                                   const int32_t* block_offsets, int32_t nb,
+                                   const int32_t* sel_offsets, const int32_t* sel_idx, int64_t cap,
+                                   float scale, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Workspace bytes for one call.  ZONE_SHAPES: N = T*H*W and d = C (heads, nb,
+ * cap ignored).  SELECT, ATTN_FWD, ATTN_BWD: the call's N, heads, d, nb, cap. */
+size_t prism_workspace_size(int32_t op, int64_t N, int32_t heads, int32_t d, int32_t nb, int64_t cap);
+
+/* Static description of a status code. */
+const char* prism_status_string(prism_status s);
+
+/* Message of the calling thread's last failing call ("" if none). */
+const char* prism_last_error(void);
+
+/* The 16 candidate shapes (b_T, b_H, b_W) in the index order used by
+ * zone_shape: by volume (64, 128, 256), then lexicographically.  Host memory. */
+void prism_candidate_shapes(int32_t out[16][3]);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PRISM_H */

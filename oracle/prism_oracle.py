@@ -416,15 +416,17 @@ def attention(Qp, Kp, Vp, offs, csr_offs, csr_idx, head, scale, dOp=None):
     return dict(O=O, lse=lse, dQ=dQ, dK=dK, dV=dV)
 
 
-def key_block_grads(Qp, Kp, Vp, dOp, offs, csr_offs, csr_idx, j, head, scale):
+def key_block_grads(Qp, Kp, Vp, dOp, offs, csr_offs, csr_idx, j, head, scale, rows=None):
     """dK and dV rows of key block j alone: the sum over every query block
-    whose selected set holds j (used to check sampled key blocks)."""
+    whose selected set holds j (used to check sampled key blocks).  `rows`
+    optionally limits the scan to candidate query blocks (each is still
+    checked for membership)."""
     d = Qp.shape[2]
     B = offs[j + 1] - offs[j]
     dK = np.zeros((B, d))
     dV = np.zeros((B, d))
     NB = len(offs) - 1
-    for i in range(NB):
+    for i in (range(NB) if rows is None else sorted(int(r) for r in rows)):
         sel = csr_idx[csr_offs[i]:csr_offs[i + 1]]
         if j not in set(int(x) for x in sel):
             continue

@@ -1,0 +1,166 @@
+"""The C-ABI boundary on the CPU: the library loads, exports every declared
+entry point, and rejects bad arguments with the right status before any
+launch.  No call here reaches a kernel."""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "prism.h")
+LIB = os.path.join(ROOT, "dynamic_block_sparse_amd", "lib", "libprism.so")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libprism.so not built")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(prism_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = _declared()
+    assert set(names) >= {"prism_zone_shapes", "prism_block_permute", "prism_select", "prism_sparse_attn_fwd",
+                          "prism_sparse_attn_bwd", "prism_workspace_size", "prism_status_string",
+                          "prism_last_error", "prism_candidate_shapes"}
+    lib = ctypes.CDLL(LIB)
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (prism_\w+)", out))
+    assert set(names) <= exported
+
+
+def test_binding_names_match_the_header():
+    from dynamic_block_sparse_amd import prism as P
+    assert sorted(P.EXPORTS) == _declared()
+    for n in P.EXPORTS:
+        assert callable(getattr(P, n))
+
+
+def test_candidate_table_matches_the_oracle():
+    from dynamic_block_sparse_amd import prism as P
+    from oracle import prism_oracle as orc
+    assert P.prism_candidate_shapes() == orc.candidate_shapes()
+
+
+def test_status_strings():
+    from dynamic_block_sparse_amd import prism as P
+    for s in range(7):
+        assert P.prism_status_string(s) and P.prism_status_string(s) != "unknown status"
+
+
+# ---------------------------------------------------------------- argument checks
+# Fake device addresses: non-null and 256-byte aligned, never dereferenced
+# because every call below fails its host-side checks first.
+
+A = 0x10000
+B = 0x20000
+Cc = 0x30000
+
+
+def _lib():
+    lib = ctypes.CDLL(LIB)
+    from dynamic_block_sparse_amd import prism as P   # sets argtypes on its own handle
+    return P._lib, P
+
+
+def test_zone_shapes_rejects_bad_grids_and_args():
+    lib, P = _lib()
+    ws_need = P.prism_workspace_size(P.OP_ZONE_SHAPES, 8 * 16 * 16, 1, 64, 0, 0)
+    assert ws_need > 0
+    call = lambda T=8, H=16, W=16, v=A, dt=0, C=64, ld=64, a=B, zs=Cc, bo=A, nb=B, ws=Cc, wsb=ws_need: \
+        lib.prism_zone_shapes(T, H, W, v, dt, C, ld, a, None, zs, bo, nb, None, None, ws, wsb, None)
+    assert call(T=12) == 2
+    assert call(H=0) == 2
+    assert call(W=-8) == 2
+    assert call(dt=7) == 3
+    assert call(v=None) == 1
+    assert call(a=None) == 1
+    assert call(C=0) == 1
+    assert call(ld=32) == 1
+    assert call(ws=None) == 5
+    assert call(wsb=ws_need - 1) == 5
+    assert "workspace" in P.prism_last_error()
+
+
+def test_zone_shapes_rejects_bad_thresholds():
+    lib, P = _lib()
+    ws_need = P.prism_workspace_size(P.OP_ZONE_SHAPES, 512, 1, 64, 0, 0)
+    bad = P.PrismShapeParams(0.2, 0.5, 1e-6)      # tau256 above tau128
+    st = lib.prism_zone_shapes(8, 8, 8, A, 0, 64, 64, B, ctypes.byref(bad), Cc, A, B, None, None, Cc, ws_need, None)
+    assert st == 1
+    bad = P.PrismShapeParams(0.5, 0.25, 0.0)      # eps must be positive
+    st = lib.prism_zone_shapes(8, 8, 8, A, 0, 64, 64, B, ctypes.byref(bad), Cc, A, B, None, None, Cc, ws_need, None)
+    assert st == 1
+
+
+def test_block_permute_rejects():
+    lib, P = _lib()
+    f = lambda T=8, zs=A, x=B, y=Cc, dt=1, re_=128, xl=128, yl=128, inv=0: \
+        lib.prism_block_permute(T, 8, 8, zs, x, y, dt, re_, xl, yl, inv, None)
+    assert f(T=4) == 2
+    assert f(zs=None) == 1
+    assert f(dt=5) == 3
+    assert f(re_=0) == 1
+    assert f(xl=64) == 1
+    assert f(inv=2) == 1
+    assert f(x=B, y=B + 64) == 1                   # overlapping buffers
+    assert "overlap" in P.prism_last_error()
+
+
+def test_select_rejects():
+    lib, P = _lib()
+    N, heads, d, nb = 2048, 1, 64, 24
+    cap = nb * nb
+    need = P.prism_workspace_size(P.OP_SELECT, N, heads, d, nb, cap)
+    f = lambda q=A, dt=0, N=N, heads=heads, d=d, ld=64, hs=64, nb=nb, k=4, p=0.9, cap=cap, ws=Cc, wsb=need: \
+        lib.prism_select(q, B, dt, N, heads, d, ld, hs, Cc, nb, k, p, 0.125, A, B, cap, Cc, None, ws, wsb, None)
+    assert f(dt=3) == 3
+    assert f(N=100) == 1
+    assert f(heads=0) == 1
+    assert f(d=96) == 4
+    assert f(ld=60) == 1
+    assert f(ld=66) == 4                           # not a multiple of 4 fp32 elements
+    assert f(nb=0) == 1
+    assert f(nb=N // 64 + 1) == 1
+    assert f(k=-1) == 1
+    assert f(p=1.5) == 1
+    assert f(p=float("nan")) == 1
+    assert f(cap=0) == 1
+    assert f(q=None) == 1
+    assert f(ws=None) == 5
+    assert f(wsb=need - 1) == 5
+
+
+def test_attention_rejects():
+    lib, P = _lib()
+    N, heads, d, nb = 2048, 2, 128, 24
+    cap = nb * nb
+    fwd = lambda q=A, dt=1, d=d, o=Cc: lib.prism_sparse_attn_fwd(q, B, Cc, o, A, dt, N, heads, d, 256, 128, B, nb, Cc,
+                                                                 A, cap, 0.088, None, 0, None)
+    assert fwd(dt=2) == 3
+    assert fwd(d=32) == 4
+    assert fwd(q=None) == 1
+    assert fwd(o=Cc + 8) == 4                      # misaligned
+    need = P.prism_workspace_size(P.OP_ATTN_BWD, N, heads, d, nb, cap)
+    assert need > 0
+    bwd = lambda ws=A, wsb=need, dq=A: lib.prism_sparse_attn_bwd(A, B, Cc, A, B, Cc, dq, B, Cc, 1, N, heads, d, 256,
+                                                                 128, A, nb, B, Cc, cap, 0.088, ws, wsb, None)
+    assert bwd(ws=None) == 5
+    assert bwd(wsb=need - 16) == 5
+    assert bwd(dq=None) == 1
+
+
+def test_workspace_sizes_grow_with_the_problem():
+    from dynamic_block_sparse_amd import prism as P
+    a = P.prism_workspace_size(P.OP_SELECT, 4096, 1, 64, 16, 256)
+    b = P.prism_workspace_size(P.OP_SELECT, 4096, 2, 64, 16, 256)
+    c = P.prism_workspace_size(P.OP_SELECT, 4096, 1, 64, 32, 1024)
+    assert 0 < a < b and a < c
+    assert P.prism_workspace_size(P.OP_ATTN_FWD, 4096, 1, 64, 16, 256) == 0
+    assert P.prism_workspace_size(P.OP_ZONE_SHAPES, 512, 1, 3072, 0, 0) >= 16 * 8

@@ -1,0 +1,296 @@
+"""Parity of the HIP path (through the C ABI) with the float64 oracle.
+
+Small grids are compared element by element in full; the named workloads
+(720p, 1080p, 2K, long) are compared at full size, in the launch
+configuration the benchmark uses, on seeded samples of heads, rows and
+blocks.  Every expected value comes from the oracle run on the generator's
+inputs; nothing from the HIP path is fed to the oracle.
+
+Bars: zone volumes, shapes, block offsets, permutations and selected sets
+bit-exact (decisions the oracle marks as lying on a boundary are reported
+and excluded; none are expected); pooled scores equal to the float32 rounding
+of the float64 definition; attention outputs and gradients within max-abs
+2e-2 and mean-abs 2e-3 for bf16 inputs and max-abs 1e-4 for fp32 inputs.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import prism_oracle as orc
+from workloads.synth import CONFIGS, custom, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"bf16": (2e-2, 2e-3), "f32": (1e-4, 1e-4)}
+
+
+def _np(t):
+    """Exact host copy as float32 (bf16 -> f32 is exact) or float64 for fp64."""
+    if t.dtype == torch.float64:
+        return t.detach().cpu().numpy()
+    return t.detach().float().cpu().numpy()
+
+
+def _path(cfg, heads=None, hc=None):
+    from dynamic_block_sparse_amd.path import PrismPath
+    return PrismPath(cfg.T, cfg.H, cfg.W, heads or cfg.heads, cfg.d, cfg.top_k, cfg.top_p,
+                     float(np.float32(1.0 / math.sqrt(cfg.d))), head_chunk=hc)
+
+
+def _assert_close(got, want, dtype, what, grad=False):
+    """O is a convex combination of V rows, so its bar is absolute.  Gradients
+    are unbounded and stored in the input dtype: a bf16 value of magnitude m
+    carries a rounding error up to 2^-9 m on its own, so their bar is the same
+    one scaled by max(1, max |reference|) (max-abs) and max(1, mean |reference|)
+    (mean-abs)."""
+    mx, mean = TOL[dtype]
+    got = np.asarray(got, dtype=np.float64)
+    want = np.asarray(want, dtype=np.float64)
+    err = np.abs(got - want)
+    if grad:
+        mx *= max(1.0, float(np.abs(want).max()))
+        mean *= max(1.0, float(np.abs(want).mean()))
+    print(f"{what}: max-abs {err.max():.3e} (bar {mx:.2e}) mean-abs {err.mean():.3e} (bar {mean:.2e}) "
+          f"max|ref| {np.abs(want).max():.3e}", flush=True)
+    assert err.max() <= mx, f"{what}: max-abs {err.max()} > {mx}"
+    assert err.mean() <= mean, f"{what}: mean-abs {err.mean()} > {mean}"
+
+
+SMALL = [
+    custom("s_f32_d64", T=8, H=16, W=16, heads=1, d=64, dtype="f32", top_k=4, top_p=0.9, seed=11),
+    custom("s_bf16_d128", T=16, H=16, W=24, heads=2, d=128, dtype="bf16", top_k=3, top_p=0.8,
+           kinds=(("smooth", 0.5), ("static", 0.25), ("fast1", 0.25)),
+           sigma={"smooth": 0.3, "static": 1e-3, "fast1": 0.1}, n_blobs=2, blob_std=(3.0, 4.0, 4.0), seed=12),
+    custom("s_bf16_d64", T=8, H=24, W=16, heads=3, d=64, dtype="bf16", top_k=2, top_p=0.95,
+           kinds=(("aniso", 0.5), ("noisy", 0.5)), sigma={"aniso": 0.1, "noisy": 1.0}, beta=3.0, seed=13),
+    custom("s_f32_d128", T=16, H=8, W=16, heads=2, d=128, dtype="f32", top_k=1, top_p=0.5, beta=1.0, seed=14),
+    custom("s_one_zone_k0_p0", T=8, H=8, W=8, heads=1, d=64, dtype="bf16", top_k=0, top_p=0.0, seed=15),
+    custom("s_dense", T=8, H=16, W=8, heads=2, d=64, dtype="bf16", top_k=10 ** 6, top_p=0.5, seed=16),
+    custom("s_p1", T=8, H=8, W=16, heads=1, d=128, dtype="bf16", top_k=1, top_p=1.0, seed=17),
+]
+
+
+def _oracle_full(cfg, x):
+    """Oracle end to end on host copies of the generator's tensors."""
+    T, H, W = cfg.T, cfg.H, cfg.W
+    N = cfg.N
+    V = _np(x["v"]).reshape(N, -1)
+    zs = orc.zone_shapes(V, _np(x["a"]), T, H, W)
+    pi = orc.permutation(T, H, W, zs["shape"])
+    offs = zs["block_offsets"]
+    sc = float(np.float32(1.0 / math.sqrt(cfg.d)))
+    res = {"zs": zs, "pi": pi, "heads": []}
+    for h in range(cfg.heads):
+        Qp, Kp, Vp = (orc.to_block_major(_np(x[n][:, h:h + 1, :]), pi) for n in ("q", "k", "v"))
+        dOp = orc.to_block_major(_np(x["do"][:, h:h + 1, :]), pi) if "do" in x else None
+        L = orc.block_logits(orc.pool_blocks(Qp, offs, 0), orc.pool_blocks(Kp, offs, 0), sc)
+        co, ci, flags = orc.select(L, cfg.top_k, cfg.top_p)
+        att = orc.attention(Qp, Kp, Vp, offs, co, ci, 0, sc, dOp=dOp)
+        res["heads"].append(dict(L=L, co=co, ci=ci, flags=flags, att=att))
+    return res
+
+
+def _csr_rows(offsets, idx, nb):
+    return [idx[offsets[i]:offsets[i + 1]] for i in range(nb)]
+
+
+@pytest.mark.parametrize("cfg", SMALL, ids=lambda c: c.name)
+def test_small_end_to_end(cfg):
+    print(f"case {cfg.name}", flush=True)
+    x = make_inputs(cfg, device="cuda")
+    path = _path(cfg)
+    out = path.step(x["q"], x["k"], x["v"], x["a"], x.get("do"))
+    torch.cuda.synchronize()
+    ref = _oracle_full(cfg, x)
+    zs = ref["zs"]
+    # zone decisions and layout
+    assert not zs["near_tie"].any()
+    assert path.nb == zs["NB"]
+    np.testing.assert_array_equal(path.zone_shape.cpu().numpy(), zs["shape"])
+    np.testing.assert_array_equal(path.block_offsets[:path.nb + 1].cpu().numpy(), zs["block_offsets"])
+    rec = path.zone_stats.cpu().numpy().reshape(-1, 16)
+    np.testing.assert_allclose(rec[:, 0:3], zs["sigma2_v"], rtol=1e-12, atol=1e-300)
+    np.testing.assert_allclose(rec[:, 3:6], zs["r"], rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(rec[:, 6], zs["abar"], rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(rec[:, 7:10], zs["sigma2_a"], rtol=1e-11, atol=1e-17)
+    np.testing.assert_allclose(rec[:, 10:13], zs["vhat"], rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(rec[:, 13], zs["rho"], rtol=1e-12, atol=1e-15)
+    np.testing.assert_array_equal(rec[:, 15], zs["B"])
+    # selection (one head chunk = all heads)
+    sel = out["selections"][0]
+    offs_g = sel.offsets.cpu().numpy()
+    idx_g = sel.idx.cpu().numpy()
+    assert (sel.total.cpu().numpy() <= sel.cap).all()
+    for h, hr in enumerate(ref["heads"]):
+        rows_g = _csr_rows(offs_g[h], idx_g[h], path.nb)
+        for i in range(path.nb):
+            if hr["flags"][i]:
+                continue
+            np.testing.assert_array_equal(rows_g[i], hr["ci"][hr["co"][i]:hr["co"][i + 1]], err_msg=f"head {h} row {i}")
+    # attention, raster order
+    for h, hr in enumerate(ref["heads"]):
+        att = hr["att"]
+        _assert_close(_np(out["o"][:, h, :]), orc.to_raster(att["O"], ref["pi"]), cfg.dtype, f"O h{h}")
+        lse_g = out["lse_block_major"][h].cpu().numpy()
+        np.testing.assert_allclose(lse_g, att["lse"], atol=1e-4 if cfg.dtype == "f32" else 2e-3)
+        if "do" in x:
+            for g, name in (("dq", "dQ"), ("dk", "dK"), ("dv", "dV")):
+                _assert_close(_np(out[g][:, h, :]), orc.to_raster(att[name], ref["pi"]), cfg.dtype, f"{name} h{h}",
+                              grad=True)
+
+
+def test_small_selection_logits_are_the_rounded_float64_scores():
+    cfg = SMALL[1]
+    x = make_inputs(cfg, device="cuda")
+    path = _path(cfg)
+    path.shapes(x["v"], x["a"])
+    qp, kp = path.permute(x["q"]), path.permute(x["k"])
+    sel = path.select(qp, kp, want_logits=True)
+    torch.cuda.synchronize()
+    ref = _oracle_full(cfg, x)
+    L = sel.logits.cpu().numpy()
+    for h, hr in enumerate(ref["heads"]):
+        diff = L[h] != hr["L"]
+        assert diff.mean() < 1e-4
+        if diff.any():
+            ulp = np.spacing(np.abs(hr["L"][diff]).astype(np.float32))
+            assert np.all(np.abs(L[h][diff] - hr["L"][diff]) <= ulp)
+
+
+def test_small_determinism():
+    cfg = SMALL[2]
+    x = make_inputs(cfg, device="cuda")
+    x["do"] = torch.randn_like(x["q"], dtype=torch.float32).to(x["q"].dtype)
+    outs = []
+    for _ in range(2):
+        path = _path(cfg)
+        o = path.step(x["q"], x["k"], x["v"], x["a"], x["do"])
+        torch.cuda.synchronize()
+        sel = o["selections"][0]
+        valid = torch.cat([sel.idx[h, :int(sel.total[h])] for h in range(cfg.heads)])
+        outs.append((path.zone_stats.clone(), sel.offsets.clone(), valid, o["o"], o["dq"], o["dk"], o["dv"]))
+    for a, b in zip(*outs):
+        assert torch.equal(a.view(torch.uint8) if a.dtype != torch.int32 else a,
+                           b.view(torch.uint8) if b.dtype != torch.int32 else b)
+
+
+def test_permutation_round_trip_with_strided_rows():
+    cfg = SMALL[1]
+    x = make_inputs(cfg, device="cuda")
+    path = _path(cfg)
+    path.shapes(x["v"], x["a"])
+    wide = torch.zeros((cfg.N, cfg.heads + 1, cfg.d), dtype=x["q"].dtype, device="cuda")
+    wide[:, :cfg.heads] = x["q"]
+    view = wide[:, :cfg.heads]                       # token stride (heads+1)*d
+    yp = path.permute(view)
+    back = path.permute(yp, inverse=True)
+    assert torch.equal(back, x["q"])
+    pi = orc.permutation(cfg.T, cfg.H, cfg.W, path.zone_shape.cpu().numpy())
+    np.testing.assert_array_equal(_np(yp), _np(x["q"])[pi])
+
+
+# ---------------------------------------------------------------- named workloads at full size
+
+FULL = ["720p", "1080p", "2k", "long"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_sampled(name):
+    cfg = CONFIGS[name]
+    print(f"case {name}: generating", flush=True)
+    rng = np.random.default_rng(1234)
+    if cfg.heads_sequential:
+        heads = sorted(rng.choice(cfg.heads, size=2, replace=False).tolist())
+        hc = 1
+    else:
+        heads = None
+        hc = None
+    x = make_inputs(cfg, device="cuda", tensors=("v",))
+    xs = make_inputs(cfg, device="cuda", heads=heads, tensors=("q", "k", "do")) if heads else \
+        make_inputs(cfg, device="cuda", tensors=("q", "k", "do"))
+    nh = len(heads) if heads else cfg.heads
+    v_att = x["v"][:, heads] if heads else x["v"]
+    path = _path(cfg, heads=nh, hc=hc)
+    path.shapes(x["v"], x["a"])
+    torch.cuda.synchronize()
+    print(f"case {name}: NB {path.nb}", flush=True)
+    # zone decisions against the oracle on all zones
+    zs = orc.zone_shapes(_np(x["v"]).reshape(cfg.N, -1), _np(x["a"]), cfg.T, cfg.H, cfg.W)
+    ok = ~zs["near_tie"]
+    print(f"case {name}: near-tie zones {int((~ok).sum())}", flush=True)
+    assert path.nb == zs["NB"] or (~ok).any()
+    np.testing.assert_array_equal(path.zone_shape.cpu().numpy()[ok], zs["shape"][ok])
+    if ok.all():
+        np.testing.assert_array_equal(path.block_offsets[:path.nb + 1].cpu().numpy(), zs["block_offsets"])
+    pi = orc.permutation(cfg.T, cfg.H, cfg.W, zs["shape"])
+    offs = zs["block_offsets"]
+    nb = zs["NB"]
+    # permutation: sampled rows of the permuted q
+    qp, kp, vp = path.permute(xs["q"]), path.permute(xs["k"]), path.permute(v_att)
+    dop = path.permute(xs["do"]) if cfg.backward else None
+    rows = rng.choice(cfg.N, size=4096, replace=False)
+    np.testing.assert_array_equal(_np(qp[torch.from_numpy(rows).cuda()]), _np(xs["q"][torch.from_numpy(pi[rows]).cuda()]))
+    sc = float(np.float32(1.0 / math.sqrt(cfg.d)))
+    check_heads = list(range(nh)) if heads else sorted(rng.choice(cfg.heads, size=2, replace=False).tolist())
+    op = torch.empty_like(qp)
+    grads = tuple(torch.empty_like(qp) for _ in range(3)) if cfg.backward else None
+    sels, lses = {}, {}
+    for h0 in range(0, nh, path.hc):
+        sel = path.select(qp, kp, h0, want_logits=True)
+        _, lse = path.forward(qp, kp, vp, sel, op=op, h0=h0)
+        if cfg.backward:
+            path.backward(qp, kp, vp, op, dop, lse, sel, grads=grads, h0=h0)
+        for hh in range(path.hc):
+            sels[h0 + hh] = (sel, hh)
+            lses[h0 + hh] = lse[hh]
+    torch.cuda.synchronize()
+    print(f"case {name}: GPU path done", flush=True)
+    for h in check_heads:
+        sel, hh = sels[h]
+        Qp, Kp, Vp = (orc.to_block_major(_np(t[:, h:h + 1, :]), pi) for t in (xs["q"], xs["k"], v_att))
+        L = orc.block_logits(orc.pool_blocks(Qp, offs, 0), orc.pool_blocks(Kp, offs, 0), sc)
+        Lg = sel.logits[hh].cpu().numpy()
+        mism = Lg != L
+        print(f"case {name} head {h}: logit mismatches {int(mism.sum())} of {L.size}", flush=True)
+        assert mism.mean() < 1e-6
+        co, ci, flags = orc.select(L, cfg.top_k, cfg.top_p)
+        bad_rows = set(np.nonzero(mism.any(axis=1))[0].tolist()) | set(np.nonzero(flags)[0].tolist())
+        og = sel.offsets[hh].cpu().numpy()
+        ig = sel.idx[hh, :og[-1]].cpu().numpy()
+        sizes = np.diff(co)
+        print(f"case {name} head {h}: mean |S_i| {sizes.mean():.1f} blocks ({sizes.mean() / nb:.4f} of NB), "
+              f"flagged rows {int(flags.sum())}", flush=True)
+        for i in range(nb):
+            if i in bad_rows:
+                continue
+            if not np.array_equal(ig[og[i]:og[i + 1]], ci[co[i]:co[i + 1]]):
+                raise AssertionError(f"{name} head {h} row {i}: selection differs")
+        # forward and dQ on sampled query blocks, dK/dV on sampled key blocks
+        qb = rng.choice(nb, size=min(64, nb), replace=False)
+        dOp = orc.to_block_major(_np(xs["do"][:, h:h + 1, :]), pi) if cfg.backward else None
+        Og = _np(op[:, h, :])
+        lg = lses[h].cpu().numpy()
+        errs = {"O": [], "dQ": [], "dK": [], "dV": []}
+        for i in qb:
+            s = ci[co[i]:co[i + 1]]
+            o_ref, lse_ref = orc.attn_fwd_block(Qp, Kp, Vp, offs, s, i, 0, sc)
+            errs["O"].append((Og[offs[i]:offs[i + 1]], o_ref))
+            np.testing.assert_allclose(lg[offs[i]:offs[i + 1]], lse_ref, atol=2e-3)
+            if cfg.backward:
+                dq_ref = orc.attn_bwd_block(Qp, Kp, Vp, dOp, offs, s, i, 0, sc)[0]
+                errs["dQ"].append((_np(grads[0][offs[i]:offs[i + 1], h, :]), dq_ref))
+        if cfg.backward:
+            kb = rng.choice(nb, size=min(32, nb), replace=False)
+            rows_of = np.repeat(np.arange(nb), np.diff(co))
+            for j in kb:
+                users = np.unique(rows_of[ci == j])
+                dk_ref, dv_ref = orc.key_block_grads(Qp, Kp, Vp, dOp, offs, co, ci, j, 0, sc, rows=users)
+                errs["dK"].append((_np(grads[1][offs[j]:offs[j + 1], h, :]), dk_ref))
+                errs["dV"].append((_np(grads[2][offs[j]:offs[j + 1], h, :]), dv_ref))
+        for k, pairs in errs.items():
+            if pairs:
+                got = np.concatenate([p[0] for p in pairs])
+                want = np.concatenate([p[1] for p in pairs])
+                _assert_close(got, want, cfg.dtype, f"{name} head {h} {k}", grad=(k != "O"))

@@ -15,7 +15,7 @@ Recipe (all parameters are builder choices unless marked as taken from the
 workload description):
   * Zones are 8x8x8 token cubes in raster order.  Each zone gets a kind:
       smooth  - frequency vector f (cycles/token per axis) log-uniform in
-                [1/64, 1/4] on every axis
+                [1/64, 1/16] on every axis
       static  - f = 0 (near-constant values)
       fast1   - f = 1/4 on one random axis, 0 on the others
       aniso   - 1/4, 1/16 and 0 on a random permutation of the axes
@@ -90,19 +90,19 @@ CONFIGS = {
     "720p": Config("720p", 32, 48, 80, 24, 128, "bf16", 8, 0.9, False,
                    kinds=(("smooth", 1.0),), sigma={"smooth": 1.0},
                    n_blobs=3, blob_cover=0.05, blob_std=None,
-                   a_background=0.0, beta=2.0, seed=1),
+                   a_background=0.0, beta=2.5, seed=1),
     # 1080p-like 32x72x120 grid: half static zones, half fast along one axis.
     "1080p": Config("1080p", 32, 72, 120, 24, 128, "bf16", 8, 0.95, True,
                     kinds=(("static", 0.5), ("fast1", 0.5)),
                     sigma={"static": 1e-3, "fast1": 0.1},
                     n_blobs=3, blob_cover=0.03, blob_std=None,
-                    a_background=0.0, beta=2.0, seed=2),
+                    a_background=0.0, beta=5.0, seed=2),
     # 2K-like 64x72x128 grid: thirds of static, anisotropic and noisy zones.
     "2k": Config("2k", 64, 72, 128, 24, 128, "bf16", 16, 0.95, True,
                  kinds=(("static", 1 / 3), ("aniso", 1 / 3), ("noisy", 1 / 3)),
                  sigma={"static": 1e-3, "aniso": 0.1, "noisy": 1.0},
                  n_blobs=5, blob_cover=0.04, blob_std=None,
-                 a_background=0.0, beta=2.0, seed=3),
+                 a_background=0.0, beta=6.0, seed=3),
     # long 2K clip 120x72x128: the 2K zone mix, small-norm (diffuse) queries,
     # uniform 0.05 audio background plus one strong blob; heads one at a time.
     "long": Config("long", 120, 72, 128, 24, 128, "bf16", 16, 0.95, True,
@@ -149,7 +149,7 @@ def _zone_params(cfg: Config):
     for m, kind in enumerate(kinds):
         if kind in ("smooth", "noisy"):
             u = torch.rand(3, generator=g, dtype=torch.float64)
-            freq[m] = torch.exp(math.log(1 / 64) + u * (math.log(1 / 4) - math.log(1 / 64)))
+            freq[m] = torch.exp(math.log(1 / 64) + u * (math.log(1 / 16) - math.log(1 / 64)))
         elif kind == "static":
             pass
         elif kind == "fast1":
