@@ -282,8 +282,14 @@ prism_status prism_sparse_attn_fwd(const void* q, const void* k, const void* v, 
     if (!std::isfinite(scale)) return fail(PRISM_E_ARG, "scale must be finite");
     (void)ws;
     (void)ws_bytes;
-    return hip_status(prism::launch_attn_fwd_simt(q, k, v, o, lse, dt == PRISM_BF16, N, heads, d, ld, hs,
-                                                  block_offsets, nb, sel_offsets, sel_idx, cap, scale, stream),
+    if (use_simt_attention(dt))
+        return hip_status(prism::launch_attn_fwd_simt(q, k, v, o, lse, dt == PRISM_BF16, N, heads, d, ld, hs,
+                                                      block_offsets, nb, sel_offsets, sel_idx, cap, scale, stream),
+                          "attention forward launch");
+    if (static_cast<int64_t>(N / 64) * heads > 0x7FFFFFFF)
+        return fail(PRISM_E_UNSUPPORTED, "too many query tiles for one launch");
+    return hip_status(prism::launch_attn_fwd_mfma(q, k, v, o, lse, N, heads, d, ld, hs, block_offsets, nb, sel_offsets,
+                                                  sel_idx, cap, scale, stream),
                       "attention forward launch");
 }
 
@@ -312,7 +318,14 @@ prism_status prism_sparse_attn_bwd(const void* q, const void* k, const void* v, 
                                                 w.scratch, stream),
                     "transposed selection launch");
     if (st != PRISM_OK) return st;
-    return hip_status(prism::launch_attn_bwd_simt(q, k, v, dout, lse, w.Dq, dq, dk, dv, bf16, N, heads, d, ld, hs,
+    if (use_simt_attention(dt))
+        return hip_status(prism::launch_attn_bwd_simt(q, k, v, dout, lse, w.Dq, dq, dk, dv, bf16, N, heads, d, ld, hs,
+                                                      block_offsets, nb, sel_offsets, sel_idx, w.tr_offsets, w.tr_idx,
+                                                      cap, scale, stream),
+                          "attention backward launch");
+    if (static_cast<int64_t>(N / 64) * heads > 0x7FFFFFFF)
+        return fail(PRISM_E_UNSUPPORTED, "too many tiles for one launch");
+    return hip_status(prism::launch_attn_bwd_mfma(q, k, v, dout, lse, w.Dq, dq, dk, dv, N, heads, d, ld, hs,
                                                   block_offsets, nb, sel_offsets, sel_idx, w.tr_offsets, w.tr_idx, cap,
                                                   scale, stream),
                       "attention backward launch");

@@ -345,7 +345,8 @@ tr_count_kernel(const int32_t* __restrict__ sel_offsets, const int32_t* __restri
     const int i = blockIdx.x, h = blockIdx.y;
     const int32_t* __restrict__ so = sel_offsets + static_cast<int64_t>(h) * (nb + 1);
     const int32_t* __restrict__ si = sel_idx + static_cast<int64_t>(h) * cap;
-    for (int e = so[i] + threadIdx.x; e < so[i + 1]; e += blockDim.x)
+    const int64_t e1 = min(static_cast<int64_t>(so[i + 1]), cap);   // a truncated list stops at cap
+    for (int64_t e = so[i] + threadIdx.x; e < e1; e += blockDim.x)
         atomicAdd(&tcount[static_cast<int64_t>(h) * nb + si[e]], 1);
 }
 
@@ -356,7 +357,8 @@ tr_fill_kernel(const int32_t* __restrict__ sel_offsets, const int32_t* __restric
     const int32_t* __restrict__ so = sel_offsets + static_cast<int64_t>(h) * (nb + 1);
     const int32_t* __restrict__ si = sel_idx + static_cast<int64_t>(h) * cap;
     const int32_t* __restrict__ to = tr_offsets + static_cast<int64_t>(h) * (nb + 1);
-    for (int e = so[i] + threadIdx.x; e < so[i + 1]; e += blockDim.x) {
+    const int64_t e1 = min(static_cast<int64_t>(so[i + 1]), cap);
+    for (int64_t e = so[i] + threadIdx.x; e < e1; e += blockDim.x) {
         const int j = si[e];
         const int slot = atomicAdd(&tcursor[static_cast<int64_t>(h) * nb + j], 1);
         tr_idx[static_cast<int64_t>(h) * cap + to[j] + slot] = i;

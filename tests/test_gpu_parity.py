@@ -268,11 +268,22 @@ def test_full_size_sampled(name):
             if not np.array_equal(ig[og[i]:og[i + 1]], ci[co[i]:co[i + 1]]):
                 raise AssertionError(f"{name} head {h} row {i}: selection differs")
         # forward and dQ on sampled query blocks, dK/dV on sampled key blocks
-        qb = rng.choice(nb, size=min(64, nb), replace=False)
         dOp = orc.to_block_major(_np(xs["do"][:, h:h + 1, :]), pi) if cfg.backward else None
         Og = _np(op[:, h, :])
         lg = lses[h].cpu().numpy()
         errs = {"O": [], "dQ": [], "dK": [], "dV": []}
+        # query blocks in seeded random order, up to 64, within an oracle cost budget
+        qcost = lambda i: float(offs[i + 1] - offs[i]) * float(sum(offs[j + 1] - offs[j] for j in ci[co[i]:co[i + 1]]))
+        qb, spent = [], 0.0
+        for i in rng.permutation(nb):
+            c = qcost(i)
+            if len(qb) >= 8 and spent + c > 2e9:
+                continue
+            qb.append(i)
+            spent += c
+            if len(qb) >= 64:
+                break
+        print(f"case {name} head {h}: checking {len(qb)} query blocks", flush=True)
         for i in qb:
             s = ci[co[i]:co[i + 1]]
             o_ref, lse_ref = orc.attn_fwd_block(Qp, Kp, Vp, offs, s, i, 0, sc)
@@ -282,13 +293,27 @@ def test_full_size_sampled(name):
                 dq_ref = orc.attn_bwd_block(Qp, Kp, Vp, dOp, offs, s, i, 0, sc)[0]
                 errs["dQ"].append((_np(grads[0][offs[i]:offs[i + 1], h, :]), dq_ref))
         if cfg.backward:
-            kb = rng.choice(nb, size=min(32, nb), replace=False)
+            # key blocks in seeded random order, up to 32 of them, while the
+            # oracle's cost (query rows x selected keys of every user row) stays
+            # within a budget; the kernel runs the same code for every block
             rows_of = np.repeat(np.arange(nb), np.diff(co))
-            for j in kb:
+            keys_of_row = np.array([float(sum(offs[j + 1] - offs[j] for j in ci[co[i]:co[i + 1]]))
+                                    for i in range(nb)])
+            cost_of_row = np.diff(offs) * keys_of_row
+            budget, spent, taken = 4e9, 0.0, 0
+            for j in rng.permutation(nb):
                 users = np.unique(rows_of[ci == j])
+                c = float(cost_of_row[users].sum())
+                if taken >= 4 and spent + c > budget:
+                    continue
                 dk_ref, dv_ref = orc.key_block_grads(Qp, Kp, Vp, dOp, offs, co, ci, j, 0, sc, rows=users)
                 errs["dK"].append((_np(grads[1][offs[j]:offs[j + 1], h, :]), dk_ref))
                 errs["dV"].append((_np(grads[2][offs[j]:offs[j + 1], h, :]), dv_ref))
+                spent += c
+                taken += 1
+                print(f"case {name} head {h}: key block {j} ({len(users)} query blocks) checked", flush=True)
+                if taken >= 32:
+                    break
         for k, pairs in errs.items():
             if pairs:
                 got = np.concatenate([p[0] for p in pairs])

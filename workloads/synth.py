@@ -109,7 +109,7 @@ CONFIGS = {
                    kinds=(("static", 1 / 3), ("aniso", 1 / 3), ("noisy", 1 / 3)),
                    sigma={"static": 1e-3, "aniso": 0.1, "noisy": 1.0},
                    n_blobs=1, blob_cover=0.02, blob_std=None,
-                   a_background=0.05, beta=0.35, heads_sequential=True, seed=4),
+                   a_background=0.05, beta=3.0, heads_sequential=True, seed=4),
 }
 
 
