@@ -54,9 +54,8 @@ def effective_flops(path, sels, d):
             tot = int(sel.total[h])
             idx = sel.idx[h, :tot].to(torch.int64)
             o = sel.offsets[h].to(torch.int64)
-            keys_per_row = torch.zeros(path.nb, dtype=torch.float64, device=B.device)
-            row_of = torch.repeat_interleave(torch.arange(path.nb, device=B.device), o[1:] - o[:-1])
-            keys_per_row.index_add_(0, row_of, B[idx])
+            cs = torch.cat([torch.zeros(1, dtype=torch.float64, device=B.device), torch.cumsum(B[idx], 0)])
+            keys_per_row = cs[o[1:]] - cs[o[:-1]]
             pairs += float((B * keys_per_row).sum())
             sizes.append((o[1:] - o[:-1]).double().mean().item())
     return 4.0 * pairs * d, 10.0 * pairs * d, float(np.mean(sizes))
@@ -122,11 +121,14 @@ def main():
                      head_chunk=1 if cfg.heads_sequential else None)
     nb = path.shapes(x["v"], x["a"])
     # buffers allocated once, outside the timed region
-    qp, kp, vp = (torch.empty_like(x["q"]) for _ in range(3))
-    dop = torch.empty_like(x["q"]) if cfg.backward else None
-    op = torch.empty_like(x["q"])
-    grads = tuple(torch.empty_like(x["q"]) for _ in range(3)) if cfg.backward else None
+    # block-major tensors live head-major ([heads, N, d] storage, [N, heads, d] views)
+    bm = lambda: path.block_major_like(x["q"])
+    qp, kp, vp = bm(), bm(), bm()
+    dop = bm() if cfg.backward else None
+    op = bm()
+    grads = (bm(), bm(), bm()) if cfg.backward else None
     outs = {n: torch.empty_like(x["q"]) for n in (("o", "dq", "dk", "dv") if cfg.backward else ("o",))}
+    ld, hs = qp.stride(0), qp.stride(1)
     hc = path.hc
     lse = torch.empty((hc, cfg.N), dtype=torch.float32, device="cuda")
     cap = nb * nb
@@ -151,26 +153,25 @@ def main():
                                 path.block_offsets, path.nb_dev, ws_zone, want_nb=False)
         ev[1].record()
         for src, dst in ((x["q"], qp), (x["k"], kp), (x["v"], vp)) + (((x["do"], dop),) if cfg.backward else ()):
-            P.prism_block_permute(cfg.T, cfg.H, cfg.W, path.zone_shape, src, dst, C, C, C, 0)
+            path.permute(src, out=dst)
         ev[2].record()
-        t_sel = t_f = t_b = 0.0
         for g, h0 in enumerate(range(0, cfg.heads, hc)):
             s = sel_bufs[g]
             q, k, v, o = (t[:, h0:h0 + hc] for t in (qp, kp, vp, op))
-            P.prism_select(q, k, cfg.N, hc, cfg.d, C, cfg.d, path.block_offsets, nb, cfg.top_k, cfg.top_p, sc,
+            P.prism_select(q, k, cfg.N, hc, cfg.d, ld, hs, path.block_offsets, nb, cfg.top_k, cfg.top_p, sc,
                            s.offsets, s.idx, cap, s.total, ws_sel)
             ev[3 + 3 * g].record()
-            P.prism_sparse_attn_fwd(q, k, v, o, lse, cfg.N, hc, cfg.d, C, cfg.d, path.block_offsets, nb, s.offsets,
+            P.prism_sparse_attn_fwd(q, k, v, o, lse, cfg.N, hc, cfg.d, ld, hs, path.block_offsets, nb, s.offsets,
                                     s.idx, cap, sc)
             ev[4 + 3 * g].record()
             if cfg.backward:
                 do_, gq, gk, gv = (t[:, h0:h0 + hc] for t in (dop,) + grads)
-                P.prism_sparse_attn_bwd(q, k, v, o, do_, lse, gq, gk, gv, cfg.N, hc, cfg.d, C, cfg.d,
+                P.prism_sparse_attn_bwd(q, k, v, o, do_, lse, gq, gk, gv, cfg.N, hc, cfg.d, ld, hs,
                                         path.block_offsets, nb, s.offsets, s.idx, cap, sc, ws_bwd)
             ev[5 + 3 * g].record()
         srcs = (op,) + (grads if cfg.backward else ())
         for src, name in zip(srcs, outs):
-            P.prism_block_permute(cfg.T, cfg.H, cfg.W, path.zone_shape, src, outs[name], C, C, C, 1)
+            path.permute(src, inverse=True, out=outs[name])
         ev[-1].record()
 
     ngroups = cfg.heads // hc

@@ -18,46 +18,61 @@ namespace prism {
 constexpr int kPermThreads = 256;
 constexpr int kPermRowsPerWave = 8;
 
+// A wave moves `sub` rows at a time (sub = 64 / vectors-per-row for short rows,
+// e.g. one head of 128 bf16 = 16 vectors -> 4 rows; 1 for long rows).
 template <typename V>
 __global__ void __launch_bounds__(kPermThreads)
 permute_rows_kernel(const V* __restrict__ x, V* __restrict__ y, const uint8_t* __restrict__ zone_shape, ZoneGrid g,
-                    int64_t N, int64_t vec_per_row, int64_t x_ld_vec, int64_t y_ld_vec, int inverse) {
+                    int64_t N, int64_t vec_per_row, int64_t x_ld_vec, int64_t y_ld_vec, int inverse, int sub) {
     const int lane = threadIdx.x & (kWave - 1);
     const int wid = threadIdx.x / kWave;
-    const int64_t first = (static_cast<int64_t>(blockIdx.x) * (kPermThreads / kWave) + wid) * kPermRowsPerWave;
+    const int rsub = sub > 1 ? lane / static_cast<int>(vec_per_row) : 0;
+    const int c0 = sub > 1 ? lane % static_cast<int>(vec_per_row) : lane;
+    const int cstep = sub > 1 ? static_cast<int>(vec_per_row) : kWave;
+    if (rsub >= sub) return;
+    const int64_t first =
+        (static_cast<int64_t>(blockIdx.x) * (kPermThreads / kWave) + wid) * kPermRowsPerWave * sub;
 #pragma unroll 1
     for (int r = 0; r < kPermRowsPerWave; ++r) {
-        const int64_t p = first + r;
+        const int64_t p = first + static_cast<int64_t>(r) * sub + rsub;
         if (p >= N) return;
         const int64_t n = block_major_to_raster(p, zone_shape, g);
         const int64_t src = inverse ? p : n;
         const int64_t dst = inverse ? n : p;
         const V* __restrict__ xs = x + src * x_ld_vec;
         V* __restrict__ yd = y + dst * y_ld_vec;
-        for (int64_t c = lane; c < vec_per_row; c += kWave) yd[c] = xs[c];
+        for (int64_t c = c0; c < vec_per_row; c += cstep) yd[c] = xs[c];
     }
 }
 
 hipError_t launch_block_permute(const void* x, void* y, int elem_bytes, int64_t row_elems, int64_t x_ld,
                                 int64_t y_ld, const uint8_t* zone_shape, ZoneGrid g, int64_t N, int inverse,
                                 hipStream_t s) {
-    const int64_t rows_per_block = (kPermThreads / kWave) * kPermRowsPerWave;
-    const dim3 grid(static_cast<unsigned>((N + rows_per_block - 1) / rows_per_block));
     const int64_t row_bytes = row_elems * elem_bytes;
+    int64_t vec = 2;
+    if ((row_bytes % 16) == 0 && ((x_ld * elem_bytes) % 16) == 0 && ((y_ld * elem_bytes) % 16) == 0 &&
+        ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(y)) % 16) == 0)
+        vec = 16;
+    else if ((row_bytes % 4) == 0 && ((x_ld * elem_bytes) % 4) == 0 && ((y_ld * elem_bytes) % 4) == 0 &&
+             ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(y)) % 4) == 0)
+        vec = 4;
+    const int64_t vpr = row_bytes / vec;
+    const int sub = vpr < kWave ? static_cast<int>(kWave / vpr) : 1;
+    const int64_t rows_per_block = (kPermThreads / kWave) * kPermRowsPerWave * sub;
+    const dim3 grid(static_cast<unsigned>((N + rows_per_block - 1) / rows_per_block));
     const int64_t xb = x_ld * elem_bytes, yb = y_ld * elem_bytes;
-    const uintptr_t align = reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(y);
-    if ((row_bytes % 16) == 0 && (xb % 16) == 0 && (yb % 16) == 0 && (align % 16) == 0) {
+    if (vec == 16) {
         hipLaunchKernelGGL(permute_rows_kernel<uint4>, grid, dim3(kPermThreads), 0, s,
-                           static_cast<const uint4*>(x), static_cast<uint4*>(y), zone_shape, g, N, row_bytes / 16,
-                           xb / 16, yb / 16, inverse);
-    } else if ((row_bytes % 4) == 0 && (xb % 4) == 0 && (yb % 4) == 0 && (align % 4) == 0) {
+                           static_cast<const uint4*>(x), static_cast<uint4*>(y), zone_shape, g, N, vpr, xb / 16,
+                           yb / 16, inverse, sub);
+    } else if (vec == 4) {
         hipLaunchKernelGGL(permute_rows_kernel<uint32_t>, grid, dim3(kPermThreads), 0, s,
-                           static_cast<const uint32_t*>(x), static_cast<uint32_t*>(y), zone_shape, g, N,
-                           row_bytes / 4, xb / 4, yb / 4, inverse);
+                           static_cast<const uint32_t*>(x), static_cast<uint32_t*>(y), zone_shape, g, N, vpr, xb / 4,
+                           yb / 4, inverse, sub);
     } else {
         hipLaunchKernelGGL(permute_rows_kernel<uint16_t>, grid, dim3(kPermThreads), 0, s,
-                           static_cast<const uint16_t*>(x), static_cast<uint16_t*>(y), zone_shape, g, N,
-                           row_bytes / 2, xb / 2, yb / 2, inverse);
+                           static_cast<const uint16_t*>(x), static_cast<uint16_t*>(y), zone_shape, g, N, vpr, xb / 2,
+                           yb / 2, inverse, sub);
     }
     return hipGetLastError();
 }

@@ -9,8 +9,9 @@
 //   logits_kernel        L[h][i][j] = fl32(scale * (Q_bar_i . K_bar_j)), the dot in
 //                        float64: the scores are rounded once, so they equal
 //                        the float64 definition's nearest float
-//   select_count_kernel  per row: max, float64 softmax mass, and a binary
-//                        search over the order-preserving 32-bit key of the
+//   select_count_kernel  per row: max, softmax masses (float64 exp, summed
+//                        as 2^-48 fixed-point integers), and a 4-pass radix
+//                        select over the order-preserving 32-bit key of the
 //                        scores for the boundary of the first max(k, n_p)
 //                        ranked blocks; ties at the boundary are resolved by
 //                        index.  No sort: the union of the two prefixes is one
@@ -131,129 +132,187 @@ __device__ __forceinline__ float key_score(uint32_t k) {
     return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
 }
 
-struct CountMass {
-    int c;
-    double m;
-};
-
-template <int NW>
-__device__ __forceinline__ CountMass block_count_mass(int c, double m, int* sc, double* sm) {
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wid = threadIdx.x / kWave;
-    c = wave_sum(c);
-    m = wave_sum(m);
-    __syncthreads();
-    if (lane == 0) {
-        sc[wid] = c;
-        sm[wid] = m;
-    }
-    __syncthreads();
-    CountMass r{sc[0], sm[0]};
-#pragma unroll
-    for (int w = 1; w < NW; ++w) {
-        r.c += sc[w];
-        r.m += sm[w];
-    }
-    return r;
+// Softmax mass of a score in fixed point: round(exp(L - M) * 2^48).  Each
+// value is at most 2^48, so the sum of a row (at most 32768 blocks) fits in 64
+// bits, and integer sums are exact in any order: histograms built with LDS
+// atomics are deterministic.  The rounding moves a row's cumulative mass by at
+// most nb * 2^-49 (< 6e-11 of the total).
+__device__ __forceinline__ uint64_t mass_fixed(uint32_t key, double M) {
+    return __double2ull_rn(exp(static_cast<double>(key_score(key)) - M) * 281474976710656.0);
 }
 
-// One workgroup of NW waves per (row i, head h); element j of the row lives in
-// thread j % (64 NW), slot j / (64 NW).
-template <int NW, int E>
-__global__ void __launch_bounds__(NW * 64)
+constexpr int kSelThreads = 256;
+
+// One workgroup per (row i, head h).  The row's keys live in LDS; the boundary
+// key of the kept prefix is found by a 4-pass radix select (8-bit digits, most
+// significant first) over (count, mass) histograms: at each pass the boundary
+// lies in the highest digit bucket b whose inclusive suffix (everything at or
+// above b, plus everything above the current prefix) satisfies
+//   count >= max(k, 1)  and  mass >= p * Z.
+__global__ void __launch_bounds__(kSelThreads)
 select_count_kernel(const float* __restrict__ logits, int nb, int top_k, double top_p, int32_t* __restrict__ row_count,
                     uint32_t* __restrict__ row_thr, int32_t* __restrict__ row_jlim) {
-    constexpr int NT = NW * 64;
-    __shared__ int sc[NW];
-    __shared__ double sm[NW];
-    __shared__ float sf[NW];
+    extern __shared__ uint32_t skey[];                 // nb keys
+    __shared__ uint32_t hcnt[256];
+    __shared__ unsigned long long hmass[256];
+    __shared__ unsigned long long red64[kSelThreads / kWave];
+    __shared__ uint32_t red32[kSelThreads / kWave];
+    __shared__ uint32_t s_digit;
+    __shared__ uint32_t s_cabove;
+    __shared__ unsigned long long s_mabove;
     const int i = blockIdx.x, h = blockIdx.y;
     const int64_t row = static_cast<int64_t>(h) * nb + i;
     const float* __restrict__ L = logits + row * nb;
-    uint32_t key[E];
-    double ev[E];
-    float lmax = -INFINITY;
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-        const int j = threadIdx.x + e * NT;
-        if (j < nb) {
-            const float x = L[j];
-            key[e] = score_key(x);
-            lmax = x > lmax ? x : lmax;
-        } else {
-            key[e] = 0u;
-        }
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wid = threadIdx.x / kWave;
+
+    uint32_t kmax = 0;
+    for (int j = threadIdx.x; j < nb; j += kSelThreads) {
+        const uint32_t kk = score_key(L[j]);
+        skey[j] = kk;
+        kmax = kk > kmax ? kk : kmax;
     }
-    const float M = block_max(lmax, sf);
-    double zpart = 0.0;
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-        ev[e] = key[e] ? exp(static_cast<double>(key_score(key[e])) - static_cast<double>(M)) : 0.0;
-        zpart += ev[e];
-    }
-    auto count_mass = [&](uint64_t u) -> CountMass {
-        int c = 0;
-        double m = 0.0;
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-            const bool in = static_cast<uint64_t>(key[e]) >= u && key[e] != 0u;
-            c += in ? 1 : 0;
-            m += in ? ev[e] : 0.0;
-        }
-        return block_count_mass<NW>(c, m, sc, sm);
-    };
-    const CountMass all = count_mass(1);          // every block: the mass is Z
-    const double target = top_p * all.m;
-    // the Top-p prefix holds at least one block, so the kept prefix has at
-    // least max(k, 1) blocks
-    const int kk = top_k > 1 ? top_k : 1;
+    kmax = block_max(kmax, red32);
+    const double M = static_cast<double>(key_score(kmax));
+    uint64_t z = 0;
+    for (int j = threadIdx.x; j < nb; j += kSelThreads) z += mass_fixed(skey[j], M);
+    z = block_sum(static_cast<unsigned long long>(z), red64);
+    const double target = top_p * static_cast<double>(z);
+    const int kk = top_k > 1 ? top_k : 1;    // the Top-p prefix holds at least one block
+
     int count;
     uint32_t thr;
     int jlim;
-    if (!(all.c >= kk && all.m >= target)) {
-        count = nb;                               // no prefix qualifies: keep every block
+    if (!(nb >= kk && static_cast<double>(z) >= target)) {
+        count = nb;                            // no prefix qualifies: keep every block
         thr = 0u;
         jlim = -1;
     } else {
-        uint64_t lo = 1, hi = 1ull << 32;         // pred(lo) holds, pred(hi) fails
-        while (hi - lo > 1) {
-            const uint64_t mid = lo + ((hi - lo) >> 1);
-            const CountMass cm = count_mass(mid);
-            if (cm.c >= kk && cm.m >= target) lo = mid;
-            else hi = mid;
-        }
-        thr = static_cast<uint32_t>(lo);
-        const CountMass gt = (lo == 0xFFFFFFFFull) ? CountMass{0, 0.0} : count_mass(lo + 1);
-        int ceq = 0;
+        uint32_t prefix = 0, cabove = 0;
+        uint64_t mabove = 0;
+        uint32_t ceq = 0;
+        for (int pass = 0; pass < 4; ++pass) {
+            const int shift = 24 - 8 * pass;
+            hcnt[threadIdx.x] = 0;             // 256 threads, 256 buckets
+            hmass[threadIdx.x] = 0;
+            __syncthreads();
+            for (int j0 = 0; j0 < nb; j0 += kSelThreads) {
+                const int j = j0 + threadIdx.x;
+                uint32_t key = 0;
+                bool act = false;
+                if (j < nb) {
+                    key = skey[j];
+                    act = pass == 0 || (key >> (shift + 8)) == prefix;
+                }
+                const uint32_t dig = (key >> shift) & 255u;
+                const uint64_t mf = act ? mass_fixed(key, M) : 0;
+                if (pass == 0) {
+                    // scores share few leading digits: sum equal digits across the
+                    // wave first, one atomic per distinct digit
+                    bool left = act;
+                    while (true) {
+                        const uint64_t bal = __ballot(left);
+                        if (!bal) break;
+                        const int leader = __ffsll(static_cast<unsigned long long>(bal)) - 1;
+                        const uint32_t dl = __shfl(dig, leader, kWave);
+                        const bool mine = left && dig == dl;
+                        const unsigned long long sum = wave_sum(static_cast<unsigned long long>(mine ? mf : 0));
+                        const int cnt = __popcll(__ballot(mine));
+                        if (lane == leader) {
+                            atomicAdd(&hcnt[dl], static_cast<uint32_t>(cnt));
+                            atomicAdd(&hmass[dl], sum);
+                        }
+                        left = left && !mine;
+                    }
+                } else if (act) {
+                    atomicAdd(&hcnt[dig], 1u);
+                    atomicAdd(&hmass[dig], static_cast<unsigned long long>(mf));
+                }
+            }
+            __syncthreads();
+            if (wid == 0) {
+                // lane l owns buckets 4l .. 4l+3; inclusive suffix sums from the top
+                uint32_t c[4];
+                unsigned long long m4[4];
+                uint32_t tc = 0;
+                unsigned long long tm = 0;
 #pragma unroll
-        for (int e = 0; e < E; ++e) ceq += key[e] == thr ? 1 : 0;
-        ceq = block_sum(ceq, sc);
-        const double eb = exp(static_cast<double>(key_score(thr)) - static_cast<double>(M));
-        int m = 0;
-        double acc = gt.m;
+                for (int r = 0; r < 4; ++r) {
+                    c[r] = hcnt[4 * lane + r];
+                    m4[r] = hmass[4 * lane + r];
+                    tc += c[r];
+                    tm += m4[r];
+                }
+                uint32_t sc = tc;
+                unsigned long long sm = tm;
+#pragma unroll
+                for (int off = 1; off < kWave; off <<= 1) {
+                    const uint32_t oc = __shfl_down(sc, off, kWave);
+                    const unsigned long long om = __shfl_down(sm, off, kWave);
+                    if (lane + off < kWave) {
+                        sc += oc;
+                        sm += om;
+                    }
+                }
+                // sc, sm: everything in lanes >= this lane; walk down this lane's buckets
+                uint32_t ec = sc - tc;
+                unsigned long long em = sm - tm;
+                int ntrue = 0;
+#pragma unroll
+                for (int r = 3; r >= 0; --r) {
+                    const uint32_t ic = ec + c[r];
+                    const unsigned long long im = em + m4[r];
+                    const bool ok = cabove + ic >= static_cast<uint32_t>(kk) &&
+                                    static_cast<double>(mabove + im) >= target;
+                    ntrue += ok ? 1 : 0;
+                    ec = ic;
+                    em = im;
+                }
+                const int b = wave_sum(ntrue) - 1;   // predicate holds exactly on buckets 0..b
+                if (lane == (b >> 2)) {
+                    // everything strictly above bucket b
+                    uint32_t xc = sc - tc;
+                    unsigned long long xm = sm - tm;
+                    for (int r = 3; r > (b & 3); --r) {
+                        xc += c[r];
+                        xm += m4[r];
+                    }
+                    s_digit = static_cast<uint32_t>(b);
+                    s_cabove = xc;
+                    s_mabove = xm;
+                }
+            }
+            __syncthreads();
+            const uint32_t b = s_digit;
+            prefix = (prefix << 8) | b;
+            cabove += s_cabove;
+            mabove += s_mabove;
+            ceq = hcnt[b];
+            __syncthreads();
+        }
+        thr = prefix;
+        // the boundary lies among the ceq ties of key thr, taken in index order
+        const uint64_t eb = mass_fixed(thr, M);
+        uint32_t m = 0;
+        uint64_t acc = mabove;
         do {
             ++m;
             acc += eb;
-        } while (m < ceq && !(gt.c + m >= kk && acc >= target));
-        count = gt.c + m;
+        } while (m < ceq && !(cabove + m >= static_cast<uint32_t>(kk) && static_cast<double>(acc) >= target));
+        count = static_cast<int>(cabove + m);
         if (m == ceq) {
             jlim = nb;
         } else {
-            // smallest index x with #(ties at index <= x) >= m
-            int a = -1, b = nb - 1;               // count(a) < m <= count(b)
-            while (b - a > 1) {
-                const int x = a + ((b - a) >> 1);
-                int c = 0;
-#pragma unroll
-                for (int e = 0; e < E; ++e) {
-                    const int j = threadIdx.x + e * NT;
-                    c += (key[e] == thr && j <= x) ? 1 : 0;
-                }
-                c = block_sum(c, sc);
-                if (c >= m) b = x;
-                else a = x;
+            // index of the m-th tie in ascending index order (rare: equal scores)
+            jlim = nb;
+            if (threadIdx.x == 0) {
+                uint32_t seen = 0;
+                for (int j = 0; j < nb; ++j)
+                    if (skey[j] == thr && ++seen == m) {
+                        jlim = j;
+                        break;
+                    }
             }
-            jlim = b;
         }
     }
     if (threadIdx.x == 0) {
@@ -434,15 +493,14 @@ hipError_t launch_select(const void* q, const void* k, bool bf16, int heads, int
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     const dim3 rg(nb, heads);
-    if (nb <= 256)
-        hipLaunchKernelGGL((select_count_kernel<1, 4>), rg, dim3(64), 0, s, logits, nb, top_k, top_p, row_count,
-                           row_thr, row_jlim);
-    else if (nb <= 4096)
-        hipLaunchKernelGGL((select_count_kernel<4, 16>), rg, dim3(256), 0, s, logits, nb, top_k, top_p, row_count,
-                           row_thr, row_jlim);
-    else
-        hipLaunchKernelGGL((select_count_kernel<16, 32>), rg, dim3(1024), 0, s, logits, nb, top_k, top_p, row_count,
-                           row_thr, row_jlim);
+    const size_t lds = static_cast<size_t>(nb) * sizeof(uint32_t);
+    if (lds > 48 * 1024) {
+        e = hipFuncSetAttribute(reinterpret_cast<const void*>(&select_count_kernel),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(select_count_kernel, rg, dim3(kSelThreads), lds, s, logits, nb, top_k, top_p, row_count,
+                       row_thr, row_jlim);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(csr_scan_kernel, dim3(heads), dim3(1024), 0, s, row_count, nb, sel_offsets, sel_total);

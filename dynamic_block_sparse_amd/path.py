@@ -59,11 +59,24 @@ class PrismPath:
                                       self.block_offsets, self.nb_dev, ws, prm=self.prm, zone_stats=self.zone_stats)
         return self.nb
 
+    def block_major_like(self, x):
+        """An [N, heads, d] view over head-major storage ([heads, N, d]): each
+        head's block-major rows are contiguous, so a 64-row tile of one head is
+        one 16 KB (bf16, d=128) run."""
+        N, nh, d = x.shape
+        return torch.empty((nh, N, d), dtype=x.dtype, device=x.device).permute(1, 0, 2)
+
     def permute(self, x, inverse=False, out=None):
-        y = torch.empty_like(x) if out is None else out
-        P.prism_block_permute(self.T, self.H, self.W, self.zone_shape, x, y, x.shape[1] * x.shape[2], x.stride(0),
-                              y.stride(0), 1 if inverse else 0)
-        return y
+        """Gather raster rows into block-major order (head-major storage), or
+        scatter block-major rows back into a raster [N, heads, d] tensor; one
+        library call per head."""
+        N, nh, d = x.shape
+        if out is None:
+            out = torch.empty((N, nh, d), dtype=x.dtype, device=x.device) if inverse else self.block_major_like(x)
+        for h in range(nh):
+            P.prism_block_permute(self.T, self.H, self.W, self.zone_shape, x[:, h], out[:, h], d, x.stride(0),
+                                  out.stride(0), 1 if inverse else 0)
+        return out
 
     def _cap(self):
         return self.nb * self.nb
@@ -84,7 +97,7 @@ class PrismPath:
     def forward(self, qp, kp, vp, sel, op=None, lse=None, h0=0):
         hc = self.hc
         if op is None:
-            op = torch.empty_like(qp)
+            op = self.block_major_like(qp)
         if lse is None:
             lse = torch.empty((hc, self.N), dtype=torch.float32, device=self.device)
         q, k, v, o = (x[:, h0:h0 + hc] for x in (qp, kp, vp, op))
@@ -95,7 +108,7 @@ class PrismPath:
     def backward(self, qp, kp, vp, op, dop, lse, sel, grads=None, h0=0):
         hc = self.hc
         if grads is None:
-            grads = tuple(torch.empty_like(qp) for _ in range(3))
+            grads = tuple(self.block_major_like(qp) for _ in range(3))
         dq, dk, dv = grads
         ws = torch.empty(P.prism_workspace_size(P.OP_ATTN_BWD, self.N, hc, self.d, self.nb, sel.cap),
                          dtype=torch.uint8, device=self.device)
@@ -111,8 +124,8 @@ class PrismPath:
         self.shapes(v, a)
         qp, kp, vp = self.permute(q), self.permute(k), self.permute(v)
         dop = self.permute(do) if do is not None else None
-        op = torch.empty_like(qp)
-        grads = tuple(torch.empty_like(qp) for _ in range(3)) if do is not None else None
+        op = self.block_major_like(qp)
+        grads = tuple(self.block_major_like(qp) for _ in range(3)) if do is not None else None
         lses, sels = [], []
         for h0 in range(0, self.heads, self.hc):
             sel = self.select(qp, kp, h0)

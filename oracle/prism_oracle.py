@@ -44,7 +44,12 @@ TAU128 = 0.5             # [P3] method §2
 TAU256 = 0.25            # [P3] method §2
 EPS = 1e-6               # [P3] method §1 prints "+ eps" with no value (reading)
 SHAPE_TIE = 1e-9         # window for equidistant shapes (reading: the pages give no tie rule)
-NEAR = 1e-12             # width of the "near a decision boundary" flags
+NEAR = 1e-12             # width of the "near a decision boundary" flags (zones)
+# Width of the selection flag, relative to the row's softmax total Z.  A
+# selection decided within this distance of p*Z depends on rounding: the HIP
+# path sums masses as 2^-48 fixed-point integers, which moves a cumulative
+# mass by at most NB * 2^-49 < 6e-11 of Z for NB <= 32768.
+CDF_NEAR = 1e-10
 
 
 # ----------------------------------------------------------------------------
@@ -323,7 +328,7 @@ def select_row(L, k, p):
     (the crossing block included), taken on a float64 CDF; since both sets are
     prefixes of one ranking, the union is the first max(k, n_p) blocks (at most
     NB).  Returns (sorted selected indices, flag) where flag marks a row whose
-    cumulative mass passes within NEAR*Z of p*Z at some prefix.
+    cumulative mass passes within CDF_NEAR*Z of p*Z at some prefix.
     """
     L = np.asarray(L, dtype=np.float64)
     NB = L.shape[0]
@@ -335,7 +340,7 @@ def select_row(L, k, p):
     hit = np.nonzero(cum >= target)[0]
     n_p = int(hit[0]) + 1 if hit.size else NB
     n = min(NB, max(int(k), n_p))
-    flag = bool(np.any(np.abs(cum - target) < NEAR * Z))
+    flag = bool(np.any(np.abs(cum - target) < CDF_NEAR * Z))
     return np.sort(order[:n]), flag
 
 

@@ -69,6 +69,10 @@ SMALL = [
     custom("s_one_zone_k0_p0", T=8, H=8, W=8, heads=1, d=64, dtype="bf16", top_k=0, top_p=0.0, seed=15),
     custom("s_dense", T=8, H=16, W=8, heads=2, d=64, dtype="bf16", top_k=10 ** 6, top_p=0.5, seed=16),
     custom("s_p1", T=8, H=8, W=16, heads=1, d=128, dtype="bf16", top_k=1, top_p=1.0, seed=17),
+    # small-norm queries: diffuse scores, Top-p keeps most blocks (the long clip's regime)
+    custom("s_diffuse", T=16, H=16, W=16, heads=2, d=128, dtype="bf16", top_k=2, top_p=0.95,
+           kinds=(("static", 1 / 3), ("aniso", 1 / 3), ("noisy", 1 / 3)),
+           sigma={"static": 1e-3, "aniso": 0.1, "noisy": 1.0}, beta=0.3, seed=18),
 ]
 
 
@@ -234,8 +238,8 @@ def test_full_size_sampled(name):
     np.testing.assert_array_equal(_np(qp[torch.from_numpy(rows).cuda()]), _np(xs["q"][torch.from_numpy(pi[rows]).cuda()]))
     sc = float(np.float32(1.0 / math.sqrt(cfg.d)))
     check_heads = list(range(nh)) if heads else sorted(rng.choice(cfg.heads, size=2, replace=False).tolist())
-    op = torch.empty_like(qp)
-    grads = tuple(torch.empty_like(qp) for _ in range(3)) if cfg.backward else None
+    op = path.block_major_like(qp)
+    grads = tuple(path.block_major_like(qp) for _ in range(3)) if cfg.backward else None
     sels, lses = {}, {}
     for h0 in range(0, nh, path.hc):
         sel = path.select(qp, kp, h0, want_logits=True)
@@ -272,19 +276,20 @@ def test_full_size_sampled(name):
         Og = _np(op[:, h, :])
         lg = lses[h].cpu().numpy()
         errs = {"O": [], "dQ": [], "dK": [], "dV": []}
-        # query blocks in seeded random order, up to 64, within an oracle cost budget
+        # query blocks in seeded random order, up to 64, within an oracle budget
+        # of (query rows x selected keys); at least one block is checked
         qcost = lambda i: float(offs[i + 1] - offs[i]) * float(sum(offs[j + 1] - offs[j] for j in ci[co[i]:co[i + 1]]))
         qb, spent = [], 0.0
         for i in rng.permutation(nb):
             c = qcost(i)
-            if len(qb) >= 8 and spent + c > 2e9:
+            if qb and spent + c > 4e8:
                 continue
             qb.append(i)
             spent += c
             if len(qb) >= 64:
                 break
         print(f"case {name} head {h}: checking {len(qb)} query blocks", flush=True)
-        for i in qb:
+        for n_done, i in enumerate(qb):
             s = ci[co[i]:co[i + 1]]
             o_ref, lse_ref = orc.attn_fwd_block(Qp, Kp, Vp, offs, s, i, 0, sc)
             errs["O"].append((Og[offs[i]:offs[i + 1]], o_ref))
@@ -292,19 +297,23 @@ def test_full_size_sampled(name):
             if cfg.backward:
                 dq_ref = orc.attn_bwd_block(Qp, Kp, Vp, dOp, offs, s, i, 0, sc)[0]
                 errs["dQ"].append((_np(grads[0][offs[i]:offs[i + 1], h, :]), dq_ref))
+            if n_done % 8 == 7:
+                print(f"case {name} head {h}: {n_done + 1} query blocks checked", flush=True)
         if cfg.backward:
             # key blocks in seeded random order, up to 32 of them, while the
             # oracle's cost (query rows x selected keys of every user row) stays
-            # within a budget; the kernel runs the same code for every block
+            # within a budget; the kernel runs the same code for every block.
+            # Where even single key blocks exceed it (the long clip keeps ~30% of
+            # blocks per row), dK/dV are covered by the diffuse small grids.
             rows_of = np.repeat(np.arange(nb), np.diff(co))
             keys_of_row = np.array([float(sum(offs[j + 1] - offs[j] for j in ci[co[i]:co[i + 1]]))
                                     for i in range(nb)])
             cost_of_row = np.diff(offs) * keys_of_row
-            budget, spent, taken = 4e9, 0.0, 0
-            for j in rng.permutation(nb):
+            budget, spent, taken = 4e8, 0.0, 0
+            for j in rng.permutation(nb)[:4096]:
                 users = np.unique(rows_of[ci == j])
                 c = float(cost_of_row[users].sum())
-                if taken >= 4 and spent + c > budget:
+                if spent + c > budget:
                     continue
                 dk_ref, dv_ref = orc.key_block_grads(Qp, Kp, Vp, dOp, offs, co, ci, j, 0, sc, rows=users)
                 errs["dK"].append((_np(grads[1][offs[j]:offs[j + 1], h, :]), dk_ref))
@@ -314,6 +323,7 @@ def test_full_size_sampled(name):
                 print(f"case {name} head {h}: key block {j} ({len(users)} query blocks) checked", flush=True)
                 if taken >= 32:
                     break
+            print(f"case {name} head {h}: {taken} key blocks checked for dK/dV", flush=True)
         for k, pairs in errs.items():
             if pairs:
                 got = np.concatenate([p[0] for p in pairs])
