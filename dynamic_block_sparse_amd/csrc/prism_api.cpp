@@ -279,7 +279,7 @@ prism_status prism_sparse_attn_fwd(const void* q, const void* k, const void* v, 
         return fail(PRISM_E_ARG, "null pointer argument");
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
         return fail(PRISM_E_UNSUPPORTED, "token tensors must be 16-byte aligned");
-    if (!std::isfinite(scale)) return fail(PRISM_E_ARG, "scale must be finite");
+    if (!std::isfinite(scale) || !(scale > 0.0f)) return fail(PRISM_E_ARG, "scale must be finite and positive");
     (void)ws;
     (void)ws_bytes;
     if (use_simt_attention(dt))
@@ -305,7 +305,7 @@ prism_status prism_sparse_attn_bwd(const void* q, const void* k, const void* v, 
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) || !aligned16(dq) ||
         !aligned16(dk) || !aligned16(dv))
         return fail(PRISM_E_UNSUPPORTED, "token tensors must be 16-byte aligned");
-    if (!std::isfinite(scale)) return fail(PRISM_E_ARG, "scale must be finite");
+    if (!std::isfinite(scale) || !(scale > 0.0f)) return fail(PRISM_E_ARG, "scale must be finite and positive");
     const size_t need = prism_workspace_size(PRISM_OP_ATTN_BWD, N, heads, d, nb, cap);
     if (!ws || ws_bytes < need)
         return fail(PRISM_E_WORKSPACE, "backward needs %zu workspace bytes, got %zu", need, ws ? ws_bytes : 0);

@@ -173,6 +173,9 @@ prism_status prism_select(const void* q, const void* k, prism_dtype dt,
  *   o              out block-major [N, heads, d], same dtype/strides
  *   lse            out [heads, N] fp32 natural-log log-sum-exp of the scaled scores
  *   sel_offsets, sel_idx, cap  the CSR written by prism_select
+ *   scale          softmax scale, finite and > 0 (1/sqrt(d)); PRISM_E_ARG otherwise
+ *   block_offsets  must be the offsets written by prism_zone_shapes for the same
+ *                  grid (every block a whole number of 64-token tiles)
  * bf16 runs on bf16 MFMA with fp32 accumulation and an fp32 online softmax;
  * f32 runs on fp32 vector arithmetic.
  */
