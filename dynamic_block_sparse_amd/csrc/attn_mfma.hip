@@ -41,12 +41,17 @@ __device__ __forceinline__ f32x16_t mfma32(u32x4_t a, u32x4_t b, f32x16_t c) {
                                                    0, 0, 0);
 }
 
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// two fp32 -> packed bf16 pair (round to nearest even), one v_cvt_pk_bf16_f32
 __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
-    const __bf16 a = static_cast<__bf16>(lo);
-    const __bf16 b = static_cast<__bf16>(hi);
-    return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, a)) |
-           (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b)) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
+
+// 2^x on the transcendental unit; results below the normal range flush to 0,
+// which is what the softmax wants for scores far below the row maximum
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // B operand of k-step s2 built from C-tile registers 8*s2 .. 8*s2+7
 __device__ __forceinline__ u32x4_t pack_kstep(const f32x16_t& x, int s2) {
@@ -248,13 +253,13 @@ attn_fwd_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
             for (int x = 0; x < 16; ++x) mx = fmaxf(mx, fmaxf(s0[x], s1[x]));
             mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * scale_log2;
             const float mnew = fmaxf(mrow, mx);
-            const float alpha = exp2f(mrow - mnew);
+            const float alpha = fast_exp2(mrow - mnew);
             mrow = mnew;
             float ls = 0.0f;
 #pragma unroll
             for (int x = 0; x < 16; ++x) {
-                s0[x] = exp2f(fmaf(s0[x], scale_log2, -mnew));
-                s1[x] = exp2f(fmaf(s1[x], scale_log2, -mnew));
+                s0[x] = fast_exp2(fmaf(s0[x], scale_log2, -mnew));
+                s1[x] = fast_exp2(fmaf(s1[x], scale_log2, -mnew));
                 ls += s0[x] + s1[x];
             }
             lrow = fmaf(lrow, alpha, ls);
@@ -417,7 +422,7 @@ attn_dq_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
             for (int x = 0; x < 16; ++x) {
-                const float p = exp2f(fmaf(sa[mt][x], scale_log2, -lrow));
+                const float p = fast_exp2(fmaf(sa[mt][x], scale_log2, -lrow));
                 sa[mt][x] = p * (pa[mt][x] - drow);     // dS^T
             }
 #pragma unroll
@@ -518,7 +523,7 @@ attn_dkdv_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
                 const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const float p = exp2f(fmaf(sa[mr][4 * g + r], scale_log2, -lv[r]));
+                    const float p = fast_exp2(fmaf(sa[mr][4 * g + r], scale_log2, -lv[r]));
                     sa[mr][4 * g + r] = p;
                     pa[mr][4 * g + r] = p * (pa[mr][4 * g + r] - dv4[r]);   // dS
                 }
