@@ -6,7 +6,9 @@
 //
 // Every block is 1, 2 or 4 64-token tiles after the block-major permutation,
 // and all rows of a block share its selected set, so the unit of work is a
-// 64-row tile against the 64-key tiles of the selected blocks.
+// 64-row tile against the 64-key tiles of the selected blocks.  A workgroup
+// has 2 waves; each wave owns 32 rows (forward, dQ) or 32 keys (dK/dV) and
+// streams the other side's tiles through LDS.
 //
 // MFMA shape v_mfma_f32_32x32x16_bf16 (lane l, half h = l / 32):
 //   A (32x16): lane holds row l%32, k = 8h .. 8h+7
@@ -21,6 +23,16 @@
 // addressed by lanes i/4, 4 + i/4, 8 + i/4 and 12 + i/4 of the group, so
 // pointing lane s at (row R + s/4, column C + 4*(s%4)) hands lane i rows
 // R .. R+3 of column C + i.
+//
+// LDS tiles are 64 rows x D bf16, unpadded, with the 16-byte chunk c of row r
+// stored at chunk position c ^ swz(r): swz(r) = 4*(r & 3) + ((r >> 2) & 3) for
+// D = 128 and 2*(r & 3) + ((r >> 2) & 1) for D = 64.  Both the 16-byte row
+// reads and the transposing reads are then free of LDS bank conflicts
+// (measured with the bank-conflict counter on gfx950; the unswizzled layout
+// and other XOR patterns conflict on one or the other).  Tiles are filled by direct global->LDS
+// loads (global_load_lds_dwordx4: lane l's 16 bytes land at base + 16 l), each
+// lane fetching the global chunk its LDS slot holds, double-buffered so the
+// next tile loads while the current one is used.
 #include "prism_device.hpp"
 #include "prism_internal.hpp"
 
@@ -32,17 +44,19 @@ typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 typedef short s16x4_t __attribute__((__vector_size__(8)));
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+typedef __attribute__((address_space(1))) void gvoid_t;
+typedef __attribute__((address_space(3))) void lvoid_t;
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+
 
 __device__ __forceinline__ f32x16_t mfma32(u32x4_t a, u32x4_t b, f32x16_t c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
                                                    0, 0, 0);
 }
-
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 // two fp32 -> packed bf16 pair (round to nearest even), one v_cvt_pk_bf16_f32
 __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
@@ -59,23 +73,116 @@ __device__ __forceinline__ u32x4_t pack_kstep(const f32x16_t& x, int s2) {
                    pack2(x[8 * s2 + 4], x[8 * s2 + 5]), pack2(x[8 * s2 + 6], x[8 * s2 + 7])};
 }
 
-__device__ __forceinline__ u32x4_t lds_read16(const uint16_t* p) { return *reinterpret_cast<const u32x4_t*>(p); }
+// Scheduling hint for an unrolled run of STEPS steps that each issue NR LDS
+// reads feeding NM MFMAs: keep the reads AHEAD steps ahead of the MFMAs that
+// consume them, so LDS latency hides behind matrix work instead of the wave
+// waiting on every step.
+template <int NR, int NM, int STEPS, int AHEAD>
+__device__ __forceinline__ void sched_reads_ahead() {
+    __builtin_amdgcn_sched_group_barrier(0x100, NR * AHEAD, 0);
+#pragma unroll
+    for (int i = 0; i < STEPS - AHEAD; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, NM * AHEAD, 0);
+}
 
-// A operand for a reduction over the rows of a row-major LDS tile `nat`
-// (row stride NS elements): output rows are the tile's columns col0 .. col0+31,
-// and the 16-row k-step starting at `base` is read in the permuted order that
-// matches pack_kstep (rows base + 4h + 0..3, then base + 8 + 4h + 0..3).
-template <int NS>
-__device__ __forceinline__ u32x4_t tr_operand(const uint16_t* nat, int base, int col0, int lane) {
+// ---------------------------------------------------------------- swizzled LDS tiles
+
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+    if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+    else return ((r & 3) << 1) | ((r >> 2) & 1);
+}
+
+// element offset of (row r, column c) in a swizzled tile, c a multiple of 4
+template <int D>
+__device__ __forceinline__ int sw_off(int r, int c) {
+    return r * D + ((((c >> 3) ^ swz<D>(r))) << 3) + (c & 7);
+}
+
+// 16-byte read of columns c .. c+7 (c a multiple of 8) of row r
+template <int D>
+__device__ __forceinline__ u32x4_t sw_read16(const uint16_t* tile, int r, int c) {
+    return *reinterpret_cast<const u32x4_t*>(tile + sw_off<D>(r, c));
+}
+
+// A operand for a reduction over the rows of a swizzled tile: output rows are
+// the tile's columns col0 .. col0+31, and the 16-row k-step starting at `base`
+// is read in the permuted order that matches pack_kstep.
+template <int D>
+__device__ __forceinline__ u32x4_t tr_operand(const uint16_t* tile, int base, int col0, int lane) {
     const int g = lane >> 4, sl = lane & 15;
     const int row = base + 4 * (g >> 1) + (sl >> 2);
     const int col = col0 + 16 * (g & 1) + 4 * (sl & 3);
-    const uint16_t* p = nat + row * NS + col;
-    const s16x4_t r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)p);
-    const s16x4_t r2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(p + 8 * NS));
+    const s16x4_t r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(tile + sw_off<D>(row, col)));
+    const s16x4_t r2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(tile + sw_off<D>(row + 8, col)));
     const u32x2_t a = __builtin_bit_cast(u32x2_t, r1);
     const u32x2_t b = __builtin_bit_cast(u32x2_t, r2);
     return u32x4_t{a.x, a.y, b.x, b.y};
+}
+
+// LDS byte address of a __shared__ object
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lvoid_t*)p));
+}
+
+// One direct global->LDS load: lane l fetches BYTES bytes at gbase + voff[l]
+// and they land at LDS address lds + BYTES * l.  It is written in asm so that
+// the compiler does not see an LDS store in flight: it would otherwise make
+// every later transposing LDS read wait for all outstanding loads, including
+// those into the other buffer.  Completion is awaited explicitly (dma_join)
+// before the buffer is read.  One wait state separates the M0 write from the
+// load that uses it.
+__device__ __forceinline__ void dma16(const void* gbase, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(gbase), "s"(lds)
+                 : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const void* gbase, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(gbase), "s"(lds)
+                 : "memory", "m0");
+}
+
+// Per-lane byte offsets for loading a 64-row tile (token stride ld elements)
+// into a swizzled LDS tile, shared by the NW waves of the workgroup: wave w
+// issues instructions w, w + NW, ...; one instruction fills 1 KB of LDS
+// (64 lanes x 16 bytes), i.e. 64 / (D / 8) consecutive rows.  Each lane loads
+// the global chunk that its LDS slot holds under the swizzle.
+template <int D, int NW>
+struct TileDma {
+    static constexpr int CPR = D / 8;       // 16-byte chunks per row
+    static constexpr int RPI = 64 / CPR;    // rows per instruction
+    static constexpr int NI = 64 / RPI;     // instructions per tile
+    static constexpr int PER = NI / NW;     // instructions per wave
+    uint32_t voff[PER];
+    __device__ void init(int64_t ld, int wave, int lane) {
+        const int pc = lane % CPR;
+#pragma unroll
+        for (int u = 0; u < PER; ++u) {
+            const int r = (u * NW + wave) * RPI + lane / CPR;
+            voff[u] = static_cast<uint32_t>((r * ld + ((pc ^ swz<D>(r)) << 3)) * 2);
+        }
+    }
+    __device__ void load(uint16_t* dst, const uint16_t* src, int wave) const {
+        const uint32_t base = lds_addr(dst);
+#pragma unroll
+        for (int u = 0; u < PER; ++u) dma16(src, voff[u], base + (u * NW + wave) * 1024);
+    }
+};
+
+// An empty use of x: the compiler waits here for the global load that
+// produced x.  Operands loaded before the tile loop are settled this way;
+// otherwise the compiler would place that wait at their first use inside the
+// loop, in every iteration, where the direct loads in flight (which it does
+// not see) would make it wait for the next tile as well.
+__device__ __forceinline__ void settle(const u32x4_t& x) { asm volatile("" ::"v"(x)); }
+__device__ __forceinline__ void settle(float x) { asm volatile("" ::"v"(x)); }
+
+// wait for this wave's direct loads, then for every wave's
+__device__ __forceinline__ void dma_join() {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
 }
 
 // Cursor over the 64-token tiles of a list of blocks (uniform across the workgroup).
@@ -111,6 +218,23 @@ struct TileCursor {
     }
 };
 
+// Double-buffered walk over the tiles of `cur`: tile t+1 is loaded into
+// buffer b^1 while tile t, in buffer b, is used.
+template <class Issue, class Compute>
+__device__ __forceinline__ void tile_pipeline(TileCursor& cur, Issue&& issue, Compute&& compute) {
+    int t = cur.next();
+    if (t < 0) return;
+    issue(t, 0);
+    dma_join();
+    for (int b = 0;; b ^= 1) {
+        t = cur.next();
+        if (t >= 0) issue(t, b ^ 1);
+        compute(b);
+        dma_join();
+        if (t < 0) return;
+    }
+}
+
 // XCD-aware mapping.  Workgroups are dispatched in id order and dealt
 // round-robin to the 8 XCDs; each XCD gets a contiguous range of the
 // (head, tile) grid, so neighbouring tiles of a head, which select overlapping
@@ -134,44 +258,26 @@ __device__ __forceinline__ int find_block(const int32_t* __restrict__ offs, int 
 
 // ---------------------------------------------------------------- forward
 //
-// 4 waves per 64-row query tile.  Each iteration stages two 64-key tiles of K
-// and V (row-major) in LDS; wave w takes query rows 32*(w & 1) against key
-// tile w >> 1 with its own online-softmax state; the two key halves are
-// merged at the end.  Scores are computed transposed, S^T = K Q^T, so a lane
-// owns one query row: its max and sum need one cross-lane swap and the O^T
-// rescale is a per-lane scalar.
+// 2 waves per 64-row query tile; wave w owns rows 32*w .. +31 and streams
+// every selected 64-key tile.  Scores are computed transposed, S^T = K Q^T,
+// so a lane owns one query row: its max and sum need one cross-lane swap and
+// the O^T rescale is a per-lane scalar.  The running maximum is raised only
+// when a tile's maximum exceeds it by more than 8 (log2 units), so O is
+// rescaled rarely; exponents stay below 2^8 in between.
 
 template <int D>
-struct FwdSmem {
-    static constexpr int NS = D + 8;   // row stride: 16-byte aligned, conflict-free 16-byte row reads
-    uint16_t k[2][64][NS];
-    uint16_t v[2][64][NS];
-};
-
-template <int D>
-struct FwdStage {
-    static constexpr int CPR = D / 8;                // 16-byte chunks per row
-    static constexpr int RPP = 256 / CPR;            // rows covered per pass by the 256 threads
-    static constexpr int PASSES = 64 / RPP;          // passes per tile
-    u32x4_t r[4 * PASSES];                           // [tensor K/V][tile 0/1][pass]
-};
-
-template <int D>
-__global__ void __launch_bounds__(256, 2)
+__global__ void __launch_bounds__(128, 1)
 attn_fwd_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
                      uint16_t* __restrict__ o, float* __restrict__ lse, int64_t N, int64_t ld, int64_t hs,
                      const int32_t* __restrict__ offs, int nb, const int32_t* __restrict__ sel_off,
                      const int32_t* __restrict__ sel_idx, int64_t cap, float scale_log2) {
-    using S = FwdStage<D>;
-    constexpr int NS = FwdSmem<D>::NS;
-    __shared__ FwdSmem<D> sm;
+    __shared__ uint16_t kbuf[2][64 * D], vbuf[2][64 * D];
     const int ntiles = static_cast<int>(N / 64);
     const int wg = xcd_remap(blockIdx.x);
     const int h = wg / ntiles;
     const int64_t p0 = static_cast<int64_t>(wg % ntiles) * 64;
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int rh = wave & 1, kh = wave >> 1;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int hl = lane >> 5, col = lane & 31;
     const int i = find_block(offs, nb, p0);
     const uint16_t* __restrict__ kh_ = k + h * hs;
@@ -180,19 +286,15 @@ attn_fwd_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     const int32_t* __restrict__ si = sel_idx + static_cast<int64_t>(h) * cap;
     const int e0 = so[i];
     const int e1 = static_cast<int>(min(static_cast<int64_t>(so[i + 1]), cap));
-
-    // staging: thread owns 16-byte column chunk sc of rows sr + RPP*pass
-    const int sc = threadIdx.x % S::CPR, sr = threadIdx.x / S::CPR;
-    int64_t goff[S::PASSES];
-#pragma unroll
-    for (int ps = 0; ps < S::PASSES; ++ps) goff[ps] = static_cast<int64_t>(sr + S::RPP * ps) * ld + sc * 8;
-
     constexpr int KS = D / 16, DM = D / 32;
+    const int64_t row = p0 + 32 * wave + col;
     u32x4_t qb[KS];
     {
-        const uint16_t* qrow = q + (p0 + 32 * rh + col) * ld + h * hs;
+        const uint16_t* qrow = q + row * ld + h * hs;
 #pragma unroll
         for (int s = 0; s < KS; ++s) qb[s] = *reinterpret_cast<const u32x4_t*>(qrow + 16 * s + 8 * hl);
+#pragma unroll
+        for (int s = 0; s < KS; ++s) settle(qb[s]);
     }
     f32x16_t oacc[DM];
 #pragma unroll
@@ -201,118 +303,69 @@ attn_fwd_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
         for (int x = 0; x < 16; ++x) oacc[m][x] = 0.0f;
     float mrow = -INFINITY, lrow = 0.0f;
 
-    TileCursor cur;
-    cur.init(si, offs, e0, e1);
-    S st;
-    auto load = [&](int t0, int t1) {
-#pragma unroll
-        for (int tl = 0; tl < 2; ++tl) {
-            const int t = tl ? t1 : t0;
-            if (t < 0) continue;
-            const uint16_t* kb = kh_ + static_cast<int64_t>(t) * ld;
-            const uint16_t* vb = vh_ + static_cast<int64_t>(t) * ld;
-#pragma unroll
-            for (int ps = 0; ps < S::PASSES; ++ps) {
-                st.r[(0 * 2 + tl) * S::PASSES + ps] = *reinterpret_cast<const u32x4_t*>(kb + goff[ps]);
-                st.r[(1 * 2 + tl) * S::PASSES + ps] = *reinterpret_cast<const u32x4_t*>(vb + goff[ps]);
-            }
-        }
+    TileDma<D, 2> dma;
+    dma.init(ld, wave, lane);
+    auto issue = [&](int t, int b) {
+        dma.load(kbuf[b], kh_ + static_cast<int64_t>(t) * ld, wave);
+        dma.load(vbuf[b], vh_ + static_cast<int64_t>(t) * ld, wave);
     };
-    int t0 = cur.next();
-    int t1 = cur.next();
-    load(t0, t1);
-    while (t0 >= 0) {
-        const bool has1 = t1 >= 0;
-        __syncthreads();
+    auto compute = [&](int b) {
+        const uint16_t* kt = kbuf[b];
+        const uint16_t* vt = vbuf[b];
+        f32x16_t s0, s1;
 #pragma unroll
-        for (int tl = 0; tl < 2; ++tl) {
-            if (tl == 1 && !has1) continue;
+        for (int x = 0; x < 16; ++x) s0[x] = s1[x] = 0.0f;
 #pragma unroll
-            for (int ps = 0; ps < S::PASSES; ++ps) {
-                *reinterpret_cast<u32x4_t*>(&sm.k[tl][sr + S::RPP * ps][sc * 8]) = st.r[(0 * 2 + tl) * S::PASSES + ps];
-                *reinterpret_cast<u32x4_t*>(&sm.v[tl][sr + S::RPP * ps][sc * 8]) = st.r[(1 * 2 + tl) * S::PASSES + ps];
-            }
+        for (int s = 0; s < KS; ++s) {
+            s0 = mfma32(sw_read16<D>(kt, col, 16 * s + 8 * hl), qb[s], s0);
+            s1 = mfma32(sw_read16<D>(kt, 32 + col, 16 * s + 8 * hl), qb[s], s1);
         }
-        __syncthreads();
-        const int n0 = cur.next();
-        const int n1 = n0 >= 0 ? cur.next() : -1;
-        if (n0 >= 0) load(n0, n1);
-        if (kh == 0 || has1) {
-            const uint16_t* kt = &sm.k[kh][0][0];
-            const uint16_t* vt = &sm.v[kh][0][0];
-            f32x16_t s0, s1;
+        sched_reads_ahead<2, 2, KS, 2>();
+        float mx = -INFINITY;
 #pragma unroll
-            for (int x = 0; x < 16; ++x) s0[x] = s1[x] = 0.0f;
-#pragma unroll
-            for (int s = 0; s < KS; ++s) {
-                s0 = mfma32(lds_read16(kt + col * NS + 16 * s + 8 * hl), qb[s], s0);
-                s1 = mfma32(lds_read16(kt + (32 + col) * NS + 16 * s + 8 * hl), qb[s], s1);
-            }
-            float mx = -INFINITY;
-#pragma unroll
-            for (int x = 0; x < 16; ++x) mx = fmaxf(mx, fmaxf(s0[x], s1[x]));
-            mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * scale_log2;
+        for (int x = 0; x < 16; ++x) mx = fmaxf(mx, fmaxf(s0[x], s1[x]));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * scale_log2;
+        if (__any(mx > mrow + 8.0f)) {
             const float mnew = fmaxf(mrow, mx);
             const float alpha = fast_exp2(mrow - mnew);
             mrow = mnew;
-            float ls = 0.0f;
-#pragma unroll
-            for (int x = 0; x < 16; ++x) {
-                s0[x] = fast_exp2(fmaf(s0[x], scale_log2, -mnew));
-                s1[x] = fast_exp2(fmaf(s1[x], scale_log2, -mnew));
-                ls += s0[x] + s1[x];
-            }
-            lrow = fmaf(lrow, alpha, ls);
+            lrow *= alpha;
 #pragma unroll
             for (int m = 0; m < DM; ++m)
 #pragma unroll
                 for (int x = 0; x < 16; ++x) oacc[m][x] *= alpha;
-            const u32x4_t pb[4] = {pack_kstep(s0, 0), pack_kstep(s0, 1), pack_kstep(s1, 0), pack_kstep(s1, 1)};
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-                for (int m = 0; m < DM; ++m) oacc[m] = mfma32(tr_operand<NS>(vt, 16 * ks, 32 * m, lane), pb[ks], oacc[m]);
         }
-        t0 = n0;
-        t1 = n1;
-    }
-    // merge the two key halves (waves kh = 1 hand their state to kh = 0)
-    __syncthreads();
-    float* red = reinterpret_cast<float*>(&sm);
-    constexpr int PER = 3 + 16 * DM;   // odd stride: lanes land in distinct banks
-    const int slot = rh * 64 + lane;
-    if (kh == 1) {
-        float* dst = red + slot * PER;
-        dst[0] = mrow;
-        dst[1] = lrow;
+        float ls = 0.0f;
 #pragma unroll
-        for (int m = 0; m < DM; ++m)
+        for (int x = 0; x < 16; ++x) {
+            s0[x] = fast_exp2(fmaf(s0[x], scale_log2, -mrow));
+            s1[x] = fast_exp2(fmaf(s1[x], scale_log2, -mrow));
+            ls += s0[x] + s1[x];
+        }
+        lrow += ls;
+        const u32x4_t pb[4] = {pack_kstep(s0, 0), pack_kstep(s0, 1), pack_kstep(s1, 0), pack_kstep(s1, 1)};
 #pragma unroll
-            for (int x = 0; x < 16; ++x) dst[2 + 16 * m + x] = oacc[m][x];
-    }
-    __syncthreads();
-    if (kh == 0) {
-        const float* src = red + slot * PER;
-        const float m1 = src[0], l1 = src[1];
-        const float mt = fmaxf(mrow, m1);
-        const float a0 = exp2f(mrow - mt);
-        const float a1 = (m1 == -INFINITY) ? 0.0f : exp2f(m1 - mt);
-        float lt = lrow * a0 + l1 * a1;
-        lt += __shfl_xor(lt, 32, 64);
-        const float inv = 1.0f / lt;
-        const int64_t row = p0 + 32 * rh + col;
-        uint16_t* orow = o + row * ld + h * hs;
+        for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-        for (int m = 0; m < DM; ++m)
+            for (int m = 0; m < DM; ++m) oacc[m] = mfma32(tr_operand<D>(vt, 16 * ks, 32 * m, lane), pb[ks], oacc[m]);
+    };
+
+    TileCursor cur;
+    cur.init(si, offs, e0, e1);
+    tile_pipeline(cur, issue, compute);
+    // lanes l and l^32 hold the two halves of a row's sum
+    const float lt = lrow + __shfl_xor(lrow, 32, 64);
+    const float inv = 1.0f / lt;
+    uint16_t* orow = o + row * ld + h * hs;
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                float x[4];
+    for (int m = 0; m < DM; ++m)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) x[r] = (oacc[m][4 * g + r] * a0 + src[2 + 16 * m + 4 * g + r] * a1) * inv;
-                *reinterpret_cast<u32x2_t*>(orow + 32 * m + 8 * g + 4 * hl) = u32x2_t{pack2(x[0], x[1]), pack2(x[2], x[3])};
-            }
-        if (hl == 0) lse[static_cast<int64_t>(h) * N + row] = (mt + __log2f(lt)) * kLn2;
-    }
+        for (int g = 0; g < 4; ++g) {
+            const f32x16_t& a = oacc[m];
+            *reinterpret_cast<u32x2_t*>(orow + 32 * m + 8 * g + 4 * hl) =
+                u32x2_t{pack2(a[4 * g] * inv, a[4 * g + 1] * inv), pack2(a[4 * g + 2] * inv, a[4 * g + 3] * inv)};
+        }
+    if (hl == 0) lse[static_cast<int64_t>(h) * N + row] = (mrow + __log2f(lt)) * kLn2;
 }
 
 // ---------------------------------------------------------------- backward
@@ -330,49 +383,19 @@ attn_fwd_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
 // backward is deterministic.
 
 template <int D>
-struct BwdTile {
-    static constexpr int NS = D + 8;
-    uint16_t a[64][NS];
-    uint16_t b[64][NS];
-};
-
-// Stage rows t .. t+63 of x and y (same strides) into tile.a / tile.b with the
-// 128 threads of the workgroup, 16-byte chunks, consecutive threads on
-// consecutive chunks of a row.
-template <int D>
-__device__ __forceinline__ void stage2(BwdTile<D>& tl, const uint16_t* __restrict__ x, const uint16_t* __restrict__ y,
-                                       int64_t ld, int t) {
-    constexpr int CPR = D / 8, RPP = 128 / CPR, PASSES = 64 / RPP;
-    const int sc = threadIdx.x % CPR, sr = threadIdx.x / CPR;
-    u32x4_t ra[PASSES], rb[PASSES];
-#pragma unroll
-    for (int ps = 0; ps < PASSES; ++ps) {
-        const int64_t off = static_cast<int64_t>(t + sr + RPP * ps) * ld + sc * 8;
-        ra[ps] = *reinterpret_cast<const u32x4_t*>(x + off);
-        rb[ps] = *reinterpret_cast<const u32x4_t*>(y + off);
-    }
-#pragma unroll
-    for (int ps = 0; ps < PASSES; ++ps) {
-        *reinterpret_cast<u32x4_t*>(&tl.a[sr + RPP * ps][sc * 8]) = ra[ps];
-        *reinterpret_cast<u32x4_t*>(&tl.b[sr + RPP * ps][sc * 8]) = rb[ps];
-    }
-}
-
-template <int D>
-__global__ void __launch_bounds__(128, 2)
+__global__ void __launch_bounds__(128, 1)
 attn_dq_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
                     const uint16_t* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ Dq,
                     uint16_t* __restrict__ dq, int64_t N, int64_t ld, int64_t hs, const int32_t* __restrict__ offs,
                     int nb, const int32_t* __restrict__ sel_off, const int32_t* __restrict__ sel_idx, int64_t cap,
                     float scale_log2, float scale) {
-    constexpr int NS = BwdTile<D>::NS;
-    __shared__ BwdTile<D> sm;     // a = K, b = V
+    __shared__ uint16_t kbuf[2][64 * D], vbuf[2][64 * D];
     const int ntiles = static_cast<int>(N / 64);
     const int wg = xcd_remap(blockIdx.x);
     const int h = wg / ntiles;
     const int64_t p0 = static_cast<int64_t>(wg % ntiles) * 64;
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int hl = lane >> 5, col = lane & 31;
     const int i = find_block(offs, nb, p0);
     const int32_t* __restrict__ so = sel_off + static_cast<int64_t>(h) * (nb + 1);
@@ -393,6 +416,13 @@ attn_dq_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     }
     const float lrow = lse[static_cast<int64_t>(h) * N + row] * kLog2e;
     const float drow = Dq[static_cast<int64_t>(h) * N + row];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+        settle(qb[s]);
+        settle(db[s]);
+    }
+    settle(lrow);
+    settle(drow);
     f32x16_t acc[DM];
 #pragma unroll
     for (int m = 0; m < DM; ++m)
@@ -400,12 +430,16 @@ attn_dq_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
         for (int x = 0; x < 16; ++x) acc[m][x] = 0.0f;
     const uint16_t* __restrict__ kh_ = k + h * hs;
     const uint16_t* __restrict__ vh_ = v + h * hs;
-    TileCursor cur;
-    cur.init(si, offs, e0, e1);
-    for (int t = cur.next(); t >= 0; t = cur.next()) {
-        __syncthreads();
-        stage2<D>(sm, kh_, vh_, ld, t);
-        __syncthreads();
+
+    TileDma<D, 2> dma;
+    dma.init(ld, wave, lane);
+    auto issue = [&](int t, int b) {
+        dma.load(kbuf[b], kh_ + static_cast<int64_t>(t) * ld, wave);
+        dma.load(vbuf[b], vh_ + static_cast<int64_t>(t) * ld, wave);
+    };
+    auto compute = [&](int b) {
+        const uint16_t* kt = kbuf[b];
+        const uint16_t* vt = vbuf[b];
         f32x16_t sa[2], pa[2];
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
@@ -415,9 +449,10 @@ attn_dq_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
         for (int s = 0; s < KS; ++s)
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt) {
-                sa[mt] = mfma32(lds_read16(&sm.a[32 * mt + col][16 * s + 8 * hl]), qb[s], sa[mt]);
-                pa[mt] = mfma32(lds_read16(&sm.b[32 * mt + col][16 * s + 8 * hl]), db[s], pa[mt]);
+                sa[mt] = mfma32(sw_read16<D>(kt, 32 * mt + col, 16 * s + 8 * hl), qb[s], sa[mt]);
+                pa[mt] = mfma32(sw_read16<D>(vt, 32 * mt + col, 16 * s + 8 * hl), db[s], pa[mt]);
             }
+        sched_reads_ahead<4, 4, KS, 2>();
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
@@ -427,11 +462,15 @@ attn_dq_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
             }
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-            const u32x4_t b = pack_kstep(sa[ks >> 1], ks & 1);
+            const u32x4_t bs = pack_kstep(sa[ks >> 1], ks & 1);
 #pragma unroll
-            for (int m = 0; m < DM; ++m) acc[m] = mfma32(tr_operand<NS>(&sm.a[0][0], 16 * ks, 32 * m, lane), b, acc[m]);
+            for (int m = 0; m < DM; ++m) acc[m] = mfma32(tr_operand<D>(kt, 16 * ks, 32 * m, lane), bs, acc[m]);
         }
-    }
+    };
+
+    TileCursor cur;
+    cur.init(si, offs, e0, e1);
+    tile_pipeline(cur, issue, compute);
     uint16_t* out = dq + row * ld + h * hs;
 #pragma unroll
     for (int m = 0; m < DM; ++m)
@@ -444,27 +483,21 @@ attn_dq_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
 }
 
 template <int D>
-struct DkvSmem {
-    BwdTile<D> t;      // a = Q, b = dO
-    float l2[64];      // lse in log2 units
-    float dd[64];      // D = rowsum(dO * O)
-};
-
-template <int D>
 __global__ void __launch_bounds__(128)
 attn_dkdv_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
                       const uint16_t* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ Dq,
                       uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, int64_t N, int64_t ld, int64_t hs,
                       const int32_t* __restrict__ offs, int nb, const int32_t* __restrict__ tr_off,
                       const int32_t* __restrict__ tr_idx, int64_t cap, float scale_log2, float scale) {
-    constexpr int NS = BwdTile<D>::NS;
-    __shared__ DkvSmem<D> sm;
+    // Q and dO tiles, lse (natural log) and D = rowsum(dO * O) of their rows
+    __shared__ uint16_t qbuf[2][64 * D], obuf[2][64 * D];
+    __shared__ float lbuf[2][64], dbuf[2][64];
     const int ntiles = static_cast<int>(N / 64);
     const int wg = xcd_remap(blockIdx.x);
     const int h = wg / ntiles;
     const int64_t k0 = static_cast<int64_t>(wg % ntiles) * 64;
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int hl = lane >> 5, col = lane & 31;
     const int j = find_block(offs, nb, k0);
     const int32_t* __restrict__ to = tr_off + static_cast<int64_t>(h) * (nb + 1);
@@ -482,6 +515,11 @@ attn_dkdv_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
             kb[s] = *reinterpret_cast<const u32x4_t*>(kp + 16 * s + 8 * hl);
             vb[s] = *reinterpret_cast<const u32x4_t*>(vp + 16 * s + 8 * hl);
         }
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            settle(kb[s]);
+            settle(vb[s]);
+        }
     }
     f32x16_t ak[DM], av[DM];
 #pragma unroll
@@ -492,14 +530,21 @@ attn_dkdv_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
     const uint16_t* __restrict__ oh_ = dout + h * hs;
     const float* __restrict__ lh = lse + static_cast<int64_t>(h) * N;
     const float* __restrict__ dh = Dq + static_cast<int64_t>(h) * N;
-    TileCursor cur;
-    cur.init(ti, offs, e0, e1);
-    for (int t = cur.next(); t >= 0; t = cur.next()) {
-        __syncthreads();
-        stage2<D>(sm.t, qh_, oh_, ld, t);
-        if (threadIdx.x < 64) sm.l2[threadIdx.x] = lh[t + threadIdx.x] * kLog2e;
-        else sm.dd[threadIdx.x - 64] = dh[t + threadIdx.x - 64];
-        __syncthreads();
+
+    TileDma<D, 2> dma;
+    dma.init(ld, wave, lane);
+    const uint32_t loff = 4 * lane;
+    auto issue = [&](int t, int b) {
+        dma.load(qbuf[b], qh_ + static_cast<int64_t>(t) * ld, wave);
+        dma.load(obuf[b], oh_ + static_cast<int64_t>(t) * ld, wave);
+        if (wave == 0) dma4(lh + t, loff, lds_addr(lbuf[b]));
+        else dma4(dh + t, loff, lds_addr(dbuf[b]));
+    };
+    auto compute = [&](int b) {
+        const uint16_t* qt = qbuf[b];
+        const uint16_t* ot = obuf[b];
+        const float* lt = lbuf[b];
+        const float* dt = dbuf[b];
         f32x16_t sa[2], pa[2];
 #pragma unroll
         for (int mr = 0; mr < 2; ++mr)
@@ -509,21 +554,22 @@ attn_dkdv_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
         for (int s = 0; s < KS; ++s)
 #pragma unroll
             for (int mr = 0; mr < 2; ++mr) {
-                sa[mr] = mfma32(lds_read16(&sm.t.a[32 * mr + col][16 * s + 8 * hl]), kb[s], sa[mr]);
-                pa[mr] = mfma32(lds_read16(&sm.t.b[32 * mr + col][16 * s + 8 * hl]), vb[s], pa[mr]);
+                sa[mr] = mfma32(sw_read16<D>(qt, 32 * mr + col, 16 * s + 8 * hl), kb[s], sa[mr]);
+                pa[mr] = mfma32(sw_read16<D>(ot, 32 * mr + col, 16 * s + 8 * hl), vb[s], pa[mr]);
             }
+        sched_reads_ahead<4, 4, KS, 2>();
         // register x of row tile mr holds query row 32*mr + 8*(x/4) + 4*hl + x%4
 #pragma unroll
         for (int mr = 0; mr < 2; ++mr)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const float4 l4 = *reinterpret_cast<const float4*>(&sm.l2[32 * mr + 8 * g + 4 * hl]);
-                const float4 d4 = *reinterpret_cast<const float4*>(&sm.dd[32 * mr + 8 * g + 4 * hl]);
+                const float4 l4 = *reinterpret_cast<const float4*>(&lt[32 * mr + 8 * g + 4 * hl]);
+                const float4 d4 = *reinterpret_cast<const float4*>(&dt[32 * mr + 8 * g + 4 * hl]);
                 const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
                 const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const float p = fast_exp2(fmaf(sa[mr][4 * g + r], scale_log2, -lv[r]));
+                    const float p = fast_exp2(fmaf(sa[mr][4 * g + r], scale_log2, -lv[r] * kLog2e));
                     sa[mr][4 * g + r] = p;
                     pa[mr][4 * g + r] = p * (pa[mr][4 * g + r] - dv4[r]);   // dS
                 }
@@ -534,11 +580,15 @@ attn_dkdv_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
             const u32x4_t bs = pack_kstep(pa[ks >> 1], ks & 1);
 #pragma unroll
             for (int m = 0; m < DM; ++m) {
-                av[m] = mfma32(tr_operand<NS>(&sm.t.b[0][0], 16 * ks, 32 * m, lane), bp, av[m]);
-                ak[m] = mfma32(tr_operand<NS>(&sm.t.a[0][0], 16 * ks, 32 * m, lane), bs, ak[m]);
+                av[m] = mfma32(tr_operand<D>(ot, 16 * ks, 32 * m, lane), bp, av[m]);
+                ak[m] = mfma32(tr_operand<D>(qt, 16 * ks, 32 * m, lane), bs, ak[m]);
             }
         }
-    }
+    };
+
+    TileCursor cur;
+    cur.init(ti, offs, e0, e1);
+    tile_pipeline(cur, issue, compute);
     uint16_t* ko = dk + key * ld + h * hs;
     uint16_t* vo = dv + key * ld + h * hs;
 #pragma unroll
@@ -546,12 +596,12 @@ attn_dkdv_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
             const f32x16_t& a = ak[m];
-            const f32x16_t& b = av[m];
+            const f32x16_t& c = av[m];
             const int dcol = 32 * m + 8 * g + 4 * hl;
             *reinterpret_cast<u32x2_t*>(ko + dcol) =
                 u32x2_t{pack2(a[4 * g] * scale, a[4 * g + 1] * scale), pack2(a[4 * g + 2] * scale, a[4 * g + 3] * scale)};
             *reinterpret_cast<u32x2_t*>(vo + dcol) =
-                u32x2_t{pack2(b[4 * g], b[4 * g + 1]), pack2(b[4 * g + 2], b[4 * g + 3])};
+                u32x2_t{pack2(c[4 * g], c[4 * g + 1]), pack2(c[4 * g + 2], c[4 * g + 3])};
         }
 }
 
@@ -567,10 +617,10 @@ hipError_t launch_attn_fwd_mfma(const void* q, const void* k, const void* v, voi
     const uint16_t* V = static_cast<const uint16_t*>(v);
     uint16_t* O = static_cast<uint16_t*>(o);
     if (d == 128)
-        hipLaunchKernelGGL(attn_fwd_mfma_kernel<128>, grid, dim3(256), 0, s, Q, K, V, O, lse, N, ld, hs, offs, nb, so,
+        hipLaunchKernelGGL(attn_fwd_mfma_kernel<128>, grid, dim3(128), 0, s, Q, K, V, O, lse, N, ld, hs, offs, nb, so,
                            si, cap, sl2);
     else
-        hipLaunchKernelGGL(attn_fwd_mfma_kernel<64>, grid, dim3(256), 0, s, Q, K, V, O, lse, N, ld, hs, offs, nb, so,
+        hipLaunchKernelGGL(attn_fwd_mfma_kernel<64>, grid, dim3(128), 0, s, Q, K, V, O, lse, N, ld, hs, offs, nb, so,
                            si, cap, sl2);
     return hipGetLastError();
 }
