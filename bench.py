@@ -1,6 +1,7 @@
 """Benchmark of the Prism dynamic block-sparse attention hot path on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--config 2k] [--no-cpu-baseline]
+    python bench.py --profile profiles     # rocprofv3 passes -> text summaries
 
 One step is one pass of the whole hot path over one batch of synthetic input
 resident in HBM: zone statistics and shapes, block-major permutation of Q, K,
@@ -15,9 +16,14 @@ only), divided by the step time.  Prints one JSON line.
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import math
 import os
+import re
+import subprocess
 import sys
 import time
 
@@ -30,6 +36,12 @@ sys.path.insert(0, ROOT)
 METRIC = "effective sparse-attn TFLOP/s fwd+bwd at 2K tokens; % of bf16 MFMA peak"
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
+CSRC = os.path.join(ROOT, "dynamic_block_sparse_amd", "csrc")
+# kernels launched by one prism_sparse_attn_bwd call (csr_scan also runs in prism_select)
+BWD_KERNELS = ("attn_bwd_dot_kernel", "tr_count_kernel", "csr_scan_kernel", "tr_fill_kernel", "tr_sort_kernel",
+               "attn_dq_mfma_kernel", "attn_dkdv_mfma_kernel")
+PMC_REGEX = "attn_|permute_rows|tr_count|tr_fill|tr_sort|csr_scan"
+ATTN_REGEX = "attn_(fwd|dq|dkdv)_mfma"
 
 
 def parse():
@@ -40,7 +52,39 @@ def parse():
     ap.add_argument("--config", default="2k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--profile", metavar="DIR", help="run the rocprofv3 passes and write summaries into DIR")
     return ap.parse_args()
+
+
+def source_hash():
+    """sha256 over the HIP/C++ sources: a counter summary is only used while it matches."""
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(CSRC, "*"))):
+        if f.endswith((".hip", ".cpp", ".hpp", ".h")):
+            h.update(os.path.basename(f).encode())
+            with open(f, "rb") as fh:
+                h.update(fh.read())
+    return h.hexdigest()
+
+
+def traffic_file(cfg_name):
+    return os.path.join(ROOT, "profiles", f"attn_bwd_{cfg_name}_traffic.txt")
+
+
+def read_traffic(cfg_name):
+    """HBM-side bytes per backward call from the committed counter summary, or
+    None when there is none or the kernels changed since it was taken."""
+    f = traffic_file(cfg_name)
+    if not os.path.exists(f):
+        return None
+    kv = {}
+    for line in open(f):
+        m = re.match(r"^([a-z0-9_]+):\s*(\S+)", line)
+        if m:
+            kv[m.group(1)] = m.group(2)
+    if kv.get("source_sha256") != source_hash() or "bytes_per_call" not in kv:
+        return None
+    return float(kv["bytes_per_call"])
 
 
 def effective_flops(path, sels, d):
@@ -98,8 +142,164 @@ def cpu_baseline(cfg, x, zone_shape_host, budget_s):
                       f"in seeded random order ({dt:.1f} s)"}
 
 
+def _run(cmd, log, limit):
+    print("[profile] " + " ".join(cmd), file=sys.stderr, flush=True)
+    with open(log, "w") as fh:
+        r = subprocess.run(cmd, stdout=fh, stderr=subprocess.STDOUT, timeout=limit)
+    if r.returncode != 0:
+        sys.exit(f"[profile] failed with status {r.returncode}; see {log}")
+    return [l for l in open(log) if l.startswith("{")]
+
+
+def _counter_rows(root):
+    rows = []
+    for f in glob.glob(os.path.join(root, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            rows += list(csv.DictReader(fh))
+    per = {}
+    for r in rows:
+        key = (int(r["Dispatch_Id"]), r["Kernel_Name"])
+        per[key] = per.get(key, 0.0) + float(r["Counter_Value"] or 0)
+    return sorted(per.items())
+
+
+def _short(name):
+    return re.sub(r"\(.*", "", name).replace("void ", "").replace("prism::", "")
+
+
+def profile(args):
+    """rocprofv3 passes over this bench (kernel trace, FETCH_SIZE, WRITE_SIZE),
+    summarised as text.  The GPU is only used by the child processes."""
+    out = args.profile
+    os.makedirs(out, exist_ok=True)
+    raw = os.path.join(ROOT, "gpurun_out", "profile_raw")
+    os.makedirs(raw, exist_ok=True)
+    me = [sys.executable, "-u", os.path.abspath(__file__), "--config", args.config, "--no-cpu-baseline"]
+    rel = lambda p: os.path.relpath(p, ROOT)
+
+    def cmd_for(prof, steps, warmup):
+        run = ["--steps", str(steps), "--warmup", str(warmup)]
+        return prof + ["--"] + me + run, " ".join(prof + ["--", "python", "bench.py", "--config", args.config,
+                                                         "--no-cpu-baseline"] + run)
+
+    tdir = os.path.join(raw, "trace")
+    tcmd, tshow = cmd_for(["rocprofv3", "--kernel-trace", "--stats", "--output-format", "csv", "-d", tdir, "-o",
+                           "trace"], 3, 1)
+    tshow = tshow.replace(tdir, rel(tdir))
+    lines = _run(tcmd, os.path.join(raw, "trace.log"), 600)
+    bench_line = json.loads(lines[-1]) if lines else {}
+    stats = glob.glob(os.path.join(raw, "trace", "**", "*kernel_stats.csv"), recursive=True)
+    rows = list(csv.DictReader(open(stats[0])))
+    avg = {_short(r["Name"]): float(r["AverageNs"]) for r in rows}
+    fwd_ns = sum(v for k, v in avg.items() if k.startswith("attn_fwd_mfma_kernel"))
+    bwd_ns = sum(v for k, v in avg.items() if k.split("<")[0] in BWD_KERNELS)
+    with open(os.path.join(out, f"attn_{args.config}_kernel_stats.txt"), "w") as fh:
+        fh.write(f"# rocprofv3 kernel statistics, {args.config} workload, 4 steps (1 warm-up)\n")
+        fh.write("# command: " + tshow + "\n")
+        fh.write(f"# made by: python bench.py --profile {out} --config {args.config}\n\n")
+        fh.write(f"{'kernel':62s} {'calls':>6s} {'avg_ms':>10s} {'total_ms':>10s} {'pct':>6s}\n")
+        other = [0, 0.0, 0.0]
+        for r in rows:
+            name = _short(r["Name"])
+            if not name.strip() or name.startswith(("at::", "rocprim::", "__amd_rocclr")):
+                other[0] += int(r["Calls"])
+                other[1] += float(r["TotalDurationNs"])
+                other[2] += float(r["Percentage"])
+                continue
+            fh.write(f"{name[:62]:62s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e6:10.3f} "
+                     f"{float(r['TotalDurationNs']) / 1e6:10.3f} {float(r['Percentage']):6.2f}\n")
+        fh.write(f"{'other (torch: synthetic inputs and bookkeeping, outside the timed path)':62s} {other[0]:6d} "
+                 f"{'':>10s} {other[1] / 1e6:10.3f} {other[2]:6.2f}\n")
+        fh.write(f"\nprism_sparse_attn_fwd call (sum of its kernels' average durations): {fwd_ns / 1e6:.3f} ms\n")
+        fh.write(f"prism_sparse_attn_bwd call (sum of its kernels' average durations): {bwd_ns / 1e6:.3f} ms\n")
+        if bench_line:
+            fh.write(f"bench stage_ms of the same run (HIP events): {json.dumps(bench_line.get('stage_ms'))}\n")
+    # counters: one pass each
+    res = {}
+    pcmds = {}
+    for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
+        d = os.path.join(raw, ctr.lower())
+        cmd, show = cmd_for(["rocprofv3", "--pmc", ctr, "--kernel-include-regex", PMC_REGEX, "--output-format", "csv",
+                             "-d", d, "-o", ctr.lower()], 1, 0)
+        pcmds[ctr] = show.replace(d, rel(d)).replace(PMC_REGEX, "'" + PMC_REGEX + "'")
+        _run(cmd, d + ".log", 300)
+        res[ctr] = _counter_rows(d)
+    import workloads.synth as synth
+    cfg = synth.CONFIGS[args.config]
+    es = 2 if cfg.dtype == "bf16" else 4
+    copy_bytes = cfg.N * cfg.d * es          # one permute launch reads and writes one head of one tensor
+    scale = {}
+    for ctr, rows_ in res.items():
+        vals = [v for (_, k), v in rows_ if "permute_rows" in k]
+        scale[ctr] = copy_bytes / (1024.0 * (sum(vals) / len(vals)))
+    # the backward call: the dispatches from attn_bwd_dot through attn_dkdv
+    per_call = {}
+    for ctr, rows_ in res.items():
+        seq = [(k, v) for (_, k), v in rows_]
+        start = max(i for i, (k, _) in enumerate(seq) if "attn_bwd_dot" in k)
+        end = max(i for i, (k, _) in enumerate(seq) if "attn_dkdv" in k)
+        per_call[ctr] = [(_short(k), v) for k, v in seq[start:end + 1]]
+    fetch = sum(v for _, v in per_call["FETCH_SIZE"]) * 1024 * scale["FETCH_SIZE"]
+    write = sum(v for _, v in per_call["WRITE_SIZE"]) * 1024 * scale["WRITE_SIZE"]
+    with open(os.path.join(out, f"attn_bwd_{args.config}_traffic.txt"), "w") as fh:
+        fh.write(f"# HBM-side traffic of one prism_sparse_attn_bwd call, {args.config} workload, from rocprofv3 counters\n")
+        for ctr, show in pcmds.items():
+            fh.write(f"# {ctr} pass: {show}\n")
+        fh.write(f"# made by: python bench.py --profile {out} --config {args.config}\n")
+        fh.write(f"# calibration: a permute launch moves {copy_bytes} bytes each way; the counters (KiB per\n"
+                 f"# dispatch) are scaled by algorithmic/counted on that copy kernel\n\n")
+        for ctr in res:
+            fh.write(f"scale_{ctr.lower()}: {scale[ctr]:.4f}\n")
+        for ctr, items in per_call.items():
+            for k, v in items:
+                fh.write(f"  {ctr} {k}: {v:.0f} KiB\n")
+        fh.write(f"fetch_bytes_per_call: {fetch:.6g}\n")
+        fh.write(f"write_bytes_per_call: {write:.6g}\n")
+        fh.write(f"bytes_per_call: {fetch + write:.6g}\n")
+        fh.write(f"source_sha256: {source_hash()}\n")
+    # utilisation counters of the attention kernels, one pass per counter group
+    groups = {"mfma_lds": ["MfmaUtil", "SQ_LDS_BANK_CONFLICT", "SQ_INSTS_LDS", "SQ_WAIT_INST_LDS"],
+              "waits": ["SQ_WAVE_CYCLES", "SQ_WAIT_ANY", "SQ_ACTIVE_INST_ANY", "SQ_BUSY_CYCLES"],
+              "l2": ["TCC_HIT_sum", "TCC_MISS_sum"]}
+    vals, shows = {}, {}
+    for g, ctrs in groups.items():
+        d = os.path.join(raw, g)
+        cmd, show = cmd_for(["rocprofv3", "--pmc"] + ctrs + ["--kernel-include-regex", ATTN_REGEX, "--output-format",
+                                                              "csv", "-d", d, "-o", g], 1, 0)
+        shows[g] = show.replace(d, rel(d)).replace(ATTN_REGEX, "'" + ATTN_REGEX + "'")
+        _run(cmd, d + ".log", 300)
+        rows = []
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            with open(f) as fh:
+                rows += list(csv.DictReader(fh))
+        for r in rows:
+            key = (_short(r["Kernel_Name"]), r["Counter_Name"])
+            vals.setdefault(key, {}).setdefault(r["Dispatch_Id"], 0.0)
+            vals[key][r["Dispatch_Id"]] += float(r["Counter_Value"] or 0)
+    with open(os.path.join(out, f"attn_{args.config}_counters.txt"), "w") as fh:
+        fh.write(f"# rocprofv3 counters of the attention kernels, {args.config} workload, one step\n")
+        for g, show in shows.items():
+            fh.write(f"# {g} pass: {show}\n")
+        fh.write(f"# made by: python bench.py --profile {out} --config {args.config}\n\n")
+        kernels = sorted({k for k, _ in vals})
+        for k in kernels:
+            m = {c: sum(v.values()) / len(v) for (kk, c), v in vals.items() if kk == k}
+            fh.write(f"{k}\n")
+            for c in sorted(m):
+                fh.write(f"  {c}: {m[c]:.6g}\n")
+            if m.get("SQ_WAVE_CYCLES"):
+                fh.write(f"  wait share (SQ_WAIT_ANY / SQ_WAVE_CYCLES): {m['SQ_WAIT_ANY'] / m['SQ_WAVE_CYCLES']:.3f}\n")
+            if m.get("TCC_HIT_sum") is not None and m.get("TCC_MISS_sum") is not None:
+                hr = m["TCC_HIT_sum"] / max(1.0, m["TCC_HIT_sum"] + m["TCC_MISS_sum"])
+                fh.write(f"  L2 hit rate: {hr:.3f}\n")
+    print(f"[profile] wrote summaries into {out}", file=sys.stderr, flush=True)
+
+
 def main():
     args = parse()
+    if args.profile:
+        profile(args)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus above 1 is not supported",
@@ -211,7 +411,15 @@ def main():
     roofline = {"kernel": "sparse attention backward (prism_sparse_attn_bwd)" if dom == "attn_bwd"
                 else "sparse attention forward (prism_sparse_attn_fwd)",
                 "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None}
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": read_traffic(cfg.name) if dom == "attn_bwd" else None}
+    # algorithmic bytes of the HBM-bound stages: V once plus the audio map (zone
+    # statistics), read + write of every permuted tensor, Q and K once (selection)
+    es = 2 if cfg.dtype == "bf16" else 4
+    ntens = 4 if cfg.backward else 3
+    alg = {"shapes": cfg.N * C * es + 4 * cfg.N, "permute_in": ntens * 2 * cfg.N * C * es,
+           "select": 2 * cfg.N * C * es, "permute_out": (4 if cfg.backward else 1) * 2 * cfg.N * C * es}
+    stage_gbs = {k: round(b / (stage_ms[k] * 1e-3) / 1e9, 1) for k, b in alg.items()}
     result = {
         "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_step, 3), "higher_is_better": True, "scaling": "weak",
@@ -226,6 +434,7 @@ def main():
         "attention_only_pct_of_bf16_peak": round(100 * attn_tflops / PEAK_BF16_TFLOPS, 3),
         "effective_tflop_per_step": round(f_eff / 1e12, 4),
         "stage_ms": {s: round(v, 3) for s, v in stage_ms.items()},
+        "stage_gbs_algorithmic": stage_gbs,
         "roofline": roofline,
     }
     if not args.no_cpu_baseline:
