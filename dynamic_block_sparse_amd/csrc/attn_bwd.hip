@@ -1,0 +1,280 @@
+// attn_bwd.hip - gradient of the block-sparse flash attention on gfx950 bf16 MFMA.
+//
+// Built with the default accumulator-register form of MFMA (see build.py):
+// the dK/dV kernel needs more than 256 registers, and the VGPR form measured
+// 9% slower here.
+#include "attn_common.hpp"
+
+namespace prism {
+
+// ---------------------------------------------------------------- backward
+//
+// dQ kernel (query-major): 2 waves per 64-row query tile, wave w owns rows
+// 32*w .. +31 and streams every selected 64-key tile:
+//   S^T = K Q^T, P^T = exp2(S^T - lse), dP^T = V dO^T, dS^T = P^T (dP^T - D),
+//   dQ^T += K^T dS^T
+// dK/dV kernel (key-major): 2 waves per 64-key tile, wave w owns keys
+// 32*w .. +31 and streams the 64-row tiles of every query block that selected
+// the tile's block (transposed CSR, ascending):
+//   S = Q K^T, P = exp2(S - lse), dP = dO V^T, dS = P (dP - D),
+//   dV^T += dO^T P, dK^T += Q^T dS
+// Each output element is accumulated by one lane in a fixed order: the
+// backward is deterministic.
+
+template <int D>
+__global__ void __launch_bounds__(128, 1)
+attn_dq_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+                    const uint16_t* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ Dq,
+                    uint16_t* __restrict__ dq, int64_t N, int64_t ld, int64_t hs, const int32_t* __restrict__ offs,
+                    int nb, const int32_t* __restrict__ sel_off, const int32_t* __restrict__ sel_idx, int64_t cap,
+                    float scale_log2, float scale) {
+    __shared__ uint16_t kbuf[2][64 * D], vbuf[2][64 * D];
+    const int ntiles = static_cast<int>(N / 64);
+    const int wg = xcd_remap(blockIdx.x);
+    const int h = wg / ntiles;
+    const int64_t p0 = static_cast<int64_t>(wg % ntiles) * 64;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int hl = lane >> 5, col = lane & 31;
+    const int i = find_block(offs, nb, p0);
+    const int32_t* __restrict__ so = sel_off + static_cast<int64_t>(h) * (nb + 1);
+    const int32_t* __restrict__ si = sel_idx + static_cast<int64_t>(h) * cap;
+    const int e0 = so[i];
+    const int e1 = static_cast<int>(min(static_cast<int64_t>(so[i + 1]), cap));
+    constexpr int KS = D / 16, DM = D / 32;
+    const int64_t row = p0 + 32 * wave + col;
+    u32x4_t qb[KS], db[KS];
+    {
+        const uint16_t* qr = q + row * ld + h * hs;
+        const uint16_t* dr = dout + row * ld + h * hs;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            qb[s] = *reinterpret_cast<const u32x4_t*>(qr + 16 * s + 8 * hl);
+            db[s] = *reinterpret_cast<const u32x4_t*>(dr + 16 * s + 8 * hl);
+        }
+    }
+    const float lrow = lse[static_cast<int64_t>(h) * N + row] * kLog2e;
+    const float drow = Dq[static_cast<int64_t>(h) * N + row];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+        settle(qb[s]);
+        settle(db[s]);
+    }
+    settle(lrow);
+    settle(drow);
+    f32x16_t acc[DM];
+#pragma unroll
+    for (int m = 0; m < DM; ++m)
+#pragma unroll
+        for (int x = 0; x < 16; ++x) acc[m][x] = 0.0f;
+    const uint16_t* __restrict__ kh_ = k + h * hs;
+    const uint16_t* __restrict__ vh_ = v + h * hs;
+
+    TileDma<D, 2> dma;
+    dma.init(ld, wave, lane);
+    auto issue = [&](int t, int b) {
+        dma.load(kbuf[b], kh_ + static_cast<int64_t>(t) * ld, wave);
+        dma.load(vbuf[b], vh_ + static_cast<int64_t>(t) * ld, wave);
+    };
+    auto compute = [&](int b) {
+        const uint16_t* kt = kbuf[b];
+        const uint16_t* vt = vbuf[b];
+        f32x16_t sa[2], pa[2];
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int x = 0; x < 16; ++x) sa[mt][x] = pa[mt][x] = 0.0f;
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt) {
+                sa[mt] = mfma32(sw_read16<D>(kt, 32 * mt + col, 16 * s + 8 * hl), qb[s], sa[mt]);
+                pa[mt] = mfma32(sw_read16<D>(vt, 32 * mt + col, 16 * s + 8 * hl), db[s], pa[mt]);
+            }
+        sched_reads_ahead<4, 4, KS, 2>();
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int x = 0; x < 16; ++x) {
+                const float p = fast_exp2(fmaf(sa[mt][x], scale_log2, -lrow));
+                sa[mt][x] = p * (pa[mt][x] - drow);     // dS^T
+            }
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const u32x4_t bs = pack_kstep(sa[ks >> 1], ks & 1);
+#pragma unroll
+            for (int m = 0; m < DM; ++m) acc[m] = mfma32(tr_operand<D>(kt, 16 * ks, 32 * m, lane), bs, acc[m]);
+        }
+    };
+
+    TileCursor cur;
+    cur.init(si, offs, e0, e1);
+    tile_pipeline(cur, issue, compute);
+    uint16_t* out = dq + row * ld + h * hs;
+#pragma unroll
+    for (int m = 0; m < DM; ++m)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const f32x16_t& a = acc[m];
+            *reinterpret_cast<u32x2_t*>(out + 32 * m + 8 * g + 4 * hl) =
+                u32x2_t{pack2(a[4 * g] * scale, a[4 * g + 1] * scale), pack2(a[4 * g + 2] * scale, a[4 * g + 3] * scale)};
+        }
+}
+
+template <int D>
+__global__ void __launch_bounds__(128)
+attn_dkdv_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+                      const uint16_t* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ Dq,
+                      uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, int64_t N, int64_t ld, int64_t hs,
+                      const int32_t* __restrict__ offs, int nb, const int32_t* __restrict__ tr_off,
+                      const int32_t* __restrict__ tr_idx, int64_t cap, float scale_log2, float scale) {
+    // Q and dO tiles, lse (natural log) and D = rowsum(dO * O) of their rows
+    __shared__ uint16_t qbuf[2][64 * D], obuf[2][64 * D];
+    __shared__ float lbuf[2][64], dbuf[2][64];
+    const int ntiles = static_cast<int>(N / 64);
+    const int wg = xcd_remap(blockIdx.x);
+    const int h = wg / ntiles;
+    const int64_t k0 = static_cast<int64_t>(wg % ntiles) * 64;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int hl = lane >> 5, col = lane & 31;
+    const int j = find_block(offs, nb, k0);
+    const int32_t* __restrict__ to = tr_off + static_cast<int64_t>(h) * (nb + 1);
+    const int32_t* __restrict__ ti = tr_idx + static_cast<int64_t>(h) * cap;
+    const int e0 = to[j];
+    const int e1 = static_cast<int>(min(static_cast<int64_t>(to[j + 1]), cap));
+    constexpr int KS = D / 16, DM = D / 32;
+    const int64_t key = k0 + 32 * wave + col;
+    u32x4_t kb[KS], vb[KS];
+    {
+        const uint16_t* kp = k + key * ld + h * hs;
+        const uint16_t* vp = v + key * ld + h * hs;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            kb[s] = *reinterpret_cast<const u32x4_t*>(kp + 16 * s + 8 * hl);
+            vb[s] = *reinterpret_cast<const u32x4_t*>(vp + 16 * s + 8 * hl);
+        }
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            settle(kb[s]);
+            settle(vb[s]);
+        }
+    }
+    f32x16_t ak[DM], av[DM];
+#pragma unroll
+    for (int m = 0; m < DM; ++m)
+#pragma unroll
+        for (int x = 0; x < 16; ++x) ak[m][x] = av[m][x] = 0.0f;
+    const uint16_t* __restrict__ qh_ = q + h * hs;
+    const uint16_t* __restrict__ oh_ = dout + h * hs;
+    const float* __restrict__ lh = lse + static_cast<int64_t>(h) * N;
+    const float* __restrict__ dh = Dq + static_cast<int64_t>(h) * N;
+
+    TileDma<D, 2> dma;
+    dma.init(ld, wave, lane);
+    const uint32_t loff = 4 * lane;
+    auto issue = [&](int t, int b) {
+        dma.load(qbuf[b], qh_ + static_cast<int64_t>(t) * ld, wave);
+        dma.load(obuf[b], oh_ + static_cast<int64_t>(t) * ld, wave);
+        if (wave == 0) dma4(lh + t, loff, lds_addr(lbuf[b]));
+        else dma4(dh + t, loff, lds_addr(dbuf[b]));
+    };
+    auto compute = [&](int b) {
+        const uint16_t* qt = qbuf[b];
+        const uint16_t* ot = obuf[b];
+        const float* lt = lbuf[b];
+        const float* dt = dbuf[b];
+        f32x16_t sa[2], pa[2];
+#pragma unroll
+        for (int mr = 0; mr < 2; ++mr)
+#pragma unroll
+            for (int x = 0; x < 16; ++x) sa[mr][x] = pa[mr][x] = 0.0f;
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+#pragma unroll
+            for (int mr = 0; mr < 2; ++mr) {
+                sa[mr] = mfma32(sw_read16<D>(qt, 32 * mr + col, 16 * s + 8 * hl), kb[s], sa[mr]);
+                pa[mr] = mfma32(sw_read16<D>(ot, 32 * mr + col, 16 * s + 8 * hl), vb[s], pa[mr]);
+            }
+        sched_reads_ahead<4, 4, KS, 2>();
+        // register x of row tile mr holds query row 32*mr + 8*(x/4) + 4*hl + x%4
+#pragma unroll
+        for (int mr = 0; mr < 2; ++mr)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const float4 l4 = *reinterpret_cast<const float4*>(&lt[32 * mr + 8 * g + 4 * hl]);
+                const float4 d4 = *reinterpret_cast<const float4*>(&dt[32 * mr + 8 * g + 4 * hl]);
+                const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+                const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float p = fast_exp2(fmaf(sa[mr][4 * g + r], scale_log2, -lv[r] * kLog2e));
+                    sa[mr][4 * g + r] = p;
+                    pa[mr][4 * g + r] = p * (pa[mr][4 * g + r] - dv4[r]);   // dS
+                }
+            }
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const u32x4_t bp = pack_kstep(sa[ks >> 1], ks & 1);
+            const u32x4_t bs = pack_kstep(pa[ks >> 1], ks & 1);
+#pragma unroll
+            for (int m = 0; m < DM; ++m) {
+                av[m] = mfma32(tr_operand<D>(ot, 16 * ks, 32 * m, lane), bp, av[m]);
+                ak[m] = mfma32(tr_operand<D>(qt, 16 * ks, 32 * m, lane), bs, ak[m]);
+            }
+        }
+    };
+
+    TileCursor cur;
+    cur.init(ti, offs, e0, e1);
+    tile_pipeline(cur, issue, compute);
+    uint16_t* ko = dk + key * ld + h * hs;
+    uint16_t* vo = dv + key * ld + h * hs;
+#pragma unroll
+    for (int m = 0; m < DM; ++m)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const f32x16_t& a = ak[m];
+            const f32x16_t& c = av[m];
+            const int dcol = 32 * m + 8 * g + 4 * hl;
+            *reinterpret_cast<u32x2_t*>(ko + dcol) =
+                u32x2_t{pack2(a[4 * g] * scale, a[4 * g + 1] * scale), pack2(a[4 * g + 2] * scale, a[4 * g + 3] * scale)};
+            *reinterpret_cast<u32x2_t*>(vo + dcol) =
+                u32x2_t{pack2(c[4 * g], c[4 * g + 1]), pack2(c[4 * g + 2], c[4 * g + 3])};
+        }
+}
+
+// ---------------------------------------------------------------- launcher
+
+hipError_t launch_attn_bwd_mfma(const void* q, const void* k, const void* v, const void* dout, const float* lse,
+                                const float* Dq, void* dq, void* dk, void* dv, int64_t N, int heads, int d, int64_t ld,
+                                int64_t hs, const int32_t* offs, int nb, const int32_t* so, const int32_t* si,
+                                const int32_t* to, const int32_t* ti, int64_t cap, float scale, hipStream_t s) {
+    const dim3 grid(static_cast<unsigned>(N / 64 * heads));
+    const float sl2 = scale * kLog2e;
+    const uint16_t* Q = static_cast<const uint16_t*>(q);
+    const uint16_t* K = static_cast<const uint16_t*>(k);
+    const uint16_t* V = static_cast<const uint16_t*>(v);
+    const uint16_t* O = static_cast<const uint16_t*>(dout);
+    uint16_t* dQ = static_cast<uint16_t*>(dq);
+    uint16_t* dK = static_cast<uint16_t*>(dk);
+    uint16_t* dV = static_cast<uint16_t*>(dv);
+    if (d == 128) {
+        hipLaunchKernelGGL(attn_dq_mfma_kernel<128>, grid, dim3(128), 0, s, Q, K, V, O, lse, Dq, dQ, N, ld, hs, offs,
+                           nb, so, si, cap, sl2, scale);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(attn_dkdv_mfma_kernel<128>, grid, dim3(128), 0, s, Q, K, V, O, lse, Dq, dK, dV, N, ld, hs,
+                           offs, nb, to, ti, cap, sl2, scale);
+    } else {
+        hipLaunchKernelGGL(attn_dq_mfma_kernel<64>, grid, dim3(128), 0, s, Q, K, V, O, lse, Dq, dQ, N, ld, hs, offs,
+                           nb, so, si, cap, sl2, scale);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(attn_dkdv_mfma_kernel<64>, grid, dim3(128), 0, s, Q, K, V, O, lse, Dq, dK, dV, N, ld, hs,
+                           offs, nb, to, ti, cap, sl2, scale);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace prism
