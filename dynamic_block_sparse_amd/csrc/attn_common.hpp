@@ -45,8 +45,6 @@ typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 typedef short s16x4_t __attribute__((__vector_size__(8)));
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
-typedef __attribute__((address_space(1))) void gvoid_t;
-typedef __attribute__((address_space(3))) void lvoid_t;
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
@@ -124,27 +122,6 @@ __device__ __forceinline__ u32x4_t tr_operand(const uint16_t* tile, int base, in
     return u32x4_t{a.x, a.y, b.x, b.y};
 }
 
-// LDS byte address of a __shared__ object
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lvoid_t*)p));
-}
-
-// One direct global->LDS load: lane l fetches BYTES bytes at gbase + voff[l]
-// and they land at LDS address lds + BYTES * l.  It is written in asm so that
-// the compiler does not see an LDS store in flight: it would otherwise make
-// every later transposing LDS read wait for all outstanding loads, including
-// those into the other buffer.  Completion is awaited explicitly (dma_join)
-// before the buffer is read.  One wait state separates the M0 write from the
-// load that uses it.
-__device__ __forceinline__ void dma16(const void* gbase, uint32_t voff, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(gbase), "s"(lds)
-                 : "memory", "m0");
-}
-__device__ __forceinline__ void dma4(const void* gbase, uint32_t voff, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(gbase), "s"(lds)
-                 : "memory", "m0");
-}
-
 // Per-lane byte offsets for loading a 64-row tile (token stride ld elements)
 // into a swizzled LDS tile, shared by the NW waves of the workgroup: wave w
 // issues instructions w, w + NW, ...; one instruction fills 1 KB of LDS
@@ -179,12 +156,6 @@ struct TileDma {
 // not see) would make it wait for the next tile as well.
 __device__ __forceinline__ void settle(const u32x4_t& x) { asm volatile("" ::"v"(x)); }
 __device__ __forceinline__ void settle(float x) { asm volatile("" ::"v"(x)); }
-
-// wait for this wave's direct loads, then for every wave's
-__device__ __forceinline__ void dma_join() {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-}
 
 // Cursor over the 64-token tiles of a list of blocks (uniform across the workgroup).
 struct TileCursor {

@@ -119,4 +119,37 @@ __device__ __forceinline__ int64_t block_major_to_raster(int64_t p, const uint8_
     return (t * g.H + h) * g.W + w;
 }
 
+// ---------------------------------------------------------------- direct global->LDS loads
+
+typedef __attribute__((address_space(1))) void gvoid_t;
+typedef __attribute__((address_space(3))) void lvoid_t;
+
+// LDS byte address of a __shared__ object
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lvoid_t*)p));
+}
+
+// One direct global->LDS load: lane l fetches BYTES bytes at gbase + voff[l]
+// (voff an unsigned 32-bit byte offset) and they land at LDS address
+// lds + BYTES * l.  It is written in asm so that the compiler does not see an
+// LDS store in flight: it would otherwise make every later LDS read that it
+// cannot tell apart (the transposing reads in particular) wait for all
+// outstanding loads, including those into another buffer.  Completion is
+// awaited explicitly (dma_join) before the buffer is read.  One wait state
+// separates the M0 write from the load that uses it.
+__device__ __forceinline__ void dma16(const void* gbase, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(gbase), "s"(lds)
+                 : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const void* gbase, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(gbase), "s"(lds)
+                 : "memory", "m0");
+}
+
+// wait for this wave's direct loads, then for every wave's
+__device__ __forceinline__ void dma_join() {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+}
+
 }  // namespace prism

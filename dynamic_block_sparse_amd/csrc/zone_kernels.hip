@@ -5,12 +5,18 @@
 // volume thresholds and the log2 optimum).
 //
 // Three kernels:
-//   zone_profile_kernel  one workgroup per (zone, 512-channel slab): each thread
-//                        owns two channels, accumulates the 24 axis-slice sums
-//                        of its channels over the zone's 512 tokens in float64
-//                        (exact for bf16 input), turns them into the per-axis
-//                        variance of the slice means, and the workgroup sums
-//                        those over its channels in a fixed order.
+//   zone_profile_dma_kernel  one workgroup per (zone, 1 KB channel slab: 512
+//                        bf16 or 256 fp32 channels).  The slab of each token row
+//                        is loaded straight into LDS (16 bytes per lane, fully
+//                        coalesced, double-buffered chunks of 16 tokens); each
+//                        thread then owns two (bf16) or one (fp32) channels,
+//                        accumulates the 24 axis-slice sums of its channels
+//                        over the zone's 512 tokens in float64 (exact for bf16
+//                        input), turns them into the per-axis variance of the
+//                        slice means, and the workgroup sums those over its
+//                        channels in a fixed order.  zone_profile_kernel does
+//                        the same with direct 4-byte loads, for layouts the
+//                        16-byte loads cannot serve.
 //   zone_reduce_kernel   one workgroup per zone: sums the slab partials in slab
 //                        order, and builds the audio terms from the 512 values
 //                        of the norm map.
@@ -83,9 +89,11 @@ zone_profile_kernel(const TIn* __restrict__ v, int64_t C, int64_t ld, ZoneGrid g
 
     if (ok0) {
         const int64_t base = ((static_cast<int64_t>(zt) * 8 * g.H + zh * 8) * g.W + zw * 8);
-#pragma unroll
+        // rolled loops; the slice sums are picked by comparison, not by a
+        // runtime index (which would put them in scratch memory)
+#pragma unroll 1
         for (int it = 0; it < 8; ++it) {
-#pragma unroll
+#pragma unroll 1
             for (int ih = 0; ih < 8; ++ih) {
                 const TIn* row = v + (base + (static_cast<int64_t>(it) * g.H + ih) * g.W) * ld + c0;
                 double x[8][2];
@@ -114,8 +122,12 @@ zone_profile_kernel(const TIn* __restrict__ v, int64_t C, int64_t ld, ZoneGrid g
                         sW[iw][c] += x[iw][c];
                         rs += x[iw][c];
                     }
-                    sT[it][c] += rs;
-                    sH[ih][c] += rs;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i)
+                        if (i == it) sT[i][c] += rs;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i)
+                        if (i == ih) sH[i][c] += rs;
                 }
             }
         }
@@ -139,6 +151,113 @@ zone_profile_kernel(const TIn* __restrict__ v, int64_t C, int64_t ld, ZoneGrid g
 #pragma unroll
             for (int i = 0; i < 8; ++i) s += (m[i] - mu) * (m[i] - mu);
             var[d] += s / 8.0;
+        }
+    }
+#pragma unroll
+    for (int d = 0; d < 3; ++d) {
+        const double t = block_sum(var[d], red);
+        if (threadIdx.x == 0) partial[(static_cast<int64_t>(zone) * nslab + slab) * 3 + d] = t;
+    }
+}
+
+// Same result as zone_profile_kernel, with the slab staged through LDS.
+// Requires: C and ld multiples of 16 bytes' worth of elements, v 16-byte aligned.
+template <typename TIn>
+__global__ void __launch_bounds__(kProfThreads)
+zone_profile_dma_kernel(const TIn* __restrict__ v, int64_t C, int64_t ld, ZoneGrid g, int nslab,
+                        double* __restrict__ partial) {
+    constexpr int CH = 1024 / static_cast<int>(sizeof(TIn));   // channels per slab
+    constexpr int CPT = CH / kProfThreads;                      // channels per thread
+    constexpr int CHUNK = 16;                                   // tokens per staged chunk
+    constexpr int NCHUNK = kZoneTokens / CHUNK;
+    __shared__ __attribute__((aligned(16))) uint8_t buf[2][CHUNK * 1024];
+    __shared__ double red[kProfThreads / kWave];
+    const int zone = blockIdx.x;
+    const int slab = blockIdx.y;
+    const int zt = zone / (g.nH * g.nW);
+    const int zh = (zone / g.nW) % g.nH;
+    const int zw = zone % g.nW;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t zbase = (static_cast<int64_t>(zt) * 8 * g.H + zh * 8) * g.W + zw * 8;
+    const TIn* __restrict__ vs = v + static_cast<int64_t>(slab) * CH;
+    // lane l loads bytes 16 l .. 16 l + 15 of the slab; lanes past C load the
+    // slab's first 16 bytes again (always inside the row) and are ignored
+    const bool lane_ok = static_cast<int64_t>(slab) * CH + (16 / static_cast<int>(sizeof(TIn))) * lane < C;
+    const uint32_t loff = lane_ok ? 16u * lane : 0u;
+    // chunk k covers T-slice it = k / 4 and H-rows ih0, ih0 + 1 with ih0 = 2 (k % 4);
+    // wave w loads its tokens 4 w .. 4 w + 3 (token j: ih = ih0 + j / 8, iw = j % 8)
+    auto issue = [&](int k, int b) {
+        const int it = k >> 2, ih0 = (k & 3) * 2;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int j = 4 * wave + u;
+            const int64_t tok = zbase + (static_cast<int64_t>(it) * g.H + ih0 + (j >> 3)) * g.W + (j & 7);
+            dma16(vs + tok * ld, loff, lds_addr(buf[b] + j * 1024));
+        }
+    };
+    const int64_t c0 = static_cast<int64_t>(slab) * CH + CPT * threadIdx.x;
+
+    double sT[8][CPT], sH[8][CPT], sW[8][CPT];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) sT[i][c] = sH[i][c] = sW[i][c] = 0.0;
+
+    issue(0, 0);
+    dma_join();
+    for (int k = 0; k < NCHUNK; ++k) {
+        const int b = k & 1;
+        if (k + 1 < NCHUNK) issue(k + 1, b ^ 1);
+        const int it = k >> 2, ih0 = (k & 3) * 2;
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            const int ih = ih0 + r;
+            double x[8][CPT];
+#pragma unroll
+            for (int iw = 0; iw < 8; ++iw) {
+                const uint8_t* p = buf[b] + (8 * r + iw) * 1024 + CPT * sizeof(TIn) * threadIdx.x;
+                if constexpr (CPT == 2) {
+                    const uint32_t u = *reinterpret_cast<const uint32_t*>(p);
+                    x[iw][0] = static_cast<double>(bf16_to_f32(static_cast<uint16_t>(u & 0xFFFFu)));
+                    x[iw][1] = static_cast<double>(bf16_to_f32(static_cast<uint16_t>(u >> 16)));
+                } else {
+                    x[iw][0] = static_cast<double>(*reinterpret_cast<const float*>(p));
+                }
+            }
+#pragma unroll
+            for (int c = 0; c < CPT; ++c) {
+                double rs = 0.0;
+#pragma unroll
+                for (int iw = 0; iw < 8; ++iw) {
+                    sW[iw][c] += x[iw][c];
+                    rs += x[iw][c];
+                }
+                for (int i = 0; i < 8; ++i)
+                    if (i == it) sT[i][c] += rs;
+                for (int i = 0; i < 8; ++i)
+                    if (i == ih) sH[i][c] += rs;
+            }
+        }
+        dma_join();
+    }
+    double var[3] = {0.0, 0.0, 0.0};
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+        if (c0 + c >= C) continue;
+#pragma unroll
+        for (int d = 0; d < 3; ++d) {
+            double m[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) m[i] = (d == 0 ? sT[i][c] : d == 1 ? sH[i][c] : sW[i][c]) / 64.0;
+            double mu = 0.0;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) mu += m[i];
+            mu /= 8.0;
+            double s2 = 0.0;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) s2 += (m[i] - mu) * (m[i] - mu);
+            var[d] += s2 / 8.0;
         }
     }
 #pragma unroll
@@ -293,16 +412,32 @@ zone_decide_kernel(double* __restrict__ rec, int nZ, double tau128, double tau25
 hipError_t launch_zone_shapes(const void* v, bool bf16, int64_t C, int64_t ld, const float* a, ZoneGrid g, int nZ,
                               double tau128, double tau256, double eps, uint8_t* zone_shape, int32_t* block_offsets,
                               int32_t* nb_dev, double* partial, double* rec, hipStream_t s) {
-    const int nslab = static_cast<int>((C + kSlab - 1) / kSlab);
-    const dim3 grid(nZ, nslab);
-    if (bf16) {
-        const int vec_ok = ((C % 2) == 0) && ((ld % 2) == 0) && ((reinterpret_cast<uintptr_t>(v) & 3) == 0);
-        hipLaunchKernelGGL(zone_profile_kernel<uint16_t>, grid, dim3(kProfThreads), 0, s,
-                           static_cast<const uint16_t*>(v), C, ld, g, nslab, partial, vec_ok);
+    const uintptr_t va = reinterpret_cast<uintptr_t>(v);
+    const int64_t vec = bf16 ? 8 : 4;   // elements per 16 bytes
+    const bool dma_ok = (C % vec) == 0 && (ld % vec) == 0 && (va & 15) == 0;
+    int nslab;
+    if (dma_ok) {
+        const int64_t ch = bf16 ? 512 : 256;
+        nslab = static_cast<int>((C + ch - 1) / ch);
+        const dim3 grid(nZ, nslab);
+        if (bf16)
+            hipLaunchKernelGGL(zone_profile_dma_kernel<uint16_t>, grid, dim3(kProfThreads), 0, s,
+                               static_cast<const uint16_t*>(v), C, ld, g, nslab, partial);
+        else
+            hipLaunchKernelGGL(zone_profile_dma_kernel<float>, grid, dim3(kProfThreads), 0, s,
+                               static_cast<const float*>(v), C, ld, g, nslab, partial);
     } else {
-        const int vec_ok = ((C % 2) == 0) && ((ld % 2) == 0) && ((reinterpret_cast<uintptr_t>(v) & 7) == 0);
-        hipLaunchKernelGGL(zone_profile_kernel<float>, grid, dim3(kProfThreads), 0, s, static_cast<const float*>(v),
-                           C, ld, g, nslab, partial, vec_ok);
+        nslab = static_cast<int>((C + kSlab - 1) / kSlab);
+        const dim3 grid(nZ, nslab);
+        if (bf16) {
+            const int vec_ok = ((C % 2) == 0) && ((ld % 2) == 0) && ((va & 3) == 0);
+            hipLaunchKernelGGL(zone_profile_kernel<uint16_t>, grid, dim3(kProfThreads), 0, s,
+                               static_cast<const uint16_t*>(v), C, ld, g, nslab, partial, vec_ok);
+        } else {
+            const int vec_ok = ((C % 2) == 0) && ((ld % 2) == 0) && ((va & 7) == 0);
+            hipLaunchKernelGGL(zone_profile_kernel<float>, grid, dim3(kProfThreads), 0, s,
+                               static_cast<const float*>(v), C, ld, g, nslab, partial, vec_ok);
+        }
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -314,8 +449,9 @@ hipError_t launch_zone_shapes(const void* v, bool bf16, int64_t C, int64_t ld, c
     return hipGetLastError();
 }
 
+// enough for either slab size (256 fp32 channels is the smallest)
 size_t zone_partial_doubles(int nZ, int64_t C) {
-    return static_cast<size_t>(nZ) * static_cast<size_t>((C + kSlab - 1) / kSlab) * 3;
+    return static_cast<size_t>(nZ) * static_cast<size_t>((C + 255) / 256) * 3;
 }
 
 }  // namespace prism

@@ -180,6 +180,36 @@ def test_small_determinism():
                            b.view(torch.uint8) if b.dtype != torch.int32 else b)
 
 
+@pytest.mark.parametrize("idx", [0, 1], ids=["f32", "bf16"])
+def test_zone_statistics_both_load_paths(idx):
+    """The zone statistics kernel loads V rows with 16-byte direct LDS loads when
+    C and the token stride allow it, and with 4-byte loads otherwise (here a
+    token stride of C + 2 elements).  Both must give the oracle's decisions."""
+    cfg = SMALL[idx]
+    print(f"case {cfg.name}", flush=True)
+    x = make_inputs(cfg, device="cuda", tensors=("v",))
+    C = cfg.heads * cfg.d
+    v2 = x["v"].reshape(cfg.N, C)
+    wide = torch.zeros((cfg.N, C + 2), dtype=v2.dtype, device="cuda")
+    wide[:, :C] = v2
+    zs = orc.zone_shapes(_np(v2), _np(x["a"]), cfg.T, cfg.H, cfg.W)
+    recs = []
+    for v in (v2, wide[:, :C]):
+        path = _path(cfg)
+        path.shapes(v, x["a"])
+        torch.cuda.synchronize()
+        assert path.nb == zs["NB"]
+        np.testing.assert_array_equal(path.zone_shape.cpu().numpy(), zs["shape"])
+        np.testing.assert_array_equal(path.block_offsets[:path.nb + 1].cpu().numpy(), zs["block_offsets"])
+        rec = path.zone_stats.cpu().numpy().reshape(-1, 16)
+        np.testing.assert_allclose(rec[:, 0:3], zs["sigma2_v"], rtol=1e-12, atol=1e-300)
+        np.testing.assert_allclose(rec[:, 3:6], zs["r"], rtol=1e-12, atol=1e-15)
+        recs.append(rec)
+    if cfg.dtype == "bf16":
+        # same slab split and the same exact sums: bitwise equal
+        np.testing.assert_array_equal(recs[0], recs[1])
+
+
 def test_permutation_round_trip_with_strided_rows():
     cfg = SMALL[1]
     x = make_inputs(cfg, device="cuda")
