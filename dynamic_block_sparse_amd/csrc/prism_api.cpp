@@ -118,6 +118,9 @@ prism_status check_tokens(prism_dtype dt, int64_t N, int32_t heads, int32_t d, i
     const int64_t vec = 16 / elem_bytes(dt);
     if (ld % vec || hs % vec)
         return fail(PRISM_E_UNSUPPORTED, "strides must be multiples of %lld elements", static_cast<long long>(vec));
+    if (ld * 64 * elem_bytes(dt) >= (int64_t{1} << 32))
+        return fail(PRISM_E_UNSUPPORTED, "ld = %lld too large: 64 rows must span less than 4 GiB",
+                    static_cast<long long>(ld));
     if (nb <= 0 || static_cast<int64_t>(nb) * 64 > N)
         return fail(PRISM_E_ARG, "nb = %d out of range for N = %lld", nb, static_cast<long long>(N));
     if (nb > 32768) return fail(PRISM_E_UNSUPPORTED, "nb = %d above the 32768-block limit", nb);

@@ -9,17 +9,23 @@
 //   logits_kernel        L[h][i][j] = fl32(scale * (Q_bar_i . K_bar_j)), the dot in
 //                        float64: the scores are rounded once, so they equal
 //                        the float64 definition's nearest float
-//   select_count_kernel  per row: max, softmax masses (float64 exp, summed
-//                        as 2^-48 fixed-point integers), and a 4-pass radix
-//                        select over the order-preserving 32-bit key of the
-//                        scores for the boundary of the first max(k, n_p)
-//                        ranked blocks; ties at the boundary are resolved by
-//                        index.  No sort: the union of the two prefixes is one
-//                        prefix of the ranking, so only its boundary matters.
+//   select_reg_kernel    per row (up to 16384 blocks): the row's order-
+//                        preserving 32-bit score keys and their softmax masses
+//                        (float64 exp, as 2^-48 fixed-point integers) are held
+//                        in registers; a binary search over the key space,
+//                        each step one block-wide (count, mass) reduction,
+//                        finds the boundary of the first max(k, n_p) ranked
+//                        blocks; ties at the boundary are resolved by index.
+//                        No sort: the union of the two prefixes is one prefix
+//                        of the ranking, so only its boundary matters.
+//   select_count_kernel  the same result for longer rows, keys in LDS, by a
+//                        4-pass radix select over (count, mass) histograms.
 //   csr_scan_kernel      per head exclusive scan of the row counts
 //   select_write_kernel  per row: ordered compaction of the selected indices
 // and, for the backward, the transposed CSR (key block -> query blocks):
 //   tr_count_kernel, csr_scan_kernel, tr_fill_kernel, tr_sort_kernel.
+#include <cstdlib>
+
 #include "prism_device.hpp"
 #include "prism_internal.hpp"
 
@@ -322,6 +328,132 @@ select_count_kernel(const float* __restrict__ logits, int nb, int top_k, double 
     }
 }
 
+// Sums over the workgroup of a (count, mass) pair; every thread gets the
+// totals.  `slot` alternates between calls so that one barrier per call
+// suffices: a slot is rewritten only after every thread has passed the
+// barrier of the call in between, i.e. after it read the slot.
+__device__ __forceinline__ void block_sum_cm(uint32_t& c, unsigned long long& m, uint32_t (*rc)[kSelThreads / kWave],
+                                             unsigned long long (*rm)[kSelThreads / kWave], int& slot) {
+    c = wave_sum(c);
+    m = wave_sum(m);
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wid = threadIdx.x / kWave;
+    if (lane == 0) {
+        rc[slot][wid] = c;
+        rm[slot][wid] = m;
+    }
+    __syncthreads();
+    c = 0;
+    m = 0;
+#pragma unroll
+    for (int w = 0; w < kSelThreads / kWave; ++w) {
+        c += rc[slot][w];
+        m += rm[slot][w];
+    }
+    slot ^= 1;
+}
+
+// One workgroup per (row i, head h); thread t holds blocks t + 256 e, e < E.
+// The kept prefix is {key > u} plus the first ties of key u in index order,
+// where u is the largest key value with count(key >= u) >= max(k, 1) and
+// mass(key >= u) >= p * Z; both sums only grow as u falls, so u is found by
+// bisection between the row's smallest and largest keys.
+template <int E>
+__global__ void __launch_bounds__(kSelThreads)
+select_reg_kernel(const float* __restrict__ logits, int nb, int top_k, double top_p, int32_t* __restrict__ row_count,
+                  uint32_t* __restrict__ row_thr, int32_t* __restrict__ row_jlim) {
+    __shared__ uint32_t red32[kSelThreads / kWave];
+    __shared__ unsigned long long red64[kSelThreads / kWave];
+    __shared__ uint32_t rc[2][kSelThreads / kWave];
+    __shared__ unsigned long long rm[2][kSelThreads / kWave];
+    const int i = blockIdx.x, h = blockIdx.y;
+    const int64_t row = static_cast<int64_t>(h) * nb + i;
+    const float* __restrict__ L = logits + row * nb;
+    uint32_t key[E];
+    unsigned long long ms[E];
+    uint32_t kmax = 0, nkmin = 0;   // nkmin = ~(smallest key)
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        const int j = threadIdx.x + kSelThreads * e;
+        // padding key 0 lies below every finite score's key and is never counted
+        key[e] = j < nb ? score_key(L[j]) : 0u;
+        kmax = key[e] > kmax ? key[e] : kmax;
+        nkmin = (j < nb && ~key[e] > nkmin) ? ~key[e] : nkmin;
+    }
+    kmax = block_max(kmax, red32);
+    const uint32_t kmin = ~block_max(nkmin, red32);
+    const double M = static_cast<double>(key_score(kmax));
+    unsigned long long z = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        ms[e] = key[e] ? mass_fixed(key[e], M) : 0ull;
+        z += ms[e];
+    }
+    z = block_sum(z, red64);
+    const double target = top_p * static_cast<double>(z);
+    const uint32_t kk = top_k > 1 ? static_cast<uint32_t>(top_k) : 1u;
+    int count, jlim;
+    uint32_t thr;
+    if (!(static_cast<uint32_t>(nb) >= kk && static_cast<double>(z) >= target)) {
+        count = nb;                    // no prefix qualifies: keep every block
+        thr = 0u;
+        jlim = -1;
+    } else {
+        int slot = 0;
+        uint32_t lo = kmin, hi = kmax + 1u;   // the predicate holds at lo, fails at hi
+        while (hi - lo > 1u) {
+            const uint32_t mid = lo + (hi - lo) / 2u;
+            uint32_t c = 0;
+            unsigned long long m = 0;
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const bool in = key[e] >= mid;
+                c += in ? 1u : 0u;
+                m += in ? ms[e] : 0ull;
+            }
+            block_sum_cm(c, m, rc, rm, slot);
+            if (c >= kk && static_cast<double>(m) >= target) lo = mid;
+            else hi = mid;
+        }
+        thr = lo;
+        // blocks strictly above the boundary key, and the ties at it
+        uint32_t cabove = 0, ceq = 0;
+        unsigned long long mabove = 0;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            cabove += key[e] > thr ? 1u : 0u;
+            mabove += key[e] > thr ? ms[e] : 0ull;
+            ceq += key[e] == thr ? 1u : 0u;
+        }
+        block_sum_cm(cabove, mabove, rc, rm, slot);
+        unsigned long long dummy = 0;
+        block_sum_cm(ceq, dummy, rc, rm, slot);
+        const uint64_t eb = mass_fixed(thr, M);
+        uint32_t m = 0;
+        uint64_t acc = mabove;
+        do {
+            ++m;
+            acc += eb;
+        } while (m < ceq && !(cabove + m >= kk && static_cast<double>(acc) >= target));
+        count = static_cast<int>(cabove + m);
+        jlim = nb;
+        if (m < ceq && threadIdx.x == 0) {
+            // index of the m-th tie in ascending index order (rare: equal scores)
+            uint32_t seen = 0;
+            for (int j = 0; j < nb; ++j)
+                if (score_key(L[j]) == thr && ++seen == m) {
+                    jlim = j;
+                    break;
+                }
+        }
+    }
+    if (threadIdx.x == 0) {
+        row_count[row] = count;
+        row_thr[row] = thr;
+        row_jlim[row] = jlim;
+    }
+}
+
 // exclusive scan of counts[h][0..n) into offsets[h][0..n]; totals[h] = sum
 __global__ void __launch_bounds__(1024)
 csr_scan_kernel(const int32_t* __restrict__ counts, int n, int32_t* __restrict__ offsets, int64_t* __restrict__ totals) {
@@ -493,14 +625,34 @@ hipError_t launch_select(const void* q, const void* k, bool bf16, int heads, int
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     const dim3 rg(nb, heads);
-    const size_t lds = static_cast<size_t>(nb) * sizeof(uint32_t);
-    if (lds > 48 * 1024) {
-        e = hipFuncSetAttribute(reinterpret_cast<const void*>(&select_count_kernel),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-        if (e != hipSuccess) return e;
+    // PRISM_SELECT_RADIX=1 forces the LDS radix kernel (used by the tests to
+    // compare the two kernels on rows of any length)
+    const char* ev = std::getenv("PRISM_SELECT_RADIX");
+    const bool radix = ev && ev[0] == '1';
+    if (!radix && nb <= 16 * kSelThreads) {
+        if (nb <= 8 * kSelThreads)
+            hipLaunchKernelGGL(select_reg_kernel<8>, rg, dim3(kSelThreads), 0, s, logits, nb, top_k, top_p, row_count,
+                               row_thr, row_jlim);
+        else
+            hipLaunchKernelGGL(select_reg_kernel<16>, rg, dim3(kSelThreads), 0, s, logits, nb, top_k, top_p,
+                               row_count, row_thr, row_jlim);
+    } else if (!radix && nb <= 64 * kSelThreads) {
+        if (nb <= 32 * kSelThreads)
+            hipLaunchKernelGGL(select_reg_kernel<32>, rg, dim3(kSelThreads), 0, s, logits, nb, top_k, top_p,
+                               row_count, row_thr, row_jlim);
+        else
+            hipLaunchKernelGGL(select_reg_kernel<64>, rg, dim3(kSelThreads), 0, s, logits, nb, top_k, top_p,
+                               row_count, row_thr, row_jlim);
+    } else {
+        const size_t lds = static_cast<size_t>(nb) * sizeof(uint32_t);
+        if (lds > 48 * 1024) {
+            e = hipFuncSetAttribute(reinterpret_cast<const void*>(&select_count_kernel),
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+            if (e != hipSuccess) return e;
+        }
+        hipLaunchKernelGGL(select_count_kernel, rg, dim3(kSelThreads), lds, s, logits, nb, top_k, top_p, row_count,
+                           row_thr, row_jlim);
     }
-    hipLaunchKernelGGL(select_count_kernel, rg, dim3(kSelThreads), lds, s, logits, nb, top_k, top_p, row_count,
-                       row_thr, row_jlim);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(csr_scan_kernel, dim3(heads), dim3(1024), 0, s, row_count, nb, sel_offsets, sel_total);

@@ -31,7 +31,13 @@
  *     and `hs` (between heads), d contiguous; every tensor of one call has the
  *     same dtype, ld and hs.  Supported d: 64 and 128.  Vector access needs the
  *     pointers 16-byte aligned and ld, hs multiples of 8 elements (bf16) or 4
- *     (f32).
+ *     (f32), and 64 * ld * element size below 2^32 bytes (tiles are addressed
+ *     with 32-bit offsets).
+ *   - Two environment variables switch to alternative kernels with the same
+ *     results, for tests: PRISM_SELECT_RADIX=1 makes prism_select use its LDS
+ *     radix-select kernel at every row length (by default it is used only for
+ *     rows of more than 16384 blocks); PRISM_ATTN_SIMT=1 makes the bf16
+ *     attention calls use the vector-ALU kernels instead of the MFMA ones.
  *   - Block-major order: zones in raster order (m = (zt*nH + zh)*nW + zw, 512
  *     positions each); inside a zone, its blocks in raster order over the block
  *     grid; inside a block, tokens in raster (t, h, w) order.  Raster token

@@ -126,6 +126,7 @@ def test_select_rejects():
     assert f(d=96) == 4
     assert f(ld=60) == 1
     assert f(ld=66) == 4                           # not a multiple of 4 fp32 elements
+    assert f(ld=1 << 24) == 4                      # 64 rows would span 4 GiB: beyond 32-bit tile offsets
     assert f(nb=0) == 1
     assert f(nb=N // 64 + 1) == 1
     assert f(k=-1) == 1

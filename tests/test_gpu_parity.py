@@ -210,6 +210,48 @@ def test_zone_statistics_both_load_paths(idx):
         np.testing.assert_array_equal(recs[0], recs[1])
 
 
+@pytest.mark.parametrize("idx", [1, 2, 5, 7], ids=lambda i: SMALL[i].name)
+def test_selection_kernels_agree(idx, monkeypatch):
+    """prism_select keeps a row's keys in registers up to 16384 blocks and uses
+    an LDS radix select beyond; PRISM_SELECT_RADIX=1 forces the latter, which
+    must give the identical CSR."""
+    cfg = SMALL[idx]
+    print(f"case {cfg.name}", flush=True)
+    x = make_inputs(cfg, device="cuda")
+    path = _path(cfg)
+    path.shapes(x["v"], x["a"])
+    qp, kp = path.permute(x["q"]), path.permute(x["k"])
+    a = path.select(qp, kp)
+    monkeypatch.setenv("PRISM_SELECT_RADIX", "1")
+    b = path.select(qp, kp)
+    torch.cuda.synchronize()
+    assert torch.equal(a.offsets, b.offsets)
+    assert torch.equal(a.total, b.total)
+    for h in range(cfg.heads):
+        t = int(a.total[h])
+        assert torch.equal(a.idx[h, :t], b.idx[h, :t])
+
+
+@pytest.mark.parametrize("idx", [1, 2], ids=lambda i: SMALL[i].name)
+def test_vector_alu_attention_in_bf16(idx, monkeypatch):
+    """PRISM_ATTN_SIMT=1 runs the bf16 attention on the vector-ALU kernels; they
+    must meet the same bar against the oracle."""
+    cfg = SMALL[idx]
+    print(f"case {cfg.name}", flush=True)
+    monkeypatch.setenv("PRISM_ATTN_SIMT", "1")
+    x = make_inputs(cfg, device="cuda")
+    path = _path(cfg)
+    out = path.step(x["q"], x["k"], x["v"], x["a"], x.get("do"))
+    torch.cuda.synchronize()
+    ref = _oracle_full(cfg, x)
+    for h, hr in enumerate(ref["heads"]):
+        att = hr["att"]
+        _assert_close(_np(out["o"][:, h, :]), orc.to_raster(att["O"], ref["pi"]), cfg.dtype, f"O h{h}")
+        for g, name in (("dq", "dQ"), ("dk", "dK"), ("dv", "dV")):
+            _assert_close(_np(out[g][:, h, :]), orc.to_raster(att[name], ref["pi"]), cfg.dtype, f"{name} h{h}",
+                          grad=True)
+
+
 def test_permutation_round_trip_with_strided_rows():
     cfg = SMALL[1]
     x = make_inputs(cfg, device="cuda")
