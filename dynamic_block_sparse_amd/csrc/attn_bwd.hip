@@ -21,14 +21,19 @@ namespace prism {
 // Each output element is accumulated by one lane in a fixed order: the
 // backward is deterministic.
 
+// dQ keeps one K and one V tile in LDS and fits 256 registers, so two waves
+// share each SIMD (measured at 2K: 82 ms against 100 ms double-buffered at one
+// wave per SIMD).  dK/dV needs 384 registers, one wave per SIMD, and
+// double-buffers its Q and dO tiles instead.
+
 template <int D>
-__global__ void __launch_bounds__(128, 1)
+__global__ void __launch_bounds__(128, 2)
 attn_dq_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
                     const uint16_t* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ Dq,
                     uint16_t* __restrict__ dq, int64_t N, int64_t ld, int64_t hs, const int32_t* __restrict__ offs,
                     int nb, const int32_t* __restrict__ sel_off, const int32_t* __restrict__ sel_idx, int64_t cap,
                     float scale_log2, float scale) {
-    __shared__ uint16_t kbuf[2][64 * D], vbuf[2][64 * D];
+    __shared__ uint16_t kbuf[1][64 * D], vbuf[1][64 * D];
     const int ntiles = static_cast<int>(N / 64);
     const int wg = xcd_remap(blockIdx.x);
     const int h = wg / ntiles;
@@ -109,7 +114,7 @@ attn_dq_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
 
     TileCursor cur;
     cur.init(si, offs, e0, e1);
-    tile_pipeline(cur, issue, compute);
+    tile_pipeline1(cur, issue, compute);
     uint16_t* out = dq + row * ld + h * hs;
 #pragma unroll
     for (int m = 0; m < DM; ++m)

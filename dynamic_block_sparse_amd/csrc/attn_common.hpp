@@ -31,8 +31,8 @@
 // (measured with the bank-conflict counter on gfx950; the unswizzled layout
 // and other XOR patterns conflict on one or the other).  Tiles are filled by direct global->LDS
 // loads (global_load_lds_dwordx4: lane l's 16 bytes land at base + 16 l), each
-// lane fetching the global chunk its LDS slot holds, double-buffered so the
-// next tile loads while the current one is used.
+// lane fetching the global chunk its LDS slot holds, so that the loads overlap
+// the compute of this or another resident workgroup.
 #pragma once
 #include "prism_device.hpp"
 #include "prism_internal.hpp"
@@ -191,7 +191,9 @@ struct TileCursor {
 };
 
 // Double-buffered walk over the tiles of `cur`: tile t+1 is loaded into
-// buffer b^1 while tile t, in buffer b, is used.
+// buffer b^1 while tile t, in buffer b, is used.  (The dK/dV kernel; the
+// forward and dQ kernels use one buffer and a second resident workgroup per
+// SIMD instead, see below.)
 template <class Issue, class Compute>
 __device__ __forceinline__ void tile_pipeline(TileCursor& cur, Issue&& issue, Compute&& compute) {
     int t = cur.next();
@@ -204,6 +206,21 @@ __device__ __forceinline__ void tile_pipeline(TileCursor& cur, Issue&& issue, Co
         compute(b);
         dma_join();
         if (t < 0) return;
+    }
+}
+
+// Single-buffered walk: load a tile, use it, load the next.  With a 32 KB
+// footprint (d = 128) four workgroups share a CU, two waves per SIMD, so one
+// workgroup's loads overlap another's compute.
+template <class Issue, class Compute>
+__device__ __forceinline__ void tile_pipeline1(TileCursor& cur, Issue&& issue, Compute&& compute) {
+    int t = cur.next();
+    while (t >= 0) {
+        issue(t, 0);
+        dma_join();
+        compute(0);
+        t = cur.next();
+        __syncthreads();
     }
 }
 

@@ -15,14 +15,22 @@ namespace prism {
 // the O^T rescale is a per-lane scalar.  The running maximum is raised only
 // when a tile's maximum exceeds it by more than 8 (log2 units), so O is
 // rescaled rarely; exponents stay below 2^8 in between.
+//
+// LDS holds one K and one V tile (32 KB at d = 128), so four workgroups, two
+// waves per SIMD, share a CU and one wave's softmax overlaps another's MFMAs.
+// Within the workgroup the loads are split by phase: K(t+1) is loaded as soon
+// as every wave has finished the scores of tile t (it lands during softmax and
+// P V), V(t+1) once every wave has finished P V (it lands during the next
+// scores).  Each phase boundary is one wait-and-barrier.  (Measured at 2K: 71
+// ms, against 79 ms with double-buffered K and V at one wave per SIMD.)
 
 template <int D>
-__global__ void __launch_bounds__(128, 1)
+__global__ void __launch_bounds__(128, 2)
 attn_fwd_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
                      uint16_t* __restrict__ o, float* __restrict__ lse, int64_t N, int64_t ld, int64_t hs,
                      const int32_t* __restrict__ offs, int nb, const int32_t* __restrict__ sel_off,
                      const int32_t* __restrict__ sel_idx, int64_t cap, float scale_log2) {
-    __shared__ uint16_t kbuf[2][64 * D], vbuf[2][64 * D];
+    __shared__ uint16_t kbuf[64 * D], vbuf[64 * D];
     const int ntiles = static_cast<int>(N / 64);
     const int wg = xcd_remap(blockIdx.x);
     const int h = wg / ntiles;
@@ -56,54 +64,62 @@ attn_fwd_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
 
     TileDma<D, 2> dma;
     dma.init(ld, wave, lane);
-    auto issue = [&](int t, int b) {
-        dma.load(kbuf[b], kh_ + static_cast<int64_t>(t) * ld, wave);
-        dma.load(vbuf[b], vh_ + static_cast<int64_t>(t) * ld, wave);
-    };
-    auto compute = [&](int b) {
-        const uint16_t* kt = kbuf[b];
-        const uint16_t* vt = vbuf[b];
-        f32x16_t s0, s1;
-#pragma unroll
-        for (int x = 0; x < 16; ++x) s0[x] = s1[x] = 0.0f;
-#pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            s0 = mfma32(sw_read16<D>(kt, col, 16 * s + 8 * hl), qb[s], s0);
-            s1 = mfma32(sw_read16<D>(kt, 32 + col, 16 * s + 8 * hl), qb[s], s1);
-        }
-        sched_reads_ahead<2, 2, KS, 2>();
-        float mx = -INFINITY;
-#pragma unroll
-        for (int x = 0; x < 16; ++x) mx = fmaxf(mx, fmaxf(s0[x], s1[x]));
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * scale_log2;
-        if (__any(mx > mrow + 8.0f)) {
-            const float mnew = fmaxf(mrow, mx);
-            const float alpha = fast_exp2(mrow - mnew);
-            mrow = mnew;
-            lrow *= alpha;
-#pragma unroll
-            for (int m = 0; m < DM; ++m)
-#pragma unroll
-                for (int x = 0; x < 16; ++x) oacc[m][x] *= alpha;
-        }
-        float ls = 0.0f;
-#pragma unroll
-        for (int x = 0; x < 16; ++x) {
-            s0[x] = fast_exp2(fmaf(s0[x], scale_log2, -mrow));
-            s1[x] = fast_exp2(fmaf(s1[x], scale_log2, -mrow));
-            ls += s0[x] + s1[x];
-        }
-        lrow += ls;
-        const u32x4_t pb[4] = {pack_kstep(s0, 0), pack_kstep(s0, 1), pack_kstep(s1, 0), pack_kstep(s1, 1)};
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-            for (int m = 0; m < DM; ++m) oacc[m] = mfma32(tr_operand<D>(vt, 16 * ks, 32 * m, lane), pb[ks], oacc[m]);
-    };
-
+    constexpr int PER = TileDma<D, 2>::PER;
     TileCursor cur;
     cur.init(si, offs, e0, e1);
-    tile_pipeline(cur, issue, compute);
+    int t = cur.next();
+    if (t >= 0) {
+        dma.load(kbuf, kh_ + static_cast<int64_t>(t) * ld, wave);
+        dma.load(vbuf, vh_ + static_cast<int64_t>(t) * ld, wave);
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(PER) : "memory");   // this wave's K loads
+        __syncthreads();
+        const uint16_t* kt = kbuf;
+        const uint16_t* vt = vbuf;
+        while (true) {
+            f32x16_t s0, s1;
+#pragma unroll
+            for (int x = 0; x < 16; ++x) s0[x] = s1[x] = 0.0f;
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                s0 = mfma32(sw_read16<D>(kt, col, 16 * s + 8 * hl), qb[s], s0);
+                s1 = mfma32(sw_read16<D>(kt, 32 + col, 16 * s + 8 * hl), qb[s], s1);
+            }
+            sched_reads_ahead<2, 2, KS, 2>();
+            dma_join();                    // V(t) landed; every wave is done with K(t)
+            const int tn = cur.next();
+            if (tn >= 0) dma.load(kbuf, kh_ + static_cast<int64_t>(tn) * ld, wave);
+            float mx = -INFINITY;
+#pragma unroll
+            for (int x = 0; x < 16; ++x) mx = fmaxf(mx, fmaxf(s0[x], s1[x]));
+            mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * scale_log2;
+            if (__any(mx > mrow + 8.0f)) {
+                const float mnew = fmaxf(mrow, mx);
+                const float alpha = fast_exp2(mrow - mnew);
+                mrow = mnew;
+                lrow *= alpha;
+#pragma unroll
+                for (int m = 0; m < DM; ++m)
+#pragma unroll
+                    for (int x = 0; x < 16; ++x) oacc[m][x] *= alpha;
+            }
+            float ls = 0.0f;
+#pragma unroll
+            for (int x = 0; x < 16; ++x) {
+                s0[x] = fast_exp2(fmaf(s0[x], scale_log2, -mrow));
+                s1[x] = fast_exp2(fmaf(s1[x], scale_log2, -mrow));
+                ls += s0[x] + s1[x];
+            }
+            lrow += ls;
+            const u32x4_t pb[4] = {pack_kstep(s0, 0), pack_kstep(s0, 1), pack_kstep(s1, 0), pack_kstep(s1, 1)};
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+                for (int m = 0; m < DM; ++m) oacc[m] = mfma32(tr_operand<D>(vt, 16 * ks, 32 * m, lane), pb[ks], oacc[m]);
+            dma_join();                    // K(tn) landed; every wave is done with V(t)
+            if (tn < 0) break;
+            dma.load(vbuf, vh_ + static_cast<int64_t>(tn) * ld, wave);
+        }
+    }
     // lanes l and l^32 hold the two halves of a row's sum
     const float lt = lrow + __shfl_xor(lrow, 32, 64);
     const float inv = 1.0f / lt;
