@@ -70,26 +70,30 @@ pool_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, int64_t ld, in
 
 // ---------------------------------------------------------------- scores
 
-constexpr int kLT = 64;   // output tile
-constexpr int kLK = 16;   // reduction chunk
+constexpr int kLT = 128;  // output tile (rows and columns)
+constexpr int kLK = 8;    // reduction chunk
 
+// One workgroup per 128 x 128 tile of one head's scores; thread (tx, ty) owns
+// rows ty + 16 a and columns tx + 16 b (a, b < 8), 64 float64 accumulators, so
+// every value read from LDS feeds 8 fused multiply-adds.  The reduction over
+// the d channels runs in ascending order for every score.
 template <int D>
 __global__ void __launch_bounds__(256)
 logits_kernel(const double* __restrict__ pooled, int nb, int heads, double scale, float* __restrict__ logits) {
-    __shared__ double As[kLK][kLT + 1];
-    __shared__ double Bs[kLK][kLT + 1];
+    __shared__ double As[kLK][kLT];
+    __shared__ double Bs[kLK][kLT];
     const int h = blockIdx.z;
     const int i0 = blockIdx.y * kLT, j0 = blockIdx.x * kLT;
     const double* __restrict__ Qb = pooled + static_cast<int64_t>(h) * nb * D;
     const double* __restrict__ Kb = pooled + (static_cast<int64_t>(heads) + h) * nb * D;
     const int tx = threadIdx.x % 16, ty = threadIdx.x / 16;
-    double acc[4][4];
+    double acc[8][8];
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int a = 0; a < 8; ++a)
 #pragma unroll
-        for (int b = 0; b < 4; ++b) acc[a][b] = 0.0;
+        for (int b = 0; b < 8; ++b) acc[a][b] = 0.0;
     for (int c0 = 0; c0 < D; c0 += kLK) {
-        // 64 rows x 16 columns of each operand: 1024 values, 4 per thread
+        // 128 rows x 8 channels of each operand: 1024 values, 4 per thread
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int idx = threadIdx.x + e * 256;
@@ -101,25 +105,25 @@ logits_kernel(const double* __restrict__ pooled, int nb, int heads, double scale
         __syncthreads();
 #pragma unroll
         for (int kk = 0; kk < kLK; ++kk) {
-            double a[4], b[4];
+            double a[8], b[8];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
+            for (int e = 0; e < 8; ++e) {
                 a[e] = As[kk][ty + 16 * e];
                 b[e] = Bs[kk][tx + 16 * e];
             }
 #pragma unroll
-            for (int x = 0; x < 4; ++x)
+            for (int x = 0; x < 8; ++x)
 #pragma unroll
-                for (int y = 0; y < 4; ++y) acc[x][y] = fma(a[x], b[y], acc[x][y]);
+                for (int y = 0; y < 8; ++y) acc[x][y] = fma(a[x], b[y], acc[x][y]);
         }
         __syncthreads();
     }
 #pragma unroll
-    for (int x = 0; x < 4; ++x) {
+    for (int x = 0; x < 8; ++x) {
         const int gi = i0 + ty + 16 * x;
         if (gi >= nb) continue;
 #pragma unroll
-        for (int y = 0; y < 4; ++y) {
+        for (int y = 0; y < 8; ++y) {
             const int gj = j0 + tx + 16 * y;
             if (gj < nb) logits[(static_cast<int64_t>(h) * nb + gi) * nb + gj] = static_cast<float>(scale * acc[x][y]);
         }
