@@ -249,6 +249,32 @@ prism_status prism_block_permute(int32_t T, int32_t H, int32_t W, const uint8_t*
                       "block_permute launch");
 }
 
+prism_status prism_block_permute_heads(int32_t T, int32_t H, int32_t W, const uint8_t* zone_shape, const void* x,
+                                       void* y, prism_dtype dt, int32_t heads, int32_t d, int64_t x_ld, int64_t x_hs,
+                                       int64_t y_ld, int64_t y_hs, int32_t inverse, hipStream_t stream) {
+    prism_status st = check_grid(T, H, W);
+    if (st != PRISM_OK) return st;
+    if (dt != PRISM_F32 && dt != PRISM_BF16) return fail(PRISM_E_DTYPE, "unknown dtype %d", static_cast<int>(dt));
+    if (!zone_shape || !x || !y) return fail(PRISM_E_ARG, "null pointer argument");
+    if (heads <= 0 || d <= 0) return fail(PRISM_E_ARG, "heads = %d and d = %d must be positive", heads, d);
+    if (x_ld < 0 || x_hs < 0 || y_ld < 0 || y_hs < 0) return fail(PRISM_E_ARG, "strides must be non-negative");
+    if (inverse != 0 && inverse != 1) return fail(PRISM_E_ARG, "inverse must be 0 or 1");
+    const int eb = elem_bytes(dt);
+    const int64_t vec = 16 / eb;
+    if (d % vec || x_ld % vec || x_hs % vec || y_ld % vec || y_hs % vec ||
+        ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(y)) & 15))
+        return fail(PRISM_E_UNSUPPORTED, "d, strides and pointers must be 16-byte multiples");
+    const int64_t N = static_cast<int64_t>(T) * H * W;
+    const char* xb = static_cast<const char*>(x);
+    const char* yb = static_cast<const char*>(y);
+    const int64_t xspan = ((N - 1) * x_ld + (heads - 1) * x_hs + d) * eb;
+    const int64_t yspan = ((N - 1) * y_ld + (heads - 1) * y_hs + d) * eb;
+    if (xb < yb + yspan && yb < xb + xspan) return fail(PRISM_E_ARG, "x and y overlap");
+    return hip_status(prism::launch_block_permute_heads(x, y, eb, heads, d, x_ld, x_hs, y_ld, y_hs, zone_shape,
+                                                        grid_of(T, H, W), N, inverse, stream),
+                      "block_permute_heads launch");
+}
+
 prism_status prism_select(const void* q, const void* k, prism_dtype dt, int64_t N, int32_t heads, int32_t d,
                           int64_t ld, int64_t hs, const int32_t* block_offsets, int32_t nb, int32_t top_k, double top_p,
                           float scale, int32_t* sel_offsets, int32_t* sel_idx, int64_t cap, int64_t* sel_total,

@@ -18,6 +18,9 @@ size_t zone_partial_doubles(int nZ, int64_t C);
 hipError_t launch_block_permute(const void* x, void* y, int elem_bytes, int64_t row_elems, int64_t x_ld,
                                 int64_t y_ld, const uint8_t* zone_shape, ZoneGrid g, int64_t N, int inverse,
                                 hipStream_t s);
+hipError_t launch_block_permute_heads(const void* x, void* y, int elem_bytes, int heads, int d, int64_t x_ld,
+                                      int64_t x_hs, int64_t y_ld, int64_t y_hs, const uint8_t* zone_shape, ZoneGrid g,
+                                      int64_t N, int inverse, hipStream_t s);
 
 hipError_t launch_select(const void* q, const void* k, bool bf16, int heads, int d, int64_t ld, int64_t hs,
                          const int32_t* offs, int nb, int top_k, double top_p, float scale, int32_t* sel_offsets,

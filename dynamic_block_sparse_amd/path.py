@@ -69,7 +69,16 @@ class PrismPath:
     def permute(self, x, inverse=False, out=None):
         """Gather raster rows into block-major order (head-major storage), or
         scatter block-major rows back into a raster [N, heads, d] tensor; one
-        library call per head."""
+        library call for all heads."""
+        N, nh, d = x.shape
+        if out is None:
+            out = torch.empty((N, nh, d), dtype=x.dtype, device=x.device) if inverse else self.block_major_like(x)
+        P.prism_block_permute_heads(self.T, self.H, self.W, self.zone_shape, x, out, nh, d, x.stride(0), x.stride(1),
+                                    out.stride(0), out.stride(1), 1 if inverse else 0)
+        return out
+
+    def permute_per_head(self, x, inverse=False, out=None):
+        """The same with one prism_block_permute call per head."""
         N, nh, d = x.shape
         if out is None:
             out = torch.empty((N, nh, d), dtype=x.dtype, device=x.device) if inverse else self.block_major_like(x)

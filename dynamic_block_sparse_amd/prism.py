@@ -25,7 +25,8 @@ ZS_STRIDE = 16
 STATUS = {0: "PRISM_OK", 1: "PRISM_E_ARG", 2: "PRISM_E_GRID", 3: "PRISM_E_DTYPE",
           4: "PRISM_E_UNSUPPORTED", 5: "PRISM_E_WORKSPACE", 6: "PRISM_E_HIP"}
 
-EXPORTS = ["prism_zone_shapes", "prism_block_permute", "prism_select", "prism_sparse_attn_fwd",
+EXPORTS = ["prism_zone_shapes", "prism_block_permute", "prism_block_permute_heads", "prism_select",
+           "prism_sparse_attn_fwd",
            "prism_sparse_attn_bwd", "prism_workspace_size", "prism_status_string", "prism_last_error",
            "prism_candidate_shapes"]
 
@@ -44,14 +45,16 @@ _vp, _i32, _i64, _f32, _f64, _sz = C.c_void_p, C.c_int32, C.c_int64, C.c_float, 
 _lib.prism_zone_shapes.argtypes = [_i32, _i32, _i32, _vp, _i32, _i64, _i64, _vp, C.POINTER(PrismShapeParams), _vp,
                                    _vp, _vp, C.POINTER(_i32), _vp, _vp, _sz, _vp]
 _lib.prism_block_permute.argtypes = [_i32, _i32, _i32, _vp, _vp, _vp, _i32, _i64, _i64, _i64, _i32, _vp]
+_lib.prism_block_permute_heads.argtypes = [_i32, _i32, _i32, _vp, _vp, _vp, _i32, _i32, _i32, _i64, _i64, _i64, _i64,
+                                           _i32, _vp]
 _lib.prism_select.argtypes = [_vp, _vp, _i32, _i64, _i32, _i32, _i64, _i64, _vp, _i32, _i32, _f64, _f32, _vp, _vp,
                               _i64, _vp, _vp, _vp, _sz, _vp]
 _lib.prism_sparse_attn_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i64, _i64, _vp, _i32, _vp,
                                        _vp, _i64, _f32, _vp, _sz, _vp]
 _lib.prism_sparse_attn_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i64,
                                        _i64, _vp, _i32, _vp, _vp, _i64, _f32, _vp, _sz, _vp]
-for _f in ("prism_zone_shapes", "prism_block_permute", "prism_select", "prism_sparse_attn_fwd",
-           "prism_sparse_attn_bwd"):
+for _f in ("prism_zone_shapes", "prism_block_permute", "prism_block_permute_heads", "prism_select",
+           "prism_sparse_attn_fwd", "prism_sparse_attn_bwd"):
     getattr(_lib, _f).restype = C.c_int
 _lib.prism_workspace_size.argtypes = [_i32, _i64, _i32, _i32, _i32, _i64]
 _lib.prism_workspace_size.restype = _sz
@@ -130,6 +133,13 @@ def prism_zone_shapes(T, H, W, v, C_, v_ld, a_map, zone_shape, block_offsets, nb
 def prism_block_permute(T, H, W, zone_shape, x, y, row_elems, x_ld, y_ld, inverse, stream=None, dtype=None):
     st = _lib.prism_block_permute(T, H, W, _ptr(zone_shape), _ptr(x), _ptr(y), _dt(x) if dtype is None else dtype,
                                   row_elems, x_ld, y_ld, int(inverse), _stream(stream))
+    _check(st)
+
+
+def prism_block_permute_heads(T, H, W, zone_shape, x, y, heads, d, x_ld, x_hs, y_ld, y_hs, inverse, stream=None,
+                              dtype=None):
+    st = _lib.prism_block_permute_heads(T, H, W, _ptr(zone_shape), _ptr(x), _ptr(y), _dt(x) if dtype is None else dtype,
+                                        heads, d, x_ld, x_hs, y_ld, y_hs, int(inverse), _stream(stream))
     _check(st)
 
 

@@ -139,6 +139,31 @@ prism_status prism_block_permute(int32_t T, int32_t H, int32_t W, const uint8_t*
                                  int64_t x_ld, int64_t y_ld, int32_t inverse, hipStream_t stream);
 
 /*
+ * prism_block_permute_heads - the same permutation for all heads of a token
+ * tensor in one call, with separate token and head strides on each side:
+ * head hh of token row r of x is x + r*x_ld + hh*x_hs (likewise y), d
+ * elements each.  Typical use: a raster [N, heads, d] tensor (x_ld = heads*d,
+ * x_hs = d) gathered into head-major block-major storage [heads, N, d]
+ * (y_ld = d, y_hs = N*d), and back with inverse = 1.
+ *
+ *   heads, d       heads per token, elements per head (d * element size a
+ *                  multiple of 16 bytes)
+ *   x_ld, x_hs     token and head strides of x in elements (16-byte multiples)
+ *   y_ld, y_hs     the same for y
+ *   x, y           16-byte aligned; the memory spans of x and y must not
+ *                  overlap; the head regions of one tensor must not overlap
+ *                  each other (not checked)
+ * Status: PRISM_E_GRID for a bad grid, PRISM_E_ARG for null pointers,
+ * non-positive heads or d, negative strides or overlapping spans,
+ * PRISM_E_UNSUPPORTED for sizes, strides or pointers that are not 16-byte
+ * multiples.
+ */
+prism_status prism_block_permute_heads(int32_t T, int32_t H, int32_t W, const uint8_t* zone_shape,
+                                       const void* x, void* y, prism_dtype dt, int32_t heads, int32_t d,
+                                       int64_t x_ld, int64_t x_hs, int64_t y_ld, int64_t y_hs,
+                                       int32_t inverse, hipStream_t stream);
+
+/*
  * prism_select - pooled block scores and hybrid Top-k U Top-p key-block
  * selection (reading guide, "Phương pháp" §3, the selected-set display).
  *

@@ -113,6 +113,26 @@ def test_block_permute_rejects():
     assert "overlap" in P.prism_last_error()
 
 
+def test_block_permute_heads_rejects():
+    lib, P = _lib()
+    X, Y = 0x1000000, 0x2000000                    # 16 MiB apart: the 8x8x8 spans do not meet
+    f = lambda T=8, zs=A, x=X, y=Y, dt=1, heads=2, d=128, xl=256, xh=128, yl=128, yh=512 * 128, inv=0: \
+        lib.prism_block_permute_heads(T, 8, 8, zs, x, y, dt, heads, d, xl, xh, yl, yh, inv, None)
+    assert f(T=12) == 2
+    assert f(zs=None) == 1
+    assert f(y=None) == 1
+    assert f(dt=7) == 3
+    assert f(heads=0) == 1
+    assert f(d=0) == 1
+    assert f(xh=-128) == 1
+    assert f(inv=3) == 1
+    assert f(d=100) == 4                           # 200 bytes: not a 16-byte multiple
+    assert f(xl=260) == 4
+    assert f(y=Y + 8) == 4                         # misaligned
+    assert f(x=X, y=X + 4096) == 1                 # overlapping spans
+    assert "overlap" in P.prism_last_error()
+
+
 def test_select_rejects():
     lib, P = _lib()
     N, heads, d, nb = 2048, 1, 64, 24

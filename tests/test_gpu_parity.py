@@ -260,11 +260,14 @@ def test_permutation_round_trip_with_strided_rows():
     wide = torch.zeros((cfg.N, cfg.heads + 1, cfg.d), dtype=x["q"].dtype, device="cuda")
     wide[:, :cfg.heads] = x["q"]
     view = wide[:, :cfg.heads]                       # token stride (heads+1)*d
-    yp = path.permute(view)
+    yp = path.permute(view)                          # all heads in one call
     back = path.permute(yp, inverse=True)
     assert torch.equal(back, x["q"])
     pi = orc.permutation(cfg.T, cfg.H, cfg.W, path.zone_shape.cpu().numpy())
     np.testing.assert_array_equal(_np(yp), _np(x["q"])[pi])
+    # one call per head gives the same bytes both ways
+    assert torch.equal(path.permute_per_head(view), yp)
+    assert torch.equal(path.permute_per_head(yp, inverse=True), x["q"])
 
 
 # ---------------------------------------------------------------- named workloads at full size
