@@ -107,20 +107,42 @@ attn_fwd_simt_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* 
     lse[static_cast<int64_t>(h) * N + p] = m + __logf(l);
 }
 
-// Dq[h][p] = sum_c dO[p,h,c] * O[p,h,c]
+// Dq[h][p] = sum_c dO[p,h,c] * O[p,h,c].  LPR lanes share a row, each with 16
+// bytes of O and of dO (EPV elements); a workgroup covers 64 rows of one head.
 template <typename T, int D>
 __global__ void __launch_bounds__(256)
 attn_bwd_dot_kernel(const T* __restrict__ o, const T* __restrict__ dout, int64_t N, int heads, int64_t ld, int64_t hs,
                     float* __restrict__ Dq) {
-    const int64_t p = static_cast<int64_t>(blockIdx.x) * 4 + threadIdx.x / 64;
+    constexpr int EPV = 16 / static_cast<int>(sizeof(T));
+    constexpr int LPR = D / EPV;            // lanes per row (power of two, <= 64)
+    constexpr int RPI = 256 / LPR;          // rows per workgroup step
     const int h = blockIdx.y;
-    const int lane = threadIdx.x & 63;
-    if (p >= N) return;
-    float s = 0.0f;
-    for (int c = lane; c < D; c += 64)
-        s = fmaf(ld_elem(dout + p * ld + h * hs + c), ld_elem(o + p * ld + h * hs + c), s);
-    s = wave_sum(s);
-    if (lane == 0) Dq[static_cast<int64_t>(h) * N + p] = s;
+    const int sub = threadIdx.x % LPR;
+#pragma unroll
+    for (int it = 0; it < 64 / RPI; ++it) {
+        const int64_t p = static_cast<int64_t>(blockIdx.x) * 64 + it * RPI + threadIdx.x / LPR;
+        float s = 0.0f;
+        if (p < N) {
+            const int64_t off = p * ld + h * hs + sub * EPV;
+            const uint4 a = *reinterpret_cast<const uint4*>(o + off);
+            const uint4 b = *reinterpret_cast<const uint4*>(dout + off);
+            const uint32_t wa[4] = {a.x, a.y, a.z, a.w}, wb[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                if constexpr (EPV == 8) {
+                    s = fmaf(bf16_to_f32(static_cast<uint16_t>(wb[e] & 0xFFFFu)),
+                             bf16_to_f32(static_cast<uint16_t>(wa[e] & 0xFFFFu)), s);
+                    s = fmaf(bf16_to_f32(static_cast<uint16_t>(wb[e] >> 16)), bf16_to_f32(static_cast<uint16_t>(wa[e] >> 16)),
+                             s);
+                } else {
+                    s = fmaf(__uint_as_float(wb[e]), __uint_as_float(wa[e]), s);
+                }
+            }
+        }
+#pragma unroll
+        for (int off = LPR / 2; off >= 1; off >>= 1) s += __shfl_xor(s, off, kWave);
+        if (p < N && sub == 0) Dq[static_cast<int64_t>(h) * N + p] = s;
+    }
 }
 
 template <typename T, int D>
@@ -269,7 +291,7 @@ hipError_t launch_attn_fwd_simt(const void* q, const void* k, const void* v, voi
 template <typename T, int D>
 static hipError_t dot_launch(const void* o, const void* dout, int64_t N, int heads, int64_t ld, int64_t hs, float* Dq,
                              hipStream_t s) {
-    hipLaunchKernelGGL((attn_bwd_dot_kernel<T, D>), dim3(static_cast<unsigned>((N + 3) / 4), heads), dim3(256), 0, s,
+    hipLaunchKernelGGL((attn_bwd_dot_kernel<T, D>), dim3(static_cast<unsigned>((N + 63) / 64), heads), dim3(256), 0, s,
                        static_cast<const T*>(o), static_cast<const T*>(dout), N, heads, ld, hs, Dq);
     return hipGetLastError();
 }

@@ -283,6 +283,8 @@ prism_status prism_select(const void* q, const void* k, prism_dtype dt, int64_t 
     if (st != PRISM_OK) return st;
     if (!q || !k || !block_offsets || !sel_offsets || !sel_idx || !sel_total)
         return fail(PRISM_E_ARG, "null pointer argument");
+    if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k)) & 15)
+        return fail(PRISM_E_UNSUPPORTED, "q and k must be 16-byte aligned");
     if (top_k < 0 || !(top_p >= 0.0 && top_p <= 1.0)) return fail(PRISM_E_ARG, "need k >= 0 and 0 <= p <= 1");
     if (!std::isfinite(scale)) return fail(PRISM_E_ARG, "scale must be finite");
     const size_t need = prism_workspace_size(PRISM_OP_SELECT, N, heads, d, nb, cap);

@@ -4,8 +4,9 @@
 // probabilities P_i, and S_i = Top-k(P_i, k) U Top-p(P_i, p)).
 //
 // Kernels, in launch order:
-//   pool_kernel          float64 block means of Q and K per head (sums of at
-//                        most 256 bf16 values are exact in float64)
+//   pool_kernel          float64 block means of Q and K per head (16-byte
+//                        loads; sums of at most 256 bf16 values of moderate
+//                        range are exact in float64, whatever the order)
 //   logits_kernel        L[h][i][j] = fl32(scale * (Q_bar_i . K_bar_j)), the dot in
 //                        float64: the scores are rounded once, so they equal
 //                        the float64 definition's nearest float
@@ -44,26 +45,45 @@ __device__ __forceinline__ double load_as_double<float>(const float* p) {
     return static_cast<double>(*p);
 }
 
-// grid (nb, heads, 2): z = 0 pools q, z = 1 pools k.  256 threads: channel
-// c = t % D, row phase t / D; the phases are combined in phase order.
+// grid (nb, heads, 2): z = 0 pools q, z = 1 pools k.  Each lane loads 16
+// bytes (EPV channels) of a row; the 256 threads cover RPS rows at a time and
+// keep float64 partial sums, which are then added over the RPS row slots in
+// slot order.
 template <typename TIn, int D>
 __global__ void __launch_bounds__(256)
 pool_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, int64_t ld, int64_t hs,
             const int32_t* __restrict__ offs, int nb, int heads, double* __restrict__ pooled) {
-    constexpr int G = 256 / D;
-    __shared__ double part[G][D];
+    constexpr int EPV = 16 / static_cast<int>(sizeof(TIn));   // channels per lane
+    constexpr int LPR = D / EPV;                                // lanes per row
+    constexpr int RPS = 256 / LPR;                              // rows per step
+    __shared__ double part[RPS][D];
     const int i = blockIdx.x, h = blockIdx.y, which = blockIdx.z;
     const TIn* __restrict__ x = (which == 0 ? q : k) + static_cast<int64_t>(h) * hs;
-    const int c = threadIdx.x % D;
-    const int ph = threadIdx.x / D;
+    const int slot = threadIdx.x / LPR, cv = threadIdx.x % LPR;
     const int r0 = offs[i], r1 = offs[i + 1];
-    double s = 0.0;
-    for (int r = r0 + ph; r < r1; r += G) s += load_as_double(x + static_cast<int64_t>(r) * ld + c);
-    part[ph][c] = s;
+    double acc[EPV];
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) acc[e] = 0.0;
+    for (int r = r0 + slot; r < r1; r += RPS) {
+        const uint4 u = *reinterpret_cast<const uint4*>(x + static_cast<int64_t>(r) * ld + cv * EPV);
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+        if constexpr (EPV == 8) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                acc[2 * e] += static_cast<double>(bf16_to_f32(static_cast<uint16_t>(w[e] & 0xFFFFu)));
+                acc[2 * e + 1] += static_cast<double>(bf16_to_f32(static_cast<uint16_t>(w[e] >> 16)));
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[e] += static_cast<double>(__uint_as_float(w[e]));
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) part[slot][cv * EPV + e] = acc[e];
     __syncthreads();
-    if (ph == 0) {
+    for (int c = threadIdx.x; c < D; c += 256) {
         double t = part[0][c];
-        for (int g = 1; g < G; ++g) t += part[g][c];
+        for (int g = 1; g < RPS; ++g) t += part[g][c];
         pooled[((static_cast<int64_t>(which) * heads + h) * nb + i) * D + c] = t / static_cast<double>(r1 - r0);
     }
 }

@@ -154,6 +154,7 @@ def test_select_rejects():
     assert f(p=float("nan")) == 1
     assert f(cap=0) == 1
     assert f(q=None) == 1
+    assert f(q=A + 8) == 4                         # misaligned
     assert f(ws=None) == 5
     assert f(wsb=need - 1) == 5
 
