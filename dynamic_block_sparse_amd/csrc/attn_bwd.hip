@@ -23,8 +23,10 @@ namespace prism {
 
 // dQ keeps one K and one V tile in LDS and fits 256 registers, so two waves
 // share each SIMD (measured at 2K: 82 ms against 100 ms double-buffered at one
-// wave per SIMD).  dK/dV needs 384 registers, one wave per SIMD, and
-// double-buffers its Q and dO tiles instead.
+// wave per SIMD).  Its loads are split by phase: dP^T, which needs only V,
+// runs first while K is still landing; V(t+1) is loaded once every wave has
+// finished dP^T, K(t+1) once every wave has finished dQ^T.  dK/dV needs 384
+// registers, one wave per SIMD, and double-buffers its Q and dO tiles instead.
 
 template <int D>
 __global__ void __launch_bounds__(128, 2)
@@ -77,44 +79,57 @@ attn_dq_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
 
     TileDma<D, 2> dma;
     dma.init(ld, wave, lane);
-    auto issue = [&](int t, int b) {
-        dma.load(kbuf[b], kh_ + static_cast<int64_t>(t) * ld, wave);
-        dma.load(vbuf[b], vh_ + static_cast<int64_t>(t) * ld, wave);
-    };
-    auto compute = [&](int b) {
-        const uint16_t* kt = kbuf[b];
-        const uint16_t* vt = vbuf[b];
-        f32x16_t sa[2], pa[2];
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-            for (int x = 0; x < 16; ++x) sa[mt][x] = pa[mt][x] = 0.0f;
-#pragma unroll
-        for (int s = 0; s < KS; ++s)
-#pragma unroll
-            for (int mt = 0; mt < 2; ++mt) {
-                sa[mt] = mfma32(sw_read16<D>(kt, 32 * mt + col, 16 * s + 8 * hl), qb[s], sa[mt]);
-                pa[mt] = mfma32(sw_read16<D>(vt, 32 * mt + col, 16 * s + 8 * hl), db[s], pa[mt]);
-            }
-        sched_reads_ahead<4, 4, KS, 2>();
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-            for (int x = 0; x < 16; ++x) {
-                const float p = fast_exp2(fmaf(sa[mt][x], scale_log2, -lrow));
-                sa[mt][x] = p * (pa[mt][x] - drow);     // dS^T
-            }
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            const u32x4_t bs = pack_kstep(sa[ks >> 1], ks & 1);
-#pragma unroll
-            for (int m = 0; m < DM; ++m) acc[m] = mfma32(tr_operand<D>(kt, 16 * ks, 32 * m, lane), bs, acc[m]);
-        }
-    };
-
+    constexpr int PER = TileDma<D, 2>::PER;
+    const uint16_t* kt = kbuf[0];
+    const uint16_t* vt = vbuf[0];
     TileCursor cur;
     cur.init(si, offs, e0, e1);
-    tile_pipeline1(cur, issue, compute);
+    int t = cur.next();
+    if (t >= 0) {
+        dma.load(vbuf[0], vh_ + static_cast<int64_t>(t) * ld, wave);
+        dma.load(kbuf[0], kh_ + static_cast<int64_t>(t) * ld, wave);
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(PER) : "memory");   // this wave's V loads
+        __syncthreads();
+        while (true) {
+            f32x16_t sa[2], pa[2];
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                for (int x = 0; x < 16; ++x) sa[mt][x] = pa[mt][x] = 0.0f;
+            // dP^T first: it needs only V, while K may still be landing
+#pragma unroll
+            for (int s = 0; s < KS; ++s)
+#pragma unroll
+                for (int mt = 0; mt < 2; ++mt)
+                    pa[mt] = mfma32(sw_read16<D>(vt, 32 * mt + col, 16 * s + 8 * hl), db[s], pa[mt]);
+            sched_reads_ahead<2, 2, KS, 2>();
+            dma_join();                        // K(t) landed; every wave is done with V(t)
+            const int tn = cur.next();
+            if (tn >= 0) dma.load(vbuf[0], vh_ + static_cast<int64_t>(tn) * ld, wave);
+#pragma unroll
+            for (int s = 0; s < KS; ++s)
+#pragma unroll
+                for (int mt = 0; mt < 2; ++mt)
+                    sa[mt] = mfma32(sw_read16<D>(kt, 32 * mt + col, 16 * s + 8 * hl), qb[s], sa[mt]);
+            sched_reads_ahead<2, 2, KS, 2>();
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                for (int x = 0; x < 16; ++x) {
+                    const float p = fast_exp2(fmaf(sa[mt][x], scale_log2, -lrow));
+                    sa[mt][x] = p * (pa[mt][x] - drow);     // dS^T
+                }
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const u32x4_t bs = pack_kstep(sa[ks >> 1], ks & 1);
+#pragma unroll
+                for (int m = 0; m < DM; ++m) acc[m] = mfma32(tr_operand<D>(kt, 16 * ks, 32 * m, lane), bs, acc[m]);
+            }
+            dma_join();                        // V(tn) landed; every wave is done with K(t)
+            if (tn < 0) break;
+            dma.load(kbuf[0], kh_ + static_cast<int64_t>(tn) * ld, wave);
+        }
+    }
     uint16_t* out = dq + row * ld + h * hs;
 #pragma unroll
     for (int m = 0; m < DM; ++m)

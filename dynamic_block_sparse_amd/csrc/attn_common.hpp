@@ -192,8 +192,8 @@ struct TileCursor {
 
 // Double-buffered walk over the tiles of `cur`: tile t+1 is loaded into
 // buffer b^1 while tile t, in buffer b, is used.  (The dK/dV kernel; the
-// forward and dQ kernels use one buffer and a second resident workgroup per
-// SIMD instead, see below.)
+// forward and dQ kernels keep one tile of each operand and a second resident
+// workgroup per SIMD instead, loading by phase.)
 template <class Issue, class Compute>
 __device__ __forceinline__ void tile_pipeline(TileCursor& cur, Issue&& issue, Compute&& compute) {
     int t = cur.next();
@@ -206,21 +206,6 @@ __device__ __forceinline__ void tile_pipeline(TileCursor& cur, Issue&& issue, Co
         compute(b);
         dma_join();
         if (t < 0) return;
-    }
-}
-
-// Single-buffered walk: load a tile, use it, load the next.  With a 32 KB
-// footprint (d = 128) four workgroups share a CU, two waves per SIMD, so one
-// workgroup's loads overlap another's compute.
-template <class Issue, class Compute>
-__device__ __forceinline__ void tile_pipeline1(TileCursor& cur, Issue&& issue, Compute&& compute) {
-    int t = cur.next();
-    while (t >= 0) {
-        issue(t, 0);
-        dma_join();
-        compute(0);
-        t = cur.next();
-        __syncthreads();
     }
 }
 
