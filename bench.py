@@ -40,7 +40,7 @@ CSRC = os.path.join(ROOT, "dynamic_block_sparse_amd", "csrc")
 # kernels launched by one prism_sparse_attn_bwd call (csr_scan also runs in prism_select)
 BWD_KERNELS = ("attn_bwd_dot_kernel", "tr_count_kernel", "csr_scan_kernel", "tr_fill_kernel", "tr_sort_kernel",
                "attn_dq_mfma_kernel", "attn_dkdv_mfma_kernel")
-PMC_REGEX = "attn_|permute_rows|tr_count|tr_fill|tr_sort|csr_scan"
+PMC_REGEX = "attn_|permute_heads|tr_count|tr_fill|tr_sort|csr_scan"
 ATTN_REGEX = "attn_(fwd|dq|dkdv)_mfma"
 
 
@@ -118,7 +118,10 @@ def cpu_baseline(cfg, x, zone_shape_host, budget_s):
     sc = float(np.float32(1.0 / math.sqrt(cfg.d)))
     pi = orc.permutation(cfg.T, cfg.H, cfg.W, zone_shape_host)
     offs, NB = orc.block_layout(zone_shape_host)
-    Qp, Kp, Vp, dOp = (orc.to_block_major(x[n][:, 0:1, :].float().cpu().numpy(), pi) for n in ("q", "k", "v", "do"))
+    names = ("q", "k", "v", "do") if cfg.backward else ("q", "k", "v")
+    Qp, Kp, Vp, *rest = (orc.to_block_major(x[n][:, 0:1, :].float().cpu().numpy(), pi) for n in names)
+    dOp = rest[0] if rest else None
+    per_pair = 14.0 if cfg.backward else 4.0
     t0 = time.perf_counter()
     Kb = orc.pool_blocks(Kp, offs, 0)
     Qb = orc.pool_blocks(Qp, offs, 0)
@@ -129,17 +132,18 @@ def cpu_baseline(cfg, x, zone_shape_host, budget_s):
         L = orc.block_logits(Qb[i:i + 1], Kb, sc)[0]
         sel, _ = orc.select_row(L, cfg.top_k, cfg.top_p)
         orc.attn_fwd_block(Qp, Kp, Vp, offs, sel, i, 0, sc)
-        orc.attn_bwd_block(Qp, Kp, Vp, dOp, offs, sel, i, 0, sc)
+        if cfg.backward:
+            orc.attn_bwd_block(Qp, Kp, Vp, dOp, offs, sel, i, 0, sc)
         Bi = offs[i + 1] - offs[i]
-        flops += 14.0 * Bi * float(sum(offs[j + 1] - offs[j] for j in sel)) * cfg.d
+        flops += per_pair * Bi * float(sum(offs[j + 1] - offs[j] for j in sel)) * cfg.d
         nblocks += 1
         if time.perf_counter() - t0 > budget_s:
             break
     dt = time.perf_counter() - t0
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
             "sample": f"float64 oracle pooling of head 0 (all {NB} blocks) then per query block: scores, "
-                      f"selection, attention forward and backward, for {nblocks} query blocks of head 0 "
-                      f"in seeded random order ({dt:.1f} s)"}
+                      f"selection, attention forward{' and backward' if cfg.backward else ''}, for {nblocks} "
+                      f"query blocks of head 0 in seeded random order ({dt:.1f} s)"}
 
 
 def _run(cmd, log, limit):
@@ -227,10 +231,12 @@ def profile(args):
     import workloads.synth as synth
     cfg = synth.CONFIGS[args.config]
     es = 2 if cfg.dtype == "bf16" else 4
-    copy_bytes = cfg.N * cfg.d * es          # one permute launch reads and writes one head of one tensor
+    copy_bytes = cfg.N * cfg.heads * cfg.d * es   # one permute launch reads and writes one whole tensor
     scale = {}
     for ctr, rows_ in res.items():
-        vals = [v for (_, k), v in rows_ if "permute_rows" in k]
+        vals = [v for (_, k), v in rows_ if "permute_heads" in k]
+        if not vals:
+            sys.exit("[profile] no permutation kernel in the counter pass: nothing to calibrate against")
         scale[ctr] = copy_bytes / (1024.0 * (sum(vals) / len(vals)))
     # the backward call: the dispatches from attn_bwd_dot through attn_dkdv
     per_call = {}
@@ -246,8 +252,8 @@ def profile(args):
         for ctr, show in pcmds.items():
             fh.write(f"# {ctr} pass: {show}\n")
         fh.write(f"# made by: python bench.py --profile {out} --config {args.config}\n")
-        fh.write(f"# calibration: a permute launch moves {copy_bytes} bytes each way; the counters (KiB per\n"
-                 f"# dispatch) are scaled by algorithmic/counted on that copy kernel\n\n")
+        fh.write(f"# calibration: a permute launch (prism_block_permute_heads) moves {copy_bytes} bytes each way;\n"
+                 f"# the counters (KiB per dispatch) are scaled by algorithmic/counted on that copy kernel\n\n")
         for ctr in res:
             fh.write(f"scale_{ctr.lower()}: {scale[ctr]:.4f}\n")
         for ctr, items in per_call.items():
