@@ -8,8 +8,9 @@
 //                        loads; sums of at most 256 bf16 values of moderate
 //                        range are exact in float64, whatever the order)
 //   logits_kernel        L[h][i][j] = fl32(scale * (Q_bar_i . K_bar_j)), the dot in
-//                        float64: the scores are rounded once, so they equal
-//                        the float64 definition's nearest float
+//                        float64 on MFMA: the scores are rounded once, so they
+//                        equal the float64 definition's nearest float up to
+//                        rare one-ulp differences from the summation order
 //   select_reg_kernel    per row (up to 16384 blocks): the row's order-
 //                        preserving 32-bit score keys and their softmax masses
 //                        (float64 exp, as 2^-48 fixed-point integers) are held
@@ -91,63 +92,87 @@ pool_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, int64_t ld, in
 // ---------------------------------------------------------------- scores
 
 constexpr int kLT = 128;  // output tile (rows and columns)
-constexpr int kLK = 8;    // reduction chunk
+constexpr int kLC = 16;   // channels per LDS chunk
 
-// One workgroup per 128 x 128 tile of one head's scores; thread (tx, ty) owns
-// rows ty + 16 a and columns tx + 16 b (a, b < 8), 64 float64 accumulators, so
-// every value read from LDS feeds 8 fused multiply-adds.  The reduction over
-// the d channels runs in ascending order for every score.
+typedef double d4_t __attribute__((ext_vector_type(4)));
+
+// One workgroup per 128 x 128 tile of one head's scores, on float64 MFMA
+// (v_mfma_f64_16x16x4f64; lane l holds A[l % 16][l / 16] and B[l / 16][l % 16],
+// and register r of the result D[4 r + l / 16][l % 16], checked with a probe).
+// Wave (wi, wj) computes the 64 x 64 sub-tile at (64 wi, 64 wj) as 4 x 4 MFMA
+// tiles.  The pooled means are staged in LDS channel-major, 16 channels at a
+// time.  Each score is rounded once to fp32 after the scale.
 template <int D>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(256, 2)
 logits_kernel(const double* __restrict__ pooled, int nb, int heads, double scale, float* __restrict__ logits) {
-    __shared__ double As[kLK][kLT];
-    __shared__ double Bs[kLK][kLT];
+    __shared__ double Qs[kLC][kLT + 2];
+    __shared__ double Ks[kLC][kLT + 2];
     const int h = blockIdx.z;
     const int i0 = blockIdx.y * kLT, j0 = blockIdx.x * kLT;
     const double* __restrict__ Qb = pooled + static_cast<int64_t>(h) * nb * D;
     const double* __restrict__ Kb = pooled + (static_cast<int64_t>(heads) + h) * nb * D;
-    const int tx = threadIdx.x % 16, ty = threadIdx.x / 16;
-    double acc[8][8];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int wi = wave >> 1, wj = wave & 1;
+    const int lr = lane & 15, lk = lane >> 4;
+    d4_t acc[4][4];
 #pragma unroll
-    for (int a = 0; a < 8; ++a)
+    for (int x = 0; x < 4; ++x)
 #pragma unroll
-        for (int b = 0; b < 8; ++b) acc[a][b] = 0.0;
-    for (int c0 = 0; c0 < D; c0 += kLK) {
-        // 128 rows x 8 channels of each operand: 1024 values, 4 per thread
+        for (int y = 0; y < 4; ++y) acc[x][y] = d4_t{0.0, 0.0, 0.0, 0.0};
+    // staging: thread t brings 8 channels (sc .. sc+7) of row t / 2 of each
+    // operand; the next chunk's global loads are in flight while this one is used
+    const int srow = threadIdx.x >> 1, sc = (threadIdx.x & 1) * 8;
+    const int gi = i0 + srow, gj = j0 + srow;
+    double qv[8], kv[8];
+    auto fetch = [&](int c0) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int idx = threadIdx.x + e * 256;
-            const int row = idx / kLK, col = idx % kLK;
-            const int gi = i0 + row, gj = j0 + row;
-            As[col][row] = gi < nb ? Qb[static_cast<int64_t>(gi) * D + c0 + col] : 0.0;
-            Bs[col][row] = gj < nb ? Kb[static_cast<int64_t>(gj) * D + c0 + col] : 0.0;
+        for (int e = 0; e < 8; e += 2) {
+            const double2 q2 = gi < nb ? *reinterpret_cast<const double2*>(Qb + static_cast<int64_t>(gi) * D + c0 + sc + e)
+                                       : double2{0.0, 0.0};
+            const double2 k2 = gj < nb ? *reinterpret_cast<const double2*>(Kb + static_cast<int64_t>(gj) * D + c0 + sc + e)
+                                       : double2{0.0, 0.0};
+            qv[e] = q2.x;
+            qv[e + 1] = q2.y;
+            kv[e] = k2.x;
+            kv[e + 1] = k2.y;
+        }
+    };
+    fetch(0);
+    for (int c0 = 0; c0 < D; c0 += kLC) {
+        __syncthreads();   // the previous chunk has been read
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            Qs[sc + e][srow] = qv[e];
+            Ks[sc + e][srow] = kv[e];
         }
         __syncthreads();
+        if (c0 + kLC < D) fetch(c0 + kLC);
 #pragma unroll
-        for (int kk = 0; kk < kLK; ++kk) {
-            double a[8], b[8];
+        for (int kk = 0; kk < kLC; kk += 4) {
+            double av[4], bv[4];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                a[e] = As[kk][ty + 16 * e];
-                b[e] = Bs[kk][tx + 16 * e];
+            for (int x = 0; x < 4; ++x) av[x] = Qs[kk + lk][64 * wi + 16 * x + lr];
+#pragma unroll
+            for (int y = 0; y < 4; ++y) bv[y] = Ks[kk + lk][64 * wj + 16 * y + lr];
+#pragma unroll
+            for (int x = 0; x < 4; ++x)
+#pragma unroll
+                for (int y = 0; y < 4; ++y) acc[x][y] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[x], bv[y], acc[x][y], 0, 0, 0);
+        }
+    }
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int oi = i0 + 64 * wi + 16 * x + 4 * r + lk;
+            if (oi >= nb) continue;
+#pragma unroll
+            for (int y = 0; y < 4; ++y) {
+                const int oj = j0 + 64 * wj + 16 * y + lr;
+                if (oj < nb) logits[(static_cast<int64_t>(h) * nb + oi) * nb + oj] = static_cast<float>(scale * acc[x][y][r]);
             }
-#pragma unroll
-            for (int x = 0; x < 8; ++x)
-#pragma unroll
-                for (int y = 0; y < 8; ++y) acc[x][y] = fma(a[x], b[y], acc[x][y]);
         }
-        __syncthreads();
-    }
-#pragma unroll
-    for (int x = 0; x < 8; ++x) {
-        const int gi = i0 + ty + 16 * x;
-        if (gi >= nb) continue;
-#pragma unroll
-        for (int y = 0; y < 8; ++y) {
-            const int gj = j0 + tx + 16 * y;
-            if (gj < nb) logits[(static_cast<int64_t>(h) * nb + gi) * nb + gj] = static_cast<float>(scale * acc[x][y]);
-        }
-    }
 }
 
 // ---------------------------------------------------------------- selection
