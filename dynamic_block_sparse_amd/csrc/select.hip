@@ -377,14 +377,54 @@ select_count_kernel(const float* __restrict__ logits, int nb, int top_k, double 
     }
 }
 
+// Wave-wide sums with DPP lane exchanges instead of LDS shuffles: two quad
+// permutes and the half-row and row mirrors leave every lane holding the sum
+// of its 16-lane row; the four row sums are then read out as scalars.  The
+// 64-bit sum adds the 32-bit halves with carry, so it is exact.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ unsigned long long dpp_add_u64(unsigned long long v) {
+    const uint32_t lo = dpp_u32<CTRL>(static_cast<uint32_t>(v));
+    const uint32_t hi = dpp_u32<CTRL>(static_cast<uint32_t>(v >> 32));
+    return v + ((static_cast<unsigned long long>(hi) << 32) | lo);
+}
+__device__ __forceinline__ uint32_t wave_sum_dpp(uint32_t v) {
+    v += dpp_u32<0xB1>(v);    // quad_perm [1,0,3,2]
+    v += dpp_u32<0x4E>(v);    // quad_perm [2,3,0,1]
+    v += dpp_u32<0x141>(v);   // row_half_mirror
+    v += dpp_u32<0x140>(v);   // row_mirror
+    return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 0)) +
+           static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 16)) +
+           static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 32)) +
+           static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 48));
+}
+__device__ __forceinline__ unsigned long long wave_sum_dpp(unsigned long long v) {
+    v = dpp_add_u64<0xB1>(v);
+    v = dpp_add_u64<0x4E>(v);
+    v = dpp_add_u64<0x141>(v);
+    v = dpp_add_u64<0x140>(v);
+    unsigned long long t = 0;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(v)), 16 * r));
+        const uint32_t hi =
+            static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(v >> 32)), 16 * r));
+        t += (static_cast<unsigned long long>(hi) << 32) | lo;
+    }
+    return t;
+}
+
 // Sums over the workgroup of a (count, mass) pair; every thread gets the
 // totals.  `slot` alternates between calls so that one barrier per call
 // suffices: a slot is rewritten only after every thread has passed the
 // barrier of the call in between, i.e. after it read the slot.
 __device__ __forceinline__ void block_sum_cm(uint32_t& c, unsigned long long& m, uint32_t (*rc)[kSelThreads / kWave],
                                              unsigned long long (*rm)[kSelThreads / kWave], int& slot) {
-    c = wave_sum(c);
-    m = wave_sum(m);
+    c = wave_sum_dpp(c);
+    m = wave_sum_dpp(m);
     const int lane = threadIdx.x & (kWave - 1);
     const int wid = threadIdx.x / kWave;
     if (lane == 0) {
@@ -402,11 +442,36 @@ __device__ __forceinline__ void block_sum_cm(uint32_t& c, unsigned long long& m,
     slot ^= 1;
 }
 
+// Single-value forms of block_sum_cm (same slot discipline).
+__device__ __forceinline__ uint32_t block_sum_c(uint32_t c, uint32_t (*rc)[kSelThreads / kWave], int& slot) {
+    c = wave_sum_dpp(c);
+    if ((threadIdx.x & (kWave - 1)) == 0) rc[slot][threadIdx.x / kWave] = c;
+    __syncthreads();
+    c = 0;
+#pragma unroll
+    for (int w = 0; w < kSelThreads / kWave; ++w) c += rc[slot][w];
+    slot ^= 1;
+    return c;
+}
+__device__ __forceinline__ unsigned long long block_sum_m(unsigned long long m,
+                                                          unsigned long long (*rm)[kSelThreads / kWave], int& slot) {
+    m = wave_sum_dpp(m);
+    if ((threadIdx.x & (kWave - 1)) == 0) rm[slot][threadIdx.x / kWave] = m;
+    __syncthreads();
+    m = 0;
+#pragma unroll
+    for (int w = 0; w < kSelThreads / kWave; ++w) m += rm[slot][w];
+    slot ^= 1;
+    return m;
+}
+
 // One workgroup per (row i, head h); thread t holds blocks t + 256 e, e < E.
 // The kept prefix is {key > u} plus the first ties of key u in index order,
 // where u is the largest key value with count(key >= u) >= max(k, 1) and
-// mass(key >= u) >= p * Z; both sums only grow as u falls, so u is found by
-// bisection between the row's smallest and largest keys.
+// mass(key >= u) >= p * Z.  Both sums only grow as u falls, so u is found by
+// bisection: first on the count alone (u <= tk, the max(k, 1)-th largest
+// key), then, only for rows whose top max(k, 1) blocks hold less than p Z, on
+// the mass below tk.
 template <int E>
 __global__ void __launch_bounds__(kSelThreads)
 select_reg_kernel(const float* __restrict__ logits, int nb, int top_k, double top_p, int32_t* __restrict__ row_count,
@@ -449,20 +514,36 @@ select_reg_kernel(const float* __restrict__ logits, int nb, int top_k, double to
         jlim = -1;
     } else {
         int slot = 0;
-        uint32_t lo = kmin, hi = kmax + 1u;   // the predicate holds at lo, fails at hi
+        // 1) tk = the largest key with count(key >= tk) >= kk: a count-only bisection
+        uint32_t lo = kmin, hi = kmax + 1u;   // count >= kk at lo, < kk at hi
         while (hi - lo > 1u) {
             const uint32_t mid = lo + (hi - lo) / 2u;
             uint32_t c = 0;
-            unsigned long long m = 0;
 #pragma unroll
-            for (int e = 0; e < E; ++e) {
-                const bool in = key[e] >= mid;
-                c += in ? 1u : 0u;
-                m += in ? ms[e] : 0ull;
-            }
-            block_sum_cm(c, m, rc, rm, slot);
-            if (c >= kk && static_cast<double>(m) >= target) lo = mid;
+            for (int e = 0; e < E; ++e) c += key[e] >= mid ? 1u : 0u;
+            c = block_sum_c(c, rc, slot);
+            if (c >= kk) lo = mid;
             else hi = mid;
+        }
+        // 2) if the blocks at or above tk already hold p Z, the boundary is tk;
+        // otherwise it lies below tk, where the count condition always holds,
+        //    and a mass-only bisection finds the largest u with mass(key >= u) >= p Z
+        unsigned long long mk = 0;
+#pragma unroll
+        for (int e = 0; e < E; ++e) mk += key[e] >= lo ? ms[e] : 0ull;
+        mk = block_sum_m(mk, rm, slot);
+        if (!(static_cast<double>(mk) >= target)) {
+            hi = lo;                           // mass fails at tk
+            lo = kmin;                         // and holds at the smallest key (all of Z)
+            while (hi - lo > 1u) {
+                const uint32_t mid = lo + (hi - lo) / 2u;
+                unsigned long long m = 0;
+#pragma unroll
+                for (int e = 0; e < E; ++e) m += key[e] >= mid ? ms[e] : 0ull;
+                m = block_sum_m(m, rm, slot);
+                if (static_cast<double>(m) >= target) lo = mid;
+                else hi = mid;
+            }
         }
         thr = lo;
         // blocks strictly above the boundary key, and the ties at it
