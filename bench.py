@@ -37,10 +37,15 @@ METRIC = "effective sparse-attn TFLOP/s fwd+bwd at 2K tokens; % of bf16 MFMA pea
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
 CSRC = os.path.join(ROOT, "dynamic_block_sparse_amd", "csrc")
-# kernels launched by one prism_sparse_attn_bwd call (csr_scan also runs in prism_select)
-BWD_KERNELS = ("attn_bwd_dot_kernel", "tr_count_kernel", "csr_scan_kernel", "tr_fill_kernel", "tr_sort_kernel",
-               "attn_dq_mfma_kernel", "attn_dkdv_mfma_kernel")
-PMC_REGEX = "attn_|permute_heads|tr_count|tr_fill|tr_sort|csr_scan"
+# kernels launched by one tile-order build, one prism_sparse_attn_fwd and one
+# prism_sparse_attn_bwd call, with their launch counts (csr_scan and fill_i32
+# also run elsewhere, always over the same heads x blocks shape)
+ORDER_KERNELS = {"fill_i32_kernel": 2, "order_count_kernel": 1, "csr_scan_kernel": 1, "order_fill_kernel": 1}
+FWD_KERNELS = dict(ORDER_KERNELS, attn_fwd_mfma_kernel=1)
+BWD_KERNELS = {"attn_bwd_dot_kernel": 1, "fill_i32_kernel": 2 + 2, "tr_count_kernel": 1, "csr_scan_kernel": 1 + 1,
+               "tr_fill_kernel": 1, "tr_sort_kernel": 1, "order_count_kernel": 1, "order_fill_kernel": 1,
+               "attn_dq_mfma_kernel": 1, "attn_dkdv_mfma_kernel": 1}
+PMC_REGEX = "attn_|permute_heads|tr_count|tr_fill|tr_sort|csr_scan|order_|fill_i32"
 ATTN_REGEX = "attn_(fwd|dq|dkdv)_mfma"
 
 
@@ -195,8 +200,8 @@ def profile(args):
     stats = glob.glob(os.path.join(raw, "trace", "**", "*kernel_stats.csv"), recursive=True)
     rows = list(csv.DictReader(open(stats[0])))
     avg = {_short(r["Name"]): float(r["AverageNs"]) for r in rows}
-    fwd_ns = sum(v for k, v in avg.items() if k.startswith("attn_fwd_mfma_kernel"))
-    bwd_ns = sum(v for k, v in avg.items() if k.split("<")[0] in BWD_KERNELS)
+    fwd_ns = sum(v * FWD_KERNELS.get(k.split("<")[0], 0) for k, v in avg.items())
+    bwd_ns = sum(v * BWD_KERNELS.get(k.split("<")[0], 0) for k, v in avg.items())
     with open(os.path.join(out, f"attn_{args.config}_kernel_stats.txt"), "w") as fh:
         fh.write(f"# rocprofv3 kernel statistics, {args.config} workload, 4 steps (1 warm-up)\n")
         fh.write("# command: " + tshow + "\n")
@@ -214,8 +219,8 @@ def profile(args):
                      f"{float(r['TotalDurationNs']) / 1e6:10.3f} {float(r['Percentage']):6.2f}\n")
         fh.write(f"{'other (torch: synthetic inputs and bookkeeping, outside the timed path)':62s} {other[0]:6d} "
                  f"{'':>10s} {other[1] / 1e6:10.3f} {other[2]:6.2f}\n")
-        fh.write(f"\nprism_sparse_attn_fwd call (sum of its kernels' average durations): {fwd_ns / 1e6:.3f} ms\n")
-        fh.write(f"prism_sparse_attn_bwd call (sum of its kernels' average durations): {bwd_ns / 1e6:.3f} ms\n")
+        fh.write(f"\nprism_sparse_attn_fwd call (its kernels' average durations x launches): {fwd_ns / 1e6:.3f} ms\n")
+        fh.write(f"prism_sparse_attn_bwd call (its kernels' average durations x launches): {bwd_ns / 1e6:.3f} ms\n")
         if bench_line:
             fh.write(f"bench stage_ms of the same run (HIP events): {json.dumps(bench_line.get('stage_ms'))}\n")
     # counters: one pass each
@@ -350,6 +355,8 @@ def main():
                          device="cuda")
     ws_bwd = torch.empty(P.prism_workspace_size(P.OP_ATTN_BWD, cfg.N, hc, cfg.d, nb, cap), dtype=torch.uint8,
                          device="cuda")
+    ws_fwd = torch.empty(P.prism_workspace_size(P.OP_ATTN_FWD, cfg.N, hc, cfg.d, nb, cap), dtype=torch.uint8,
+                         device="cuda")
     C = cfg.heads * cfg.d
     stages = ["shapes", "permute_in", "select", "attn_fwd", "attn_bwd", "permute_out"]
 
@@ -368,7 +375,7 @@ def main():
                            s.offsets, s.idx, cap, s.total, ws_sel)
             ev[3 + 3 * g].record()
             P.prism_sparse_attn_fwd(q, k, v, o, lse, cfg.N, hc, cfg.d, ld, hs, path.block_offsets, nb, s.offsets,
-                                    s.idx, cap, sc)
+                                    s.idx, cap, sc, ws=ws_fwd)
             ev[4 + 3 * g].record()
             if cfg.backward:
                 do_, gq, gk, gv = (t[:, h0:h0 + hc] for t in (dop,) + grads)

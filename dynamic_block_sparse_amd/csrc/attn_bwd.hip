@@ -27,6 +27,12 @@ namespace prism {
 // runs first while K is still landing; V(t+1) is loaded once every wave has
 // finished dP^T, K(t+1) once every wave has finished dQ^T.  dK/dV needs 384
 // registers, one wave per SIMD, and double-buffers its Q and dO tiles instead.
+//
+// dQ takes its query tiles in the visiting order built by launch_tile_order
+// (grouped by first selected key block).  dK/dV keeps raster order: grouping
+// its key tiles by the first query block that selects them was measured 1.6%
+// slower at 2K, where neighbouring key tiles already share most of their
+// query tiles in L2.
 
 template <int D>
 __global__ void __launch_bounds__(128, 2)
@@ -34,12 +40,12 @@ attn_dq_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
                     const uint16_t* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ Dq,
                     uint16_t* __restrict__ dq, int64_t N, int64_t ld, int64_t hs, const int32_t* __restrict__ offs,
                     int nb, const int32_t* __restrict__ sel_off, const int32_t* __restrict__ sel_idx, int64_t cap,
-                    float scale_log2, float scale) {
+                    const int32_t* __restrict__ order, float scale_log2, float scale) {
     __shared__ uint16_t kbuf[1][64 * D], vbuf[1][64 * D];
     const int ntiles = static_cast<int>(N / 64);
     const int wg = xcd_remap(blockIdx.x);
     const int h = wg / ntiles;
-    const int64_t p0 = static_cast<int64_t>(wg % ntiles) * 64;
+    const int64_t p0 = static_cast<int64_t>(tile_of(order, wg, ntiles)) * 64;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int hl = lane >> 5, col = lane & 31;
@@ -269,7 +275,8 @@ attn_dkdv_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
 hipError_t launch_attn_bwd_mfma(const void* q, const void* k, const void* v, const void* dout, const float* lse,
                                 const float* Dq, void* dq, void* dk, void* dv, int64_t N, int heads, int d, int64_t ld,
                                 int64_t hs, const int32_t* offs, int nb, const int32_t* so, const int32_t* si,
-                                const int32_t* to, const int32_t* ti, int64_t cap, float scale, hipStream_t s) {
+                                const int32_t* to, const int32_t* ti, int64_t cap, const int32_t* qorder,
+                                float scale, hipStream_t s) {
     const dim3 grid(static_cast<unsigned>(N / 64 * heads));
     const float sl2 = scale * kLog2e;
     const uint16_t* Q = static_cast<const uint16_t*>(q);
@@ -281,14 +288,14 @@ hipError_t launch_attn_bwd_mfma(const void* q, const void* k, const void* v, con
     uint16_t* dV = static_cast<uint16_t*>(dv);
     if (d == 128) {
         hipLaunchKernelGGL(attn_dq_mfma_kernel<128>, grid, dim3(128), 0, s, Q, K, V, O, lse, Dq, dQ, N, ld, hs, offs,
-                           nb, so, si, cap, sl2, scale);
+                           nb, so, si, cap, qorder, sl2, scale);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL(attn_dkdv_mfma_kernel<128>, grid, dim3(128), 0, s, Q, K, V, O, lse, Dq, dK, dV, N, ld, hs,
                            offs, nb, to, ti, cap, sl2, scale);
     } else {
         hipLaunchKernelGGL(attn_dq_mfma_kernel<64>, grid, dim3(128), 0, s, Q, K, V, O, lse, Dq, dQ, N, ld, hs, offs,
-                           nb, so, si, cap, sl2, scale);
+                           nb, so, si, cap, qorder, sl2, scale);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL(attn_dkdv_mfma_kernel<64>, grid, dim3(128), 0, s, Q, K, V, O, lse, Dq, dK, dV, N, ld, hs,

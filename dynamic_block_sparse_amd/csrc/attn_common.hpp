@@ -220,6 +220,13 @@ __device__ __forceinline__ int xcd_remap(int w) {
     return (w % 8) * (G / 8) + w / 8;
 }
 
+// tile visited by workgroup wg (an entry outside the head's range, which a
+// consistent set of block offsets never leaves, falls back to raster order)
+__device__ __forceinline__ int tile_of(const int32_t* __restrict__ order, int wg, int ntiles) {
+    const int t = order[wg];
+    return static_cast<unsigned>(t) < static_cast<unsigned>(ntiles) ? t : wg % ntiles;
+}
+
 __device__ __forceinline__ int find_block(const int32_t* __restrict__ offs, int nb, int64_t p) {
     int a = 0, b = nb;
     while (b - a > 1) {

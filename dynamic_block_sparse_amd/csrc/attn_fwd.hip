@@ -23,18 +23,23 @@ namespace prism {
 // P V), V(t+1) once every wave has finished P V (it lands during the next
 // scores).  Each phase boundary is one wait-and-barrier.  (Measured at 2K: 71
 // ms, against 79 ms with double-buffered K and V at one wave per SIMD.)
+//
+// Query tiles are taken in the visiting order built by launch_tile_order
+// (tiles grouped by their first selected key block): order[h * ntiles + j] is
+// the j-th tile of head h.
 
 template <int D>
 __global__ void __launch_bounds__(128, 2)
 attn_fwd_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
                      uint16_t* __restrict__ o, float* __restrict__ lse, int64_t N, int64_t ld, int64_t hs,
                      const int32_t* __restrict__ offs, int nb, const int32_t* __restrict__ sel_off,
-                     const int32_t* __restrict__ sel_idx, int64_t cap, float scale_log2) {
+                     const int32_t* __restrict__ sel_idx, int64_t cap, const int32_t* __restrict__ order,
+                     float scale_log2) {
     __shared__ uint16_t kbuf[64 * D], vbuf[64 * D];
     const int ntiles = static_cast<int>(N / 64);
     const int wg = xcd_remap(blockIdx.x);
     const int h = wg / ntiles;
-    const int64_t p0 = static_cast<int64_t>(wg % ntiles) * 64;
+    const int64_t p0 = static_cast<int64_t>(tile_of(order, wg, ntiles)) * 64;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int hl = lane >> 5, col = lane & 31;
@@ -137,11 +142,9 @@ attn_fwd_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
 
 // ---------------------------------------------------------------- launcher
 
-// ---------------------------------------------------------------- launchers
-
 hipError_t launch_attn_fwd_mfma(const void* q, const void* k, const void* v, void* o, float* lse, int64_t N, int heads,
                                 int d, int64_t ld, int64_t hs, const int32_t* offs, int nb, const int32_t* so,
-                                const int32_t* si, int64_t cap, float scale, hipStream_t s) {
+                                const int32_t* si, int64_t cap, const int32_t* order, float scale, hipStream_t s) {
     const dim3 grid(static_cast<unsigned>(N / 64 * heads));
     const float sl2 = scale * kLog2e;
     const uint16_t* Q = static_cast<const uint16_t*>(q);
@@ -150,10 +153,10 @@ hipError_t launch_attn_fwd_mfma(const void* q, const void* k, const void* v, voi
     uint16_t* O = static_cast<uint16_t*>(o);
     if (d == 128)
         hipLaunchKernelGGL(attn_fwd_mfma_kernel<128>, grid, dim3(128), 0, s, Q, K, V, O, lse, N, ld, hs, offs, nb, so,
-                           si, cap, sl2);
+                           si, cap, order, sl2);
     else
         hipLaunchKernelGGL(attn_fwd_mfma_kernel<64>, grid, dim3(128), 0, s, Q, K, V, O, lse, N, ld, hs, offs, nb, so,
-                           si, cap, sl2);
+                           si, cap, order, sl2);
     return hipGetLastError();
 }
 

@@ -73,6 +73,8 @@ struct BwdWs {
     int32_t* tr_offsets;
     int32_t* tr_idx;
     int32_t* scratch;
+    int32_t* ostart;   // bucket starts of the tile order
+    int32_t* qorder;   // dQ tile order
 };
 BwdWs carve_bwd(Carver& c, int64_t N, int64_t heads, int64_t nb, int64_t cap) {
     BwdWs w;
@@ -81,6 +83,22 @@ BwdWs carve_bwd(Carver& c, int64_t N, int64_t heads, int64_t nb, int64_t cap) {
     w.tr_offsets = c.take<int32_t>(heads * (nb + 1));
     w.tr_idx = c.take<int32_t>(heads * cap);
     w.scratch = c.take<int32_t>(heads * cap);
+    w.ostart = c.take<int32_t>(heads * (nb + 1));
+    w.qorder = c.take<int32_t>(heads * (N / 64));
+    return w;
+}
+
+// Visiting order of the 64-token tiles for the attention kernels.
+struct OrderWs {
+    int32_t* bucket;
+    int32_t* start;
+    int32_t* order;
+};
+OrderWs carve_order(Carver& c, int64_t N, int64_t heads, int64_t nb) {
+    OrderWs w;
+    w.bucket = c.take<int32_t>(heads * nb);
+    w.start = c.take<int32_t>(heads * (nb + 1));
+    w.order = c.take<int32_t>(heads * (N / 64));
     return w;
 }
 
@@ -178,7 +196,11 @@ size_t prism_workspace_size(int32_t op, int64_t N, int32_t heads, int32_t d, int
             carve_select(c, heads, d, nb);
             return c.off;
         }
-        case PRISM_OP_ATTN_FWD: return 0;
+        case PRISM_OP_ATTN_FWD: {
+            Carver c(nullptr);
+            carve_order(c, N, heads, nb);
+            return c.off;
+        }
         case PRISM_OP_ATTN_BWD: {
             Carver c(nullptr);
             carve_bwd(c, N, heads, nb, cap);
@@ -311,16 +333,23 @@ prism_status prism_sparse_attn_fwd(const void* q, const void* k, const void* v, 
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
         return fail(PRISM_E_UNSUPPORTED, "token tensors must be 16-byte aligned");
     if (!std::isfinite(scale) || !(scale > 0.0f)) return fail(PRISM_E_ARG, "scale must be finite and positive");
-    (void)ws;
-    (void)ws_bytes;
+    const size_t need = prism_workspace_size(PRISM_OP_ATTN_FWD, N, heads, d, nb, cap);
+    if (!ws || ws_bytes < need)
+        return fail(PRISM_E_WORKSPACE, "forward needs %zu workspace bytes, got %zu", need, ws ? ws_bytes : 0);
     if (use_simt_attention(dt))
         return hip_status(prism::launch_attn_fwd_simt(q, k, v, o, lse, dt == PRISM_BF16, N, heads, d, ld, hs,
                                                       block_offsets, nb, sel_offsets, sel_idx, cap, scale, stream),
                           "attention forward launch");
     if (static_cast<int64_t>(N / 64) * heads > 0x7FFFFFFF)
         return fail(PRISM_E_UNSUPPORTED, "too many query tiles for one launch");
+    Carver c(ws);
+    OrderWs w = carve_order(c, N, heads, nb);
+    st = hip_status(prism::launch_tile_order(sel_offsets, sel_idx, cap, block_offsets, nb, heads, N / 64, w.bucket,
+                                             w.start, w.order, stream),
+                    "tile order launch");
+    if (st != PRISM_OK) return st;
     return hip_status(prism::launch_attn_fwd_mfma(q, k, v, o, lse, N, heads, d, ld, hs, block_offsets, nb, sel_offsets,
-                                                  sel_idx, cap, scale, stream),
+                                                  sel_idx, cap, w.order, scale, stream),
                       "attention forward launch");
 }
 
@@ -356,9 +385,14 @@ prism_status prism_sparse_attn_bwd(const void* q, const void* k, const void* v, 
                           "attention backward launch");
     if (static_cast<int64_t>(N / 64) * heads > 0x7FFFFFFF)
         return fail(PRISM_E_UNSUPPORTED, "too many tiles for one launch");
+    // the order kernels count into tcount, which the transposed CSR no longer needs
+    st = hip_status(prism::launch_tile_order(sel_offsets, sel_idx, cap, block_offsets, nb, heads, N / 64, w.tcount,
+                                             w.ostart, w.qorder, stream),
+                    "tile order launch");
+    if (st != PRISM_OK) return st;
     return hip_status(prism::launch_attn_bwd_mfma(q, k, v, dout, lse, w.Dq, dq, dk, dv, N, heads, d, ld, hs,
                                                   block_offsets, nb, sel_offsets, sel_idx, w.tr_offsets, w.tr_idx, cap,
-                                                  scale, stream),
+                                                  w.qorder, scale, stream),
                       "attention backward launch");
 }
 

@@ -37,7 +37,7 @@ hipError_t launch_attn_fwd_simt(const void* q, const void* k, const void* v, voi
 
 hipError_t launch_attn_fwd_mfma(const void* q, const void* k, const void* v, void* o, float* lse, int64_t N, int heads,
                                 int d, int64_t ld, int64_t hs, const int32_t* offs, int nb, const int32_t* so,
-                                const int32_t* si, int64_t cap, float scale, hipStream_t s);
+                                const int32_t* si, int64_t cap, const int32_t* order, float scale, hipStream_t s);
 
 hipError_t launch_bwd_dot(const void* o, const void* dout, bool bf16, int64_t N, int heads, int d, int64_t ld,
                           int64_t hs, float* Dq, hipStream_t s);
@@ -45,7 +45,8 @@ hipError_t launch_bwd_dot(const void* o, const void* dout, bool bf16, int64_t N,
 hipError_t launch_attn_bwd_mfma(const void* q, const void* k, const void* v, const void* dout, const float* lse,
                                 const float* Dq, void* dq, void* dk, void* dv, int64_t N, int heads, int d, int64_t ld,
                                 int64_t hs, const int32_t* offs, int nb, const int32_t* so, const int32_t* si,
-                                const int32_t* to, const int32_t* ti, int64_t cap, float scale, hipStream_t s);
+                                const int32_t* to, const int32_t* ti, int64_t cap, const int32_t* qorder,
+                                float scale, hipStream_t s);
 
 hipError_t launch_attn_bwd_simt(const void* q, const void* k, const void* v, const void* dout, const float* lse,
                                 const float* Dq, void* dq, void* dk, void* dv, bool bf16, int64_t N, int heads, int d,
@@ -53,4 +54,8 @@ hipError_t launch_attn_bwd_simt(const void* q, const void* k, const void* v, con
                                 const int32_t* si, const int32_t* to, const int32_t* ti, int64_t cap, float scale,
                                 hipStream_t s);
 
+// visiting order of the query tiles (per head: tile ids grouped by first selected block)
+hipError_t launch_tile_order(const int32_t* sel_offsets, const int32_t* sel_idx, int64_t cap, const int32_t* offs,
+                             int nb, int heads, int64_t ntiles, int32_t* bucket, int32_t* start, int32_t* order,
+                             hipStream_t s);
 }  // namespace prism

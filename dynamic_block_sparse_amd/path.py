@@ -109,9 +109,11 @@ class PrismPath:
             op = self.block_major_like(qp)
         if lse is None:
             lse = torch.empty((hc, self.N), dtype=torch.float32, device=self.device)
+        ws = torch.empty(P.prism_workspace_size(P.OP_ATTN_FWD, self.N, hc, self.d, self.nb, sel.cap),
+                         dtype=torch.uint8, device=self.device)
         q, k, v, o = (x[:, h0:h0 + hc] for x in (qp, kp, vp, op))
         P.prism_sparse_attn_fwd(q, k, v, o, lse, self.N, hc, self.d, q.stride(0), q.stride(1), self.block_offsets,
-                                self.nb, sel.offsets, sel.idx, sel.cap, self.scale)
+                                self.nb, sel.offsets, sel.idx, sel.cap, self.scale, ws=ws)
         return op, lse
 
     def backward(self, qp, kp, vp, op, dop, lse, sel, grads=None, h0=0):

@@ -207,8 +207,12 @@ prism_status prism_select(const void* q, const void* k, prism_dtype dt,
  *   scale          softmax scale, finite and > 0 (1/sqrt(d)); PRISM_E_ARG otherwise
  *   block_offsets  must be the offsets written by prism_zone_shapes for the same
  *                  grid (every block a whole number of 64-token tiles)
+ *   ws, ws_bytes   prism_workspace_size(PRISM_OP_ATTN_FWD, ...) bytes: the order in
+ *                  which the query tiles are visited (grouped by first selected
+ *                  block, which shares key tiles in L2); PRISM_E_WORKSPACE if short
  * bf16 runs on bf16 MFMA with fp32 accumulation and an fp32 online softmax;
- * f32 runs on fp32 vector arithmetic.
+ * f32 runs on fp32 vector arithmetic.  The outputs do not depend on the
+ * visiting order: each row is accumulated over its blocks in ascending order.
  */
 prism_status prism_sparse_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                                    prism_dtype dt, int64_t N, int32_t heads, int32_t d,
@@ -227,6 +231,8 @@ prism_status prism_sparse_attn_fwd(const void* q, const void* k, const void* v, 
  *   o, dout        forward output and upstream gradient (block-major)
  *   lse            forward log-sum-exp
  *   dq, dk, dv     out block-major, same dtype/strides (fully overwritten)
+ *   ws, ws_bytes   prism_workspace_size(PRISM_OP_ATTN_BWD, ...) bytes: row sums,
+ *                  the transposed selection and the dQ tile visiting order
  * Deterministic: every output element is accumulated in a fixed order.
  */
 prism_status prism_sparse_attn_bwd(const void* q, const void* k, const void* v, const void* o,

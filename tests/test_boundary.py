@@ -163,12 +163,16 @@ def test_attention_rejects():
     lib, P = _lib()
     N, heads, d, nb = 2048, 2, 128, 24
     cap = nb * nb
-    fwd = lambda q=A, dt=1, d=d, o=Cc: lib.prism_sparse_attn_fwd(q, B, Cc, o, A, dt, N, heads, d, 256, 128, B, nb, Cc,
-                                                                 A, cap, 0.088, None, 0, None)
+    fneed = P.prism_workspace_size(P.OP_ATTN_FWD, N, heads, d, nb, cap)
+    assert fneed >= 4 * heads * (N // 64)          # at least the tile order
+    fwd = lambda q=A, dt=1, d=d, o=Cc, ws=B, wsb=fneed: lib.prism_sparse_attn_fwd(
+        q, B, Cc, o, A, dt, N, heads, d, 256, 128, B, nb, Cc, A, cap, 0.088, ws, wsb, None)
     assert fwd(dt=2) == 3
     assert fwd(d=32) == 4
     assert fwd(q=None) == 1
     assert fwd(o=Cc + 8) == 4                      # misaligned
+    assert fwd(ws=None) == 5
+    assert fwd(wsb=fneed - 16) == 5
     need = P.prism_workspace_size(P.OP_ATTN_BWD, N, heads, d, nb, cap)
     assert need > 0
     bwd = lambda ws=A, wsb=need, dq=A: lib.prism_sparse_attn_bwd(A, B, Cc, A, B, Cc, dq, B, Cc, 1, N, heads, d, 256,
@@ -184,5 +188,6 @@ def test_workspace_sizes_grow_with_the_problem():
     b = P.prism_workspace_size(P.OP_SELECT, 4096, 2, 64, 16, 256)
     c = P.prism_workspace_size(P.OP_SELECT, 4096, 1, 64, 32, 1024)
     assert 0 < a < b and a < c
-    assert P.prism_workspace_size(P.OP_ATTN_FWD, 4096, 1, 64, 16, 256) == 0
+    f1 = P.prism_workspace_size(P.OP_ATTN_FWD, 4096, 1, 64, 16, 256)
+    assert 0 < f1 < P.prism_workspace_size(P.OP_ATTN_FWD, 4096, 2, 64, 16, 256)
     assert P.prism_workspace_size(P.OP_ZONE_SHAPES, 512, 1, 3072, 0, 0) >= 16 * 8

@@ -313,8 +313,9 @@ def test_full_size_sampled(name):
     np.testing.assert_array_equal(_np(qp[torch.from_numpy(rows).cuda()]), _np(xs["q"][torch.from_numpy(pi[rows]).cuda()]))
     sc = float(np.float32(1.0 / math.sqrt(cfg.d)))
     check_heads = list(range(nh)) if heads else sorted(rng.choice(cfg.heads, size=2, replace=False).tolist())
-    op = path.block_major_like(qp)
-    grads = tuple(path.block_major_like(qp) for _ in range(3)) if cfg.backward else None
+    # NaN-filled outputs: every tile must be written, whatever order the tiles are visited in
+    op = path.block_major_like(qp).fill_(float("nan"))
+    grads = tuple(path.block_major_like(qp).fill_(float("nan")) for _ in range(3)) if cfg.backward else None
     sels, lses = {}, {}
     for h0 in range(0, nh, path.hc):
         sel = path.select(qp, kp, h0, want_logits=True)
@@ -326,6 +327,8 @@ def test_full_size_sampled(name):
             lses[h0 + hh] = lse[hh]
     torch.cuda.synchronize()
     print(f"case {name}: GPU path done", flush=True)
+    for t in (op,) + (grads or ()):
+        assert bool(torch.isfinite(t[:, :nh]).all())
     for h in check_heads:
         sel, hh = sels[h]
         Qp, Kp, Vp = (orc.to_block_major(_np(t[:, h:h + 1, :]), pi) for t in (xs["q"], xs["k"], v_att))
