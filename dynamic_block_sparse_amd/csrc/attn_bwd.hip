@@ -1,8 +1,6 @@
 // attn_bwd.hip - gradient of the block-sparse flash attention on gfx950 bf16 MFMA.
 //
-// Built with the default accumulator-register form of MFMA (see build.py):
-// the dK/dV kernel needs more than 256 registers, and the VGPR form measured
-// 9% slower here.
+// Built with the default accumulator-register form of MFMA (see build.py).
 #include "attn_common.hpp"
 
 namespace prism {
@@ -13,9 +11,9 @@ namespace prism {
 // 32*w .. +31 and streams every selected 64-key tile:
 //   S^T = K Q^T, P^T = exp2(S^T - lse), dP^T = V dO^T, dS^T = P^T (dP^T - D),
 //   dQ^T += K^T dS^T
-// dK/dV kernel (key-major): 2 waves per 64-key tile, wave w owns keys
-// 32*w .. +31 and streams the 64-row tiles of every query block that selected
-// the tile's block (transposed CSR, ascending):
+// dK/dV kernel (key-major): 4 waves per 64-key tile (two roles per 32-key
+// half, below) stream the 64-row tiles of every query block that selected the
+// tile's block (transposed CSR, ascending):
 //   S = Q K^T, P = exp2(S - lse), dP = dO V^T, dS = P (dP - D),
 //   dV^T += dO^T P, dK^T += Q^T dS
 // Each output element is accumulated by one lane in a fixed order: the
@@ -25,8 +23,8 @@ namespace prism {
 // share each SIMD (measured at 2K: 82 ms against 100 ms double-buffered at one
 // wave per SIMD).  Its loads are split by phase: dP^T, which needs only V,
 // runs first while K is still landing; V(t+1) is loaded once every wave has
-// finished dP^T, K(t+1) once every wave has finished dQ^T.  dK/dV needs 384
-// registers, one wave per SIMD, and double-buffers its Q and dO tiles instead.
+// finished dP^T, K(t+1) once every wave has finished dQ^T.  dK/dV
+// double-buffers its Q and dO tiles.
 //
 // dQ takes its query tiles in the visiting order built by launch_tile_order
 // (grouped by first selected key block).  dK/dV keeps raster order: grouping
@@ -147,8 +145,28 @@ attn_dq_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
         }
 }
 
+// dK/dV: 4 waves per 64-key tile, in two roles per 32-key half.  Role 0 holds
+// the half's K fragments and computes S = Q K^T, P and dV^T += dO^T P; role 1
+// holds its V fragments and computes dP = dO V^T, dS = P (dP - D) and
+// dK^T += Q^T dS, taking P from role 0 through LDS.  A wave then keeps one
+// accumulator (dV^T or dK^T of 32 keys) instead of two, two waves fit per SIMD,
+// and the MFMA work is the same 16 d-step products per row half as with one
+// wave doing both.  The query tile is processed in two 32-row halves so that
+// the P exchange needs 4 KB per key half:
+//   A  role 0: S(0), P(0), P(0) -> LDS         role 1: dP(0)
+//   -- barrier
+//   B  role 0: S(1), P(1), dV += P(0)          role 1: dP(1), dS(0), dK += dS(0)
+//   -- barrier (role 1 has read P(0))
+//      role 0: P(1) -> LDS
+//   -- barrier
+//   C  role 0: dV += P(1)                      role 1: dS(1), dK += dS(1)
+// P and dS are computed exactly as with a single wave, and every accumulator
+// takes its 16-row k-steps in ascending order, so results do not depend on the
+// split.  (Measured at 2K: 103.5 ms against 107.3 ms for 2 waves that each
+// computed all four products for 32 keys in 381 registers, one wave per SIMD.)
+
 template <int D>
-__global__ void __launch_bounds__(128)
+__global__ void __launch_bounds__(256, 2)
 attn_dkdv_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
                       const uint16_t* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ Dq,
                       uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, int64_t N, int64_t ld, int64_t hs,
@@ -157,12 +175,15 @@ attn_dkdv_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
     // Q and dO tiles, lse (natural log) and D = rowsum(dO * O) of their rows
     __shared__ uint16_t qbuf[2][64 * D], obuf[2][64 * D];
     __shared__ float lbuf[2][64], dbuf[2][64];
+    // P of one 32-row half per key half: [key half][register group][lane][4]
+    __shared__ float pbuf[2][4][64][4];
     const int ntiles = static_cast<int>(N / 64);
     const int wg = xcd_remap(blockIdx.x);
     const int h = wg / ntiles;
     const int64_t k0 = static_cast<int64_t>(wg % ntiles) * 64;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int role = wave & 1, kh = wave >> 1;
     const int hl = lane >> 5, col = lane & 31;
     const int j = find_block(offs, nb, k0);
     const int32_t* __restrict__ to = tr_off + static_cast<int64_t>(h) * (nb + 1);
@@ -170,103 +191,113 @@ attn_dkdv_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
     const int e0 = to[j];
     const int e1 = static_cast<int>(min(static_cast<int64_t>(to[j + 1]), cap));
     constexpr int KS = D / 16, DM = D / 32;
-    const int64_t key = k0 + 32 * wave + col;
-    u32x4_t kb[KS], vb[KS];
+    const int64_t key = k0 + 32 * kh + col;
+    // K fragments (role 0) or V fragments (role 1) of this wave's 32 keys
+    u32x4_t kv[KS];
     {
-        const uint16_t* kp = k + key * ld + h * hs;
-        const uint16_t* vp = v + key * ld + h * hs;
+        const uint16_t* src = (role ? v : k) + key * ld + h * hs;
 #pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            kb[s] = *reinterpret_cast<const u32x4_t*>(kp + 16 * s + 8 * hl);
-            vb[s] = *reinterpret_cast<const u32x4_t*>(vp + 16 * s + 8 * hl);
-        }
+        for (int s = 0; s < KS; ++s) kv[s] = *reinterpret_cast<const u32x4_t*>(src + 16 * s + 8 * hl);
 #pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            settle(kb[s]);
-            settle(vb[s]);
-        }
+        for (int s = 0; s < KS; ++s) settle(kv[s]);
     }
-    f32x16_t ak[DM], av[DM];
+    f32x16_t acc[DM];   // dV^T (role 0) or dK^T (role 1)
 #pragma unroll
     for (int m = 0; m < DM; ++m)
 #pragma unroll
-        for (int x = 0; x < 16; ++x) ak[m][x] = av[m][x] = 0.0f;
+        for (int x = 0; x < 16; ++x) acc[m][x] = 0.0f;
     const uint16_t* __restrict__ qh_ = q + h * hs;
     const uint16_t* __restrict__ oh_ = dout + h * hs;
     const float* __restrict__ lh = lse + static_cast<int64_t>(h) * N;
     const float* __restrict__ dh = Dq + static_cast<int64_t>(h) * N;
+    float4* __restrict__ pex = reinterpret_cast<float4*>(&pbuf[kh][0][0][0]) + lane;
 
-    TileDma<D, 2> dma;
+    TileDma<D, 4> dma;
     dma.init(ld, wave, lane);
     const uint32_t loff = 4 * lane;
     auto issue = [&](int t, int b) {
         dma.load(qbuf[b], qh_ + static_cast<int64_t>(t) * ld, wave);
         dma.load(obuf[b], oh_ + static_cast<int64_t>(t) * ld, wave);
         if (wave == 0) dma4(lh + t, loff, lds_addr(lbuf[b]));
-        else dma4(dh + t, loff, lds_addr(dbuf[b]));
+        else if (wave == 1) dma4(dh + t, loff, lds_addr(dbuf[b]));
     };
     auto compute = [&](int b) {
-        const uint16_t* qt = qbuf[b];
-        const uint16_t* ot = obuf[b];
+        const uint16_t* rb = role ? obuf[b] : qbuf[b];   // row operand: Q for S, dO for dP
+        const uint16_t* tb = role ? qbuf[b] : obuf[b];   // transposed operand: dO^T for dV, Q^T for dK
         const float* lt = lbuf[b];
         const float* dt = dbuf[b];
-        f32x16_t sa[2], pa[2];
+        // S (role 0) or dP (role 1) of row half mr: register x holds query row
+        // 32*mr + 8*(x/4) + 4*hl + x%4 against key col of the wave's half
+        auto rows = [&](int mr) {
+            f32x16_t x;
 #pragma unroll
-        for (int mr = 0; mr < 2; ++mr)
+            for (int i = 0; i < 16; ++i) x[i] = 0.0f;
 #pragma unroll
-            for (int x = 0; x < 16; ++x) sa[mr][x] = pa[mr][x] = 0.0f;
-#pragma unroll
-        for (int s = 0; s < KS; ++s)
-#pragma unroll
-            for (int mr = 0; mr < 2; ++mr) {
-                sa[mr] = mfma32(sw_read16<D>(qt, 32 * mr + col, 16 * s + 8 * hl), kb[s], sa[mr]);
-                pa[mr] = mfma32(sw_read16<D>(ot, 32 * mr + col, 16 * s + 8 * hl), vb[s], pa[mr]);
-            }
-        sched_reads_ahead<4, 4, KS, 2>();
-        // register x of row tile mr holds query row 32*mr + 8*(x/4) + 4*hl + x%4
-#pragma unroll
-        for (int mr = 0; mr < 2; ++mr)
+            for (int s = 0; s < KS; ++s) x = mfma32(sw_read16<D>(rb, 32 * mr + col, 16 * s + 8 * hl), kv[s], x);
+            return x;
+        };
+        auto softmax = [&](f32x16_t& x, int mr) {   // S -> P (role 0)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const float4 l4 = *reinterpret_cast<const float4*>(&lt[32 * mr + 8 * g + 4 * hl]);
-                const float4 d4 = *reinterpret_cast<const float4*>(&dt[32 * mr + 8 * g + 4 * hl]);
                 const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-                const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float p = fast_exp2(fmaf(sa[mr][4 * g + r], scale_log2, -lv[r] * kLog2e));
-                    sa[mr][4 * g + r] = p;
-                    pa[mr][4 * g + r] = p * (pa[mr][4 * g + r] - dv4[r]);   // dS
-                }
+                for (int r = 0; r < 4; ++r) x[4 * g + r] = fast_exp2(fmaf(x[4 * g + r], scale_log2, -lv[r] * kLog2e));
             }
+        };
+        auto dsoft = [&](f32x16_t& x, int mr) {     // dP -> dS = P (dP - D) (role 1)
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            const u32x4_t bp = pack_kstep(sa[ks >> 1], ks & 1);
-            const u32x4_t bs = pack_kstep(pa[ks >> 1], ks & 1);
-#pragma unroll
-            for (int m = 0; m < DM; ++m) {
-                av[m] = mfma32(tr_operand<D>(ot, 16 * ks, 32 * m, lane), bp, av[m]);
-                ak[m] = mfma32(tr_operand<D>(qt, 16 * ks, 32 * m, lane), bs, ak[m]);
+            for (int g = 0; g < 4; ++g) {
+                const float4 p4 = pex[64 * g];
+                const float4 d4 = *reinterpret_cast<const float4*>(&dt[32 * mr + 8 * g + 4 * hl]);
+                x[4 * g + 0] = p4.x * (x[4 * g + 0] - d4.x);
+                x[4 * g + 1] = p4.y * (x[4 * g + 1] - d4.y);
+                x[4 * g + 2] = p4.z * (x[4 * g + 2] - d4.z);
+                x[4 * g + 3] = p4.w * (x[4 * g + 3] - d4.w);
             }
+        };
+        auto publish = [&](const f32x16_t& x) {     // P -> LDS (role 0)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) pex[64 * g] = float4{x[4 * g], x[4 * g + 1], x[4 * g + 2], x[4 * g + 3]};
+        };
+        auto accumulate = [&](const f32x16_t& x, int mr) {   // acc += tb^T x over the half's 32 rows
+#pragma unroll
+            for (int k2 = 0; k2 < 2; ++k2) {
+                const u32x4_t bx = pack_kstep(x, k2);
+#pragma unroll
+                for (int m = 0; m < DM; ++m)
+                    acc[m] = mfma32(tr_operand<D>(tb, 32 * mr + 16 * k2, 32 * m, lane), bx, acc[m]);
+            }
+        };
+        f32x16_t x0 = rows(0);
+        if (role == 0) {
+            softmax(x0, 0);
+            publish(x0);
         }
+        __syncthreads();
+        f32x16_t x1 = rows(1);
+        if (role == 0) softmax(x1, 1);
+        else dsoft(x0, 0);
+        accumulate(x0, 0);
+        __syncthreads();   // role 1 has read P of half 0
+        if (role == 0) publish(x1);
+        __syncthreads();
+        if (role) dsoft(x1, 1);
+        accumulate(x1, 1);
     };
 
     TileCursor cur;
     cur.init(ti, offs, e0, e1);
     tile_pipeline(cur, issue, compute);
-    uint16_t* ko = dk + key * ld + h * hs;
-    uint16_t* vo = dv + key * ld + h * hs;
+    uint16_t* out = (role ? dk : dv) + key * ld + h * hs;
+    const float f = role ? scale : 1.0f;
 #pragma unroll
     for (int m = 0; m < DM; ++m)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-            const f32x16_t& a = ak[m];
-            const f32x16_t& c = av[m];
-            const int dcol = 32 * m + 8 * g + 4 * hl;
-            *reinterpret_cast<u32x2_t*>(ko + dcol) =
-                u32x2_t{pack2(a[4 * g] * scale, a[4 * g + 1] * scale), pack2(a[4 * g + 2] * scale, a[4 * g + 3] * scale)};
-            *reinterpret_cast<u32x2_t*>(vo + dcol) =
-                u32x2_t{pack2(c[4 * g], c[4 * g + 1]), pack2(c[4 * g + 2], c[4 * g + 3])};
+            const f32x16_t& a = acc[m];
+            *reinterpret_cast<u32x2_t*>(out + 32 * m + 8 * g + 4 * hl) =
+                u32x2_t{pack2(a[4 * g] * f, a[4 * g + 1] * f), pack2(a[4 * g + 2] * f, a[4 * g + 3] * f)};
         }
 }
 
@@ -291,14 +322,14 @@ hipError_t launch_attn_bwd_mfma(const void* q, const void* k, const void* v, con
                            nb, so, si, cap, qorder, sl2, scale);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(attn_dkdv_mfma_kernel<128>, grid, dim3(128), 0, s, Q, K, V, O, lse, Dq, dK, dV, N, ld, hs,
+        hipLaunchKernelGGL(attn_dkdv_mfma_kernel<128>, grid, dim3(256), 0, s, Q, K, V, O, lse, Dq, dK, dV, N, ld, hs,
                            offs, nb, to, ti, cap, sl2, scale);
     } else {
         hipLaunchKernelGGL(attn_dq_mfma_kernel<64>, grid, dim3(128), 0, s, Q, K, V, O, lse, Dq, dQ, N, ld, hs, offs,
                            nb, so, si, cap, qorder, sl2, scale);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(attn_dkdv_mfma_kernel<64>, grid, dim3(128), 0, s, Q, K, V, O, lse, Dq, dK, dV, N, ld, hs,
+        hipLaunchKernelGGL(attn_dkdv_mfma_kernel<64>, grid, dim3(256), 0, s, Q, K, V, O, lse, Dq, dK, dV, N, ld, hs,
                            offs, nb, to, ti, cap, sl2, scale);
     }
     return hipGetLastError();
