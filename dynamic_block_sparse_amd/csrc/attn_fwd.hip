@@ -115,11 +115,21 @@ attn_fwd_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
                 ls += s0[x] + s1[x];
             }
             lrow += ls;
+            // P = P_hi + P_lo in two bf16 parts, so that O carries P to about 16
+            // bits instead of bf16's 8 (the output's own bf16 rounding is then
+            // the only error of that size)
             const u32x4_t pb[4] = {pack_kstep(s0, 0), pack_kstep(s0, 1), pack_kstep(s1, 0), pack_kstep(s1, 1)};
+            u32x4_t pl[4];
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) pl[ks] = pack_residual(ks < 2 ? s0 : s1, ks & 1, pb[ks]);
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-                for (int m = 0; m < DM; ++m) oacc[m] = mfma32(tr_operand<D>(vt, 16 * ks, 32 * m, lane), pb[ks], oacc[m]);
+                for (int m = 0; m < DM; ++m) {
+                    const u32x4_t vtr = tr_operand<D>(vt, 16 * ks, 32 * m, lane);
+                    oacc[m] = mfma32(vtr, pb[ks], oacc[m]);
+                    oacc[m] = mfma32(vtr, pl[ks], oacc[m]);
+                }
             dma_join();                    // K(tn) landed; every wave is done with V(t)
             if (tn < 0) break;
             dma.load(vbuf, vh_ + static_cast<int64_t>(tn) * ld, wave);

@@ -26,3 +26,18 @@ def pytest_collection_modifyitems(config, items):
     for it in items:
         if "gpu" in it.keywords:
             it.add_marker(skip)
+
+
+@pytest.fixture
+def progress(request):
+    """Print a progress line at once, past pytest's output capture: full-size
+    cases run for minutes, and their steps should be visible while they do."""
+    capman = request.config.pluginmanager.getplugin("capturemanager")
+
+    def emit(msg):
+        if capman is None:
+            print(msg, flush=True)
+            return
+        with capman.global_and_fixture_disabled():
+            print(msg, flush=True)
+    return emit

@@ -276,9 +276,9 @@ FULL = ["720p", "1080p", "2k", "long"]
 
 
 @pytest.mark.parametrize("name", FULL)
-def test_full_size_sampled(name):
+def test_full_size_sampled(name, progress):
     cfg = CONFIGS[name]
-    print(f"case {name}: generating", flush=True)
+    progress(f"case {name}: generating")
     rng = np.random.default_rng(1234)
     if cfg.heads_sequential:
         heads = sorted(rng.choice(cfg.heads, size=2, replace=False).tolist())
@@ -294,11 +294,12 @@ def test_full_size_sampled(name):
     path = _path(cfg, heads=nh, hc=hc)
     path.shapes(x["v"], x["a"])
     torch.cuda.synchronize()
-    print(f"case {name}: NB {path.nb}", flush=True)
+    progress(f"case {name}: NB {path.nb}")
     # zone decisions against the oracle on all zones
+    progress(f"case {name}: oracle zone statistics")
     zs = orc.zone_shapes(_np(x["v"]).reshape(cfg.N, -1), _np(x["a"]), cfg.T, cfg.H, cfg.W)
     ok = ~zs["near_tie"]
-    print(f"case {name}: near-tie zones {int((~ok).sum())}", flush=True)
+    progress(f"case {name}: near-tie zones {int((~ok).sum())}")
     assert path.nb == zs["NB"] or (~ok).any()
     np.testing.assert_array_equal(path.zone_shape.cpu().numpy()[ok], zs["shape"][ok])
     if ok.all():
@@ -326,7 +327,7 @@ def test_full_size_sampled(name):
             sels[h0 + hh] = (sel, hh)
             lses[h0 + hh] = lse[hh]
     torch.cuda.synchronize()
-    print(f"case {name}: GPU path done", flush=True)
+    progress(f"case {name}: GPU path done")
     for t in (op,) + (grads or ()):
         assert bool(torch.isfinite(t[:, :nh]).all())
     for h in check_heads:
@@ -335,15 +336,16 @@ def test_full_size_sampled(name):
         L = orc.block_logits(orc.pool_blocks(Qp, offs, 0), orc.pool_blocks(Kp, offs, 0), sc)
         Lg = sel.logits[hh].cpu().numpy()
         mism = Lg != L
-        print(f"case {name} head {h}: logit mismatches {int(mism.sum())} of {L.size}", flush=True)
+        progress(f"case {name} head {h}: logit mismatches {int(mism.sum())} of {L.size}")
         assert mism.mean() < 1e-6
+        progress(f"case {name} head {h}: oracle selection")
         co, ci, flags = orc.select(L, cfg.top_k, cfg.top_p)
         bad_rows = set(np.nonzero(mism.any(axis=1))[0].tolist()) | set(np.nonzero(flags)[0].tolist())
         og = sel.offsets[hh].cpu().numpy()
         ig = sel.idx[hh, :og[-1]].cpu().numpy()
         sizes = np.diff(co)
-        print(f"case {name} head {h}: mean |S_i| {sizes.mean():.1f} blocks ({sizes.mean() / nb:.4f} of NB), "
-              f"flagged rows {int(flags.sum())}", flush=True)
+        progress(f"case {name} head {h}: mean |S_i| {sizes.mean():.1f} blocks ({sizes.mean() / nb:.4f} of NB), "
+              f"flagged rows {int(flags.sum())}")
         for i in range(nb):
             if i in bad_rows:
                 continue
@@ -366,7 +368,7 @@ def test_full_size_sampled(name):
             spent += c
             if len(qb) >= 64:
                 break
-        print(f"case {name} head {h}: checking {len(qb)} query blocks", flush=True)
+        progress(f"case {name} head {h}: checking {len(qb)} query blocks")
         for n_done, i in enumerate(qb):
             s = ci[co[i]:co[i + 1]]
             o_ref, lse_ref = orc.attn_fwd_block(Qp, Kp, Vp, offs, s, i, 0, sc)
@@ -376,7 +378,7 @@ def test_full_size_sampled(name):
                 dq_ref = orc.attn_bwd_block(Qp, Kp, Vp, dOp, offs, s, i, 0, sc)[0]
                 errs["dQ"].append((_np(grads[0][offs[i]:offs[i + 1], h, :]), dq_ref))
             if n_done % 8 == 7:
-                print(f"case {name} head {h}: {n_done + 1} query blocks checked", flush=True)
+                progress(f"case {name} head {h}: {n_done + 1} query blocks checked")
         if cfg.backward:
             # key blocks in seeded random order, up to 32 of them, while the
             # oracle's cost (query rows x selected keys of every user row) stays
@@ -398,10 +400,10 @@ def test_full_size_sampled(name):
                 errs["dV"].append((_np(grads[2][offs[j]:offs[j + 1], h, :]), dv_ref))
                 spent += c
                 taken += 1
-                print(f"case {name} head {h}: key block {j} ({len(users)} query blocks) checked", flush=True)
+                progress(f"case {name} head {h}: key block {j} ({len(users)} query blocks) checked")
                 if taken >= 32:
                     break
-            print(f"case {name} head {h}: {taken} key blocks checked for dK/dV", flush=True)
+            progress(f"case {name} head {h}: {taken} key blocks checked for dK/dV")
         for k, pairs in errs.items():
             if pairs:
                 got = np.concatenate([p[0] for p in pairs])
