@@ -23,7 +23,7 @@ Where the pages leave a step open, the reading taken is stated at the function.
 
 Parity status per function:
   pinned by closed forms, brute force or library routines in the CPU tests:
-    candidate_shapes, axis_profiles, video_variance, audio_terms (as read),
+    audio_norm_map (the norm; its normalisation is a reading), candidate_shapes, axis_profiles, video_variance, audio_terms (as read),
     indicator, volume, optimum_log2, nearest_shape, block layout, permutation,
     pool_blocks, block_logits, select_row, attention forward and backward.
   parity unpinned (readings with no number on the pages to check against):
@@ -50,6 +50,33 @@ NEAR = 1e-12             # width of the "near a decision boundary" flags (zones)
 # path sums masses as 2^-48 fixed-point integers, which moves a cumulative
 # mass by at most NB * 2^-49 < 6e-11 of Z for NB <= 32768.
 CDF_NEAR = 1e-10
+
+
+# ----------------------------------------------------------------------------
+# step 0: the audio-to-video norm map ([P3] method §1: a at each token is the
+# 2-norm of the audio-to-video cross-attention output cached from the layer
+# before)
+
+def audio_norm_map(Hhat, chunk=None):
+    """a_n = ||h_n||_2 over the channels of token n's cross-attention output
+    Hhat [N, C], divided by its largest value over the clip.
+
+    Reading: the pages define the norm and state a_bar in [0, 1] but give no
+    normalisation; division by the clip-wide maximum is the plainest one that
+    lands in [0, 1] (a clip whose outputs are all zero maps to zeros).
+    float64 throughout, rounded once to float32 (the map's type).  `chunk`
+    processes that many rows at a time (same arithmetic, less memory).
+    Returns (norms float64 [N], a float32 [N])."""
+    X = np.asarray(Hhat)
+    n = X.shape[0]
+    step = n if not chunk else int(chunk)
+    norms = np.empty(n, dtype=np.float64)
+    for r0 in range(0, n, max(step, 1)):
+        Y = np.asarray(X[r0:r0 + step], dtype=np.float64)
+        norms[r0:r0 + step] = np.sqrt((Y * Y).sum(axis=1))
+    top = norms.max() if n else 0.0
+    a = norms / top if top > 0 else np.zeros(n, dtype=np.float64)
+    return norms, a.astype(np.float32)
 
 
 # ----------------------------------------------------------------------------

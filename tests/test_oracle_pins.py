@@ -29,6 +29,53 @@ def _read_rows(name):
     return rows
 
 
+# ---------------------------------------------------------------- audio norm map
+
+def test_norm_map_pythagorean_rows():
+    # integer rows with integer norms: (3,4)->5, (5,12)->13, (8,15)->17, (1,2,2)->3
+    H = np.zeros((5, 6))
+    H[0, :2] = (3, 4)
+    H[1, 2:4] = (5, 12)
+    H[2, [0, 5]] = (8, -15)
+    H[3, 1:4] = (1, -2, 2)
+    norms, a = orc.audio_norm_map(H)
+    assert norms.tolist() == [5.0, 13.0, 17.0, 3.0, 0.0]
+    want = [float(np.float32(k / 17)) for k in (5, 13, 17, 3, 0)]      # closed forms k/17
+    assert a.dtype == np.float32 and a.tolist() == want
+    assert a[2] == 1.0                                  # the largest token maps to 1
+
+
+def test_norm_map_constant_and_one_hot_rows():
+    C = 64
+    H = np.zeros((3, C))
+    H[0] = 1.0                                          # sqrt(64) = 8
+    H[1, 17] = -2.5                                     # one-hot: |value|
+    H[2] = 0.5                                          # 0.5 sqrt(64) = 4
+    norms, a = orc.audio_norm_map(H)
+    assert norms.tolist() == [8.0, 2.5, 4.0]
+    assert a.tolist() == [1.0, 0.3125, 0.5]
+
+
+def test_norm_map_matches_hypot_and_is_sign_and_scale_invariant():
+    rng = np.random.default_rng(5)
+    H = rng.standard_normal((40, 24)) * rng.uniform(0.01, 3.0, size=(40, 1))
+    norms, a = orc.audio_norm_map(H)
+    ref = np.array([math.hypot(*row) for row in H])       # a different library routine
+    np.testing.assert_allclose(norms, ref, rtol=1e-14)
+    assert int(np.argmax(a)) == int(np.argmax(ref)) and a.max() == 1.0
+    assert (orc.audio_norm_map(-H)[1] == a).all()
+    assert (orc.audio_norm_map(H * 2.0 ** 7)[1] == a).all()   # powers of two scale exactly
+    _, a_chunked = orc.audio_norm_map(H, chunk=7)
+    assert (a_chunked == a).all()
+
+
+def test_norm_map_degenerate_inputs():
+    _, a = orc.audio_norm_map(np.zeros((10, 8)))
+    assert a.dtype == np.float32 and (a == 0).all()      # an all-zero clip stays zero
+    norms, a = orc.audio_norm_map(np.zeros((0, 8)))
+    assert norms.shape == (0,) and a.shape == (0,)
+
+
 # ---------------------------------------------------------------- candidates
 
 def test_candidate_set_matches_hand_typed_table():
