@@ -306,6 +306,36 @@ def profile(args):
     print(f"[profile] wrote summaries into {out}", file=sys.stderr, flush=True)
 
 
+def measure_norm_map(cfg, reps=10):
+    """prism_audio_norm_map on a synthetic cross-attention output of the
+    workload's shape (N tokens x heads*d channels, the workload's dtype), timed
+    with HIP events on the launch stream outside the step.  Algorithmic bytes:
+    the rows read once and the fp32 map written once."""
+    import workloads.synth as synth
+    from dynamic_block_sparse_amd import prism as P
+    print("[bench] audio norm map", file=sys.stderr, flush=True)
+    h = synth.cross_attn_output(cfg, device="cuda")
+    N, C = h.shape
+    a = torch.empty(N, dtype=torch.float32, device="cuda")
+    ws = torch.empty(P.prism_workspace_size(P.OP_NORM_MAP, N, 0, 0, 0, 0), dtype=torch.uint8, device="cuda")
+    for _ in range(3):
+        P.prism_audio_norm_map(h, N, C, C, a, ws)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        P.prism_audio_norm_map(h, N, C, C, a, ws)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    alg = N * C * h.element_size() + 4 * N
+    del h
+    gbs = alg / (ms * 1e-3) / 1e9
+    return {"input": f"{N} x {C} {cfg.dtype}", "ms": round(ms, 4), "algorithmic_bytes": alg,
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(gbs / PEAK_HBM_GBS, 4)}}
+
+
 def main():
     args = parse()
     if args.profile:
@@ -450,6 +480,7 @@ def main():
         "stage_gbs_algorithmic": stage_gbs,
         "roofline": roofline,
     }
+    result["next_rows"] = {"f1_audio_norm_map": measure_norm_map(cfg)}
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(cfg, x, path.zone_shape.cpu().numpy(), args.cpu_seconds)

@@ -4,6 +4,7 @@
 // thread-local message.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -201,6 +202,9 @@ size_t prism_workspace_size(int32_t op, int64_t N, int32_t heads, int32_t d, int
             carve_order(c, N, heads, nb);
             return c.off;
         }
+        case PRISM_OP_NORM_MAP:
+            return align_up(static_cast<size_t>(N) * sizeof(double)) +
+                   align_up(static_cast<size_t>(prism::kNormMapMaxBlocks) * sizeof(double));
         case PRISM_OP_ATTN_BWD: {
             Carver c(nullptr);
             carve_bwd(c, N, heads, nb, cap);
@@ -208,6 +212,23 @@ size_t prism_workspace_size(int32_t op, int64_t N, int32_t heads, int32_t d, int
         }
     }
     return 0;
+}
+
+prism_status prism_audio_norm_map(const void* h, prism_dtype dt, int64_t N, int64_t C, int64_t ld, float* a,
+                                  double* norms, void* ws, size_t ws_bytes, hipStream_t stream) {
+    if (dt != PRISM_F32 && dt != PRISM_BF16) return fail(PRISM_E_DTYPE, "unknown dtype %d", static_cast<int>(dt));
+    if (!h || !a) return fail(PRISM_E_ARG, "null pointer argument");
+    if (N <= 0 || C <= 0 || ld < C)
+        return fail(PRISM_E_ARG, "need N > 0, C > 0 and ld >= C (N = %lld, C = %lld, ld = %lld)",
+                    static_cast<long long>(N), static_cast<long long>(C), static_cast<long long>(ld));
+    const size_t need = prism_workspace_size(PRISM_OP_NORM_MAP, N, 0, 0, 0, 0);
+    if (!ws || ws_bytes < need)
+        return fail(PRISM_E_WORKSPACE, "norm map needs %zu workspace bytes, got %zu", need, ws ? ws_bytes : 0);
+    Carver c(ws);
+    double* own = c.take<double>(static_cast<size_t>(N));
+    double* bmax = c.take<double>(static_cast<size_t>(prism::kNormMapMaxBlocks));
+    return hip_status(prism::launch_norm_map(h, dt == PRISM_BF16, N, C, ld, a, norms ? norms : own, bmax, stream),
+                      "norm map launch");
 }
 
 prism_status prism_zone_shapes(int32_t T, int32_t H, int32_t W, const void* v, prism_dtype vdt, int64_t C,

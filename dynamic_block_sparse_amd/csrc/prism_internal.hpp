@@ -58,4 +58,11 @@ hipError_t launch_attn_bwd_simt(const void* q, const void* k, const void* v, con
 hipError_t launch_tile_order(const int32_t* sel_offsets, const int32_t* sel_idx, int64_t cap, const int32_t* offs,
                              int nb, int heads, int64_t ntiles, int32_t* bucket, int32_t* start, int32_t* order,
                              hipStream_t s);
+// audio-to-video norm map: per-token 2-norms (float64) and their clip-wide
+// normalisation; block_max holds norm_map_blocks(N) <= kNormMapMaxBlocks doubles
+constexpr int kNormMapMaxBlocks = 4096;
+int norm_map_blocks(int64_t N);
+hipError_t launch_norm_map(const void* h, bool bf16, int64_t N, int64_t C, int64_t ld, float* a, double* norms,
+                           double* block_max, hipStream_t s);
+
 }  // namespace prism

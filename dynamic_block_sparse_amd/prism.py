@@ -20,12 +20,12 @@ if not os.path.exists(_LIB_PATH):
 _lib = C.CDLL(_LIB_PATH)
 
 PRISM_F32, PRISM_BF16 = 0, 1
-OP_ZONE_SHAPES, OP_SELECT, OP_ATTN_FWD, OP_ATTN_BWD = 0, 1, 2, 3
+OP_ZONE_SHAPES, OP_SELECT, OP_ATTN_FWD, OP_ATTN_BWD, OP_NORM_MAP = 0, 1, 2, 3, 4
 ZS_STRIDE = 16
 STATUS = {0: "PRISM_OK", 1: "PRISM_E_ARG", 2: "PRISM_E_GRID", 3: "PRISM_E_DTYPE",
           4: "PRISM_E_UNSUPPORTED", 5: "PRISM_E_WORKSPACE", 6: "PRISM_E_HIP"}
 
-EXPORTS = ["prism_zone_shapes", "prism_block_permute", "prism_block_permute_heads", "prism_select",
+EXPORTS = ["prism_audio_norm_map", "prism_zone_shapes", "prism_block_permute", "prism_block_permute_heads", "prism_select",
            "prism_sparse_attn_fwd",
            "prism_sparse_attn_bwd", "prism_workspace_size", "prism_status_string", "prism_last_error",
            "prism_candidate_shapes"]
@@ -53,7 +53,8 @@ _lib.prism_sparse_attn_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _i64, _i32
                                        _vp, _i64, _f32, _vp, _sz, _vp]
 _lib.prism_sparse_attn_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i64,
                                        _i64, _vp, _i32, _vp, _vp, _i64, _f32, _vp, _sz, _vp]
-for _f in ("prism_zone_shapes", "prism_block_permute", "prism_block_permute_heads", "prism_select",
+_lib.prism_audio_norm_map.argtypes = [_vp, _i32, _i64, _i64, _i64, _vp, _vp, _vp, _sz, _vp]
+for _f in ("prism_audio_norm_map", "prism_zone_shapes", "prism_block_permute", "prism_block_permute_heads", "prism_select",
            "prism_sparse_attn_fwd", "prism_sparse_attn_bwd"):
     getattr(_lib, _f).restype = C.c_int
 _lib.prism_workspace_size.argtypes = [_i32, _i64, _i32, _i32, _i32, _i64]
@@ -140,6 +141,13 @@ def prism_block_permute_heads(T, H, W, zone_shape, x, y, heads, d, x_ld, x_hs, y
                               dtype=None):
     st = _lib.prism_block_permute_heads(T, H, W, _ptr(zone_shape), _ptr(x), _ptr(y), _dt(x) if dtype is None else dtype,
                                         heads, d, x_ld, x_hs, y_ld, y_hs, int(inverse), _stream(stream))
+    _check(st)
+
+
+def prism_audio_norm_map(h, N, C, ld, a, ws, norms=None, stream=None, dtype=None):
+    st = _lib.prism_audio_norm_map(_ptr(h), _dt(h) if dtype is None else dtype, N, C, ld, _ptr(a), _ptr(norms),
+                                   _ptr(ws), ws.numel() * ws.element_size() if ws is not None else 0,
+                                   _stream(stream))
     _check(st)
 
 

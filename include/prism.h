@@ -72,7 +72,8 @@ typedef enum { PRISM_F32 = 0, PRISM_BF16 = 1 } prism_dtype;
 typedef struct { double tau128, tau256, eps; } prism_shape_params;
 
 /* operation codes for prism_workspace_size */
-enum { PRISM_OP_ZONE_SHAPES = 0, PRISM_OP_SELECT = 1, PRISM_OP_ATTN_FWD = 2, PRISM_OP_ATTN_BWD = 3 };
+enum { PRISM_OP_ZONE_SHAPES = 0, PRISM_OP_SELECT = 1, PRISM_OP_ATTN_FWD = 2, PRISM_OP_ATTN_BWD = 3,
+       PRISM_OP_NORM_MAP = 4 };
 
 /* Per-zone record written by prism_zone_shapes when `zone_stats` is not NULL:
  * 16 doubles per zone. */
@@ -87,6 +88,29 @@ enum {
     PRISM_ZS_B = 15,          /* block volume 64, 128 or 256 */
     PRISM_ZS_STRIDE = 16
 };
+
+/*
+ * prism_audio_norm_map - the audio-to-video norm map that prism_zone_shapes
+ * takes as a_map: a at token n is the 2-norm of the audio-to-video
+ * cross-attention output cached from the layer before (reading guide,
+ * "Phương pháp" §1, definition of a), divided by its largest value over the
+ * clip so that it lies in [0, 1] (the pages state the range but give no
+ * normalisation; an all-zero clip maps to zeros).
+ *
+ *   h       device [N, C] rows of the cross-attention output in raster token
+ *           order, row stride ld >= C elements, bf16 or fp32
+ *   a       out device [N] fp32 map, values in [0, 1]
+ *   norms   optional out device [N] float64 raw norms (NULL: kept in ws)
+ *   ws, ws_bytes  prism_workspace_size(PRISM_OP_NORM_MAP, N, 0, 0, 0, 0) bytes (depends on N only)
+ *
+ * Squares are summed in float64 (exact for bf16 and fp32 values), the square
+ * root is float64, and a = float(norm / max) is rounded once.  Rows are read
+ * with 16-byte loads when h and the row stride are 16-byte aligned, 4- or
+ * 2-byte loads otherwise.  Errors: PRISM_E_ARG for a NULL pointer, N <= 0,
+ * C <= 0 or ld < C; PRISM_E_DTYPE; PRISM_E_WORKSPACE.
+ */
+prism_status prism_audio_norm_map(const void* h, prism_dtype dt, int64_t N, int64_t C, int64_t ld,
+                                  float* a, double* norms, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * prism_zone_shapes - macro-zones, variation indicator, block volume and shape,

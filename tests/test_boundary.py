@@ -24,7 +24,7 @@ def _declared():
 
 def test_every_declared_symbol_is_exported():
     names = _declared()
-    assert set(names) >= {"prism_zone_shapes", "prism_block_permute", "prism_select", "prism_sparse_attn_fwd",
+    assert set(names) >= {"prism_audio_norm_map", "prism_zone_shapes", "prism_block_permute", "prism_select", "prism_sparse_attn_fwd",
                           "prism_sparse_attn_bwd", "prism_workspace_size", "prism_status_string",
                           "prism_last_error", "prism_candidate_shapes"}
     lib = ctypes.CDLL(LIB)
@@ -191,3 +191,19 @@ def test_workspace_sizes_grow_with_the_problem():
     f1 = P.prism_workspace_size(P.OP_ATTN_FWD, 4096, 1, 64, 16, 256)
     assert 0 < f1 < P.prism_workspace_size(P.OP_ATTN_FWD, 4096, 2, 64, 16, 256)
     assert P.prism_workspace_size(P.OP_ZONE_SHAPES, 512, 1, 3072, 0, 0) >= 16 * 8
+
+
+def test_norm_map_rejects():
+    lib, P = _lib()
+    need = P.prism_workspace_size(P.OP_NORM_MAP, 1000, 0, 0, 0, 0)
+    assert need >= 8 * 1000
+    f = lambda h=A, dt=1, N=1000, C=64, ld=64, a=B, ws=Cc, wsb=need: lib.prism_audio_norm_map(h, dt, N, C, ld, a, None,
+                                                                                          ws, wsb, None)
+    assert f(dt=2) == 3
+    assert f(h=None) == 1
+    assert f(a=None) == 1
+    assert f(N=0) == 1
+    assert f(C=0) == 1
+    assert f(ld=63) == 1
+    assert f(ws=None) == 5
+    assert f(wsb=need - 8) == 5

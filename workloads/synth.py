@@ -243,6 +243,27 @@ def audio_map(cfg: Config, device="cpu"):
     return a.clamp_(0.0, 1.0).reshape(-1).contiguous()
 
 
+def cross_attn_output(cfg: Config | str, device="cpu", channels=None, chunk=65536):
+    """Synthetic audio-to-video cross-attention output h [N, C] in the config's
+    dtype (C = heads * d unless `channels` is given): row n is seeded Gaussian
+    noise times (audio_map(n) + 0.01) / sqrt(C), so the per-token magnitude
+    follows the audio map's blobs.  Generated `chunk` rows at a time."""
+    if isinstance(cfg, str):
+        cfg = CONFIGS[cfg]
+    device = torch.device(device)
+    C = int(channels or cfg.heads * cfg.d)
+    scale = (audio_map(cfg, device) + 0.01) * (1.0 / math.sqrt(C))
+    g = torch.Generator(device=device)
+    g.manual_seed((cfg.seed + 1) * 7_919_000 + 17)
+    out = torch.empty((cfg.N, C), dtype=_out_dtype(cfg), device=device)
+    for r0 in range(0, cfg.N, chunk):
+        r1 = min(cfg.N, r0 + chunk)
+        x = torch.randn((r1 - r0, C), generator=g, device=device, dtype=torch.float32)
+        x *= scale[r0:r1].view(-1, 1)
+        out[r0:r1] = x.to(out.dtype)
+    return out
+
+
 def make_inputs(cfg: Config | str, device="cpu", heads=None, tensors=("q", "k", "v", "do")):
     """Generate the inputs of one configuration.
 
