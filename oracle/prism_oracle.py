@@ -7,6 +7,9 @@ no code, table or constant with the product: every step below is written out
 again from the pages, in NumPy float64, slowly and in the pages' order.
 
 Sources ("the pages"):
+  [P5] "In-Context Sparse Attention" article at aitrends.kr (next row f3 only):
+       query-block sharpness M_i routes blocks to an exact "sharp" group or a
+       "flat" group computed with block-mean keys (zeroth-order Taylor).
   [P3] "Prism: Dynamic Sparse Attention cho Huấn luyện Mô hình Tạo Video-Âm thanh
        Đồng thời Độ phân giải Gốc 2K", reading guide at xyznot.com (paper
        2610.05416).  Sections used: "Các ý tưởng cốt lõi" (core ideas) and
@@ -26,6 +29,9 @@ Parity status per function:
     audio_norm_map (the norm; its normalisation is a reading), candidate_shapes, axis_profiles, video_variance, audio_terms (as read),
     indicator, volume, optimum_log2, nearest_shape, block layout, permutation,
     pool_blocks, block_logits, select_row, attention forward and backward.
+    next row f3: block_sharpness, flat_route, taylor_attn_fwd_block (each pinned
+    to closed forms of its reading: uniform and one-hot rows, brute-force
+    ranking, constant-key blocks where the expansion is exact, a zero query).
   parity unpinned (readings with no number on the pages to check against):
     the formula of the audio coupling a_bar and of the normalised directional
     audio variance v_hat (audio_terms), and the density rho (density).  Their
@@ -467,3 +473,54 @@ def key_block_grads(Qp, Kp, Vp, dOp, offs, csr_offs, csr_idx, j, head, scale, ro
         dK += dk[pos]
         dV += dv[pos]
     return dK, dV
+
+
+# ----------------------------------------------------------------------------
+# next row f3: sharpness routing and the zeroth-order Taylor path for flat
+# query blocks ("In-Context Sparse Attention" article, sections on grouped
+# computation and the zeroth-order Taylor kernel)
+
+def block_sharpness(L):
+    """M_i, the variance of query block i's softmax distribution.  Reading: the
+    distribution is the softmax of the row's pooled scores L[i, :] over all
+    key blocks (the scores that the selection ranks); the variance is the
+    population variance of its NB probabilities.  float64."""
+    X = np.asarray(L, dtype=np.float64)
+    NB = X.shape[1]
+    P = np.exp(X - X.max(axis=1, keepdims=True))
+    P /= P.sum(axis=1, keepdims=True)
+    return ((P - 1.0 / NB) ** 2).mean(axis=1)
+
+
+def flat_route(M, flat_ratio):
+    """Flat flags: the floor(flat_ratio * NB) query blocks of lowest sharpness,
+    ties toward the lower index; the rest are sharp.  Reading: the article
+    names a flat-ratio parameter and a threshold on M_i without values; a
+    ratio fixes the threshold per head."""
+    M = np.asarray(M, dtype=np.float64)
+    NB = M.shape[0]
+    n_flat = int(math.floor(float(flat_ratio) * NB))
+    order = sorted(range(NB), key=lambda i: (M[i], i))
+    flat = np.zeros(NB, dtype=bool)
+    flat[order[:n_flat]] = True
+    return flat
+
+
+def taylor_attn_fwd_block(Qp, Kp, Vp, offs, sel, i, head, scale):
+    """Flat path for query block i: every selected key block j enters as its
+    mean key K_bar_j and mean value V_bar_j, counted B_j times, which is the
+    zeroth-order expansion of exp(q.k) around k = K_bar_j:
+        O_q = sum_j B_j exp(s q.K_bar_j) V_bar_j / sum_j B_j exp(s q.K_bar_j).
+    Reading: the article applies the block-mean kernel to the flat group's
+    key blocks; here those are the block's selected set S_i.  Returns the
+    output rows and the natural-log log-sum-exp of the weights."""
+    q = np.asarray(Qp[offs[i]:offs[i + 1], head, :], dtype=np.float64)
+    sel = [int(j) for j in sel]
+    kb = np.stack([np.asarray(Kp[offs[j]:offs[j + 1], head, :], dtype=np.float64).mean(axis=0) for j in sel])
+    vb = np.stack([np.asarray(Vp[offs[j]:offs[j + 1], head, :], dtype=np.float64).mean(axis=0) for j in sel])
+    cnt = np.array([float(offs[j + 1] - offs[j]) for j in sel])
+    s = float(np.float32(scale)) * (q @ kb.T) + np.log(cnt)[None, :]
+    m = s.max(axis=1, keepdims=True)
+    e = np.exp(s - m)
+    l = e.sum(axis=1, keepdims=True)
+    return (e @ vb) / l, (m + np.log(l))[:, 0]

@@ -606,3 +606,71 @@ def test_zone_shapes_on_a_designed_grid():
     assert cands[res["shape"][3]][0] == 2
     assert res["NB"] == 8 + 2 + 8 + 4
     assert res["near_tie"][3]                              # rho sits exactly on tau256
+
+
+# ---------------------------------------------------------------- next row f3: routing and the flat path
+
+def test_sharpness_closed_forms():
+    NB = 12
+    L = np.zeros((4, NB))
+    L[1, 5] = 1000.0                                      # one block takes all the mass
+    L[2, :3] = math.log(2.0)                              # three blocks weigh twice the rest
+    L[3] = np.arange(NB) * 0.0 + 7.0                      # constant row, shifted
+    M = orc.block_sharpness(L)
+    assert M[0] == 0.0 and M[3] == 0.0                    # uniform rows
+    assert math.isclose(M[1], (NB - 1) / NB ** 2, rel_tol=1e-15)
+    # two-level row: p_hot = 2/(NB+3), p_cold = 1/(NB+3), variance by exact rationals
+    ph, pc, mu = Fraction(2, NB + 3), Fraction(1, NB + 3), Fraction(1, NB)
+    want = (3 * (ph - mu) ** 2 + (NB - 3) * (pc - mu) ** 2) / NB
+    assert math.isclose(M[2], float(want), rel_tol=1e-12)
+    assert (orc.block_sharpness(L + 5.0) == M).all()     # a constant per row does not matter
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_flat_route_is_a_stable_ranking(seed):
+    rng = np.random.default_rng(seed)
+    M = rng.integers(0, 6, size=40).astype(np.float64)   # many ties
+    for ratio in (0.0, 0.1, 0.5, 0.99, 1.0):
+        flat = orc.flat_route(M, ratio)
+        n = int(math.floor(ratio * 40))
+        want = np.zeros(40, dtype=bool)
+        want[np.argsort(M, kind="stable")[:n]] = True     # stable: ties to the lower index
+        assert (flat == want).all() and flat.sum() == n
+
+
+def _constant_key_problem(seed):
+    rng = np.random.default_rng(seed)
+    offs = np.array([0, 64, 192, 256, 512, 576])
+    N, d = offs[-1], 16
+    Kp = np.empty((N, 1, d))
+    for j in range(len(offs) - 1):
+        Kp[offs[j]:offs[j + 1], 0] = rng.standard_normal(d)   # every key of block j equal
+    Qp = rng.standard_normal((N, 1, d))
+    Vp = rng.standard_normal((N, 1, d))
+    return offs, Qp, Kp, Vp
+
+
+def test_taylor_path_is_exact_when_keys_are_constant_per_block():
+    offs, Qp, Kp, Vp = _constant_key_problem(3)
+    sel, i, scale = [0, 2, 3], 1, 0.3
+    o, lse = orc.taylor_attn_fwd_block(Qp, Kp, Vp, offs, sel, i, 0, scale)
+    keys = np.concatenate([np.arange(offs[j], offs[j + 1]) for j in sel])
+    q = torch.tensor(Qp[offs[i]:offs[i + 1], 0])[None, None]
+    k = torch.tensor(Kp[keys, 0])[None, None]
+    v = torch.tensor(Vp[keys, 0])[None, None]
+    want = torch.nn.functional.scaled_dot_product_attention(q, k, v, scale=float(np.float32(scale)))[0, 0].numpy()
+    np.testing.assert_allclose(o, want, rtol=1e-12, atol=1e-12)
+    s = float(np.float32(scale)) * (q[0, 0].numpy() @ k[0, 0].numpy().T)
+    np.testing.assert_allclose(lse, np.log(np.exp(s).sum(axis=1)), rtol=1e-12)
+
+
+def test_taylor_path_with_a_zero_query_is_the_mean_value():
+    offs, Qp, Kp, Vp = _constant_key_problem(4)
+    rng = np.random.default_rng(9)
+    Kp = rng.standard_normal(Kp.shape)                   # keys no longer constant: q = 0 ignores them
+    Qp[offs[2]:offs[3]] = 0.0
+    sel = [1, 4]
+    o, lse = orc.taylor_attn_fwd_block(Qp, Kp, Vp, offs, sel, 2, 0, 0.25)
+    keys = np.concatenate([np.arange(offs[j], offs[j + 1]) for j in sel])
+    np.testing.assert_allclose(o, np.broadcast_to(Vp[keys, 0].mean(axis=0), o.shape), rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(lse, math.log(len(keys)), rtol=1e-14)
