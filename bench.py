@@ -57,6 +57,8 @@ def parse():
     ap.add_argument("--config", default="2k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--flat-ratio", type=float, default=0.5,
+                    help="flat ratio of the routed-forward measurement (next row f3)")
     ap.add_argument("--profile", metavar="DIR", help="run the rocprofv3 passes and write summaries into DIR")
     return ap.parse_args()
 
@@ -336,6 +338,38 @@ def measure_norm_map(cfg, reps=10):
                          "frac": round(gbs / PEAK_HBM_GBS, 4)}}
 
 
+def measure_routed(path, qp, kp, vp, ratio, reps=3):
+    """Sharpness routing and the routed forward (flat blocks on the block-mean
+    path) against the exact forward, on the first head group of the step's
+    permuted tensors, timed with HIP events outside the step."""
+    print("[bench] routed forward", file=sys.stderr, flush=True)
+    sel = path.select(qp, kp, 0, want_logits=True)
+    flat, _ = path.route(sel, ratio, want_sharpness=True)
+    path.forward(qp, kp, vp, sel)
+    path.routed_forward(qp, kp, vp, sel, flat)
+    torch.cuda.synchronize()
+
+    def timed(fn):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    route_ms = timed(lambda: path.route(sel, ratio))
+    exact_ms = timed(lambda: path.forward(qp, kp, vp, sel))
+    routed_ms = timed(lambda: path.routed_forward(qp, kp, vp, sel, flat))
+    sizes = (path.block_offsets[1:path.nb + 1] - path.block_offsets[:path.nb]).to(torch.float64)
+    flat_tokens = float((flat.to(torch.float64) * sizes).sum()) / (path.hc * path.N)
+    del sel
+    return {"flat_ratio": ratio, "heads": path.hc, "flat_token_fraction": round(flat_tokens, 4),
+            "route_ms": round(route_ms, 3), "exact_forward_ms": round(exact_ms, 3),
+            "routed_forward_ms": round(routed_ms, 3),
+            "forward_speedup": round(exact_ms / (routed_ms + route_ms), 3)}
+
+
 def main():
     args = parse()
     if args.profile:
@@ -480,7 +514,8 @@ def main():
         "stage_gbs_algorithmic": stage_gbs,
         "roofline": roofline,
     }
-    result["next_rows"] = {"f1_audio_norm_map": measure_norm_map(cfg)}
+    result["next_rows"] = {"f1_audio_norm_map": measure_norm_map(cfg),
+                           "f3_routed_forward": measure_routed(path, qp, kp, vp, args.flat_ratio)}
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(cfg, x, path.zone_shape.cpu().numpy(), args.cpu_seconds)

@@ -45,13 +45,14 @@ __global__ void __launch_bounds__(64)
 attn_fwd_simt_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, T* __restrict__ o,
                      float* __restrict__ lse, int64_t N, int64_t ld, int64_t hs, const int32_t* __restrict__ offs,
                      int nb, const int32_t* __restrict__ sel_off, const int32_t* __restrict__ sel_idx, int64_t cap,
-                     float scale) {
+                     const uint8_t* __restrict__ skip, float scale) {
     __shared__ float Ks[kChunk][D + 1];
     __shared__ float Vs[kChunk][D + 1];
     const int h = blockIdx.y;
     const int64_t p0 = static_cast<int64_t>(blockIdx.x) * 64;
     const int64_t p = p0 + threadIdx.x;
     const int i = block_of(offs, nb, p0);
+    if (skip && skip[static_cast<int64_t>(h) * nb + i]) return;   // routed to another path
     const T* __restrict__ qh = q + h * hs;
     const T* __restrict__ kh = k + h * hs;
     const T* __restrict__ vh = v + h * hs;
@@ -270,22 +271,23 @@ attn_dkdv_simt_kernel(const T* __restrict__ q, const T* __restrict__ k, const T*
 template <typename T, int D>
 static hipError_t fwd_simt(const void* q, const void* k, const void* v, void* o, float* lse, int64_t N, int heads,
                            int64_t ld, int64_t hs, const int32_t* offs, int nb, const int32_t* so, const int32_t* si,
-                           int64_t cap, float scale, hipStream_t s) {
+                           int64_t cap, const uint8_t* skip, float scale, hipStream_t s) {
     const dim3 grid(static_cast<unsigned>(N / 64), heads);
     hipLaunchKernelGGL((attn_fwd_simt_kernel<T, D>), grid, dim3(64), 0, s, static_cast<const T*>(q),
                        static_cast<const T*>(k), static_cast<const T*>(v), static_cast<T*>(o), lse, N, ld, hs, offs, nb,
-                       so, si, cap, scale);
+                       so, si, cap, skip, scale);
     return hipGetLastError();
 }
 
 hipError_t launch_attn_fwd_simt(const void* q, const void* k, const void* v, void* o, float* lse, bool bf16, int64_t N,
                                 int heads, int d, int64_t ld, int64_t hs, const int32_t* offs, int nb,
-                                const int32_t* so, const int32_t* si, int64_t cap, float scale, hipStream_t s) {
+                                const int32_t* so, const int32_t* si, int64_t cap, const uint8_t* skip, float scale,
+                                hipStream_t s) {
     if (bf16)
-        return d == 128 ? fwd_simt<uint16_t, 128>(q, k, v, o, lse, N, heads, ld, hs, offs, nb, so, si, cap, scale, s)
-                        : fwd_simt<uint16_t, 64>(q, k, v, o, lse, N, heads, ld, hs, offs, nb, so, si, cap, scale, s);
-    return d == 128 ? fwd_simt<float, 128>(q, k, v, o, lse, N, heads, ld, hs, offs, nb, so, si, cap, scale, s)
-                    : fwd_simt<float, 64>(q, k, v, o, lse, N, heads, ld, hs, offs, nb, so, si, cap, scale, s);
+        return d == 128 ? fwd_simt<uint16_t, 128>(q, k, v, o, lse, N, heads, ld, hs, offs, nb, so, si, cap, skip, scale, s)
+                        : fwd_simt<uint16_t, 64>(q, k, v, o, lse, N, heads, ld, hs, offs, nb, so, si, cap, skip, scale, s);
+    return d == 128 ? fwd_simt<float, 128>(q, k, v, o, lse, N, heads, ld, hs, offs, nb, so, si, cap, skip, scale, s)
+                    : fwd_simt<float, 64>(q, k, v, o, lse, N, heads, ld, hs, offs, nb, so, si, cap, skip, scale, s);
 }
 
 template <typename T, int D>

@@ -189,6 +189,8 @@ void prism_candidate_shapes(int32_t out[16][3]) {
 }
 
 size_t prism_workspace_size(int32_t op, int64_t N, int32_t heads, int32_t d, int32_t nb, int64_t cap) {
+    if (op == PRISM_OP_FLAT_ROUTE)   // no token count: heads x nb sharpness values
+        return heads > 0 && nb > 0 ? align_up(static_cast<size_t>(heads) * nb * sizeof(double)) : 0;
     if (N <= 0) return 0;
     switch (op) {
         case PRISM_OP_ZONE_SHAPES: return zone_ws(N, d);
@@ -200,6 +202,13 @@ size_t prism_workspace_size(int32_t op, int64_t N, int32_t heads, int32_t d, int
         case PRISM_OP_ATTN_FWD: {
             Carver c(nullptr);
             carve_order(c, N, heads, nb);
+            return c.off;
+        }
+        case PRISM_OP_ROUTED_FWD: {
+            Carver c(nullptr);
+            carve_order(c, N, heads, nb);
+            c.take<float>(static_cast<size_t>(heads) * nb * d);
+            c.take<float>(static_cast<size_t>(heads) * nb * d);
             return c.off;
         }
         case PRISM_OP_NORM_MAP:
@@ -342,11 +351,12 @@ prism_status prism_select(const void* q, const void* k, prism_dtype dt, int64_t 
                       "select launch");
 }
 
-prism_status prism_sparse_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, prism_dtype dt,
-                                   int64_t N, int32_t heads, int32_t d, int64_t ld, int64_t hs,
-                                   const int32_t* block_offsets, int32_t nb, const int32_t* sel_offsets,
-                                   const int32_t* sel_idx, int64_t cap, float scale, void* ws, size_t ws_bytes,
-                                   hipStream_t stream) {
+namespace {
+
+// Checks shared by the exact and the routed forward.
+prism_status check_fwd(const void* q, const void* k, const void* v, const void* o, const float* lse, prism_dtype dt,
+                       int64_t N, int32_t heads, int32_t d, int64_t ld, int64_t hs, const int32_t* block_offsets,
+                       int32_t nb, const int32_t* sel_offsets, const int32_t* sel_idx, int64_t cap, float scale) {
     prism_status st = check_tokens(dt, N, heads, d, ld, hs, nb, cap);
     if (st != PRISM_OK) return st;
     if (!q || !k || !v || !o || !lse || !block_offsets || !sel_offsets || !sel_idx)
@@ -354,24 +364,91 @@ prism_status prism_sparse_attn_fwd(const void* q, const void* k, const void* v, 
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
         return fail(PRISM_E_UNSUPPORTED, "token tensors must be 16-byte aligned");
     if (!std::isfinite(scale) || !(scale > 0.0f)) return fail(PRISM_E_ARG, "scale must be finite and positive");
+    if (static_cast<int64_t>(N / 64) * heads > 0x7FFFFFFF)
+        return fail(PRISM_E_UNSUPPORTED, "too many query tiles for one launch");
+    return PRISM_OK;
+}
+
+// Exact forward over the tiles whose block is not marked in `skip` (NULL: all).
+prism_status exact_fwd(const void* q, const void* k, const void* v, void* o, float* lse, prism_dtype dt, int64_t N,
+                       int32_t heads, int32_t d, int64_t ld, int64_t hs, const int32_t* block_offsets, int32_t nb,
+                       const int32_t* sel_offsets, const int32_t* sel_idx, int64_t cap, const uint8_t* skip,
+                       float scale, Carver& c, hipStream_t stream) {
+    OrderWs w = carve_order(c, N, heads, nb);
+    if (use_simt_attention(dt))
+        return hip_status(prism::launch_attn_fwd_simt(q, k, v, o, lse, dt == PRISM_BF16, N, heads, d, ld, hs,
+                                                      block_offsets, nb, sel_offsets, sel_idx, cap, skip, scale,
+                                                      stream),
+                          "attention forward launch");
+    prism_status st = hip_status(prism::launch_tile_order(sel_offsets, sel_idx, cap, block_offsets, nb, heads, N / 64,
+                                                          w.bucket, w.start, w.order, stream),
+                                 "tile order launch");
+    if (st != PRISM_OK) return st;
+    return hip_status(prism::launch_attn_fwd_mfma(q, k, v, o, lse, N, heads, d, ld, hs, block_offsets, nb, sel_offsets,
+                                                  sel_idx, cap, w.order, skip, scale, stream),
+                      "attention forward launch");
+}
+
+}  // namespace
+
+prism_status prism_sparse_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, prism_dtype dt,
+                                   int64_t N, int32_t heads, int32_t d, int64_t ld, int64_t hs,
+                                   const int32_t* block_offsets, int32_t nb, const int32_t* sel_offsets,
+                                   const int32_t* sel_idx, int64_t cap, float scale, void* ws, size_t ws_bytes,
+                                   hipStream_t stream) {
+    prism_status st = check_fwd(q, k, v, o, lse, dt, N, heads, d, ld, hs, block_offsets, nb, sel_offsets, sel_idx, cap,
+                                scale);
+    if (st != PRISM_OK) return st;
     const size_t need = prism_workspace_size(PRISM_OP_ATTN_FWD, N, heads, d, nb, cap);
     if (!ws || ws_bytes < need)
         return fail(PRISM_E_WORKSPACE, "forward needs %zu workspace bytes, got %zu", need, ws ? ws_bytes : 0);
-    if (use_simt_attention(dt))
-        return hip_status(prism::launch_attn_fwd_simt(q, k, v, o, lse, dt == PRISM_BF16, N, heads, d, ld, hs,
-                                                      block_offsets, nb, sel_offsets, sel_idx, cap, scale, stream),
-                          "attention forward launch");
-    if (static_cast<int64_t>(N / 64) * heads > 0x7FFFFFFF)
-        return fail(PRISM_E_UNSUPPORTED, "too many query tiles for one launch");
     Carver c(ws);
-    OrderWs w = carve_order(c, N, heads, nb);
-    st = hip_status(prism::launch_tile_order(sel_offsets, sel_idx, cap, block_offsets, nb, heads, N / 64, w.bucket,
-                                             w.start, w.order, stream),
-                    "tile order launch");
+    return exact_fwd(q, k, v, o, lse, dt, N, heads, d, ld, hs, block_offsets, nb, sel_offsets, sel_idx, cap, nullptr,
+                     scale, c, stream);
+}
+
+prism_status prism_flat_route(const float* logits, int32_t heads, int32_t nb, double flat_ratio, uint8_t* flat,
+                              double* sharpness, void* ws, size_t ws_bytes, hipStream_t stream) {
+    if (!logits || !flat) return fail(PRISM_E_ARG, "null pointer argument");
+    if (heads <= 0 || nb <= 0 || heads > 65535) return fail(PRISM_E_ARG, "need 0 < heads <= 65535 and nb > 0");
+    if (!(flat_ratio >= 0.0 && flat_ratio <= 1.0)) return fail(PRISM_E_ARG, "need 0 <= flat_ratio <= 1");
+    double* M = sharpness;
+    if (!M) {
+        const size_t need = prism_workspace_size(PRISM_OP_FLAT_ROUTE, 0, heads, 0, nb, 0);
+        if (!ws || ws_bytes < need)
+            return fail(PRISM_E_WORKSPACE, "flat routing needs %zu workspace bytes, got %zu", need, ws ? ws_bytes : 0);
+        Carver c(ws);
+        M = c.take<double>(static_cast<size_t>(heads) * nb);
+    }
+    const int n_flat = static_cast<int>(std::floor(flat_ratio * static_cast<double>(nb)));
+    return hip_status(prism::launch_flat_route(logits, heads, nb, n_flat, M, flat, stream), "flat routing launch");
+}
+
+prism_status prism_routed_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, prism_dtype dt,
+                                   int64_t N, int32_t heads, int32_t d, int64_t ld, int64_t hs,
+                                   const int32_t* block_offsets, int32_t nb, const int32_t* sel_offsets,
+                                   const int32_t* sel_idx, int64_t cap, const uint8_t* flat, float scale, void* ws,
+                                   size_t ws_bytes, hipStream_t stream) {
+    prism_status st = check_fwd(q, k, v, o, lse, dt, N, heads, d, ld, hs, block_offsets, nb, sel_offsets, sel_idx, cap,
+                                scale);
     if (st != PRISM_OK) return st;
-    return hip_status(prism::launch_attn_fwd_mfma(q, k, v, o, lse, N, heads, d, ld, hs, block_offsets, nb, sel_offsets,
-                                                  sel_idx, cap, w.order, scale, stream),
-                      "attention forward launch");
+    if (!flat) return fail(PRISM_E_ARG, "null pointer argument");
+    const size_t need = prism_workspace_size(PRISM_OP_ROUTED_FWD, N, heads, d, nb, cap);
+    if (!ws || ws_bytes < need)
+        return fail(PRISM_E_WORKSPACE, "routed forward needs %zu workspace bytes, got %zu", need, ws ? ws_bytes : 0);
+    Carver c(ws);
+    st = exact_fwd(q, k, v, o, lse, dt, N, heads, d, ld, hs, block_offsets, nb, sel_offsets, sel_idx, cap, flat, scale,
+                   c, stream);
+    if (st != PRISM_OK) return st;
+    float* kbar = c.take<float>(static_cast<size_t>(heads) * nb * d);
+    float* vbar = c.take<float>(static_cast<size_t>(heads) * nb * d);
+    const bool bf16 = dt == PRISM_BF16;
+    st = hip_status(prism::launch_block_means(k, v, bf16, heads, d, ld, hs, block_offsets, nb, kbar, vbar, stream),
+                    "block means launch");
+    if (st != PRISM_OK) return st;
+    return hip_status(prism::launch_attn_flat(q, kbar, vbar, o, lse, bf16, N, heads, d, ld, hs, block_offsets, nb,
+                                              sel_offsets, sel_idx, cap, flat, scale, stream),
+                      "flat attention launch");
 }
 
 prism_status prism_sparse_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,

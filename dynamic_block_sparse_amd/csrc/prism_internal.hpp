@@ -33,11 +33,13 @@ hipError_t launch_transpose_csr(const int32_t* sel_offsets, const int32_t* sel_i
 
 hipError_t launch_attn_fwd_simt(const void* q, const void* k, const void* v, void* o, float* lse, bool bf16, int64_t N,
                                 int heads, int d, int64_t ld, int64_t hs, const int32_t* offs, int nb,
-                                const int32_t* so, const int32_t* si, int64_t cap, float scale, hipStream_t s);
+                                const int32_t* so, const int32_t* si, int64_t cap, const uint8_t* skip, float scale,
+                                hipStream_t s);
 
 hipError_t launch_attn_fwd_mfma(const void* q, const void* k, const void* v, void* o, float* lse, int64_t N, int heads,
                                 int d, int64_t ld, int64_t hs, const int32_t* offs, int nb, const int32_t* so,
-                                const int32_t* si, int64_t cap, const int32_t* order, float scale, hipStream_t s);
+                                const int32_t* si, int64_t cap, const int32_t* order, const uint8_t* skip, float scale,
+                                hipStream_t s);
 
 hipError_t launch_bwd_dot(const void* o, const void* dout, bool bf16, int64_t N, int heads, int d, int64_t ld,
                           int64_t hs, float* Dq, hipStream_t s);
@@ -64,5 +66,15 @@ constexpr int kNormMapMaxBlocks = 4096;
 int norm_map_blocks(int64_t N);
 hipError_t launch_norm_map(const void* h, bool bf16, int64_t N, int64_t C, int64_t ld, float* a, double* norms,
                            double* block_max, hipStream_t s);
+
+// next row f3: sharpness routing and the block-mean flat path
+hipError_t launch_flat_route(const float* logits, int heads, int nb, int n_flat, double* sharpness, uint8_t* flat,
+                             hipStream_t s);
+hipError_t launch_block_means(const void* k, const void* v, bool bf16, int heads, int d, int64_t ld, int64_t hs,
+                              const int32_t* offs, int nb, float* kbar, float* vbar, hipStream_t s);
+hipError_t launch_attn_flat(const void* q, const float* kbar, const float* vbar, void* o, float* lse, bool bf16,
+                            int64_t N, int heads, int d, int64_t ld, int64_t hs, const int32_t* offs, int nb,
+                            const int32_t* so, const int32_t* si, int64_t cap, const uint8_t* flat, float scale,
+                            hipStream_t s);
 
 }  // namespace prism

@@ -116,6 +116,28 @@ class PrismPath:
                                 self.nb, sel.offsets, sel.idx, sel.cap, self.scale, ws=ws)
         return op, lse
 
+    def route(self, sel, flat_ratio, want_sharpness=False):
+        """Flat flags [hc, nb] (uint8) of a selection made with want_logits=True,
+        and the float64 sharpness when asked for."""
+        hc, nb = self.hc, self.nb
+        flat = torch.empty((hc, nb), dtype=torch.uint8, device=self.device)
+        M = torch.empty((hc, nb), dtype=torch.float64, device=self.device)
+        P.prism_flat_route(sel.logits, hc, nb, flat_ratio, flat, sharpness=M)
+        return (flat, M) if want_sharpness else flat
+
+    def routed_forward(self, qp, kp, vp, sel, flat, op=None, lse=None, h0=0):
+        hc = self.hc
+        if op is None:
+            op = self.block_major_like(qp)
+        if lse is None:
+            lse = torch.empty((hc, self.N), dtype=torch.float32, device=self.device)
+        ws = torch.empty(P.prism_workspace_size(P.OP_ROUTED_FWD, self.N, hc, self.d, self.nb, sel.cap),
+                         dtype=torch.uint8, device=self.device)
+        q, k, v, o = (x[:, h0:h0 + hc] for x in (qp, kp, vp, op))
+        P.prism_routed_attn_fwd(q, k, v, o, lse, self.N, hc, self.d, q.stride(0), q.stride(1), self.block_offsets,
+                                self.nb, sel.offsets, sel.idx, sel.cap, flat, self.scale, ws)
+        return op, lse
+
     def backward(self, qp, kp, vp, op, dop, lse, sel, grads=None, h0=0):
         hc = self.hc
         if grads is None:

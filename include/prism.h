@@ -73,7 +73,7 @@ typedef struct { double tau128, tau256, eps; } prism_shape_params;
 
 /* operation codes for prism_workspace_size */
 enum { PRISM_OP_ZONE_SHAPES = 0, PRISM_OP_SELECT = 1, PRISM_OP_ATTN_FWD = 2, PRISM_OP_ATTN_BWD = 3,
-       PRISM_OP_NORM_MAP = 4 };
+       PRISM_OP_NORM_MAP = 4, PRISM_OP_FLAT_ROUTE = 5, PRISM_OP_ROUTED_FWD = 6 };
 
 /* Per-zone record written by prism_zone_shapes when `zone_stats` is not NULL:
  * 16 doubles per zone. */
@@ -267,6 +267,45 @@ prism_status prism_sparse_attn_bwd(const void* q, const void* k, const void* v, 
                                    const int32_t* block_offsets, int32_t nb,
                                    const int32_t* sel_offsets, const int32_t* sel_idx, int64_t cap,
                                    float scale, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * prism_flat_route - sharpness routing of query blocks (next row after the
+ * exact path; "In-Context Sparse Attention" article, grouped computation):
+ * M_i is the variance of the softmax of query block i's pooled scores over its
+ * NB key blocks, and the floor(flat_ratio * NB) blocks of lowest M_i per head
+ * are flat, ties toward the lower index (the article names a flat ratio and a
+ * threshold on M_i without values).
+ *
+ *   logits     device [heads, NB, NB] fp32 pooled scores (prism_select's logits)
+ *   flat_ratio in [0, 1]
+ *   flat       out device [heads, NB] uint8: 1 flat, 0 sharp
+ *   sharpness  optional out device [heads, NB] float64 M_i (NULL: kept in ws,
+ *              prism_workspace_size(PRISM_OP_FLAT_ROUTE, 0, heads, 0, nb, 0) bytes)
+ * M_i is computed in float64 as written: max, sum of exp, then the squared
+ * deviations of the probabilities from 1/NB.  Errors: PRISM_E_ARG for a NULL
+ * pointer, heads or nb out of range, flat_ratio outside [0, 1];
+ * PRISM_E_WORKSPACE.
+ */
+prism_status prism_flat_route(const float* logits, int32_t heads, int32_t nb, double flat_ratio, uint8_t* flat,
+                              double* sharpness, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * prism_routed_attn_fwd - forward with sharp blocks on the exact path of
+ * prism_sparse_attn_fwd and flat blocks (flat[h*NB + i] != 0) on the
+ * block-mean path: every selected key block j enters as its mean key and mean
+ * value, counted B_j times (the article's zeroth-order Taylor kernel, over the
+ * block's selected set):
+ *     O_q = sum_j B_j exp(s q.K_bar_j) V_bar_j / sum_j B_j exp(s q.K_bar_j),
+ *     lse_q = log sum_j B_j exp(s q.K_bar_j).
+ * Arguments as prism_sparse_attn_fwd, plus `flat` from prism_flat_route;
+ * workspace prism_workspace_size(PRISM_OP_ROUTED_FWD, ...) bytes.  Block means
+ * are float64 sums rounded once to fp32; the flat path computes in fp32.
+ */
+prism_status prism_routed_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, prism_dtype dt,
+                                   int64_t N, int32_t heads, int32_t d, int64_t ld, int64_t hs,
+                                   const int32_t* block_offsets, int32_t nb, const int32_t* sel_offsets,
+                                   const int32_t* sel_idx, int64_t cap, const uint8_t* flat, float scale, void* ws,
+                                   size_t ws_bytes, hipStream_t stream);
 
 /* Workspace bytes for one call.  ZONE_SHAPES: N = T*H*W and d = C (heads, nb,
  * cap ignored).  SELECT, ATTN_FWD, ATTN_BWD: the call's N, heads, d, nb, cap. */

@@ -207,3 +207,30 @@ def test_norm_map_rejects():
     assert f(ld=63) == 1
     assert f(ws=None) == 5
     assert f(wsb=need - 8) == 5
+
+
+def test_flat_route_and_routed_forward_reject():
+    lib, P = _lib()
+    heads, nb = 2, 24
+    need = P.prism_workspace_size(P.OP_FLAT_ROUTE, 0, heads, 0, nb, 0)
+    assert need >= 8 * heads * nb
+    r = lambda L=A, h=heads, n=nb, ratio=0.5, fl=B, M=None, ws=Cc, wsb=need: lib.prism_flat_route(L, h, n, ratio, fl, M,
+                                                                                                 ws, wsb, None)
+    assert r(L=None) == 1
+    assert r(fl=None) == 1
+    assert r(h=0) == 1
+    assert r(n=0) == 1
+    assert r(ratio=1.5) == 1
+    assert r(ratio=float("nan")) == 1
+    assert r(ws=None) == 5
+    assert r(wsb=need - 8) == 5
+    N, d = 2048, 128
+    cap = nb * nb
+    fneed = P.prism_workspace_size(P.OP_ROUTED_FWD, N, heads, d, nb, cap)
+    assert fneed > P.prism_workspace_size(P.OP_ATTN_FWD, N, heads, d, nb, cap) + 2 * 4 * heads * nb * d - 1
+    f = lambda fl=B, ws=Cc, wsb=fneed, dt=1: lib.prism_routed_attn_fwd(A, B, Cc, Cc, A, dt, N, heads, d, 256, 128, B, nb,
+                                                                       Cc, A, cap, fl, 0.088, ws, wsb, None)
+    assert f(dt=2) == 3
+    assert f(fl=None) == 1
+    assert f(ws=None) == 5
+    assert f(wsb=fneed - 16) == 5
