@@ -74,6 +74,7 @@ struct BwdWs {
     int32_t* tr_offsets;
     int32_t* tr_idx;
     int32_t* scratch;
+    int32_t* obucket;  // bucket counts of the tile order
     int32_t* ostart;   // bucket starts of the tile order
     int32_t* qorder;   // dQ tile order
 };
@@ -84,7 +85,9 @@ BwdWs carve_bwd(Carver& c, int64_t N, int64_t heads, int64_t nb, int64_t cap) {
     w.tr_offsets = c.take<int32_t>(heads * (nb + 1));
     w.tr_idx = c.take<int32_t>(heads * cap);
     w.scratch = c.take<int32_t>(heads * cap);
-    w.ostart = c.take<int32_t>(heads * (nb + 1));
+    const int64_t units = prism::tile_order_units(static_cast<int>(heads));
+    w.obucket = c.take<int32_t>(units * nb);
+    w.ostart = c.take<int32_t>(units * (nb + 1));
     w.qorder = c.take<int32_t>(heads * (N / 64));
     return w;
 }
@@ -97,8 +100,9 @@ struct OrderWs {
 };
 OrderWs carve_order(Carver& c, int64_t N, int64_t heads, int64_t nb) {
     OrderWs w;
-    w.bucket = c.take<int32_t>(heads * nb);
-    w.start = c.take<int32_t>(heads * (nb + 1));
+    const int64_t units = prism::tile_order_units(static_cast<int>(heads));
+    w.bucket = c.take<int32_t>(units * nb);
+    w.start = c.take<int32_t>(units * (nb + 1));
     w.order = c.take<int32_t>(heads * (N / 64));
     return w;
 }
@@ -483,8 +487,7 @@ prism_status prism_sparse_attn_bwd(const void* q, const void* k, const void* v, 
                           "attention backward launch");
     if (static_cast<int64_t>(N / 64) * heads > 0x7FFFFFFF)
         return fail(PRISM_E_UNSUPPORTED, "too many tiles for one launch");
-    // the order kernels count into tcount, which the transposed CSR no longer needs
-    st = hip_status(prism::launch_tile_order(sel_offsets, sel_idx, cap, block_offsets, nb, heads, N / 64, w.tcount,
+    st = hip_status(prism::launch_tile_order(sel_offsets, sel_idx, cap, block_offsets, nb, heads, N / 64, w.obucket,
                                              w.ostart, w.qorder, stream),
                     "tile order launch");
     if (st != PRISM_OK) return st;

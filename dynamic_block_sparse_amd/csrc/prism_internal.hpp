@@ -56,7 +56,11 @@ hipError_t launch_attn_bwd_simt(const void* q, const void* k, const void* v, con
                                 const int32_t* si, const int32_t* to, const int32_t* ti, int64_t cap, float scale,
                                 hipStream_t s);
 
-// visiting order of the query tiles (per head: tile ids grouped by first selected block)
+// visiting order of the query tiles: within each unit (a head's part of one
+// XCD's range of the launch order), tile ids grouped by first selected block;
+// bucket holds tile_order_units(heads) * nb and start tile_order_units(heads) *
+// (nb + 1) ints
+inline int tile_order_units(int heads) { return heads + 8; }
 hipError_t launch_tile_order(const int32_t* sel_offsets, const int32_t* sel_idx, int64_t cap, const int32_t* offs,
                              int nb, int heads, int64_t ntiles, int32_t* bucket, int32_t* start, int32_t* order,
                              hipStream_t s);

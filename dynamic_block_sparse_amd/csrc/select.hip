@@ -751,30 +751,56 @@ __device__ __forceinline__ int order_key(const int32_t* __restrict__ so, const i
     return key >= 0 && key < nb ? key : 0;
 }
 
-// bucket[h][key] += number of tiles of each block whose first selected block is key
-__global__ void __launch_bounds__(256)
-order_count_kernel(const int32_t* __restrict__ sel_offsets, const int32_t* __restrict__ sel_idx, int64_t cap,
-                   const int32_t* __restrict__ offs, int nb, int32_t* __restrict__ bucket) {
-    const int i = blockIdx.x * 256 + threadIdx.x, h = blockIdx.y;
-    if (i >= nb) return;
-    const int32_t* so = sel_offsets + static_cast<int64_t>(h) * (nb + 1);
-    const int32_t* si = sel_idx + static_cast<int64_t>(h) * cap;
-    atomicAdd(&bucket[static_cast<int64_t>(h) * nb + order_key(so, si, cap, i, nb)], (offs[i + 1] - offs[i]) / 64);
+// The sort is done within units: the intersections of a head with one XCD's
+// contiguous range of the launch order (the attention kernels deal positions
+// [x G/8, (x+1) G/8) to XCD x).  Each XCD therefore keeps the tiles, and so the
+// work, that raster order gives it; only their order within its range changes.
+// (Sorting a whole head at once moved the selections' heavy, diffuse tiles into
+// one XCD's range when a launch held a single head: 2.4x slower on a
+// 1,105,920-token clip.)  Along the launch order neither the head nor the range
+// index decreases, so unit = head + range index names each unit once.
+__device__ __forceinline__ void tile_unit(int h, int t, int64_t ntiles, int64_t seg, int& unit, int64_t& base) {
+    const int64_t p = static_cast<int64_t>(h) * ntiles + t;
+    const int64_t r = p / seg;
+    unit = h + static_cast<int>(r);
+    base = max(static_cast<int64_t>(h) * ntiles, r * seg);
 }
 
-// order[h][start[key] + slot ...] = the block's tiles, in tile order
+// bucket[unit][key] += 1 for every tile, key = its block's first selected block
 __global__ void __launch_bounds__(256)
-order_fill_kernel(const int32_t* __restrict__ sel_offsets, const int32_t* __restrict__ sel_idx, int64_t cap,
-                  const int32_t* __restrict__ offs, int nb, int64_t ntiles, const int32_t* __restrict__ start,
-                  int32_t* __restrict__ cursor, int32_t* __restrict__ order) {
+order_count_kernel(const int32_t* __restrict__ sel_offsets, const int32_t* __restrict__ sel_idx, int64_t cap,
+                   const int32_t* __restrict__ offs, int nb, int64_t ntiles, int64_t seg, int32_t* __restrict__ bucket) {
     const int i = blockIdx.x * 256 + threadIdx.x, h = blockIdx.y;
     if (i >= nb) return;
     const int32_t* so = sel_offsets + static_cast<int64_t>(h) * (nb + 1);
     const int32_t* si = sel_idx + static_cast<int64_t>(h) * cap;
     const int key = order_key(so, si, cap, i, nb);
-    const int t0 = offs[i] / 64, nt = (offs[i + 1] - offs[i]) / 64;
-    const int pos = start[static_cast<int64_t>(h) * (nb + 1) + key] + atomicAdd(&cursor[static_cast<int64_t>(h) * nb + key], nt);
-    for (int t = 0; t < nt; ++t) order[static_cast<int64_t>(h) * ntiles + pos + t] = t0 + t;
+    for (int t = offs[i] / 64; t < offs[i + 1] / 64; ++t) {
+        int u;
+        int64_t base;
+        tile_unit(h, t, ntiles, seg, u, base);
+        atomicAdd(&bucket[static_cast<int64_t>(u) * nb + key], 1);
+    }
+}
+
+// order[base(unit) + start[unit][key] + slot] = tile
+__global__ void __launch_bounds__(256)
+order_fill_kernel(const int32_t* __restrict__ sel_offsets, const int32_t* __restrict__ sel_idx, int64_t cap,
+                  const int32_t* __restrict__ offs, int nb, int64_t ntiles, int64_t seg,
+                  const int32_t* __restrict__ start, int32_t* __restrict__ cursor, int32_t* __restrict__ order) {
+    const int i = blockIdx.x * 256 + threadIdx.x, h = blockIdx.y;
+    if (i >= nb) return;
+    const int32_t* so = sel_offsets + static_cast<int64_t>(h) * (nb + 1);
+    const int32_t* si = sel_idx + static_cast<int64_t>(h) * cap;
+    const int key = order_key(so, si, cap, i, nb);
+    for (int t = offs[i] / 64; t < offs[i + 1] / 64; ++t) {
+        int u;
+        int64_t base;
+        tile_unit(h, t, ntiles, seg, u, base);
+        const int64_t pos = base + start[static_cast<int64_t>(u) * (nb + 1) + key] +
+                            atomicAdd(&cursor[static_cast<int64_t>(u) * nb + key], 1);
+        order[pos] = t;
+    }
 }
 
 // ---------------------------------------------------------------- launchers
@@ -876,17 +902,20 @@ hipError_t launch_transpose_csr(const int32_t* sel_offsets, const int32_t* sel_i
 hipError_t launch_tile_order(const int32_t* sel_offsets, const int32_t* sel_idx, int64_t cap, const int32_t* offs,
                              int nb, int heads, int64_t ntiles, int32_t* bucket, int32_t* start, int32_t* order,
                              hipStream_t s) {
-    const int64_t nbk = static_cast<int64_t>(heads) * nb;
+    const int64_t G = ntiles * heads;
+    const int64_t seg = G % 8 ? G : G / 8;            // one XCD's range of the launch order
+    const int units = tile_order_units(heads);
+    const int64_t nbk = static_cast<int64_t>(units) * nb;
     hipError_t e = fill_zero(bucket, nbk, s);
     if (e != hipSuccess) return e;
     const dim3 g((nb + 255) / 256, heads);
-    hipLaunchKernelGGL(order_count_kernel, g, dim3(256), 0, s, sel_offsets, sel_idx, cap, offs, nb, bucket);
+    hipLaunchKernelGGL(order_count_kernel, g, dim3(256), 0, s, sel_offsets, sel_idx, cap, offs, nb, ntiles, seg, bucket);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(csr_scan_kernel, dim3(heads), dim3(1024), 0, s, bucket, nb, start,
+    hipLaunchKernelGGL(csr_scan_kernel, dim3(units), dim3(1024), 0, s, bucket, nb, start,
                        static_cast<int64_t*>(nullptr));
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if ((e = fill_zero(bucket, nbk, s)) != hipSuccess) return e;
-    hipLaunchKernelGGL(order_fill_kernel, g, dim3(256), 0, s, sel_offsets, sel_idx, cap, offs, nb, ntiles, start,
+    hipLaunchKernelGGL(order_fill_kernel, g, dim3(256), 0, s, sel_offsets, sel_idx, cap, offs, nb, ntiles, seg, start,
                        bucket, order);
     return hipGetLastError();
 }
