@@ -35,8 +35,9 @@ FLAGS = [
 # Per-source flags.  The forward kernel keeps its MFMA accumulators in
 # ordinary VGPRs: it fits in 256 of them that way, whereas with accumulator
 # registers the allocator copied O and the scores between the two register
-# files on every tile iteration (8% faster at 2K).  The backward kernels
-# need more than 256 registers and are 9% faster in the default form.
+# files on every tile iteration (8% faster at 2K).  The backward file keeps
+# the default form: its dK/dV kernel fits 256 registers and the compiler
+# already keeps its accumulators in VGPRs.
 EXTRA_FLAGS = {"attn_fwd.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form"]}
 
 

@@ -164,6 +164,8 @@ attn_dq_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
 // takes its 16-row k-steps in ascending order, so results do not depend on the
 // split.  (Measured at 2K: 103.5 ms against 107.3 ms for 2 waves that each
 // computed all four products for 32 keys in 381 registers, one wave per SIMD.)
+// The MFMA runs raise the wave's issue priority and the softmax lowers it, so
+// that of the two waves sharing a SIMD the one with matrix work goes first.
 
 template <int D>
 __global__ void __launch_bounds__(256, 2)
@@ -229,11 +231,13 @@ attn_dkdv_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
         // S (role 0) or dP (role 1) of row half mr: register x holds query row
         // 32*mr + 8*(x/4) + 4*hl + x%4 against key col of the wave's half
         auto rows = [&](int mr) {
+            __builtin_amdgcn_s_setprio(1);
             f32x16_t x;
 #pragma unroll
             for (int i = 0; i < 16; ++i) x[i] = 0.0f;
 #pragma unroll
             for (int s = 0; s < KS; ++s) x = mfma32(sw_read16<D>(rb, 32 * mr + col, 16 * s + 8 * hl), kv[s], x);
+            __builtin_amdgcn_s_setprio(0);
             return x;
         };
         auto softmax = [&](f32x16_t& x, int mr) {   // S -> P (role 0)
@@ -261,6 +265,7 @@ attn_dkdv_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
             for (int g = 0; g < 4; ++g) pex[64 * g] = float4{x[4 * g], x[4 * g + 1], x[4 * g + 2], x[4 * g + 3]};
         };
         auto accumulate = [&](const f32x16_t& x, int mr) {   // acc += tb^T x over the half's 32 rows
+            __builtin_amdgcn_s_setprio(1);
 #pragma unroll
             for (int k2 = 0; k2 < 2; ++k2) {
                 const u32x4_t bx = pack_kstep(x, k2);
@@ -268,6 +273,7 @@ attn_dkdv_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
                 for (int m = 0; m < DM; ++m)
                     acc[m] = mfma32(tr_operand<D>(tb, 32 * mr + 16 * k2, 32 * m, lane), bx, acc[m]);
             }
+            __builtin_amdgcn_s_setprio(0);
         };
         f32x16_t x0 = rows(0);
         if (role == 0) {

@@ -24,6 +24,8 @@ namespace prism {
 // scores).  Each phase boundary is one wait-and-barrier.  (Measured at 2K: 71
 // ms, against 79 ms with double-buffered K and V at one wave per SIMD.)
 //
+// The scores run at raised wave priority, the softmax at the default one.
+//
 // Query tiles are taken in the visiting order built by launch_tile_order
 // (tiles grouped by their first selected key block): order[h * ntiles + j] is
 // the j-th tile of head h.
@@ -82,6 +84,7 @@ attn_fwd_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
         const uint16_t* kt = kbuf;
         const uint16_t* vt = vbuf;
         while (true) {
+            __builtin_amdgcn_s_setprio(1);
             f32x16_t s0, s1;
 #pragma unroll
             for (int x = 0; x < 16; ++x) s0[x] = s1[x] = 0.0f;
@@ -91,6 +94,7 @@ attn_fwd_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
                 s1 = mfma32(sw_read16<D>(kt, 32 + col, 16 * s + 8 * hl), qb[s], s1);
             }
             sched_reads_ahead<2, 2, KS, 2>();
+            __builtin_amdgcn_s_setprio(0);
             dma_join();                    // V(t) landed; every wave is done with K(t)
             const int tn = cur.next();
             if (tn >= 0) dma.load(kbuf, kh_ + static_cast<int64_t>(tn) * ld, wave);
