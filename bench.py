@@ -57,6 +57,8 @@ def parse():
     ap.add_argument("--config", default="2k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-next-rows", action="store_true",
+                    help="skip the measurements of the next rows (the profile passes use this)")
     ap.add_argument("--flat-ratio", type=float, default=0.5,
                     help="flat ratio of the routed-forward measurement (next row f3)")
     ap.add_argument("--profile", metavar="DIR", help="run the rocprofv3 passes and write summaries into DIR")
@@ -185,13 +187,14 @@ def profile(args):
     os.makedirs(out, exist_ok=True)
     raw = os.path.join(ROOT, "gpurun_out", "profile_raw")
     os.makedirs(raw, exist_ok=True)
-    me = [sys.executable, "-u", os.path.abspath(__file__), "--config", args.config, "--no-cpu-baseline"]
+    me = [sys.executable, "-u", os.path.abspath(__file__), "--config", args.config, "--no-cpu-baseline",
+          "--no-next-rows"]
     rel = lambda p: os.path.relpath(p, ROOT)
 
     def cmd_for(prof, steps, warmup):
         run = ["--steps", str(steps), "--warmup", str(warmup)]
         return prof + ["--"] + me + run, " ".join(prof + ["--", "python", "bench.py", "--config", args.config,
-                                                         "--no-cpu-baseline"] + run)
+                                                         "--no-cpu-baseline", "--no-next-rows"] + run)
 
     tdir = os.path.join(raw, "trace")
     tcmd, tshow = cmd_for(["rocprofv3", "--kernel-trace", "--stats", "--output-format", "csv", "-d", tdir, "-o",
@@ -514,8 +517,9 @@ def main():
         "stage_gbs_algorithmic": stage_gbs,
         "roofline": roofline,
     }
-    result["next_rows"] = {"f1_audio_norm_map": measure_norm_map(cfg),
-                           "f3_routed_forward": measure_routed(path, qp, kp, vp, args.flat_ratio)}
+    if not args.no_next_rows:
+        result["next_rows"] = {"f1_audio_norm_map": measure_norm_map(cfg),
+                               "f3_routed_forward": measure_routed(path, qp, kp, vp, args.flat_ratio)}
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(cfg, x, path.zone_shape.cpu().numpy(), args.cpu_seconds)
