@@ -29,9 +29,12 @@ Parity status per function:
     audio_norm_map (the norm; its normalisation is a reading), candidate_shapes, axis_profiles, video_variance, audio_terms (as read),
     indicator, volume, optimum_log2, nearest_shape, block layout, permutation,
     pool_blocks, block_logits, select_row, attention forward and backward.
-    next row f3: block_sharpness, flat_route, taylor_attn_fwd_block (each pinned
+    next row f3: block_sharpness, flat_route, taylor_attn_fwd_block,
+    taylor_attn_bwd_block and routed_attention (each pinned
     to closed forms of its reading: uniform and one-hot rows, brute-force
-    ranking, constant-key blocks where the expansion is exact, a zero query).
+    ranking, constant-key blocks where the expansion is exact, a zero query;
+    the backward against torch autograd of the block-mean attention and
+    against finite differences).
   parity unpinned (readings with no number on the pages to check against):
     the formula of the audio coupling a_bar and of the normalised directional
     audio variance v_hat (audio_terms), and the density rho (density).  Their
@@ -524,3 +527,64 @@ def taylor_attn_fwd_block(Qp, Kp, Vp, offs, sel, i, head, scale):
     e = np.exp(s - m)
     l = e.sum(axis=1, keepdims=True)
     return (e @ vb) / l, (m + np.log(l))[:, 0]
+
+
+def taylor_attn_bwd_block(Qp, Kp, Vp, dOp, offs, sel, i, head, scale):
+    """Gradient of taylor_attn_fwd_block for query block i, the selection and
+    the routing held constant (reading: the article gives no backward; this is
+    the chain rule through the block means).  With w_j the weights of the
+    forward, D = rowsum(dO * O), dS_j = w_j (dO . V_bar_j - D):
+        dq = s sum_j dS_j K_bar_j,
+        dK_bar_j = s sum_q dS_qj q,   dV_bar_j = sum_q w_qj dO_q,
+    and every token of key block j receives dK_bar_j / B_j and dV_bar_j / B_j.
+    Returns (dq [B_i, d], {j: (dK_bar_j, dV_bar_j)})."""
+    s_ = float(np.float32(scale))
+    q = np.asarray(Qp[offs[i]:offs[i + 1], head, :], dtype=np.float64)
+    do = np.asarray(dOp[offs[i]:offs[i + 1], head, :], dtype=np.float64)
+    sel = [int(j) for j in sel]
+    kb = np.stack([np.asarray(Kp[offs[j]:offs[j + 1], head, :], dtype=np.float64).mean(axis=0) for j in sel])
+    vb = np.stack([np.asarray(Vp[offs[j]:offs[j + 1], head, :], dtype=np.float64).mean(axis=0) for j in sel])
+    cnt = np.array([float(offs[j + 1] - offs[j]) for j in sel])
+    sc = s_ * (q @ kb.T) + np.log(cnt)[None, :]
+    w = np.exp(sc - sc.max(axis=1, keepdims=True))
+    w /= w.sum(axis=1, keepdims=True)
+    o = w @ vb
+    D = (do * o).sum(axis=1, keepdims=True)
+    dS = w * (do @ vb.T - D)
+    dq = s_ * (dS @ kb)
+    dkb = s_ * (dS.T @ q)
+    dvb = w.T @ do
+    return dq, {j: (dkb[n], dvb[n]) for n, j in enumerate(sel)}
+
+
+def routed_attention(Qp, Kp, Vp, offs, csr_offs, csr_idx, flat, head, scale, dOp=None):
+    """Routed forward (and backward): exact attention for sharp query blocks,
+    the block-mean path for flat ones; dK and dV sum the exact contributions
+    of sharp blocks and the block-mean contributions (dK_bar_j / B_j per token)
+    of flat ones."""
+    N, _, d = Qp.shape
+    NB = len(offs) - 1
+    O = np.zeros((N, d))
+    lse = np.zeros(N)
+    dQ, dK, dV = (np.zeros((N, d)) for _ in range(3)) if dOp is not None else (None, None, None)
+    for i in range(NB):
+        sel = csr_idx[csr_offs[i]:csr_offs[i + 1]]
+        fwd = taylor_attn_fwd_block if flat[i] else attn_fwd_block
+        o, l = fwd(Qp, Kp, Vp, offs, sel, i, head, scale)
+        O[offs[i]:offs[i + 1]] = o
+        lse[offs[i]:offs[i + 1]] = l
+        if dOp is None:
+            continue
+        if flat[i]:
+            dq, g = taylor_attn_bwd_block(Qp, Kp, Vp, dOp, offs, sel, i, head, scale)
+            dQ[offs[i]:offs[i + 1]] = dq
+            for j, (dkb, dvb) in g.items():
+                B = offs[j + 1] - offs[j]
+                dK[offs[j]:offs[j + 1]] += dkb / B
+                dV[offs[j]:offs[j + 1]] += dvb / B
+        else:
+            dq, keys, dk, dv = attn_bwd_block(Qp, Kp, Vp, dOp, offs, sel, i, head, scale)
+            dQ[offs[i]:offs[i + 1]] = dq
+            dK[keys] += dk
+            dV[keys] += dv
+    return dict(O=O, lse=lse, dQ=dQ, dK=dK, dV=dV)

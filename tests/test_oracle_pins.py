@@ -674,3 +674,59 @@ def test_taylor_path_with_a_zero_query_is_the_mean_value():
     keys = np.concatenate([np.arange(offs[j], offs[j + 1]) for j in sel])
     np.testing.assert_allclose(o, np.broadcast_to(Vp[keys, 0].mean(axis=0), o.shape), rtol=1e-13, atol=1e-14)
     np.testing.assert_allclose(lse, math.log(len(keys)), rtol=1e-14)
+
+
+def _torch_block_mean_attention(Q, K, V, offs, sel, i, scale):
+    """Block-mean attention of query block i written directly on token tensors
+    (the means are taken inside, so autograd reaches every token)."""
+    q = Q[offs[i]:offs[i + 1]]
+    kb = torch.stack([K[offs[j]:offs[j + 1]].mean(dim=0) for j in sel])
+    vb = torch.stack([V[offs[j]:offs[j + 1]].mean(dim=0) for j in sel])
+    cnt = torch.tensor([float(offs[j + 1] - offs[j]) for j in sel], dtype=torch.float64)
+    w = torch.softmax(scale * (q @ kb.T) + torch.log(cnt)[None, :], dim=1)
+    return w @ vb
+
+
+def test_taylor_backward_matches_autograd():
+    rng = np.random.default_rng(21)
+    offs = np.array([0, 64, 192, 256, 512, 576])
+    N, d = offs[-1], 8
+    Qp, Kp, Vp, dOp = (rng.standard_normal((N, 1, d)) for _ in range(4))
+    sel, i, scale = [0, 1, 3, 4], 2, 0.4
+    dq, g = orc.taylor_attn_bwd_block(Qp, Kp, Vp, dOp, offs, sel, i, 0, scale)
+    Q, K, V = (torch.tensor(x[:, 0], requires_grad=True) for x in (Qp, Kp, Vp))
+    o = _torch_block_mean_attention(Q, K, V, offs, sel, i, float(np.float32(scale)))
+    (o * torch.tensor(dOp[offs[i]:offs[i + 1], 0])).sum().backward()
+    np.testing.assert_allclose(dq, Q.grad[offs[i]:offs[i + 1]].numpy(), rtol=1e-10, atol=1e-12)
+    for j in sel:
+        B = offs[j + 1] - offs[j]
+        np.testing.assert_allclose(np.broadcast_to(g[j][0] / B, (B, d)), K.grad[offs[j]:offs[j + 1]].numpy(),
+                                   rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(np.broadcast_to(g[j][1] / B, (B, d)), V.grad[offs[j]:offs[j + 1]].numpy(),
+                                   rtol=1e-10, atol=1e-12)
+    assert not K.grad[offs[2]:offs[3]].any()                      # an unselected block gets nothing
+
+
+def test_routed_attention_gradients_by_finite_differences():
+    rng = np.random.default_rng(22)
+    offs = np.array([0, 64, 128, 256, 320])
+    N, d = offs[-1], 4
+    Qp, Kp, Vp, dOp = (rng.standard_normal((N, 1, d)) * 0.5 for _ in range(4))
+    co = np.array([0, 2, 4, 7, 9])
+    ci = np.array([0, 2, 1, 3, 0, 1, 2, 2, 3])
+    flat = np.array([True, False, True, False])
+    scale = 0.7
+    r = orc.routed_attention(Qp, Kp, Vp, offs, co, ci, flat, 0, scale, dOp=dOp)
+    loss = lambda Q, K, V: float((orc.routed_attention(Q, K, V, offs, co, ci, flat, 0, scale)["O"] * dOp[:, 0]).sum())
+    h = 1e-6
+    for name, X, G in (("Q", Qp, r["dQ"]), ("K", Kp, r["dK"]), ("V", Vp, r["dV"])):
+        for t, c in ((5, 1), (70, 3), (130, 0), (300, 2)):
+            Xp, Xm = X.copy(), X.copy()
+            Xp[t, 0, c] += h
+            Xm[t, 0, c] -= h
+            args = {"Q": (Qp, Kp, Vp), "K": (Qp, Kp, Vp), "V": (Qp, Kp, Vp)}[name]
+            sub = {"Q": 0, "K": 1, "V": 2}[name]
+            ap, am = list(args), list(args)
+            ap[sub], am[sub] = Xp, Xm
+            fd = (loss(*ap) - loss(*am)) / (2 * h)
+            assert math.isclose(G[t, c], fd, rel_tol=1e-5, abs_tol=1e-8), (name, t, c, G[t, c], fd)
