@@ -341,7 +341,7 @@ def measure_norm_map(cfg, reps=10):
                          "frac": round(gbs / PEAK_HBM_GBS, 4)}}
 
 
-def measure_routed(path, qp, kp, vp, ratio, reps=3):
+def measure_routed(path, qp, kp, vp, ratio, dop=None, reps=3):
     """Sharpness routing and the routed forward (flat blocks on the block-mean
     path) against the exact forward, on the first head group of the step's
     permuted tensors, timed with HIP events outside the step."""
@@ -364,13 +364,26 @@ def measure_routed(path, qp, kp, vp, ratio, reps=3):
     route_ms = timed(lambda: path.route(sel, ratio))
     exact_ms = timed(lambda: path.forward(qp, kp, vp, sel))
     routed_ms = timed(lambda: path.routed_forward(qp, kp, vp, sel, flat))
+    bwd = {}
+    if dop is not None:
+        op, lse = path.forward(qp, kp, vp, sel)
+        rop, rlse = path.routed_forward(qp, kp, vp, sel, flat)
+        grads = tuple(path.block_major_like(qp) for _ in range(3))
+        path.backward(qp, kp, vp, op, dop, lse, sel, grads=grads)
+        path.routed_backward(qp, kp, vp, rop, dop, rlse, sel, flat, grads=grads)
+        torch.cuda.synchronize()
+        eb = timed(lambda: path.backward(qp, kp, vp, op, dop, lse, sel, grads=grads))
+        rb = timed(lambda: path.routed_backward(qp, kp, vp, rop, dop, rlse, sel, flat, grads=grads))
+        bwd = {"exact_backward_ms": round(eb, 3), "routed_backward_ms": round(rb, 3),
+               "fwd_bwd_speedup": round((exact_ms + eb) / (route_ms + routed_ms + rb), 3)}
+        del op, lse, rop, rlse, grads
     sizes = (path.block_offsets[1:path.nb + 1] - path.block_offsets[:path.nb]).to(torch.float64)
     flat_tokens = float((flat.to(torch.float64) * sizes).sum()) / (path.hc * path.N)
     del sel
     return {"flat_ratio": ratio, "heads": path.hc, "flat_token_fraction": round(flat_tokens, 4),
             "route_ms": round(route_ms, 3), "exact_forward_ms": round(exact_ms, 3),
             "routed_forward_ms": round(routed_ms, 3),
-            "forward_speedup": round(exact_ms / (routed_ms + route_ms), 3)}
+            "forward_speedup": round(exact_ms / (routed_ms + route_ms), 3), **bwd}
 
 
 def main():
@@ -519,7 +532,7 @@ def main():
     }
     if not args.no_next_rows:
         result["next_rows"] = {"f1_audio_norm_map": measure_norm_map(cfg),
-                               "f3_routed_forward": measure_routed(path, qp, kp, vp, args.flat_ratio)}
+                               "f3_routed_forward": measure_routed(path, qp, kp, vp, args.flat_ratio, dop)}
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(cfg, x, path.zone_shape.cpu().numpy(), args.cpu_seconds)

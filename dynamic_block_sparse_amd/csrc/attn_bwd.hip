@@ -38,7 +38,8 @@ attn_dq_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
                     const uint16_t* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ Dq,
                     uint16_t* __restrict__ dq, int64_t N, int64_t ld, int64_t hs, const int32_t* __restrict__ offs,
                     int nb, const int32_t* __restrict__ sel_off, const int32_t* __restrict__ sel_idx, int64_t cap,
-                    const int32_t* __restrict__ order, float scale_log2, float scale) {
+                    const int32_t* __restrict__ order, const uint8_t* __restrict__ skip, float scale_log2,
+                    float scale) {
     __shared__ uint16_t kbuf[1][64 * D], vbuf[1][64 * D];
     const int ntiles = static_cast<int>(N / 64);
     const int wg = xcd_remap(blockIdx.x);
@@ -48,6 +49,7 @@ attn_dq_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int hl = lane >> 5, col = lane & 31;
     const int i = find_block(offs, nb, p0);
+    if (skip && skip[static_cast<int64_t>(h) * nb + i]) return;   // routed to another path
     const int32_t* __restrict__ so = sel_off + static_cast<int64_t>(h) * (nb + 1);
     const int32_t* __restrict__ si = sel_idx + static_cast<int64_t>(h) * cap;
     const int e0 = so[i];
@@ -173,7 +175,8 @@ attn_dkdv_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
                       const uint16_t* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ Dq,
                       uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, int64_t N, int64_t ld, int64_t hs,
                       const int32_t* __restrict__ offs, int nb, const int32_t* __restrict__ tr_off,
-                      const int32_t* __restrict__ tr_idx, int64_t cap, float scale_log2, float scale) {
+                      const int32_t* __restrict__ tr_idx, int64_t cap, const float* __restrict__ dkbar,
+                      const float* __restrict__ dvbar, float scale_log2, float scale) {
     // Q and dO tiles, lse (natural log) and D = rowsum(dO * O) of their rows
     __shared__ uint16_t qbuf[2][64 * D], obuf[2][64 * D];
     __shared__ float lbuf[2][64], dbuf[2][64];
@@ -297,13 +300,21 @@ attn_dkdv_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
     tile_pipeline(cur, issue, compute);
     uint16_t* out = (role ? dk : dv) + key * ld + h * hs;
     const float f = role ? scale : 1.0f;
+    // routed backward: the block-mean gradient of this key block, shared by its B tokens
+    const float* __restrict__ add = role ? dkbar : dvbar;
+    const float* __restrict__ addj = add ? add + (static_cast<int64_t>(h) * nb + j) * D : nullptr;
+    const float invB = 1.0f / static_cast<float>(offs[j + 1] - offs[j]);
 #pragma unroll
     for (int m = 0; m < DM; ++m)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
             const f32x16_t& a = acc[m];
-            *reinterpret_cast<u32x2_t*>(out + 32 * m + 8 * g + 4 * hl) =
-                u32x2_t{pack2(a[4 * g] * f, a[4 * g + 1] * f), pack2(a[4 * g + 2] * f, a[4 * g + 3] * f)};
+            const int dc = 32 * m + 8 * g + 4 * hl;
+            float r[4] = {a[4 * g] * f, a[4 * g + 1] * f, a[4 * g + 2] * f, a[4 * g + 3] * f};
+            if (addj)
+#pragma unroll
+                for (int x = 0; x < 4; ++x) r[x] += addj[dc + x] * invB;
+            *reinterpret_cast<u32x2_t*>(out + dc) = u32x2_t{pack2(r[0], r[1]), pack2(r[2], r[3])};
         }
 }
 
@@ -313,7 +324,10 @@ hipError_t launch_attn_bwd_mfma(const void* q, const void* k, const void* v, con
                                 const float* Dq, void* dq, void* dk, void* dv, int64_t N, int heads, int d, int64_t ld,
                                 int64_t hs, const int32_t* offs, int nb, const int32_t* so, const int32_t* si,
                                 const int32_t* to, const int32_t* ti, int64_t cap, const int32_t* qorder,
-                                float scale, hipStream_t s) {
+                                const RouteGrad* rg, float scale, hipStream_t s) {
+    const uint8_t* skip = rg ? rg->skip_q : nullptr;
+    const float* dkb = rg ? rg->dkbar : nullptr;
+    const float* dvb = rg ? rg->dvbar : nullptr;
     const dim3 grid(static_cast<unsigned>(N / 64 * heads));
     const float sl2 = scale * kLog2e;
     const uint16_t* Q = static_cast<const uint16_t*>(q);
@@ -325,18 +339,18 @@ hipError_t launch_attn_bwd_mfma(const void* q, const void* k, const void* v, con
     uint16_t* dV = static_cast<uint16_t*>(dv);
     if (d == 128) {
         hipLaunchKernelGGL(attn_dq_mfma_kernel<128>, grid, dim3(128), 0, s, Q, K, V, O, lse, Dq, dQ, N, ld, hs, offs,
-                           nb, so, si, cap, qorder, sl2, scale);
+                           nb, so, si, cap, qorder, skip, sl2, scale);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL(attn_dkdv_mfma_kernel<128>, grid, dim3(256), 0, s, Q, K, V, O, lse, Dq, dK, dV, N, ld, hs,
-                           offs, nb, to, ti, cap, sl2, scale);
+                           offs, nb, to, ti, cap, dkb, dvb, sl2, scale);
     } else {
         hipLaunchKernelGGL(attn_dq_mfma_kernel<64>, grid, dim3(128), 0, s, Q, K, V, O, lse, Dq, dQ, N, ld, hs, offs,
-                           nb, so, si, cap, qorder, sl2, scale);
+                           nb, so, si, cap, qorder, skip, sl2, scale);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL(attn_dkdv_mfma_kernel<64>, grid, dim3(256), 0, s, Q, K, V, O, lse, Dq, dK, dV, N, ld, hs,
-                           offs, nb, to, ti, cap, sl2, scale);
+                           offs, nb, to, ti, cap, dkb, dvb, sl2, scale);
     }
     return hipGetLastError();
 }

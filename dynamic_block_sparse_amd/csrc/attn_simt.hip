@@ -152,13 +152,14 @@ attn_dq_simt_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* _
                     const T* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ Dq,
                     T* __restrict__ dq, int64_t N, int64_t ld, int64_t hs, const int32_t* __restrict__ offs, int nb,
                     const int32_t* __restrict__ sel_off, const int32_t* __restrict__ sel_idx, int64_t cap,
-                    float scale) {
+                    const uint8_t* __restrict__ skip, float scale) {
     __shared__ float Ks[kChunk][D + 1];
     __shared__ float Vs[kChunk][D + 1];
     const int h = blockIdx.y;
     const int64_t p0 = static_cast<int64_t>(blockIdx.x) * 64;
     const int64_t p = p0 + threadIdx.x;
     const int i = block_of(offs, nb, p0);
+    if (skip && skip[static_cast<int64_t>(h) * nb + i]) return;   // routed to another path
     const T* __restrict__ kh = k + h * hs;
     const T* __restrict__ vh = v + h * hs;
     float qr[D], dor[D], acc[D];
@@ -208,7 +209,8 @@ attn_dkdv_simt_kernel(const T* __restrict__ q, const T* __restrict__ k, const T*
                       const T* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ Dq,
                       T* __restrict__ dk, T* __restrict__ dv, int64_t N, int64_t ld, int64_t hs,
                       const int32_t* __restrict__ offs, int nb, const int32_t* __restrict__ tr_off,
-                      const int32_t* __restrict__ tr_idx, int64_t cap, float scale) {
+                      const int32_t* __restrict__ tr_idx, int64_t cap, const float* __restrict__ dkbar,
+                      const float* __restrict__ dvbar, float scale) {
     __shared__ float Qs[kChunk][D + 1];
     __shared__ float Os[kChunk][D + 1];
     __shared__ float Ls[kChunk], Ds[kChunk];
@@ -261,10 +263,13 @@ attn_dkdv_simt_kernel(const T* __restrict__ q, const T* __restrict__ k, const T*
             }
         }
     }
+    // routed backward: the block-mean gradients of this key block, shared by its B tokens
+    const float invB = 1.0f / static_cast<float>(offs[j + 1] - offs[j]);
+    const int64_t jb = (static_cast<int64_t>(h) * nb + j) * D;
 #pragma unroll
     for (int c = 0; c < D; ++c) {
-        st_elem(dk + p * ld + h * hs + c, ak[c] * scale);
-        st_elem(dv + p * ld + h * hs + c, av[c]);
+        st_elem(dk + p * ld + h * hs + c, ak[c] * scale + (dkbar ? dkbar[jb + c] * invB : 0.0f));
+        st_elem(dv + p * ld + h * hs + c, av[c] + (dvbar ? dvbar[jb + c] * invB : 0.0f));
     }
 }
 
@@ -311,33 +316,35 @@ template <typename T, int D>
 static hipError_t bwd_simt(const void* q, const void* k, const void* v, const void* dout, const float* lse,
                            const float* Dq, void* dq, void* dk, void* dv, int64_t N, int heads, int64_t ld,
                            int64_t hs, const int32_t* offs, int nb, const int32_t* so, const int32_t* si,
-                           const int32_t* to, const int32_t* ti, int64_t cap, float scale, hipStream_t s) {
+                           const int32_t* to, const int32_t* ti, int64_t cap, const RouteGrad* rg, float scale,
+                           hipStream_t s) {
     const dim3 grid(static_cast<unsigned>(N / 64), heads);
     hipLaunchKernelGGL((attn_dq_simt_kernel<T, D>), grid, dim3(64), 0, s, static_cast<const T*>(q),
                        static_cast<const T*>(k), static_cast<const T*>(v), static_cast<const T*>(dout), lse, Dq,
-                       static_cast<T*>(dq), N, ld, hs, offs, nb, so, si, cap, scale);
+                       static_cast<T*>(dq), N, ld, hs, offs, nb, so, si, cap, rg ? rg->skip_q : nullptr, scale);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((attn_dkdv_simt_kernel<T, D>), grid, dim3(64), 0, s, static_cast<const T*>(q),
                        static_cast<const T*>(k), static_cast<const T*>(v), static_cast<const T*>(dout), lse, Dq,
-                       static_cast<T*>(dk), static_cast<T*>(dv), N, ld, hs, offs, nb, to, ti, cap, scale);
+                       static_cast<T*>(dk), static_cast<T*>(dv), N, ld, hs, offs, nb, to, ti, cap,
+                       rg ? rg->dkbar : nullptr, rg ? rg->dvbar : nullptr, scale);
     return hipGetLastError();
 }
 
 hipError_t launch_attn_bwd_simt(const void* q, const void* k, const void* v, const void* dout, const float* lse,
                                 const float* Dq, void* dq, void* dk, void* dv, bool bf16, int64_t N, int heads, int d,
                                 int64_t ld, int64_t hs, const int32_t* offs, int nb, const int32_t* so,
-                                const int32_t* si, const int32_t* to, const int32_t* ti, int64_t cap, float scale,
-                                hipStream_t s) {
+                                const int32_t* si, const int32_t* to, const int32_t* ti, int64_t cap,
+                                const RouteGrad* rg, float scale, hipStream_t s) {
     if (bf16)
         return d == 128 ? bwd_simt<uint16_t, 128>(q, k, v, dout, lse, Dq, dq, dk, dv, N, heads, ld, hs, offs, nb, so,
-                                                   si, to, ti, cap, scale, s)
+                                                   si, to, ti, cap, rg, scale, s)
                         : bwd_simt<uint16_t, 64>(q, k, v, dout, lse, Dq, dq, dk, dv, N, heads, ld, hs, offs, nb, so, si,
-                                                  to, ti, cap, scale, s);
+                                                  to, ti, cap, rg, scale, s);
     return d == 128 ? bwd_simt<float, 128>(q, k, v, dout, lse, Dq, dq, dk, dv, N, heads, ld, hs, offs, nb, so, si, to,
-                                            ti, cap, scale, s)
+                                            ti, cap, rg, scale, s)
                     : bwd_simt<float, 64>(q, k, v, dout, lse, Dq, dq, dk, dv, N, heads, ld, hs, offs, nb, so, si, to,
-                                           ti, cap, scale, s);
+                                           ti, cap, rg, scale, s);
 }
 
 }  // namespace prism

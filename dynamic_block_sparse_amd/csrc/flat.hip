@@ -218,6 +218,198 @@ attn_flat_kernel(const T* __restrict__ q, const float* __restrict__ kbar, const 
     if (part == 0) lse[static_cast<int64_t>(h) * N + p] = m + logf(l);
 }
 
+// Backward of the flat path (the selection and routing held constant): for a
+// flat query row q with forward weights w_j = B_j e^{s q.K_bar_j - lse_q},
+// D_q = rowsum(dO * O) and dS_j = w_j (dO_q . V_bar_j - D_q):
+//   dq = s sum_j dS_j K_bar_j                         (attn_flat_dq_kernel)
+//   dK_bar_j = s sum_q dS_qj q,  dV_bar_j = sum_q w_qj dO_q   (flat_kgrad_kernel,
+//   key-major over the flat query blocks that selected j, fixed order)
+// and the dK/dV kernel adds dK_bar_j / B_j, dV_bar_j / B_j to every token of j.
+
+template <typename T, int D>
+__global__ void __launch_bounds__(256)
+attn_flat_dq_kernel(const T* __restrict__ q, const T* __restrict__ dout, const float* __restrict__ kbar,
+                    const float* __restrict__ vbar, const float* __restrict__ lse, const float* __restrict__ Dq,
+                    T* __restrict__ dq, int64_t N, int64_t ld, int64_t hs, const int32_t* __restrict__ offs, int nb,
+                    const int32_t* __restrict__ sel_off, const int32_t* __restrict__ sel_idx, int64_t cap,
+                    const uint8_t* __restrict__ flat, float scale) {
+    constexpr int PW = D / 4, PS = PW + 4, CH = 16;
+    __shared__ float Ks[CH][4][PS], Vs[CH][4][PS];
+    __shared__ float lb[CH];
+    const int ntiles = static_cast<int>(N / 64);
+    const int h = blockIdx.x / ntiles;
+    const int64_t p0 = static_cast<int64_t>(blockIdx.x % ntiles) * 64;
+    const int i = block_containing(offs, nb, p0);
+    if (!flat[static_cast<int64_t>(h) * nb + i]) return;
+    const int r = threadIdx.x >> 2, part = threadIdx.x & 3;
+    const int64_t p = p0 + r;
+    float qr[PW], dr[PW], acc[PW];
+    const T* __restrict__ qrow = q + p * ld + h * hs + part * PW;
+    const T* __restrict__ drow = dout + p * ld + h * hs + part * PW;
+#pragma unroll
+    for (int c = 0; c < PW; ++c) {
+        qr[c] = elem_in(qrow + c);
+        dr[c] = elem_in(drow + c);
+        acc[c] = 0.0f;
+    }
+    const float L = lse[static_cast<int64_t>(h) * N + p];
+    const float Dd = Dq[static_cast<int64_t>(h) * N + p];
+    const int32_t* __restrict__ so = sel_off + static_cast<int64_t>(h) * (nb + 1);
+    const int32_t* __restrict__ si = sel_idx + static_cast<int64_t>(h) * cap;
+    const int e0 = so[i];
+    const int e1 = static_cast<int>(min(static_cast<int64_t>(so[i + 1]), cap));
+    const float* __restrict__ kh = kbar + static_cast<int64_t>(h) * nb * D;
+    const float* __restrict__ vh = vbar + static_cast<int64_t>(h) * nb * D;
+    for (int e = e0; e < e1; e += CH) {
+        const int n = min(CH, e1 - e);
+        __syncthreads();
+        for (int x = threadIdx.x; x < n * D; x += 256) {
+            const int jj = x / D, c = x % D;
+            const int64_t j = si[e + jj];
+            Ks[jj][c / PW][c % PW] = kh[j * D + c];
+            Vs[jj][c / PW][c % PW] = vh[j * D + c];
+        }
+        if (threadIdx.x < n) {
+            const int j = si[e + threadIdx.x];
+            lb[threadIdx.x] = logf(static_cast<float>(offs[j + 1] - offs[j]));
+        }
+        __syncthreads();
+        for (int jj = 0; jj < n; ++jj) {
+            float d1 = 0.0f, d2 = 0.0f;
+#pragma unroll
+            for (int c = 0; c < PW; ++c) {
+                d1 = fmaf(qr[c], Ks[jj][part][c], d1);
+                d2 = fmaf(dr[c], Vs[jj][part][c], d2);
+            }
+            d1 += __shfl_xor(d1, 1, 64);
+            d1 += __shfl_xor(d1, 2, 64);
+            d2 += __shfl_xor(d2, 1, 64);
+            d2 += __shfl_xor(d2, 2, 64);
+            const float w = expf(fmaf(d1, scale, lb[jj]) - L);
+            const float ds = w * (d2 - Dd);
+#pragma unroll
+            for (int c = 0; c < PW; ++c) acc[c] = fmaf(ds, Ks[jj][part][c], acc[c]);
+        }
+    }
+    T* __restrict__ out = dq + p * ld + h * hs + part * PW;
+#pragma unroll
+    for (int c = 0; c < PW; ++c) elem_out(out + c, acc[c] * scale);
+}
+
+// grid (NB, heads): key block j against the rows of every flat query block
+// that selected it (ascending), 64 row slots of 4 lanes, reduced over slots in
+// slot order
+template <typename T, int D>
+__global__ void __launch_bounds__(256)
+flat_kgrad_kernel(const T* __restrict__ q, const T* __restrict__ dout, const float* __restrict__ kbar,
+                  const float* __restrict__ vbar, const float* __restrict__ lse, const float* __restrict__ Dq,
+                  int64_t N, int64_t ld, int64_t hs, const int32_t* __restrict__ offs, int nb,
+                  const int32_t* __restrict__ fto, const int32_t* __restrict__ fti, int64_t cap, float scale,
+                  float* __restrict__ dkbar, float* __restrict__ dvbar) {
+    constexpr int PW = D / 4;
+    __shared__ float red[64][D];
+    const int j = blockIdx.x, h = blockIdx.y;
+    const int slot = threadIdx.x >> 2, part = threadIdx.x & 3;
+    const int64_t jb = (static_cast<int64_t>(h) * nb + j) * D;
+    float kb[PW], vb[PW], ka[PW], va[PW];
+#pragma unroll
+    for (int c = 0; c < PW; ++c) {
+        kb[c] = kbar[jb + part * PW + c];
+        vb[c] = vbar[jb + part * PW + c];
+        ka[c] = va[c] = 0.0f;
+    }
+    const float lbj = logf(static_cast<float>(offs[j + 1] - offs[j]));
+    const int32_t* __restrict__ to = fto + static_cast<int64_t>(h) * (nb + 1);
+    const int32_t* __restrict__ ti = fti + static_cast<int64_t>(h) * cap;
+    const int e0 = to[j];
+    const int e1 = static_cast<int>(min(static_cast<int64_t>(to[j + 1]), cap));
+    for (int e = e0; e < e1; ++e) {
+        const int i = ti[e];
+        // blocks hold a whole number of 64-token tiles: every slot has a row
+        for (int64_t row = offs[i] + slot; row < offs[i + 1]; row += 64) {
+            float qr[PW], dr[PW];
+            const T* __restrict__ qrow = q + row * ld + h * hs + part * PW;
+            const T* __restrict__ drow = dout + row * ld + h * hs + part * PW;
+            float d1 = 0.0f, d2 = 0.0f;
+#pragma unroll
+            for (int c = 0; c < PW; ++c) {
+                qr[c] = elem_in(qrow + c);
+                dr[c] = elem_in(drow + c);
+                d1 = fmaf(qr[c], kb[c], d1);
+                d2 = fmaf(dr[c], vb[c], d2);
+            }
+            d1 += __shfl_xor(d1, 1, 64);
+            d1 += __shfl_xor(d1, 2, 64);
+            d2 += __shfl_xor(d2, 1, 64);
+            d2 += __shfl_xor(d2, 2, 64);
+            const float w = expf(fmaf(d1, scale, lbj) - lse[static_cast<int64_t>(h) * N + row]);
+            const float ds = w * (d2 - Dq[static_cast<int64_t>(h) * N + row]);
+#pragma unroll
+            for (int c = 0; c < PW; ++c) {
+                ka[c] = fmaf(ds, qr[c], ka[c]);
+                va[c] = fmaf(w, dr[c], va[c]);
+            }
+        }
+    }
+#pragma unroll
+    for (int c = 0; c < PW; ++c) red[slot][part * PW + c] = ka[c];
+    __syncthreads();
+    for (int c = threadIdx.x; c < D; c += 256) {
+        float t = 0.0f;
+        for (int s2 = 0; s2 < 64; ++s2) t += red[s2][c];
+        dkbar[jb + c] = t * scale;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < PW; ++c) red[slot][part * PW + c] = va[c];
+    __syncthreads();
+    for (int c = threadIdx.x; c < D; c += 256) {
+        float t = 0.0f;
+        for (int s2 = 0; s2 < 64; ++s2) t += red[s2][c];
+        dvbar[jb + c] = t;
+    }
+}
+
+hipError_t launch_flat_dq(const void* q, const void* dout, const float* kbar, const float* vbar, const float* lse,
+                          const float* Dq, void* dq, bool bf16, int64_t N, int heads, int d, int64_t ld, int64_t hs,
+                          const int32_t* offs, int nb, const int32_t* so, const int32_t* si, int64_t cap,
+                          const uint8_t* flat, float scale, hipStream_t s) {
+    const dim3 grid(static_cast<unsigned>(N / 64 * heads));
+#define PRISM_FLAT_DQ(T, DD)                                                                                        \
+    hipLaunchKernelGGL((attn_flat_dq_kernel<T, DD>), grid, dim3(256), 0, s, static_cast<const T*>(q),              \
+                       static_cast<const T*>(dout), kbar, vbar, lse, Dq, static_cast<T*>(dq), N, ld, hs, offs, nb, \
+                       so, si, cap, flat, scale)
+    if (bf16) {
+        if (d == 128) PRISM_FLAT_DQ(uint16_t, 128);
+        else PRISM_FLAT_DQ(uint16_t, 64);
+    } else {
+        if (d == 128) PRISM_FLAT_DQ(float, 128);
+        else PRISM_FLAT_DQ(float, 64);
+    }
+#undef PRISM_FLAT_DQ
+    return hipGetLastError();
+}
+
+hipError_t launch_flat_kgrad(const void* q, const void* dout, const float* kbar, const float* vbar, const float* lse,
+                             const float* Dq, bool bf16, int64_t N, int heads, int d, int64_t ld, int64_t hs,
+                             const int32_t* offs, int nb, const int32_t* fto, const int32_t* fti, int64_t cap,
+                             float scale, float* dkbar, float* dvbar, hipStream_t s) {
+    const dim3 grid(nb, heads);
+#define PRISM_FLAT_KG(T, DD)                                                                                       \
+    hipLaunchKernelGGL((flat_kgrad_kernel<T, DD>), grid, dim3(256), 0, s, static_cast<const T*>(q),               \
+                       static_cast<const T*>(dout), kbar, vbar, lse, Dq, N, ld, hs, offs, nb, fto, fti, cap, scale, \
+                       dkbar, dvbar)
+    if (bf16) {
+        if (d == 128) PRISM_FLAT_KG(uint16_t, 128);
+        else PRISM_FLAT_KG(uint16_t, 64);
+    } else {
+        if (d == 128) PRISM_FLAT_KG(float, 128);
+        else PRISM_FLAT_KG(float, 64);
+    }
+#undef PRISM_FLAT_KG
+    return hipGetLastError();
+}
+
 hipError_t launch_flat_route(const float* logits, int heads, int nb, int n_flat, double* sharpness, uint8_t* flat,
                              hipStream_t s) {
     hipLaunchKernelGGL(sharpness_kernel, dim3(nb, heads), dim3(256), 0, s, logits, nb, sharpness);

@@ -107,6 +107,27 @@ OrderWs carve_order(Carver& c, int64_t N, int64_t heads, int64_t nb) {
     return w;
 }
 
+// Extra workspace of the routed backward: the transposed CSR restricted to
+// flat query blocks, the block means and their gradients.
+struct RoutedBwdWs {
+    int32_t* fto;
+    int32_t* fti;
+    float* kbar;
+    float* vbar;
+    float* dkbar;
+    float* dvbar;
+};
+RoutedBwdWs carve_routed_bwd(Carver& c, int64_t heads, int64_t d, int64_t nb, int64_t cap) {
+    RoutedBwdWs w;
+    w.fto = c.take<int32_t>(heads * (nb + 1));
+    w.fti = c.take<int32_t>(heads * cap);
+    w.kbar = c.take<float>(heads * nb * d);
+    w.vbar = c.take<float>(heads * nb * d);
+    w.dkbar = c.take<float>(heads * nb * d);
+    w.dvbar = c.take<float>(heads * nb * d);
+    return w;
+}
+
 size_t zone_ws(int64_t N, int64_t C) {
     const int nZ = static_cast<int>(N / prism::kZoneTokens);
     return align_up(prism::zone_partial_doubles(nZ, C) * sizeof(double)) +
@@ -213,6 +234,12 @@ size_t prism_workspace_size(int32_t op, int64_t N, int32_t heads, int32_t d, int
             carve_order(c, N, heads, nb);
             c.take<float>(static_cast<size_t>(heads) * nb * d);
             c.take<float>(static_cast<size_t>(heads) * nb * d);
+            return c.off;
+        }
+        case PRISM_OP_ROUTED_BWD: {
+            Carver c(nullptr);
+            carve_bwd(c, N, heads, nb, cap);
+            carve_routed_bwd(c, heads, d, nb, cap);
             return c.off;
         }
         case PRISM_OP_NORM_MAP:
@@ -455,11 +482,12 @@ prism_status prism_routed_attn_fwd(const void* q, const void* k, const void* v, 
                       "flat attention launch");
 }
 
-prism_status prism_sparse_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
-                                   const float* lse, void* dq, void* dk, void* dv, prism_dtype dt, int64_t N,
-                                   int32_t heads, int32_t d, int64_t ld, int64_t hs, const int32_t* block_offsets,
-                                   int32_t nb, const int32_t* sel_offsets, const int32_t* sel_idx, int64_t cap,
-                                   float scale, void* ws, size_t ws_bytes, hipStream_t stream) {
+namespace {
+
+prism_status check_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                       const void* dq, const void* dk, const void* dv, prism_dtype dt, int64_t N, int32_t heads,
+                       int32_t d, int64_t ld, int64_t hs, const int32_t* block_offsets, int32_t nb,
+                       const int32_t* sel_offsets, const int32_t* sel_idx, int64_t cap, float scale) {
     prism_status st = check_tokens(dt, N, heads, d, ld, hs, nb, cap);
     if (st != PRISM_OK) return st;
     if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !block_offsets || !sel_offsets || !sel_idx)
@@ -468,33 +496,99 @@ prism_status prism_sparse_attn_bwd(const void* q, const void* k, const void* v, 
         !aligned16(dk) || !aligned16(dv))
         return fail(PRISM_E_UNSUPPORTED, "token tensors must be 16-byte aligned");
     if (!std::isfinite(scale) || !(scale > 0.0f)) return fail(PRISM_E_ARG, "scale must be finite and positive");
+    if (static_cast<int64_t>(N / 64) * heads > 0x7FFFFFFF)
+        return fail(PRISM_E_UNSUPPORTED, "too many tiles for one launch");
+    return PRISM_OK;
+}
+
+// dQ and dK/dV on the exact path, from a transposed CSR already built in w;
+// rg (NULL for the plain backward) carries the routed extras.
+prism_status exact_bwd(const void* q, const void* k, const void* v, const void* dout, const float* lse, void* dq,
+                       void* dk, void* dv, prism_dtype dt, int64_t N, int32_t heads, int32_t d, int64_t ld, int64_t hs,
+                       const int32_t* block_offsets, int32_t nb, const int32_t* sel_offsets, const int32_t* sel_idx,
+                       int64_t cap, float scale, const BwdWs& w, const prism::RouteGrad* rg, hipStream_t stream) {
+    if (use_simt_attention(dt))
+        return hip_status(prism::launch_attn_bwd_simt(q, k, v, dout, lse, w.Dq, dq, dk, dv, dt == PRISM_BF16, N, heads,
+                                                      d, ld, hs, block_offsets, nb, sel_offsets, sel_idx, w.tr_offsets,
+                                                      w.tr_idx, cap, rg, scale, stream),
+                          "attention backward launch");
+    prism_status st = hip_status(prism::launch_tile_order(sel_offsets, sel_idx, cap, block_offsets, nb, heads, N / 64,
+                                                          w.obucket, w.ostart, w.qorder, stream),
+                                 "tile order launch");
+    if (st != PRISM_OK) return st;
+    return hip_status(prism::launch_attn_bwd_mfma(q, k, v, dout, lse, w.Dq, dq, dk, dv, N, heads, d, ld, hs,
+                                                  block_offsets, nb, sel_offsets, sel_idx, w.tr_offsets, w.tr_idx, cap,
+                                                  w.qorder, rg, scale, stream),
+                      "attention backward launch");
+}
+
+}  // namespace
+
+prism_status prism_sparse_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                                   const float* lse, void* dq, void* dk, void* dv, prism_dtype dt, int64_t N,
+                                   int32_t heads, int32_t d, int64_t ld, int64_t hs, const int32_t* block_offsets,
+                                   int32_t nb, const int32_t* sel_offsets, const int32_t* sel_idx, int64_t cap,
+                                   float scale, void* ws, size_t ws_bytes, hipStream_t stream) {
+    prism_status st = check_bwd(q, k, v, o, dout, lse, dq, dk, dv, dt, N, heads, d, ld, hs, block_offsets, nb,
+                                sel_offsets, sel_idx, cap, scale);
+    if (st != PRISM_OK) return st;
     const size_t need = prism_workspace_size(PRISM_OP_ATTN_BWD, N, heads, d, nb, cap);
     if (!ws || ws_bytes < need)
         return fail(PRISM_E_WORKSPACE, "backward needs %zu workspace bytes, got %zu", need, ws ? ws_bytes : 0);
     Carver c(ws);
     BwdWs w = carve_bwd(c, N, heads, nb, cap);
+    st = hip_status(prism::launch_bwd_dot(o, dout, dt == PRISM_BF16, N, heads, d, ld, hs, w.Dq, stream),
+                    "backward dot launch");
+    if (st != PRISM_OK) return st;
+    st = hip_status(prism::launch_transpose_csr(sel_offsets, sel_idx, nb, heads, cap, w.tcount, w.tr_offsets, w.tr_idx,
+                                                w.scratch, nullptr, 0, stream),
+                    "transposed selection launch");
+    if (st != PRISM_OK) return st;
+    return exact_bwd(q, k, v, dout, lse, dq, dk, dv, dt, N, heads, d, ld, hs, block_offsets, nb, sel_offsets, sel_idx,
+                     cap, scale, w, nullptr, stream);
+}
+
+prism_status prism_routed_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                                   const float* lse, void* dq, void* dk, void* dv, prism_dtype dt, int64_t N,
+                                   int32_t heads, int32_t d, int64_t ld, int64_t hs, const int32_t* block_offsets,
+                                   int32_t nb, const int32_t* sel_offsets, const int32_t* sel_idx, int64_t cap,
+                                   const uint8_t* flat, float scale, void* ws, size_t ws_bytes, hipStream_t stream) {
+    prism_status st = check_bwd(q, k, v, o, dout, lse, dq, dk, dv, dt, N, heads, d, ld, hs, block_offsets, nb,
+                                sel_offsets, sel_idx, cap, scale);
+    if (st != PRISM_OK) return st;
+    if (!flat) return fail(PRISM_E_ARG, "null pointer argument");
+    const size_t need = prism_workspace_size(PRISM_OP_ROUTED_BWD, N, heads, d, nb, cap);
+    if (!ws || ws_bytes < need)
+        return fail(PRISM_E_WORKSPACE, "routed backward needs %zu workspace bytes, got %zu", need, ws ? ws_bytes : 0);
+    Carver c(ws);
+    BwdWs w = carve_bwd(c, N, heads, nb, cap);
+    RoutedBwdWs r = carve_routed_bwd(c, heads, d, nb, cap);
     const bool bf16 = dt == PRISM_BF16;
     st = hip_status(prism::launch_bwd_dot(o, dout, bf16, N, heads, d, ld, hs, w.Dq, stream), "backward dot launch");
     if (st != PRISM_OK) return st;
+    // key block -> sharp query blocks (exact dK/dV) and -> flat query blocks (block-mean gradients)
     st = hip_status(prism::launch_transpose_csr(sel_offsets, sel_idx, nb, heads, cap, w.tcount, w.tr_offsets, w.tr_idx,
-                                                w.scratch, stream),
+                                                w.scratch, flat, 0, stream),
                     "transposed selection launch");
     if (st != PRISM_OK) return st;
-    if (use_simt_attention(dt))
-        return hip_status(prism::launch_attn_bwd_simt(q, k, v, dout, lse, w.Dq, dq, dk, dv, bf16, N, heads, d, ld, hs,
-                                                      block_offsets, nb, sel_offsets, sel_idx, w.tr_offsets, w.tr_idx,
-                                                      cap, scale, stream),
-                          "attention backward launch");
-    if (static_cast<int64_t>(N / 64) * heads > 0x7FFFFFFF)
-        return fail(PRISM_E_UNSUPPORTED, "too many tiles for one launch");
-    st = hip_status(prism::launch_tile_order(sel_offsets, sel_idx, cap, block_offsets, nb, heads, N / 64, w.obucket,
-                                             w.ostart, w.qorder, stream),
-                    "tile order launch");
+    st = hip_status(prism::launch_transpose_csr(sel_offsets, sel_idx, nb, heads, cap, w.tcount, r.fto, r.fti,
+                                                w.scratch, flat, 1, stream),
+                    "transposed selection launch");
     if (st != PRISM_OK) return st;
-    return hip_status(prism::launch_attn_bwd_mfma(q, k, v, dout, lse, w.Dq, dq, dk, dv, N, heads, d, ld, hs,
-                                                  block_offsets, nb, sel_offsets, sel_idx, w.tr_offsets, w.tr_idx, cap,
-                                                  w.qorder, scale, stream),
-                      "attention backward launch");
+    st = hip_status(prism::launch_block_means(k, v, bf16, heads, d, ld, hs, block_offsets, nb, r.kbar, r.vbar, stream),
+                    "block means launch");
+    if (st != PRISM_OK) return st;
+    st = hip_status(prism::launch_flat_dq(q, dout, r.kbar, r.vbar, lse, w.Dq, dq, bf16, N, heads, d, ld, hs,
+                                          block_offsets, nb, sel_offsets, sel_idx, cap, flat, scale, stream),
+                    "flat dQ launch");
+    if (st != PRISM_OK) return st;
+    st = hip_status(prism::launch_flat_kgrad(q, dout, r.kbar, r.vbar, lse, w.Dq, bf16, N, heads, d, ld, hs,
+                                             block_offsets, nb, r.fto, r.fti, cap, scale, r.dkbar, r.dvbar, stream),
+                    "flat key-block gradient launch");
+    if (st != PRISM_OK) return st;
+    const prism::RouteGrad rg{flat, r.dkbar, r.dvbar};
+    return exact_bwd(q, k, v, dout, lse, dq, dk, dv, dt, N, heads, d, ld, hs, block_offsets, nb, sel_offsets, sel_idx,
+                     cap, scale, w, &rg, stream);
 }
 
 }  // extern "C"

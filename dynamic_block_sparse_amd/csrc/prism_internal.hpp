@@ -27,9 +27,19 @@ hipError_t launch_select(const void* q, const void* k, bool bf16, int heads, int
                          int32_t* sel_idx, int64_t cap, int64_t* sel_total, float* logits, double* pooled,
                          int32_t* row_count, uint32_t* row_thr, int32_t* row_jlim, hipStream_t s);
 
+// rowmask (NULL: every query block) keeps query block i when
+// (rowmask[h*nb + i] != 0) == want
 hipError_t launch_transpose_csr(const int32_t* sel_offsets, const int32_t* sel_idx, int nb, int heads, int64_t cap,
                                 int32_t* tcount, int32_t* tr_offsets, int32_t* tr_idx, int32_t* scratch,
-                                hipStream_t s);
+                                const uint8_t* rowmask, int want, hipStream_t s);
+
+// Extras of the routed backward: dQ skips the tiles of flat query blocks, and
+// dK/dV add to every token of key block j the block-mean gradients / B_j.
+struct RouteGrad {
+    const uint8_t* skip_q;   // [heads, nb] or NULL
+    const float* dkbar;      // [heads, nb, d] or NULL (already scaled)
+    const float* dvbar;      // [heads, nb, d] or NULL
+};
 
 hipError_t launch_attn_fwd_simt(const void* q, const void* k, const void* v, void* o, float* lse, bool bf16, int64_t N,
                                 int heads, int d, int64_t ld, int64_t hs, const int32_t* offs, int nb,
@@ -48,13 +58,13 @@ hipError_t launch_attn_bwd_mfma(const void* q, const void* k, const void* v, con
                                 const float* Dq, void* dq, void* dk, void* dv, int64_t N, int heads, int d, int64_t ld,
                                 int64_t hs, const int32_t* offs, int nb, const int32_t* so, const int32_t* si,
                                 const int32_t* to, const int32_t* ti, int64_t cap, const int32_t* qorder,
-                                float scale, hipStream_t s);
+                                const RouteGrad* rg, float scale, hipStream_t s);
 
 hipError_t launch_attn_bwd_simt(const void* q, const void* k, const void* v, const void* dout, const float* lse,
                                 const float* Dq, void* dq, void* dk, void* dv, bool bf16, int64_t N, int heads, int d,
                                 int64_t ld, int64_t hs, const int32_t* offs, int nb, const int32_t* so,
-                                const int32_t* si, const int32_t* to, const int32_t* ti, int64_t cap, float scale,
-                                hipStream_t s);
+                                const int32_t* si, const int32_t* to, const int32_t* ti, int64_t cap,
+                                const RouteGrad* rg, float scale, hipStream_t s);
 
 // visiting order of the query tiles: within each unit (a head's part of one
 // XCD's range of the launch order), tile ids grouped by first selected block;
@@ -76,6 +86,14 @@ hipError_t launch_flat_route(const float* logits, int heads, int nb, int n_flat,
                              hipStream_t s);
 hipError_t launch_block_means(const void* k, const void* v, bool bf16, int heads, int d, int64_t ld, int64_t hs,
                               const int32_t* offs, int nb, float* kbar, float* vbar, hipStream_t s);
+hipError_t launch_flat_dq(const void* q, const void* dout, const float* kbar, const float* vbar, const float* lse,
+                          const float* Dq, void* dq, bool bf16, int64_t N, int heads, int d, int64_t ld, int64_t hs,
+                          const int32_t* offs, int nb, const int32_t* so, const int32_t* si, int64_t cap,
+                          const uint8_t* flat, float scale, hipStream_t s);
+hipError_t launch_flat_kgrad(const void* q, const void* dout, const float* kbar, const float* vbar, const float* lse,
+                             const float* Dq, bool bf16, int64_t N, int heads, int d, int64_t ld, int64_t hs,
+                             const int32_t* offs, int nb, const int32_t* fto, const int32_t* fti, int64_t cap,
+                             float scale, float* dkbar, float* dvbar, hipStream_t s);
 hipError_t launch_attn_flat(const void* q, const float* kbar, const float* vbar, void* o, float* lse, bool bf16,
                             int64_t N, int heads, int d, int64_t ld, int64_t hs, const int32_t* offs, int nb,
                             const int32_t* so, const int32_t* si, int64_t cap, const uint8_t* flat, float scale,

@@ -663,8 +663,9 @@ select_write_kernel(const float* __restrict__ logits, int nb, const uint32_t* __
 
 __global__ void __launch_bounds__(256)
 tr_count_kernel(const int32_t* __restrict__ sel_offsets, const int32_t* __restrict__ sel_idx, int nb, int64_t cap,
-                int32_t* __restrict__ tcount) {
+                const uint8_t* __restrict__ rowmask, int want, int32_t* __restrict__ tcount) {
     const int i = blockIdx.x, h = blockIdx.y;
+    if (rowmask && (rowmask[static_cast<int64_t>(h) * nb + i] != 0) != (want != 0)) return;
     const int32_t* __restrict__ so = sel_offsets + static_cast<int64_t>(h) * (nb + 1);
     const int32_t* __restrict__ si = sel_idx + static_cast<int64_t>(h) * cap;
     const int64_t e1 = min(static_cast<int64_t>(so[i + 1]), cap);   // a truncated list stops at cap
@@ -674,8 +675,10 @@ tr_count_kernel(const int32_t* __restrict__ sel_offsets, const int32_t* __restri
 
 __global__ void __launch_bounds__(256)
 tr_fill_kernel(const int32_t* __restrict__ sel_offsets, const int32_t* __restrict__ sel_idx, int nb, int64_t cap,
-               const int32_t* __restrict__ tr_offsets, int32_t* __restrict__ tcursor, int32_t* __restrict__ tr_idx) {
+               const uint8_t* __restrict__ rowmask, int want, const int32_t* __restrict__ tr_offsets,
+               int32_t* __restrict__ tcursor, int32_t* __restrict__ tr_idx) {
     const int i = blockIdx.x, h = blockIdx.y;
+    if (rowmask && (rowmask[static_cast<int64_t>(h) * nb + i] != 0) != (want != 0)) return;
     const int32_t* __restrict__ so = sel_offsets + static_cast<int64_t>(h) * (nb + 1);
     const int32_t* __restrict__ si = sel_idx + static_cast<int64_t>(h) * cap;
     const int32_t* __restrict__ to = tr_offsets + static_cast<int64_t>(h) * (nb + 1);
@@ -883,17 +886,18 @@ hipError_t fill_zero(int32_t* p, int64_t n, hipStream_t s) {
 
 hipError_t launch_transpose_csr(const int32_t* sel_offsets, const int32_t* sel_idx, int nb, int heads, int64_t cap,
                                 int32_t* tcount, int32_t* tr_offsets, int32_t* tr_idx, int32_t* scratch,
-                                hipStream_t s) {
+                                const uint8_t* rowmask, int want, hipStream_t s) {
     hipError_t e = fill_zero(tcount, static_cast<int64_t>(heads) * nb, s);
     if (e != hipSuccess) return e;
     const dim3 rg(nb, heads);
-    hipLaunchKernelGGL(tr_count_kernel, rg, dim3(256), 0, s, sel_offsets, sel_idx, nb, cap, tcount);
+    hipLaunchKernelGGL(tr_count_kernel, rg, dim3(256), 0, s, sel_offsets, sel_idx, nb, cap, rowmask, want, tcount);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(csr_scan_kernel, dim3(heads), dim3(1024), 0, s, tcount, nb, tr_offsets,
                        static_cast<int64_t*>(nullptr));
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if ((e = fill_zero(tcount, static_cast<int64_t>(heads) * nb, s)) != hipSuccess) return e;
-    hipLaunchKernelGGL(tr_fill_kernel, rg, dim3(256), 0, s, sel_offsets, sel_idx, nb, cap, tr_offsets, tcount, tr_idx);
+    hipLaunchKernelGGL(tr_fill_kernel, rg, dim3(256), 0, s, sel_offsets, sel_idx, nb, cap, rowmask, want, tr_offsets,
+                       tcount, tr_idx);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(tr_sort_kernel, rg, dim3(256), 0, s, tr_offsets, nb, cap, tr_idx, scratch);
     return hipGetLastError();

@@ -138,6 +138,18 @@ class PrismPath:
                                 self.nb, sel.offsets, sel.idx, sel.cap, flat, self.scale, ws)
         return op, lse
 
+    def routed_backward(self, qp, kp, vp, op, dop, lse, sel, flat, grads=None, h0=0):
+        hc = self.hc
+        if grads is None:
+            grads = tuple(self.block_major_like(qp) for _ in range(3))
+        dq, dk, dv = grads
+        ws = torch.empty(P.prism_workspace_size(P.OP_ROUTED_BWD, self.N, hc, self.d, self.nb, sel.cap),
+                         dtype=torch.uint8, device=self.device)
+        q, k, v, o, do, gq, gk, gv = (x[:, h0:h0 + hc] for x in (qp, kp, vp, op, dop, dq, dk, dv))
+        P.prism_routed_attn_bwd(q, k, v, o, do, lse, gq, gk, gv, self.N, hc, self.d, q.stride(0), q.stride(1),
+                                self.block_offsets, self.nb, sel.offsets, sel.idx, sel.cap, flat, self.scale, ws)
+        return dq, dk, dv
+
     def backward(self, qp, kp, vp, op, dop, lse, sel, grads=None, h0=0):
         hc = self.hc
         if grads is None:

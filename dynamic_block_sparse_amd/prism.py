@@ -20,13 +20,14 @@ if not os.path.exists(_LIB_PATH):
 _lib = C.CDLL(_LIB_PATH)
 
 PRISM_F32, PRISM_BF16 = 0, 1
-OP_ZONE_SHAPES, OP_SELECT, OP_ATTN_FWD, OP_ATTN_BWD, OP_NORM_MAP, OP_FLAT_ROUTE, OP_ROUTED_FWD = range(7)
+(OP_ZONE_SHAPES, OP_SELECT, OP_ATTN_FWD, OP_ATTN_BWD, OP_NORM_MAP, OP_FLAT_ROUTE, OP_ROUTED_FWD,
+ OP_ROUTED_BWD) = range(8)
 ZS_STRIDE = 16
 STATUS = {0: "PRISM_OK", 1: "PRISM_E_ARG", 2: "PRISM_E_GRID", 3: "PRISM_E_DTYPE",
           4: "PRISM_E_UNSUPPORTED", 5: "PRISM_E_WORKSPACE", 6: "PRISM_E_HIP"}
 
 EXPORTS = ["prism_audio_norm_map", "prism_zone_shapes", "prism_block_permute", "prism_block_permute_heads", "prism_select",
-           "prism_sparse_attn_fwd", "prism_flat_route", "prism_routed_attn_fwd",
+           "prism_sparse_attn_fwd", "prism_flat_route", "prism_routed_attn_fwd", "prism_routed_attn_bwd",
            "prism_sparse_attn_bwd", "prism_workspace_size", "prism_status_string", "prism_last_error",
            "prism_candidate_shapes"]
 
@@ -57,7 +58,9 @@ _lib.prism_audio_norm_map.argtypes = [_vp, _i32, _i64, _i64, _i64, _vp, _vp, _vp
 _lib.prism_flat_route.argtypes = [_vp, _i32, _i32, _f64, _vp, _vp, _vp, _sz, _vp]
 _lib.prism_routed_attn_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i64, _i64, _vp, _i32, _vp,
                                        _vp, _i64, _vp, _f32, _vp, _sz, _vp]
-for _f in ("prism_flat_route", "prism_routed_attn_fwd", "prism_audio_norm_map", "prism_zone_shapes", "prism_block_permute", "prism_block_permute_heads", "prism_select",
+_lib.prism_routed_attn_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i64,
+                                       _i64, _vp, _i32, _vp, _vp, _i64, _vp, _f32, _vp, _sz, _vp]
+for _f in ("prism_flat_route", "prism_routed_attn_fwd", "prism_routed_attn_bwd", "prism_audio_norm_map", "prism_zone_shapes", "prism_block_permute", "prism_block_permute_heads", "prism_select",
            "prism_sparse_attn_fwd", "prism_sparse_attn_bwd"):
     getattr(_lib, _f).restype = C.c_int
 _lib.prism_workspace_size.argtypes = [_i32, _i64, _i32, _i32, _i32, _i64]
@@ -184,6 +187,16 @@ def prism_routed_attn_fwd(q, k, v, o, lse, N, heads, d, ld, hs, block_offsets, n
                                     N, heads, d, ld, hs, _ptr(block_offsets), nb, _ptr(sel_offsets), _ptr(sel_idx),
                                     cap, _ptr(flat), float(scale), _ptr(ws),
                                     ws.numel() * ws.element_size() if ws is not None else 0, _stream(stream))
+    _check(st)
+
+
+def prism_routed_attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, N, heads, d, ld, hs, block_offsets, nb, sel_offsets,
+                          sel_idx, cap, flat, scale, ws, stream=None, dtype=None):
+    st = _lib.prism_routed_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk),
+                                    _ptr(dv), _dt(q) if dtype is None else dtype, N, heads, d, ld, hs,
+                                    _ptr(block_offsets), nb, _ptr(sel_offsets), _ptr(sel_idx), cap, _ptr(flat),
+                                    float(scale), _ptr(ws), ws.numel() * ws.element_size() if ws is not None else 0,
+                                    _stream(stream))
     _check(st)
 
 

@@ -73,7 +73,7 @@ typedef struct { double tau128, tau256, eps; } prism_shape_params;
 
 /* operation codes for prism_workspace_size */
 enum { PRISM_OP_ZONE_SHAPES = 0, PRISM_OP_SELECT = 1, PRISM_OP_ATTN_FWD = 2, PRISM_OP_ATTN_BWD = 3,
-       PRISM_OP_NORM_MAP = 4, PRISM_OP_FLAT_ROUTE = 5, PRISM_OP_ROUTED_FWD = 6 };
+       PRISM_OP_NORM_MAP = 4, PRISM_OP_FLAT_ROUTE = 5, PRISM_OP_ROUTED_FWD = 6, PRISM_OP_ROUTED_BWD = 7 };
 
 /* Per-zone record written by prism_zone_shapes when `zone_stats` is not NULL:
  * 16 doubles per zone. */
@@ -306,6 +306,26 @@ prism_status prism_routed_attn_fwd(const void* q, const void* k, const void* v, 
                                    const int32_t* block_offsets, int32_t nb, const int32_t* sel_offsets,
                                    const int32_t* sel_idx, int64_t cap, const uint8_t* flat, float scale, void* ws,
                                    size_t ws_bytes, hipStream_t stream);
+
+/*
+ * prism_routed_attn_bwd - gradient of prism_routed_attn_fwd, the selection
+ * and the routing held constant.  Sharp query blocks contribute exactly as in
+ * prism_sparse_attn_bwd.  A flat query row q with weights w_j, D_q =
+ * rowsum(dO * O) and dS_j = w_j (dO_q . V_bar_j - D_q) contributes
+ *     dq = scale sum_j dS_j K_bar_j,
+ *     dK_bar_j += scale dS_j q,   dV_bar_j += w_j dO_q,
+ * and every token of key block j receives dK_bar_j / B_j and dV_bar_j / B_j
+ * (the chain rule through the block means; the article gives no backward).
+ * Arguments as prism_sparse_attn_bwd plus `flat`; workspace
+ * prism_workspace_size(PRISM_OP_ROUTED_BWD, ...) bytes.  Deterministic: the
+ * block-mean gradients are summed per key block in a fixed order and added to
+ * the exact dK/dV before rounding.
+ */
+prism_status prism_routed_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                                   const float* lse, void* dq, void* dk, void* dv, prism_dtype dt, int64_t N,
+                                   int32_t heads, int32_t d, int64_t ld, int64_t hs, const int32_t* block_offsets,
+                                   int32_t nb, const int32_t* sel_offsets, const int32_t* sel_idx, int64_t cap,
+                                   const uint8_t* flat, float scale, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Workspace bytes for one call.  ZONE_SHAPES: N = T*H*W and d = C (heads, nb,
  * cap ignored).  SELECT, ATTN_FWD, ATTN_BWD: the call's N, heads, d, nb, cap. */

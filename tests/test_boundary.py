@@ -234,3 +234,17 @@ def test_flat_route_and_routed_forward_reject():
     assert f(fl=None) == 1
     assert f(ws=None) == 5
     assert f(wsb=fneed - 16) == 5
+
+
+def test_routed_backward_rejects():
+    lib, P = _lib()
+    N, heads, d, nb = 2048, 2, 128, 24
+    cap = nb * nb
+    need = P.prism_workspace_size(P.OP_ROUTED_BWD, N, heads, d, nb, cap)
+    assert need > P.prism_workspace_size(P.OP_ATTN_BWD, N, heads, d, nb, cap) + 4 * 4 * heads * nb * d - 1
+    f = lambda fl=B, ws=A, wsb=need, dq=A: lib.prism_routed_attn_bwd(A, B, Cc, A, B, Cc, dq, B, Cc, 1, N, heads, d, 256,
+                                                                     128, A, nb, B, Cc, cap, fl, 0.088, ws, wsb, None)
+    assert f(dq=None) == 1
+    assert f(fl=None) == 1
+    assert f(ws=None) == 5
+    assert f(wsb=need - 16) == 5

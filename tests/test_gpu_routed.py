@@ -41,7 +41,19 @@ def _path(cfg, heads=None, hc=None):
                      float(np.float32(1.0 / math.sqrt(cfg.d))), head_chunk=hc)
 
 
-def _check_head(h, hh, path, sel, flat_g, M_g, op, lse, xs, zs, pi, cfg, ratio, blocks, v_att=None):
+GRAD_TOL = {"bf16": (2e-2, 2e-3), "f32": (1e-4, 1e-4)}
+
+
+def _close_grad(got, want, dtype, what):
+    mx, mean = GRAD_TOL[dtype]
+    mx *= max(1.0, float(np.abs(want).max()))
+    mean *= max(1.0, float(np.abs(want).mean()))
+    err = np.abs(got - want)
+    print(f"{what}: max-abs {err.max():.3e} (bar {mx:.2e}) mean-abs {err.mean():.3e}", flush=True)
+    assert err.max() <= mx and err.mean() <= mean, what
+
+
+def _check_head(h, hh, path, sel, flat_g, M_g, op, lse, xs, zs, pi, cfg, ratio, blocks, v_att=None, dq=None):
     """Oracle chain for head h (global index into the input tensors), compared
     on `blocks` (None: every block).  hh indexes the GPU head chunk."""
     offs, nb = zs["block_offsets"], zs["NB"]
@@ -69,6 +81,8 @@ def _check_head(h, hh, path, sel, flat_g, M_g, op, lse, xs, zs, pi, cfg, ratio, 
     Og = _np(op[:, hh, :])
     lg = lse[hh].cpu().numpy()
     errs = {"flat": [], "sharp": []}
+    derrs = {"flat dQ": [], "sharp dQ": []}
+    dOp = orc.to_block_major(_np(xs["do"][:, h:h + 1, :]), pi) if dq is not None else None
     for i in (range(nb) if blocks is None else blocks):
         if flags[i] or fg[i] != flat[i]:
             continue
@@ -77,6 +91,15 @@ def _check_head(h, hh, path, sel, flat_g, M_g, op, lse, xs, zs, pi, cfg, ratio, 
         o_ref, l_ref = fn(Qp, Kp, Vp, offs, s, i, 0, sc)
         errs["flat" if flat[i] else "sharp"].append((Og[offs[i]:offs[i + 1]], o_ref))
         np.testing.assert_allclose(lg[offs[i]:offs[i + 1]], l_ref, atol=1e-4 if cfg.dtype == "f32" else 2e-3)
+        if dq is not None:
+            dq_ref = (orc.taylor_attn_bwd_block if flat[i] else orc.attn_bwd_block)(Qp, Kp, Vp, dOp, offs, s, i, 0,
+                                                                                    sc)[0]
+            derrs["flat dQ" if flat[i] else "sharp dQ"].append((_np(dq[offs[i]:offs[i + 1], hh, :]), dq_ref))
+    for kind, pairs in derrs.items():
+        if pairs:
+            got = np.concatenate([p_[0] for p_ in pairs])
+            want = np.concatenate([p_[1] for p_ in pairs])
+            _close_grad(got, want, cfg.dtype, f"head {h} {kind} ({len(pairs)} blocks)")
     mx, mean = TOL[cfg.dtype]
     for kind, pairs in errs.items():
         if not pairs:
@@ -135,7 +158,7 @@ def test_routed_forward_2k_size(progress):
     heads = sorted(rng.choice(cfg.heads, size=2, replace=False).tolist())
     progress(f"routed 2k: heads {heads}, generating")
     x = make_inputs(cfg, device="cuda", tensors=("v",))
-    xs = make_inputs(cfg, device="cuda", heads=heads, tensors=("q", "k"))
+    xs = make_inputs(cfg, device="cuda", heads=heads, tensors=("q", "k", "do"))
     path = _path(cfg, heads=2)
     path.shapes(x["v"], x["a"])
     v_att = x["v"][:, heads]
@@ -144,14 +167,68 @@ def test_routed_forward_2k_size(progress):
     flat, M = path.route(sel, 0.5, want_sharpness=True)
     op = path.block_major_like(qp).fill_(float("nan"))
     _, lse = path.routed_forward(qp, kp, vp, sel, flat, op=op)
+    dop = path.permute(xs["do"])
+    grads = tuple(path.block_major_like(qp).fill_(float("nan")) for _ in range(3))
+    path.routed_backward(qp, kp, vp, op, dop, lse, sel, flat, grads=grads)
     torch.cuda.synchronize()
     assert bool(torch.isfinite(op).all())
+    for g in grads:
+        assert bool(torch.isfinite(g).all())
     progress("routed 2k: oracle zone statistics")
     zs = orc.zone_shapes(_np(x["v"]).reshape(cfg.N, -1), _np(x["a"]), cfg.T, cfg.H, cfg.W)
     assert zs["NB"] == path.nb
     pi = orc.permutation(cfg.T, cfg.H, cfg.W, zs["shape"])
     blocks = sorted(rng.choice(zs["NB"], size=48, replace=False).tolist())
-    xs_full = {"q": xs["q"], "k": xs["k"], "v": v_att}
+    xs_full = {"q": xs["q"], "k": xs["k"], "v": v_att, "do": xs["do"]}
     for hh, h in enumerate(heads):
         progress(f"routed 2k: head {h}")
-        _check_head(hh, hh, path, sel, flat, M, op, lse, xs_full, zs, pi, cfg, 0.5, blocks)
+        _check_head(hh, hh, path, sel, flat, M, op, lse, xs_full, zs, pi, cfg, 0.5, blocks, dq=grads[0])
+
+
+@pytest.mark.parametrize("cfg", CASES, ids=lambda c: c.name)
+@pytest.mark.parametrize("ratio", [0.5, 1.0])
+def test_routed_backward_small(cfg, ratio):
+    x = make_inputs(cfg, device="cuda")
+    path = _path(cfg)
+    path.shapes(x["v"], x["a"])
+    qp, kp, vp, dop = (path.permute(x[n]) for n in ("q", "k", "v", "do"))
+    sel = path.select(qp, kp, want_logits=True)
+    flat = path.route(sel, ratio)
+    op, lse = path.routed_forward(qp, kp, vp, sel, flat)
+    grads = tuple(path.block_major_like(qp).fill_(float("nan")) for _ in range(3))
+    path.routed_backward(qp, kp, vp, op, dop, lse, sel, flat, grads=grads)
+    torch.cuda.synchronize()
+    for g in grads:
+        assert bool(torch.isfinite(g).all())
+    zs = orc.zone_shapes(_np(x["v"]).reshape(cfg.N, -1), _np(x["a"]), cfg.T, cfg.H, cfg.W)
+    pi = orc.permutation(cfg.T, cfg.H, cfg.W, zs["shape"])
+    offs = zs["block_offsets"]
+    sc = float(np.float32(1.0 / math.sqrt(cfg.d)))
+    for h in range(cfg.heads):
+        Qp, Kp, Vp, dOp = (orc.to_block_major(_np(x[n][:, h:h + 1, :]), pi) for n in ("q", "k", "v", "do"))
+        L = orc.block_logits(orc.pool_blocks(Qp, offs, 0), orc.pool_blocks(Kp, offs, 0), sc)
+        assert not (sel.logits[h].cpu().numpy() != L).any()
+        co, ci, flags = orc.select(L, cfg.top_k, cfg.top_p)
+        assert not flags.any()
+        fl = orc.flat_route(orc.block_sharpness(L), ratio)
+        np.testing.assert_array_equal(flat[h].cpu().numpy().astype(bool), fl)
+        # the oracle's D uses its float64 O, the GPU's the bf16 O of its forward (within the gradient bar)
+        ref = orc.routed_attention(Qp, Kp, Vp, offs, co, ci, fl, 0, sc, dOp=dOp)
+        for name, g in (("dQ", grads[0]), ("dK", grads[1]), ("dV", grads[2])):
+            _close_grad(_np(g[:, h, :]), ref[name], cfg.dtype, f"{cfg.name} r={ratio} head {h} {name}")
+
+
+def test_routed_backward_with_no_flat_block_is_the_exact_backward():
+    cfg = CASES[0]
+    x = make_inputs(cfg, device="cuda")
+    path = _path(cfg)
+    path.shapes(x["v"], x["a"])
+    qp, kp, vp, dop = (path.permute(x[n]) for n in ("q", "k", "v", "do"))
+    sel = path.select(qp, kp, want_logits=True)
+    flat = path.route(sel, 0.0)
+    op, lse = path.forward(qp, kp, vp, sel)
+    g1 = path.routed_backward(qp, kp, vp, op, dop, lse, sel, flat)
+    g2 = path.backward(qp, kp, vp, op, dop, lse, sel)
+    torch.cuda.synchronize()
+    for a, b in zip(g1, g2):
+        assert torch.equal(a, b)
