@@ -29,6 +29,8 @@ Parity status per function:
     audio_norm_map (the norm; its normalisation is a reading), candidate_shapes, axis_profiles, video_variance, audio_terms (as read),
     indicator, volume, optimum_log2, nearest_shape, block layout, permutation,
     pool_blocks, block_logits, select_row, attention forward and backward.
+    next row f4: hilbert_zone_order (adjacency of consecutive zones on 2^k
+    cubes, a permutation, restriction of the enclosing cube's order).
     next row f3: block_sharpness, flat_route, taylor_attn_fwd_block,
     taylor_attn_bwd_block and routed_attention (each pinned
     to closed forms of its reading: uniform and one-hot rows, brute-force
@@ -275,16 +277,61 @@ def zone_shapes(V, a, T, H, W, tau128=TAU128, tau256=TAU256, eps=EPS):
 # each; inside a zone its blocks in raster order over the block grid; inside a
 # block its tokens in raster (t, h, w) order.
 
-def block_layout(shape_idx):
-    """block_offsets[NB+1] (token offsets of each block in block-major order) and NB."""
+def block_layout(shape_idx, zone_order=None):
+    """block_offsets[NB+1] (token offsets of each block in block-major order) and NB.
+    zone_order[pos] = the raster zone at position pos (None: raster order)."""
     cands = candidate_shapes()
+    order = range(len(shape_idx)) if zone_order is None else zone_order
     offs = [0]
-    for m, c in enumerate(shape_idx):
-        bt, bh, bw = cands[int(c)]
+    for pos, m in enumerate(order):
+        bt, bh, bw = cands[int(shape_idx[int(m)])]
         vol = bt * bh * bw
         for j in range(ZONE ** 3 // vol):
-            offs.append(ZONE ** 3 * m + (j + 1) * vol)
+            offs.append(ZONE ** 3 * pos + (j + 1) * vol)
     return np.asarray(offs, dtype=np.int64), len(offs) - 1
+
+
+def hilbert_zone_order(T, H, W):
+    """Next row f4 (DFSAttn article, Hilbert-curve reordering, applied to zones):
+    the zones sorted by their index along a 3D Hilbert curve.  Reading: the
+    curve of J. Skilling's transform ("Programming the Hilbert curve", 2004)
+    over the smallest 2^k cube holding the zone grid, axes (t, h, w) with t the
+    most significant, zones outside the grid skipped.  Returns order[pos] =
+    raster zone index."""
+    nT, nH, nW = zone_grid(T, H, W)
+    bits = max(1, int(math.ceil(math.log2(max(nT, nH, nW)))))
+
+    def index(x):
+        x = list(x)
+        top = 1 << (bits - 1)
+        q = top
+        while q > 1:                       # undo the excess work (inverse rotations)
+            low = q - 1
+            for i in range(3):
+                if x[i] & q:
+                    x[0] ^= low
+                else:
+                    swap = (x[0] ^ x[i]) & low
+                    x[0] ^= swap
+                    x[i] ^= swap
+            q >>= 1
+        for i in (1, 2):                   # Gray encode
+            x[i] ^= x[i - 1]
+        flip, q = 0, top
+        while q > 1:
+            if x[2] & q:
+                flip ^= q - 1
+            q >>= 1
+        x = [v ^ flip for v in x]
+        h = 0
+        for bit in range(bits - 1, -1, -1):   # interleave: t, h, w per level
+            for i in range(3):
+                h = (h << 1) | ((x[i] >> bit) & 1)
+        return h
+
+    zones = [(zt, zh, zw) for zt in range(nT) for zh in range(nH) for zw in range(nW)]
+    keys = [index(z) for z in zones]
+    return np.asarray(sorted(range(len(zones)), key=lambda m: keys[m]), dtype=np.int64)
 
 
 def _zone_local_order(shape):
@@ -303,20 +350,24 @@ def _zone_local_order(shape):
     return np.array(it), np.array(ih), np.array(iw)
 
 
-def permutation(T, H, W, shape_idx):
-    """pi[p] = raster index of the token at block-major position p."""
+def permutation(T, H, W, shape_idx, zone_order=None):
+    """pi[p] = raster index of the token at block-major position p; zone_order
+    as in block_layout (None: raster order)."""
     nT, nH, nW = zone_grid(T, H, W)
     cands = candidate_shapes()
     local = [_zone_local_order(s) for s in cands]
     pi = np.empty(T * H * W, dtype=np.int64)
-    for m, c in enumerate(shape_idx):
+    order = range(len(shape_idx)) if zone_order is None else zone_order
+    for pos, m in enumerate(order):
+        m = int(m)
+        c = shape_idx[m]
         zt, rem = divmod(m, nH * nW)
         zh, zw = divmod(rem, nW)
         it, ih, iw = local[int(c)]
         t = ZONE * zt + it
         h = ZONE * zh + ih
         w = ZONE * zw + iw
-        pi[ZONE ** 3 * m:ZONE ** 3 * (m + 1)] = (t * H + h) * W + w
+        pi[ZONE ** 3 * pos:ZONE ** 3 * (pos + 1)] = (t * H + h) * W + w
     return pi
 
 

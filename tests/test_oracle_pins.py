@@ -730,3 +730,42 @@ def test_routed_attention_gradients_by_finite_differences():
             ap[sub], am[sub] = Xp, Xm
             fd = (loss(*ap) - loss(*am)) / (2 * h)
             assert math.isclose(G[t, c], fd, rel_tol=1e-5, abs_tol=1e-8), (name, t, c, G[t, c], fd)
+
+
+# ---------------------------------------------------------------- next row f4: Hilbert zone order
+
+@pytest.mark.parametrize("n", [1, 2, 4, 8])
+def test_hilbert_order_walks_face_adjacent_zones_on_cubes(n):
+    T = H = W = 8 * n
+    order = orc.hilbert_zone_order(T, H, W)
+    assert sorted(order.tolist()) == list(range(n ** 3))
+    coords = [np.array(np.unravel_index(m, (n, n, n))) for m in order]
+    assert (coords[0] == 0).all()                                 # starts at the origin
+    for a, b in zip(coords, coords[1:]):
+        assert int(np.abs(a - b).sum()) == 1                      # one step along one axis
+
+
+def test_hilbert_order_on_other_grids_is_the_cube_order_restricted():
+    T, H, W = 8 * 3, 8 * 5, 8 * 2
+    order = orc.hilbert_zone_order(T, H, W)
+    assert sorted(order.tolist()) == list(range(3 * 5 * 2))
+    cube = orc.hilbert_zone_order(64, 64, 64)                     # 8 x 8 x 8 zones
+    inside = [np.unravel_index(m, (8, 8, 8)) for m in cube]
+    want = [(t * 5 + h) * 2 + w for t, h, w in inside if t < 3 and h < 5 and w < 2]
+    assert order.tolist() == want
+
+
+def test_layout_and_permutation_follow_the_zone_order():
+    T, H, W = 16, 24, 16
+    rng = np.random.default_rng(3)
+    shape = rng.integers(0, 16, size=2 * 3 * 2)
+    order = orc.hilbert_zone_order(T, H, W)
+    offs, nb = orc.block_layout(shape, order)
+    offs_r, nb_r = orc.block_layout(shape)
+    assert nb == nb_r and offs[-1] == T * H * W
+    assert (orc.block_layout(shape, np.arange(len(shape)))[0] == offs_r).all()
+    pi = orc.permutation(T, H, W, shape, order)
+    pi_r = orc.permutation(T, H, W, shape)
+    assert sorted(pi.tolist()) == list(range(T * H * W))
+    for pos, m in enumerate(order):                               # each zone's 512 tokens move as a unit
+        assert (pi[512 * pos:512 * (pos + 1)] == pi_r[512 * m:512 * (m + 1)]).all()
