@@ -386,6 +386,55 @@ def measure_routed(path, qp, kp, vp, ratio, dop=None, reps=3):
             "forward_speedup": round(exact_ms / (routed_ms + route_ms), 3), **bwd}
 
 
+def measure_zone_order(cfg, x, path, qp, kp, vp, dop=None, reps=3):
+    """The Hilbert zone order against raster order on the same inputs: block
+    layout, permutation of Q, K, V (and dO), selection, forward and backward of
+    the first head group, timed with HIP events outside the step.  Both orders
+    select the same work (same blocks, renumbered), so the effective FLOPs are
+    reported for each as a check."""
+    from dynamic_block_sparse_amd.path import PrismPath
+    print("[bench] hilbert zone order", file=sys.stderr, flush=True)
+    hp = PrismPath(cfg.T, cfg.H, cfg.W, cfg.heads, cfg.d, cfg.top_k, cfg.top_p, path.scale, head_chunk=path.hc,
+                   zone_order="hilbert")
+    hp.shapes(x["v"], x["a"])
+    names = ("q", "k", "v") + (("do",) if dop is not None else ())
+    hb = {n: hp.permute(x[n]) for n in names}
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    res = {}
+    for tag, p, t in (("raster", path, {"q": qp, "k": kp, "v": vp, "do": dop}), ("hilbert", hp, hb)):
+        sel = p.select(t["q"], t["k"], 0)
+        op, lse = p.forward(t["q"], t["k"], t["v"], sel)
+        r = {"permute_ms": round(timed(lambda: p.permute(x["q"], out=t["q"])), 3),
+             "select_ms": round(timed(lambda: p.select(t["q"], t["k"], 0)), 3),
+             "forward_ms": round(timed(lambda: p.forward(t["q"], t["k"], t["v"], sel, op=op, lse=lse)), 3)}
+        f_fwd, f_bwd, mean_sel = effective_flops(p, [sel], cfg.d)
+        if dop is not None:
+            grads = tuple(p.block_major_like(t["q"]) for _ in range(3))
+            r["backward_ms"] = round(timed(lambda: p.backward(t["q"], t["k"], t["v"], op, t["do"], lse, sel,
+                                                              grads=grads)), 3)
+            del grads
+        r["effective_tflop"] = round((f_fwd + (f_bwd if dop is not None else 0.0)) / 1e12, 6)
+        r["mean_selected_blocks"] = round(mean_sel, 3)
+        res[tag] = r
+        del sel, op, lse
+    del hb
+    att = lambda r: r["forward_ms"] + r.get("backward_ms", 0.0)
+    res["heads"] = path.hc
+    res["attention_speedup"] = round(att(res["raster"]) / att(res["hilbert"]), 3)
+    return res
+
+
 def main():
     args = parse()
     if args.profile:
@@ -532,7 +581,8 @@ def main():
     }
     if not args.no_next_rows:
         result["next_rows"] = {"f1_audio_norm_map": measure_norm_map(cfg),
-                               "f3_routed_forward": measure_routed(path, qp, kp, vp, args.flat_ratio, dop)}
+                               "f3_routed_forward": measure_routed(path, qp, kp, vp, args.flat_ratio, dop),
+                               "f4_hilbert_zone_order": measure_zone_order(cfg, x, path, qp, kp, vp, dop)}
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(cfg, x, path.zone_shape.cpu().numpy(), args.cpu_seconds)

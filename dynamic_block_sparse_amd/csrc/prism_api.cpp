@@ -11,6 +11,8 @@
 #include <cstdlib>
 #include <cstring>
 #include <string>
+#include <utility>
+#include <vector>
 
 #include "prism.h"
 #include "prism_device.hpp"
@@ -174,14 +176,46 @@ prism_status check_tokens(prism_dtype dt, int64_t N, int32_t heads, int32_t d, i
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
-prism::ZoneGrid grid_of(int32_t T, int32_t H, int32_t W) {
+prism::ZoneGrid grid_of(int32_t T, int32_t H, int32_t W, const int32_t* zone_order = nullptr) {
     prism::ZoneGrid g;
     g.T = T;
     g.H = H;
     g.W = W;
     g.nH = H / 8;
     g.nW = W / 8;
+    g.order = zone_order;
     return g;
+}
+
+// Index of cell x (3 axes, `bits` bits each) along the 3D Hilbert curve of
+// J. Skilling's transform ("Programming the Hilbert curve", AIP Conf. Proc.
+// 707, 2004): undo the per-level rotations and reflections, Gray-code the
+// axes, then interleave their bits from the top level down, axis 0 first.
+uint64_t hilbert_index3(uint32_t x0, uint32_t x1, uint32_t x2, int bits) {
+    uint32_t x[3] = {x0, x1, x2};
+    const uint32_t top = 1u << (bits - 1);
+    for (uint32_t q = top; q > 1; q >>= 1) {
+        const uint32_t low = q - 1;
+        for (int i = 0; i < 3; ++i) {
+            if (x[i] & q) {
+                x[0] ^= low;
+            } else {
+                const uint32_t sw = (x[0] ^ x[i]) & low;
+                x[0] ^= sw;
+                x[i] ^= sw;
+            }
+        }
+    }
+    x[1] ^= x[0];
+    x[2] ^= x[1];
+    uint32_t flip = 0;
+    for (uint32_t q = top; q > 1; q >>= 1)
+        if (x[2] & q) flip ^= q - 1;
+    for (int i = 0; i < 3; ++i) x[i] ^= flip;
+    uint64_t h = 0;
+    for (int b = bits - 1; b >= 0; --b)
+        for (int i = 0; i < 3; ++i) h = (h << 1) | ((x[i] >> b) & 1u);
+    return h;
 }
 
 }  // namespace
@@ -202,6 +236,26 @@ const char* prism_status_string(prism_status s) {
 }
 
 const char* prism_last_error(void) { return g_last_error.c_str(); }
+
+prism_status prism_hilbert_zone_order(int32_t T, int32_t H, int32_t W, int32_t* order) {
+    prism_status st = check_grid(T, H, W);
+    if (st != PRISM_OK) return st;
+    if (!order) return fail(PRISM_E_ARG, "null pointer argument");
+    const int nT = T / 8, nH = H / 8, nW = W / 8;
+    int bits = 1;
+    while ((1 << bits) < std::max(nT, std::max(nH, nW))) ++bits;
+    if (bits > 21) return fail(PRISM_E_UNSUPPORTED, "zone grid too large for a 63-bit Hilbert index");
+    const int64_t nZ = static_cast<int64_t>(nT) * nH * nW;
+    std::vector<std::pair<uint64_t, int32_t>> keyed(static_cast<size_t>(nZ));
+    for (int64_t m = 0; m < nZ; ++m) {
+        const int zt = static_cast<int>(m / (static_cast<int64_t>(nH) * nW));
+        const int zh = static_cast<int>((m / nW) % nH), zw = static_cast<int>(m % nW);
+        keyed[static_cast<size_t>(m)] = {hilbert_index3(zt, zh, zw, bits), static_cast<int32_t>(m)};
+    }
+    std::sort(keyed.begin(), keyed.end());
+    for (int64_t pos = 0; pos < nZ; ++pos) order[pos] = keyed[static_cast<size_t>(pos)].second;
+    return PRISM_OK;
+}
 
 void prism_candidate_shapes(int32_t out[16][3]) {
     for (int i = 0; i < 16; ++i) {
@@ -274,7 +328,7 @@ prism_status prism_audio_norm_map(const void* h, prism_dtype dt, int64_t N, int6
 prism_status prism_zone_shapes(int32_t T, int32_t H, int32_t W, const void* v, prism_dtype vdt, int64_t C,
                                int64_t v_ld, const float* a_map, const prism_shape_params* prm, uint8_t* zone_shape,
                                int32_t* block_offsets, int32_t* nb_dev, int32_t* nb_host, double* zone_stats, void* ws,
-                               size_t ws_bytes, hipStream_t stream) {
+                               size_t ws_bytes, const int32_t* zone_order, hipStream_t stream) {
     prism_status st = check_grid(T, H, W);
     if (st != PRISM_OK) return st;
     if (vdt != PRISM_F32 && vdt != PRISM_BF16) return fail(PRISM_E_DTYPE, "unknown dtype %d", static_cast<int>(vdt));
@@ -293,7 +347,7 @@ prism_status prism_zone_shapes(int32_t T, int32_t H, int32_t W, const void* v, p
     const int nZ = static_cast<int>(N / prism::kZoneTokens);
     double* partial = c.take<double>(prism::zone_partial_doubles(nZ, C));
     double* rec = c.take<double>(static_cast<size_t>(nZ) * PRISM_ZS_STRIDE);
-    st = hip_status(prism::launch_zone_shapes(v, vdt == PRISM_BF16, C, v_ld, a_map, grid_of(T, H, W), nZ, p.tau128,
+    st = hip_status(prism::launch_zone_shapes(v, vdt == PRISM_BF16, C, v_ld, a_map, grid_of(T, H, W, zone_order), nZ, p.tau128,
                                               p.tau256, p.eps, zone_shape, block_offsets, nb_dev, partial, rec, stream),
                     "zone_shapes launch");
     if (st != PRISM_OK) return st;
@@ -313,7 +367,7 @@ prism_status prism_zone_shapes(int32_t T, int32_t H, int32_t W, const void* v, p
 
 prism_status prism_block_permute(int32_t T, int32_t H, int32_t W, const uint8_t* zone_shape, const void* x, void* y,
                                  prism_dtype dt, int64_t row_elems, int64_t x_ld, int64_t y_ld, int32_t inverse,
-                                 hipStream_t stream) {
+                                 const int32_t* zone_order, hipStream_t stream) {
     prism_status st = check_grid(T, H, W);
     if (st != PRISM_OK) return st;
     if (dt != PRISM_F32 && dt != PRISM_BF16) return fail(PRISM_E_DTYPE, "unknown dtype %d", static_cast<int>(dt));
@@ -327,14 +381,15 @@ prism_status prism_block_permute(int32_t T, int32_t H, int32_t W, const uint8_t*
     const char* yb = static_cast<const char*>(y);
     const int64_t xspan = ((N - 1) * x_ld + row_elems) * eb, yspan = ((N - 1) * y_ld + row_elems) * eb;
     if (xb < yb + yspan && yb < xb + xspan) return fail(PRISM_E_ARG, "x and y overlap");
-    return hip_status(prism::launch_block_permute(x, y, eb, row_elems, x_ld, y_ld, zone_shape, grid_of(T, H, W), N,
+    return hip_status(prism::launch_block_permute(x, y, eb, row_elems, x_ld, y_ld, zone_shape, grid_of(T, H, W, zone_order), N,
                                                   inverse, stream),
                       "block_permute launch");
 }
 
 prism_status prism_block_permute_heads(int32_t T, int32_t H, int32_t W, const uint8_t* zone_shape, const void* x,
                                        void* y, prism_dtype dt, int32_t heads, int32_t d, int64_t x_ld, int64_t x_hs,
-                                       int64_t y_ld, int64_t y_hs, int32_t inverse, hipStream_t stream) {
+                                       int64_t y_ld, int64_t y_hs, int32_t inverse, const int32_t* zone_order,
+                                       hipStream_t stream) {
     prism_status st = check_grid(T, H, W);
     if (st != PRISM_OK) return st;
     if (dt != PRISM_F32 && dt != PRISM_BF16) return fail(PRISM_E_DTYPE, "unknown dtype %d", static_cast<int>(dt));
@@ -354,7 +409,7 @@ prism_status prism_block_permute_heads(int32_t T, int32_t H, int32_t W, const ui
     const int64_t yspan = ((N - 1) * y_ld + (heads - 1) * y_hs + d) * eb;
     if (xb < yb + yspan && yb < xb + xspan) return fail(PRISM_E_ARG, "x and y overlap");
     return hip_status(prism::launch_block_permute_heads(x, y, eb, heads, d, x_ld, x_hs, y_ld, y_hs, zone_shape,
-                                                        grid_of(T, H, W), N, inverse, stream),
+                                                        grid_of(T, H, W, zone_order), N, inverse, stream),
                       "block_permute_heads launch");
 }
 

@@ -93,10 +93,11 @@ __device__ __forceinline__ T block_max(T v, T* scratch) {
 // Map block-major position p to its raster token index for the zone shapes.
 struct ZoneGrid {
     int T, H, W, nH, nW;
+    const int32_t* order;   // order[pos] = raster zone at block-major zone position pos (NULL: raster)
 };
 __device__ __forceinline__ int64_t block_major_to_raster(int64_t p, const uint8_t* __restrict__ zone_shape,
                                                          const ZoneGrid g) {
-    const int64_t m = p >> 9;
+    const int64_t m = g.order ? static_cast<int64_t>(g.order[p >> 9]) : (p >> 9);
     const int q = static_cast<int>(p & 511);
     int bt, bh, bw;
     shape_of(zone_shape[m], bt, bh, bw);

@@ -22,7 +22,8 @@
 //                        of the norm map.
 //   zone_decide_kernel   one workgroup for the grid: global maximum of S_v,
 //                        density, volume, indicator, optimum, nearest shape,
-//                        then a scan over zones for the block offsets.
+//                        then a scan over zones, in their block-major order,
+//                        for the block offsets.
 #include "prism_device.hpp"
 #include "prism_internal.hpp"
 
@@ -336,7 +337,8 @@ zone_reduce_kernel(const double* __restrict__ partial, int nslab, int64_t C, con
 
 __global__ void __launch_bounds__(1024)
 zone_decide_kernel(double* __restrict__ rec, int nZ, double tau128, double tau256, double eps,
-                   uint8_t* __restrict__ zone_shape, int32_t* __restrict__ block_offsets, int32_t* __restrict__ nb_dev) {
+                   const int32_t* __restrict__ order, uint8_t* __restrict__ zone_shape,
+                   int32_t* __restrict__ block_offsets, int32_t* __restrict__ nb_dev) {
     __shared__ double redd[16];
     __shared__ int32_t scan[1024];
     __shared__ int32_t carry;
@@ -351,7 +353,6 @@ zone_decide_kernel(double* __restrict__ rec, int nZ, double tau128, double tau25
     __syncthreads();
     for (int base = 0; base < nZ; base += blockDim.x) {
         const int m = base + threadIdx.x;
-        int nblk = 0;
         if (m < nZ) {
             double* r = rec + static_cast<int64_t>(m) * 16;
             const double abar = r[6];
@@ -383,9 +384,15 @@ zone_decide_kernel(double* __restrict__ rec, int nZ, double tau128, double tau25
             zone_shape[m] = static_cast<uint8_t>(pick);
             r[13] = rho;
             r[15] = static_cast<double>(B);
-            nblk = kZoneTokens / B;
         }
-        // inclusive scan of block counts over this chunk of zones
+    }
+    __syncthreads();   // every zone's volume is in rec[15]
+    // block offsets: an inclusive scan of block counts over the zones in their
+    // block-major order (order[pos], or raster when order is NULL)
+    for (int base = 0; base < nZ; base += blockDim.x) {
+        const int pos = base + threadIdx.x;
+        const int m = pos < nZ ? (order ? order[pos] : pos) : 0;
+        const int nblk = pos < nZ ? kZoneTokens / static_cast<int>(rec[static_cast<int64_t>(m) * 16 + 15]) : 0;
         scan[threadIdx.x] = nblk;
         __syncthreads();
         for (int off = 1; off < static_cast<int>(blockDim.x); off <<= 1) {
@@ -395,9 +402,9 @@ zone_decide_kernel(double* __restrict__ rec, int nZ, double tau128, double tau25
             __syncthreads();
         }
         const int first = carry + scan[threadIdx.x] - nblk;
-        if (m < nZ) {
+        if (pos < nZ) {
             const int B = kZoneTokens / nblk;
-            for (int j = 0; j < nblk; ++j) block_offsets[first + j] = m * kZoneTokens + j * B;
+            for (int j = 0; j < nblk; ++j) block_offsets[first + j] = pos * kZoneTokens + j * B;
         }
         __syncthreads();
         if (threadIdx.x == blockDim.x - 1) carry += scan[threadIdx.x];
@@ -444,8 +451,8 @@ hipError_t launch_zone_shapes(const void* v, bool bf16, int64_t C, int64_t ld, c
     hipLaunchKernelGGL(zone_reduce_kernel, dim3(nZ), dim3(64), 0, s, partial, nslab, C, a, g, rec);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(zone_decide_kernel, dim3(1), dim3(1024), 0, s, rec, nZ, tau128, tau256, eps, zone_shape,
-                       block_offsets, nb_dev);
+    hipLaunchKernelGGL(zone_decide_kernel, dim3(1), dim3(1024), 0, s, rec, nZ, tau128, tau256, eps, g.order,
+                       zone_shape, block_offsets, nb_dev);
     return hipGetLastError();
 }
 

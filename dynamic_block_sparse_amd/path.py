@@ -31,7 +31,10 @@ class PrismPath:
     by default; 1 processes heads one at a time).
     """
 
-    def __init__(self, T, H, W, heads, d, top_k, top_p, scale, head_chunk=None, prm=None, device="cuda"):
+    def __init__(self, T, H, W, heads, d, top_k, top_p, scale, head_chunk=None, prm=None, device="cuda",
+                 zone_order="raster"):
+        """zone_order: "raster" (zones in raster order) or "hilbert" (zones along
+        the 3D Hilbert curve, prism_hilbert_zone_order)."""
         self.T, self.H, self.W = T, H, W
         self.N = T * H * W
         self.nZ = self.N // 512
@@ -47,6 +50,12 @@ class PrismPath:
         self.nb_dev = torch.empty(1, dtype=torch.int32, device=self.device)
         self.zone_stats = torch.empty(self.nZ * P.ZS_STRIDE, dtype=torch.float64, device=self.device)
         self.nb = None
+        if zone_order not in ("raster", "hilbert"):
+            raise ValueError("zone_order must be 'raster' or 'hilbert'")
+        self.zone_order = None
+        if zone_order == "hilbert":
+            self.zone_order = torch.tensor(P.prism_hilbert_zone_order(T, H, W), dtype=torch.int32,
+                                           device=self.device)
 
     # -------------------------------------------------------------- stages
     def shapes(self, v, a):
@@ -56,7 +65,8 @@ class PrismPath:
         ws = torch.empty(P.prism_workspace_size(P.OP_ZONE_SHAPES, self.N, 1, C, 0, 0), dtype=torch.uint8,
                          device=self.device)
         self.nb = P.prism_zone_shapes(self.T, self.H, self.W, v, C, v.stride(0), a, self.zone_shape,
-                                      self.block_offsets, self.nb_dev, ws, prm=self.prm, zone_stats=self.zone_stats)
+                                      self.block_offsets, self.nb_dev, ws, prm=self.prm, zone_stats=self.zone_stats,
+                                      zone_order=self.zone_order)
         return self.nb
 
     def block_major_like(self, x):
@@ -74,7 +84,7 @@ class PrismPath:
         if out is None:
             out = torch.empty((N, nh, d), dtype=x.dtype, device=x.device) if inverse else self.block_major_like(x)
         P.prism_block_permute_heads(self.T, self.H, self.W, self.zone_shape, x, out, nh, d, x.stride(0), x.stride(1),
-                                    out.stride(0), out.stride(1), 1 if inverse else 0)
+                                    out.stride(0), out.stride(1), 1 if inverse else 0, zone_order=self.zone_order)
         return out
 
     def permute_per_head(self, x, inverse=False, out=None):
@@ -84,7 +94,7 @@ class PrismPath:
             out = torch.empty((N, nh, d), dtype=x.dtype, device=x.device) if inverse else self.block_major_like(x)
         for h in range(nh):
             P.prism_block_permute(self.T, self.H, self.W, self.zone_shape, x[:, h], out[:, h], d, x.stride(0),
-                                  out.stride(0), 1 if inverse else 0)
+                                  out.stride(0), 1 if inverse else 0, zone_order=self.zone_order)
         return out
 
     def _cap(self):

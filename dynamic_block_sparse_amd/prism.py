@@ -26,7 +26,7 @@ ZS_STRIDE = 16
 STATUS = {0: "PRISM_OK", 1: "PRISM_E_ARG", 2: "PRISM_E_GRID", 3: "PRISM_E_DTYPE",
           4: "PRISM_E_UNSUPPORTED", 5: "PRISM_E_WORKSPACE", 6: "PRISM_E_HIP"}
 
-EXPORTS = ["prism_audio_norm_map", "prism_zone_shapes", "prism_block_permute", "prism_block_permute_heads", "prism_select",
+EXPORTS = ["prism_hilbert_zone_order", "prism_audio_norm_map", "prism_zone_shapes", "prism_block_permute", "prism_block_permute_heads", "prism_select",
            "prism_sparse_attn_fwd", "prism_flat_route", "prism_routed_attn_fwd", "prism_routed_attn_bwd",
            "prism_sparse_attn_bwd", "prism_workspace_size", "prism_status_string", "prism_last_error",
            "prism_candidate_shapes"]
@@ -44,10 +44,12 @@ class PrismError(RuntimeError):
 
 _vp, _i32, _i64, _f32, _f64, _sz = C.c_void_p, C.c_int32, C.c_int64, C.c_float, C.c_double, C.c_size_t
 _lib.prism_zone_shapes.argtypes = [_i32, _i32, _i32, _vp, _i32, _i64, _i64, _vp, C.POINTER(PrismShapeParams), _vp,
-                                   _vp, _vp, C.POINTER(_i32), _vp, _vp, _sz, _vp]
-_lib.prism_block_permute.argtypes = [_i32, _i32, _i32, _vp, _vp, _vp, _i32, _i64, _i64, _i64, _i32, _vp]
+                                   _vp, _vp, C.POINTER(_i32), _vp, _vp, _sz, _vp, _vp]
+_lib.prism_block_permute.argtypes = [_i32, _i32, _i32, _vp, _vp, _vp, _i32, _i64, _i64, _i64, _i32, _vp, _vp]
 _lib.prism_block_permute_heads.argtypes = [_i32, _i32, _i32, _vp, _vp, _vp, _i32, _i32, _i32, _i64, _i64, _i64, _i64,
-                                           _i32, _vp]
+                                           _i32, _vp, _vp]
+_lib.prism_hilbert_zone_order.argtypes = [_i32, _i32, _i32, C.POINTER(_i32)]
+_lib.prism_hilbert_zone_order.restype = C.c_int
 _lib.prism_select.argtypes = [_vp, _vp, _i32, _i64, _i32, _i32, _i64, _i64, _vp, _i32, _i32, _f64, _f32, _vp, _vp,
                               _i64, _vp, _vp, _vp, _sz, _vp]
 _lib.prism_sparse_attn_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i64, _i64, _vp, _i32, _vp,
@@ -125,29 +127,40 @@ def prism_workspace_size(op, N, heads, d, nb, cap):
 
 
 def prism_zone_shapes(T, H, W, v, C_, v_ld, a_map, zone_shape, block_offsets, nb_dev, ws, prm=None,
-                      zone_stats=None, want_nb=True, stream=None, dtype=None):
+                      zone_stats=None, want_nb=True, stream=None, dtype=None, zone_order=None):
     """v: raster [N, C] (any view with token stride v_ld); returns NB when want_nb."""
     nb_host = _i32(-1)
     p = PrismShapeParams(*prm) if prm is not None else None
     st = _lib.prism_zone_shapes(T, H, W, _ptr(v), _dt(v) if dtype is None else dtype, C_, v_ld, _ptr(a_map),
                                 C.byref(p) if p is not None else None, _ptr(zone_shape), _ptr(block_offsets),
                                 _ptr(nb_dev), C.byref(nb_host) if want_nb else None, _ptr(zone_stats), _ptr(ws),
-                                ws.numel() * ws.element_size() if ws is not None else 0, _stream(stream))
+                                ws.numel() * ws.element_size() if ws is not None else 0, _ptr(zone_order),
+                                _stream(stream))
     _check(st)
     return int(nb_host.value) if want_nb else None
 
 
-def prism_block_permute(T, H, W, zone_shape, x, y, row_elems, x_ld, y_ld, inverse, stream=None, dtype=None):
+def prism_block_permute(T, H, W, zone_shape, x, y, row_elems, x_ld, y_ld, inverse, stream=None, dtype=None,
+                        zone_order=None):
     st = _lib.prism_block_permute(T, H, W, _ptr(zone_shape), _ptr(x), _ptr(y), _dt(x) if dtype is None else dtype,
-                                  row_elems, x_ld, y_ld, int(inverse), _stream(stream))
+                                  row_elems, x_ld, y_ld, int(inverse), _ptr(zone_order), _stream(stream))
     _check(st)
 
 
 def prism_block_permute_heads(T, H, W, zone_shape, x, y, heads, d, x_ld, x_hs, y_ld, y_hs, inverse, stream=None,
-                              dtype=None):
+                              dtype=None, zone_order=None):
     st = _lib.prism_block_permute_heads(T, H, W, _ptr(zone_shape), _ptr(x), _ptr(y), _dt(x) if dtype is None else dtype,
-                                        heads, d, x_ld, x_hs, y_ld, y_hs, int(inverse), _stream(stream))
+                                        heads, d, x_ld, x_hs, y_ld, y_hs, int(inverse), _ptr(zone_order),
+                                        _stream(stream))
     _check(st)
+
+
+def prism_hilbert_zone_order(T, H, W):
+    """Host list: order[pos] = raster zone index along the 3D Hilbert curve."""
+    nZ = (T // 8) * (H // 8) * (W // 8)
+    buf = (_i32 * max(nZ, 1))()
+    _check(_lib.prism_hilbert_zone_order(T, H, W, buf))
+    return [int(buf[i]) for i in range(nZ)]
 
 
 def prism_audio_norm_map(h, N, C, ld, a, ws, norms=None, stream=None, dtype=None):

@@ -131,6 +131,10 @@ prism_status prism_audio_norm_map(const void* h, prism_dtype dt, int64_t N, int6
  *   nb_host        optional host int32*: when not NULL the call synchronises
  *                  `stream` and stores NB there
  *   zone_stats     optional out [nZ * PRISM_ZS_STRIDE] doubles (layout above)
+ *   zone_order     optional device [nZ] int32: zone_order[pos] is the raster zone
+ *                  placed at block-major zone position pos (NULL: raster order;
+ *                  prism_hilbert_zone_order gives the Hilbert order).  The block
+ *                  offsets follow it; pass the same array to the permutations.
  *
  * Statistics accumulate in float64.  Decisions: rho < tau256 -> 256, else
  * rho < tau128 -> 128, else 64; the shape is the candidate of that volume
@@ -143,7 +147,7 @@ prism_status prism_zone_shapes(int32_t T, int32_t H, int32_t W,
                                const float* a_map, const prism_shape_params* prm,
                                uint8_t* zone_shape, int32_t* block_offsets, int32_t* nb_dev,
                                int32_t* nb_host, double* zone_stats,
-                               void* ws, size_t ws_bytes, hipStream_t stream);
+                               void* ws, size_t ws_bytes, const int32_t* zone_order, hipStream_t stream);
 
 /*
  * prism_block_permute - gather rows from raster into block-major order
@@ -157,10 +161,12 @@ prism_status prism_zone_shapes(int32_t T, int32_t H, int32_t W,
  *   row_elems      elements moved per token (e.g. heads*d)
  *   x_ld, y_ld     token strides of x and y in elements (>= row_elems)
  *   x, y           must not overlap
+ *   zone_order     the zone order given to prism_zone_shapes (NULL: raster)
  */
 prism_status prism_block_permute(int32_t T, int32_t H, int32_t W, const uint8_t* zone_shape,
                                  const void* x, void* y, prism_dtype dt, int64_t row_elems,
-                                 int64_t x_ld, int64_t y_ld, int32_t inverse, hipStream_t stream);
+                                 int64_t x_ld, int64_t y_ld, int32_t inverse, const int32_t* zone_order,
+                                 hipStream_t stream);
 
 /*
  * prism_block_permute_heads - the same permutation for all heads of a token
@@ -185,7 +191,7 @@ prism_status prism_block_permute(int32_t T, int32_t H, int32_t W, const uint8_t*
 prism_status prism_block_permute_heads(int32_t T, int32_t H, int32_t W, const uint8_t* zone_shape,
                                        const void* x, void* y, prism_dtype dt, int32_t heads, int32_t d,
                                        int64_t x_ld, int64_t x_hs, int64_t y_ld, int64_t y_hs,
-                                       int32_t inverse, hipStream_t stream);
+                                       int32_t inverse, const int32_t* zone_order, hipStream_t stream);
 
 /*
  * prism_select - pooled block scores and hybrid Top-k U Top-p key-block
@@ -326,6 +332,19 @@ prism_status prism_routed_attn_bwd(const void* q, const void* k, const void* v, 
                                    int32_t heads, int32_t d, int64_t ld, int64_t hs, const int32_t* block_offsets,
                                    int32_t nb, const int32_t* sel_offsets, const int32_t* sel_idx, int64_t cap,
                                    const uint8_t* flat, float scale, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * prism_hilbert_zone_order - host function (next row after the exact path; the
+ * DFSAttn article's Hilbert-curve reordering, applied to zones): order[pos] =
+ * the raster zone index of the pos-th zone along the 3D Hilbert curve of
+ * J. Skilling's transform over the smallest 2^k cube holding the zone grid,
+ * axes (t, h, w) with t the most significant, zones outside the grid skipped.
+ *
+ *   order   out host [nZ] int32 (nZ = T/8 * H/8 * W/8); copy it to the device
+ *           for prism_zone_shapes and the permutations
+ * Errors: PRISM_E_GRID, PRISM_E_ARG for a NULL pointer.
+ */
+prism_status prism_hilbert_zone_order(int32_t T, int32_t H, int32_t W, int32_t* order);
 
 /* Workspace bytes for one call.  ZONE_SHAPES: N = T*H*W and d = C (heads, nb,
  * cap ignored).  SELECT, ATTN_FWD, ATTN_BWD: the call's N, heads, d, nb, cap. */

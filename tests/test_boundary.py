@@ -74,7 +74,7 @@ def test_zone_shapes_rejects_bad_grids_and_args():
     ws_need = P.prism_workspace_size(P.OP_ZONE_SHAPES, 8 * 16 * 16, 1, 64, 0, 0)
     assert ws_need > 0
     call = lambda T=8, H=16, W=16, v=A, dt=0, C=64, ld=64, a=B, zs=Cc, bo=A, nb=B, ws=Cc, wsb=ws_need: \
-        lib.prism_zone_shapes(T, H, W, v, dt, C, ld, a, None, zs, bo, nb, None, None, ws, wsb, None)
+        lib.prism_zone_shapes(T, H, W, v, dt, C, ld, a, None, zs, bo, nb, None, None, ws, wsb, None, None)
     assert call(T=12) == 2
     assert call(H=0) == 2
     assert call(W=-8) == 2
@@ -92,17 +92,19 @@ def test_zone_shapes_rejects_bad_thresholds():
     lib, P = _lib()
     ws_need = P.prism_workspace_size(P.OP_ZONE_SHAPES, 512, 1, 64, 0, 0)
     bad = P.PrismShapeParams(0.2, 0.5, 1e-6)      # tau256 above tau128
-    st = lib.prism_zone_shapes(8, 8, 8, A, 0, 64, 64, B, ctypes.byref(bad), Cc, A, B, None, None, Cc, ws_need, None)
+    st = lib.prism_zone_shapes(8, 8, 8, A, 0, 64, 64, B, ctypes.byref(bad), Cc, A, B, None, None, Cc, ws_need, None,
+                               None)
     assert st == 1
     bad = P.PrismShapeParams(0.5, 0.25, 0.0)      # eps must be positive
-    st = lib.prism_zone_shapes(8, 8, 8, A, 0, 64, 64, B, ctypes.byref(bad), Cc, A, B, None, None, Cc, ws_need, None)
+    st = lib.prism_zone_shapes(8, 8, 8, A, 0, 64, 64, B, ctypes.byref(bad), Cc, A, B, None, None, Cc, ws_need, None,
+                               None)
     assert st == 1
 
 
 def test_block_permute_rejects():
     lib, P = _lib()
     f = lambda T=8, zs=A, x=B, y=Cc, dt=1, re_=128, xl=128, yl=128, inv=0: \
-        lib.prism_block_permute(T, 8, 8, zs, x, y, dt, re_, xl, yl, inv, None)
+        lib.prism_block_permute(T, 8, 8, zs, x, y, dt, re_, xl, yl, inv, None, None)
     assert f(T=4) == 2
     assert f(zs=None) == 1
     assert f(dt=5) == 3
@@ -117,7 +119,7 @@ def test_block_permute_heads_rejects():
     lib, P = _lib()
     X, Y = 0x1000000, 0x2000000                    # 16 MiB apart: the 8x8x8 spans do not meet
     f = lambda T=8, zs=A, x=X, y=Y, dt=1, heads=2, d=128, xl=256, xh=128, yl=128, yh=512 * 128, inv=0: \
-        lib.prism_block_permute_heads(T, 8, 8, zs, x, y, dt, heads, d, xl, xh, yl, yh, inv, None)
+        lib.prism_block_permute_heads(T, 8, 8, zs, x, y, dt, heads, d, xl, xh, yl, yh, inv, None, None)
     assert f(T=12) == 2
     assert f(zs=None) == 1
     assert f(y=None) == 1
@@ -248,3 +250,20 @@ def test_routed_backward_rejects():
     assert f(fl=None) == 1
     assert f(ws=None) == 5
     assert f(wsb=need - 16) == 5
+
+
+@pytest.mark.parametrize("grid", [(8, 8, 8), (16, 16, 16), (64, 64, 64), (64, 72, 128), (24, 40, 16), (120, 72, 128)])
+def test_hilbert_zone_order_matches_the_oracle(grid):
+    """The library's host Hilbert order (its own implementation of Skilling's
+    transform) against the oracle's, on cubes and on the workloads' grids."""
+    from dynamic_block_sparse_amd import prism as P
+    from oracle import prism_oracle as orc
+    T, H, W = grid
+    assert P.prism_hilbert_zone_order(T, H, W) == orc.hilbert_zone_order(T, H, W).tolist()
+
+
+def test_hilbert_zone_order_rejects():
+    lib, P = _lib()
+    buf = (ctypes.c_int32 * 8)()
+    assert lib.prism_hilbert_zone_order(12, 8, 8, buf) == 2
+    assert lib.prism_hilbert_zone_order(8, 8, 8, None) == 1
