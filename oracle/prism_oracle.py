@@ -7,6 +7,8 @@ no code, table or constant with the product: every step below is written out
 again from the pages, in NumPy float64, slowly and in the pages' order.
 
 Sources ("the pages"):
+  [P4] DFSAttn article at gist.science (next row f4 only): 3D Hilbert-curve
+       token reordering and sub-block scoring of large blocks.
   [P5] "In-Context Sparse Attention" article at aitrends.kr (next row f3 only):
        query-block sharpness M_i routes blocks to an exact "sharp" group or a
        "flat" group computed with block-mean keys (zeroth-order Taylor).
@@ -30,7 +32,10 @@ Parity status per function:
     indicator, volume, optimum_log2, nearest_shape, block layout, permutation,
     pool_blocks, block_logits, select_row, attention forward and backward.
     next row f4: hilbert_zone_order (adjacency of consecutive zones on 2^k
-    cubes, a permutation, restriction of the enclosing cube's order).
+    cubes, a permutation, restriction of the enclosing cube's order);
+    subblock_logits (reduces to block_logits for 64-token blocks, equals
+    them when a block's runs share one mean, closed forms for two and four
+    runs, Jensen bounds against brute-force pair scores).
     next row f3: block_sharpness, flat_route, taylor_attn_fwd_block,
     taylor_attn_bwd_block and routed_attention (each pinned
     to closed forms of its reading: uniform and one-hot rows, brute-force
@@ -405,6 +410,40 @@ def block_logits(Qbar, Kbar, scale):
     block-size weighting."""
     L = float(np.float32(scale)) * (Qbar @ Kbar.T)
     return L.astype(np.float32)
+
+
+
+SUB = 64   # sub-block length for the sub-block scoring variant (the smallest block volume)
+
+
+def subblock_logits(Qp, Kp, offs, head, scale, rows=None):
+    """Next row f4, scoring variant (DFSAttn article, sub-block scoring: a
+    large block is scored through the finer scores of its parts, and those are
+    added up).  Reading: each block is cut into its consecutive SUB-token runs
+    in block-major order; every run is mean-pooled; the score of block pair
+    (i, j) is the log of the mean, over all run pairs (a in i, b in j), of
+    exp(scale * Q_bar_a . K_bar_b).  The addition is taken in probability
+    space and divided by the number of pairs, so a pair of 64-token blocks
+    keeps its plain pooled score and blocks of every size stay on one scale.
+    Float64, with each pair group's maximum factored out, rounded once to
+    float32.  rows: the query blocks to score (default all).  Returns
+    [len(rows), NB] float32."""
+    offs = np.asarray(offs, dtype=np.int64)
+    NB = len(offs) - 1
+    runs = np.arange(0, offs[-1] + 1, SUB)
+    Qs = pool_blocks(Qp, runs, head)
+    Ks = pool_blocks(Kp, runs, head)
+    sc = float(np.float32(scale))
+    first = offs[:-1] // SUB                      # first run of each block
+    rows = range(NB) if rows is None else rows
+    out = np.empty((len(rows), NB), dtype=np.float32)
+    for r, i in enumerate(rows):
+        S = sc * (Qs[offs[i] // SUB:offs[i + 1] // SUB] @ Ks.T)        # [runs of i, all key runs]
+        m = np.maximum.reduceat(S.max(axis=0), first)                   # per key block
+        mean_e = np.add.reduceat(np.exp(S - np.repeat(m, np.diff(offs) // SUB)[None, :]).sum(axis=0), first)
+        mean_e /= S.shape[0] * (np.diff(offs) // SUB)
+        out[r] = (m + np.log(mean_e)).astype(np.float32)
+    return out
 
 
 def select_row(L, k, p):

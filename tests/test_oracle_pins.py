@@ -769,3 +769,106 @@ def test_layout_and_permutation_follow_the_zone_order():
     assert sorted(pi.tolist()) == list(range(T * H * W))
     for pos, m in enumerate(order):                               # each zone's 512 tokens move as a unit
         assert (pi[512 * pos:512 * (pos + 1)] == pi_r[512 * m:512 * (m + 1)]).all()
+
+
+# ---------------------------------------------------------------- next row f4: sub-block scoring
+
+def _runs_tensor(run_means, d):
+    """[64 * len(run_means), 1, d] rows: every row of run r equals run_means[r]."""
+    return np.repeat(np.asarray(run_means, dtype=np.float64), orc.SUB, axis=0)[:, None, :d]
+
+
+def test_subblock_logits_are_the_plain_scores_for_64_token_blocks():
+    rng = np.random.default_rng(40)
+    nb, d = 9, 16
+    offs = np.arange(nb + 1) * 64
+    Q = rng.standard_normal((64 * nb, 1, d))
+    K = rng.standard_normal((64 * nb, 1, d))
+    want = orc.block_logits(orc.pool_blocks(Q, offs, 0), orc.pool_blocks(K, offs, 0), 0.25)
+    got = orc.subblock_logits(Q, K, offs, 0, 0.25)
+    assert got.dtype == np.float32 and (got == want).all()
+
+
+def test_subblock_logits_equal_the_plain_scores_when_runs_share_one_mean():
+    # small integers times 2^-3: every mean and dot product below is exact
+    rng = np.random.default_rng(41)
+    d = 8
+    offs = np.array([0, 256, 384, 448, 704])                      # blocks of 256, 128, 64, 256
+    sizes = np.diff(offs) // 64
+    qb = rng.integers(-4, 5, size=(len(sizes), d)) / 8.0
+    kb = rng.integers(-4, 5, size=(len(sizes), d)) / 8.0
+    Q = _runs_tensor(np.repeat(qb, sizes, axis=0), d)
+    K = _runs_tensor(np.repeat(kb, sizes, axis=0), d)
+    want = orc.block_logits(orc.pool_blocks(Q, offs, 0), orc.pool_blocks(K, offs, 0), 0.5)
+    got = orc.subblock_logits(Q, K, offs, 0, 0.5)
+    assert (got == want).all()
+
+
+def test_subblock_logits_closed_forms():
+    d = 4
+    e0 = [1.0, 0.0, 0.0, 0.0]
+    # query block of two runs with means 2 e0 and 0, key block of two runs both e0:
+    # run-pair scores 2, 2, 0, 0, so the score is log((e^2 + 1) / 2)
+    Q = _runs_tensor([[2.0, 0, 0, 0], [0.0, 0, 0, 0]], d)
+    K = _runs_tensor([e0, e0], d)
+    got = orc.subblock_logits(Q, K, np.array([0, 128]), 0, 1.0)
+    assert math.isclose(float(got[0, 0]), math.log((math.e ** 2 + 1.0) / 2.0), rel_tol=2 ** -23)
+    # one query run against a key block of four runs scored 0, 1, 2, 3: log((1 + e + e^2 + e^3) / 4)
+    Q = _runs_tensor([e0] * 4, d)
+    K = _runs_tensor([[0.0, 0, 0, 0], e0, [2.0, 0, 0, 0], [3.0, 0, 0, 0]], d)
+    offs = np.array([0, 256])
+    got = orc.subblock_logits(Q, K, offs, 0, 1.0)
+    want = math.log(sum(math.exp(s) for s in range(4)) / 4.0)
+    assert math.isclose(float(got[0, 0]), want, rel_tol=2 ** -23)
+    # a large score range: the factored maximum keeps it finite (log(mean) of e^900 and e^0)
+    K = _runs_tensor([[900.0, 0, 0, 0], [0.0, 0, 0, 0], [0.0, 0, 0, 0], [0.0, 0, 0, 0]], d)
+    got = orc.subblock_logits(Q, K, offs, 0, 1.0)
+    assert math.isclose(float(got[0, 0]), 900.0 + math.log(0.25), rel_tol=2 ** -23)
+
+
+def test_subblock_logits_lie_between_the_plain_score_and_the_best_run_pair():
+    rng = np.random.default_rng(42)
+    d = 8
+    offs = np.array([0, 64, 320, 448, 512, 768])
+    N = int(offs[-1])
+    Q = rng.standard_normal((N, 1, d))
+    K = rng.standard_normal((N, 1, d))
+    scale = 0.5
+    got = orc.subblock_logits(Q, K, offs, 0, scale).astype(np.float64)
+    plain = orc.block_logits(orc.pool_blocks(Q, offs, 0), orc.pool_blocks(K, offs, 0), scale).astype(np.float64)
+    nb = len(offs) - 1
+    for i in range(nb):
+        for j in range(nb):
+            # brute force: every run pair's score from explicit token loops
+            best = -math.inf
+            for a in range(offs[i], offs[i + 1], 64):
+                qa = [sum(Q[t, 0, c] for t in range(a, a + 64)) / 64.0 for c in range(d)]
+                for b in range(offs[j], offs[j + 1], 64):
+                    kb = [sum(K[t, 0, c] for t in range(b, b + 64)) / 64.0 for c in range(d)]
+                    best = max(best, scale * sum(x * y for x, y in zip(qa, kb)))
+            tol = 2 ** -22 * max(1.0, abs(best))
+            assert plain[i, j] - tol <= got[i, j] <= best + tol, (i, j)
+            if offs[i + 1] - offs[i] > 64 or offs[j + 1] - offs[j] > 64:
+                assert got[i, j] > plain[i, j] + 1e-6, (i, j)          # Jensen, strict for unequal runs
+
+
+def test_subblock_logits_do_not_depend_on_the_order_of_runs_in_a_block():
+    rng = np.random.default_rng(43)
+    d = 8
+    offs = np.array([0, 256, 320])
+    runs_q = rng.integers(-4, 5, size=(5, d)) / 8.0
+    runs_k = rng.integers(-4, 5, size=(5, d)) / 8.0
+    base = orc.subblock_logits(_runs_tensor(runs_q, d), _runs_tensor(runs_k, d), offs, 0, 0.5)
+    p = [2, 0, 3, 1, 4]
+    moved = orc.subblock_logits(_runs_tensor(runs_q[p], d), _runs_tensor(runs_k[p], d), offs, 0, 0.5)
+    assert (base == moved).all()
+
+
+def test_subblock_logits_rows_argument_scores_a_subset():
+    rng = np.random.default_rng(44)
+    offs = np.array([0, 128, 192, 448])
+    Q = rng.standard_normal((448, 1, 16))
+    K = rng.standard_normal((448, 1, 16))
+    full = orc.subblock_logits(Q, K, offs, 0, 0.25)
+    part = orc.subblock_logits(Q, K, offs, 0, 0.25, rows=[2, 0])
+    assert (part == full[[2, 0]]).all()
