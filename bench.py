@@ -435,6 +435,44 @@ def measure_zone_order(cfg, x, path, qp, kp, vp, dop=None, reps=3):
     return res
 
 
+
+def measure_subblock(cfg, path, qp, kp, vp, dop=None, reps=3):
+    """Sub-block scoring (prism_select_subblock) against the plain pooled
+    scores (prism_select) on the first head group of the step's permuted
+    tensors: selection time, the selected work, and the attention time over
+    each selection, timed with HIP events outside the step."""
+    print("[bench] sub-block scoring", file=sys.stderr, flush=True)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    res = {}
+    for scoring in ("block", "subblock"):
+        sel = path.select(qp, kp, 0, scoring=scoring)
+        r = {"select_ms": round(timed(lambda: path.select(qp, kp, 0, scoring=scoring)), 3)}
+        op, lse = path.forward(qp, kp, vp, sel)
+        r["forward_ms"] = round(timed(lambda: path.forward(qp, kp, vp, sel, op=op, lse=lse)), 3)
+        if dop is not None:
+            grads = tuple(path.block_major_like(qp) for _ in range(3))
+            r["backward_ms"] = round(timed(lambda: path.backward(qp, kp, vp, op, dop, lse, sel, grads=grads)), 3)
+            del grads
+        f_fwd, f_bwd, mean_sel = effective_flops(path, [sel], cfg.d)
+        r["effective_tflop"] = round((f_fwd + (f_bwd if dop is not None else 0.0)) / 1e12, 4)
+        r["mean_selected_blocks"] = round(mean_sel, 3)
+        res[scoring] = r
+        del sel, op, lse
+    res["heads"] = path.hc
+    return res
+
+
 def main():
     args = parse()
     if args.profile:
@@ -582,7 +620,8 @@ def main():
     if not args.no_next_rows:
         result["next_rows"] = {"f1_audio_norm_map": measure_norm_map(cfg),
                                "f3_routed_forward": measure_routed(path, qp, kp, vp, args.flat_ratio, dop),
-                               "f4_hilbert_zone_order": measure_zone_order(cfg, x, path, qp, kp, vp, dop)}
+                               "f4_hilbert_zone_order": measure_zone_order(cfg, x, path, qp, kp, vp, dop),
+                               "f4_subblock_scoring": measure_subblock(cfg, path, qp, kp, vp, dop)}
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(cfg, x, path.zone_shape.cpu().numpy(), args.cpu_seconds)

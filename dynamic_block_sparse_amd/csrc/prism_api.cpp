@@ -70,6 +70,27 @@ SelectWs carve_select(Carver& c, int64_t heads, int64_t d, int64_t nb) {
     return w;
 }
 
+// sub-block scoring: the selection's per-row buffers and scores, plus the runs
+struct SubSelectWs {
+    float* logits;
+    int32_t* row_count;
+    uint32_t* row_thr;
+    int32_t* row_jlim;
+    prism::SubblockWs sub;
+};
+SubSelectWs carve_select_sub(Carver& c, int64_t N, int64_t heads, int64_t d, int64_t nb) {
+    SubSelectWs w;
+    const int64_t nr = N / 64;
+    w.logits = c.take<float>(heads * nb * nb);
+    w.row_count = c.take<int32_t>(heads * nb);
+    w.row_thr = c.take<uint32_t>(heads * nb);
+    w.row_jlim = c.take<int32_t>(heads * nb);
+    w.sub.run_offs = c.take<int32_t>(nr + 1);
+    w.sub.run_pooled = c.take<double>(2 * heads * nr * d);
+    w.sub.run_scores = c.take<double>(heads * nr * nr);
+    return w;
+}
+
 struct BwdWs {
     float* Dq;
     int32_t* tcount;
@@ -278,6 +299,11 @@ size_t prism_workspace_size(int32_t op, int64_t N, int32_t heads, int32_t d, int
             carve_select(c, heads, d, nb);
             return c.off;
         }
+        case PRISM_OP_SELECT_SUB: {
+            Carver c(nullptr);
+            carve_select_sub(c, N, heads, d, nb);
+            return c.off;
+        }
         case PRISM_OP_ATTN_FWD: {
             Carver c(nullptr);
             carve_order(c, N, heads, nb);
@@ -435,6 +461,34 @@ prism_status prism_select(const void* q, const void* k, prism_dtype dt, int64_t 
                                            scale, sel_offsets, sel_idx, cap, sel_total, L, w.pooled, w.row_count,
                                            w.row_thr, w.row_jlim, stream),
                       "select launch");
+}
+
+prism_status prism_select_subblock(const void* q, const void* k, prism_dtype dt, int64_t N, int32_t heads, int32_t d,
+                                   int64_t ld, int64_t hs, const int32_t* block_offsets, int32_t nb, int32_t top_k,
+                                   double top_p, float scale, int32_t* sel_offsets, int32_t* sel_idx, int64_t cap,
+                                   int64_t* sel_total, float* logits, void* ws, size_t ws_bytes, hipStream_t stream) {
+    prism_status st = check_tokens(dt, N, heads, d, ld, hs, nb, cap);
+    if (st != PRISM_OK) return st;
+    if (!q || !k || !block_offsets || !sel_offsets || !sel_idx || !sel_total)
+        return fail(PRISM_E_ARG, "null pointer argument");
+    if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k)) & 15)
+        return fail(PRISM_E_UNSUPPORTED, "q and k must be 16-byte aligned");
+    if (top_k < 0 || !(top_p >= 0.0 && top_p <= 1.0)) return fail(PRISM_E_ARG, "need k >= 0 and 0 <= p <= 1");
+    if (!std::isfinite(scale)) return fail(PRISM_E_ARG, "scale must be finite");
+    if (N % 64 != 0) return fail(PRISM_E_ARG, "sub-block scoring needs N a multiple of 64 (N = %lld)",
+                                 static_cast<long long>(N));
+    if (N / 64 > 0x7FFFFFFF / 256) return fail(PRISM_E_UNSUPPORTED, "too many runs for one launch");
+    const size_t need = prism_workspace_size(PRISM_OP_SELECT_SUB, N, heads, d, nb, cap);
+    if (!ws || ws_bytes < need)
+        return fail(PRISM_E_WORKSPACE, "sub-block select needs %zu workspace bytes, got %zu", need,
+                    ws ? ws_bytes : 0);
+    Carver c(ws);
+    SubSelectWs w = carve_select_sub(c, N, heads, d, nb);
+    float* L = logits ? logits : w.logits;
+    return hip_status(prism::launch_select_subblock(q, k, dt == PRISM_BF16, heads, d, ld, hs, N, block_offsets, nb,
+                                                    top_k, top_p, scale, sel_offsets, sel_idx, cap, sel_total, L,
+                                                    w.sub, w.row_count, w.row_thr, w.row_jlim, stream),
+                      "sub-block select launch");
 }
 
 namespace {

@@ -27,6 +27,19 @@ hipError_t launch_select(const void* q, const void* k, bool bf16, int heads, int
                          int32_t* sel_idx, int64_t cap, int64_t* sel_total, float* logits, double* pooled,
                          int32_t* row_count, uint32_t* row_thr, int32_t* row_jlim, hipStream_t s);
 
+// Sub-block scoring: the runs (64-token pieces) of the N tokens, their float64
+// means of Q and K, and their pairwise float64 scores.
+struct SubblockWs {
+    int32_t* run_offs;     // [N/64 + 1]
+    double* run_pooled;    // [2, heads, N/64, d]
+    double* run_scores;    // [heads, N/64, N/64]
+};
+hipError_t launch_select_subblock(const void* q, const void* k, bool bf16, int heads, int d, int64_t ld, int64_t hs,
+                                  int64_t N, const int32_t* offs, int nb, int top_k, double top_p, float scale,
+                                  int32_t* sel_offsets, int32_t* sel_idx, int64_t cap, int64_t* sel_total,
+                                  float* logits, const SubblockWs& w, int32_t* row_count, uint32_t* row_thr,
+                                  int32_t* row_jlim, hipStream_t s);
+
 // rowmask (NULL: every query block) keeps query block i when
 // (rowmask[h*nb + i] != 0) == want
 hipError_t launch_transpose_csr(const int32_t* sel_offsets, const int32_t* sel_idx, int nb, int heads, int64_t cap,

@@ -102,10 +102,11 @@ typedef double d4_t __attribute__((ext_vector_type(4)));
 // and register r of the result D[4 r + l / 16][l % 16], checked with a probe).
 // Wave (wi, wj) computes the 64 x 64 sub-tile at (64 wi, 64 wj) as 4 x 4 MFMA
 // tiles.  The pooled means are staged in LDS channel-major, 16 channels at a
-// time.  Each score is rounded once to fp32 after the scale.
-template <int D>
+// time.  Each score is rounded once to fp32 after the scale (TOut = float), or
+// kept in float64 (TOut = double, the run-pair scores of sub-block scoring).
+template <int D, typename TOut>
 __global__ void __launch_bounds__(256, 2)
-logits_kernel(const double* __restrict__ pooled, int nb, int heads, double scale, float* __restrict__ logits) {
+logits_kernel(const double* __restrict__ pooled, int nb, int heads, double scale, TOut* __restrict__ logits) {
     __shared__ double Qs[kLC][kLT + 2];
     __shared__ double Ks[kLC][kLT + 2];
     const int h = blockIdx.z;
@@ -171,9 +172,51 @@ logits_kernel(const double* __restrict__ pooled, int nb, int heads, double scale
 #pragma unroll
             for (int y = 0; y < 4; ++y) {
                 const int oj = j0 + 64 * wj + 16 * y + lr;
-                if (oj < nb) logits[(static_cast<int64_t>(h) * nb + oi) * nb + oj] = static_cast<float>(scale * acc[x][y][r]);
+                if (oj < nb) logits[(static_cast<int64_t>(h) * nb + oi) * nb + oj] = static_cast<TOut>(scale * acc[x][y][r]);
             }
         }
+}
+
+// ---------------------------------------------------------------- sub-block scores
+//
+// Scoring variant (DFSAttn article, sub-block scoring): every block is cut
+// into its consecutive 64-token runs (a block holds 1, 2 or 4 of them and
+// starts at a multiple of 64 tokens), the runs are pooled like blocks and
+// scored pairwise in float64 by logits_kernel<D, double>, and the score of
+// block pair (i, j) is the log of the mean of exp over its run pairs.
+
+__global__ void __launch_bounds__(256) run_offsets_kernel(int32_t* __restrict__ run_offs, int64_t nr) {
+    const int64_t r = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    if (r <= nr) run_offs[r] = static_cast<int32_t>(r * 64);
+}
+
+// grid (nb, heads): one workgroup per query block, a thread per key block at a
+// time.  S[h][a][b] holds scale * (Q_bar_a . K_bar_b) for runs a, b (nr x nr
+// per head).  The pair maximum m is factored out; the exponentials are added
+// over the key runs in order, each of them first over the query runs in order;
+// the mean divides by the pair count; m + log(mean) is rounded once to fp32.
+__global__ void __launch_bounds__(256)
+subblock_reduce_kernel(const double* __restrict__ S, int64_t nr, const int32_t* __restrict__ offs, int nb,
+                       float* __restrict__ logits) {
+    const int i = blockIdx.x, h = blockIdx.y;
+    const int a0 = offs[i] >> 6;
+    const int na = (offs[i + 1] >> 6) - a0;
+    const double* __restrict__ Sh = S + (static_cast<int64_t>(h) * nr + a0) * nr;
+    float* __restrict__ out = logits + (static_cast<int64_t>(h) * nb + i) * nb;
+    for (int j = threadIdx.x; j < nb; j += 256) {
+        const int b0 = offs[j] >> 6;
+        const int nbj = (offs[j + 1] >> 6) - b0;
+        double m = -INFINITY;
+        for (int b = 0; b < nbj; ++b)
+            for (int a = 0; a < na; ++a) m = fmax(m, Sh[static_cast<int64_t>(a) * nr + b0 + b]);
+        double tot = 0.0;
+        for (int b = 0; b < nbj; ++b) {
+            double cs = 0.0;
+            for (int a = 0; a < na; ++a) cs += exp(Sh[static_cast<int64_t>(a) * nr + b0 + b] - m);
+            tot += cs;
+        }
+        out[j] = static_cast<float>(m + log(tot / static_cast<double>(na * nbj)));
+    }
 }
 
 // ---------------------------------------------------------------- selection
@@ -808,40 +851,52 @@ order_fill_kernel(const int32_t* __restrict__ sel_offsets, const int32_t* __rest
 
 // ---------------------------------------------------------------- launchers
 
-hipError_t launch_select(const void* q, const void* k, bool bf16, int heads, int d, int64_t ld, int64_t hs,
-                         const int32_t* offs, int nb, int top_k, double top_p, float scale, int32_t* sel_offsets,
-                         int32_t* sel_idx, int64_t cap, int64_t* sel_total, float* logits, double* pooled,
-                         int32_t* row_count, uint32_t* row_thr, int32_t* row_jlim, hipStream_t s) {
-    const dim3 pg(nb, heads, 2);
+namespace {
+
+// float64 means of Q and K over the ranges offs[i] .. offs[i+1] (blocks or runs)
+hipError_t launch_pool(const void* q, const void* k, bool bf16, int heads, int d, int64_t ld, int64_t hs,
+                       const int32_t* offs, int n, double* pooled, hipStream_t s) {
+    const dim3 pg(n, heads, 2);
     if (bf16) {
         if (d == 128)
             hipLaunchKernelGGL((pool_kernel<uint16_t, 128>), pg, dim3(256), 0, s, static_cast<const uint16_t*>(q),
-                               static_cast<const uint16_t*>(k), ld, hs, offs, nb, heads, pooled);
+                               static_cast<const uint16_t*>(k), ld, hs, offs, n, heads, pooled);
         else
             hipLaunchKernelGGL((pool_kernel<uint16_t, 64>), pg, dim3(256), 0, s, static_cast<const uint16_t*>(q),
-                               static_cast<const uint16_t*>(k), ld, hs, offs, nb, heads, pooled);
+                               static_cast<const uint16_t*>(k), ld, hs, offs, n, heads, pooled);
     } else {
         if (d == 128)
             hipLaunchKernelGGL((pool_kernel<float, 128>), pg, dim3(256), 0, s, static_cast<const float*>(q),
-                               static_cast<const float*>(k), ld, hs, offs, nb, heads, pooled);
+                               static_cast<const float*>(k), ld, hs, offs, n, heads, pooled);
         else
             hipLaunchKernelGGL((pool_kernel<float, 64>), pg, dim3(256), 0, s, static_cast<const float*>(q),
-                               static_cast<const float*>(k), ld, hs, offs, nb, heads, pooled);
+                               static_cast<const float*>(k), ld, hs, offs, n, heads, pooled);
     }
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const dim3 lg((nb + kLT - 1) / kLT, (nb + kLT - 1) / kLT, heads);
+    return hipGetLastError();
+}
+
+template <typename TOut>
+hipError_t launch_scores(const double* pooled, int n, int heads, int d, float scale, TOut* out, hipStream_t s) {
+    const dim3 lg((n + kLT - 1) / kLT, (n + kLT - 1) / kLT, heads);
     if (d == 128)
-        hipLaunchKernelGGL(logits_kernel<128>, lg, dim3(256), 0, s, pooled, nb, heads, static_cast<double>(scale), logits);
+        hipLaunchKernelGGL((logits_kernel<128, TOut>), lg, dim3(256), 0, s, pooled, n, heads,
+                           static_cast<double>(scale), out);
     else
-        hipLaunchKernelGGL(logits_kernel<64>, lg, dim3(256), 0, s, pooled, nb, heads, static_cast<double>(scale), logits);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
+        hipLaunchKernelGGL((logits_kernel<64, TOut>), lg, dim3(256), 0, s, pooled, n, heads,
+                           static_cast<double>(scale), out);
+    return hipGetLastError();
+}
+
+// the selection proper, from the fp32 scores of every row
+hipError_t select_rows(const float* logits, int heads, int nb, int top_k, double top_p, int32_t* sel_offsets,
+                       int32_t* sel_idx, int64_t cap, int64_t* sel_total, int32_t* row_count, uint32_t* row_thr,
+                       int32_t* row_jlim, hipStream_t s) {
     const dim3 rg(nb, heads);
     // PRISM_SELECT_RADIX=1 forces the LDS radix kernel (used by the tests to
     // compare the two kernels on rows of any length)
     const char* ev = std::getenv("PRISM_SELECT_RADIX");
     const bool radix = ev && ev[0] == '1';
+    hipError_t e;
     if (!radix && nb <= 16 * kSelThreads) {
         if (nb <= 8 * kSelThreads)
             hipLaunchKernelGGL(select_reg_kernel<8>, rg, dim3(kSelThreads), 0, s, logits, nb, top_k, top_p, row_count,
@@ -874,6 +929,41 @@ hipError_t launch_select(const void* q, const void* k, bool bf16, int heads, int
     hipLaunchKernelGGL(select_write_kernel<4>, rg, dim3(256), 0, s, logits, nb, row_thr, row_jlim, sel_offsets,
                        sel_idx, cap);
     return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_select(const void* q, const void* k, bool bf16, int heads, int d, int64_t ld, int64_t hs,
+                         const int32_t* offs, int nb, int top_k, double top_p, float scale, int32_t* sel_offsets,
+                         int32_t* sel_idx, int64_t cap, int64_t* sel_total, float* logits, double* pooled,
+                         int32_t* row_count, uint32_t* row_thr, int32_t* row_jlim, hipStream_t s) {
+    hipError_t e = launch_pool(q, k, bf16, heads, d, ld, hs, offs, nb, pooled, s);
+    if (e != hipSuccess) return e;
+    e = launch_scores<float>(pooled, nb, heads, d, scale, logits, s);
+    if (e != hipSuccess) return e;
+    return select_rows(logits, heads, nb, top_k, top_p, sel_offsets, sel_idx, cap, sel_total, row_count, row_thr,
+                       row_jlim, s);
+}
+
+hipError_t launch_select_subblock(const void* q, const void* k, bool bf16, int heads, int d, int64_t ld, int64_t hs,
+                                  int64_t N, const int32_t* offs, int nb, int top_k, double top_p, float scale,
+                                  int32_t* sel_offsets, int32_t* sel_idx, int64_t cap, int64_t* sel_total,
+                                  float* logits, const SubblockWs& w, int32_t* row_count, uint32_t* row_thr,
+                                  int32_t* row_jlim, hipStream_t s) {
+    const int64_t nr = N / 64;
+    hipLaunchKernelGGL(run_offsets_kernel, dim3(static_cast<unsigned>((nr + 1 + 255) / 256)), dim3(256), 0, s,
+                       w.run_offs, nr);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    e = launch_pool(q, k, bf16, heads, d, ld, hs, w.run_offs, static_cast<int>(nr), w.run_pooled, s);
+    if (e != hipSuccess) return e;
+    e = launch_scores<double>(w.run_pooled, static_cast<int>(nr), heads, d, scale, w.run_scores, s);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(subblock_reduce_kernel, dim3(nb, heads), dim3(256), 0, s, w.run_scores, nr, offs, nb, logits);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return select_rows(logits, heads, nb, top_k, top_p, sel_offsets, sel_idx, cap, sel_total, row_count, row_thr,
+                       row_jlim, s);
 }
 
 // zeroes n counters with a kernel (not a memset node, so that a captured

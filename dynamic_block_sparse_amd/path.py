@@ -32,9 +32,14 @@ class PrismPath:
     """
 
     def __init__(self, T, H, W, heads, d, top_k, top_p, scale, head_chunk=None, prm=None, device="cuda",
-                 zone_order="raster"):
+                 zone_order="raster", scoring="block"):
         """zone_order: "raster" (zones in raster order) or "hilbert" (zones along
-        the 3D Hilbert curve, prism_hilbert_zone_order)."""
+        the 3D Hilbert curve, prism_hilbert_zone_order).  scoring: "block"
+        (pooled block scores) or "subblock" (64-token runs scored in pairs,
+        prism_select_subblock)."""
+        if scoring not in ("block", "subblock"):
+            raise ValueError("scoring must be 'block' or 'subblock'")
+        self.scoring = scoring
         self.T, self.H, self.W = T, H, W
         self.N = T * H * W
         self.nZ = self.N // 512
@@ -100,17 +105,21 @@ class PrismPath:
     def _cap(self):
         return self.nb * self.nb
 
-    def select(self, qp, kp, h0=0, want_logits=False):
+    def select(self, qp, kp, h0=0, want_logits=False, scoring=None):
+        """scoring: "block" (pooled block scores, prism_select) or "subblock"
+        (prism_select_subblock); default the path's own."""
+        scoring = scoring or self.scoring
         nb, hc, cap = self.nb, self.hc, self._cap()
         offsets = torch.empty((hc, nb + 1), dtype=torch.int32, device=self.device)
         idx = torch.empty((hc, cap), dtype=torch.int32, device=self.device)
         total = torch.empty(hc, dtype=torch.int64, device=self.device)
         logits = torch.empty((hc, nb, nb), dtype=torch.float32, device=self.device) if want_logits else None
-        ws = torch.empty(P.prism_workspace_size(P.OP_SELECT, self.N, hc, self.d, nb, cap), dtype=torch.uint8,
+        op, fn = (P.OP_SELECT, P.prism_select) if scoring == "block" else (P.OP_SELECT_SUB, P.prism_select_subblock)
+        ws = torch.empty(P.prism_workspace_size(op, self.N, hc, self.d, nb, cap), dtype=torch.uint8,
                          device=self.device)
         q, k = qp[:, h0:h0 + hc], kp[:, h0:h0 + hc]
-        P.prism_select(q, k, self.N, hc, self.d, q.stride(0), q.stride(1), self.block_offsets, nb, self.top_k,
-                       self.top_p, self.scale, offsets, idx, cap, total, ws, logits=logits)
+        fn(q, k, self.N, hc, self.d, q.stride(0), q.stride(1), self.block_offsets, nb, self.top_k, self.top_p,
+           self.scale, offsets, idx, cap, total, ws, logits=logits)
         return Selection(offsets, idx, total, cap, logits)
 
     def forward(self, qp, kp, vp, sel, op=None, lse=None, h0=0):

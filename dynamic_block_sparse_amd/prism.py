@@ -21,13 +21,13 @@ _lib = C.CDLL(_LIB_PATH)
 
 PRISM_F32, PRISM_BF16 = 0, 1
 (OP_ZONE_SHAPES, OP_SELECT, OP_ATTN_FWD, OP_ATTN_BWD, OP_NORM_MAP, OP_FLAT_ROUTE, OP_ROUTED_FWD,
- OP_ROUTED_BWD) = range(8)
+ OP_ROUTED_BWD, OP_SELECT_SUB) = range(9)
 ZS_STRIDE = 16
 STATUS = {0: "PRISM_OK", 1: "PRISM_E_ARG", 2: "PRISM_E_GRID", 3: "PRISM_E_DTYPE",
           4: "PRISM_E_UNSUPPORTED", 5: "PRISM_E_WORKSPACE", 6: "PRISM_E_HIP"}
 
 EXPORTS = ["prism_hilbert_zone_order", "prism_audio_norm_map", "prism_zone_shapes", "prism_block_permute", "prism_block_permute_heads", "prism_select",
-           "prism_sparse_attn_fwd", "prism_flat_route", "prism_routed_attn_fwd", "prism_routed_attn_bwd",
+           "prism_select_subblock", "prism_sparse_attn_fwd", "prism_flat_route", "prism_routed_attn_fwd", "prism_routed_attn_bwd",
            "prism_sparse_attn_bwd", "prism_workspace_size", "prism_status_string", "prism_last_error",
            "prism_candidate_shapes"]
 
@@ -52,6 +52,7 @@ _lib.prism_hilbert_zone_order.argtypes = [_i32, _i32, _i32, C.POINTER(_i32)]
 _lib.prism_hilbert_zone_order.restype = C.c_int
 _lib.prism_select.argtypes = [_vp, _vp, _i32, _i64, _i32, _i32, _i64, _i64, _vp, _i32, _i32, _f64, _f32, _vp, _vp,
                               _i64, _vp, _vp, _vp, _sz, _vp]
+_lib.prism_select_subblock.argtypes = _lib.prism_select.argtypes
 _lib.prism_sparse_attn_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i64, _i64, _vp, _i32, _vp,
                                        _vp, _i64, _f32, _vp, _sz, _vp]
 _lib.prism_sparse_attn_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i64,
@@ -63,7 +64,7 @@ _lib.prism_routed_attn_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _i64, _i32
 _lib.prism_routed_attn_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i64,
                                        _i64, _vp, _i32, _vp, _vp, _i64, _vp, _f32, _vp, _sz, _vp]
 for _f in ("prism_flat_route", "prism_routed_attn_fwd", "prism_routed_attn_bwd", "prism_audio_norm_map", "prism_zone_shapes", "prism_block_permute", "prism_block_permute_heads", "prism_select",
-           "prism_sparse_attn_fwd", "prism_sparse_attn_bwd"):
+           "prism_select_subblock", "prism_sparse_attn_fwd", "prism_sparse_attn_bwd"):
     getattr(_lib, _f).restype = C.c_int
 _lib.prism_workspace_size.argtypes = [_i32, _i64, _i32, _i32, _i32, _i64]
 _lib.prism_workspace_size.restype = _sz
@@ -176,6 +177,16 @@ def prism_select(q, k, N, heads, d, ld, hs, block_offsets, nb, top_k, top_p, sca
                            _ptr(block_offsets), nb, top_k, float(top_p), float(scale), _ptr(sel_offsets),
                            _ptr(sel_idx), cap, _ptr(sel_total), _ptr(logits), _ptr(ws),
                            ws.numel() * ws.element_size() if ws is not None else 0, _stream(stream))
+    _check(st)
+
+
+def prism_select_subblock(q, k, N, heads, d, ld, hs, block_offsets, nb, top_k, top_p, scale, sel_offsets, sel_idx,
+                          cap, sel_total, ws, logits=None, stream=None, dtype=None):
+    """prism_select with sub-block scores (64-token runs pooled and scored in pairs)."""
+    st = _lib.prism_select_subblock(_ptr(q), _ptr(k), _dt(q) if dtype is None else dtype, N, heads, d, ld, hs,
+                                    _ptr(block_offsets), nb, top_k, float(top_p), float(scale), _ptr(sel_offsets),
+                                    _ptr(sel_idx), cap, _ptr(sel_total), _ptr(logits), _ptr(ws),
+                                    ws.numel() * ws.element_size() if ws is not None else 0, _stream(stream))
     _check(st)
 
 

@@ -73,7 +73,8 @@ typedef struct { double tau128, tau256, eps; } prism_shape_params;
 
 /* operation codes for prism_workspace_size */
 enum { PRISM_OP_ZONE_SHAPES = 0, PRISM_OP_SELECT = 1, PRISM_OP_ATTN_FWD = 2, PRISM_OP_ATTN_BWD = 3,
-       PRISM_OP_NORM_MAP = 4, PRISM_OP_FLAT_ROUTE = 5, PRISM_OP_ROUTED_FWD = 6, PRISM_OP_ROUTED_BWD = 7 };
+       PRISM_OP_NORM_MAP = 4, PRISM_OP_FLAT_ROUTE = 5, PRISM_OP_ROUTED_FWD = 6, PRISM_OP_ROUTED_BWD = 7,
+       PRISM_OP_SELECT_SUB = 8 };
 
 /* Per-zone record written by prism_zone_shapes when `zone_stats` is not NULL:
  * 16 doubles per zone. */
@@ -224,6 +225,36 @@ prism_status prism_select(const void* q, const void* k, prism_dtype dt,
                           int32_t* sel_offsets, int32_t* sel_idx, int64_t cap,
                           int64_t* sel_total, float* logits,
                           void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * prism_select_subblock - prism_select with sub-block scores (scoring variant
+ * of the DFSAttn article, "sub-block scoring": a large block is judged by the
+ * finer scores of its parts, added up).  Arguments, outputs and the selection
+ * rule are those of prism_select; only the score of block pair (i, j) differs:
+ *
+ *   every block is cut into its consecutive 64-token runs (blocks from
+ *   prism_zone_shapes hold 1, 2 or 4 runs and start at multiples of 64; other
+ *   block_offsets must keep that property, which is not checked); runs are
+ *   pooled by their float64 means; the score is
+ *     m + log( mean over run pairs (a in i, b in j) of exp(s_ab - m) ),
+ *   s_ab = scale * (Q_bar_a . K_bar_b) in float64, m the largest s_ab of the
+ *   pair, evaluated in float64 and rounded once to fp32.  A pair of 64-token
+ *   blocks keeps its prism_select score; a larger pair scores at least the
+ *   plain score of its means and at most its best run pair.
+ *
+ *   N              a multiple of 64
+ *   ws, ws_bytes   prism_workspace_size(PRISM_OP_SELECT_SUB, N, heads, d, nb, 0)
+ *                  bytes: the run-pair scores take heads * (N/64)^2 doubles
+ *                  (16.3 GB for 24 heads of 589,824 tokens)
+ * Status: as prism_select, plus PRISM_E_ARG when N is not a multiple of 64.
+ */
+prism_status prism_select_subblock(const void* q, const void* k, prism_dtype dt,
+                                   int64_t N, int32_t heads, int32_t d, int64_t ld, int64_t hs,
+                                   const int32_t* block_offsets, int32_t nb,
+                                   int32_t top_k, double top_p, float scale,
+                                   int32_t* sel_offsets, int32_t* sel_idx, int64_t cap,
+                                   int64_t* sel_total, float* logits,
+                                   void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * prism_sparse_attn_fwd - exact attention restricted to the selected key blocks

@@ -161,6 +161,30 @@ def test_select_rejects():
     assert f(wsb=need - 1) == 5
 
 
+def test_select_subblock_rejects():
+    lib, P = _lib()
+    N, heads, d, nb = 2048, 2, 64, 24
+    cap = nb * nb
+    need = P.prism_workspace_size(P.OP_SELECT_SUB, N, heads, d, nb, cap)
+    assert need >= heads * (N // 64) ** 2 * 8 + 2 * heads * (N // 64) * d * 8   # run-pair scores and run means
+    f = lambda q=A, dt=0, N=N, heads=heads, d=d, nb=nb, k=4, p=0.9, cap=cap, ws=Cc, wsb=need: \
+        lib.prism_select_subblock(q, B, dt, N, heads, d, 128, 64, Cc, nb, k, p, 0.125, A, B, cap, Cc, None, ws, wsb,
+                                  None)
+    assert f(dt=3) == 3
+    assert f(N=100) == 1
+    assert f(N=2048 + 32) == 1                     # not a multiple of 64
+    assert f(heads=0) == 1
+    assert f(d=96) == 4
+    assert f(nb=0) == 1
+    assert f(k=-1) == 1
+    assert f(p=-0.5) == 1
+    assert f(q=None) == 1
+    assert f(q=A + 8) == 4
+    assert f(ws=None) == 5
+    assert f(wsb=need - 1) == 5
+    assert "workspace" in P.prism_last_error()
+
+
 def test_attention_rejects():
     lib, P = _lib()
     N, heads, d, nb = 2048, 2, 128, 24
