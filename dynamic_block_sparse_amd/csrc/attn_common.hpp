@@ -72,19 +72,6 @@ __device__ __forceinline__ u32x4_t pack_kstep(const f32x16_t& x, int s2) {
                    pack2(x[8 * s2 + 4], x[8 * s2 + 5]), pack2(x[8 * s2 + 6], x[8 * s2 + 7])};
 }
 
-// The rounding residuals x - bf16(x) of the k-step packed by pack_kstep(x, s2)
-// into `hi`, themselves packed to bf16: hi + residual carries x to about 16
-// significant bits.
-__device__ __forceinline__ u32x4_t pack_residual(const f32x16_t& x, int s2, const u32x4_t& hi) {
-    u32x4_t r;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-        const float h0 = __uint_as_float(hi[w] << 16), h1 = __uint_as_float(hi[w] & 0xffff0000u);
-        r[w] = pack2(x[8 * s2 + 2 * w] - h0, x[8 * s2 + 2 * w + 1] - h1);
-    }
-    return r;
-}
-
 // Scheduling hint for an unrolled run of STEPS steps that each issue NR LDS
 // reads feeding NM MFMAs: keep the reads AHEAD steps ahead of the MFMAs that
 // consume them, so LDS latency hides behind matrix work instead of the wave

@@ -68,7 +68,7 @@ attn_fwd_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     for (int m = 0; m < DM; ++m)
 #pragma unroll
         for (int x = 0; x < 16; ++x) oacc[m][x] = 0.0f;
-    float mrow = -INFINITY, lrow = 0.0f;
+    float mrow = -INFINITY, lrow = 0.0f, lrnd = 0.0f;   // row sums of P exact and of P rounded to bf16
 
     TileDma<D, 2> dma;
     dma.init(ld, wave, lane);
@@ -107,6 +107,7 @@ attn_fwd_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
                 const float alpha = fast_exp2(mrow - mnew);
                 mrow = mnew;
                 lrow *= alpha;
+                lrnd *= alpha;
 #pragma unroll
                 for (int m = 0; m < DM; ++m)
 #pragma unroll
@@ -120,21 +121,23 @@ attn_fwd_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
                 ls += s0[x] + s1[x];
             }
             lrow += ls;
-            // P = P_hi + P_lo in two bf16 parts, so that O carries P to about 16
-            // bits instead of bf16's 8 (the output's own bf16 rounding is then
-            // the only error of that size)
+            // P is rounded once to bf16 for P V, and O is normalised by the sum
+            // of the same rounded values: O is then an exact convex combination
+            // of V rows with the rounded weights, so a rounding error shared by
+            // the weights (similar values of P rounding the same way) cancels
+            // instead of scaling O.  The log-sum-exp keeps the exact sum.
             const u32x4_t pb[4] = {pack_kstep(s0, 0), pack_kstep(s0, 1), pack_kstep(s1, 0), pack_kstep(s1, 1)};
-            u32x4_t pl[4];
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) pl[ks] = pack_residual(ks < 2 ? s0 : s1, ks & 1, pb[ks]);
+            float lr = 0.0f;
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-                for (int m = 0; m < DM; ++m) {
-                    const u32x4_t vtr = tr_operand<D>(vt, 16 * ks, 32 * m, lane);
-                    oacc[m] = mfma32(vtr, pb[ks], oacc[m]);
-                    oacc[m] = mfma32(vtr, pl[ks], oacc[m]);
-                }
+                for (int w = 0; w < 4; ++w)
+                    lr += __uint_as_float(pb[ks][w] << 16) + __uint_as_float(pb[ks][w] & 0xffff0000u);
+            lrnd += lr;
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+                for (int m = 0; m < DM; ++m) oacc[m] = mfma32(tr_operand<D>(vt, 16 * ks, 32 * m, lane), pb[ks], oacc[m]);
             dma_join();                    // K(tn) landed; every wave is done with V(t)
             if (tn < 0) break;
             dma.load(vbuf, vh_ + static_cast<int64_t>(tn) * ld, wave);
@@ -142,7 +145,7 @@ attn_fwd_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     }
     // lanes l and l^32 hold the two halves of a row's sum
     const float lt = lrow + __shfl_xor(lrow, 32, 64);
-    const float inv = 1.0f / lt;
+    const float inv = 1.0f / (lrnd + __shfl_xor(lrnd, 32, 64));
     uint16_t* orow = o + row * ld + h * hs;
 #pragma unroll
     for (int m = 0; m < DM; ++m)
