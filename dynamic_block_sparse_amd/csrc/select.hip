@@ -829,23 +829,59 @@ order_count_kernel(const int32_t* __restrict__ sel_offsets, const int32_t* __res
     }
 }
 
-// order[base(unit) + start[unit][key] + slot] = tile
-__global__ void __launch_bounds__(256)
+// order[base(unit) + start[unit][key] + slot] = tile, with the slots of one
+// key in ascending tile order (a stable counting sort, so the visiting order is
+// deterministic and keeps spatial order inside a key).  One workgroup per
+// (range r, head h) pair, i.e. per unit; its tiles are ranked in chunks of
+// blockDim.x: a tile's slot is the number of earlier tiles of its key in the
+// chunk plus cursor[unit][key], the count left by earlier chunks.
+__global__ void __launch_bounds__(1024)
 order_fill_kernel(const int32_t* __restrict__ sel_offsets, const int32_t* __restrict__ sel_idx, int64_t cap,
                   const int32_t* __restrict__ offs, int nb, int64_t ntiles, int64_t seg,
                   const int32_t* __restrict__ start, int32_t* __restrict__ cursor, int32_t* __restrict__ order) {
-    const int i = blockIdx.x * 256 + threadIdx.x, h = blockIdx.y;
-    if (i >= nb) return;
+    __shared__ int32_t keys[1024];
+    const int r = blockIdx.x, h = blockIdx.y;
+    const int64_t lo = max(static_cast<int64_t>(h) * ntiles, static_cast<int64_t>(r) * seg);
+    const int64_t hi = min(static_cast<int64_t>(h + 1) * ntiles, static_cast<int64_t>(r + 1) * seg);
+    if (lo >= hi) return;   // head h has no tile in range r
+    const int u = h + r;
     const int32_t* so = sel_offsets + static_cast<int64_t>(h) * (nb + 1);
     const int32_t* si = sel_idx + static_cast<int64_t>(h) * cap;
-    const int key = order_key(so, si, cap, i, nb);
-    for (int t = offs[i] / 64; t < offs[i + 1] / 64; ++t) {
-        int u;
-        int64_t base;
-        tile_unit(h, t, ntiles, seg, u, base);
-        const int64_t pos = base + start[static_cast<int64_t>(u) * (nb + 1) + key] +
-                            atomicAdd(&cursor[static_cast<int64_t>(u) * nb + key], 1);
-        order[pos] = t;
+    const int32_t* st = start + static_cast<int64_t>(u) * (nb + 1);
+    int32_t* cu = cursor + static_cast<int64_t>(u) * nb;
+    const int n = static_cast<int>(blockDim.x);
+    for (int64_t c0 = lo; c0 < hi; c0 += n) {
+        const int64_t p = c0 + threadIdx.x;
+        const bool live = p < hi;
+        const int t = live ? static_cast<int>(p - static_cast<int64_t>(h) * ntiles) : 0;
+        int key = -1;
+        if (live) {
+            int a = 0, b = nb;   // block holding token 64 t
+            while (b - a > 1) {
+                const int m = (a + b) >> 1;
+                if (offs[m] <= 64 * t) a = m;
+                else b = m;
+            }
+            key = order_key(so, si, cap, a, nb);
+        }
+        keys[threadIdx.x] = key;
+        __syncthreads();
+        int rank = 0;
+        bool last = true;
+        int cur = 0;
+        if (live) {
+            for (int j = 0; j < static_cast<int>(threadIdx.x); ++j) rank += keys[j] == key;
+            for (int j = threadIdx.x + 1; j < n; ++j)
+                if (keys[j] == key) {
+                    last = false;
+                    break;
+                }
+            cur = cu[key];
+            order[lo + st[key] + cur + rank] = t;
+        }
+        __syncthreads();   // every tile of the chunk has read its key's count
+        if (live && last) cu[key] = cur + rank + 1;
+        __syncthreads();   // counts updated before the next chunk reads them
     }
 }
 
@@ -1009,8 +1045,8 @@ hipError_t launch_tile_order(const int32_t* sel_offsets, const int32_t* sel_idx,
                        static_cast<int64_t*>(nullptr));
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if ((e = fill_zero(bucket, nbk, s)) != hipSuccess) return e;
-    hipLaunchKernelGGL(order_fill_kernel, g, dim3(256), 0, s, sel_offsets, sel_idx, cap, offs, nb, ntiles, seg, start,
-                       bucket, order);
+    hipLaunchKernelGGL(order_fill_kernel, dim3(8, heads), dim3(1024), 0, s, sel_offsets, sel_idx, cap, offs, nb,
+                       ntiles, seg, start, bucket, order);
     return hipGetLastError();
 }
 
