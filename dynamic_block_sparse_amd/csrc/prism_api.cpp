@@ -111,7 +111,7 @@ BwdWs carve_bwd(Carver& c, int64_t N, int64_t heads, int64_t nb, int64_t cap) {
     const int64_t units = prism::tile_order_units(static_cast<int>(heads));
     w.obucket = c.take<int32_t>(units * nb);
     w.ostart = c.take<int32_t>(units * (nb + 1));
-    w.qorder = c.take<int32_t>(heads * (N / 64));
+    w.qorder = c.take<int32_t>(2 * heads * (N / 64));
     return w;
 }
 
@@ -126,7 +126,7 @@ OrderWs carve_order(Carver& c, int64_t N, int64_t heads, int64_t nb) {
     const int64_t units = prism::tile_order_units(static_cast<int>(heads));
     w.bucket = c.take<int32_t>(units * nb);
     w.start = c.take<int32_t>(units * (nb + 1));
-    w.order = c.take<int32_t>(heads * (N / 64));
+    w.order = c.take<int32_t>(2 * heads * (N / 64));
     return w;
 }
 

@@ -82,7 +82,8 @@ hipError_t launch_attn_bwd_simt(const void* q, const void* k, const void* v, con
 // visiting order of the query tiles: within each unit (a head's part of one
 // XCD's range of the launch order), tile ids grouped by first selected block;
 // bucket holds tile_order_units(heads) * nb and start tile_order_units(heads) *
-// (nb + 1) ints
+// (nb + 1) ints; order holds 2 * heads * ntiles ints (the second half keeps
+// each tile's key while the first is filled)
 inline int tile_order_units(int heads) { return heads + 8; }
 hipError_t launch_tile_order(const int32_t* sel_offsets, const int32_t* sel_idx, int64_t cap, const int32_t* offs,
                              int nb, int heads, int64_t ntiles, int32_t* bucket, int32_t* start, int32_t* order,

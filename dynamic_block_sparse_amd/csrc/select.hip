@@ -815,7 +815,8 @@ __device__ __forceinline__ void tile_unit(int h, int t, int64_t ntiles, int64_t 
 // bucket[unit][key] += 1 for every tile, key = its block's first selected block
 __global__ void __launch_bounds__(256)
 order_count_kernel(const int32_t* __restrict__ sel_offsets, const int32_t* __restrict__ sel_idx, int64_t cap,
-                   const int32_t* __restrict__ offs, int nb, int64_t ntiles, int64_t seg, int32_t* __restrict__ bucket) {
+                   const int32_t* __restrict__ offs, int nb, int64_t ntiles, int64_t seg, int32_t* __restrict__ bucket,
+                   int32_t* __restrict__ tkey) {
     const int i = blockIdx.x * 256 + threadIdx.x, h = blockIdx.y;
     if (i >= nb) return;
     const int32_t* so = sel_offsets + static_cast<int64_t>(h) * (nb + 1);
@@ -826,61 +827,57 @@ order_count_kernel(const int32_t* __restrict__ sel_offsets, const int32_t* __res
         int64_t base;
         tile_unit(h, t, ntiles, seg, u, base);
         atomicAdd(&bucket[static_cast<int64_t>(u) * nb + key], 1);
+        tkey[static_cast<int64_t>(h) * ntiles + t] = key;
     }
 }
 
 // order[base(unit) + start[unit][key] + slot] = tile, with the slots of one
 // key in ascending tile order (a stable counting sort, so the visiting order is
-// deterministic and keeps spatial order inside a key).  One workgroup per
-// (range r, head h) pair, i.e. per unit; its tiles are ranked in chunks of
-// blockDim.x: a tile's slot is the number of earlier tiles of its key in the
-// chunk plus cursor[unit][key], the count left by earlier chunks.
-__global__ void __launch_bounds__(1024)
-order_fill_kernel(const int32_t* __restrict__ sel_offsets, const int32_t* __restrict__ sel_idx, int64_t cap,
-                  const int32_t* __restrict__ offs, int nb, int64_t ntiles, int64_t seg,
+// deterministic and keeps spatial order inside a key).  One workgroup of
+// kOrderChunk threads per (range r, head h) pair, i.e. per unit; its tiles are
+// ranked in chunks of kOrderChunk: a tile's slot is the number of earlier tiles
+// of its key in the chunk plus cursor[unit][key], the count left by earlier
+// chunks.  tkey[h * ntiles + t] is tile t's key (written by order_count_kernel).
+constexpr int kOrderChunk = 1024;
+__global__ void __launch_bounds__(kOrderChunk)
+order_fill_kernel(const int32_t* __restrict__ tkey, int nb, int64_t ntiles, int64_t seg,
                   const int32_t* __restrict__ start, int32_t* __restrict__ cursor, int32_t* __restrict__ order) {
-    __shared__ int32_t keys[1024];
+    __shared__ int4 keys4[kOrderChunk / 4];
+    int32_t* keys = reinterpret_cast<int32_t*>(keys4);
     const int r = blockIdx.x, h = blockIdx.y;
     const int64_t lo = max(static_cast<int64_t>(h) * ntiles, static_cast<int64_t>(r) * seg);
     const int64_t hi = min(static_cast<int64_t>(h + 1) * ntiles, static_cast<int64_t>(r + 1) * seg);
     if (lo >= hi) return;   // head h has no tile in range r
     const int u = h + r;
-    const int32_t* so = sel_offsets + static_cast<int64_t>(h) * (nb + 1);
-    const int32_t* si = sel_idx + static_cast<int64_t>(h) * cap;
     const int32_t* st = start + static_cast<int64_t>(u) * (nb + 1);
     int32_t* cu = cursor + static_cast<int64_t>(u) * nb;
-    const int n = static_cast<int>(blockDim.x);
-    for (int64_t c0 = lo; c0 < hi; c0 += n) {
-        const int64_t p = c0 + threadIdx.x;
+    const int tid = threadIdx.x;
+    for (int64_t c0 = lo; c0 < hi; c0 += kOrderChunk) {
+        const int64_t p = c0 + tid;   // launch position h * ntiles + t
         const bool live = p < hi;
-        const int t = live ? static_cast<int>(p - static_cast<int64_t>(h) * ntiles) : 0;
-        int key = -1;
-        if (live) {
-            int a = 0, b = nb;   // block holding token 64 t
-            while (b - a > 1) {
-                const int m = (a + b) >> 1;
-                if (offs[m] <= 64 * t) a = m;
-                else b = m;
-            }
-            key = order_key(so, si, cap, a, nb);
-        }
-        keys[threadIdx.x] = key;
+        const int key = live ? tkey[p] : -1;
+        keys[tid] = key;
         __syncthreads();
-        int rank = 0;
-        bool last = true;
+        // earlier tiles of the same key in this chunk, and whether a later one exists
+        int rank = 0, after = 0;
+#pragma unroll 8
+        for (int j4 = 0; j4 < kOrderChunk / 4; ++j4) {
+            const int4 kk = keys4[j4];
+            const int j = 4 * j4;
+            const int m[4] = {kk.x == key, kk.y == key, kk.z == key, kk.w == key};
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                rank += (j + x < tid) ? m[x] : 0;
+                after |= (j + x > tid) ? m[x] : 0;
+            }
+        }
         int cur = 0;
         if (live) {
-            for (int j = 0; j < static_cast<int>(threadIdx.x); ++j) rank += keys[j] == key;
-            for (int j = threadIdx.x + 1; j < n; ++j)
-                if (keys[j] == key) {
-                    last = false;
-                    break;
-                }
             cur = cu[key];
-            order[lo + st[key] + cur + rank] = t;
+            order[lo + st[key] + cur + rank] = static_cast<int32_t>(p - static_cast<int64_t>(h) * ntiles);
         }
         __syncthreads();   // every tile of the chunk has read its key's count
-        if (live && last) cu[key] = cur + rank + 1;
+        if (live && !after) cu[key] = cur + rank + 1;
         __syncthreads();   // counts updated before the next chunk reads them
     }
 }
@@ -1039,14 +1036,16 @@ hipError_t launch_tile_order(const int32_t* sel_offsets, const int32_t* sel_idx,
     hipError_t e = fill_zero(bucket, nbk, s);
     if (e != hipSuccess) return e;
     const dim3 g((nb + 255) / 256, heads);
-    hipLaunchKernelGGL(order_count_kernel, g, dim3(256), 0, s, sel_offsets, sel_idx, cap, offs, nb, ntiles, seg, bucket);
+    int32_t* tkey = order + heads * ntiles;            // second half of the order buffer
+    hipLaunchKernelGGL(order_count_kernel, g, dim3(256), 0, s, sel_offsets, sel_idx, cap, offs, nb, ntiles, seg, bucket,
+                       tkey);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(csr_scan_kernel, dim3(units), dim3(1024), 0, s, bucket, nb, start,
                        static_cast<int64_t*>(nullptr));
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if ((e = fill_zero(bucket, nbk, s)) != hipSuccess) return e;
-    hipLaunchKernelGGL(order_fill_kernel, dim3(8, heads), dim3(1024), 0, s, sel_offsets, sel_idx, cap, offs, nb,
-                       ntiles, seg, start, bucket, order);
+    hipLaunchKernelGGL(order_fill_kernel, dim3(8, heads), dim3(kOrderChunk), 0, s, tkey, nb, ntiles, seg, start,
+                       bucket, order);
     return hipGetLastError();
 }
 
