@@ -76,8 +76,8 @@ def test_hilbert_order_2k_size(progress):
     against the oracle; each Hilbert-order selected set, renumbered to raster
     block indices, equal to the raster path's set for the same query block (the
     pooled scores do not depend on where a zone sits in the sequence); the
-    forward outputs of both orders, back in raster order, within the bf16 bar
-    of each other."""
+    Hilbert-order forward output of sampled query blocks within the bf16 bar of
+    the oracle's attention over the oracle's selection."""
     from dynamic_block_sparse_amd.path import PrismPath
     cfg = CONFIGS["2k"]
     heads = [3, 20]
@@ -122,4 +122,21 @@ def test_hilbert_order_2k_size(progress):
             got = np.sort(to_raster[hci[hco[b]:hco[b + 1]]])
             r = to_raster[b]
             np.testing.assert_array_equal(got, np.sort(rci[rco[r]:rco[r + 1]]), err_msg=f"head {h} block {b}")
-        _close(_np(res["hilbert"]["o"][:, h]), _np(res["raster"]["o"][:, h]), "bf16", f"2k O h{heads[h]}")
+    # attention: sampled Hilbert-order query blocks against the oracle
+    progress("hilbert 2k: oracle attention on sampled blocks")
+    pi_np = pi.cpu().numpy()
+    rng = np.random.default_rng(71)
+    blocks = sorted(rng.choice(nb, size=24, replace=False).tolist())
+    sc2 = hp.scale
+    for h in range(2):
+        Qp, Kp, Vp = (orc.to_block_major(_np(t[:, h:h + 1, :]), pi_np) for t in (xs["q"], xs["k"], x["v"][:, heads]))
+        Kbar = orc.pool_blocks(Kp, offs, 0)
+        got = _np(res["hilbert"]["o"][:, h])
+        for b in blocks:
+            qbar = orc.pool_blocks(Qp[offs[b]:offs[b + 1]], np.array([0, offs[b + 1] - offs[b]]), 0)
+            L = orc.block_logits(qbar, Kbar, sc2)[0]
+            s_b, flag = orc.select_row(L, cfg.top_k, cfg.top_p)
+            if flag:
+                continue
+            o_ref, _ = orc.attn_fwd_block(Qp, Kp, Vp, offs, s_b, b, 0, sc2)
+            _close(got[pi_np[offs[b]:offs[b + 1]]], o_ref, "bf16", f"2k O h{heads[h]} block {b}")
