@@ -38,8 +38,8 @@ attn_dq_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
                     const uint16_t* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ Dq,
                     uint16_t* __restrict__ dq, int64_t N, int64_t ld, int64_t hs, const int32_t* __restrict__ offs,
                     int nb, const int32_t* __restrict__ sel_off, const int32_t* __restrict__ sel_idx, int64_t cap,
-                    const int32_t* __restrict__ order, const uint8_t* __restrict__ skip, float scale_log2,
-                    float scale) {
+                    const int32_t* __restrict__ order, const uint8_t* __restrict__ skip, const RowMap om,
+                    float scale_log2, float scale) {
     __shared__ uint16_t kbuf[1][64 * D], vbuf[1][64 * D];
     const int ntiles = static_cast<int>(N / 64);
     const int wg = xcd_remap(blockIdx.x);
@@ -136,7 +136,7 @@ attn_dq_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
             dma.load(kbuf[0], kh_ + static_cast<int64_t>(tn) * ld, wave);
         }
     }
-    uint16_t* out = dq + row * ld + h * hs;
+    uint16_t* out = dq + row_offset(om, row, h);
 #pragma unroll
     for (int m = 0; m < DM; ++m)
 #pragma unroll
@@ -176,7 +176,7 @@ attn_dkdv_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
                       uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, int64_t N, int64_t ld, int64_t hs,
                       const int32_t* __restrict__ offs, int nb, const int32_t* __restrict__ tr_off,
                       const int32_t* __restrict__ tr_idx, int64_t cap, const float* __restrict__ dkbar,
-                      const float* __restrict__ dvbar, float scale_log2, float scale) {
+                      const float* __restrict__ dvbar, const RowMap om, float scale_log2, float scale) {
     // Q and dO tiles, lse (natural log) and D = rowsum(dO * O) of their rows
     __shared__ uint16_t qbuf[2][64 * D], obuf[2][64 * D];
     __shared__ float lbuf[2][64], dbuf[2][64];
@@ -298,7 +298,7 @@ attn_dkdv_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
     TileCursor cur;
     cur.init(ti, offs, e0, e1);
     tile_pipeline(cur, issue, compute);
-    uint16_t* out = (role ? dk : dv) + key * ld + h * hs;
+    uint16_t* out = (role ? dk : dv) + row_offset(om, key, h);
     const float f = role ? scale : 1.0f;
     // routed backward: the block-mean gradient of this key block, shared by its B tokens
     const float* __restrict__ add = role ? dkbar : dvbar;
@@ -324,7 +324,7 @@ hipError_t launch_attn_bwd_mfma(const void* q, const void* k, const void* v, con
                                 const float* Dq, void* dq, void* dk, void* dv, int64_t N, int heads, int d, int64_t ld,
                                 int64_t hs, const int32_t* offs, int nb, const int32_t* so, const int32_t* si,
                                 const int32_t* to, const int32_t* ti, int64_t cap, const int32_t* qorder,
-                                const RouteGrad* rg, float scale, hipStream_t s) {
+                                const RouteGrad* rg, const RowMap& om, float scale, hipStream_t s) {
     const uint8_t* skip = rg ? rg->skip_q : nullptr;
     const float* dkb = rg ? rg->dkbar : nullptr;
     const float* dvb = rg ? rg->dvbar : nullptr;
@@ -339,18 +339,18 @@ hipError_t launch_attn_bwd_mfma(const void* q, const void* k, const void* v, con
     uint16_t* dV = static_cast<uint16_t*>(dv);
     if (d == 128) {
         hipLaunchKernelGGL(attn_dq_mfma_kernel<128>, grid, dim3(128), 0, s, Q, K, V, O, lse, Dq, dQ, N, ld, hs, offs,
-                           nb, so, si, cap, qorder, skip, sl2, scale);
+                           nb, so, si, cap, qorder, skip, om, sl2, scale);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL(attn_dkdv_mfma_kernel<128>, grid, dim3(256), 0, s, Q, K, V, O, lse, Dq, dK, dV, N, ld, hs,
-                           offs, nb, to, ti, cap, dkb, dvb, sl2, scale);
+                           offs, nb, to, ti, cap, dkb, dvb, om, sl2, scale);
     } else {
         hipLaunchKernelGGL(attn_dq_mfma_kernel<64>, grid, dim3(128), 0, s, Q, K, V, O, lse, Dq, dQ, N, ld, hs, offs,
-                           nb, so, si, cap, qorder, skip, sl2, scale);
+                           nb, so, si, cap, qorder, skip, om, sl2, scale);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL(attn_dkdv_mfma_kernel<64>, grid, dim3(256), 0, s, Q, K, V, O, lse, Dq, dK, dV, N, ld, hs,
-                           offs, nb, to, ti, cap, dkb, dvb, sl2, scale);
+                           offs, nb, to, ti, cap, dkb, dvb, om, sl2, scale);
     }
     return hipGetLastError();
 }

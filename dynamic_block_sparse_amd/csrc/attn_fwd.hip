@@ -36,7 +36,7 @@ attn_fwd_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
                      uint16_t* __restrict__ o, float* __restrict__ lse, int64_t N, int64_t ld, int64_t hs,
                      const int32_t* __restrict__ offs, int nb, const int32_t* __restrict__ sel_off,
                      const int32_t* __restrict__ sel_idx, int64_t cap, const int32_t* __restrict__ order,
-                     const uint8_t* __restrict__ skip, float scale_log2) {
+                     const uint8_t* __restrict__ skip, const RowMap om, float scale_log2) {
     __shared__ uint16_t kbuf[64 * D], vbuf[64 * D];
     const int ntiles = static_cast<int>(N / 64);
     const int wg = xcd_remap(blockIdx.x);
@@ -146,7 +146,7 @@ attn_fwd_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     // lanes l and l^32 hold the two halves of a row's sum
     const float lt = lrow + __shfl_xor(lrow, 32, 64);
     const float inv = 1.0f / (lrnd + __shfl_xor(lrnd, 32, 64));
-    uint16_t* orow = o + row * ld + h * hs;
+    uint16_t* orow = o + row_offset(om, row, h);
 #pragma unroll
     for (int m = 0; m < DM; ++m)
 #pragma unroll
@@ -162,8 +162,8 @@ attn_fwd_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
 
 hipError_t launch_attn_fwd_mfma(const void* q, const void* k, const void* v, void* o, float* lse, int64_t N, int heads,
                                 int d, int64_t ld, int64_t hs, const int32_t* offs, int nb, const int32_t* so,
-                                const int32_t* si, int64_t cap, const int32_t* order, const uint8_t* skip, float scale,
-                                hipStream_t s) {
+                                const int32_t* si, int64_t cap, const int32_t* order, const uint8_t* skip,
+                                const RowMap& om, float scale, hipStream_t s) {
     const dim3 grid(static_cast<unsigned>(N / 64 * heads));
     const float sl2 = scale * kLog2e;
     const uint16_t* Q = static_cast<const uint16_t*>(q);
@@ -172,10 +172,10 @@ hipError_t launch_attn_fwd_mfma(const void* q, const void* k, const void* v, voi
     uint16_t* O = static_cast<uint16_t*>(o);
     if (d == 128)
         hipLaunchKernelGGL(attn_fwd_mfma_kernel<128>, grid, dim3(128), 0, s, Q, K, V, O, lse, N, ld, hs, offs, nb, so,
-                           si, cap, order, skip, sl2);
+                           si, cap, order, skip, om, sl2);
     else
         hipLaunchKernelGGL(attn_fwd_mfma_kernel<64>, grid, dim3(128), 0, s, Q, K, V, O, lse, N, ld, hs, offs, nb, so,
-                           si, cap, order, skip, sl2);
+                           si, cap, order, skip, om, sl2);
     return hipGetLastError();
 }
 

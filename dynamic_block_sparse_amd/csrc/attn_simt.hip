@@ -45,7 +45,7 @@ __global__ void __launch_bounds__(64)
 attn_fwd_simt_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, T* __restrict__ o,
                      float* __restrict__ lse, int64_t N, int64_t ld, int64_t hs, const int32_t* __restrict__ offs,
                      int nb, const int32_t* __restrict__ sel_off, const int32_t* __restrict__ sel_idx, int64_t cap,
-                     const uint8_t* __restrict__ skip, float scale) {
+                     const uint8_t* __restrict__ skip, const RowMap om, float scale) {
     __shared__ float Ks[kChunk][D + 1];
     __shared__ float Vs[kChunk][D + 1];
     const int h = blockIdx.y;
@@ -102,9 +102,9 @@ attn_fwd_simt_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* 
         }
     }
     const float inv = 1.0f / l;
-    T* __restrict__ oh = o + h * hs;
+    T* __restrict__ orow = o + row_offset(om, p, h);
 #pragma unroll
-    for (int c = 0; c < D; ++c) st_elem(oh + p * ld + c, acc[c] * inv);
+    for (int c = 0; c < D; ++c) st_elem(orow + c, acc[c] * inv);
     lse[static_cast<int64_t>(h) * N + p] = m + __logf(l);
 }
 
@@ -113,7 +113,7 @@ attn_fwd_simt_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* 
 template <typename T, int D>
 __global__ void __launch_bounds__(256)
 attn_bwd_dot_kernel(const T* __restrict__ o, const T* __restrict__ dout, int64_t N, int heads, int64_t ld, int64_t hs,
-                    float* __restrict__ Dq) {
+                    const RowMap om, float* __restrict__ Dq) {
     constexpr int EPV = 16 / static_cast<int>(sizeof(T));
     constexpr int LPR = D / EPV;            // lanes per row (power of two, <= 64)
     constexpr int RPI = 256 / LPR;          // rows per workgroup step
@@ -124,9 +124,8 @@ attn_bwd_dot_kernel(const T* __restrict__ o, const T* __restrict__ dout, int64_t
         const int64_t p = static_cast<int64_t>(blockIdx.x) * 64 + it * RPI + threadIdx.x / LPR;
         float s = 0.0f;
         if (p < N) {
-            const int64_t off = p * ld + h * hs + sub * EPV;
-            const uint4 a = *reinterpret_cast<const uint4*>(o + off);
-            const uint4 b = *reinterpret_cast<const uint4*>(dout + off);
+            const uint4 a = *reinterpret_cast<const uint4*>(o + row_offset(om, p, h) + sub * EPV);
+            const uint4 b = *reinterpret_cast<const uint4*>(dout + p * ld + h * hs + sub * EPV);
             const uint32_t wa[4] = {a.x, a.y, a.z, a.w}, wb[4] = {b.x, b.y, b.z, b.w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -152,7 +151,7 @@ attn_dq_simt_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* _
                     const T* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ Dq,
                     T* __restrict__ dq, int64_t N, int64_t ld, int64_t hs, const int32_t* __restrict__ offs, int nb,
                     const int32_t* __restrict__ sel_off, const int32_t* __restrict__ sel_idx, int64_t cap,
-                    const uint8_t* __restrict__ skip, float scale) {
+                    const uint8_t* __restrict__ skip, const RowMap om, float scale) {
     __shared__ float Ks[kChunk][D + 1];
     __shared__ float Vs[kChunk][D + 1];
     const int h = blockIdx.y;
@@ -199,8 +198,9 @@ attn_dq_simt_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* _
             }
         }
     }
+    T* __restrict__ drow = dq + row_offset(om, p, h);
 #pragma unroll
-    for (int c = 0; c < D; ++c) st_elem(dq + p * ld + h * hs + c, acc[c] * scale);
+    for (int c = 0; c < D; ++c) st_elem(drow + c, acc[c] * scale);
 }
 
 template <typename T, int D>
@@ -210,7 +210,7 @@ attn_dkdv_simt_kernel(const T* __restrict__ q, const T* __restrict__ k, const T*
                       T* __restrict__ dk, T* __restrict__ dv, int64_t N, int64_t ld, int64_t hs,
                       const int32_t* __restrict__ offs, int nb, const int32_t* __restrict__ tr_off,
                       const int32_t* __restrict__ tr_idx, int64_t cap, const float* __restrict__ dkbar,
-                      const float* __restrict__ dvbar, float scale) {
+                      const float* __restrict__ dvbar, const RowMap om, float scale) {
     __shared__ float Qs[kChunk][D + 1];
     __shared__ float Os[kChunk][D + 1];
     __shared__ float Ls[kChunk], Ds[kChunk];
@@ -266,68 +266,69 @@ attn_dkdv_simt_kernel(const T* __restrict__ q, const T* __restrict__ k, const T*
     // routed backward: the block-mean gradients of this key block, shared by its B tokens
     const float invB = 1.0f / static_cast<float>(offs[j + 1] - offs[j]);
     const int64_t jb = (static_cast<int64_t>(h) * nb + j) * D;
+    const int64_t orow = row_offset(om, p, h);
 #pragma unroll
     for (int c = 0; c < D; ++c) {
-        st_elem(dk + p * ld + h * hs + c, ak[c] * scale + (dkbar ? dkbar[jb + c] * invB : 0.0f));
-        st_elem(dv + p * ld + h * hs + c, av[c] + (dvbar ? dvbar[jb + c] * invB : 0.0f));
+        st_elem(dk + orow + c, ak[c] * scale + (dkbar ? dkbar[jb + c] * invB : 0.0f));
+        st_elem(dv + orow + c, av[c] + (dvbar ? dvbar[jb + c] * invB : 0.0f));
     }
 }
 
 template <typename T, int D>
 static hipError_t fwd_simt(const void* q, const void* k, const void* v, void* o, float* lse, int64_t N, int heads,
                            int64_t ld, int64_t hs, const int32_t* offs, int nb, const int32_t* so, const int32_t* si,
-                           int64_t cap, const uint8_t* skip, float scale, hipStream_t s) {
+                           int64_t cap, const uint8_t* skip, const RowMap& om, float scale, hipStream_t s) {
     const dim3 grid(static_cast<unsigned>(N / 64), heads);
     hipLaunchKernelGGL((attn_fwd_simt_kernel<T, D>), grid, dim3(64), 0, s, static_cast<const T*>(q),
                        static_cast<const T*>(k), static_cast<const T*>(v), static_cast<T*>(o), lse, N, ld, hs, offs, nb,
-                       so, si, cap, skip, scale);
+                       so, si, cap, skip, om, scale);
     return hipGetLastError();
 }
 
 hipError_t launch_attn_fwd_simt(const void* q, const void* k, const void* v, void* o, float* lse, bool bf16, int64_t N,
                                 int heads, int d, int64_t ld, int64_t hs, const int32_t* offs, int nb,
-                                const int32_t* so, const int32_t* si, int64_t cap, const uint8_t* skip, float scale,
-                                hipStream_t s) {
+                                const int32_t* so, const int32_t* si, int64_t cap, const uint8_t* skip,
+                                const RowMap& om, float scale, hipStream_t s) {
     if (bf16)
-        return d == 128 ? fwd_simt<uint16_t, 128>(q, k, v, o, lse, N, heads, ld, hs, offs, nb, so, si, cap, skip, scale, s)
-                        : fwd_simt<uint16_t, 64>(q, k, v, o, lse, N, heads, ld, hs, offs, nb, so, si, cap, skip, scale, s);
-    return d == 128 ? fwd_simt<float, 128>(q, k, v, o, lse, N, heads, ld, hs, offs, nb, so, si, cap, skip, scale, s)
-                    : fwd_simt<float, 64>(q, k, v, o, lse, N, heads, ld, hs, offs, nb, so, si, cap, skip, scale, s);
+        return d == 128 ? fwd_simt<uint16_t, 128>(q, k, v, o, lse, N, heads, ld, hs, offs, nb, so, si, cap, skip, om, scale, s)
+                        : fwd_simt<uint16_t, 64>(q, k, v, o, lse, N, heads, ld, hs, offs, nb, so, si, cap, skip, om, scale, s);
+    return d == 128 ? fwd_simt<float, 128>(q, k, v, o, lse, N, heads, ld, hs, offs, nb, so, si, cap, skip, om, scale, s)
+                    : fwd_simt<float, 64>(q, k, v, o, lse, N, heads, ld, hs, offs, nb, so, si, cap, skip, om, scale, s);
 }
 
 template <typename T, int D>
-static hipError_t dot_launch(const void* o, const void* dout, int64_t N, int heads, int64_t ld, int64_t hs, float* Dq,
-                             hipStream_t s) {
+static hipError_t dot_launch(const void* o, const void* dout, int64_t N, int heads, int64_t ld, int64_t hs,
+                             const RowMap& om, float* Dq, hipStream_t s) {
     hipLaunchKernelGGL((attn_bwd_dot_kernel<T, D>), dim3(static_cast<unsigned>((N + 63) / 64), heads), dim3(256), 0, s,
-                       static_cast<const T*>(o), static_cast<const T*>(dout), N, heads, ld, hs, Dq);
+                       static_cast<const T*>(o), static_cast<const T*>(dout), N, heads, ld, hs, om, Dq);
     return hipGetLastError();
 }
 
 hipError_t launch_bwd_dot(const void* o, const void* dout, bool bf16, int64_t N, int heads, int d, int64_t ld,
-                          int64_t hs, float* Dq, hipStream_t s) {
+                          int64_t hs, const RowMap& om, float* Dq, hipStream_t s) {
     if (bf16)
-        return d == 128 ? dot_launch<uint16_t, 128>(o, dout, N, heads, ld, hs, Dq, s)
-                        : dot_launch<uint16_t, 64>(o, dout, N, heads, ld, hs, Dq, s);
-    return d == 128 ? dot_launch<float, 128>(o, dout, N, heads, ld, hs, Dq, s)
-                    : dot_launch<float, 64>(o, dout, N, heads, ld, hs, Dq, s);
+        return d == 128 ? dot_launch<uint16_t, 128>(o, dout, N, heads, ld, hs, om, Dq, s)
+                        : dot_launch<uint16_t, 64>(o, dout, N, heads, ld, hs, om, Dq, s);
+    return d == 128 ? dot_launch<float, 128>(o, dout, N, heads, ld, hs, om, Dq, s)
+                    : dot_launch<float, 64>(o, dout, N, heads, ld, hs, om, Dq, s);
 }
 
 template <typename T, int D>
 static hipError_t bwd_simt(const void* q, const void* k, const void* v, const void* dout, const float* lse,
                            const float* Dq, void* dq, void* dk, void* dv, int64_t N, int heads, int64_t ld,
                            int64_t hs, const int32_t* offs, int nb, const int32_t* so, const int32_t* si,
-                           const int32_t* to, const int32_t* ti, int64_t cap, const RouteGrad* rg, float scale,
-                           hipStream_t s) {
+                           const int32_t* to, const int32_t* ti, int64_t cap, const RouteGrad* rg,
+                           const RowMap& om, float scale, hipStream_t s) {
     const dim3 grid(static_cast<unsigned>(N / 64), heads);
     hipLaunchKernelGGL((attn_dq_simt_kernel<T, D>), grid, dim3(64), 0, s, static_cast<const T*>(q),
                        static_cast<const T*>(k), static_cast<const T*>(v), static_cast<const T*>(dout), lse, Dq,
-                       static_cast<T*>(dq), N, ld, hs, offs, nb, so, si, cap, rg ? rg->skip_q : nullptr, scale);
+                       static_cast<T*>(dq), N, ld, hs, offs, nb, so, si, cap, rg ? rg->skip_q : nullptr, om, scale);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((attn_dkdv_simt_kernel<T, D>), grid, dim3(64), 0, s, static_cast<const T*>(q),
                        static_cast<const T*>(k), static_cast<const T*>(v), static_cast<const T*>(dout), lse, Dq,
                        static_cast<T*>(dk), static_cast<T*>(dv), N, ld, hs, offs, nb, to, ti, cap,
-                       rg ? rg->dkbar : nullptr, rg ? rg->dvbar : nullptr, scale);
+                       rg ? rg->dkbar : nullptr, rg ? rg->dvbar : nullptr, om, scale);
     return hipGetLastError();
 }
 
@@ -335,16 +336,16 @@ hipError_t launch_attn_bwd_simt(const void* q, const void* k, const void* v, con
                                 const float* Dq, void* dq, void* dk, void* dv, bool bf16, int64_t N, int heads, int d,
                                 int64_t ld, int64_t hs, const int32_t* offs, int nb, const int32_t* so,
                                 const int32_t* si, const int32_t* to, const int32_t* ti, int64_t cap,
-                                const RouteGrad* rg, float scale, hipStream_t s) {
+                                const RouteGrad* rg, const RowMap& om, float scale, hipStream_t s) {
     if (bf16)
         return d == 128 ? bwd_simt<uint16_t, 128>(q, k, v, dout, lse, Dq, dq, dk, dv, N, heads, ld, hs, offs, nb, so,
-                                                   si, to, ti, cap, rg, scale, s)
+                                                   si, to, ti, cap, rg, om, scale, s)
                         : bwd_simt<uint16_t, 64>(q, k, v, dout, lse, Dq, dq, dk, dv, N, heads, ld, hs, offs, nb, so, si,
-                                                  to, ti, cap, rg, scale, s);
+                                                  to, ti, cap, rg, om, scale, s);
     return d == 128 ? bwd_simt<float, 128>(q, k, v, dout, lse, Dq, dq, dk, dv, N, heads, ld, hs, offs, nb, so, si, to,
-                                            ti, cap, rg, scale, s)
+                                            ti, cap, rg, om, scale, s)
                     : bwd_simt<float, 64>(q, k, v, dout, lse, Dq, dq, dk, dv, N, heads, ld, hs, offs, nb, so, si, to,
-                                           ti, cap, rg, scale, s);
+                                           ti, cap, rg, om, scale, s);
 }
 
 }  // namespace prism

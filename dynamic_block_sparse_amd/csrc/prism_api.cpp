@@ -208,6 +208,33 @@ prism::ZoneGrid grid_of(int32_t T, int32_t H, int32_t W, const int32_t* zone_ord
     return g;
 }
 
+// Output rows block-major (layout NULL: the inputs' strides) or scattered to
+// raster order through the zone shapes.
+prism_status row_map(const prism_raster_layout* L, prism_dtype dt, int64_t N, int64_t ld, int64_t hs,
+                     prism::RowMap& m) {
+    m.zone_shape = nullptr;
+    m.g = grid_of(8, 8, 8);
+    m.ld = ld;
+    m.hs = hs;
+    if (!L) return PRISM_OK;
+    prism_status st = check_grid(L->T, L->H, L->W);
+    if (st != PRISM_OK) return st;
+    if (static_cast<int64_t>(L->T) * L->H * L->W != N)
+        return fail(PRISM_E_ARG, "raster layout grid %d x %d x %d does not hold N = %lld tokens", L->T, L->H, L->W,
+                    static_cast<long long>(N));
+    if (!L->zone_shape) return fail(PRISM_E_ARG, "raster layout needs zone_shape");
+    const int64_t vec = dt == PRISM_BF16 ? 8 : 4;   // elements per 16 bytes
+    if (L->ld <= 0 || L->hs < 0 || L->ld % vec || L->hs % vec)
+        return fail(PRISM_E_UNSUPPORTED, "raster layout strides must be non-negative multiples of 16 bytes "
+                                         "(ld = %lld, hs = %lld)",
+                    static_cast<long long>(L->ld), static_cast<long long>(L->hs));
+    m.zone_shape = L->zone_shape;
+    m.g = grid_of(L->T, L->H, L->W, L->zone_order);
+    m.ld = L->ld;
+    m.hs = L->hs;
+    return PRISM_OK;
+}
+
 // Index of cell x (3 axes, `bits` bits each) along the 3D Hilbert curve of
 // J. Skilling's transform ("Programming the Hilbert curve", AIP Conf. Proc.
 // 707, 2004): undo the per-level rotations and reflections, Gray-code the
@@ -513,19 +540,19 @@ prism_status check_fwd(const void* q, const void* k, const void* v, const void* 
 prism_status exact_fwd(const void* q, const void* k, const void* v, void* o, float* lse, prism_dtype dt, int64_t N,
                        int32_t heads, int32_t d, int64_t ld, int64_t hs, const int32_t* block_offsets, int32_t nb,
                        const int32_t* sel_offsets, const int32_t* sel_idx, int64_t cap, const uint8_t* skip,
-                       float scale, Carver& c, hipStream_t stream) {
+                       const prism::RowMap& om, float scale, Carver& c, hipStream_t stream) {
     OrderWs w = carve_order(c, N, heads, nb);
     if (use_simt_attention(dt))
         return hip_status(prism::launch_attn_fwd_simt(q, k, v, o, lse, dt == PRISM_BF16, N, heads, d, ld, hs,
-                                                      block_offsets, nb, sel_offsets, sel_idx, cap, skip, scale,
-                                                      stream),
+                                                      block_offsets, nb, sel_offsets, sel_idx, cap, skip, om,
+                                                      scale, stream),
                           "attention forward launch");
     prism_status st = hip_status(prism::launch_tile_order(sel_offsets, sel_idx, cap, block_offsets, nb, heads, N / 64,
                                                           w.bucket, w.start, w.order, stream),
                                  "tile order launch");
     if (st != PRISM_OK) return st;
     return hip_status(prism::launch_attn_fwd_mfma(q, k, v, o, lse, N, heads, d, ld, hs, block_offsets, nb, sel_offsets,
-                                                  sel_idx, cap, w.order, skip, scale, stream),
+                                                  sel_idx, cap, w.order, skip, om, scale, stream),
                       "attention forward launch");
 }
 
@@ -534,17 +561,19 @@ prism_status exact_fwd(const void* q, const void* k, const void* v, void* o, flo
 prism_status prism_sparse_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, prism_dtype dt,
                                    int64_t N, int32_t heads, int32_t d, int64_t ld, int64_t hs,
                                    const int32_t* block_offsets, int32_t nb, const int32_t* sel_offsets,
-                                   const int32_t* sel_idx, int64_t cap, float scale, void* ws, size_t ws_bytes,
-                                   hipStream_t stream) {
+                                   const int32_t* sel_idx, int64_t cap, float scale, const prism_raster_layout* out,
+                                   void* ws, size_t ws_bytes, hipStream_t stream) {
     prism_status st = check_fwd(q, k, v, o, lse, dt, N, heads, d, ld, hs, block_offsets, nb, sel_offsets, sel_idx, cap,
                                 scale);
     if (st != PRISM_OK) return st;
+    prism::RowMap om;
+    if ((st = row_map(out, dt, N, ld, hs, om)) != PRISM_OK) return st;
     const size_t need = prism_workspace_size(PRISM_OP_ATTN_FWD, N, heads, d, nb, cap);
     if (!ws || ws_bytes < need)
         return fail(PRISM_E_WORKSPACE, "forward needs %zu workspace bytes, got %zu", need, ws ? ws_bytes : 0);
     Carver c(ws);
     return exact_fwd(q, k, v, o, lse, dt, N, heads, d, ld, hs, block_offsets, nb, sel_offsets, sel_idx, cap, nullptr,
-                     scale, c, stream);
+                     om, scale, c, stream);
 }
 
 prism_status prism_flat_route(const float* logits, int32_t heads, int32_t nb, double flat_ratio, uint8_t* flat,
@@ -577,8 +606,10 @@ prism_status prism_routed_attn_fwd(const void* q, const void* k, const void* v, 
     if (!ws || ws_bytes < need)
         return fail(PRISM_E_WORKSPACE, "routed forward needs %zu workspace bytes, got %zu", need, ws ? ws_bytes : 0);
     Carver c(ws);
-    st = exact_fwd(q, k, v, o, lse, dt, N, heads, d, ld, hs, block_offsets, nb, sel_offsets, sel_idx, cap, flat, scale,
-                   c, stream);
+    prism::RowMap om;
+    row_map(nullptr, dt, N, ld, hs, om);
+    st = exact_fwd(q, k, v, o, lse, dt, N, heads, d, ld, hs, block_offsets, nb, sel_offsets, sel_idx, cap, flat, om,
+                   scale, c, stream);
     if (st != PRISM_OK) return st;
     float* kbar = c.take<float>(static_cast<size_t>(heads) * nb * d);
     float* vbar = c.take<float>(static_cast<size_t>(heads) * nb * d);
@@ -615,11 +646,12 @@ prism_status check_bwd(const void* q, const void* k, const void* v, const void* 
 prism_status exact_bwd(const void* q, const void* k, const void* v, const void* dout, const float* lse, void* dq,
                        void* dk, void* dv, prism_dtype dt, int64_t N, int32_t heads, int32_t d, int64_t ld, int64_t hs,
                        const int32_t* block_offsets, int32_t nb, const int32_t* sel_offsets, const int32_t* sel_idx,
-                       int64_t cap, float scale, const BwdWs& w, const prism::RouteGrad* rg, hipStream_t stream) {
+                       int64_t cap, float scale, const BwdWs& w, const prism::RouteGrad* rg, const prism::RowMap& om,
+                       hipStream_t stream) {
     if (use_simt_attention(dt))
         return hip_status(prism::launch_attn_bwd_simt(q, k, v, dout, lse, w.Dq, dq, dk, dv, dt == PRISM_BF16, N, heads,
                                                       d, ld, hs, block_offsets, nb, sel_offsets, sel_idx, w.tr_offsets,
-                                                      w.tr_idx, cap, rg, scale, stream),
+                                                      w.tr_idx, cap, rg, om, scale, stream),
                           "attention backward launch");
     prism_status st = hip_status(prism::launch_tile_order(sel_offsets, sel_idx, cap, block_offsets, nb, heads, N / 64,
                                                           w.obucket, w.ostart, w.qorder, stream),
@@ -627,7 +659,7 @@ prism_status exact_bwd(const void* q, const void* k, const void* v, const void* 
     if (st != PRISM_OK) return st;
     return hip_status(prism::launch_attn_bwd_mfma(q, k, v, dout, lse, w.Dq, dq, dk, dv, N, heads, d, ld, hs,
                                                   block_offsets, nb, sel_offsets, sel_idx, w.tr_offsets, w.tr_idx, cap,
-                                                  w.qorder, rg, scale, stream),
+                                                  w.qorder, rg, om, scale, stream),
                       "attention backward launch");
 }
 
@@ -637,16 +669,19 @@ prism_status prism_sparse_attn_bwd(const void* q, const void* k, const void* v, 
                                    const float* lse, void* dq, void* dk, void* dv, prism_dtype dt, int64_t N,
                                    int32_t heads, int32_t d, int64_t ld, int64_t hs, const int32_t* block_offsets,
                                    int32_t nb, const int32_t* sel_offsets, const int32_t* sel_idx, int64_t cap,
-                                   float scale, void* ws, size_t ws_bytes, hipStream_t stream) {
+                                   float scale, const prism_raster_layout* io, void* ws, size_t ws_bytes,
+                                   hipStream_t stream) {
     prism_status st = check_bwd(q, k, v, o, dout, lse, dq, dk, dv, dt, N, heads, d, ld, hs, block_offsets, nb,
                                 sel_offsets, sel_idx, cap, scale);
     if (st != PRISM_OK) return st;
+    prism::RowMap om;
+    if ((st = row_map(io, dt, N, ld, hs, om)) != PRISM_OK) return st;
     const size_t need = prism_workspace_size(PRISM_OP_ATTN_BWD, N, heads, d, nb, cap);
     if (!ws || ws_bytes < need)
         return fail(PRISM_E_WORKSPACE, "backward needs %zu workspace bytes, got %zu", need, ws ? ws_bytes : 0);
     Carver c(ws);
     BwdWs w = carve_bwd(c, N, heads, nb, cap);
-    st = hip_status(prism::launch_bwd_dot(o, dout, dt == PRISM_BF16, N, heads, d, ld, hs, w.Dq, stream),
+    st = hip_status(prism::launch_bwd_dot(o, dout, dt == PRISM_BF16, N, heads, d, ld, hs, om, w.Dq, stream),
                     "backward dot launch");
     if (st != PRISM_OK) return st;
     st = hip_status(prism::launch_transpose_csr(sel_offsets, sel_idx, nb, heads, cap, w.tcount, w.tr_offsets, w.tr_idx,
@@ -654,7 +689,7 @@ prism_status prism_sparse_attn_bwd(const void* q, const void* k, const void* v, 
                     "transposed selection launch");
     if (st != PRISM_OK) return st;
     return exact_bwd(q, k, v, dout, lse, dq, dk, dv, dt, N, heads, d, ld, hs, block_offsets, nb, sel_offsets, sel_idx,
-                     cap, scale, w, nullptr, stream);
+                     cap, scale, w, nullptr, om, stream);
 }
 
 prism_status prism_routed_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
@@ -673,7 +708,9 @@ prism_status prism_routed_attn_bwd(const void* q, const void* k, const void* v, 
     BwdWs w = carve_bwd(c, N, heads, nb, cap);
     RoutedBwdWs r = carve_routed_bwd(c, heads, d, nb, cap);
     const bool bf16 = dt == PRISM_BF16;
-    st = hip_status(prism::launch_bwd_dot(o, dout, bf16, N, heads, d, ld, hs, w.Dq, stream), "backward dot launch");
+    prism::RowMap om;
+    row_map(nullptr, dt, N, ld, hs, om);
+    st = hip_status(prism::launch_bwd_dot(o, dout, bf16, N, heads, d, ld, hs, om, w.Dq, stream), "backward dot launch");
     if (st != PRISM_OK) return st;
     // key block -> sharp query blocks (exact dK/dV) and -> flat query blocks (block-mean gradients)
     st = hip_status(prism::launch_transpose_csr(sel_offsets, sel_idx, nb, heads, cap, w.tcount, w.tr_offsets, w.tr_idx,
@@ -697,7 +734,7 @@ prism_status prism_routed_attn_bwd(const void* q, const void* k, const void* v, 
     if (st != PRISM_OK) return st;
     const prism::RouteGrad rg{flat, r.dkbar, r.dvbar};
     return exact_bwd(q, k, v, dout, lse, dq, dk, dv, dt, N, heads, d, ld, hs, block_offsets, nb, sel_offsets, sel_idx,
-                     cap, scale, w, &rg, stream);
+                     cap, scale, w, &rg, om, stream);
 }
 
 }  // extern "C"

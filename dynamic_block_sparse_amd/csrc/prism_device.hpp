@@ -120,6 +120,20 @@ __device__ __forceinline__ int64_t block_major_to_raster(int64_t p, const uint8_
     return (t * g.H + h) * g.W + w;
 }
 
+// Where the attention kernels write their output rows (and where the backward
+// reads O): the row at block-major position p goes to raster token pi(p) of the
+// grid, at element offset pi(p) * ld + h * hs, when zone_shape is set; with
+// zone_shape NULL it stays at p (ld and hs are then the inputs' strides).
+struct RowMap {
+    const uint8_t* zone_shape;
+    ZoneGrid g;
+    int64_t ld, hs;
+};
+__device__ __forceinline__ int64_t row_offset(const RowMap& m, int64_t p, int h) {
+    const int64_t r = m.zone_shape ? block_major_to_raster(p, m.zone_shape, m.g) : p;
+    return r * m.ld + static_cast<int64_t>(h) * m.hs;
+}
+
 // ---------------------------------------------------------------- direct global->LDS loads
 
 typedef __attribute__((address_space(1))) void gvoid_t;

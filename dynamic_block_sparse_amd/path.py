@@ -122,17 +122,27 @@ class PrismPath:
            self.scale, offsets, idx, cap, total, ws, logits=logits)
         return Selection(offsets, idx, total, cap, logits)
 
-    def forward(self, qp, kp, vp, sel, op=None, lse=None, h0=0):
+    def raster_layout(self, x):
+        """prism_raster_layout for a raster [N, heads', d] tensor x: attention
+        rows are written straight to raster order (the inverse permutation
+        applied in the kernels' epilogues)."""
+        zo = self.zone_order.data_ptr() if self.zone_order is not None else None
+        return P.PrismRasterLayout(self.T, self.H, self.W, self.zone_shape.data_ptr(), zo, x.stride(0), x.stride(1))
+
+    def forward(self, qp, kp, vp, sel, op=None, lse=None, h0=0, raster=False):
+        """raster: op is (or is allocated as) a raster [N, heads, d] tensor and
+        the kernels write O there directly."""
         hc = self.hc
         if op is None:
-            op = self.block_major_like(qp)
+            op = torch.empty_like(qp, memory_format=torch.contiguous_format) if raster else self.block_major_like(qp)
         if lse is None:
             lse = torch.empty((hc, self.N), dtype=torch.float32, device=self.device)
         ws = torch.empty(P.prism_workspace_size(P.OP_ATTN_FWD, self.N, hc, self.d, self.nb, sel.cap),
                          dtype=torch.uint8, device=self.device)
         q, k, v, o = (x[:, h0:h0 + hc] for x in (qp, kp, vp, op))
         P.prism_sparse_attn_fwd(q, k, v, o, lse, self.N, hc, self.d, q.stride(0), q.stride(1), self.block_offsets,
-                                self.nb, sel.offsets, sel.idx, sel.cap, self.scale, ws=ws)
+                                self.nb, sel.offsets, sel.idx, sel.cap, self.scale, ws=ws,
+                                layout=self.raster_layout(op) if raster else None)
         return op, lse
 
     def route(self, sel, flat_ratio, want_sharpness=False):
@@ -169,36 +179,43 @@ class PrismPath:
                                 self.block_offsets, self.nb, sel.offsets, sel.idx, sel.cap, flat, self.scale, ws)
         return dq, dk, dv
 
-    def backward(self, qp, kp, vp, op, dop, lse, sel, grads=None, h0=0):
+    def backward(self, qp, kp, vp, op, dop, lse, sel, grads=None, h0=0, raster=False):
+        """raster: op and the gradients are raster [N, heads, d] tensors with
+        one set of strides (the kernels read O and write dQ, dK, dV there)."""
         hc = self.hc
         if grads is None:
-            grads = tuple(self.block_major_like(qp) for _ in range(3))
+            grads = tuple((torch.empty_like(qp, memory_format=torch.contiguous_format) if raster
+                           else self.block_major_like(qp)) for _ in range(3))
         dq, dk, dv = grads
+        if raster and any(t.stride() != op.stride() for t in grads):
+            raise ValueError("raster O and gradients must share their strides")
         ws = torch.empty(P.prism_workspace_size(P.OP_ATTN_BWD, self.N, hc, self.d, self.nb, sel.cap),
                          dtype=torch.uint8, device=self.device)
         q, k, v, o, do, gq, gk, gv = (x[:, h0:h0 + hc] for x in (qp, kp, vp, op, dop, dq, dk, dv))
         P.prism_sparse_attn_bwd(q, k, v, o, do, lse, gq, gk, gv, self.N, hc, self.d, q.stride(0), q.stride(1),
-                                self.block_offsets, self.nb, sel.offsets, sel.idx, sel.cap, self.scale, ws)
+                                self.block_offsets, self.nb, sel.offsets, sel.idx, sel.cap, self.scale, ws,
+                                layout=self.raster_layout(op) if raster else None)
         return dq, dk, dv
 
     # -------------------------------------------------------------- whole step
     def step(self, q, k, v, a, do=None):
         """Shapes, permutation, selection, forward (and backward when `do` is
-        given), inverse permutation.  Returns raster-order results."""
+        given), with the outputs written straight to raster order.  Returns
+        raster-order results."""
         self.shapes(v, a)
         qp, kp, vp = self.permute(q), self.permute(k), self.permute(v)
         dop = self.permute(do) if do is not None else None
-        op = self.block_major_like(qp)
-        grads = tuple(self.block_major_like(qp) for _ in range(3)) if do is not None else None
+        op = torch.empty_like(q)
+        grads = tuple(torch.empty_like(q) for _ in range(3)) if do is not None else None
         lses, sels = [], []
         for h0 in range(0, self.heads, self.hc):
             sel = self.select(qp, kp, h0)
-            _, lse = self.forward(qp, kp, vp, sel, op=op, h0=h0)
+            _, lse = self.forward(qp, kp, vp, sel, op=op, h0=h0, raster=True)
             if do is not None:
-                self.backward(qp, kp, vp, op, dop, lse, sel, grads=grads, h0=h0)
+                self.backward(qp, kp, vp, op, dop, lse, sel, grads=grads, h0=h0, raster=True)
             lses.append(lse)
             sels.append(sel)
-        out = {"o": self.permute(op, inverse=True), "lse_block_major": torch.cat(lses, 0), "selections": sels}
+        out = {"o": op, "lse_block_major": torch.cat(lses, 0), "selections": sels}
         if do is not None:
-            out["dq"], out["dk"], out["dv"] = (self.permute(g, inverse=True) for g in grads)
+            out["dq"], out["dk"], out["dv"] = grads
         return out

@@ -36,6 +36,12 @@ class PrismShapeParams(C.Structure):
     _fields_ = [("tau128", C.c_double), ("tau256", C.c_double), ("eps", C.c_double)]
 
 
+class PrismRasterLayout(C.Structure):
+    """prism_raster_layout: attention outputs written straight to raster order."""
+    _fields_ = [("T", C.c_int32), ("H", C.c_int32), ("W", C.c_int32), ("zone_shape", C.c_void_p),
+                ("zone_order", C.c_void_p), ("ld", C.c_int64), ("hs", C.c_int64)]
+
+
 class PrismError(RuntimeError):
     def __init__(self, status, message):
         super().__init__(f"{STATUS.get(status, status)}: {message}")
@@ -54,9 +60,10 @@ _lib.prism_select.argtypes = [_vp, _vp, _i32, _i64, _i32, _i32, _i64, _i64, _vp,
                               _i64, _vp, _vp, _vp, _sz, _vp]
 _lib.prism_select_subblock.argtypes = _lib.prism_select.argtypes
 _lib.prism_sparse_attn_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i64, _i64, _vp, _i32, _vp,
-                                       _vp, _i64, _f32, _vp, _sz, _vp]
+                                       _vp, _i64, _f32, C.POINTER(PrismRasterLayout), _vp, _sz, _vp]
 _lib.prism_sparse_attn_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i64,
-                                       _i64, _vp, _i32, _vp, _vp, _i64, _f32, _vp, _sz, _vp]
+                                       _i64, _vp, _i32, _vp, _vp, _i64, _f32, C.POINTER(PrismRasterLayout), _vp, _sz,
+                                       _vp]
 _lib.prism_audio_norm_map.argtypes = [_vp, _i32, _i64, _i64, _i64, _vp, _vp, _vp, _sz, _vp]
 _lib.prism_flat_route.argtypes = [_vp, _i32, _i32, _f64, _vp, _vp, _vp, _sz, _vp]
 _lib.prism_routed_attn_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i64, _i64, _vp, _i32, _vp,
@@ -191,11 +198,12 @@ def prism_select_subblock(q, k, N, heads, d, ld, hs, block_offsets, nb, top_k, t
 
 
 def prism_sparse_attn_fwd(q, k, v, o, lse, N, heads, d, ld, hs, block_offsets, nb, sel_offsets, sel_idx, cap, scale,
-                          ws=None, stream=None, dtype=None):
+                          ws=None, stream=None, dtype=None, layout=None):
+    """layout: None (o block-major with q's strides) or a PrismRasterLayout."""
     st = _lib.prism_sparse_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _dt(q) if dtype is None else dtype,
                                     N, heads, d, ld, hs, _ptr(block_offsets), nb, _ptr(sel_offsets), _ptr(sel_idx), cap,
-                                    float(scale), _ptr(ws), ws.numel() * ws.element_size() if ws is not None else 0,
-                                    _stream(stream))
+                                    float(scale), C.byref(layout) if layout is not None else None, _ptr(ws),
+                                    ws.numel() * ws.element_size() if ws is not None else 0, _stream(stream))
     _check(st)
 
 
@@ -225,10 +233,11 @@ def prism_routed_attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, N, heads, d, ld, hs
 
 
 def prism_sparse_attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, N, heads, d, ld, hs, block_offsets, nb, sel_offsets,
-                          sel_idx, cap, scale, ws, stream=None, dtype=None):
+                          sel_idx, cap, scale, ws, stream=None, dtype=None, layout=None):
+    """layout: None (o, dq, dk, dv block-major with q's strides) or a PrismRasterLayout."""
     st = _lib.prism_sparse_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk),
                                     _ptr(dv), _dt(q) if dtype is None else dtype, N, heads, d, ld, hs,
                                     _ptr(block_offsets), nb, _ptr(sel_offsets), _ptr(sel_idx), cap, float(scale),
-                                    _ptr(ws), ws.numel() * ws.element_size() if ws is not None else 0,
-                                    _stream(stream))
+                                    C.byref(layout) if layout is not None else None, _ptr(ws),
+                                    ws.numel() * ws.element_size() if ws is not None else 0, _stream(stream))
     _check(st)

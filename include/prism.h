@@ -257,17 +257,36 @@ prism_status prism_select_subblock(const void* q, const void* k, prism_dtype dt,
                                    void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * Raster placement of attention outputs: the inverse of the block-major
+ * permutation applied as the rows are written, instead of a separate
+ * prism_block_permute(..., inverse = 1) pass.  The row at block-major
+ * position p goes to raster token pi(p) of the T x H x W grid laid out by
+ * zone_shape (and zone_order), at element offset pi(p) * ld + h * hs from the
+ * output pointer.  ld > 0 and hs >= 0 are multiples of 16 bytes in elements.
+ */
+typedef struct {
+    int32_t T, H, W;              /* grid of prism_zone_shapes; T*H*W must equal N */
+    const uint8_t* zone_shape;    /* device, from prism_zone_shapes */
+    const int32_t* zone_order;    /* device zone order given to prism_zone_shapes, or NULL */
+    int64_t ld, hs;               /* token and head strides of the raster tensors, elements */
+} prism_raster_layout;
+
+/*
  * prism_sparse_attn_fwd - exact attention restricted to the selected key blocks
  * (reading guide, "Phương pháp" §3: online-softmax attention over S_i only).
  * Non-causal, no dropout, no bias.
  *
  *   q, k, v        block-major [N, heads, d]
- *   o              out block-major [N, heads, d], same dtype/strides
- *   lse            out [heads, N] fp32 natural-log log-sum-exp of the scaled scores
+ *   o              out [N, heads, d], same dtype: block-major with q's strides when
+ *                  `out` is NULL, else raster as `out` describes
+ *   lse            out [heads, N] fp32 natural-log log-sum-exp of the scaled scores,
+ *                  indexed by block-major position in either case
  *   sel_offsets, sel_idx, cap  the CSR written by prism_select
  *   scale          softmax scale, finite and > 0 (1/sqrt(d)); PRISM_E_ARG otherwise
  *   block_offsets  must be the offsets written by prism_zone_shapes for the same
  *                  grid (every block a whole number of 64-token tiles)
+ *   out            NULL or the raster placement of o (PRISM_E_GRID / PRISM_E_ARG /
+ *                  PRISM_E_UNSUPPORTED for a bad grid, token count or stride)
  *   ws, ws_bytes   prism_workspace_size(PRISM_OP_ATTN_FWD, ...) bytes: the order in
  *                  which the query tiles are visited (grouped by first selected
  *                  block, which shares key tiles in L2); PRISM_E_WORKSPACE if short
@@ -280,7 +299,8 @@ prism_status prism_sparse_attn_fwd(const void* q, const void* k, const void* v, 
                                    int64_t ld, int64_t hs,
                                    const int32_t* block_offsets, int32_t nb,
                                    const int32_t* sel_offsets, const int32_t* sel_idx, int64_t cap,
-                                   float scale, void* ws, size_t ws_bytes, hipStream_t stream);
+                                   float scale, const prism_raster_layout* out,
+                                   void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * prism_sparse_attn_bwd - gradient of prism_sparse_attn_fwd with respect to
@@ -289,9 +309,14 @@ prism_status prism_sparse_attn_fwd(const void* q, const void* k, const void* v, 
  * masked softmax: P = exp(scale*q.k - lse), dV = P^T dO, dP = dO V^T,
  * dS = P (dP - rowsum(dO * O)), dQ = scale dS K, dK = scale dS^T Q.
  *
- *   o, dout        forward output and upstream gradient (block-major)
+ *   o              forward output: block-major with q's strides, or raster as `io`
+ *                  describes
+ *   dout           upstream gradient, block-major
  *   lse            forward log-sum-exp
- *   dq, dk, dv     out block-major, same dtype/strides (fully overwritten)
+ *   dq, dk, dv     out, same dtype, fully overwritten: block-major with q's strides,
+ *                  or raster as `io` describes
+ *   io             NULL or the raster placement of o, dq, dk and dv (checks as in
+ *                  prism_sparse_attn_fwd)
  *   ws, ws_bytes   prism_workspace_size(PRISM_OP_ATTN_BWD, ...) bytes: row sums,
  *                  the transposed selection and the dQ tile visiting order
  * Deterministic: every output element is accumulated in a fixed order.
@@ -303,7 +328,8 @@ prism_status prism_sparse_attn_bwd(const void* q, const void* k, const void* v, 
                                    int64_t ld, int64_t hs,
                                    const int32_t* block_offsets, int32_t nb,
                                    const int32_t* sel_offsets, const int32_t* sel_idx, int64_t cap,
-                                   float scale, void* ws, size_t ws_bytes, hipStream_t stream);
+                                   float scale, const prism_raster_layout* io,
+                                   void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * prism_flat_route - sharpness routing of query blocks (next row after the

@@ -186,26 +186,40 @@ def test_select_subblock_rejects():
 
 
 def test_attention_rejects():
+    import ctypes
     lib, P = _lib()
     N, heads, d, nb = 2048, 2, 128, 24
     cap = nb * nb
     fneed = P.prism_workspace_size(P.OP_ATTN_FWD, N, heads, d, nb, cap)
     assert fneed >= 4 * heads * (N // 64)          # at least the tile order
-    fwd = lambda q=A, dt=1, d=d, o=Cc, ws=B, wsb=fneed: lib.prism_sparse_attn_fwd(
-        q, B, Cc, o, A, dt, N, heads, d, 256, 128, B, nb, Cc, A, cap, 0.088, ws, wsb, None)
+    good = P.PrismRasterLayout(8, 16, 16, Cc, None, heads * d, d)
+    fwd = lambda q=A, dt=1, d=d, o=Cc, ws=B, wsb=fneed, lay=None: lib.prism_sparse_attn_fwd(
+        q, B, Cc, o, A, dt, N, heads, d, 256, 128, B, nb, Cc, A, cap, 0.088,
+        ctypes.byref(lay) if lay is not None else None, ws, wsb, None)
     assert fwd(dt=2) == 3
     assert fwd(d=32) == 4
     assert fwd(q=None) == 1
     assert fwd(o=Cc + 8) == 4                      # misaligned
     assert fwd(ws=None) == 5
     assert fwd(wsb=fneed - 16) == 5
+    # raster placement of the outputs: grid, token count, zone shapes, strides
+    assert fwd(lay=P.PrismRasterLayout(8, 16, 12, Cc, None, heads * d, d)) == 2     # W not a multiple of 8
+    assert fwd(lay=P.PrismRasterLayout(8, 16, 8, Cc, None, heads * d, d)) == 1      # 1024 tokens, not N
+    assert fwd(lay=P.PrismRasterLayout(8, 16, 16, None, None, heads * d, d)) == 1   # no zone shapes
+    assert fwd(lay=P.PrismRasterLayout(8, 16, 16, Cc, None, heads * d + 4, d)) == 4  # 8-byte stride (bf16)
+    assert fwd(lay=P.PrismRasterLayout(8, 16, 16, Cc, None, 0, d)) == 4
+    assert fwd(lay=P.PrismRasterLayout(8, 16, 16, Cc, None, heads * d, -8)) == 4
+    assert fwd(lay=good, ws=None) == 5             # a valid layout passes its checks
     need = P.prism_workspace_size(P.OP_ATTN_BWD, N, heads, d, nb, cap)
     assert need > 0
-    bwd = lambda ws=A, wsb=need, dq=A: lib.prism_sparse_attn_bwd(A, B, Cc, A, B, Cc, dq, B, Cc, 1, N, heads, d, 256,
-                                                                 128, A, nb, B, Cc, cap, 0.088, ws, wsb, None)
+    bwd = lambda ws=A, wsb=need, dq=A, lay=None: lib.prism_sparse_attn_bwd(
+        A, B, Cc, A, B, Cc, dq, B, Cc, 1, N, heads, d, 256, 128, A, nb, B, Cc, cap, 0.088,
+        ctypes.byref(lay) if lay is not None else None, ws, wsb, None)
     assert bwd(ws=None) == 5
     assert bwd(wsb=need - 16) == 5
     assert bwd(dq=None) == 1
+    assert bwd(lay=P.PrismRasterLayout(16, 16, 16, Cc, None, heads * d, d)) == 1     # 4096 tokens, not N
+    assert bwd(lay=good, ws=None) == 5
 
 
 def test_workspace_sizes_grow_with_the_problem():
