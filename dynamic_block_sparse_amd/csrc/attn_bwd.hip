@@ -17,7 +17,9 @@ namespace prism {
 //   S = Q K^T, P = exp2(S - lse), dP = dO V^T, dS = P (dP - D),
 //   dV^T += dO^T P, dK^T += Q^T dS
 // Each output element is accumulated by one lane in a fixed order: the
-// backward is deterministic.
+// backward is deterministic.  dQ, dK and dV rows go to their block-major
+// position or, through the RowMap, to their raster token (where the row-dot
+// pass also reads O).
 
 // dQ keeps one K and one V tile in LDS and fits 256 registers, so two waves
 // share each SIMD (measured at 2K: 82 ms against 100 ms double-buffered at one

@@ -25,6 +25,9 @@ namespace prism {
 // ms, against 79 ms with double-buffered K and V at one wave per SIMD.)
 //
 // The scores run at raised wave priority, the softmax at the default one.
+// P enters P V rounded to bf16 and O is divided by the sum of those rounded
+// values; the log-sum-exp keeps the exact fp32 sum.  Output rows go to their
+// block-major position or, through the RowMap, to their raster token.
 //
 // Query tiles are taken in the visiting order built by launch_tile_order
 // (tiles grouped by their first selected key block): order[h * ntiles + j] is
