@@ -473,6 +473,32 @@ def measure_subblock(cfg, path, qp, kp, vp, dop=None, reps=3):
     return res
 
 
+
+def measure_reuse(cfg, x, path, reps=2):
+    """Selection reuse across diffusion steps: PrismPath.step with a fresh
+    selection against a step that reuses the cached zone shapes, layout and
+    selected sets (zone statistics, shapes and selection skipped), on the
+    workload's inputs, timed with HIP events outside the measured step."""
+    print("[bench] selection reuse", file=sys.stderr, flush=True)
+    args = (x["q"], x["k"], x["v"], x["a"], x.get("do"))
+
+    def timed(reuse):
+        path.step(*args, reuse=reuse)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            path.step(*args, reuse=reuse)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    fresh = timed(False)
+    reused = timed(True)
+    return {"fresh_step_ms": round(fresh, 3), "reused_step_ms": round(reused, 3),
+            "saved_per_reused_step_ms": round(fresh - reused, 3)}
+
+
 def main():
     args = parse()
     if args.profile:
@@ -621,6 +647,8 @@ def main():
                                "f3_routed_forward": measure_routed(path, qp, kp, vp, args.flat_ratio, dop),
                                "f4_hilbert_zone_order": measure_zone_order(cfg, x, path, qp, kp, vp, dop),
                                "f4_subblock_scoring": measure_subblock(cfg, path, qp, kp, vp, dop)}
+        if ms_step < 5000:   # whole extra steps: skipped for the long clip (about 20 s a step)
+            result["next_rows"]["f2_selection_reuse"] = measure_reuse(cfg, x, path)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(cfg, x, path.zone_shape.cpu().numpy(), args.cpu_seconds)

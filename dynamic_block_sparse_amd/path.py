@@ -7,6 +7,7 @@ kernels.
 """
 from __future__ import annotations
 
+import math
 from dataclasses import dataclass
 
 import torch
@@ -21,6 +22,30 @@ class Selection:
     total: torch.Tensor       # int64 [hc]
     cap: int
     logits: torch.Tensor | None
+
+
+def sparsity_schedule(step, steps, first, last):
+    """(top_k, top_p) for diffusion step `step` of `steps` (0-based).
+
+    Next row after the exact path (DFSAttn article, adaptive sparsity: early,
+    noisy steps look at almost every block; sparsity grows as the sample
+    sharpens).  The article gives no schedule; this reading moves linearly in
+    the step index from `first` = (k0, p0), the permissive end, to `last` =
+    (k1, p1), the workload's own values, with k rounded to the nearest integer.
+    """
+    if steps <= 0 or not 0 <= step < steps:
+        raise ValueError("need 0 <= step < steps")
+    f = step / (steps - 1) if steps > 1 else 1.0
+    (k0, p0), (k1, p1) = first, last
+    return int(math.floor(k0 + (k1 - k0) * f + 0.5)), p0 + (p1 - p0) * f
+
+
+def reuses_selection(step, refresh_every):
+    """True when step `step` reuses the previous step's selection (a fresh
+    selection every `refresh_every` steps, the first step always fresh)."""
+    if refresh_every < 1:
+        raise ValueError("refresh_every must be at least 1")
+    return step % refresh_every != 0
 
 
 class PrismPath:
@@ -55,6 +80,7 @@ class PrismPath:
         self.nb_dev = torch.empty(1, dtype=torch.int32, device=self.device)
         self.zone_stats = torch.empty(self.nZ * P.ZS_STRIDE, dtype=torch.float64, device=self.device)
         self.nb = None
+        self._reuse = None   # selections of the last fresh step, for step(..., reuse=True)
         if zone_order not in ("raster", "hilbert"):
             raise ValueError("zone_order must be 'raster' or 'hilbert'")
         self.zone_order = None
@@ -198,23 +224,35 @@ class PrismPath:
         return dq, dk, dv
 
     # -------------------------------------------------------------- whole step
-    def step(self, q, k, v, a, do=None):
+    def step(self, q, k, v, a, do=None, reuse=False):
         """Shapes, permutation, selection, forward (and backward when `do` is
         given), with the outputs written straight to raster order.  Returns
-        raster-order results."""
-        self.shapes(v, a)
+        raster-order results.
+
+        reuse: keep the zone shapes, block layout and selected sets of the
+        last step run without reuse (selection reuse across diffusion steps,
+        DFSAttn article, cached masks): zone statistics, shapes and selection
+        are skipped, and the new tensors are permuted with the cached layout
+        and attend over the cached sets.  The sets refer to blocks of that
+        layout, so the layout is reused with them."""
+        if reuse and self._reuse is None:
+            raise ValueError("no selection to reuse: run a step without reuse first")
+        if not reuse:
+            self.shapes(v, a)
         qp, kp, vp = self.permute(q), self.permute(k), self.permute(v)
         dop = self.permute(do) if do is not None else None
         op = torch.empty_like(q)
         grads = tuple(torch.empty_like(q) for _ in range(3)) if do is not None else None
         lses, sels = [], []
-        for h0 in range(0, self.heads, self.hc):
-            sel = self.select(qp, kp, h0)
+        for g, h0 in enumerate(range(0, self.heads, self.hc)):
+            sel = self._reuse[g] if reuse else self.select(qp, kp, h0)
             _, lse = self.forward(qp, kp, vp, sel, op=op, h0=h0, raster=True)
             if do is not None:
                 self.backward(qp, kp, vp, op, dop, lse, sel, grads=grads, h0=h0, raster=True)
             lses.append(lse)
             sels.append(sel)
+        if not reuse:
+            self._reuse = sels
         out = {"o": op, "lse_block_major": torch.cat(lses, 0), "selections": sels}
         if do is not None:
             out["dq"], out["dk"], out["dv"] = grads
