@@ -524,6 +524,9 @@ select_reg_kernel(const float* __restrict__ logits, int nb, int top_k, double to
     __shared__ unsigned long long red64[kSelThreads / kWave];
     __shared__ uint32_t rc[2][kSelThreads / kWave];
     __shared__ unsigned long long rm[2][kSelThreads / kWave];
+    __shared__ uint32_t ckey[kSelThreads];            // compacted undecided keys
+    __shared__ unsigned long long cms[kSelThreads];   // and their masses
+    __shared__ uint32_t ccnt, cres;
     const int i = blockIdx.x, h = blockIdx.y;
     const int64_t row = static_cast<int64_t>(h) * nb + i;
     const float* __restrict__ L = logits + row * nb;
@@ -558,37 +561,109 @@ select_reg_kernel(const float* __restrict__ logits, int nb, int top_k, double to
         jlim = -1;
     } else {
         int slot = 0;
-        // 1) tk = the largest key with count(key >= tk) >= kk: a count-only bisection
-        uint32_t lo = kmin, hi = kmax + 1u;   // count >= kk at lo, < kk at hi
-        while (hi - lo > 1u) {
-            const uint32_t mid = lo + (hi - lo) / 2u;
-            uint32_t c = 0;
+        // Largest u in [lo, hi) whose suffix (keys >= u) satisfies the count
+        // condition (by_count) or the mass condition, given that it holds at lo
+        // and fails at hi.  Each step of the bisection sums over the whole row;
+        // once at most kSelThreads keys lie in [lo, hi), they are compacted into
+        // LDS and wave 0 finishes the search on them alone, adding the exact
+        // (count, mass) of the keys at or above hi.  The sums are integers, so
+        // the result does not depend on the order of the compacted keys.
+        auto finish = [&](uint32_t lo, uint32_t hi, uint32_t bc, unsigned long long bm, bool by_count) -> uint32_t {
+            if (threadIdx.x == 0) ccnt = 0u;
+            __syncthreads();
 #pragma unroll
-            for (int e = 0; e < E; ++e) c += key[e] >= mid ? 1u : 0u;
-            c = block_sum_c(c, rc, slot);
-            if (c >= kk) lo = mid;
-            else hi = mid;
-        }
+            for (int e = 0; e < E; ++e)
+                if (key[e] >= lo && key[e] < hi) {
+                    const uint32_t at = atomicAdd(&ccnt, 1u);
+                    ckey[at] = key[e];
+                    cms[at] = ms[e];
+                }
+            __syncthreads();
+            if (threadIdx.x < kWave) {
+                constexpr int CPL = kSelThreads / kWave;   // candidates per lane
+                const uint32_t n = ccnt;
+                uint32_t ck[CPL];
+                unsigned long long cm[CPL];
+#pragma unroll
+                for (int x = 0; x < CPL; ++x) {
+                    const uint32_t j = threadIdx.x + kWave * x;
+                    ck[x] = j < n ? ckey[j] : 0u;   // key 0 lies below every finite score's key
+                    cm[x] = j < n ? cms[j] : 0ull;
+                }
+                while (hi - lo > 1u) {
+                    const uint32_t mid = lo + (hi - lo) / 2u;
+                    bool ok;
+                    if (by_count) {
+                        uint32_t c = 0;
+#pragma unroll
+                        for (int x = 0; x < CPL; ++x) c += ck[x] >= mid ? 1u : 0u;
+                        ok = bc + wave_sum_dpp(c) >= kk;
+                    } else {
+                        unsigned long long m = 0;
+#pragma unroll
+                        for (int x = 0; x < CPL; ++x) m += ck[x] >= mid ? cm[x] : 0ull;
+                        ok = static_cast<double>(bm + wave_sum_dpp(m)) >= target;
+                    }
+                    if (ok) lo = mid;
+                    else hi = mid;
+                }
+                if (threadIdx.x == 0) cres = lo;
+            }
+            __syncthreads();
+            return cres;
+        };
+        // c_lo = count(key >= lo) and c_hi = count(key >= hi) are carried along,
+        // so the number of keys still undecided is known without another pass;
+        // m_hi = mass(key >= hi) when the mass condition is searched.
+        auto search = [&](uint32_t lo, uint32_t hi, uint32_t c_lo, uint32_t c_hi, unsigned long long m_hi,
+                          bool by_count) -> uint32_t {
+            while (hi - lo > 1u) {
+                if (c_lo - c_hi <= static_cast<uint32_t>(kSelThreads)) return finish(lo, hi, c_hi, m_hi, by_count);
+                const uint32_t mid = lo + (hi - lo) / 2u;
+                uint32_t c = 0;
+                unsigned long long m = 0;
+                bool ok;
+                if (by_count) {
+#pragma unroll
+                    for (int e = 0; e < E; ++e) c += key[e] >= mid ? 1u : 0u;
+                    c = block_sum_c(c, rc, slot);
+                    ok = c >= kk;
+                } else {
+#pragma unroll
+                    for (int e = 0; e < E; ++e) {
+                        c += key[e] >= mid ? 1u : 0u;
+                        m += key[e] >= mid ? ms[e] : 0ull;
+                    }
+                    block_sum_cm(c, m, rc, rm, slot);
+                    ok = static_cast<double>(m) >= target;
+                }
+                if (ok) {
+                    lo = mid;
+                    c_lo = c;
+                } else {
+                    hi = mid;
+                    c_hi = c;
+                    m_hi = m;
+                }
+            }
+            return lo;
+        };
+        // 1) tk = the largest key with count(key >= tk) >= kk: count condition
+        //    (all nb keys lie at or above kmin, none above kmax)
+        uint32_t lo = search(kmin, kmax + 1u, static_cast<uint32_t>(nb), 0u, 0ull, true);
         // 2) if the blocks at or above tk already hold p Z, the boundary is tk;
         // otherwise it lies below tk, where the count condition always holds,
-        //    and a mass-only bisection finds the largest u with mass(key >= u) >= p Z
+        //    and the mass condition finds the largest u with mass(key >= u) >= p Z
+        uint32_t ck_ = 0;
         unsigned long long mk = 0;
 #pragma unroll
-        for (int e = 0; e < E; ++e) mk += key[e] >= lo ? ms[e] : 0ull;
-        mk = block_sum_m(mk, rm, slot);
-        if (!(static_cast<double>(mk) >= target)) {
-            hi = lo;                           // mass fails at tk
-            lo = kmin;                         // and holds at the smallest key (all of Z)
-            while (hi - lo > 1u) {
-                const uint32_t mid = lo + (hi - lo) / 2u;
-                unsigned long long m = 0;
-#pragma unroll
-                for (int e = 0; e < E; ++e) m += key[e] >= mid ? ms[e] : 0ull;
-                m = block_sum_m(m, rm, slot);
-                if (static_cast<double>(m) >= target) lo = mid;
-                else hi = mid;
-            }
+        for (int e = 0; e < E; ++e) {
+            ck_ += key[e] >= lo ? 1u : 0u;
+            mk += key[e] >= lo ? ms[e] : 0ull;
         }
+        block_sum_cm(ck_, mk, rc, rm, slot);
+        if (!(static_cast<double>(mk) >= target))   // holds at kmin (all of Z), fails at tk
+            lo = search(kmin, lo, static_cast<uint32_t>(nb), ck_, mk, false);
         thr = lo;
         // blocks strictly above the boundary key, and the ties at it
         uint32_t cabove = 0, ceq = 0;
