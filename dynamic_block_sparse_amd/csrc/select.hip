@@ -910,15 +910,19 @@ order_count_kernel(const int32_t* __restrict__ sel_offsets, const int32_t* __res
 // key in ascending tile order (a stable counting sort, so the visiting order is
 // deterministic and keeps spatial order inside a key).  One workgroup of
 // kOrderChunk threads per (range r, head h) pair, i.e. per unit; its tiles are
-// ranked in chunks of kOrderChunk: a tile's slot is the number of earlier tiles
+// placed in chunks of kOrderChunk: a tile's slot is the number of earlier tiles
 // of its key in the chunk plus cursor[unit][key], the count left by earlier
-// chunks.  tkey[h * ntiles + t] is tile t's key (written by order_count_kernel).
+// chunks.  The in-chunk rank comes from a bitonic sort of (key, position)
+// pairs in LDS: in the sorted chunk a tile's rank is its distance from the
+// first entry of its key, found by binary search.  tkey[h * ntiles + t] is
+// tile t's key (written by order_count_kernel).
 constexpr int kOrderChunk = 1024;
 __global__ void __launch_bounds__(kOrderChunk)
 order_fill_kernel(const int32_t* __restrict__ tkey, int nb, int64_t ntiles, int64_t seg,
                   const int32_t* __restrict__ start, int32_t* __restrict__ cursor, int32_t* __restrict__ order) {
-    __shared__ int4 keys4[kOrderChunk / 4];
-    int32_t* keys = reinterpret_cast<int32_t*>(keys4);
+    __shared__ unsigned long long sk[kOrderChunk];   // (key << 32) | chunk position, sorted in place
+    __shared__ int32_t rank_of[kOrderChunk];
+    __shared__ uint8_t last_of[kOrderChunk];
     const int r = blockIdx.x, h = blockIdx.y;
     const int64_t lo = max(static_cast<int64_t>(h) * ntiles, static_cast<int64_t>(r) * seg);
     const int64_t hi = min(static_cast<int64_t>(h + 1) * ntiles, static_cast<int64_t>(r + 1) * seg);
@@ -931,29 +935,47 @@ order_fill_kernel(const int32_t* __restrict__ tkey, int nb, int64_t ntiles, int6
         const int64_t p = c0 + tid;   // launch position h * ntiles + t
         const bool live = p < hi;
         const int key = live ? tkey[p] : -1;
-        keys[tid] = key;
+        // dead positions sort after every key
+        sk[tid] = (static_cast<unsigned long long>(live ? static_cast<uint32_t>(key) : 0xFFFFFFFFu) << 32) |
+                  static_cast<uint32_t>(tid);
         __syncthreads();
-        // earlier tiles of the same key in this chunk, and whether a later one exists
-        int rank = 0, after = 0;
-#pragma unroll 8
-        for (int j4 = 0; j4 < kOrderChunk / 4; ++j4) {
-            const int4 kk = keys4[j4];
-            const int j = 4 * j4;
-            const int m[4] = {kk.x == key, kk.y == key, kk.z == key, kk.w == key};
-#pragma unroll
-            for (int x = 0; x < 4; ++x) {
-                rank += (j + x < tid) ? m[x] : 0;
-                after |= (j + x > tid) ? m[x] : 0;
+        for (int size = 2; size <= kOrderChunk; size <<= 1)
+            for (int stride = size >> 1; stride > 0; stride >>= 1) {
+                const int j = tid ^ stride;
+                if (j > tid) {
+                    const unsigned long long x = sk[tid], y = sk[j];
+                    if ((x > y) == ((tid & size) == 0)) {
+                        sk[tid] = y;
+                        sk[j] = x;
+                    }
+                }
+                __syncthreads();
             }
+        {
+            // sorted position tid: rank = distance from the first entry of its key
+            const unsigned long long v = sk[tid];
+            const uint32_t vk = static_cast<uint32_t>(v >> 32);
+            int a = 0, b = tid;   // first position whose key is vk lies in [a, b]
+            while (a < b) {
+                const int m = (a + b) >> 1;
+                if (static_cast<uint32_t>(sk[m] >> 32) < vk) a = m + 1;
+                else b = m;
+            }
+            const int pos = static_cast<int>(v & 0xFFFFFFFFu);
+            rank_of[pos] = tid - a;
+            last_of[pos] = tid == kOrderChunk - 1 || static_cast<uint32_t>(sk[tid + 1] >> 32) != vk;
         }
+        __syncthreads();
+        const int rank = rank_of[tid];
+        const bool last = last_of[tid] != 0;
         int cur = 0;
         if (live) {
             cur = cu[key];
             order[lo + st[key] + cur + rank] = static_cast<int32_t>(p - static_cast<int64_t>(h) * ntiles);
         }
         __syncthreads();   // every tile of the chunk has read its key's count
-        if (live && !after) cu[key] = cur + rank + 1;
-        __syncthreads();   // counts updated before the next chunk reads them
+        if (live && last) cu[key] = cur + rank + 1;
+        __syncthreads();   // counts updated and LDS free before the next chunk
     }
 }
 
