@@ -314,15 +314,17 @@ def test_full_size_sampled(name, progress):
     np.testing.assert_array_equal(_np(qp[torch.from_numpy(rows).cuda()]), _np(xs["q"][torch.from_numpy(pi[rows]).cuda()]))
     sc = float(np.float32(1.0 / math.sqrt(cfg.d)))
     check_heads = list(range(nh)) if heads else sorted(rng.choice(cfg.heads, size=2, replace=False).tolist())
-    # NaN-filled outputs: every tile must be written, whatever order the tiles are visited in
-    op = path.block_major_like(qp).fill_(float("nan"))
-    grads = tuple(path.block_major_like(qp).fill_(float("nan")) for _ in range(3)) if cfg.backward else None
+    # the launch configuration the benchmark times: outputs written straight to
+    # raster order, head chunks as in the benchmark; NaN-filled, so every row
+    # must be written whatever order the tiles are visited in
+    op = torch.empty_like(xs["q"]).fill_(float("nan"))
+    grads = tuple(torch.empty_like(xs["q"]).fill_(float("nan")) for _ in range(3)) if cfg.backward else None
     sels, lses = {}, {}
     for h0 in range(0, nh, path.hc):
         sel = path.select(qp, kp, h0, want_logits=True)
-        _, lse = path.forward(qp, kp, vp, sel, op=op, h0=h0)
+        _, lse = path.forward(qp, kp, vp, sel, op=op, h0=h0, raster=True)
         if cfg.backward:
-            path.backward(qp, kp, vp, op, dop, lse, sel, grads=grads, h0=h0)
+            path.backward(qp, kp, vp, op, dop, lse, sel, grads=grads, h0=h0, raster=True)
         for hh in range(path.hc):
             sels[h0 + hh] = (sel, hh)
             lses[h0 + hh] = lse[hh]
@@ -330,6 +332,8 @@ def test_full_size_sampled(name, progress):
     progress(f"case {name}: GPU path done")
     for t in (op,) + (grads or ()):
         assert bool(torch.isfinite(t[:, :nh]).all())
+    pi_t = torch.from_numpy(pi).cuda()
+    bm = lambda t, a, b, h: _np(t[pi_t[a:b], h, :])   # block-major rows a..b-1 of a raster output
     for h in check_heads:
         sel, hh = sels[h]
         Qp, Kp, Vp = (orc.to_block_major(_np(t[:, h:h + 1, :]), pi) for t in (xs["q"], xs["k"], v_att))
@@ -353,7 +357,6 @@ def test_full_size_sampled(name, progress):
                 raise AssertionError(f"{name} head {h} row {i}: selection differs")
         # forward and dQ on sampled query blocks, dK/dV on sampled key blocks
         dOp = orc.to_block_major(_np(xs["do"][:, h:h + 1, :]), pi) if cfg.backward else None
-        Og = _np(op[:, h, :])
         lg = lses[h].cpu().numpy()
         errs = {"O": [], "dQ": [], "dK": [], "dV": []}
         # query blocks in seeded random order, up to 64, within an oracle budget
@@ -372,11 +375,11 @@ def test_full_size_sampled(name, progress):
         for n_done, i in enumerate(qb):
             s = ci[co[i]:co[i + 1]]
             o_ref, lse_ref = orc.attn_fwd_block(Qp, Kp, Vp, offs, s, i, 0, sc)
-            errs["O"].append((Og[offs[i]:offs[i + 1]], o_ref))
+            errs["O"].append((bm(op, offs[i], offs[i + 1], h), o_ref))
             np.testing.assert_allclose(lg[offs[i]:offs[i + 1]], lse_ref, atol=2e-3)
             if cfg.backward:
                 dq_ref = orc.attn_bwd_block(Qp, Kp, Vp, dOp, offs, s, i, 0, sc)[0]
-                errs["dQ"].append((_np(grads[0][offs[i]:offs[i + 1], h, :]), dq_ref))
+                errs["dQ"].append((bm(grads[0], offs[i], offs[i + 1], h), dq_ref))
             if n_done % 8 == 7:
                 progress(f"case {name} head {h}: {n_done + 1} query blocks checked")
         if cfg.backward:
@@ -396,8 +399,8 @@ def test_full_size_sampled(name, progress):
                 if spent + c > budget:
                     continue
                 dk_ref, dv_ref = orc.key_block_grads(Qp, Kp, Vp, dOp, offs, co, ci, j, 0, sc, rows=users)
-                errs["dK"].append((_np(grads[1][offs[j]:offs[j + 1], h, :]), dk_ref))
-                errs["dV"].append((_np(grads[2][offs[j]:offs[j + 1], h, :]), dv_ref))
+                errs["dK"].append((bm(grads[1], offs[j], offs[j + 1], h), dk_ref))
+                errs["dV"].append((bm(grads[2], offs[j], offs[j + 1], h), dv_ref))
                 spent += c
                 taken += 1
                 progress(f"case {name} head {h}: key block {j} ({len(users)} query blocks) checked")
