@@ -223,6 +223,10 @@ class PrismPath:
                                 layout=self.raster_layout(op) if raster else None)
         return dq, dk, dv
 
+    def release_selection(self):
+        """Drop the selections kept for step(..., reuse=True)."""
+        self._reuse = None
+
     # -------------------------------------------------------------- whole step
     def step(self, q, k, v, a, do=None, reuse=False):
         """Shapes, permutation, selection, forward (and backward when `do` is
@@ -234,7 +238,9 @@ class PrismPath:
         DFSAttn article, cached masks): zone statistics, shapes and selection
         are skipped, and the new tensors are permuted with the cached layout
         and attend over the cached sets.  The sets refer to blocks of that
-        layout, so the layout is reused with them."""
+        layout, so the layout is reused with them.  A step run without reuse
+        keeps a reference to its selections for that purpose (their CSR
+        buffers stay allocated); release_selection() drops it."""
         if reuse and self._reuse is None:
             raise ValueError("no selection to reuse: run a step without reuse first")
         if not reuse:

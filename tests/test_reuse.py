@@ -77,6 +77,9 @@ def test_reused_selection_matches_the_oracle_over_the_earlier_sets():
     torch.cuda.synchronize()
     assert out2["selections"][0] is out1["selections"][0]
     assert torch.equal(path.block_offsets[:path.nb + 1], offs_gpu)
+    path.release_selection()
+    with pytest.raises(ValueError):
+        path.step(x2["q"], x2["k"], x2["v"], x2["a"], x2["do"], reuse=True)
     # oracle: layout and sets from the first inputs, attention of the second ones over them
     zs = orc.zone_shapes(_np(x1["v"]).reshape(CFG.N, -1), _np(x1["a"]), CFG.T, CFG.H, CFG.W)
     assert not zs["near_tie"].any()
