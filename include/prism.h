@@ -360,7 +360,7 @@ prism_status prism_flat_route(const float* logits, int32_t heads, int32_t nb, do
  * block's selected set):
  *     O_q = sum_j B_j exp(s q.K_bar_j) V_bar_j / sum_j B_j exp(s q.K_bar_j),
  *     lse_q = log sum_j B_j exp(s q.K_bar_j).
- * Arguments as prism_sparse_attn_fwd, plus `flat` from prism_flat_route;
+ * Arguments as prism_sparse_attn_fwd without `out` (o is block-major), plus `flat` from prism_flat_route;
  * workspace prism_workspace_size(PRISM_OP_ROUTED_FWD, ...) bytes.  Block means
  * are float64 sums rounded once to fp32; the flat path computes in fp32.
  */
@@ -379,7 +379,7 @@ prism_status prism_routed_attn_fwd(const void* q, const void* k, const void* v, 
  *     dK_bar_j += scale dS_j q,   dV_bar_j += w_j dO_q,
  * and every token of key block j receives dK_bar_j / B_j and dV_bar_j / B_j
  * (the chain rule through the block means; the article gives no backward).
- * Arguments as prism_sparse_attn_bwd plus `flat`; workspace
+ * Arguments as prism_sparse_attn_bwd without `io` (o, dq, dk, dv block-major), plus `flat`; workspace
  * prism_workspace_size(PRISM_OP_ROUTED_BWD, ...) bytes.  Deterministic: the
  * block-mean gradients are summed per key block in a fixed order and added to
  * the exact dK/dV before rounding.
