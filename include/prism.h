@@ -262,7 +262,8 @@ prism_status prism_select_subblock(const void* q, const void* k, prism_dtype dt,
  * prism_block_permute(..., inverse = 1) pass.  The row at block-major
  * position p goes to raster token pi(p) of the T x H x W grid laid out by
  * zone_shape (and zone_order), at element offset pi(p) * ld + h * hs from the
- * output pointer.  ld > 0 and hs >= 0 are multiples of 16 bytes in elements.
+ * output pointer.  ld > 0 and hs >= 0 are multiples of 16 bytes in elements;
+ * the head regions of one output must not overlap each other (not checked).
  */
 typedef struct {
     int32_t T, H, W;              /* grid of prism_zone_shapes; T*H*W must equal N */
