@@ -45,7 +45,8 @@ FWD_KERNELS = dict(ORDER_KERNELS, attn_fwd_mfma_kernel=1)
 BWD_KERNELS = {"attn_bwd_dot_kernel": 1, "fill_i32_kernel": 2 + 2, "tr_count_kernel": 1, "csr_scan_kernel": 1 + 1,
                "tr_fill_kernel": 1, "tr_sort_kernel": 1, "order_count_kernel": 1, "order_fill_kernel": 1,
                "attn_dq_mfma_kernel": 1, "attn_dkdv_mfma_kernel": 1}
-PMC_REGEX = "attn_|permute_heads|tr_count|tr_fill|tr_sort|csr_scan|order_|fill_i32"
+PMC_REGEX = ("attn_|permute_heads|tr_count|tr_fill|tr_sort|csr_scan|order_|fill_i32|zone_profile|pool_kernel|"
+             "logits_kernel|select_reg|select_write")
 ATTN_REGEX = "attn_(fwd|dq|dkdv)_mfma"
 
 
@@ -273,6 +274,35 @@ def profile(args):
         fh.write(f"write_bytes_per_call: {write:.6g}\n")
         fh.write(f"bytes_per_call: {fetch + write:.6g}\n")
         fh.write(f"source_sha256: {source_hash()}\n")
+    # the bandwidth-bound stages from the same two passes: bytes per dispatch,
+    # counted (scaled as above) against algorithmic
+    nb_run = int(bench_line.get("config", {}).get("blocks", 0)) if bench_line else 0
+    C = cfg.heads * cfg.d
+    stage_alg = {"zone_profile": ("zone statistics: read V, the a map", cfg.N * C * es + 4 * cfg.N),
+                 "permute_heads": ("permutation of one tensor: read + write", 2 * cfg.N * C * es),
+                 "pool_kernel": ("block means: read Q and K", 2 * cfg.N * C * es),
+                 "logits_kernel": ("scores: write fp32 [heads, NB, NB]", cfg.heads * nb_run * nb_run * 4),
+                 "select_reg": ("selection: read the scores", cfg.heads * nb_run * nb_run * 4),
+                 "select_write": ("CSR write: read the scores", cfg.heads * nb_run * nb_run * 4)}
+    with open(os.path.join(out, f"stages_{args.config}_traffic.txt"), "w") as fh:
+        fh.write(f"# HBM-side traffic of the bandwidth-bound stages, {args.config} workload, from the same rocprofv3 "
+                 f"passes\n")
+        for ctr, show in pcmds.items():
+            fh.write(f"# {ctr} pass: {show}\n")
+        fh.write(f"# made by: python bench.py --profile {out} --config {args.config}\n")
+        fh.write("# bytes per dispatch: the counters (KiB) scaled as in the attention traffic summary\n\n")
+        fh.write(f"{'kernel':28s} {'dispatches':>10s} {'fetch_GB':>10s} {'write_GB':>10s} {'algorithmic_GB':>15s} "
+                 f"{'counted/alg':>12s}  work\n")
+        for key, (what, alg_b) in stage_alg.items():
+            f_v = [v for (_, k), v in res["FETCH_SIZE"] if key in k]
+            w_v = [v for (_, k), v in res["WRITE_SIZE"] if key in k]
+            if not f_v or not w_v:
+                continue
+            fb = sum(f_v) / len(f_v) * 1024 * scale["FETCH_SIZE"]
+            wb = sum(w_v) / len(w_v) * 1024 * scale["WRITE_SIZE"]
+            ratio = (fb + wb) / alg_b if alg_b else float("nan")
+            fh.write(f"{key:28s} {len(f_v):10d} {fb / 1e9:10.3f} {wb / 1e9:10.3f} {alg_b / 1e9:15.3f} {ratio:12.3f}  "
+                     f"{what}\n")
     # utilisation counters of the attention kernels, one pass per counter group
     groups = {"mfma_lds": ["MfmaUtil", "SQ_LDS_BANK_CONFLICT", "SQ_INSTS_LDS", "SQ_WAIT_INST_LDS"],
               "waits": ["SQ_WAVE_CYCLES", "SQ_WAIT_ANY", "SQ_ACTIVE_INST_ANY", "SQ_BUSY_CYCLES"],

@@ -104,13 +104,31 @@ typedef double d4_t __attribute__((ext_vector_type(4)));
 // tiles.  The pooled means are staged in LDS channel-major, 16 channels at a
 // time.  Each score is rounded once to fp32 after the scale (TOut = float), or
 // kept in float64 (TOut = double, the run-pair scores of sub-block scoring).
+//
+// Tiles are visited XCD-aware and grouped: the 1D grid is dealt to the 8 XCDs
+// in contiguous ranges, and inside a head kLGroup rows of query tiles sweep the
+// key tiles together, so each key tile's pooled means are read from L2 by the
+// kLGroup workgroups that use it while it is resident.  (In plain row order,
+// dealt round-robin, the 2K scores fetched 10.7 GB beyond L2 for 4.6 GB of
+// output.)
+constexpr int kLGroup = 8;
 template <int D, typename TOut>
 __global__ void __launch_bounds__(256, 2)
 logits_kernel(const double* __restrict__ pooled, int nb, int heads, double scale, TOut* __restrict__ logits) {
     __shared__ double Qs[kLC][kLT + 2];
     __shared__ double Ks[kLC][kLT + 2];
-    const int h = blockIdx.z;
-    const int i0 = blockIdx.y * kLT, j0 = blockIdx.x * kLT;
+    const int nt = (nb + kLT - 1) / kLT;
+    const int G = static_cast<int>(gridDim.x);
+    const int w = G % 8 ? static_cast<int>(blockIdx.x)
+                        : static_cast<int>(blockIdx.x % 8) * (G / 8) + static_cast<int>(blockIdx.x / 8);
+    const int h = w / (nt * nt);
+    const int u = w - h * nt * nt;
+    const int per_group = kLGroup * nt;
+    const int first = (u / per_group) * kLGroup;
+    const int gsize = min(nt - first, kLGroup);
+    const int ti = first + (u % per_group) % gsize;
+    const int tj = (u % per_group) / gsize;
+    const int i0 = ti * kLT, j0 = tj * kLT;
     const double* __restrict__ Qb = pooled + static_cast<int64_t>(h) * nb * D;
     const double* __restrict__ Kb = pooled + (static_cast<int64_t>(heads) + h) * nb * D;
     const int lane = threadIdx.x & (kWave - 1);
@@ -1007,7 +1025,8 @@ hipError_t launch_pool(const void* q, const void* k, bool bf16, int heads, int d
 
 template <typename TOut>
 hipError_t launch_scores(const double* pooled, int n, int heads, int d, float scale, TOut* out, hipStream_t s) {
-    const dim3 lg((n + kLT - 1) / kLT, (n + kLT - 1) / kLT, heads);
+    const int nt = (n + kLT - 1) / kLT;
+    const dim3 lg(static_cast<unsigned>(nt * nt * heads));
     if (d == 128)
         hipLaunchKernelGGL((logits_kernel<128, TOut>), lg, dim3(256), 0, s, pooled, n, heads,
                            static_cast<double>(scale), out);
