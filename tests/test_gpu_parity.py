@@ -412,3 +412,25 @@ def test_full_size_sampled(name, progress):
                 got = np.concatenate([p[0] for p in pairs])
                 want = np.concatenate([p[1] for p in pairs])
                 _assert_close(got, want, cfg.dtype, f"{name} head {h} {k}", grad=(k != "O"))
+
+
+def test_degenerate_zero_values_and_map():
+    """V and the audio map all zero: every zone is constant (each directional
+    ratio 1/3, the reading for a zero variance sum), O is exactly 0, and so are
+    dQ and dK (dP = dO V^T = 0 and D = rowsum(dO * O) = 0); dV = P^T dO is not."""
+    cfg = SMALL[1]
+    x = make_inputs(cfg, device="cuda")
+    x["v"] = torch.zeros_like(x["v"])
+    x["a"] = torch.zeros_like(x["a"])
+    path = _path(cfg)
+    out = path.step(x["q"], x["k"], x["v"], x["a"], x["do"])
+    torch.cuda.synchronize()
+    ref = _oracle_full(cfg, x)
+    zs = ref["zs"]
+    assert not zs["near_tie"].any()
+    np.testing.assert_array_equal(path.zone_shape.cpu().numpy(), zs["shape"])
+    np.testing.assert_array_equal(path.block_offsets[:path.nb + 1].cpu().numpy(), zs["block_offsets"])
+    assert bool((out["o"] == 0).all()) and bool((out["dq"] == 0).all()) and bool((out["dk"] == 0).all())
+    for h, hr in enumerate(ref["heads"]):
+        _assert_close(_np(out["dv"][:, h, :]), orc.to_raster(hr["att"]["dV"], ref["pi"]), cfg.dtype, f"dV h{h}",
+                      grad=True)
