@@ -434,3 +434,47 @@ def test_degenerate_zero_values_and_map():
     for h, hr in enumerate(ref["heads"]):
         _assert_close(_np(out["dv"][:, h, :]), orc.to_raster(hr["att"]["dV"], ref["pi"]), cfg.dtype, f"dV h{h}",
                       grad=True)
+
+
+def test_more_than_16384_blocks_uses_the_radix_selection(progress):
+    """A grid of noisy zones (every block 64 tokens) with NB above 16384: the
+    selection runs on the LDS radix kernel by default.  Layout bit-exact,
+    sampled selection rows bit-exact, sampled forward blocks within the bar."""
+    cfg = custom("nb_large", T=128, H=72, W=128, heads=1, d=128, dtype="bf16", top_k=16, top_p=0.95,
+                 kinds=(("noisy", 1.0),), sigma={"noisy": 1.0}, beta=2.0, seed=19)
+    progress("nb>16384: generating")
+    x = make_inputs(cfg, device="cuda", tensors=("q", "k", "v"))
+    path = _path(cfg)
+    path.shapes(x["v"], x["a"])
+    assert path.nb > 16384, path.nb
+    qp, kp, vp = path.permute(x["q"]), path.permute(x["k"]), path.permute(x["v"])
+    sel = path.select(qp, kp)
+    op, lse = path.forward(qp, kp, vp, sel)
+    torch.cuda.synchronize()
+    progress(f"nb>16384: NB {path.nb}, oracle")
+    zs = orc.zone_shapes(_np(x["v"]).reshape(cfg.N, -1), _np(x["a"]), cfg.T, cfg.H, cfg.W)
+    assert not zs["near_tie"].any()
+    offs = zs["block_offsets"]
+    np.testing.assert_array_equal(path.block_offsets[:path.nb + 1].cpu().numpy(), offs)
+    pi = orc.permutation(cfg.T, cfg.H, cfg.W, zs["shape"])
+    sc = float(np.float32(1.0 / math.sqrt(cfg.d)))
+    Qp, Kp, Vp = (orc.to_block_major(_np(x[n]), pi) for n in ("q", "k", "v"))
+    Kbar = orc.pool_blocks(Kp, offs, 0)
+    og = sel.offsets[0].cpu().numpy()
+    ig = sel.idx[0, :og[-1]].cpu().numpy()
+    Og = _np(op[:, 0, :])
+    rng = np.random.default_rng(23)
+    checked, pairs = 0, []
+    for i in sorted(rng.choice(path.nb, size=24, replace=False).tolist()):
+        qbar = orc.pool_blocks(Qp[offs[i]:offs[i + 1]], np.array([0, offs[i + 1] - offs[i]]), 0)
+        L = orc.block_logits(qbar, Kbar, sc)[0]
+        s, flag = orc.select_row(L, cfg.top_k, cfg.top_p)
+        if flag:
+            continue
+        np.testing.assert_array_equal(ig[og[i]:og[i + 1]], s, err_msg=f"row {i}")
+        o_ref, _ = orc.attn_fwd_block(Qp, Kp, Vp, offs, s, i, 0, sc)
+        pairs.append((Og[offs[i]:offs[i + 1]], o_ref))
+        checked += 1
+    assert checked >= 12
+    _assert_close(np.concatenate([p[0] for p in pairs]), np.concatenate([p[1] for p in pairs]), cfg.dtype,
+                  "nb>16384 O")
