@@ -478,3 +478,64 @@ def test_more_than_16384_blocks_uses_the_radix_selection(progress):
     assert checked >= 12
     _assert_close(np.concatenate([p[0] for p in pairs]), np.concatenate([p[1] for p in pairs]), cfg.dtype,
                   "nb>16384 O")
+
+
+def test_maximum_block_count(progress):
+    """NB at the library's 32768-block limit (a 128^3 grid of noisy zones, every
+    block 64 tokens): the radix selection's LDS holds the whole row (128 KB).
+    Layout bit-exact; on sampled query blocks the selection rows are bit-exact
+    and O, lse and dQ are within the bars; every O, dQ, dK and dV row is written
+    and finite (NaN-filled beforehand).  The noise level that puts every zone
+    at 64-token blocks leaves Q at a spread of about 8 and K, V at about 4; they
+    are scaled by powers of two (exact in bf16): K and V to unit spread, Q to a
+    spread of 4, which keeps scores of spread 4 and O at unit scale, where the
+    bars (absolute for O) are stated.  The zone decisions are ratios of V
+    statistics and do not change."""
+    cfg = custom("nb_max", T=128, H=128, W=128, heads=1, d=128, dtype="bf16", top_k=16, top_p=0.95,
+                 kinds=(("noisy", 1.0),), sigma={"noisy": 4.0}, beta=2.0, seed=19)
+    progress("nb max: generating")
+    x = make_inputs(cfg, device="cuda", tensors=("q", "k", "v", "do"))
+    for n, f in (("q", 0.5), ("k", 0.25), ("v", 0.25)):
+        x[n] = x[n] * f
+    path = _path(cfg)
+    path.shapes(x["v"], x["a"])
+    assert path.nb == 32768, path.nb
+    qp, kp, vp, dop = (path.permute(x[n]) for n in ("q", "k", "v", "do"))
+    sel = path.select(qp, kp)
+    op = path.block_major_like(qp).fill_(float("nan"))
+    _, lse = path.forward(qp, kp, vp, sel, op=op)
+    grads = tuple(path.block_major_like(qp).fill_(float("nan")) for _ in range(3))
+    path.backward(qp, kp, vp, op, dop, lse, sel, grads=grads)
+    torch.cuda.synchronize()
+    for t in (op,) + grads:
+        assert bool(torch.isfinite(t).all())
+    progress("nb max: oracle")
+    zs = orc.zone_shapes(_np(x["v"]).reshape(cfg.N, -1), _np(x["a"]), cfg.T, cfg.H, cfg.W)
+    assert not zs["near_tie"].any()
+    offs = zs["block_offsets"]
+    np.testing.assert_array_equal(path.block_offsets[:path.nb + 1].cpu().numpy(), offs)
+    pi = orc.permutation(cfg.T, cfg.H, cfg.W, zs["shape"])
+    sc = float(np.float32(1.0 / math.sqrt(cfg.d)))
+    Qp, Kp, Vp, dOp = (orc.to_block_major(_np(x[n]), pi) for n in ("q", "k", "v", "do"))
+    Kbar = orc.pool_blocks(Kp, offs, 0)
+    og = sel.offsets[0].cpu().numpy()
+    ig = sel.idx[0, :og[-1]].cpu().numpy()
+    Og, dQg, lg = _np(op[:, 0, :]), _np(grads[0][:, 0, :]), lse[0].cpu().numpy()
+    rng = np.random.default_rng(29)
+    o_pairs, dq_pairs = [], []
+    for i in sorted(rng.choice(path.nb, size=24, replace=False).tolist()):
+        qbar = orc.pool_blocks(Qp[offs[i]:offs[i + 1]], np.array([0, offs[i + 1] - offs[i]]), 0)
+        s, flag = orc.select_row(orc.block_logits(qbar, Kbar, sc)[0], cfg.top_k, cfg.top_p)
+        if flag:
+            continue
+        np.testing.assert_array_equal(ig[og[i]:og[i + 1]], s, err_msg=f"row {i}")
+        o_ref, lse_ref = orc.attn_fwd_block(Qp, Kp, Vp, offs, s, i, 0, sc)
+        np.testing.assert_allclose(lg[offs[i]:offs[i + 1]], lse_ref, atol=2e-3)
+        o_pairs.append((Og[offs[i]:offs[i + 1]], o_ref))
+        dq_pairs.append((dQg[offs[i]:offs[i + 1]], orc.attn_bwd_block(Qp, Kp, Vp, dOp, offs, s, i, 0, sc)[0]))
+    assert len(o_pairs) >= 12
+    assert max(float(np.abs(p[1]).max()) for p in o_pairs) > 0.5   # O at unit scale
+    progress(f"nb max: {len(o_pairs)} query blocks checked")
+    for what, pairs, grad in (("O", o_pairs, False), ("dQ", dq_pairs, True)):
+        _assert_close(np.concatenate([p[0] for p in pairs]), np.concatenate([p[1] for p in pairs]), cfg.dtype,
+                      f"nb max {what}", grad=grad)
