@@ -871,7 +871,8 @@ tr_sort_kernel(const int32_t* __restrict__ tr_offsets, int nb, int64_t cap, int3
 // on one XCD start on the same key tiles and share them in L2 (at 2K the
 // forward gains 6%).  The order only changes timing: every tile's result is
 // accumulated in its own fixed order, so the outputs are the same bits under
-// any order.  Ties between tiles of equal key are left to the atomics.
+// any order.  Tiles of equal key keep their launch order (a stable counting
+// sort), so the order itself is deterministic too.
 
 __global__ void __launch_bounds__(256) fill_i32_kernel(int32_t* __restrict__ p, int64_t n, int32_t v) {
     for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n; i += static_cast<int64_t>(gridDim.x) * 256)
