@@ -183,10 +183,11 @@ def _short(name):
 
 def profile(args):
     """rocprofv3 passes over this bench (kernel trace, FETCH_SIZE, WRITE_SIZE),
-    summarised as text.  The GPU is only used by the child processes."""
+    summarised as text into the --profile folder; the raw rocprofv3 output goes
+    to profile_raw beside it.  The GPU is only used by the child processes."""
     out = args.profile
     os.makedirs(out, exist_ok=True)
-    raw = os.path.join(ROOT, "gpurun_out", "profile_raw")
+    raw = os.path.join(os.path.dirname(os.path.abspath(out)), "profile_raw")
     os.makedirs(raw, exist_ok=True)
     me = [sys.executable, "-u", os.path.abspath(__file__), "--config", args.config, "--no-cpu-baseline",
           "--no-next-rows"]
