@@ -33,6 +33,10 @@
  *     pointers 16-byte aligned and ld, hs multiples of 8 elements (bf16) or 4
  *     (f32), and 64 * ld * element size below 2^32 bytes (tiles are addressed
  *     with 32-bit offsets).
+ *   - Block counts: every call that takes `nb` needs 1 <= nb and 64 * nb <= N
+ *     (PRISM_E_ARG otherwise) and nb <= 32768 (PRISM_E_UNSUPPORTED above: the
+ *     longest selection row, 32768 fp32 keys, is held in one workgroup's LDS).
+ *     A 128 x 128 x 128 grid of 64-token blocks reaches the limit exactly.
  *   - Two environment variables switch to alternative kernels with the same
  *     results, for tests: PRISM_SELECT_RADIX=1 makes prism_select use its LDS
  *     radix-select kernel at every row length (by default it is used only for

@@ -151,6 +151,8 @@ def test_select_rejects():
     assert f(ld=1 << 24) == 4                      # 64 rows would span 4 GiB: beyond 32-bit tile offsets
     assert f(nb=0) == 1
     assert f(nb=N // 64 + 1) == 1
+    assert f(N=64 * 32769, nb=32769) == 4          # above the 32768-block limit
+    assert "32768" in P.prism_last_error()
     assert f(k=-1) == 1
     assert f(p=1.5) == 1
     assert f(p=float("nan")) == 1
