@@ -537,7 +537,7 @@ def main():
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus above 1 is not supported",
+        print(json.dumps({"error": "the benchmark runs on one GPU; --gpus above 1 is not supported (the path shards by head, one process per GPU, with no kernel change)",
                           "n_gpus": args.gpus}))
         sys.exit(2)
     if not torch.cuda.is_available():
