@@ -753,13 +753,19 @@ csr_scan_kernel(const int32_t* __restrict__ counts, int n, int32_t* __restrict__
     }
 }
 
+// The row is taken kWriteChunks chunks of NW*64 keys at a time: each thread
+// has that many independent loads in flight, and one barrier per pass orders
+// the chunks (the per-wave counts are double-buffered, so the next pass can
+// write its counts while a slower wave still reads this pass's).
+constexpr int kWriteChunks = 4;
 template <int NW>
 __global__ void __launch_bounds__(NW * 64)
 select_write_kernel(const float* __restrict__ logits, int nb, const uint32_t* __restrict__ row_thr,
                     const int32_t* __restrict__ row_jlim, const int32_t* __restrict__ sel_offsets,
                     int32_t* __restrict__ sel_idx, int64_t cap) {
     constexpr int NT = NW * 64;
-    __shared__ int sc[NW];
+    constexpr int U = kWriteChunks;
+    __shared__ int sc[2][U * NW];
     const int i = blockIdx.x, h = blockIdx.y;
     const int64_t row = static_cast<int64_t>(h) * nb + i;
     const float* __restrict__ L = logits + row * nb;
@@ -769,29 +775,48 @@ select_write_kernel(const float* __restrict__ logits, int nb, const uint32_t* __
     int32_t* __restrict__ out = sel_idx + static_cast<int64_t>(h) * cap;
     const int lane = threadIdx.x & (kWave - 1);
     const int wid = threadIdx.x / kWave;
-    for (int base = 0; base < nb; base += NT) {
-        const int j = base + threadIdx.x;
-        bool f = false;
-        if (j < nb) {
-            const uint32_t kk = score_key(L[j]);
-            f = kk > thr || (kk == thr && j <= jlim);
-        }
-        const uint64_t bal = __ballot(f);
-        const int before = __popcll(bal & ((lane == 0) ? 0ull : (~0ull >> (64 - lane))));
-        __syncthreads();
-        if (lane == 0) sc[wid] = __popcll(bal);
-        __syncthreads();
-        int woff = 0, tot = 0;
+    const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));   // lanes under this one
+    int buf = 0;
+    for (int base = 0; base < nb; base += U * NT) {
+        float v[U];
 #pragma unroll
-        for (int w = 0; w < NW; ++w) {
-            woff += w < wid ? sc[w] : 0;
-            tot += sc[w];
+        for (int u = 0; u < U; ++u) {
+            const int j = base + u * NT + static_cast<int>(threadIdx.x);
+            v[u] = j < nb ? L[j] : 0.0f;
         }
-        if (f) {
-            const int64_t p = pos + woff + before;
-            if (p < cap) out[p] = j;
+        bool f[U];
+        int before[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int j = base + u * NT + static_cast<int>(threadIdx.x);
+            f[u] = false;
+            if (j < nb) {
+                const uint32_t kk = score_key(v[u]);
+                f[u] = kk > thr || (kk == thr && j <= jlim);
+            }
+            const uint64_t bal = __ballot(f[u]);
+            before[u] = __popcll(bal & below);
+            if (lane == 0) sc[buf][u * NW + wid] = __popcll(bal);
         }
-        pos += tot;
+        __syncthreads();
+        // chunk u of wave w starts after every chunk before u and, inside u,
+        // after the waves below w
+        int acc = 0, woff[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int w = 0; w < NW; ++w) {
+                if (w == wid) woff[u] = acc;
+                acc += sc[buf][u * NW + w];
+            }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (f[u]) {
+                const int64_t p = pos + woff[u] + before[u];
+                if (p < cap) out[p] = base + u * NT + static_cast<int>(threadIdx.x);
+            }
+        pos += acc;
+        buf ^= 1;
     }
 }
 
