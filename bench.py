@@ -393,21 +393,24 @@ def measure_routed(path, qp, kp, vp, ratio, dop=None, reps=3):
         return e0.elapsed_time(e1) / reps
 
     route_ms = timed(lambda: path.route(sel, ratio))
-    exact_ms = timed(lambda: path.forward(qp, kp, vp, sel))
-    routed_ms = timed(lambda: path.routed_forward(qp, kp, vp, sel, flat))
+    op, rop = path.block_major_like(qp), path.block_major_like(qp)
+    res_e, res_r = (path.residual_like(op), path.residual_like(rop)) if dop is not None else (None, None)
+    exact_ms = timed(lambda: path.forward(qp, kp, vp, sel, op=op, ores=res_e))
+    routed_ms = timed(lambda: path.routed_forward(qp, kp, vp, sel, flat, op=rop, ores=res_r))
     bwd = {}
     if dop is not None:
-        op, lse = path.forward(qp, kp, vp, sel)
-        rop, rlse = path.routed_forward(qp, kp, vp, sel, flat)
+        _, lse = path.forward(qp, kp, vp, sel, op=op, ores=res_e)
+        _, rlse = path.routed_forward(qp, kp, vp, sel, flat, op=rop, ores=res_r)
         grads = tuple(path.block_major_like(qp) for _ in range(3))
-        path.backward(qp, kp, vp, op, dop, lse, sel, grads=grads)
-        path.routed_backward(qp, kp, vp, rop, dop, rlse, sel, flat, grads=grads)
+        path.backward(qp, kp, vp, op, dop, lse, sel, grads=grads, ores=res_e)
+        path.routed_backward(qp, kp, vp, rop, dop, rlse, sel, flat, grads=grads, ores=res_r)
         torch.cuda.synchronize()
-        eb = timed(lambda: path.backward(qp, kp, vp, op, dop, lse, sel, grads=grads))
-        rb = timed(lambda: path.routed_backward(qp, kp, vp, rop, dop, rlse, sel, flat, grads=grads))
+        eb = timed(lambda: path.backward(qp, kp, vp, op, dop, lse, sel, grads=grads, ores=res_e))
+        rb = timed(lambda: path.routed_backward(qp, kp, vp, rop, dop, rlse, sel, flat, grads=grads, ores=res_r))
         bwd = {"exact_backward_ms": round(eb, 3), "routed_backward_ms": round(rb, 3),
                "fwd_bwd_speedup": round((exact_ms + eb) / (route_ms + routed_ms + rb), 3)}
-        del op, lse, rop, rlse, grads
+        del lse, rlse, grads
+    del op, rop, res_e, res_r
     sizes = (path.block_offsets[1:path.nb + 1] - path.block_offsets[:path.nb]).to(torch.float64)
     flat_tokens = float((flat.to(torch.float64) * sizes).sum()) / (path.hc * path.N)
     del sel
@@ -445,15 +448,17 @@ def measure_zone_order(cfg, x, path, qp, kp, vp, dop=None, reps=3):
     res = {}
     for tag, p, t in (("raster", path, {"q": qp, "k": kp, "v": vp, "do": dop}), ("hilbert", hp, hb)):
         sel = p.select(t["q"], t["k"], 0)
-        op, lse = p.forward(t["q"], t["k"], t["v"], sel)
+        op = p.block_major_like(t["q"])
+        ores = p.residual_like(op) if dop is not None else None
+        _, lse = p.forward(t["q"], t["k"], t["v"], sel, op=op, ores=ores)
         r = {"permute_ms": round(timed(lambda: p.permute(x["q"], out=t["q"])), 3),
              "select_ms": round(timed(lambda: p.select(t["q"], t["k"], 0)), 3),
-             "forward_ms": round(timed(lambda: p.forward(t["q"], t["k"], t["v"], sel, op=op, lse=lse)), 3)}
+             "forward_ms": round(timed(lambda: p.forward(t["q"], t["k"], t["v"], sel, op=op, lse=lse, ores=ores)), 3)}
         f_fwd, f_bwd, mean_sel = effective_flops(p, [sel], cfg.d)
         if dop is not None:
             grads = tuple(p.block_major_like(t["q"]) for _ in range(3))
             r["backward_ms"] = round(timed(lambda: p.backward(t["q"], t["k"], t["v"], op, t["do"], lse, sel,
-                                                              grads=grads)), 3)
+                                                              grads=grads, ores=ores)), 3)
             del grads
         r["effective_tflop"] = round((f_fwd + (f_bwd if dop is not None else 0.0)) / 1e12, 6)
         r["mean_selected_blocks"] = round(mean_sel, 3)
@@ -489,11 +494,14 @@ def measure_subblock(cfg, path, qp, kp, vp, dop=None, reps=3):
     for scoring in ("block", "subblock"):
         sel = path.select(qp, kp, 0, scoring=scoring)
         r = {"select_ms": round(timed(lambda: path.select(qp, kp, 0, scoring=scoring)), 3)}
-        op, lse = path.forward(qp, kp, vp, sel)
-        r["forward_ms"] = round(timed(lambda: path.forward(qp, kp, vp, sel, op=op, lse=lse)), 3)
+        op = path.block_major_like(qp)
+        ores = path.residual_like(op) if dop is not None else None
+        _, lse = path.forward(qp, kp, vp, sel, op=op, ores=ores)
+        r["forward_ms"] = round(timed(lambda: path.forward(qp, kp, vp, sel, op=op, lse=lse, ores=ores)), 3)
         if dop is not None:
             grads = tuple(path.block_major_like(qp) for _ in range(3))
-            r["backward_ms"] = round(timed(lambda: path.backward(qp, kp, vp, op, dop, lse, sel, grads=grads)), 3)
+            r["backward_ms"] = round(timed(lambda: path.backward(qp, kp, vp, op, dop, lse, sel, grads=grads,
+                                                                 ores=ores)), 3)
             del grads
         f_fwd, f_bwd, mean_sel = effective_flops(path, [sel], cfg.d)
         r["effective_tflop"] = round((f_fwd + (f_bwd if dop is not None else 0.0)) / 1e12, 4)
@@ -561,6 +569,8 @@ def main():
     qp, kp, vp = bm(), bm(), bm()
     dop = bm() if cfg.backward else None
     outs = {n: torch.empty_like(x["q"]) for n in (("o", "dq", "dk", "dv") if cfg.backward else ("o",))}
+    # the bf16 residual of O, which the backward's row dot reads (training steps only)
+    ores = path.residual_like(outs["o"]) if cfg.backward else None
     ld, hs = qp.stride(0), qp.stride(1)
     hc = path.hc
     lse = torch.empty((hc, cfg.N), dtype=torch.float32, device="cuda")
@@ -600,14 +610,16 @@ def main():
             P.prism_select(q, k, cfg.N, hc, cfg.d, ld, hs, path.block_offsets, nb, cfg.top_k, cfg.top_p, sc,
                            s.offsets, s.idx, cap, s.total, ws_sel)
             ev[3 + 3 * g].record()
+            r = ores[:, h0:h0 + hc] if ores is not None else None
             P.prism_sparse_attn_fwd(q, k, v, o, lse, cfg.N, hc, cfg.d, ld, hs, path.block_offsets, nb, s.offsets,
-                                    s.idx, cap, sc, ws=ws_fwd, layout=lay)
+                                    s.idx, cap, sc, ws=ws_fwd, layout=lay, o_res=r)
             ev[4 + 3 * g].record()
             if cfg.backward:
                 do_ = dop[:, h0:h0 + hc]
                 gq, gk, gv = (outs[n][:, h0:h0 + hc] for n in ("dq", "dk", "dv"))
                 P.prism_sparse_attn_bwd(q, k, v, o, do_, lse, gq, gk, gv, cfg.N, hc, cfg.d, ld, hs,
-                                        path.block_offsets, nb, s.offsets, s.idx, cap, sc, ws_bwd, layout=lay)
+                                        path.block_offsets, nb, s.offsets, s.idx, cap, sc, ws_bwd, layout=lay,
+                                        o_res=r)
             ev[5 + 3 * g].record()
         ev[-1].record()
 

@@ -11,6 +11,11 @@ namespace prism {
 // 32*w .. +31 and streams every selected 64-key tile:
 //   S^T = K Q^T, P^T = exp2(S^T - lse), dP^T = V dO^T, dS^T = P^T (dP^T - D),
 //   dQ^T += K^T dS^T
+// with D = rowsum(dO * O) from the row-dot pass (O plus its residual when the
+// forward wrote one); it also sums P dP over the row's keys and leaves that,
+// the exact D, in place of the row-dot value for the dK/dV kernel.  (D from
+// the forward's O alone carries the rounding of P in the forward's P V; in dK
+// that error is summed over every query row that uses the key.)
 // dK/dV kernel (key-major): 4 waves per 64-key tile (two roles per 32-key
 // half, below) stream the 64-row tiles of every query block that selected the
 // tile's block (transposed CSR, ascending):
@@ -37,7 +42,7 @@ namespace prism {
 template <int D>
 __global__ void __launch_bounds__(128, 2)
 attn_dq_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-                    const uint16_t* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ Dq,
+                    const uint16_t* __restrict__ dout, const float* __restrict__ lse, float* __restrict__ Dq,
                     uint16_t* __restrict__ dq, int64_t N, int64_t ld, int64_t hs, const int32_t* __restrict__ offs,
                     int nb, const int32_t* __restrict__ sel_off, const int32_t* __restrict__ sel_idx, int64_t cap,
                     const int32_t* __restrict__ order, const uint8_t* __restrict__ skip, const RowMap om,
@@ -82,6 +87,7 @@ attn_dq_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     for (int m = 0; m < DM; ++m)
 #pragma unroll
         for (int x = 0; x < 16; ++x) acc[m][x] = 0.0f;
+    float dex = 0.0f;   // this lane's part of sum_t P dP over the row's keys
     const uint16_t* __restrict__ kh_ = k + h * hs;
     const uint16_t* __restrict__ vh_ = v + h * hs;
 
@@ -125,6 +131,7 @@ attn_dq_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
 #pragma unroll
                 for (int x = 0; x < 16; ++x) {
                     const float p = fast_exp2(fmaf(sa[mt][x], scale_log2, -lrow));
+                    dex = fmaf(p, pa[mt][x], dex);
                     sa[mt][x] = p * (pa[mt][x] - drow);     // dS^T
                 }
 #pragma unroll
@@ -147,6 +154,12 @@ attn_dq_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
             *reinterpret_cast<u32x2_t*>(out + 32 * m + 8 * g + 4 * hl) =
                 u32x2_t{pack2(a[4 * g] * scale, a[4 * g + 1] * scale), pack2(a[4 * g + 2] * scale, a[4 * g + 3] * scale)};
         }
+    // D = sum_t P dP over the row's keys, from the same fp32 P and dP as dS:
+    // the definition of rowsum(dO * O) for the exact softmax, which the
+    // forward's O (P rounded to bf16 in P V) only approximates.  The dK/dV
+    // kernel, launched next, reads it; each row belongs to one workgroup.
+    const float dsum = dex + __shfl_xor(dex, 32, 64);
+    if (hl == 0) Dq[static_cast<int64_t>(h) * N + row] = dsum;
 }
 
 // dK/dV: 4 waves per 64-key tile, in two roles per 32-key half.  Role 0 holds
@@ -323,7 +336,7 @@ attn_dkdv_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
 // ---------------------------------------------------------------- launcher
 
 hipError_t launch_attn_bwd_mfma(const void* q, const void* k, const void* v, const void* dout, const float* lse,
-                                const float* Dq, void* dq, void* dk, void* dv, int64_t N, int heads, int d, int64_t ld,
+                                float* Dq, void* dq, void* dk, void* dv, int64_t N, int heads, int d, int64_t ld,
                                 int64_t hs, const int32_t* offs, int nb, const int32_t* so, const int32_t* si,
                                 const int32_t* to, const int32_t* ti, int64_t cap, const int32_t* qorder,
                                 const RouteGrad* rg, const RowMap& om, float scale, hipStream_t s) {

@@ -62,6 +62,13 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
 
+// bf16 residual of four fp32 values r against their rounded pair hi:
+// r - float(hi), rounded to bf16.  hi + residual carries r to about 16 bits.
+__device__ __forceinline__ u32x2_t residual4(const float (&r)[4], const u32x2_t& hi) {
+    return u32x2_t{pack2(r[0] - __uint_as_float(hi.x << 16), r[1] - __uint_as_float(hi.x & 0xffff0000u)),
+                   pack2(r[2] - __uint_as_float(hi.y << 16), r[3] - __uint_as_float(hi.y & 0xffff0000u))};
+}
+
 // 2^x on the transcendental unit; results below the normal range flush to 0,
 // which is what the softmax wants for scores far below the row maximum
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

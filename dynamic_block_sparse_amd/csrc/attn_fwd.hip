@@ -39,7 +39,7 @@ attn_fwd_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
                      uint16_t* __restrict__ o, float* __restrict__ lse, int64_t N, int64_t ld, int64_t hs,
                      const int32_t* __restrict__ offs, int nb, const int32_t* __restrict__ sel_off,
                      const int32_t* __restrict__ sel_idx, int64_t cap, const int32_t* __restrict__ order,
-                     const uint8_t* __restrict__ skip, const RowMap om, float scale_log2) {
+                     const uint8_t* __restrict__ skip, const RowMap om, float scale_log2, uint16_t* __restrict__ ores) {
     __shared__ uint16_t kbuf[64 * D], vbuf[64 * D];
     const int ntiles = static_cast<int>(N / 64);
     const int wg = xcd_remap(blockIdx.x);
@@ -148,15 +148,19 @@ attn_fwd_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     }
     // lanes l and l^32 hold the two halves of a row's sum
     const float lt = lrow + __shfl_xor(lrow, 32, 64);
-    const float inv = 1.0f / (lrnd + __shfl_xor(lrnd, 32, 64));
-    uint16_t* orow = o + row_offset(om, row, h);
+    const float lsum = lrnd + __shfl_xor(lrnd, 32, 64);
+    const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;   // a row with no stored entry: O = 0, lse = -inf
+    const int64_t ro = row_offset(om, row, h);
 #pragma unroll
     for (int m = 0; m < DM; ++m)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
             const f32x16_t& a = oacc[m];
-            *reinterpret_cast<u32x2_t*>(orow + 32 * m + 8 * g + 4 * hl) =
-                u32x2_t{pack2(a[4 * g] * inv, a[4 * g + 1] * inv), pack2(a[4 * g + 2] * inv, a[4 * g + 3] * inv)};
+            const float r[4] = {a[4 * g] * inv, a[4 * g + 1] * inv, a[4 * g + 2] * inv, a[4 * g + 3] * inv};
+            const u32x2_t hi{pack2(r[0], r[1]), pack2(r[2], r[3])};
+            const int64_t at = ro + 32 * m + 8 * g + 4 * hl;
+            *reinterpret_cast<u32x2_t*>(o + at) = hi;
+            if (ores) *reinterpret_cast<u32x2_t*>(ores + at) = residual4(r, hi);
         }
     if (hl == 0) lse[static_cast<int64_t>(h) * N + row] = (mrow + __log2f(lt)) * kLn2;
 }
@@ -166,8 +170,9 @@ attn_fwd_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
 hipError_t launch_attn_fwd_mfma(const void* q, const void* k, const void* v, void* o, float* lse, int64_t N, int heads,
                                 int d, int64_t ld, int64_t hs, const int32_t* offs, int nb, const int32_t* so,
                                 const int32_t* si, int64_t cap, const int32_t* order, const uint8_t* skip,
-                                const RowMap& om, float scale, hipStream_t s) {
+                                const RowMap& om, float scale, void* ores, hipStream_t s) {
     const dim3 grid(static_cast<unsigned>(N / 64 * heads));
+    uint16_t* R = static_cast<uint16_t*>(ores);
     const float sl2 = scale * kLog2e;
     const uint16_t* Q = static_cast<const uint16_t*>(q);
     const uint16_t* K = static_cast<const uint16_t*>(k);
@@ -175,10 +180,10 @@ hipError_t launch_attn_fwd_mfma(const void* q, const void* k, const void* v, voi
     uint16_t* O = static_cast<uint16_t*>(o);
     if (d == 128)
         hipLaunchKernelGGL(attn_fwd_mfma_kernel<128>, grid, dim3(128), 0, s, Q, K, V, O, lse, N, ld, hs, offs, nb, so,
-                           si, cap, order, skip, om, sl2);
+                           si, cap, order, skip, om, sl2, R);
     else
         hipLaunchKernelGGL(attn_fwd_mfma_kernel<64>, grid, dim3(128), 0, s, Q, K, V, O, lse, N, ld, hs, offs, nb, so,
-                           si, cap, order, skip, om, sl2);
+                           si, cap, order, skip, om, sl2, R);
     return hipGetLastError();
 }
 

@@ -45,7 +45,7 @@ __global__ void __launch_bounds__(64)
 attn_fwd_simt_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, T* __restrict__ o,
                      float* __restrict__ lse, int64_t N, int64_t ld, int64_t hs, const int32_t* __restrict__ offs,
                      int nb, const int32_t* __restrict__ sel_off, const int32_t* __restrict__ sel_idx, int64_t cap,
-                     const uint8_t* __restrict__ skip, const RowMap om, float scale) {
+                     const uint8_t* __restrict__ skip, const RowMap om, float scale, T* __restrict__ ores) {
     __shared__ float Ks[kChunk][D + 1];
     __shared__ float Vs[kChunk][D + 1];
     const int h = blockIdx.y;
@@ -101,10 +101,14 @@ attn_fwd_simt_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* 
             m = mn;
         }
     }
-    const float inv = 1.0f / l;
-    T* __restrict__ orow = o + row_offset(om, p, h);
+    const float inv = l > 0.0f ? 1.0f / l : 0.0f;   // a row with no stored entry: O = 0, lse = -inf
+    const int64_t ro = row_offset(om, p, h);
 #pragma unroll
-    for (int c = 0; c < D; ++c) st_elem(orow + c, acc[c] * inv);
+    for (int c = 0; c < D; ++c) {
+        const float x = acc[c] * inv;
+        st_elem(o + ro + c, x);
+        if (ores) st_elem(ores + ro + c, x - ld_elem(o + ro + c));   // bf16 residual (NULL for fp32)
+    }
     lse[static_cast<int64_t>(h) * N + p] = m + __logf(l);
 }
 
@@ -113,7 +117,7 @@ attn_fwd_simt_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* 
 template <typename T, int D>
 __global__ void __launch_bounds__(256)
 attn_bwd_dot_kernel(const T* __restrict__ o, const T* __restrict__ dout, int64_t N, int heads, int64_t ld, int64_t hs,
-                    const RowMap om, float* __restrict__ Dq) {
+                    const RowMap om, float* __restrict__ Dq, const T* __restrict__ ores) {
     constexpr int EPV = 16 / static_cast<int>(sizeof(T));
     constexpr int LPR = D / EPV;            // lanes per row (power of two, <= 64)
     constexpr int RPI = 256 / LPR;          // rows per workgroup step
@@ -124,16 +128,22 @@ attn_bwd_dot_kernel(const T* __restrict__ o, const T* __restrict__ dout, int64_t
         const int64_t p = static_cast<int64_t>(blockIdx.x) * 64 + it * RPI + threadIdx.x / LPR;
         float s = 0.0f;
         if (p < N) {
-            const uint4 a = *reinterpret_cast<const uint4*>(o + row_offset(om, p, h) + sub * EPV);
+            const int64_t ro = row_offset(om, p, h) + sub * EPV;
+            const uint4 a = *reinterpret_cast<const uint4*>(o + ro);
             const uint4 b = *reinterpret_cast<const uint4*>(dout + p * ld + h * hs + sub * EPV);
-            const uint32_t wa[4] = {a.x, a.y, a.z, a.w}, wb[4] = {b.x, b.y, b.z, b.w};
+            uint4 c = make_uint4(0, 0, 0, 0);
+            if (ores) c = *reinterpret_cast<const uint4*>(ores + ro);
+            const uint32_t wa[4] = {a.x, a.y, a.z, a.w}, wb[4] = {b.x, b.y, b.z, b.w}, wc[4] = {c.x, c.y, c.z, c.w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 if constexpr (EPV == 8) {
-                    s = fmaf(bf16_to_f32(static_cast<uint16_t>(wb[e] & 0xFFFFu)),
-                             bf16_to_f32(static_cast<uint16_t>(wa[e] & 0xFFFFu)), s);
-                    s = fmaf(bf16_to_f32(static_cast<uint16_t>(wb[e] >> 16)), bf16_to_f32(static_cast<uint16_t>(wa[e] >> 16)),
-                             s);
+                    // O = hi + residual: both halves enter the row dot
+                    const float lo_o = bf16_to_f32(static_cast<uint16_t>(wa[e] & 0xFFFFu)) +
+                                       bf16_to_f32(static_cast<uint16_t>(wc[e] & 0xFFFFu));
+                    const float hi_o = bf16_to_f32(static_cast<uint16_t>(wa[e] >> 16)) +
+                                       bf16_to_f32(static_cast<uint16_t>(wc[e] >> 16));
+                    s = fmaf(bf16_to_f32(static_cast<uint16_t>(wb[e] & 0xFFFFu)), lo_o, s);
+                    s = fmaf(bf16_to_f32(static_cast<uint16_t>(wb[e] >> 16)), hi_o, s);
                 } else {
                     s = fmaf(__uint_as_float(wb[e]), __uint_as_float(wa[e]), s);
                 }
@@ -277,40 +287,45 @@ attn_dkdv_simt_kernel(const T* __restrict__ q, const T* __restrict__ k, const T*
 template <typename T, int D>
 static hipError_t fwd_simt(const void* q, const void* k, const void* v, void* o, float* lse, int64_t N, int heads,
                            int64_t ld, int64_t hs, const int32_t* offs, int nb, const int32_t* so, const int32_t* si,
-                           int64_t cap, const uint8_t* skip, const RowMap& om, float scale, hipStream_t s) {
+                           int64_t cap, const uint8_t* skip, const RowMap& om, float scale, void* ores, hipStream_t s) {
     const dim3 grid(static_cast<unsigned>(N / 64), heads);
     hipLaunchKernelGGL((attn_fwd_simt_kernel<T, D>), grid, dim3(64), 0, s, static_cast<const T*>(q),
                        static_cast<const T*>(k), static_cast<const T*>(v), static_cast<T*>(o), lse, N, ld, hs, offs, nb,
-                       so, si, cap, skip, om, scale);
+                       so, si, cap, skip, om, scale, static_cast<T*>(ores));
     return hipGetLastError();
 }
 
 hipError_t launch_attn_fwd_simt(const void* q, const void* k, const void* v, void* o, float* lse, bool bf16, int64_t N,
                                 int heads, int d, int64_t ld, int64_t hs, const int32_t* offs, int nb,
                                 const int32_t* so, const int32_t* si, int64_t cap, const uint8_t* skip,
-                                const RowMap& om, float scale, hipStream_t s) {
+                                const RowMap& om, float scale, void* ores, hipStream_t s) {
     if (bf16)
-        return d == 128 ? fwd_simt<uint16_t, 128>(q, k, v, o, lse, N, heads, ld, hs, offs, nb, so, si, cap, skip, om, scale, s)
-                        : fwd_simt<uint16_t, 64>(q, k, v, o, lse, N, heads, ld, hs, offs, nb, so, si, cap, skip, om, scale, s);
-    return d == 128 ? fwd_simt<float, 128>(q, k, v, o, lse, N, heads, ld, hs, offs, nb, so, si, cap, skip, om, scale, s)
-                    : fwd_simt<float, 64>(q, k, v, o, lse, N, heads, ld, hs, offs, nb, so, si, cap, skip, om, scale, s);
+        return d == 128 ? fwd_simt<uint16_t, 128>(q, k, v, o, lse, N, heads, ld, hs, offs, nb, so, si, cap, skip, om, scale,
+                                                  ores, s)
+                        : fwd_simt<uint16_t, 64>(q, k, v, o, lse, N, heads, ld, hs, offs, nb, so, si, cap, skip, om, scale,
+                                                 ores, s);
+    return d == 128 ? fwd_simt<float, 128>(q, k, v, o, lse, N, heads, ld, hs, offs, nb, so, si, cap, skip, om, scale,
+                                           nullptr, s)
+                    : fwd_simt<float, 64>(q, k, v, o, lse, N, heads, ld, hs, offs, nb, so, si, cap, skip, om, scale,
+                                          nullptr, s);
 }
 
 template <typename T, int D>
 static hipError_t dot_launch(const void* o, const void* dout, int64_t N, int heads, int64_t ld, int64_t hs,
-                             const RowMap& om, float* Dq, hipStream_t s) {
+                             const RowMap& om, float* Dq, const void* ores, hipStream_t s) {
     hipLaunchKernelGGL((attn_bwd_dot_kernel<T, D>), dim3(static_cast<unsigned>((N + 63) / 64), heads), dim3(256), 0, s,
-                       static_cast<const T*>(o), static_cast<const T*>(dout), N, heads, ld, hs, om, Dq);
+                       static_cast<const T*>(o), static_cast<const T*>(dout), N, heads, ld, hs, om, Dq,
+                       static_cast<const T*>(ores));
     return hipGetLastError();
 }
 
 hipError_t launch_bwd_dot(const void* o, const void* dout, bool bf16, int64_t N, int heads, int d, int64_t ld,
-                          int64_t hs, const RowMap& om, float* Dq, hipStream_t s) {
+                          int64_t hs, const RowMap& om, float* Dq, const void* ores, hipStream_t s) {
     if (bf16)
-        return d == 128 ? dot_launch<uint16_t, 128>(o, dout, N, heads, ld, hs, om, Dq, s)
-                        : dot_launch<uint16_t, 64>(o, dout, N, heads, ld, hs, om, Dq, s);
-    return d == 128 ? dot_launch<float, 128>(o, dout, N, heads, ld, hs, om, Dq, s)
-                    : dot_launch<float, 64>(o, dout, N, heads, ld, hs, om, Dq, s);
+        return d == 128 ? dot_launch<uint16_t, 128>(o, dout, N, heads, ld, hs, om, Dq, ores, s)
+                        : dot_launch<uint16_t, 64>(o, dout, N, heads, ld, hs, om, Dq, ores, s);
+    return d == 128 ? dot_launch<float, 128>(o, dout, N, heads, ld, hs, om, Dq, nullptr, s)
+                    : dot_launch<float, 64>(o, dout, N, heads, ld, hs, om, Dq, nullptr, s);
 }
 
 template <typename T, int D>

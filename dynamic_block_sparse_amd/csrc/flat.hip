@@ -150,7 +150,8 @@ __global__ void __launch_bounds__(256)
 attn_flat_kernel(const T* __restrict__ q, const float* __restrict__ kbar, const float* __restrict__ vbar,
                  T* __restrict__ o, float* __restrict__ lse, int64_t N, int64_t ld, int64_t hs,
                  const int32_t* __restrict__ offs, int nb, const int32_t* __restrict__ sel_off,
-                 const int32_t* __restrict__ sel_idx, int64_t cap, const uint8_t* __restrict__ flat, float scale) {
+                 const int32_t* __restrict__ sel_idx, int64_t cap, const uint8_t* __restrict__ flat, float scale,
+                 T* __restrict__ ores) {
     constexpr int PW = D / 4;          // channels per lane
     constexpr int PS = PW + 4;         // padded LDS stride of a lane's slice
     constexpr int CH = 16;             // selected blocks staged per round
@@ -211,10 +212,13 @@ attn_flat_kernel(const T* __restrict__ q, const float* __restrict__ kbar, const 
             for (int c = 0; c < PW; ++c) acc[c] = fmaf(pj, Vs[jj][part][c], acc[c]);
         }
     }
-    const float inv = 1.0f / l;
+    const float inv = l > 0.0f ? 1.0f / l : 0.0f;   // a row with no stored entry: O = 0, lse = -inf
     T* __restrict__ orow = o + p * ld + h * hs + part * PW;
 #pragma unroll
-    for (int c = 0; c < PW; ++c) elem_out(orow + c, acc[c] * inv);
+    for (int c = 0; c < PW; ++c) {
+        elem_out(orow + c, acc[c] * inv);
+        if (ores) elem_out(ores + (orow - o) + c, acc[c] * inv - elem_in(orow + c));   // bf16 residual
+    }
     if (part == 0) lse[static_cast<int64_t>(h) * N + p] = m + logf(l);
 }
 
@@ -434,26 +438,26 @@ hipError_t launch_block_means(const void* k, const void* v, bool bf16, int heads
 hipError_t launch_attn_flat(const void* q, const float* kbar, const float* vbar, void* o, float* lse, bool bf16,
                             int64_t N, int heads, int d, int64_t ld, int64_t hs, const int32_t* offs, int nb,
                             const int32_t* so, const int32_t* si, int64_t cap, const uint8_t* flat, float scale,
-                            hipStream_t s) {
+                            void* ores, hipStream_t s) {
     const dim3 grid(static_cast<unsigned>(N / 64 * heads));
     if (bf16) {
         const uint16_t* Q = static_cast<const uint16_t*>(q);
         uint16_t* O = static_cast<uint16_t*>(o);
         if (d == 128)
             hipLaunchKernelGGL((attn_flat_kernel<uint16_t, 128>), grid, dim3(256), 0, s, Q, kbar, vbar, O, lse, N, ld,
-                               hs, offs, nb, so, si, cap, flat, scale);
+                               hs, offs, nb, so, si, cap, flat, scale, static_cast<uint16_t*>(ores));
         else
             hipLaunchKernelGGL((attn_flat_kernel<uint16_t, 64>), grid, dim3(256), 0, s, Q, kbar, vbar, O, lse, N, ld, hs,
-                               offs, nb, so, si, cap, flat, scale);
+                               offs, nb, so, si, cap, flat, scale, static_cast<uint16_t*>(ores));
     } else {
         const float* Q = static_cast<const float*>(q);
         float* O = static_cast<float*>(o);
         if (d == 128)
             hipLaunchKernelGGL((attn_flat_kernel<float, 128>), grid, dim3(256), 0, s, Q, kbar, vbar, O, lse, N, ld, hs,
-                               offs, nb, so, si, cap, flat, scale);
+                               offs, nb, so, si, cap, flat, scale, static_cast<float*>(nullptr));
         else
             hipLaunchKernelGGL((attn_flat_kernel<float, 64>), grid, dim3(256), 0, s, Q, kbar, vbar, O, lse, N, ld, hs,
-                               offs, nb, so, si, cap, flat, scale);
+                               offs, nb, so, si, cap, flat, scale, static_cast<float*>(nullptr));
     }
     return hipGetLastError();
 }

@@ -520,6 +520,15 @@ prism_status prism_select_subblock(const void* q, const void* k, prism_dtype dt,
 
 namespace {
 
+// The optional bf16 residual of O: NULL, or 16-byte aligned storage with o's
+// layout; an fp32 O needs none.
+prism_status check_residual(const void* o_res, prism_dtype dt) {
+    if (!o_res) return PRISM_OK;
+    if (dt != PRISM_BF16) return fail(PRISM_E_ARG, "o_res is for bf16 outputs only (pass NULL for fp32)");
+    if (!aligned16(o_res)) return fail(PRISM_E_UNSUPPORTED, "o_res must be 16-byte aligned");
+    return PRISM_OK;
+}
+
 // Checks shared by the exact and the routed forward.
 prism_status check_fwd(const void* q, const void* k, const void* v, const void* o, const float* lse, prism_dtype dt,
                        int64_t N, int32_t heads, int32_t d, int64_t ld, int64_t hs, const int32_t* block_offsets,
@@ -537,43 +546,44 @@ prism_status check_fwd(const void* q, const void* k, const void* v, const void* 
 }
 
 // Exact forward over the tiles whose block is not marked in `skip` (NULL: all).
-prism_status exact_fwd(const void* q, const void* k, const void* v, void* o, float* lse, prism_dtype dt, int64_t N,
-                       int32_t heads, int32_t d, int64_t ld, int64_t hs, const int32_t* block_offsets, int32_t nb,
-                       const int32_t* sel_offsets, const int32_t* sel_idx, int64_t cap, const uint8_t* skip,
-                       const prism::RowMap& om, float scale, Carver& c, hipStream_t stream) {
+prism_status exact_fwd(const void* q, const void* k, const void* v, void* o, float* lse, void* o_res, prism_dtype dt,
+                       int64_t N, int32_t heads, int32_t d, int64_t ld, int64_t hs, const int32_t* block_offsets,
+                       int32_t nb, const int32_t* sel_offsets, const int32_t* sel_idx, int64_t cap,
+                       const uint8_t* skip, const prism::RowMap& om, float scale, Carver& c, hipStream_t stream) {
     OrderWs w = carve_order(c, N, heads, nb);
     if (use_simt_attention(dt))
         return hip_status(prism::launch_attn_fwd_simt(q, k, v, o, lse, dt == PRISM_BF16, N, heads, d, ld, hs,
                                                       block_offsets, nb, sel_offsets, sel_idx, cap, skip, om,
-                                                      scale, stream),
+                                                      scale, o_res, stream),
                           "attention forward launch");
     prism_status st = hip_status(prism::launch_tile_order(sel_offsets, sel_idx, cap, block_offsets, nb, heads, N / 64,
                                                           w.bucket, w.start, w.order, stream),
                                  "tile order launch");
     if (st != PRISM_OK) return st;
     return hip_status(prism::launch_attn_fwd_mfma(q, k, v, o, lse, N, heads, d, ld, hs, block_offsets, nb, sel_offsets,
-                                                  sel_idx, cap, w.order, skip, om, scale, stream),
+                                                  sel_idx, cap, w.order, skip, om, scale, o_res, stream),
                       "attention forward launch");
 }
 
 }  // namespace
 
-prism_status prism_sparse_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, prism_dtype dt,
-                                   int64_t N, int32_t heads, int32_t d, int64_t ld, int64_t hs,
+prism_status prism_sparse_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, void* o_res,
+                                   prism_dtype dt, int64_t N, int32_t heads, int32_t d, int64_t ld, int64_t hs,
                                    const int32_t* block_offsets, int32_t nb, const int32_t* sel_offsets,
                                    const int32_t* sel_idx, int64_t cap, float scale, const prism_raster_layout* out,
                                    void* ws, size_t ws_bytes, hipStream_t stream) {
     prism_status st = check_fwd(q, k, v, o, lse, dt, N, heads, d, ld, hs, block_offsets, nb, sel_offsets, sel_idx, cap,
                                 scale);
     if (st != PRISM_OK) return st;
+    if ((st = check_residual(o_res, dt)) != PRISM_OK) return st;
     prism::RowMap om;
     if ((st = row_map(out, dt, N, ld, hs, om)) != PRISM_OK) return st;
     const size_t need = prism_workspace_size(PRISM_OP_ATTN_FWD, N, heads, d, nb, cap);
     if (!ws || ws_bytes < need)
         return fail(PRISM_E_WORKSPACE, "forward needs %zu workspace bytes, got %zu", need, ws ? ws_bytes : 0);
     Carver c(ws);
-    return exact_fwd(q, k, v, o, lse, dt, N, heads, d, ld, hs, block_offsets, nb, sel_offsets, sel_idx, cap, nullptr,
-                     om, scale, c, stream);
+    return exact_fwd(q, k, v, o, lse, o_res, dt, N, heads, d, ld, hs, block_offsets, nb, sel_offsets, sel_idx, cap,
+                     nullptr, om, scale, c, stream);
 }
 
 prism_status prism_flat_route(const float* logits, int32_t heads, int32_t nb, double flat_ratio, uint8_t* flat,
@@ -593,14 +603,15 @@ prism_status prism_flat_route(const float* logits, int32_t heads, int32_t nb, do
     return hip_status(prism::launch_flat_route(logits, heads, nb, n_flat, M, flat, stream), "flat routing launch");
 }
 
-prism_status prism_routed_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, prism_dtype dt,
-                                   int64_t N, int32_t heads, int32_t d, int64_t ld, int64_t hs,
+prism_status prism_routed_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, void* o_res,
+                                   prism_dtype dt, int64_t N, int32_t heads, int32_t d, int64_t ld, int64_t hs,
                                    const int32_t* block_offsets, int32_t nb, const int32_t* sel_offsets,
                                    const int32_t* sel_idx, int64_t cap, const uint8_t* flat, float scale, void* ws,
                                    size_t ws_bytes, hipStream_t stream) {
     prism_status st = check_fwd(q, k, v, o, lse, dt, N, heads, d, ld, hs, block_offsets, nb, sel_offsets, sel_idx, cap,
                                 scale);
     if (st != PRISM_OK) return st;
+    if ((st = check_residual(o_res, dt)) != PRISM_OK) return st;
     if (!flat) return fail(PRISM_E_ARG, "null pointer argument");
     const size_t need = prism_workspace_size(PRISM_OP_ROUTED_FWD, N, heads, d, nb, cap);
     if (!ws || ws_bytes < need)
@@ -608,8 +619,8 @@ prism_status prism_routed_attn_fwd(const void* q, const void* k, const void* v, 
     Carver c(ws);
     prism::RowMap om;
     row_map(nullptr, dt, N, ld, hs, om);
-    st = exact_fwd(q, k, v, o, lse, dt, N, heads, d, ld, hs, block_offsets, nb, sel_offsets, sel_idx, cap, flat, om,
-                   scale, c, stream);
+    st = exact_fwd(q, k, v, o, lse, o_res, dt, N, heads, d, ld, hs, block_offsets, nb, sel_offsets, sel_idx, cap, flat,
+                   om, scale, c, stream);
     if (st != PRISM_OK) return st;
     float* kbar = c.take<float>(static_cast<size_t>(heads) * nb * d);
     float* vbar = c.take<float>(static_cast<size_t>(heads) * nb * d);
@@ -618,7 +629,7 @@ prism_status prism_routed_attn_fwd(const void* q, const void* k, const void* v, 
                     "block means launch");
     if (st != PRISM_OK) return st;
     return hip_status(prism::launch_attn_flat(q, kbar, vbar, o, lse, bf16, N, heads, d, ld, hs, block_offsets, nb,
-                                              sel_offsets, sel_idx, cap, flat, scale, stream),
+                                              sel_offsets, sel_idx, cap, flat, scale, o_res, stream),
                       "flat attention launch");
 }
 
@@ -665,15 +676,16 @@ prism_status exact_bwd(const void* q, const void* k, const void* v, const void* 
 
 }  // namespace
 
-prism_status prism_sparse_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
-                                   const float* lse, void* dq, void* dk, void* dv, prism_dtype dt, int64_t N,
-                                   int32_t heads, int32_t d, int64_t ld, int64_t hs, const int32_t* block_offsets,
-                                   int32_t nb, const int32_t* sel_offsets, const int32_t* sel_idx, int64_t cap,
-                                   float scale, const prism_raster_layout* io, void* ws, size_t ws_bytes,
-                                   hipStream_t stream) {
+prism_status prism_sparse_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* o_res,
+                                   const void* dout, const float* lse, void* dq, void* dk, void* dv, prism_dtype dt,
+                                   int64_t N, int32_t heads, int32_t d, int64_t ld, int64_t hs,
+                                   const int32_t* block_offsets, int32_t nb, const int32_t* sel_offsets,
+                                   const int32_t* sel_idx, int64_t cap, float scale, const prism_raster_layout* io,
+                                   void* ws, size_t ws_bytes, hipStream_t stream) {
     prism_status st = check_bwd(q, k, v, o, dout, lse, dq, dk, dv, dt, N, heads, d, ld, hs, block_offsets, nb,
                                 sel_offsets, sel_idx, cap, scale);
     if (st != PRISM_OK) return st;
+    if ((st = check_residual(o_res, dt)) != PRISM_OK) return st;
     prism::RowMap om;
     if ((st = row_map(io, dt, N, ld, hs, om)) != PRISM_OK) return st;
     const size_t need = prism_workspace_size(PRISM_OP_ATTN_BWD, N, heads, d, nb, cap);
@@ -681,7 +693,7 @@ prism_status prism_sparse_attn_bwd(const void* q, const void* k, const void* v, 
         return fail(PRISM_E_WORKSPACE, "backward needs %zu workspace bytes, got %zu", need, ws ? ws_bytes : 0);
     Carver c(ws);
     BwdWs w = carve_bwd(c, N, heads, nb, cap);
-    st = hip_status(prism::launch_bwd_dot(o, dout, dt == PRISM_BF16, N, heads, d, ld, hs, om, w.Dq, stream),
+    st = hip_status(prism::launch_bwd_dot(o, dout, dt == PRISM_BF16, N, heads, d, ld, hs, om, w.Dq, o_res, stream),
                     "backward dot launch");
     if (st != PRISM_OK) return st;
     st = hip_status(prism::launch_transpose_csr(sel_offsets, sel_idx, nb, heads, cap, w.tcount, w.tr_offsets, w.tr_idx,
@@ -692,14 +704,16 @@ prism_status prism_sparse_attn_bwd(const void* q, const void* k, const void* v, 
                      cap, scale, w, nullptr, om, stream);
 }
 
-prism_status prism_routed_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
-                                   const float* lse, void* dq, void* dk, void* dv, prism_dtype dt, int64_t N,
-                                   int32_t heads, int32_t d, int64_t ld, int64_t hs, const int32_t* block_offsets,
-                                   int32_t nb, const int32_t* sel_offsets, const int32_t* sel_idx, int64_t cap,
-                                   const uint8_t* flat, float scale, void* ws, size_t ws_bytes, hipStream_t stream) {
+prism_status prism_routed_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* o_res,
+                                   const void* dout, const float* lse, void* dq, void* dk, void* dv, prism_dtype dt,
+                                   int64_t N, int32_t heads, int32_t d, int64_t ld, int64_t hs,
+                                   const int32_t* block_offsets, int32_t nb, const int32_t* sel_offsets,
+                                   const int32_t* sel_idx, int64_t cap, const uint8_t* flat, float scale, void* ws,
+                                   size_t ws_bytes, hipStream_t stream) {
     prism_status st = check_bwd(q, k, v, o, dout, lse, dq, dk, dv, dt, N, heads, d, ld, hs, block_offsets, nb,
                                 sel_offsets, sel_idx, cap, scale);
     if (st != PRISM_OK) return st;
+    if ((st = check_residual(o_res, dt)) != PRISM_OK) return st;
     if (!flat) return fail(PRISM_E_ARG, "null pointer argument");
     const size_t need = prism_workspace_size(PRISM_OP_ROUTED_BWD, N, heads, d, nb, cap);
     if (!ws || ws_bytes < need)
@@ -710,7 +724,8 @@ prism_status prism_routed_attn_bwd(const void* q, const void* k, const void* v, 
     const bool bf16 = dt == PRISM_BF16;
     prism::RowMap om;
     row_map(nullptr, dt, N, ld, hs, om);
-    st = hip_status(prism::launch_bwd_dot(o, dout, bf16, N, heads, d, ld, hs, om, w.Dq, stream), "backward dot launch");
+    st = hip_status(prism::launch_bwd_dot(o, dout, bf16, N, heads, d, ld, hs, om, w.Dq, o_res, stream),
+                    "backward dot launch");
     if (st != PRISM_OK) return st;
     // key block -> sharp query blocks (exact dK/dV) and -> flat query blocks (block-mean gradients)
     st = hip_status(prism::launch_transpose_csr(sel_offsets, sel_idx, nb, heads, cap, w.tcount, w.tr_offsets, w.tr_idx,

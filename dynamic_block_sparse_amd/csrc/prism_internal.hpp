@@ -57,18 +57,18 @@ struct RouteGrad {
 hipError_t launch_attn_fwd_simt(const void* q, const void* k, const void* v, void* o, float* lse, bool bf16, int64_t N,
                                 int heads, int d, int64_t ld, int64_t hs, const int32_t* offs, int nb,
                                 const int32_t* so, const int32_t* si, int64_t cap, const uint8_t* skip,
-                                const RowMap& om, float scale, hipStream_t s);
+                                const RowMap& om, float scale, void* ores, hipStream_t s);
 
 hipError_t launch_attn_fwd_mfma(const void* q, const void* k, const void* v, void* o, float* lse, int64_t N, int heads,
                                 int d, int64_t ld, int64_t hs, const int32_t* offs, int nb, const int32_t* so,
                                 const int32_t* si, int64_t cap, const int32_t* order, const uint8_t* skip,
-                                const RowMap& om, float scale, hipStream_t s);
+                                const RowMap& om, float scale, void* ores, hipStream_t s);
 
 hipError_t launch_bwd_dot(const void* o, const void* dout, bool bf16, int64_t N, int heads, int d, int64_t ld,
-                          int64_t hs, const RowMap& om, float* Dq, hipStream_t s);
+                          int64_t hs, const RowMap& om, float* Dq, const void* ores, hipStream_t s);
 
 hipError_t launch_attn_bwd_mfma(const void* q, const void* k, const void* v, const void* dout, const float* lse,
-                                const float* Dq, void* dq, void* dk, void* dv, int64_t N, int heads, int d, int64_t ld,
+                                float* Dq, void* dq, void* dk, void* dv, int64_t N, int heads, int d, int64_t ld,
                                 int64_t hs, const int32_t* offs, int nb, const int32_t* so, const int32_t* si,
                                 const int32_t* to, const int32_t* ti, int64_t cap, const int32_t* qorder,
                                 const RouteGrad* rg, const RowMap& om, float scale, hipStream_t s);
@@ -111,6 +111,6 @@ hipError_t launch_flat_kgrad(const void* q, const void* dout, const float* kbar,
 hipError_t launch_attn_flat(const void* q, const float* kbar, const float* vbar, void* o, float* lse, bool bf16,
                             int64_t N, int heads, int d, int64_t ld, int64_t hs, const int32_t* offs, int nb,
                             const int32_t* so, const int32_t* si, int64_t cap, const uint8_t* flat, float scale,
-                            hipStream_t s);
+                            void* ores, hipStream_t s);
 
 }  // namespace prism

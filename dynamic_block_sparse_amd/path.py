@@ -131,11 +131,13 @@ class PrismPath:
     def _cap(self):
         return self.nb * self.nb
 
-    def select(self, qp, kp, h0=0, want_logits=False, scoring=None):
+    def select(self, qp, kp, h0=0, want_logits=False, scoring=None, cap=None):
         """scoring: "block" (pooled block scores, prism_select) or "subblock"
-        (prism_select_subblock); default the path's own."""
+        (prism_select_subblock); default the path's own.  cap: CSR capacity per
+        head (default nb * nb, which never truncates)."""
         scoring = scoring or self.scoring
-        nb, hc, cap = self.nb, self.hc, self._cap()
+        nb, hc = self.nb, self.hc
+        cap = self._cap() if cap is None else int(cap)
         offsets = torch.empty((hc, nb + 1), dtype=torch.int32, device=self.device)
         idx = torch.empty((hc, cap), dtype=torch.int32, device=self.device)
         total = torch.empty(hc, dtype=torch.int64, device=self.device)
@@ -155,9 +157,16 @@ class PrismPath:
         zo = self.zone_order.data_ptr() if self.zone_order is not None else None
         return P.PrismRasterLayout(self.T, self.H, self.W, self.zone_shape.data_ptr(), zo, x.stride(0), x.stride(1))
 
-    def forward(self, qp, kp, vp, sel, op=None, lse=None, h0=0, raster=False):
+    def residual_like(self, op):
+        """A buffer for the bf16 residual of O, laid out like op (None for fp32)."""
+        if op.dtype != torch.bfloat16:
+            return None
+        return torch.empty_strided(op.shape, op.stride(), dtype=op.dtype, device=op.device)
+
+    def forward(self, qp, kp, vp, sel, op=None, lse=None, h0=0, raster=False, ores=None):
         """raster: op is (or is allocated as) a raster [N, heads, d] tensor and
-        the kernels write O there directly."""
+        the kernels write O there directly.  ores: None, or a tensor laid out
+        like op that receives the bf16 residual of O (pass it to backward)."""
         hc = self.hc
         if op is None:
             op = torch.empty_like(qp, memory_format=torch.contiguous_format) if raster else self.block_major_like(qp)
@@ -168,7 +177,8 @@ class PrismPath:
         q, k, v, o = (x[:, h0:h0 + hc] for x in (qp, kp, vp, op))
         P.prism_sparse_attn_fwd(q, k, v, o, lse, self.N, hc, self.d, q.stride(0), q.stride(1), self.block_offsets,
                                 self.nb, sel.offsets, sel.idx, sel.cap, self.scale, ws=ws,
-                                layout=self.raster_layout(op) if raster else None)
+                                layout=self.raster_layout(op) if raster else None,
+                                o_res=ores[:, h0:h0 + hc] if ores is not None else None)
         return op, lse
 
     def route(self, sel, flat_ratio, want_sharpness=False):
@@ -180,7 +190,7 @@ class PrismPath:
         P.prism_flat_route(sel.logits, hc, nb, flat_ratio, flat, sharpness=M)
         return (flat, M) if want_sharpness else flat
 
-    def routed_forward(self, qp, kp, vp, sel, flat, op=None, lse=None, h0=0):
+    def routed_forward(self, qp, kp, vp, sel, flat, op=None, lse=None, h0=0, ores=None):
         hc = self.hc
         if op is None:
             op = self.block_major_like(qp)
@@ -190,10 +200,11 @@ class PrismPath:
                          dtype=torch.uint8, device=self.device)
         q, k, v, o = (x[:, h0:h0 + hc] for x in (qp, kp, vp, op))
         P.prism_routed_attn_fwd(q, k, v, o, lse, self.N, hc, self.d, q.stride(0), q.stride(1), self.block_offsets,
-                                self.nb, sel.offsets, sel.idx, sel.cap, flat, self.scale, ws)
+                                self.nb, sel.offsets, sel.idx, sel.cap, flat, self.scale, ws,
+                                o_res=ores[:, h0:h0 + hc] if ores is not None else None)
         return op, lse
 
-    def routed_backward(self, qp, kp, vp, op, dop, lse, sel, flat, grads=None, h0=0):
+    def routed_backward(self, qp, kp, vp, op, dop, lse, sel, flat, grads=None, h0=0, ores=None):
         hc = self.hc
         if grads is None:
             grads = tuple(self.block_major_like(qp) for _ in range(3))
@@ -202,12 +213,15 @@ class PrismPath:
                          dtype=torch.uint8, device=self.device)
         q, k, v, o, do, gq, gk, gv = (x[:, h0:h0 + hc] for x in (qp, kp, vp, op, dop, dq, dk, dv))
         P.prism_routed_attn_bwd(q, k, v, o, do, lse, gq, gk, gv, self.N, hc, self.d, q.stride(0), q.stride(1),
-                                self.block_offsets, self.nb, sel.offsets, sel.idx, sel.cap, flat, self.scale, ws)
+                                self.block_offsets, self.nb, sel.offsets, sel.idx, sel.cap, flat, self.scale, ws,
+                                o_res=ores[:, h0:h0 + hc] if ores is not None else None)
         return dq, dk, dv
 
-    def backward(self, qp, kp, vp, op, dop, lse, sel, grads=None, h0=0, raster=False):
+    def backward(self, qp, kp, vp, op, dop, lse, sel, grads=None, h0=0, raster=False, ores=None):
         """raster: op and the gradients are raster [N, heads, d] tensors with
-        one set of strides (the kernels read O and write dQ, dK, dV there)."""
+        one set of strides (the kernels read O and write dQ, dK, dV there).
+        ores: the residual of O written by forward (None: rowsum(dO * O) from
+        the rounded O alone)."""
         hc = self.hc
         if grads is None:
             grads = tuple((torch.empty_like(qp, memory_format=torch.contiguous_format) if raster
@@ -220,7 +234,8 @@ class PrismPath:
         q, k, v, o, do, gq, gk, gv = (x[:, h0:h0 + hc] for x in (qp, kp, vp, op, dop, dq, dk, dv))
         P.prism_sparse_attn_bwd(q, k, v, o, do, lse, gq, gk, gv, self.N, hc, self.d, q.stride(0), q.stride(1),
                                 self.block_offsets, self.nb, sel.offsets, sel.idx, sel.cap, self.scale, ws,
-                                layout=self.raster_layout(op) if raster else None)
+                                layout=self.raster_layout(op) if raster else None,
+                                o_res=ores[:, h0:h0 + hc] if ores is not None else None)
         return dq, dk, dv
 
     def release_selection(self):
@@ -248,13 +263,14 @@ class PrismPath:
         qp, kp, vp = self.permute(q), self.permute(k), self.permute(v)
         dop = self.permute(do) if do is not None else None
         op = torch.empty_like(q)
+        ores = self.residual_like(op) if do is not None else None
         grads = tuple(torch.empty_like(q) for _ in range(3)) if do is not None else None
         lses, sels = [], []
         for g, h0 in enumerate(range(0, self.heads, self.hc)):
             sel = self._reuse[g] if reuse else self.select(qp, kp, h0)
-            _, lse = self.forward(qp, kp, vp, sel, op=op, h0=h0, raster=True)
+            _, lse = self.forward(qp, kp, vp, sel, op=op, h0=h0, raster=True, ores=ores)
             if do is not None:
-                self.backward(qp, kp, vp, op, dop, lse, sel, grads=grads, h0=h0, raster=True)
+                self.backward(qp, kp, vp, op, dop, lse, sel, grads=grads, h0=h0, raster=True, ores=ores)
             lses.append(lse)
             sels.append(sel)
         if not reuse:

@@ -59,16 +59,16 @@ _lib.prism_hilbert_zone_order.restype = C.c_int
 _lib.prism_select.argtypes = [_vp, _vp, _i32, _i64, _i32, _i32, _i64, _i64, _vp, _i32, _i32, _f64, _f32, _vp, _vp,
                               _i64, _vp, _vp, _vp, _sz, _vp]
 _lib.prism_select_subblock.argtypes = _lib.prism_select.argtypes
-_lib.prism_sparse_attn_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i64, _i64, _vp, _i32, _vp,
+_lib.prism_sparse_attn_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i64, _i64, _vp, _i32, _vp,
                                        _vp, _i64, _f32, C.POINTER(PrismRasterLayout), _vp, _sz, _vp]
-_lib.prism_sparse_attn_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i64,
+_lib.prism_sparse_attn_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i64,
                                        _i64, _vp, _i32, _vp, _vp, _i64, _f32, C.POINTER(PrismRasterLayout), _vp, _sz,
                                        _vp]
 _lib.prism_audio_norm_map.argtypes = [_vp, _i32, _i64, _i64, _i64, _vp, _vp, _vp, _sz, _vp]
 _lib.prism_flat_route.argtypes = [_vp, _i32, _i32, _f64, _vp, _vp, _vp, _sz, _vp]
-_lib.prism_routed_attn_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i64, _i64, _vp, _i32, _vp,
+_lib.prism_routed_attn_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i64, _i64, _vp, _i32, _vp,
                                        _vp, _i64, _vp, _f32, _vp, _sz, _vp]
-_lib.prism_routed_attn_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i64,
+_lib.prism_routed_attn_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i64,
                                        _i64, _vp, _i32, _vp, _vp, _i64, _vp, _f32, _vp, _sz, _vp]
 for _f in ("prism_flat_route", "prism_routed_attn_fwd", "prism_routed_attn_bwd", "prism_audio_norm_map", "prism_zone_shapes", "prism_block_permute", "prism_block_permute_heads", "prism_select",
            "prism_select_subblock", "prism_sparse_attn_fwd", "prism_sparse_attn_bwd"):
@@ -198,9 +198,11 @@ def prism_select_subblock(q, k, N, heads, d, ld, hs, block_offsets, nb, top_k, t
 
 
 def prism_sparse_attn_fwd(q, k, v, o, lse, N, heads, d, ld, hs, block_offsets, nb, sel_offsets, sel_idx, cap, scale,
-                          ws=None, stream=None, dtype=None, layout=None):
-    """layout: None (o block-major with q's strides) or a PrismRasterLayout."""
-    st = _lib.prism_sparse_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _dt(q) if dtype is None else dtype,
+                          ws=None, stream=None, dtype=None, layout=None, o_res=None):
+    """layout: None (o block-major with q's strides) or a PrismRasterLayout.
+    o_res: None or a tensor laid out like o that receives the bf16 residual of O."""
+    st = _lib.prism_sparse_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(o_res),
+                                    _dt(q) if dtype is None else dtype,
                                     N, heads, d, ld, hs, _ptr(block_offsets), nb, _ptr(sel_offsets), _ptr(sel_idx), cap,
                                     float(scale), C.byref(layout) if layout is not None else None, _ptr(ws),
                                     ws.numel() * ws.element_size() if ws is not None else 0, _stream(stream))
@@ -214,8 +216,9 @@ def prism_flat_route(logits, heads, nb, flat_ratio, flat, sharpness=None, ws=Non
 
 
 def prism_routed_attn_fwd(q, k, v, o, lse, N, heads, d, ld, hs, block_offsets, nb, sel_offsets, sel_idx, cap, flat,
-                          scale, ws, stream=None, dtype=None):
-    st = _lib.prism_routed_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _dt(q) if dtype is None else dtype,
+                          scale, ws, stream=None, dtype=None, o_res=None):
+    st = _lib.prism_routed_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(o_res),
+                                    _dt(q) if dtype is None else dtype,
                                     N, heads, d, ld, hs, _ptr(block_offsets), nb, _ptr(sel_offsets), _ptr(sel_idx),
                                     cap, _ptr(flat), float(scale), _ptr(ws),
                                     ws.numel() * ws.element_size() if ws is not None else 0, _stream(stream))
@@ -223,8 +226,9 @@ def prism_routed_attn_fwd(q, k, v, o, lse, N, heads, d, ld, hs, block_offsets, n
 
 
 def prism_routed_attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, N, heads, d, ld, hs, block_offsets, nb, sel_offsets,
-                          sel_idx, cap, flat, scale, ws, stream=None, dtype=None):
-    st = _lib.prism_routed_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk),
+                          sel_idx, cap, flat, scale, ws, stream=None, dtype=None, o_res=None):
+    st = _lib.prism_routed_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(o_res), _ptr(dout), _ptr(lse), _ptr(dq),
+                                    _ptr(dk),
                                     _ptr(dv), _dt(q) if dtype is None else dtype, N, heads, d, ld, hs,
                                     _ptr(block_offsets), nb, _ptr(sel_offsets), _ptr(sel_idx), cap, _ptr(flat),
                                     float(scale), _ptr(ws), ws.numel() * ws.element_size() if ws is not None else 0,
@@ -233,9 +237,11 @@ def prism_routed_attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, N, heads, d, ld, hs
 
 
 def prism_sparse_attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, N, heads, d, ld, hs, block_offsets, nb, sel_offsets,
-                          sel_idx, cap, scale, ws, stream=None, dtype=None, layout=None):
-    """layout: None (o, dq, dk, dv block-major with q's strides) or a PrismRasterLayout."""
-    st = _lib.prism_sparse_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk),
+                          sel_idx, cap, scale, ws, stream=None, dtype=None, layout=None, o_res=None):
+    """layout: None (o, dq, dk, dv block-major with q's strides) or a PrismRasterLayout.
+    o_res: None or the forward's residual of O (laid out like o)."""
+    st = _lib.prism_sparse_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(o_res), _ptr(dout), _ptr(lse), _ptr(dq),
+                                    _ptr(dk),
                                     _ptr(dv), _dt(q) if dtype is None else dtype, N, heads, d, ld, hs,
                                     _ptr(block_offsets), nb, _ptr(sel_offsets), _ptr(sel_idx), cap, float(scale),
                                     C.byref(layout) if layout is not None else None, _ptr(ws),

@@ -286,7 +286,15 @@ typedef struct {
  *                  `out` is NULL, else raster as `out` describes
  *   lse            out [heads, N] fp32 natural-log log-sum-exp of the scaled scores,
  *                  indexed by block-major position in either case
- *   sel_offsets, sel_idx, cap  the CSR written by prism_select
+ *   o_res          optional out (NULL: not written; bf16 only, NULL for fp32): the
+ *                  bf16 residual O - bf16(O) of every element, in o's layout and
+ *                  strides.  O + o_res carries O to about 16 bits, which the
+ *                  backward needs for rowsum(dO * O): that row dot computed from
+ *                  the rounded O moves dK by up to 2^-9 |O| |dO| |Q| per user row
+ *   sel_offsets, sel_idx, cap  the CSR written by prism_select; it must be complete
+ *                  (sel_total <= cap for every head, which cap = nb*nb guarantees).
+ *                  Given a truncated one, each row attends over the entries stored
+ *                  for it below cap, and a row with none gets O = 0 and lse = -inf
  *   scale          softmax scale, finite and > 0 (1/sqrt(d)); PRISM_E_ARG otherwise
  *   block_offsets  must be the offsets written by prism_zone_shapes for the same
  *                  grid (every block a whole number of 64-token tiles)
@@ -300,7 +308,7 @@ typedef struct {
  * visiting order: each row is accumulated over its blocks in ascending order.
  */
 prism_status prism_sparse_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
-                                   prism_dtype dt, int64_t N, int32_t heads, int32_t d,
+                                   void* o_res, prism_dtype dt, int64_t N, int32_t heads, int32_t d,
                                    int64_t ld, int64_t hs,
                                    const int32_t* block_offsets, int32_t nb,
                                    const int32_t* sel_offsets, const int32_t* sel_idx, int64_t cap,
@@ -316,8 +324,13 @@ prism_status prism_sparse_attn_fwd(const void* q, const void* k, const void* v, 
  *
  *   o              forward output: block-major with q's strides, or raster as `io`
  *                  describes
+ *   o_res          the forward's residual of O (same layout as o), or NULL: then
+ *                  rowsum(dO * O) is taken from the rounded O alone
  *   dout           upstream gradient, block-major
  *   lse            forward log-sum-exp
+ *   sel_offsets, sel_idx, cap  the CSR given to the forward (complete; with a
+ *                  truncated one the gradient is that of the forward over the
+ *                  stored entries, and a row with none contributes nothing)
  *   dq, dk, dv     out, same dtype, fully overwritten: block-major with q's strides,
  *                  or raster as `io` describes
  *   io             NULL or the raster placement of o, dq, dk and dv (checks as in
@@ -327,7 +340,7 @@ prism_status prism_sparse_attn_fwd(const void* q, const void* k, const void* v, 
  * Deterministic: every output element is accumulated in a fixed order.
  */
 prism_status prism_sparse_attn_bwd(const void* q, const void* k, const void* v, const void* o,
-                                   const void* dout, const float* lse,
+                                   const void* o_res, const void* dout, const float* lse,
                                    void* dq, void* dk, void* dv,
                                    prism_dtype dt, int64_t N, int32_t heads, int32_t d,
                                    int64_t ld, int64_t hs,
@@ -369,8 +382,8 @@ prism_status prism_flat_route(const float* logits, int32_t heads, int32_t nb, do
  * workspace prism_workspace_size(PRISM_OP_ROUTED_FWD, ...) bytes.  Block means
  * are float64 sums rounded once to fp32; the flat path computes in fp32.
  */
-prism_status prism_routed_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, prism_dtype dt,
-                                   int64_t N, int32_t heads, int32_t d, int64_t ld, int64_t hs,
+prism_status prism_routed_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, void* o_res,
+                                   prism_dtype dt, int64_t N, int32_t heads, int32_t d, int64_t ld, int64_t hs,
                                    const int32_t* block_offsets, int32_t nb, const int32_t* sel_offsets,
                                    const int32_t* sel_idx, int64_t cap, const uint8_t* flat, float scale, void* ws,
                                    size_t ws_bytes, hipStream_t stream);
@@ -389,11 +402,12 @@ prism_status prism_routed_attn_fwd(const void* q, const void* k, const void* v, 
  * block-mean gradients are summed per key block in a fixed order and added to
  * the exact dK/dV before rounding.
  */
-prism_status prism_routed_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
-                                   const float* lse, void* dq, void* dk, void* dv, prism_dtype dt, int64_t N,
-                                   int32_t heads, int32_t d, int64_t ld, int64_t hs, const int32_t* block_offsets,
-                                   int32_t nb, const int32_t* sel_offsets, const int32_t* sel_idx, int64_t cap,
-                                   const uint8_t* flat, float scale, void* ws, size_t ws_bytes, hipStream_t stream);
+prism_status prism_routed_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* o_res,
+                                   const void* dout, const float* lse, void* dq, void* dk, void* dv, prism_dtype dt,
+                                   int64_t N, int32_t heads, int32_t d, int64_t ld, int64_t hs,
+                                   const int32_t* block_offsets, int32_t nb, const int32_t* sel_offsets,
+                                   const int32_t* sel_idx, int64_t cap, const uint8_t* flat, float scale, void* ws,
+                                   size_t ws_bytes, hipStream_t stream);
 
 /*
  * prism_hilbert_zone_order - host function (next row after the exact path; the

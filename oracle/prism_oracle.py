@@ -505,12 +505,19 @@ def attn_fwd_block(Qp, Kp, Vp, offs, sel, i, head, scale):
     return (e @ v) / l, (m + np.log(l))[:, 0]
 
 
-def attn_bwd_block(Qp, Kp, Vp, dOp, offs, sel, i, head, scale):
+def attn_bwd_block(Qp, Kp, Vp, dOp, offs, sel, i, head, scale, with_terms=False):
     """Gradient contributions of query block i, by the chain rule of the
     masked softmax: P = softmax(s), dP = dO V^T, dS = P * (dP - rowsum(P*dP)),
     dQ = scale dS K, dK = scale dS^T Q, dV = P^T dO.  The selection itself is a
     constant (no gradient flows through the discrete choice).  Returns
-    (dQ rows of block i, key indices, dK rows, dV rows for those keys)."""
+    (dQ rows of block i, key indices, dK rows, dV rows for those keys).
+
+    with_terms: also return, for every element of dQ, dK and dV, the sum of
+    the squares of the products it sums (sum_t (scale dS_qt k_tc)^2 for dQ,
+    sum_q (scale dS_qt q_qc)^2 for dK, sum_q (P_qt dO_qc)^2 for dV): the scale
+    of the error that rounding one factor of every product (dS or P) to a
+    short format leaves in the sum.  Test infrastructure for the parity bars;
+    the gradient itself does not use it."""
     sc = float(np.float32(scale))
     q = np.asarray(Qp[offs[i]:offs[i + 1], head, :], dtype=np.float64)
     do = np.asarray(dOp[offs[i]:offs[i + 1], head, :], dtype=np.float64)
@@ -522,50 +529,62 @@ def attn_bwd_block(Qp, Kp, Vp, dOp, offs, sel, i, head, scale):
     P = e / e.sum(axis=1, keepdims=True)
     dP = do @ v.T
     dS = P * (dP - (P * dP).sum(axis=1, keepdims=True))
-    return sc * (dS @ k), keys, sc * (dS.T @ q), P.T @ do
+    out = (sc * (dS @ k), keys, sc * (dS.T @ q), P.T @ do)
+    if not with_terms:
+        return out
+    dS2, P2 = dS * dS, P * P
+    return out + (sc * sc * (dS2 @ (k * k)), sc * sc * (dS2.T @ (q * q)), P2.T @ (do * do))
 
 
 def attention(Qp, Kp, Vp, offs, csr_offs, csr_idx, head, scale, dOp=None):
-    """Forward (and backward if dOp is given) of one head over every block."""
+    """Forward (and backward if dOp is given) of one head over every block.
+    With dOp, also the summed squared products of every gradient element
+    (attn_bwd_block's with_terms) as tQ, tK, tV."""
     N, _, d = Qp.shape
     NB = len(offs) - 1
     O = np.zeros((N, d))
     lse = np.zeros(N)
-    dQ = dK = dV = None
+    dQ = dK = dV = tQ = tK = tV = None
     if dOp is not None:
         dQ, dK, dV = np.zeros((N, d)), np.zeros((N, d)), np.zeros((N, d))
+        tQ, tK, tV = np.zeros((N, d)), np.zeros((N, d)), np.zeros((N, d))
     for i in range(NB):
         sel = csr_idx[csr_offs[i]:csr_offs[i + 1]]
         o, l = attn_fwd_block(Qp, Kp, Vp, offs, sel, i, head, scale)
         O[offs[i]:offs[i + 1]] = o
         lse[offs[i]:offs[i + 1]] = l
         if dOp is not None:
-            dq, keys, dk, dv = attn_bwd_block(Qp, Kp, Vp, dOp, offs, sel, i, head, scale)
+            dq, keys, dk, dv, tq, tk, tv = attn_bwd_block(Qp, Kp, Vp, dOp, offs, sel, i, head, scale, with_terms=True)
             dQ[offs[i]:offs[i + 1]] = dq
             dK[keys] += dk
             dV[keys] += dv
-    return dict(O=O, lse=lse, dQ=dQ, dK=dK, dV=dV)
+            tQ[offs[i]:offs[i + 1]] = tq
+            tK[keys] += tk
+            tV[keys] += tv
+    return dict(O=O, lse=lse, dQ=dQ, dK=dK, dV=dV, tQ=tQ, tK=tK, tV=tV)
 
 
-def key_block_grads(Qp, Kp, Vp, dOp, offs, csr_offs, csr_idx, j, head, scale, rows=None):
+def key_block_grads(Qp, Kp, Vp, dOp, offs, csr_offs, csr_idx, j, head, scale, rows=None, with_terms=False):
     """dK and dV rows of key block j alone: the sum over every query block
     whose selected set holds j (used to check sampled key blocks).  `rows`
     optionally limits the scan to candidate query blocks (each is still
-    checked for membership)."""
+    checked for membership).  with_terms: also the summed squared products of
+    every element (as attn_bwd_block)."""
     d = Qp.shape[2]
     B = offs[j + 1] - offs[j]
-    dK = np.zeros((B, d))
-    dV = np.zeros((B, d))
+    dK, dV, tK, tV = np.zeros((B, d)), np.zeros((B, d)), np.zeros((B, d)), np.zeros((B, d))
     NB = len(offs) - 1
     for i in (range(NB) if rows is None else sorted(int(r) for r in rows)):
         sel = csr_idx[csr_offs[i]:csr_offs[i + 1]]
         if j not in set(int(x) for x in sel):
             continue
-        _, keys, dk, dv = attn_bwd_block(Qp, Kp, Vp, dOp, offs, sel, i, head, scale)
+        _, keys, dk, dv, _, tk, tv = attn_bwd_block(Qp, Kp, Vp, dOp, offs, sel, i, head, scale, with_terms=True)
         pos = np.nonzero((keys >= offs[j]) & (keys < offs[j + 1]))[0]
         dK += dk[pos]
         dV += dv[pos]
-    return dK, dV
+        tK += tk[pos]
+        tV += tv[pos]
+    return (dK, dV, tK, tV) if with_terms else (dK, dV)
 
 
 # ----------------------------------------------------------------------------

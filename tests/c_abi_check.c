@@ -67,7 +67,7 @@ int main(void) {
     CHECK(14, strlen(prism_last_error()) > 0);
     const prism_raster_layout bad = {8, 8, 12, (const uint8_t*)0x1000, NULL, 128, 64};
     CHECK(15, prism_sparse_attn_fwd((void*)0x10000, (void*)0x20000, (void*)0x30000, (void*)0x40000,
-                                    (float*)0x50000, PRISM_BF16, 768, 1, 64, 64, 64, (const int32_t*)0x60000, 12,
+                                    (float*)0x50000, NULL, PRISM_BF16, 768, 1, 64, 64, 64, (const int32_t*)0x60000, 12,
                                     (const int32_t*)0x70000, (const int32_t*)0x80000, 144, 0.125f, &bad, NULL, 0,
                                     0) == PRISM_E_GRID);
     printf("c abi ok\n");

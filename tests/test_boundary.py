@@ -195,8 +195,8 @@ def test_attention_rejects():
     fneed = P.prism_workspace_size(P.OP_ATTN_FWD, N, heads, d, nb, cap)
     assert fneed >= 4 * heads * (N // 64)          # at least the tile order
     good = P.PrismRasterLayout(8, 16, 16, Cc, None, heads * d, d)
-    fwd = lambda q=A, dt=1, d=d, o=Cc, ws=B, wsb=fneed, lay=None: lib.prism_sparse_attn_fwd(
-        q, B, Cc, o, A, dt, N, heads, d, 256, 128, B, nb, Cc, A, cap, 0.088,
+    fwd = lambda q=A, dt=1, d=d, o=Cc, ws=B, wsb=fneed, lay=None, res=None: lib.prism_sparse_attn_fwd(
+        q, B, Cc, o, A, res, dt, N, heads, d, 256, 128, B, nb, Cc, A, cap, 0.088,
         ctypes.byref(lay) if lay is not None else None, ws, wsb, None)
     assert fwd(dt=2) == 3
     assert fwd(d=32) == 4
@@ -204,6 +204,9 @@ def test_attention_rejects():
     assert fwd(o=Cc + 8) == 4                      # misaligned
     assert fwd(ws=None) == 5
     assert fwd(wsb=fneed - 16) == 5
+    assert fwd(res=B + 8) == 4                     # misaligned residual
+    assert fwd(res=B, dt=0) == 1                   # residual of an fp32 output
+    assert fwd(res=B, ws=None) == 5                # an aligned bf16 residual passes its checks
     # raster placement of the outputs: grid, token count, zone shapes, strides
     assert fwd(lay=P.PrismRasterLayout(8, 16, 12, Cc, None, heads * d, d)) == 2     # W not a multiple of 8
     assert fwd(lay=P.PrismRasterLayout(8, 16, 8, Cc, None, heads * d, d)) == 1      # 1024 tokens, not N
@@ -214,12 +217,13 @@ def test_attention_rejects():
     assert fwd(lay=good, ws=None) == 5             # a valid layout passes its checks
     need = P.prism_workspace_size(P.OP_ATTN_BWD, N, heads, d, nb, cap)
     assert need > 0
-    bwd = lambda ws=A, wsb=need, dq=A, lay=None: lib.prism_sparse_attn_bwd(
-        A, B, Cc, A, B, Cc, dq, B, Cc, 1, N, heads, d, 256, 128, A, nb, B, Cc, cap, 0.088,
+    bwd = lambda ws=A, wsb=need, dq=A, lay=None, res=None: lib.prism_sparse_attn_bwd(
+        A, B, Cc, A, res, B, Cc, dq, B, Cc, 1, N, heads, d, 256, 128, A, nb, B, Cc, cap, 0.088,
         ctypes.byref(lay) if lay is not None else None, ws, wsb, None)
     assert bwd(ws=None) == 5
     assert bwd(wsb=need - 16) == 5
     assert bwd(dq=None) == 1
+    assert bwd(res=Cc + 4) == 4
     assert bwd(lay=P.PrismRasterLayout(16, 16, 16, Cc, None, heads * d, d)) == 1     # 4096 tokens, not N
     assert bwd(lay=good, ws=None) == 5
 
@@ -270,8 +274,8 @@ def test_flat_route_and_routed_forward_reject():
     cap = nb * nb
     fneed = P.prism_workspace_size(P.OP_ROUTED_FWD, N, heads, d, nb, cap)
     assert fneed > P.prism_workspace_size(P.OP_ATTN_FWD, N, heads, d, nb, cap) + 2 * 4 * heads * nb * d - 1
-    f = lambda fl=B, ws=Cc, wsb=fneed, dt=1: lib.prism_routed_attn_fwd(A, B, Cc, Cc, A, dt, N, heads, d, 256, 128, B, nb,
-                                                                       Cc, A, cap, fl, 0.088, ws, wsb, None)
+    f = lambda fl=B, ws=Cc, wsb=fneed, dt=1: lib.prism_routed_attn_fwd(A, B, Cc, Cc, A, None, dt, N, heads, d, 256, 128,
+                                                                       B, nb, Cc, A, cap, fl, 0.088, ws, wsb, None)
     assert f(dt=2) == 3
     assert f(fl=None) == 1
     assert f(ws=None) == 5
@@ -284,8 +288,9 @@ def test_routed_backward_rejects():
     cap = nb * nb
     need = P.prism_workspace_size(P.OP_ROUTED_BWD, N, heads, d, nb, cap)
     assert need > P.prism_workspace_size(P.OP_ATTN_BWD, N, heads, d, nb, cap) + 4 * 4 * heads * nb * d - 1
-    f = lambda fl=B, ws=A, wsb=need, dq=A: lib.prism_routed_attn_bwd(A, B, Cc, A, B, Cc, dq, B, Cc, 1, N, heads, d, 256,
-                                                                     128, A, nb, B, Cc, cap, fl, 0.088, ws, wsb, None)
+    f = lambda fl=B, ws=A, wsb=need, dq=A: lib.prism_routed_attn_bwd(A, B, Cc, A, None, B, Cc, dq, B, Cc, 1, N, heads, d,
+                                                                     256, 128, A, nb, B, Cc, cap, fl, 0.088, ws, wsb,
+                                                                     None)
     assert f(dq=None) == 1
     assert f(fl=None) == 1
     assert f(ws=None) == 5

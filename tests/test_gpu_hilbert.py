@@ -8,11 +8,11 @@ import pytest
 import torch
 
 from oracle import prism_oracle as orc
+from parity_bars import TOL, assert_close
 from workloads.synth import CONFIGS, custom, make_inputs
 
 pytestmark = pytest.mark.gpu
 
-TOL = {"bf16": (2e-2, 2e-3), "f32": (1e-4, 1e-4)}
 
 CASES = [
     custom("h_bf16_d128", T=16, H=24, W=16, heads=2, d=128, dtype="bf16", top_k=3, top_p=0.8,
@@ -26,14 +26,8 @@ def _np(t):
     return t.detach().float().cpu().numpy()
 
 
-def _close(got, want, dtype, what, grad=False):
-    mx, mean = TOL[dtype]
-    if grad:
-        mx *= max(1.0, float(np.abs(want).max()))
-        mean *= max(1.0, float(np.abs(want).mean()))
-    err = np.abs(got - want)
-    print(f"{what}: max-abs {err.max():.3e} (bar {mx:.2e}) mean-abs {err.mean():.3e}", flush=True)
-    assert err.max() <= mx and err.mean() <= mean, what
+def _close(got, want, dtype, what, grad=False, terms=None):
+    assert_close(np.asarray(got), np.asarray(want), dtype, what, grad=grad, terms=terms)
 
 
 @pytest.mark.parametrize("cfg", CASES, ids=lambda c: c.name)
@@ -68,7 +62,8 @@ def test_hilbert_order_end_to_end(cfg):
         att = orc.attention(Qp, Kp, Vp, offs, co, ci, 0, sc, dOp=dOp)
         _close(_np(out["o"][:, h, :]), orc.to_raster(att["O"], pi), cfg.dtype, f"{cfg.name} O h{h}")
         for g, name in (("dq", "dQ"), ("dk", "dK"), ("dv", "dV")):
-            _close(_np(out[g][:, h, :]), orc.to_raster(att[name], pi), cfg.dtype, f"{cfg.name} {name} h{h}", grad=True)
+            _close(_np(out[g][:, h, :]), orc.to_raster(att[name], pi), cfg.dtype, f"{cfg.name} {name} h{h}", grad=True,
+                   terms=orc.to_raster(att["t" + name[1]], pi))
 
 
 def test_hilbert_order_2k_size(progress):

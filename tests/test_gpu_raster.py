@@ -27,13 +27,18 @@ CASES = [
 def _check(path, x, heads_slice=None):
     qp, kp, vp, dop = (path.permute(x[n]) for n in ("q", "k", "v", "do"))
     sel = path.select(qp, kp)
-    ob, lse = path.forward(qp, kp, vp, sel)
-    orr, lse2 = path.forward(qp, kp, vp, sel, raster=True)
-    gb = path.backward(qp, kp, vp, ob, dop, lse, sel)
-    gr = path.backward(qp, kp, vp, orr, dop, lse2, sel, raster=True)
+    ob = path.block_major_like(qp)
+    orr = torch.empty_like(x["q"])
+    rb, rr = path.residual_like(ob), path.residual_like(orr)
+    _, lse = path.forward(qp, kp, vp, sel, op=ob, ores=rb)
+    _, lse2 = path.forward(qp, kp, vp, sel, op=orr, raster=True, ores=rr)
+    gb = path.backward(qp, kp, vp, ob, dop, lse, sel, ores=rb)
+    gr = path.backward(qp, kp, vp, orr, dop, lse2, sel, raster=True, ores=rr)
     torch.cuda.synchronize()
     assert torch.equal(lse, lse2)
     assert torch.equal(path.permute(ob, inverse=True), orr)
+    if rb is not None:
+        assert torch.equal(path.permute(rb, inverse=True), rr)
     for name, a, b in zip(("dQ", "dK", "dV"), gb, gr):
         assert torch.equal(path.permute(a, inverse=True), b), name
 

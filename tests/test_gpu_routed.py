@@ -14,11 +14,11 @@ import pytest
 import torch
 
 from oracle import prism_oracle as orc
+from parity_bars import TOL, assert_close
 from workloads.synth import CONFIGS, custom, make_inputs
 
 pytestmark = pytest.mark.gpu
 
-TOL = {"bf16": (2e-2, 2e-3), "f32": (1e-4, 1e-4)}
 
 CASES = [
     custom("r_bf16_d128", T=16, H=16, W=24, heads=2, d=128, dtype="bf16", top_k=3, top_p=0.8,
@@ -41,16 +41,8 @@ def _path(cfg, heads=None, hc=None):
                      float(np.float32(1.0 / math.sqrt(cfg.d))), head_chunk=hc)
 
 
-GRAD_TOL = {"bf16": (2e-2, 2e-3), "f32": (1e-4, 1e-4)}
-
-
 def _close_grad(got, want, dtype, what):
-    mx, mean = GRAD_TOL[dtype]
-    mx *= max(1.0, float(np.abs(want).max()))
-    mean *= max(1.0, float(np.abs(want).mean()))
-    err = np.abs(got - want)
-    print(f"{what}: max-abs {err.max():.3e} (bar {mx:.2e}) mean-abs {err.mean():.3e}", flush=True)
-    assert err.max() <= mx and err.mean() <= mean, what
+    assert_close(np.asarray(got), np.asarray(want), dtype, what, grad=True)
 
 
 def _check_head(h, hh, path, sel, flat_g, M_g, op, lse, xs, zs, pi, cfg, ratio, blocks, v_att=None, dq=None):
@@ -166,10 +158,11 @@ def test_routed_forward_2k_size(progress):
     sel = path.select(qp, kp, want_logits=True)
     flat, M = path.route(sel, 0.5, want_sharpness=True)
     op = path.block_major_like(qp).fill_(float("nan"))
-    _, lse = path.routed_forward(qp, kp, vp, sel, flat, op=op)
+    ores = path.residual_like(op)
+    _, lse = path.routed_forward(qp, kp, vp, sel, flat, op=op, ores=ores)
     dop = path.permute(xs["do"])
     grads = tuple(path.block_major_like(qp).fill_(float("nan")) for _ in range(3))
-    path.routed_backward(qp, kp, vp, op, dop, lse, sel, flat, grads=grads)
+    path.routed_backward(qp, kp, vp, op, dop, lse, sel, flat, grads=grads, ores=ores)
     torch.cuda.synchronize()
     assert bool(torch.isfinite(op).all())
     for g in grads:
@@ -194,9 +187,11 @@ def test_routed_backward_small(cfg, ratio):
     qp, kp, vp, dop = (path.permute(x[n]) for n in ("q", "k", "v", "do"))
     sel = path.select(qp, kp, want_logits=True)
     flat = path.route(sel, ratio)
-    op, lse = path.routed_forward(qp, kp, vp, sel, flat)
+    op = path.block_major_like(qp)
+    ores = path.residual_like(op)
+    _, lse = path.routed_forward(qp, kp, vp, sel, flat, op=op, ores=ores)
     grads = tuple(path.block_major_like(qp).fill_(float("nan")) for _ in range(3))
-    path.routed_backward(qp, kp, vp, op, dop, lse, sel, flat, grads=grads)
+    path.routed_backward(qp, kp, vp, op, dop, lse, sel, flat, grads=grads, ores=ores)
     torch.cuda.synchronize()
     for g in grads:
         assert bool(torch.isfinite(g).all())
@@ -212,7 +207,6 @@ def test_routed_backward_small(cfg, ratio):
         assert not flags.any()
         fl = orc.flat_route(orc.block_sharpness(L), ratio)
         np.testing.assert_array_equal(flat[h].cpu().numpy().astype(bool), fl)
-        # the oracle's D uses its float64 O, the GPU's the bf16 O of its forward (within the gradient bar)
         ref = orc.routed_attention(Qp, Kp, Vp, offs, co, ci, fl, 0, sc, dOp=dOp)
         for name, g in (("dQ", grads[0]), ("dK", grads[1]), ("dV", grads[2])):
             _close_grad(_np(g[:, h, :]), ref[name], cfg.dtype, f"{cfg.name} r={ratio} head {h} {name}")
@@ -226,9 +220,11 @@ def test_routed_backward_with_no_flat_block_is_the_exact_backward():
     qp, kp, vp, dop = (path.permute(x[n]) for n in ("q", "k", "v", "do"))
     sel = path.select(qp, kp, want_logits=True)
     flat = path.route(sel, 0.0)
-    op, lse = path.forward(qp, kp, vp, sel)
-    g1 = path.routed_backward(qp, kp, vp, op, dop, lse, sel, flat)
-    g2 = path.backward(qp, kp, vp, op, dop, lse, sel)
+    op = path.block_major_like(qp)
+    ores = path.residual_like(op)
+    _, lse = path.forward(qp, kp, vp, sel, op=op, ores=ores)
+    g1 = path.routed_backward(qp, kp, vp, op, dop, lse, sel, flat, ores=ores)
+    g2 = path.backward(qp, kp, vp, op, dop, lse, sel, ores=ores)
     torch.cuda.synchronize()
     for a, b in zip(g1, g2):
         assert torch.equal(a, b)

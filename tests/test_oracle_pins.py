@@ -578,6 +578,41 @@ def test_key_block_grads_and_unselected_keys():
     assert len(chosen) < c["NB"]
 
 
+def test_squared_product_terms_by_brute_force():
+    """The summed squared products that the parity bars use, against explicit
+    loops over every product of every gradient element: dQ[q,c] sums
+    scale dS[q,t] K[t,c] over keys t, dK[t,c] sums scale dS[q,t] Q[q,c] over
+    queries q, dV[t,c] sums P[q,t] dO[q,c] over queries q (torch autograd
+    supplies P and dS independently of the oracle)."""
+    c = _tiny_case(seed=6, H=8, W=8, d=4, k=2, p=0.5)
+    M = torch.from_numpy(_mask(c))
+    out = orc.attention(c["Qp"], c["Kp"], c["Vp"], c["offs"], c["co"], c["ci"], 0, c["scale"], dOp=c["dOp"])
+    sc = float(np.float32(c["scale"]))
+    q, k, v = (torch.from_numpy(c[x][:, 0, :]) for x in ("Q", "K", "V"))
+    do = torch.from_numpy(c["dO"][:, 0, :])
+    s = (sc * (q @ k.T)).masked_fill(~M, float("-inf")).requires_grad_(True)
+    Pm = torch.softmax(s, dim=1)
+    (Pm @ v).backward(do)
+    P, dS = Pm.detach().numpy(), (s.grad / 1.0).numpy()     # dS = dL/ds (the score gradient before the scale)
+    Q, K, dO = q.numpy(), k.numpy(), do.numpy()
+    N, d = Q.shape
+    tQ, tK, tV = np.zeros((N, d)), np.zeros((N, d)), np.zeros((N, d))
+    for a in range(N):          # every (query a, key b) product, channels side by side
+        for b in range(N):
+            tQ[a] += (sc * dS[a, b] * K[b]) ** 2
+            tK[b] += (sc * dS[a, b] * Q[a]) ** 2
+            tV[b] += (P[a, b] * dO[a]) ** 2
+    assert 0 < (P > 0).mean() < 1
+    for name, want in (("tQ", tQ), ("tK", tK), ("tV", tV)):
+        np.testing.assert_allclose(orc.to_raster(out[name], c["pi"]), want, rtol=1e-10, atol=1e-300)
+    j = int(c["ci"][0])
+    offs = c["offs"]
+    _, _, tk, tv = orc.key_block_grads(c["Qp"], c["Kp"], c["Vp"], c["dOp"], offs, c["co"], c["ci"], j, 0,
+                                       c["scale"], with_terms=True)
+    np.testing.assert_allclose(tk, out["tK"][offs[j]:offs[j + 1]], rtol=1e-12, atol=1e-300)
+    np.testing.assert_allclose(tv, out["tV"][offs[j]:offs[j + 1]], rtol=1e-12, atol=1e-300)
+
+
 # ---------------------------------------------------------------- end to end
 
 def test_zone_shapes_on_a_designed_grid():
@@ -743,6 +778,50 @@ def test_hilbert_order_walks_face_adjacent_zones_on_cubes(n):
     assert (coords[0] == 0).all()                                 # starts at the origin
     for a, b in zip(coords, coords[1:]):
         assert int(np.abs(a - b).sum()) == 1                      # one step along one axis
+
+
+def _subcube_runs_contiguous(order, dims, j):
+    """True when, along `order` (raster zone indices over a grid of `dims`
+    zones), the zones of every aligned 2^j sub-cube form one contiguous run."""
+    coords = np.array(np.unravel_index(np.asarray(order), dims)).T
+    cube_id = [tuple(c >> j) for c in coords]
+    seen, prev = set(), None
+    for c in cube_id:
+        if c != prev:
+            if c in seen:
+                return False
+            seen.add(c)
+            prev = c
+    return True
+
+
+@pytest.mark.parametrize("n", [2, 4, 8])
+def test_hilbert_order_visits_every_aligned_subcube_in_one_run(n):
+    """The defining property of a Hilbert curve: it fills each aligned 2^j
+    sub-cube completely before it leaves it, at every level j.  A snake
+    (boustrophedon) walk is also face-adjacent, but it leaves a 2-cube after
+    two zones and comes back later, so it fails here."""
+    order = orc.hilbert_zone_order(8 * n, 8 * n, 8 * n)
+    for j in range(1, int(math.log2(n)) + 1):
+        assert _subcube_runs_contiguous(order, (n, n, n), j), j
+    snake = []
+    for t in range(n):
+        for hh in range(n):
+            hs = hh if t % 2 == 0 else n - 1 - hh
+            ws = range(n) if (t * n + hh) % 2 == 0 else range(n - 1, -1, -1)
+            snake += [(t * n + hs) * n + w for w in ws]
+    assert sorted(snake) == list(range(n ** 3))
+    if n >= 4:   # on a 2-cube the only aligned 2-cube is the whole grid
+        assert not _subcube_runs_contiguous(snake, (n, n, n), 1)
+
+
+def test_hilbert_order_keeps_subcube_runs_on_other_grids():
+    """On a grid that is not a power-of-two cube the zones outside it are
+    skipped, so every aligned sub-cube's part inside the grid is still one run."""
+    dims = (3, 5, 2)
+    order = orc.hilbert_zone_order(8 * dims[0], 8 * dims[1], 8 * dims[2])
+    for j in (1, 2):
+        assert _subcube_runs_contiguous(order, dims, j), j
 
 
 def test_hilbert_order_on_other_grids_is_the_cube_order_restricted():

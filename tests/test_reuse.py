@@ -9,6 +9,8 @@ import numpy as np
 import pytest
 import torch
 
+from parity_bars import assert_close
+
 from oracle import prism_oracle as orc
 from workloads.synth import custom, make_inputs
 
@@ -45,21 +47,14 @@ CFG = custom("reuse_bf16", T=16, H=16, W=24, heads=2, d=128, dtype="bf16", top_k
 CFG_NEXT = custom("reuse_bf16_next", T=16, H=16, W=24, heads=2, d=128, dtype="bf16", top_k=3, top_p=0.8,
                   kinds=(("smooth", 0.5), ("static", 0.25), ("fast1", 0.25)),
                   sigma={"smooth": 0.3, "static": 1e-3, "fast1": 0.1}, n_blobs=2, blob_std=(3.0, 4.0, 4.0), seed=92)
-TOL = (2e-2, 2e-3)
 
 
 def _np(t):
     return t.detach().float().cpu().numpy()
 
 
-def _close(got, want, what, grad=False):
-    mx, mean = TOL
-    if grad:
-        mx *= max(1.0, float(np.abs(want).max()))
-        mean *= max(1.0, float(np.abs(want).mean()))
-    err = np.abs(got - want)
-    print(f"{what}: max-abs {err.max():.3e} (bar {mx:.2e}) mean-abs {err.mean():.3e}", flush=True)
-    assert err.max() <= mx and err.mean() <= mean, what
+def _close(got, want, what, grad=False, terms=None):
+    assert_close(np.asarray(got), np.asarray(want), "bf16", what, grad=grad, terms=terms)
 
 
 @pytest.mark.gpu
@@ -94,4 +89,5 @@ def test_reused_selection_matches_the_oracle_over_the_earlier_sets():
         att = orc.attention(Q2, K2, V2, offs, co, ci, 0, sc, dOp=dO2)
         _close(_np(out2["o"][:, h, :]), orc.to_raster(att["O"], pi), f"O h{h}")
         for g, name in (("dq", "dQ"), ("dk", "dK"), ("dv", "dV")):
-            _close(_np(out2[g][:, h, :]), orc.to_raster(att[name], pi), f"{name} h{h}", grad=True)
+            _close(_np(out2[g][:, h, :]), orc.to_raster(att[name], pi), f"{name} h{h}", grad=True,
+                   terms=orc.to_raster(att["t" + name[1]], pi))
