@@ -45,7 +45,8 @@ def grad_bar(want, dtype, terms=None):
 def assert_close(got, want, dtype, what, grad=False, terms=None):
     """O is a convex combination of V rows, so its bar is absolute.  Gradients
     take grad_bar() element by element, and a mean-abs bar scaled by
-    max(1, mean |reference|).  Prints the worst error-to-bar ratio, where it
+    max(1, mean |reference|), plus (with terms) twice the mean standard
+    deviation of the operand rounding.  Prints the worst error-to-bar ratio, where it
     falls, how many elements exceed the literal absolute bar, and (with terms)
     the worst ratio under the strict bar as well."""
     mx, mean = TOL[dtype]
@@ -54,6 +55,10 @@ def assert_close(got, want, dtype, what, grad=False, terms=None):
     err = np.abs(got - want)
     bar = grad_bar(want, dtype, terms) if grad else np.full_like(want, mx)
     mean_bar = mean * max(1.0, float(np.abs(want).mean())) if grad else mean
+    if grad and terms is not None:
+        # the mean |error| of a zero-mean sum of roundings with standard
+        # deviation s is about 0.8 s; the bar adds two of the mean s
+        mean_bar += 2.0 * float(np.mean(OPERAND_U[dtype] * np.sqrt(np.asarray(terms, dtype=np.float64) / 3.0)))
     ratio = err / bar
     w = np.unravel_index(int(np.argmax(ratio)), ratio.shape)
     strict = ""
