@@ -1,7 +1,8 @@
 // prism_api.cpp - the C ABI declared in include/prism.h: argument checks,
-// workspace carving and kernel launches.  Nothing here allocates device memory
-// or keeps state between calls; errors are reported by status code plus a
-// thread-local message.
+// workspace carving and kernel launches.  Nothing here allocates device
+// memory; errors are reported by status code plus a thread-local message.  The
+// one piece of state is the per-device address of the fixed scratch array that
+// prism_zone_shapes_noalloc uses instead of a workspace.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -10,6 +11,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <utility>
 #include <vector>
@@ -378,24 +380,32 @@ prism_status prism_audio_norm_map(const void* h, prism_dtype dt, int64_t N, int6
                       "norm map launch");
 }
 
-prism_status prism_zone_shapes(int32_t T, int32_t H, int32_t W, const void* v, prism_dtype vdt, int64_t C,
-                               int64_t v_ld, const float* a_map, const prism_shape_params* prm, uint8_t* zone_shape,
-                               int32_t* block_offsets, int32_t* nb_dev, int32_t* nb_host, double* zone_stats, void* ws,
-                               size_t ws_bytes, const int32_t* zone_order, hipStream_t stream) {
+namespace {
+
+prism_status check_zone_args(int32_t T, int32_t H, int32_t W, const void* v, prism_dtype vdt, int64_t C, int64_t v_ld,
+                             const float* a_map, const prism_shape_params* prm, uint8_t* zone_shape,
+                             int32_t* block_offsets, int32_t* nb_dev, prism_shape_params& p) {
     prism_status st = check_grid(T, H, W);
     if (st != PRISM_OK) return st;
     if (vdt != PRISM_F32 && vdt != PRISM_BF16) return fail(PRISM_E_DTYPE, "unknown dtype %d", static_cast<int>(vdt));
     if (!v || !a_map || !zone_shape || !block_offsets || !nb_dev) return fail(PRISM_E_ARG, "null pointer argument");
     if (C <= 0 || v_ld < C) return fail(PRISM_E_ARG, "bad channel count C = %lld or stride v_ld = %lld",
                                         static_cast<long long>(C), static_cast<long long>(v_ld));
-    prism_shape_params p{0.5, 0.25, 1e-6};
+    p = prism_shape_params{0.5, 0.25, 1e-6};
     if (prm) p = *prm;
     if (!(p.tau256 >= 0.0 && p.tau256 <= p.tau128 && p.tau128 <= 1.0) || !(p.eps > 0.0) || !std::isfinite(p.eps))
         return fail(PRISM_E_ARG, "thresholds must satisfy 0 <= tau256 <= tau128 <= 1 and eps > 0");
+    return PRISM_OK;
+}
+
+// the launches of prism_zone_shapes on checked arguments and a large enough
+// scratch (a workspace, or the fixed array of the no-allocation call)
+prism_status zone_shapes_launch(int32_t T, int32_t H, int32_t W, const void* v, prism_dtype vdt, int64_t C,
+                                int64_t v_ld, const float* a_map, const prism_shape_params& p, uint8_t* zone_shape,
+                                int32_t* block_offsets, int32_t* nb_dev, int32_t* nb_host, double* zone_stats,
+                                void* ws, const int32_t* zone_order, hipStream_t stream) {
     const int64_t N = static_cast<int64_t>(T) * H * W;
-    const size_t need = zone_ws(N, C);
-    if (!ws || ws_bytes < need)
-        return fail(PRISM_E_WORKSPACE, "zone_shapes needs %zu workspace bytes, got %zu", need, ws ? ws_bytes : 0);
+    prism_status st = PRISM_OK;
     Carver c(ws);
     const int nZ = static_cast<int>(N / prism::kZoneTokens);
     double* partial = c.take<double>(prism::zone_partial_doubles(nZ, C));
@@ -416,6 +426,80 @@ prism_status prism_zone_shapes(int32_t T, int32_t H, int32_t W, const void* v, p
         st = hip_status(hipStreamSynchronize(stream), "stream synchronize");
     }
     return st;
+}
+
+}  // namespace
+
+prism_status prism_zone_shapes(int32_t T, int32_t H, int32_t W, const void* v, prism_dtype vdt, int64_t C,
+                               int64_t v_ld, const float* a_map, const prism_shape_params* prm, uint8_t* zone_shape,
+                               int32_t* block_offsets, int32_t* nb_dev, int32_t* nb_host, double* zone_stats, void* ws,
+                               size_t ws_bytes, const int32_t* zone_order, hipStream_t stream) {
+    prism_shape_params p;
+    prism_status st = check_zone_args(T, H, W, v, vdt, C, v_ld, a_map, prm, zone_shape, block_offsets, nb_dev, p);
+    if (st != PRISM_OK) return st;
+    const size_t need = zone_ws(static_cast<int64_t>(T) * H * W, C);
+    if (!ws || ws_bytes < need)
+        return fail(PRISM_E_WORKSPACE, "zone_shapes needs %zu workspace bytes, got %zu", need, ws ? ws_bytes : 0);
+    return zone_shapes_launch(T, H, W, v, vdt, C, v_ld, a_map, p, zone_shape, block_offsets, nb_dev, nb_host,
+                              zone_stats, ws, zone_order, stream);
+}
+
+// ---------------------------------------------------------------- zone shapes without allocation
+//
+// prism_zone_shapes_noalloc takes the scratch of prism_zone_shapes (the
+// per-slab partial sums and the per-zone records) from this fixed array.
+// Each GPU that the library runs on holds its own copy until the process
+// ends.  On the host the array's name is only a stand-in, never a device
+// address: the address is looked up once per device, with that device
+// current, and kept in g_scratch, and only that address reaches a kernel.
+// Every scratch value is written before it is read, so nothing is cleared
+// between calls; calls that overlap on one GPU share the array and race.
+
+static __device__ __align__(256) unsigned char scratch[PRISM_ZONE_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices];
+
+// the current device's address of `scratch`
+prism_status current_scratch(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(PRISM_E_UNSUPPORTED, "device %d: the no-allocation scratch covers devices 0..%d", dev,
+                    kMaxDevices - 1);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) return hip_status(e != hipSuccess ? e : hipErrorInvalidSymbol, "scratch address");
+        g_scratch[dev] = p;
+    }
+    *out = g_scratch[dev];
+    return PRISM_OK;
+}
+
+}  // namespace
+
+prism_status prism_zone_shapes_noalloc(int32_t T, int32_t H, int32_t W, const void* v, prism_dtype vdt, int64_t C,
+                                       int64_t v_ld, const float* a_map, const prism_shape_params* prm,
+                                       uint8_t* zone_shape, int32_t* block_offsets, int32_t* nb_dev, int32_t* nb_host,
+                                       double* zone_stats, const int32_t* zone_order, hipStream_t stream) {
+    prism_shape_params p;
+    prism_status st = check_zone_args(T, H, W, v, vdt, C, v_ld, a_map, prm, zone_shape, block_offsets, nb_dev, p);
+    if (st != PRISM_OK) return st;
+    const size_t need = zone_ws(static_cast<int64_t>(T) * H * W, C);
+    if (need > PRISM_ZONE_SCRATCH_BYTES)
+        return fail(PRISM_E_WORKSPACE,
+                    "zone shapes of this grid need %zu scratch bytes, more than the %zu of the no-allocation call",
+                    need, static_cast<size_t>(PRISM_ZONE_SCRATCH_BYTES));
+    void* ws = nullptr;
+    if ((st = current_scratch(&ws)) != PRISM_OK) return st;
+    return zone_shapes_launch(T, H, W, v, vdt, C, v_ld, a_map, p, zone_shape, block_offsets, nb_dev, nb_host,
+                              zone_stats, ws, zone_order, stream);
 }
 
 prism_status prism_block_permute(int32_t T, int32_t H, int32_t W, const uint8_t* zone_shape, const void* x, void* y,

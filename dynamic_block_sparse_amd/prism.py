@@ -26,7 +26,8 @@ ZS_STRIDE = 16
 STATUS = {0: "PRISM_OK", 1: "PRISM_E_ARG", 2: "PRISM_E_GRID", 3: "PRISM_E_DTYPE",
           4: "PRISM_E_UNSUPPORTED", 5: "PRISM_E_WORKSPACE", 6: "PRISM_E_HIP"}
 
-EXPORTS = ["prism_hilbert_zone_order", "prism_audio_norm_map", "prism_zone_shapes", "prism_block_permute", "prism_block_permute_heads", "prism_select",
+EXPORTS = ["prism_hilbert_zone_order", "prism_audio_norm_map", "prism_zone_shapes", "prism_zone_shapes_noalloc",
+           "prism_block_permute", "prism_block_permute_heads", "prism_select",
            "prism_select_subblock", "prism_sparse_attn_fwd", "prism_flat_route", "prism_routed_attn_fwd", "prism_routed_attn_bwd",
            "prism_sparse_attn_bwd", "prism_workspace_size", "prism_status_string", "prism_last_error",
            "prism_candidate_shapes"]
@@ -51,6 +52,8 @@ class PrismError(RuntimeError):
 _vp, _i32, _i64, _f32, _f64, _sz = C.c_void_p, C.c_int32, C.c_int64, C.c_float, C.c_double, C.c_size_t
 _lib.prism_zone_shapes.argtypes = [_i32, _i32, _i32, _vp, _i32, _i64, _i64, _vp, C.POINTER(PrismShapeParams), _vp,
                                    _vp, _vp, C.POINTER(_i32), _vp, _vp, _sz, _vp, _vp]
+_lib.prism_zone_shapes_noalloc.argtypes = [_i32, _i32, _i32, _vp, _i32, _i64, _i64, _vp, C.POINTER(PrismShapeParams),
+                                           _vp, _vp, _vp, C.POINTER(_i32), _vp, _vp, _vp]
 _lib.prism_block_permute.argtypes = [_i32, _i32, _i32, _vp, _vp, _vp, _i32, _i64, _i64, _i64, _i32, _vp, _vp]
 _lib.prism_block_permute_heads.argtypes = [_i32, _i32, _i32, _vp, _vp, _vp, _i32, _i32, _i32, _i64, _i64, _i64, _i64,
                                            _i32, _vp, _vp]
@@ -70,7 +73,7 @@ _lib.prism_routed_attn_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i64,
                                        _vp, _i64, _vp, _f32, _vp, _sz, _vp]
 _lib.prism_routed_attn_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i64,
                                        _i64, _vp, _i32, _vp, _vp, _i64, _vp, _f32, _vp, _sz, _vp]
-for _f in ("prism_flat_route", "prism_routed_attn_fwd", "prism_routed_attn_bwd", "prism_audio_norm_map", "prism_zone_shapes", "prism_block_permute", "prism_block_permute_heads", "prism_select",
+for _f in ("prism_zone_shapes_noalloc", "prism_flat_route", "prism_routed_attn_fwd", "prism_routed_attn_bwd", "prism_audio_norm_map", "prism_zone_shapes", "prism_block_permute", "prism_block_permute_heads", "prism_select",
            "prism_select_subblock", "prism_sparse_attn_fwd", "prism_sparse_attn_bwd"):
     getattr(_lib, _f).restype = C.c_int
 _lib.prism_workspace_size.argtypes = [_i32, _i64, _i32, _i32, _i32, _i64]
@@ -146,6 +149,23 @@ def prism_zone_shapes(T, H, W, v, C_, v_ld, a_map, zone_shape, block_offsets, nb
                                 _stream(stream))
     _check(st)
     return int(nb_host.value) if want_nb else None
+
+
+def prism_zone_shapes_noalloc(T, H, W, v, C_, v_ld, a_map, zone_shape, block_offsets, nb_dev, prm=None,
+                              zone_stats=None, want_nb=True, stream=None, dtype=None, zone_order=None):
+    """prism_zone_shapes with its scratch in the library's fixed device array
+    (no workspace, nothing allocated); returns NB when want_nb."""
+    nb_host = _i32(-1)
+    p = PrismShapeParams(*prm) if prm is not None else None
+    st = _lib.prism_zone_shapes_noalloc(T, H, W, _ptr(v), _dt(v) if dtype is None else dtype, C_, v_ld, _ptr(a_map),
+                                        C.byref(p) if p is not None else None, _ptr(zone_shape), _ptr(block_offsets),
+                                        _ptr(nb_dev), C.byref(nb_host) if want_nb else None, _ptr(zone_stats),
+                                        _ptr(zone_order), _stream(stream))
+    _check(st)
+    return int(nb_host.value) if want_nb else None
+
+
+ZONE_SCRATCH_BYTES = 8 << 20   # PRISM_ZONE_SCRATCH_BYTES
 
 
 def prism_block_permute(T, H, W, zone_shape, x, y, row_elems, x_ld, y_ld, inverse, stream=None, dtype=None,

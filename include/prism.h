@@ -155,6 +155,32 @@ prism_status prism_zone_shapes(int32_t T, int32_t H, int32_t W,
                                void* ws, size_t ws_bytes, const int32_t* zone_order, hipStream_t stream);
 
 /*
+ * prism_zone_shapes_noalloc - prism_zone_shapes for callers that cannot
+ * allocate device memory (code under stream capture into a graph, tight
+ * serving loops, harnesses that forbid hipMalloc): the same arguments, checks,
+ * kernels and outputs, without `ws` and `ws_bytes`.  Its scratch is a fixed
+ * device array of PRISM_ZONE_SCRATCH_BYTES inside the library, one per GPU,
+ * held until the process ends; the call allocates nothing (nb_host, when not
+ * NULL, still synchronizes the stream).
+ *   Limit: the scratch that prism_workspace_size(PRISM_OP_ZONE_SHAPES, N, 0, C,
+ *   0, 0) reports must fit in PRISM_ZONE_SCRATCH_BYTES, about
+ *   nZ * (3 ceil(C / 256) + 16) * 8 bytes (20,000 zones, 10 million tokens, at
+ *   C = 3072); a larger grid returns PRISM_E_WORKSPACE before any launch.
+ *   Every call on one GPU shares that GPU's array: calls that overlap on one
+ *   GPU (two streams, two threads) race and must be serialized.  Each call
+ *   writes every scratch value before it reads it, so nothing left by an
+ *   earlier call reaches the outputs.
+ * Status: as prism_zone_shapes; PRISM_E_UNSUPPORTED on a device index above 63.
+ */
+#define PRISM_ZONE_SCRATCH_BYTES (8u << 20)
+prism_status prism_zone_shapes_noalloc(int32_t T, int32_t H, int32_t W,
+                                       const void* v, prism_dtype vdt, int64_t C, int64_t v_ld,
+                                       const float* a_map, const prism_shape_params* prm,
+                                       uint8_t* zone_shape, int32_t* block_offsets, int32_t* nb_dev,
+                                       int32_t* nb_host, double* zone_stats,
+                                       const int32_t* zone_order, hipStream_t stream);
+
+/*
  * prism_block_permute - gather rows from raster into block-major order
  * (inverse = 0: y[p] = x[pi(p)]) or scatter them back (inverse = 1:
  * y[pi(p)] = x[p]), pi being the block-major order defined above for the zone

@@ -312,3 +312,22 @@ def test_hilbert_zone_order_rejects():
     buf = (ctypes.c_int32 * 8)()
     assert lib.prism_hilbert_zone_order(12, 8, 8, buf) == 2
     assert lib.prism_hilbert_zone_order(8, 8, 8, None) == 1
+
+
+def test_zone_shapes_noalloc_rejects_before_any_launch():
+    """The no-allocation zone shapes call checks its arguments like
+    prism_zone_shapes and rejects a grid whose scratch exceeds the fixed
+    array (PRISM_E_WORKSPACE) before it looks up the array or launches."""
+    lib, P = _lib()
+    f = lambda T=8, H=8, W=8, v=A, C_=128, a=B, zs=Cc: lib.prism_zone_shapes_noalloc(
+        T, H, W, v, 1, C_, C_, a, None, zs, Cc, Cc, None, None, None, None)
+    assert f(T=12) == 2
+    assert f(v=None) == 1
+    assert f(C_=0) == 1
+    # 64 x 64 x 64 zones at 3072 channels: about 109 MB of scratch
+    big = P.prism_workspace_size(P.OP_ZONE_SHAPES, 512 ** 3, 0, 3072, 0, 0)
+    assert big > P.ZONE_SCRATCH_BYTES
+    assert f(T=512, H=512, W=512, C_=3072) == 5
+    assert "no-allocation" in P.prism_last_error()
+    # the 2K workload's grid fits
+    assert P.prism_workspace_size(P.OP_ZONE_SHAPES, 64 * 72 * 128, 0, 3072, 0, 0) <= P.ZONE_SCRATCH_BYTES
