@@ -40,14 +40,29 @@ CSRC = os.path.join(ROOT, "dynamic_block_sparse_amd", "csrc")
 # kernels launched by one tile-order build, one prism_sparse_attn_fwd and one
 # prism_sparse_attn_bwd call, with their launch counts (csr_scan and fill_i32
 # also run elsewhere, always over the same heads x blocks shape)
+# (one head group: the workload's heads fit the library's default group)
+SPLIT_KERNELS = {"fill_i32_kernel": 3, "csr_scan_kernel": 2, "split_cost_kernel": 1, "split_pick_kernel": 1,
+                 "split_rows_kernel": 1, "split_count_kernel": 1, "split_fill_kernel": 1}
 ORDER_KERNELS = {"fill_i32_kernel": 2, "order_count_kernel": 1, "csr_scan_kernel": 1, "order_fill_kernel": 1}
-FWD_KERNELS = dict(ORDER_KERNELS, attn_fwd_mfma_kernel=1)
-BWD_KERNELS = {"attn_bwd_dot_kernel": 1, "fill_i32_kernel": 2 + 2, "tr_count_kernel": 1, "csr_scan_kernel": 1 + 1,
-               "tr_fill_kernel": 1, "tr_sort_kernel": 1, "order_count_kernel": 1, "order_fill_kernel": 1,
-               "attn_dq_mfma_kernel": 1, "attn_dkdv_mfma_kernel": 1}
-PMC_REGEX = ("attn_|permute_heads|tr_count|tr_fill|tr_sort|csr_scan|order_|fill_i32|zone_profile|pool_kernel|"
+
+
+def _merge(*ds, **kw):
+    out = {}
+    for d in ds + (kw,):
+        for k, v in d.items():
+            out[k] = out.get(k, 0) + v
+    return out
+
+
+FWD_KERNELS = _merge(SPLIT_KERNELS, ORDER_KERNELS, attn_fwd_mfma_kernel=1, attn_fwd_chunk_kernel=1,
+                     attn_fwd_combine_kernel=1)
+BWD_KERNELS = _merge(SPLIT_KERNELS, ORDER_KERNELS, {"attn_bwd_dot_kernel": 1, "fill_i32_kernel": 2,
+                                                    "tr_count_kernel": 1, "csr_scan_kernel": 1, "tr_fill_kernel": 1,
+                                                    "tr_sort_kernel": 1},
+                     attn_dq_mfma_kernel=1, attn_dq_chunk_kernel=1, attn_dq_combine_kernel=1, attn_dkdv_mfma_kernel=1)
+PMC_REGEX = ("attn_|split_|permute_heads|tr_count|tr_fill|tr_sort|csr_scan|order_|fill_i32|zone_profile|pool_kernel|"
              "logits_kernel|select_reg|select_write")
-ATTN_REGEX = "attn_(fwd|dq|dkdv)_mfma"
+ATTN_REGEX = "attn_(fwd|dq|dkdv)_(mfma|chunk)"
 
 
 def parse():
@@ -581,14 +596,13 @@ def main():
         sel_bufs.append(Selection(torch.empty((hc, nb + 1), dtype=torch.int32, device="cuda"),
                                   torch.empty((hc, cap), dtype=torch.int32, device="cuda"),
                                   torch.empty(hc, dtype=torch.int64, device="cuda"), cap, None))
-    ws_zone = torch.empty(P.prism_workspace_size(P.OP_ZONE_SHAPES, cfg.N, 1, cfg.heads * cfg.d, 0, 0),
-                          dtype=torch.uint8, device="cuda")
-    ws_sel = torch.empty(P.prism_workspace_size(P.OP_SELECT, cfg.N, hc, cfg.d, nb, cap), dtype=torch.uint8,
-                         device="cuda")
-    ws_bwd = torch.empty(P.prism_workspace_size(P.OP_ATTN_BWD, cfg.N, hc, cfg.d, nb, cap), dtype=torch.uint8,
-                         device="cuda")
-    ws_fwd = torch.empty(P.prism_workspace_size(P.OP_ATTN_FWD, cfg.N, hc, cfg.d, nb, cap), dtype=torch.uint8,
-                         device="cuda")
+    # the calls run one after another on one stream, so one workspace serves them all
+    ws_sizes = {"zone": P.prism_workspace_size(P.OP_ZONE_SHAPES, cfg.N, 1, cfg.heads * cfg.d, 0, 0),
+                "sel": P.prism_workspace_size(P.OP_SELECT, cfg.N, hc, cfg.d, nb, cap),
+                "fwd": P.prism_workspace_size(P.OP_ATTN_FWD, cfg.N, hc, cfg.d, nb, cap),
+                "bwd": P.prism_workspace_size(P.OP_ATTN_BWD, cfg.N, hc, cfg.d, nb, cap)}
+    ws_all = torch.empty(max(ws_sizes.values()), dtype=torch.uint8, device="cuda")
+    ws_zone, ws_sel, ws_fwd, ws_bwd = (ws_all[:ws_sizes[k]] for k in ("zone", "sel", "fwd", "bwd"))
     C = cfg.heads * cfg.d
     stages = ["shapes", "permute_in", "select", "attn_fwd", "attn_bwd"]
     # the attention kernels write O, dQ, dK and dV straight to raster order

@@ -22,7 +22,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libprism.so")
 
-SOURCES = ["norm_map.hip", "flat.hip", "zone_kernels.hip", "permute.hip", "select.hip", "attn_simt.hip", "attn_fwd.hip", "attn_bwd.hip",
+SOURCES = ["norm_map.hip", "flat.hip", "zone_kernels.hip", "permute.hip", "select.hip", "attn_simt.hip", "attn_split.hip",
+           "attn_fwd.hip", "attn_bwd.hip",
            "prism_api.cpp"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")

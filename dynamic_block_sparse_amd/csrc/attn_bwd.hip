@@ -2,6 +2,7 @@
 //
 // Built with the default accumulator-register form of MFMA (see build.py).
 #include "attn_common.hpp"
+#include "attn_split.hpp"
 
 namespace prism {
 
@@ -40,27 +41,23 @@ namespace prism {
 // query tiles in L2.
 
 template <int D>
-__global__ void __launch_bounds__(128, 2)
-attn_dq_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-                    const uint16_t* __restrict__ dout, const float* __restrict__ lse, float* __restrict__ Dq,
-                    uint16_t* __restrict__ dq, int64_t N, int64_t ld, int64_t hs, const int32_t* __restrict__ offs,
-                    int nb, const int32_t* __restrict__ sel_off, const int32_t* __restrict__ sel_idx, int64_t cap,
-                    const int32_t* __restrict__ order, const uint8_t* __restrict__ skip, const RowMap om,
-                    float scale_log2, float scale) {
-    __shared__ uint16_t kbuf[1][64 * D], vbuf[1][64 * D];
-    const int ntiles = static_cast<int>(N / 64);
-    const int wg = xcd_remap(blockIdx.x);
-    const int h = wg / ntiles;
-    const int64_t p0 = static_cast<int64_t>(tile_of(order, wg, ntiles)) * 64;
+struct DqState {
+    f32x16_t acc[D / 32];   // dQ^T of the wave's 32 rows (before the scale)
+    float dex;              // this lane's part of sum_t P dP over the keys
+};
+
+// One pass of the workgroup's query tile (rows p0 .. p0+63 of head h) over the
+// key tiles of selected entries e0 .. e1-1 of `si`.
+template <int D>
+__device__ __forceinline__ void dq_pass(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kh_,
+                                        const uint16_t* __restrict__ vh_, const uint16_t* __restrict__ dout,
+                                        const float* __restrict__ lse, const float* __restrict__ Dq, int64_t N,
+                                        int64_t ld, int64_t hs, int h, int64_t p0, const int32_t* __restrict__ offs,
+                                        const int32_t* __restrict__ si, int e0, int e1, uint16_t* kb, uint16_t* vb,
+                                        float scale_log2, DqState<D>& st) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int hl = lane >> 5, col = lane & 31;
-    const int i = find_block(offs, nb, p0);
-    if (skip && skip[static_cast<int64_t>(h) * nb + i]) return;   // routed to another path
-    const int32_t* __restrict__ so = sel_off + static_cast<int64_t>(h) * (nb + 1);
-    const int32_t* __restrict__ si = sel_idx + static_cast<int64_t>(h) * cap;
-    const int e0 = so[i];
-    const int e1 = static_cast<int>(min(static_cast<int64_t>(so[i + 1]), cap));
     constexpr int KS = D / 16, DM = D / 32;
     const int64_t row = p0 + 32 * wave + col;
     u32x4_t qb[KS], db[KS];
@@ -82,26 +79,23 @@ attn_dq_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     }
     settle(lrow);
     settle(drow);
-    f32x16_t acc[DM];
 #pragma unroll
     for (int m = 0; m < DM; ++m)
 #pragma unroll
-        for (int x = 0; x < 16; ++x) acc[m][x] = 0.0f;
-    float dex = 0.0f;   // this lane's part of sum_t P dP over the row's keys
-    const uint16_t* __restrict__ kh_ = k + h * hs;
-    const uint16_t* __restrict__ vh_ = v + h * hs;
+        for (int x = 0; x < 16; ++x) st.acc[m][x] = 0.0f;
+    float dex = 0.0f;
 
     TileDma<D, 2> dma;
     dma.init(ld, wave, lane);
     constexpr int PER = TileDma<D, 2>::PER;
-    const uint16_t* kt = kbuf[0];
-    const uint16_t* vt = vbuf[0];
+    const uint16_t* kt = kb;
+    const uint16_t* vt = vb;
     TileCursor cur;
     cur.init(si, offs, e0, e1);
     int t = cur.next();
     if (t >= 0) {
-        dma.load(vbuf[0], vh_ + static_cast<int64_t>(t) * ld, wave);
-        dma.load(kbuf[0], kh_ + static_cast<int64_t>(t) * ld, wave);
+        dma.load(vb, vh_ + static_cast<int64_t>(t) * ld, wave);
+        dma.load(kb, kh_ + static_cast<int64_t>(t) * ld, wave);
         asm volatile("s_waitcnt vmcnt(%0)" ::"n"(PER) : "memory");   // this wave's V loads
         __syncthreads();
         while (true) {
@@ -111,21 +105,11 @@ attn_dq_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
 #pragma unroll
                 for (int x = 0; x < 16; ++x) sa[mt][x] = pa[mt][x] = 0.0f;
             // dP^T first: it needs only V, while K may still be landing
-#pragma unroll
-            for (int s = 0; s < KS; ++s)
-#pragma unroll
-                for (int mt = 0; mt < 2; ++mt)
-                    pa[mt] = mfma32(sw_read16<D>(vt, 32 * mt + col, 16 * s + 8 * hl), db[s], pa[mt]);
-            sched_reads_ahead<2, 2, KS, 2>();
+            rows_x_ksteps<D>(vt, col, hl, db, pa[0], pa[1]);
             dma_join();                        // K(t) landed; every wave is done with V(t)
             const int tn = cur.next();
-            if (tn >= 0) dma.load(vbuf[0], vh_ + static_cast<int64_t>(tn) * ld, wave);
-#pragma unroll
-            for (int s = 0; s < KS; ++s)
-#pragma unroll
-                for (int mt = 0; mt < 2; ++mt)
-                    sa[mt] = mfma32(sw_read16<D>(kt, 32 * mt + col, 16 * s + 8 * hl), qb[s], sa[mt]);
-            sched_reads_ahead<2, 2, KS, 2>();
+            if (tn >= 0) dma.load(vb, vh_ + static_cast<int64_t>(tn) * ld, wave);
+            rows_x_ksteps<D>(kt, col, hl, qb, sa[0], sa[1]);
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
@@ -138,28 +122,142 @@ attn_dq_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
             for (int ks = 0; ks < 4; ++ks) {
                 const u32x4_t bs = pack_kstep(sa[ks >> 1], ks & 1);
 #pragma unroll
-                for (int m = 0; m < DM; ++m) acc[m] = mfma32(tr_operand<D>(kt, 16 * ks, 32 * m, lane), bs, acc[m]);
+                for (int m = 0; m < DM; ++m)
+                    st.acc[m] = mfma32(tr_operand<D>(kt, 16 * ks, 32 * m, lane), bs, st.acc[m]);
             }
             dma_join();                        // V(tn) landed; every wave is done with K(t)
             if (tn < 0) break;
-            dma.load(kbuf[0], kh_ + static_cast<int64_t>(tn) * ld, wave);
+            dma.load(kb, kh_ + static_cast<int64_t>(tn) * ld, wave);
         }
     }
+    st.dex = dex;
+}
+
+// Write dQ (scaled, bf16) of the tile's rows and, in place of the row-dot
+// value, D = sum_t P dP over the row's keys: the definition of rowsum(dO * O)
+// for the exact softmax, from the same fp32 P and dP as dS, which the
+// forward's O (P rounded to bf16 in P V) only approximates.  The dK/dV kernel,
+// launched after, reads it; each row belongs to one workgroup.
+template <int D>
+__device__ __forceinline__ void dq_store(const DqState<D>& st, uint16_t* __restrict__ dq, float* __restrict__ Dq,
+                                         const RowMap& om, int64_t N, int h, int64_t p0, float scale) {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int hl = lane >> 5, col = lane & 31;
+    constexpr int DM = D / 32;
+    const int64_t row = p0 + 32 * wave + col;
     uint16_t* out = dq + row_offset(om, row, h);
 #pragma unroll
     for (int m = 0; m < DM; ++m)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-            const f32x16_t& a = acc[m];
+            const f32x16_t& a = st.acc[m];
             *reinterpret_cast<u32x2_t*>(out + 32 * m + 8 * g + 4 * hl) =
                 u32x2_t{pack2(a[4 * g] * scale, a[4 * g + 1] * scale), pack2(a[4 * g + 2] * scale, a[4 * g + 3] * scale)};
         }
-    // D = sum_t P dP over the row's keys, from the same fp32 P and dP as dS:
-    // the definition of rowsum(dO * O) for the exact softmax, which the
-    // forward's O (P rounded to bf16 in P V) only approximates.  The dK/dV
-    // kernel, launched next, reads it; each row belongs to one workgroup.
-    const float dsum = dex + __shfl_xor(dex, 32, 64);
+    const float dsum = st.dex + __shfl_xor(st.dex, 32, 64);
     if (hl == 0) Dq[static_cast<int64_t>(h) * N + row] = dsum;
+}
+
+template <int D>
+__global__ void __launch_bounds__(128, 2)
+attn_dq_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+                    const uint16_t* __restrict__ dout, const float* __restrict__ lse, float* __restrict__ Dq,
+                    uint16_t* __restrict__ dq, int64_t N, int64_t ld, int64_t hs, const int32_t* __restrict__ offs,
+                    int nb, const int32_t* __restrict__ sel_off, const int32_t* __restrict__ sel_idx, int64_t cap,
+                    const int32_t* __restrict__ order, const uint8_t* __restrict__ skip, const RowMap om,
+                    float scale_log2, float scale) {
+    __shared__ uint16_t kbuf[64 * D], vbuf[64 * D];
+    const int ntiles = static_cast<int>(N / 64);
+    const int wg = xcd_remap(blockIdx.x);
+    const int h = wg / ntiles;
+    const int64_t p0 = static_cast<int64_t>(tile_of(order, wg, ntiles)) * 64;
+    const int i = find_block(offs, nb, p0);
+    if (skip && skip[static_cast<int64_t>(h) * nb + i]) return;   // split into chunks, or routed to another path
+    const int32_t* __restrict__ so = sel_off + static_cast<int64_t>(h) * (nb + 1);
+    const int e0 = so[i];
+    const int e1 = static_cast<int>(min(static_cast<int64_t>(so[i + 1]), cap));
+    DqState<D> st;
+    dq_pass<D>(q, k + h * hs, v + h * hs, dout, lse, Dq, N, ld, hs, h, p0, offs,
+               sel_idx + static_cast<int64_t>(h) * cap, e0, e1, kbuf, vbuf, scale_log2, st);
+    dq_store<D>(st, dq, Dq, om, N, h, p0, scale);
+}
+
+// one key-range chunk of a split row's tile (attn_split.hpp): fp32 partial
+// dQ^T in register layout and the lanes' parts of sum P dP
+template <int D>
+__global__ void __launch_bounds__(128, 2)
+attn_dq_chunk_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+                     const uint16_t* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ Dq,
+                     int64_t N, int64_t ld, int64_t hs, const int32_t* __restrict__ offs,
+                     const int32_t* __restrict__ sel_idx, int64_t cap, SplitView sv, float scale_log2) {
+    __shared__ uint16_t kbuf[64 * D], vbuf[64 * D];
+    int idx;
+    if (!split_item_of(sv, idx)) return;   // beyond the plan's item count
+    const int4 it = sv.items[idx];
+    const int ntiles = static_cast<int>(N / 64);
+    const int h = it.x / ntiles;
+    const int64_t p0 = static_cast<int64_t>(it.x - h * ntiles) * 64;
+    DqState<D> st;
+    dq_pass<D>(q, k + h * hs, v + h * hs, dout, lse, Dq, N, ld, hs, h, p0, offs,
+               sel_idx + static_cast<int64_t>(h) * cap, it.y, it.z, kbuf, vbuf, scale_log2, st);
+    constexpr int DM = D / 32;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    float* __restrict__ P = sv.partials + static_cast<int64_t>(it.w) * fwd_partial_floats(D);
+    float4* po = reinterpret_cast<float4*>(P) + wave * DM * 4 * 64 + lane;
+#pragma unroll
+    for (int m = 0; m < DM; ++m)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+            po[(m * 4 + g) * 64] = float4{st.acc[m][4 * g], st.acc[m][4 * g + 1], st.acc[m][4 * g + 2],
+                                          st.acc[m][4 * g + 3]};
+    P[2 * DM * 16 * 64 + wave * 64 + lane] = st.dex;
+}
+
+// per split tile: the chunks' partials summed in chunk order, then written as
+// the tile kernel would
+template <int D>
+__global__ void __launch_bounds__(128)
+attn_dq_combine_kernel(uint16_t* __restrict__ dq, float* __restrict__ Dq, int64_t N, const int32_t* __restrict__ offs,
+                       int nb, SplitView sv, const RowMap om, float scale) {
+    const int ntiles = static_cast<int>(N / 64);
+    const int wg = blockIdx.x;
+    const int h = wg / ntiles;
+    const int64_t p0 = static_cast<int64_t>(wg - h * ntiles) * 64;
+    const int i = find_block(offs, nb, p0);
+    const int64_t ri = static_cast<int64_t>(h) * nb + i;
+    if (!sv.heavy[ri]) return;
+    const int nt = (offs[i + 1] - offs[i]) >> 6;
+    const int t = static_cast<int>((p0 - offs[i]) >> 6);
+    const int nch = sv.nchunk[ri];
+    const int64_t slot0 = split_part_base(sv, h) + sv.pbase[static_cast<int64_t>(h) * (nb + 1) + i] + t;
+    constexpr int DM = D / 32;
+    constexpr int PF = fwd_partial_floats(D);
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    DqState<D> st;
+#pragma unroll
+    for (int m = 0; m < DM; ++m)
+#pragma unroll
+        for (int x = 0; x < 16; ++x) st.acc[m][x] = 0.0f;
+    st.dex = 0.0f;
+    for (int c = 0; c < nch; ++c) {
+        const float* __restrict__ P = sv.partials + (slot0 + static_cast<int64_t>(c) * nt) * PF;
+        const float4* po = reinterpret_cast<const float4*>(P) + wave * DM * 4 * 64 + lane;
+#pragma unroll
+        for (int m = 0; m < DM; ++m)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const float4 x = po[(m * 4 + g) * 64];
+                st.acc[m][4 * g] += x.x;
+                st.acc[m][4 * g + 1] += x.y;
+                st.acc[m][4 * g + 2] += x.z;
+                st.acc[m][4 * g + 3] += x.w;
+            }
+        st.dex += P[2 * DM * 16 * 64 + wave * 64 + lane];
+    }
+    dq_store<D>(st, dq, Dq, om, N, h, p0, scale);
 }
 
 // dK/dV: 4 waves per 64-key tile, in two roles per 32-key half.  Role 0 holds
@@ -335,12 +433,59 @@ attn_dkdv_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
 
 // ---------------------------------------------------------------- launcher
 
-hipError_t launch_attn_bwd_mfma(const void* q, const void* k, const void* v, const void* dout, const float* lse,
-                                float* Dq, void* dq, void* dk, void* dv, int64_t N, int heads, int d, int64_t ld,
-                                int64_t hs, const int32_t* offs, int nb, const int32_t* so, const int32_t* si,
-                                const int32_t* to, const int32_t* ti, int64_t cap, const int32_t* qorder,
-                                const RouteGrad* rg, const RowMap& om, float scale, hipStream_t s) {
-    const uint8_t* skip = rg ? rg->skip_q : nullptr;
+hipError_t launch_attn_dq_mfma(const void* q, const void* k, const void* v, const void* dout, const float* lse,
+                              float* Dq, void* dq, int64_t N, int heads, int d, int64_t ld, int64_t hs,
+                              const int32_t* offs, int nb, const int32_t* so, const int32_t* si, int64_t cap,
+                              const int32_t* qorder, const uint8_t* skip, const RowMap& om, float scale,
+                              hipStream_t s) {
+    const dim3 grid(static_cast<unsigned>(N / 64 * heads));
+    const float sl2 = scale * kLog2e;
+    const uint16_t* Q = static_cast<const uint16_t*>(q);
+    const uint16_t* K = static_cast<const uint16_t*>(k);
+    const uint16_t* V = static_cast<const uint16_t*>(v);
+    const uint16_t* O = static_cast<const uint16_t*>(dout);
+    uint16_t* dQ = static_cast<uint16_t*>(dq);
+    if (d == 128)
+        hipLaunchKernelGGL(attn_dq_mfma_kernel<128>, grid, dim3(128), 0, s, Q, K, V, O, lse, Dq, dQ, N, ld, hs, offs,
+                           nb, so, si, cap, qorder, skip, om, sl2, scale);
+    else
+        hipLaunchKernelGGL(attn_dq_mfma_kernel<64>, grid, dim3(128), 0, s, Q, K, V, O, lse, Dq, dQ, N, ld, hs, offs,
+                           nb, so, si, cap, qorder, skip, om, sl2, scale);
+    return hipGetLastError();
+}
+
+hipError_t launch_attn_dq_split(const void* q, const void* k, const void* v, const void* dout, const float* lse,
+                                float* Dq, void* dq, int64_t N, int heads, int d, int64_t ld, int64_t hs,
+                                const int32_t* offs, int nb, const int32_t* si, int64_t cap, const SplitView& sv,
+                                const RowMap& om, float scale, hipStream_t s) {
+    const float sl2 = scale * kLog2e;
+    const uint16_t* Q = static_cast<const uint16_t*>(q);
+    const uint16_t* K = static_cast<const uint16_t*>(k);
+    const uint16_t* V = static_cast<const uint16_t*>(v);
+    const uint16_t* O = static_cast<const uint16_t*>(dout);
+    uint16_t* dQ = static_cast<uint16_t*>(dq);
+    const dim3 cgrid(static_cast<unsigned>(split_grid(sv)));
+    const dim3 tgrid(static_cast<unsigned>(N / 64 * heads));
+    if (d == 128) {
+        hipLaunchKernelGGL(attn_dq_chunk_kernel<128>, cgrid, dim3(128), 0, s, Q, K, V, O, lse, Dq, N, ld, hs, offs, si,
+                           cap, sv, sl2);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(attn_dq_combine_kernel<128>, tgrid, dim3(128), 0, s, dQ, Dq, N, offs, nb, sv, om, scale);
+    } else {
+        hipLaunchKernelGGL(attn_dq_chunk_kernel<64>, cgrid, dim3(128), 0, s, Q, K, V, O, lse, Dq, N, ld, hs, offs, si,
+                           cap, sv, sl2);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(attn_dq_combine_kernel<64>, tgrid, dim3(128), 0, s, dQ, Dq, N, offs, nb, sv, om, scale);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_attn_dkdv_mfma(const void* q, const void* k, const void* v, const void* dout, const float* lse,
+                                 const float* Dq, void* dk, void* dv, int64_t N, int heads, int d, int64_t ld,
+                                 int64_t hs, const int32_t* offs, int nb, const int32_t* to, const int32_t* ti,
+                                 int64_t cap, const RouteGrad* rg, const RowMap& om, float scale, hipStream_t s) {
     const float* dkb = rg ? rg->dkbar : nullptr;
     const float* dvb = rg ? rg->dvbar : nullptr;
     const dim3 grid(static_cast<unsigned>(N / 64 * heads));
@@ -349,24 +494,14 @@ hipError_t launch_attn_bwd_mfma(const void* q, const void* k, const void* v, con
     const uint16_t* K = static_cast<const uint16_t*>(k);
     const uint16_t* V = static_cast<const uint16_t*>(v);
     const uint16_t* O = static_cast<const uint16_t*>(dout);
-    uint16_t* dQ = static_cast<uint16_t*>(dq);
     uint16_t* dK = static_cast<uint16_t*>(dk);
     uint16_t* dV = static_cast<uint16_t*>(dv);
-    if (d == 128) {
-        hipLaunchKernelGGL(attn_dq_mfma_kernel<128>, grid, dim3(128), 0, s, Q, K, V, O, lse, Dq, dQ, N, ld, hs, offs,
-                           nb, so, si, cap, qorder, skip, om, sl2, scale);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
+    if (d == 128)
         hipLaunchKernelGGL(attn_dkdv_mfma_kernel<128>, grid, dim3(256), 0, s, Q, K, V, O, lse, Dq, dK, dV, N, ld, hs,
                            offs, nb, to, ti, cap, dkb, dvb, om, sl2, scale);
-    } else {
-        hipLaunchKernelGGL(attn_dq_mfma_kernel<64>, grid, dim3(128), 0, s, Q, K, V, O, lse, Dq, dQ, N, ld, hs, offs,
-                           nb, so, si, cap, qorder, skip, om, sl2, scale);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
+    else
         hipLaunchKernelGGL(attn_dkdv_mfma_kernel<64>, grid, dim3(256), 0, s, Q, K, V, O, lse, Dq, dK, dV, N, ld, hs,
                            offs, nb, to, ti, cap, dkb, dvb, om, sl2, scale);
-    }
     return hipGetLastError();
 }
 

@@ -69,6 +69,12 @@ __device__ __forceinline__ u32x2_t residual4(const float (&r)[4], const u32x2_t&
                    pack2(r[2] - __uint_as_float(hi.y << 16), r[3] - __uint_as_float(hi.y & 0xffff0000u))};
 }
 
+// acc + lo + hi of a packed bf16 pair, one v_dot2 against (1, 1)
+__device__ __forceinline__ float sum_bf16_pair(uint32_t w, float acc) {
+    const bf16x2_t one = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w), one, acc, false);
+}
+
 // 2^x on the transcendental unit; results below the normal range flush to 0,
 // which is what the softmax wants for scores far below the row maximum
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -95,6 +101,43 @@ __device__ __forceinline__ void sched_reads_ahead() {
 }
 
 // ---------------------------------------------------------------- swizzled LDS tiles
+
+template <int D>
+__device__ __forceinline__ u32x4_t sw_read16(const uint16_t* tile, int r, int c);
+
+// c0, c1 += A B over the D channels, where the A operands are the 16-byte rows
+// (col and 32 + col) of a swizzled 64 x D tile and B the k-steps held in b:
+// the two 32-row halves of the product of the tile with a 32-column operand.
+// The tile fragments are read two k-steps ahead of the MFMAs that use them
+// (left to itself the compiler reads each one just before its MFMA and waits
+// the whole LDS latency every step); a schedule barrier keeps each step's
+// reads and MFMAs in that order.
+template <int D>
+__device__ __forceinline__ void rows_x_ksteps(const uint16_t* tile, int col, int hl, const u32x4_t (&b)[D / 16],
+                                              f32x16_t& c0, f32x16_t& c1) {
+    constexpr int KS = D / 16;
+    u32x4_t a[2][2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+        a[s][0] = sw_read16<D>(tile, col, 16 * s + 8 * hl);
+        a[s][1] = sw_read16<D>(tile, 32 + col, 16 * s + 8 * hl);
+    }
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+        u32x4_t n0, n1;
+        if (s + 2 < KS) {
+            n0 = sw_read16<D>(tile, col, 16 * (s + 2) + 8 * hl);
+            n1 = sw_read16<D>(tile, 32 + col, 16 * (s + 2) + 8 * hl);
+        }
+        c0 = mfma32(a[s & 1][0], b[s], c0);
+        c1 = mfma32(a[s & 1][1], b[s], c1);
+        if (s + 2 < KS) {
+            a[s & 1][0] = n0;
+            a[s & 1][1] = n1;
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
 
 template <int D>
 __device__ __forceinline__ int swz(int r) {

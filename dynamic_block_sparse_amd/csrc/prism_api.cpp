@@ -16,6 +16,7 @@
 #include <utility>
 #include <vector>
 
+#include "attn_split.hpp"
 #include "prism.h"
 #include "prism_device.hpp"
 #include "prism_internal.hpp"
@@ -103,17 +104,18 @@ struct BwdWs {
     int32_t* ostart;   // bucket starts of the tile order
     int32_t* qorder;   // dQ tile order
 };
-BwdWs carve_bwd(Carver& c, int64_t N, int64_t heads, int64_t nb, int64_t cap) {
+// `hg` heads share the per-group buffers (the dQ tile order), all heads the rest
+BwdWs carve_bwd(Carver& c, int64_t N, int64_t heads, int64_t hg, int64_t nb, int64_t cap) {
     BwdWs w;
     w.Dq = c.take<float>(heads * N);
     w.tcount = c.take<int32_t>(heads * nb);
     w.tr_offsets = c.take<int32_t>(heads * (nb + 1));
     w.tr_idx = c.take<int32_t>(heads * cap);
     w.scratch = c.take<int32_t>(heads * cap);
-    const int64_t units = prism::tile_order_units(static_cast<int>(heads));
+    const int64_t units = prism::tile_order_units(static_cast<int>(hg));
     w.obucket = c.take<int32_t>(units * nb);
     w.ostart = c.take<int32_t>(units * (nb + 1));
-    w.qorder = c.take<int32_t>(2 * heads * (N / 64));
+    w.qorder = c.take<int32_t>(2 * hg * (N / 64));
     return w;
 }
 
@@ -129,6 +131,51 @@ OrderWs carve_order(Carver& c, int64_t N, int64_t heads, int64_t nb) {
     w.bucket = c.take<int32_t>(units * nb);
     w.start = c.take<int32_t>(units * (nb + 1));
     w.order = c.take<int32_t>(2 * heads * (N / 64));
+    return w;
+}
+
+// The forward and dQ process heads in groups of at most `group` heads, each
+// group with the same per-group buffers (tile order, split plan, partials).
+// Rows with more than T0 key tiles (or the lowest multiple 2^k T0 whose items
+// fit the slot capacity, `slots` per query tile of the group) are split into
+// key ranges of W blocks.  The environment may override the four for
+// experiments (PRISM_SPLIT_W, PRISM_SPLIT_T: 0 turns the split off,
+// PRISM_SPLIT_GROUP, PRISM_SPLIT_SLOTS); the workspace size and the calls read
+// the same values.
+struct SplitParams {
+    int W, T0, group, slots;   // slots: partial slots per query tile of a group
+};
+int env_int(const char* name, int dflt, int lo, int hi) {
+    const char* e = std::getenv(name);
+    if (!e || !*e) return dflt;
+    const long v = std::strtol(e, nullptr, 10);
+    return v < lo ? lo : (v > hi ? hi : static_cast<int>(v));
+}
+SplitParams split_params() {
+    return SplitParams{env_int("PRISM_SPLIT_W", 128, 1, 1 << 15), env_int("PRISM_SPLIT_T", 256, 0, 1 << 20),
+                       env_int("PRISM_SPLIT_GROUP", 64, 1, 1 << 10), env_int("PRISM_SPLIT_SLOTS", 2, 1, 1 << 10)};
+}
+int64_t group_heads(int64_t heads, const SplitParams& sp) { return std::min<int64_t>(heads, sp.group); }
+// partial-slot capacity of one group, a multiple of 8
+int64_t split_slots(int64_t N, int64_t hg, const SplitParams& sp) { return (sp.slots * (N / 64) * hg + 7) / 8 * 8; }
+
+prism::SplitWs carve_split(Carver& c, int64_t N, int64_t hg, int64_t nb, int64_t d, const SplitParams& sp) {
+    prism::SplitWs w;
+    const int64_t nR = (nb + sp.W - 1) / sp.W;
+    w.cap_slots = split_slots(N, hg, sp);
+    w.cost = c.take<int32_t>(hg * nb);
+    w.nch = c.take<int32_t>(hg * nb);
+    w.heavy = c.take<uint8_t>(hg * nb);
+    w.pcount = c.take<int32_t>(hg * nb);
+    w.pbase = c.take<int32_t>(hg * (nb + 1));
+    w.ptot = c.take<int64_t>(hg);
+    w.bucket = c.take<int32_t>(hg * nR);
+    w.bstart = c.take<int32_t>(hg * (nR + 1));
+    w.btot = c.take<int64_t>(hg);
+    w.demand = c.take<unsigned long long>(8);
+    w.tsel = c.take<int32_t>(1);
+    w.items = c.take<int4>(w.cap_slots);
+    w.partials = c.take<float>(w.cap_slots * prism::fwd_partial_floats(static_cast<int>(d)));
     return w;
 }
 
@@ -334,20 +381,25 @@ size_t prism_workspace_size(int32_t op, int64_t N, int32_t heads, int32_t d, int
             return c.off;
         }
         case PRISM_OP_ATTN_FWD: {
+            const SplitParams sp = split_params();
+            const int64_t hg = group_heads(heads, sp);
             Carver c(nullptr);
-            carve_order(c, N, heads, nb);
+            carve_order(c, N, hg, nb);
+            carve_split(c, N, hg, nb, d, sp);
             return c.off;
         }
         case PRISM_OP_ROUTED_FWD: {
+            const int64_t hg = group_heads(heads, split_params());
             Carver c(nullptr);
-            carve_order(c, N, heads, nb);
+            carve_order(c, N, hg, nb);
             c.take<float>(static_cast<size_t>(heads) * nb * d);
             c.take<float>(static_cast<size_t>(heads) * nb * d);
             return c.off;
         }
         case PRISM_OP_ROUTED_BWD: {
+            const int64_t hg = group_heads(heads, split_params());
             Carver c(nullptr);
-            carve_bwd(c, N, heads, nb, cap);
+            carve_bwd(c, N, heads, hg, nb, cap);
             carve_routed_bwd(c, heads, d, nb, cap);
             return c.off;
         }
@@ -355,8 +407,11 @@ size_t prism_workspace_size(int32_t op, int64_t N, int32_t heads, int32_t d, int
             return align_up(static_cast<size_t>(N) * sizeof(double)) +
                    align_up(static_cast<size_t>(prism::kNormMapMaxBlocks) * sizeof(double));
         case PRISM_OP_ATTN_BWD: {
+            const SplitParams sp = split_params();
+            const int64_t hg = group_heads(heads, sp);
             Carver c(nullptr);
-            carve_bwd(c, N, heads, nb, cap);
+            carve_bwd(c, N, heads, hg, nb, cap);
+            carve_split(c, N, hg, nb, d, sp);
             return c.off;
         }
     }
@@ -629,24 +684,68 @@ prism_status check_fwd(const void* q, const void* k, const void* v, const void* 
     return PRISM_OK;
 }
 
+// Element offset of head g0 in a bf16 token tensor, as a pointer.
+const void* at_head_c(const void* p, int64_t g0, int64_t hs) {
+    return p ? static_cast<const void*>(static_cast<const uint16_t*>(p) + g0 * hs) : nullptr;
+}
+void* at_head(void* p, int64_t g0, int64_t hs) {
+    return p ? static_cast<void*>(static_cast<uint16_t*>(p) + g0 * hs) : nullptr;
+}
+
 // Exact forward over the tiles whose block is not marked in `skip` (NULL: all).
+// The MFMA path takes the heads in groups (split_params); within a group the
+// rows with long selected lists are split into key-range chunks (not on the
+// routed path, which passes `skip`), the other tiles run in the visiting order
+// of launch_tile_order, and a combine merges the chunks.
 prism_status exact_fwd(const void* q, const void* k, const void* v, void* o, float* lse, void* o_res, prism_dtype dt,
                        int64_t N, int32_t heads, int32_t d, int64_t ld, int64_t hs, const int32_t* block_offsets,
                        int32_t nb, const int32_t* sel_offsets, const int32_t* sel_idx, int64_t cap,
                        const uint8_t* skip, const prism::RowMap& om, float scale, Carver& c, hipStream_t stream) {
-    OrderWs w = carve_order(c, N, heads, nb);
     if (use_simt_attention(dt))
         return hip_status(prism::launch_attn_fwd_simt(q, k, v, o, lse, dt == PRISM_BF16, N, heads, d, ld, hs,
                                                       block_offsets, nb, sel_offsets, sel_idx, cap, skip, om,
                                                       scale, o_res, stream),
                           "attention forward launch");
-    prism_status st = hip_status(prism::launch_tile_order(sel_offsets, sel_idx, cap, block_offsets, nb, heads, N / 64,
-                                                          w.bucket, w.start, w.order, stream),
-                                 "tile order launch");
-    if (st != PRISM_OK) return st;
-    return hip_status(prism::launch_attn_fwd_mfma(q, k, v, o, lse, N, heads, d, ld, hs, block_offsets, nb, sel_offsets,
-                                                  sel_idx, cap, w.order, skip, om, scale, o_res, stream),
-                      "attention forward launch");
+    const SplitParams sp = split_params();
+    const int64_t hg = group_heads(heads, sp);
+    OrderWs w = carve_order(c, N, hg, nb);
+    const bool split = !skip && sp.T0 > 0;
+    prism::SplitWs sw{};
+    if (!skip) sw = carve_split(c, N, hg, nb, d, sp);
+    for (int64_t g0 = 0; g0 < heads; g0 += hg) {
+        const int n = static_cast<int>(std::min<int64_t>(hg, heads - g0));
+        const int32_t* so = sel_offsets + g0 * (nb + 1);
+        const int32_t* si = sel_idx + g0 * cap;
+        const void* qg = at_head_c(q, g0, hs);
+        const void* kg = at_head_c(k, g0, hs);
+        const void* vg = at_head_c(v, g0, hs);
+        void* og = at_head(o, g0, om.hs);
+        void* rg = at_head(o_res, g0, om.hs);
+        float* lg = lse + g0 * N;
+        const uint8_t* sk = skip ? skip + g0 * nb : nullptr;
+        prism_status st;
+        if (split) {
+            st = hip_status(prism::launch_split_plan(so, si, cap, block_offsets, nb, n, N / 64, sp.W, sp.T0, sw, stream),
+                            "split plan launch");
+            if (st != PRISM_OK) return st;
+            sk = sw.heavy;
+        }
+        st = hip_status(prism::launch_tile_order(so, si, cap, block_offsets, nb, n, N / 64, w.bucket, w.start, w.order,
+                                                 stream),
+                        "tile order launch");
+        if (st != PRISM_OK) return st;
+        st = hip_status(prism::launch_attn_fwd_mfma(qg, kg, vg, og, lg, N, n, d, ld, hs, block_offsets, nb, so, si, cap,
+                                                    w.order, sk, om, scale, rg, stream),
+                        "attention forward launch");
+        if (st != PRISM_OK) return st;
+        if (split) {
+            st = hip_status(prism::launch_attn_fwd_split(qg, kg, vg, og, lg, N, n, d, ld, hs, block_offsets, nb, si, cap,
+                                                         prism::split_view(sw, n), om, scale, rg, stream),
+                            "split forward launch");
+            if (st != PRISM_OK) return st;
+        }
+    }
+    return PRISM_OK;
 }
 
 }  // namespace
@@ -737,25 +836,63 @@ prism_status check_bwd(const void* q, const void* k, const void* v, const void* 
 }
 
 // dQ and dK/dV on the exact path, from a transposed CSR already built in w;
-// rg (NULL for the plain backward) carries the routed extras.
+// rg (NULL for the plain backward) carries the routed extras.  dQ takes the
+// heads in groups like the forward, with the same key-range split of long rows
+// (not on the routed path); dK/dV then runs once over all heads.  `c` follows
+// carve_bwd in the workspace.
 prism_status exact_bwd(const void* q, const void* k, const void* v, const void* dout, const float* lse, void* dq,
                        void* dk, void* dv, prism_dtype dt, int64_t N, int32_t heads, int32_t d, int64_t ld, int64_t hs,
                        const int32_t* block_offsets, int32_t nb, const int32_t* sel_offsets, const int32_t* sel_idx,
                        int64_t cap, float scale, const BwdWs& w, const prism::RouteGrad* rg, const prism::RowMap& om,
-                       hipStream_t stream) {
+                       Carver& c, hipStream_t stream) {
     if (use_simt_attention(dt))
         return hip_status(prism::launch_attn_bwd_simt(q, k, v, dout, lse, w.Dq, dq, dk, dv, dt == PRISM_BF16, N, heads,
                                                       d, ld, hs, block_offsets, nb, sel_offsets, sel_idx, w.tr_offsets,
                                                       w.tr_idx, cap, rg, om, scale, stream),
                           "attention backward launch");
-    prism_status st = hip_status(prism::launch_tile_order(sel_offsets, sel_idx, cap, block_offsets, nb, heads, N / 64,
-                                                          w.obucket, w.ostart, w.qorder, stream),
-                                 "tile order launch");
-    if (st != PRISM_OK) return st;
-    return hip_status(prism::launch_attn_bwd_mfma(q, k, v, dout, lse, w.Dq, dq, dk, dv, N, heads, d, ld, hs,
-                                                  block_offsets, nb, sel_offsets, sel_idx, w.tr_offsets, w.tr_idx, cap,
-                                                  w.qorder, rg, om, scale, stream),
-                      "attention backward launch");
+    const SplitParams sp = split_params();
+    const int64_t hg = group_heads(heads, sp);
+    const bool split = !rg && sp.T0 > 0;
+    prism::SplitWs sw{};
+    if (!rg) sw = carve_split(c, N, hg, nb, d, sp);
+    for (int64_t g0 = 0; g0 < heads; g0 += hg) {
+        const int n = static_cast<int>(std::min<int64_t>(hg, heads - g0));
+        const int32_t* so = sel_offsets + g0 * (nb + 1);
+        const int32_t* si = sel_idx + g0 * cap;
+        const void* qg = at_head_c(q, g0, hs);
+        const void* kg = at_head_c(k, g0, hs);
+        const void* vg = at_head_c(v, g0, hs);
+        const void* dog = at_head_c(dout, g0, hs);
+        void* dqg = at_head(dq, g0, om.hs);
+        const float* lg = lse + g0 * N;
+        float* Dg = w.Dq + g0 * N;
+        const uint8_t* sk = rg && rg->skip_q ? rg->skip_q + g0 * nb : nullptr;
+        prism_status st;
+        if (split) {
+            st = hip_status(prism::launch_split_plan(so, si, cap, block_offsets, nb, n, N / 64, sp.W, sp.T0, sw, stream),
+                            "split plan launch");
+            if (st != PRISM_OK) return st;
+            sk = sw.heavy;
+        }
+        st = hip_status(prism::launch_tile_order(so, si, cap, block_offsets, nb, n, N / 64, w.obucket, w.ostart,
+                                                 w.qorder, stream),
+                        "tile order launch");
+        if (st != PRISM_OK) return st;
+        st = hip_status(prism::launch_attn_dq_mfma(qg, kg, vg, dog, lg, Dg, dqg, N, n, d, ld, hs, block_offsets, nb, so,
+                                                   si, cap, w.qorder, sk, om, scale, stream),
+                        "dQ launch");
+        if (st != PRISM_OK) return st;
+        if (split) {
+            st = hip_status(prism::launch_attn_dq_split(qg, kg, vg, dog, lg, Dg, dqg, N, n, d, ld, hs, block_offsets, nb,
+                                                        si, cap, prism::split_view(sw, n), om, scale, stream),
+                            "split dQ launch");
+            if (st != PRISM_OK) return st;
+        }
+    }
+    return hip_status(prism::launch_attn_dkdv_mfma(q, k, v, dout, lse, w.Dq, dk, dv, N, heads, d, ld, hs,
+                                                   block_offsets, nb, w.tr_offsets, w.tr_idx, cap, rg, om, scale,
+                                                   stream),
+                      "dK/dV launch");
 }
 
 }  // namespace
@@ -776,7 +913,7 @@ prism_status prism_sparse_attn_bwd(const void* q, const void* k, const void* v, 
     if (!ws || ws_bytes < need)
         return fail(PRISM_E_WORKSPACE, "backward needs %zu workspace bytes, got %zu", need, ws ? ws_bytes : 0);
     Carver c(ws);
-    BwdWs w = carve_bwd(c, N, heads, nb, cap);
+    BwdWs w = carve_bwd(c, N, heads, group_heads(heads, split_params()), nb, cap);
     st = hip_status(prism::launch_bwd_dot(o, dout, dt == PRISM_BF16, N, heads, d, ld, hs, om, w.Dq, o_res, stream),
                     "backward dot launch");
     if (st != PRISM_OK) return st;
@@ -785,7 +922,7 @@ prism_status prism_sparse_attn_bwd(const void* q, const void* k, const void* v, 
                     "transposed selection launch");
     if (st != PRISM_OK) return st;
     return exact_bwd(q, k, v, dout, lse, dq, dk, dv, dt, N, heads, d, ld, hs, block_offsets, nb, sel_offsets, sel_idx,
-                     cap, scale, w, nullptr, om, stream);
+                     cap, scale, w, nullptr, om, c, stream);
 }
 
 prism_status prism_routed_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* o_res,
@@ -803,7 +940,7 @@ prism_status prism_routed_attn_bwd(const void* q, const void* k, const void* v, 
     if (!ws || ws_bytes < need)
         return fail(PRISM_E_WORKSPACE, "routed backward needs %zu workspace bytes, got %zu", need, ws ? ws_bytes : 0);
     Carver c(ws);
-    BwdWs w = carve_bwd(c, N, heads, nb, cap);
+    BwdWs w = carve_bwd(c, N, heads, group_heads(heads, split_params()), nb, cap);
     RoutedBwdWs r = carve_routed_bwd(c, heads, d, nb, cap);
     const bool bf16 = dt == PRISM_BF16;
     prism::RowMap om;
@@ -833,7 +970,7 @@ prism_status prism_routed_attn_bwd(const void* q, const void* k, const void* v, 
     if (st != PRISM_OK) return st;
     const prism::RouteGrad rg{flat, r.dkbar, r.dvbar};
     return exact_bwd(q, k, v, dout, lse, dq, dk, dv, dt, N, heads, d, ld, hs, block_offsets, nb, sel_offsets, sel_idx,
-                     cap, scale, w, &rg, om, stream);
+                     cap, scale, w, &rg, om, c, stream);
 }
 
 }  // extern "C"

@@ -8,6 +8,8 @@
 
 namespace prism {
 
+struct SplitView;   // attn_split.hpp
+
 struct ZoneGrid;
 
 hipError_t launch_zone_shapes(const void* v, bool bf16, int64_t C, int64_t ld, const float* a, ZoneGrid g, int nZ,
@@ -67,11 +69,23 @@ hipError_t launch_attn_fwd_mfma(const void* q, const void* k, const void* v, voi
 hipError_t launch_bwd_dot(const void* o, const void* dout, bool bf16, int64_t N, int heads, int d, int64_t ld,
                           int64_t hs, const RowMap& om, float* Dq, const void* ores, hipStream_t s);
 
-hipError_t launch_attn_bwd_mfma(const void* q, const void* k, const void* v, const void* dout, const float* lse,
-                                float* Dq, void* dq, void* dk, void* dv, int64_t N, int heads, int d, int64_t ld,
-                                int64_t hs, const int32_t* offs, int nb, const int32_t* so, const int32_t* si,
-                                const int32_t* to, const int32_t* ti, int64_t cap, const int32_t* qorder,
-                                const RouteGrad* rg, const RowMap& om, float scale, hipStream_t s);
+// dQ of one group of heads (pointers at the group's first head): the tile
+// kernel over the tiles not marked in `skip`, then, for a split plan, its
+// chunks and combine; dK/dV of all heads after every group's dQ (it reads the
+// exact row dots that the dQ kernels leave in Dq)
+hipError_t launch_attn_dq_mfma(const void* q, const void* k, const void* v, const void* dout, const float* lse,
+                              float* Dq, void* dq, int64_t N, int heads, int d, int64_t ld, int64_t hs,
+                              const int32_t* offs, int nb, const int32_t* so, const int32_t* si, int64_t cap,
+                              const int32_t* qorder, const uint8_t* skip, const RowMap& om, float scale,
+                              hipStream_t s);
+hipError_t launch_attn_dq_split(const void* q, const void* k, const void* v, const void* dout, const float* lse,
+                                float* Dq, void* dq, int64_t N, int heads, int d, int64_t ld, int64_t hs,
+                                const int32_t* offs, int nb, const int32_t* si, int64_t cap, const SplitView& sv,
+                                const RowMap& om, float scale, hipStream_t s);
+hipError_t launch_attn_dkdv_mfma(const void* q, const void* k, const void* v, const void* dout, const float* lse,
+                                 const float* Dq, void* dk, void* dv, int64_t N, int heads, int d, int64_t ld,
+                                 int64_t hs, const int32_t* offs, int nb, const int32_t* to, const int32_t* ti,
+                                 int64_t cap, const RouteGrad* rg, const RowMap& om, float scale, hipStream_t s);
 
 hipError_t launch_attn_bwd_simt(const void* q, const void* k, const void* v, const void* dout, const float* lse,
                                 const float* Dq, void* dq, void* dk, void* dv, bool bf16, int64_t N, int heads, int d,
@@ -88,6 +102,47 @@ inline int tile_order_units(int heads) { return heads + 8; }
 hipError_t launch_tile_order(const int32_t* sel_offsets, const int32_t* sel_idx, int64_t cap, const int32_t* offs,
                              int nb, int heads, int64_t ntiles, int32_t* bucket, int32_t* start, int32_t* order,
                              hipStream_t s);
+// counters cleared by a kernel (not a memset node, so that a captured graph
+// replays it like the other launches)
+hipError_t fill_zero(int32_t* p, int64_t n, hipStream_t s);
+// per-head exclusive scan: offsets[h][0..n] of counts[h][0..n), totals[h] = sum (totals may be NULL)
+hipError_t launch_csr_scan(const int32_t* counts, int n, int32_t* offsets, int64_t* totals, int heads, hipStream_t s);
+
+// Key-range split of long selected lists for one launch (a group of heads;
+// attn_split.hpp).  Buffers from the call's workspace: cost, nch, heavy,
+// pcount [heads][nb]; pbase [heads][nb + 1]; ptot, btot [heads]; bucket
+// [heads][nR] (also the fill cursors); bstart [heads][nR + 1]; demand [8];
+// tsel [1]; items [cap_slots]; partials [cap_slots][fwd_partial_floats(d)];
+// nR = ceil(nb / W).  Rows with more than the chosen threshold of key tiles
+// are split into W-block key ranges; the threshold is the lowest of T0,
+// 2 T0, ..., 128 T0 whose items fit cap_slots (none: nothing is split; T0 = 0
+// disables the split).
+struct SplitWs {
+    int32_t* cost;
+    int32_t* nch;
+    uint8_t* heavy;
+    int32_t* pcount;
+    int32_t* pbase;
+    int64_t* ptot;
+    int32_t* bucket;
+    int32_t* bstart;
+    int64_t* btot;
+    unsigned long long* demand;
+    int32_t* tsel;
+    int4* items;
+    float* partials;
+    int64_t cap_slots;
+};
+hipError_t launch_split_plan(const int32_t* sel_off, const int32_t* sel_idx, int64_t cap, const int32_t* offs, int nb,
+                             int heads, int64_t ntiles, int W, int T0, const SplitWs& w, hipStream_t s);
+SplitView split_view(const SplitWs& w, int heads);
+// chunk items of a plan (fp32 partials), then the combine that writes O, its
+// residual and lse of the split rows
+hipError_t launch_attn_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse, int64_t N,
+                                 int heads, int d, int64_t ld, int64_t hs, const int32_t* offs, int nb,
+                                 const int32_t* si, int64_t cap, const SplitView& sv, const RowMap& om, float scale,
+                                 void* ores, hipStream_t s);
+
 // audio-to-video norm map: per-token 2-norms (float64) and their clip-wide
 // normalisation; block_max holds norm_map_blocks(N) <= kNormMapMaxBlocks doubles
 constexpr int kNormMapMaxBlocks = 4096;

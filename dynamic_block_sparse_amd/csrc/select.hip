@@ -1149,6 +1149,11 @@ hipError_t fill_zero(int32_t* p, int64_t n, hipStream_t s) {
     return hipGetLastError();
 }
 
+hipError_t launch_csr_scan(const int32_t* counts, int n, int32_t* offsets, int64_t* totals, int heads, hipStream_t s) {
+    hipLaunchKernelGGL(csr_scan_kernel, dim3(heads), dim3(1024), 0, s, counts, n, offsets, totals);
+    return hipGetLastError();
+}
+
 hipError_t launch_transpose_csr(const int32_t* sel_offsets, const int32_t* sel_idx, int nb, int heads, int64_t cap,
                                 int32_t* tcount, int32_t* tr_offsets, int32_t* tr_idx, int32_t* scratch,
                                 const uint8_t* rowmask, int want, hipStream_t s) {

@@ -273,7 +273,7 @@ def test_flat_route_and_routed_forward_reject():
     N, d = 2048, 128
     cap = nb * nb
     fneed = P.prism_workspace_size(P.OP_ROUTED_FWD, N, heads, d, nb, cap)
-    assert fneed > P.prism_workspace_size(P.OP_ATTN_FWD, N, heads, d, nb, cap) + 2 * 4 * heads * nb * d - 1
+    assert fneed >= 2 * 4 * heads * nb * d + 4 * heads * (N // 64)   # block means and the tile order
     f = lambda fl=B, ws=Cc, wsb=fneed, dt=1: lib.prism_routed_attn_fwd(A, B, Cc, Cc, A, None, dt, N, heads, d, 256, 128,
                                                                        B, nb, Cc, A, cap, fl, 0.088, ws, wsb, None)
     assert f(dt=2) == 3
@@ -287,7 +287,7 @@ def test_routed_backward_rejects():
     N, heads, d, nb = 2048, 2, 128, 24
     cap = nb * nb
     need = P.prism_workspace_size(P.OP_ROUTED_BWD, N, heads, d, nb, cap)
-    assert need > P.prism_workspace_size(P.OP_ATTN_BWD, N, heads, d, nb, cap) + 4 * 4 * heads * nb * d - 1
+    assert need >= 4 * 4 * heads * nb * d + 4 * heads * N     # block-mean gradients and the row dots
     f = lambda fl=B, ws=A, wsb=need, dq=A: lib.prism_routed_attn_bwd(A, B, Cc, A, None, B, Cc, dq, B, Cc, 1, N, heads, d,
                                                                      256, 128, A, nb, B, Cc, cap, fl, 0.088, ws, wsb,
                                                                      None)

@@ -699,3 +699,39 @@ def test_truncated_selection_attends_over_the_stored_entries():
         for g, want, t, name in zip(grads, (dQ, dK, dV), (tQ, tK, tV), ("dQ", "dK", "dV")):
             assert_close(_np(g[:, h, :]), want, cfg.dtype, f"truncated {name} h{h}", grad=True, terms=t)
     assert empty_rows > 0
+
+
+@pytest.mark.parametrize("w,group", [(3, 8), (1, 1), (5, 2)], ids=["w3", "w1_group1", "w5_group2"])
+def test_split_rows_match_the_oracle(w, group, monkeypatch):
+    """The forward and dQ split rows with long selected lists into key-range
+    chunks and merge the chunks' partials.  Forced on every row of a small
+    diffuse grid (a threshold of one key tile, ranges of w blocks, heads in
+    groups of `group`): O, lse and the gradients against the oracle in full,
+    and run to run bitwise."""
+    cfg = SMALL[7]     # s_diffuse: Top-p keeps most blocks
+    print(f"case {cfg.name} W={w} group={group}", flush=True)
+    monkeypatch.setenv("PRISM_SPLIT_T", "1")
+    monkeypatch.setenv("PRISM_SPLIT_W", str(w))
+    monkeypatch.setenv("PRISM_SPLIT_GROUP", str(group))
+    monkeypatch.setenv("PRISM_SPLIT_SLOTS", "256")    # room for every row's chunks
+    x = make_inputs(cfg, device="cuda")
+    outs = []
+    for _ in range(2):
+        path = _path(cfg)
+        outs.append(path.step(x["q"], x["k"], x["v"], x["a"], x["do"]))
+    monkeypatch.setenv("PRISM_SPLIT_T", "0")
+    whole = _path(cfg).step(x["q"], x["k"], x["v"], x["a"], x["do"])
+    torch.cuda.synchronize()
+    for n in ("o", "dq", "dk", "dv"):
+        assert torch.equal(outs[0][n], outs[1][n]), n
+    # merged chunks sum in another order than one pass over the whole list
+    assert not torch.equal(outs[0]["o"], whole["o"]) and not torch.equal(outs[0]["dq"], whole["dq"])
+    out = outs[0]
+    ref = _oracle_full(cfg, x)
+    for h, hr in enumerate(ref["heads"]):
+        att = hr["att"]
+        assert_close(_np(out["o"][:, h, :]), orc.to_raster(att["O"], ref["pi"]), cfg.dtype, f"split O h{h}")
+        np.testing.assert_allclose(out["lse_block_major"][h].cpu().numpy(), att["lse"], atol=2e-3)
+        for g, name in (("dq", "dQ"), ("dk", "dK"), ("dv", "dV")):
+            assert_close(_np(out[g][:, h, :]), orc.to_raster(att[name], ref["pi"]), cfg.dtype, f"split {name} h{h}",
+                         grad=True, terms=orc.to_raster(att["t" + name[1]], ref["pi"]))
