@@ -268,9 +268,9 @@ attn_dq_combine_kernel(uint16_t* __restrict__ dq, float* __restrict__ Dq, int64_
 // and the MFMA work is the same 16 d-step products per row half as with one
 // wave doing both.  The query tile is processed in two 32-row halves so that
 // the P exchange needs 4 KB per key half:
-//   A  role 0: S(0), P(0), P(0) -> LDS         role 1: dP(0)
+//   A  role 0: S, P(0) -> LDS, P(1)            role 1: dP
 //   -- barrier
-//   B  role 0: S(1), P(1), dV += P(0)          role 1: dP(1), dS(0), dK += dS(0)
+//   B  role 0: dV += P(0)                      role 1: dS(0), dK += dS(0)
 //   -- barrier (role 1 has read P(0))
 //      role 0: P(1) -> LDS
 //   -- barrier
@@ -295,6 +295,8 @@ attn_dkdv_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
     __shared__ float lbuf[2][64], dbuf[2][64];
     // P of one 32-row half per key half: [key half][register group][lane][4]
     __shared__ float pbuf[2][4][64][4];
+    // each role-0 wave's copy of the tile's lse, times log2(e)
+    __shared__ float l2buf[2][64];
     const int ntiles = static_cast<int>(N / 64);
     const int wg = xcd_remap(blockIdx.x);
     const int h = wg / ntiles;
@@ -318,6 +320,11 @@ attn_dkdv_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
         for (int s = 0; s < KS; ++s) kv[s] = *reinterpret_cast<const u32x4_t*>(src + 16 * s + 8 * hl);
 #pragma unroll
         for (int s = 0; s < KS; ++s) settle(kv[s]);
+        // role 1 holds -V (a sign flip, exact in bf16): its products then
+        // start from D and give D - dP with no separate subtraction
+        const uint32_t flip = role ? 0x80008000u : 0u;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) kv[s] ^= flip;
     }
     f32x16_t acc[DM];   // dV^T (role 0) or dK^T (role 1)
 #pragma unroll
@@ -339,41 +346,51 @@ attn_dkdv_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
         if (wave == 0) dma4(lh + t, loff, lds_addr(lbuf[b]));
         else if (wave == 1) dma4(dh + t, loff, lds_addr(dbuf[b]));
     };
+    // The buffer index is a template constant, so LDS addresses are
+    // loop-invariant lane offsets plus immediates.
     auto compute = [&](int b) {
         const uint16_t* rb = role ? obuf[b] : qbuf[b];   // row operand: Q for S, dO for dP
         const uint16_t* tb = role ? qbuf[b] : obuf[b];   // transposed operand: dO^T for dV, Q^T for dK
-        const float* lt = lbuf[b];
         const float* dt = dbuf[b];
-        // S (role 0) or dP (role 1) of row half mr: register x holds query row
-        // 32*mr + 8*(x/4) + 4*hl + x%4 against key col of the wave's half
-        auto rows = [&](int mr) {
-            __builtin_amdgcn_s_setprio(1);
-            f32x16_t x;
+        const float* l2 = l2buf[kh];
+        if (role == 0) l2buf[kh][lane] = lbuf[b][lane] * kLog2e;   // read back by this wave only
+        // S (role 0) or D - dP (role 1) of both row halves: register x of half
+        // mr holds query row 32*mr + 8*(x/4) + 4*hl + x%4 against key col of
+        // the wave's half (two independent MFMA chains, LDS reads two steps
+        // ahead)
+        f32x16_t x0, x1;
+        if (role == 0) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) x[i] = 0.0f;
+            for (int i = 0; i < 16; ++i) x0[i] = x1[i] = 0.0f;
+        } else {
 #pragma unroll
-            for (int s = 0; s < KS; ++s) x = mfma32(sw_read16<D>(rb, 32 * mr + col, 16 * s + 8 * hl), kv[s], x);
-            __builtin_amdgcn_s_setprio(0);
-            return x;
-        };
+            for (int g = 0; g < 4; ++g) {
+                const float4 d0 = *reinterpret_cast<const float4*>(&dt[8 * g + 4 * hl]);
+                const float4 d1 = *reinterpret_cast<const float4*>(&dt[32 + 8 * g + 4 * hl]);
+                x0[4 * g] = d0.x, x0[4 * g + 1] = d0.y, x0[4 * g + 2] = d0.z, x0[4 * g + 3] = d0.w;
+                x1[4 * g] = d1.x, x1[4 * g + 1] = d1.y, x1[4 * g + 2] = d1.z, x1[4 * g + 3] = d1.w;
+            }
+        }
+        __builtin_amdgcn_s_setprio(1);
+        rows_x_ksteps<D>(rb, col, hl, kv, x0, x1);
+        __builtin_amdgcn_s_setprio(0);
         auto softmax = [&](f32x16_t& x, int mr) {   // S -> P (role 0)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const float4 l4 = *reinterpret_cast<const float4*>(&lt[32 * mr + 8 * g + 4 * hl]);
+                const float4 l4 = *reinterpret_cast<const float4*>(&l2[32 * mr + 8 * g + 4 * hl]);
                 const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
 #pragma unroll
-                for (int r = 0; r < 4; ++r) x[4 * g + r] = fast_exp2(fmaf(x[4 * g + r], scale_log2, -lv[r] * kLog2e));
+                for (int r = 0; r < 4; ++r) x[4 * g + r] = fast_exp2(fmaf(x[4 * g + r], scale_log2, -lv[r]));
             }
         };
-        auto dsoft = [&](f32x16_t& x, int mr) {     // dP -> dS = P (dP - D) (role 1)
+        auto dsoft = [&](f32x16_t& x) {             // D - dP -> -dS = P (D - dP) (role 1)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const float4 p4 = pex[64 * g];
-                const float4 d4 = *reinterpret_cast<const float4*>(&dt[32 * mr + 8 * g + 4 * hl]);
-                x[4 * g + 0] = p4.x * (x[4 * g + 0] - d4.x);
-                x[4 * g + 1] = p4.y * (x[4 * g + 1] - d4.y);
-                x[4 * g + 2] = p4.z * (x[4 * g + 2] - d4.z);
-                x[4 * g + 3] = p4.w * (x[4 * g + 3] - d4.w);
+                x[4 * g + 0] *= p4.x;
+                x[4 * g + 1] *= p4.y;
+                x[4 * g + 2] *= p4.z;
+                x[4 * g + 3] *= p4.w;
             }
         };
         auto publish = [&](const f32x16_t& x) {     // P -> LDS (role 0)
@@ -391,20 +408,18 @@ attn_dkdv_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
             }
             __builtin_amdgcn_s_setprio(0);
         };
-        f32x16_t x0 = rows(0);
         if (role == 0) {
             softmax(x0, 0);
             publish(x0);
+            softmax(x1, 1);
         }
         __syncthreads();
-        f32x16_t x1 = rows(1);
-        if (role == 0) softmax(x1, 1);
-        else dsoft(x0, 0);
+        if (role) dsoft(x0);
         accumulate(x0, 0);
         __syncthreads();   // role 1 has read P of half 0
         if (role == 0) publish(x1);
         __syncthreads();
-        if (role) dsoft(x1, 1);
+        if (role) dsoft(x1);
         accumulate(x1, 1);
     };
 
@@ -412,7 +427,7 @@ attn_dkdv_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
     cur.init(ti, offs, e0, e1);
     tile_pipeline(cur, issue, compute);
     uint16_t* out = (role ? dk : dv) + row_offset(om, key, h);
-    const float f = role ? scale : 1.0f;
+    const float f = role ? -scale : 1.0f;   // role 1 summed Q^T (-dS)
     // routed backward: the block-mean gradient of this key block, shared by its B tokens
     const float* __restrict__ add = role ? dkbar : dvbar;
     const float* __restrict__ addj = add ? add + (static_cast<int64_t>(h) * nb + j) * D : nullptr;
