@@ -589,7 +589,14 @@ def main():
     ld, hs = qp.stride(0), qp.stride(1)
     hc = path.hc
     lse = torch.empty((hc, cfg.N), dtype=torch.float32, device="cuda")
-    cap = nb * nb
+    # CSR capacity from the counts: one sizing selection per head group
+    # before the timed region (the timed steps select the same sets again)
+    for src, dst in ((x["q"], qp), (x["k"], kp)):
+        path.permute(src, out=dst)
+    for h0 in range(0, cfg.heads, hc):
+        path.select(qp, kp, h0)
+    cap = path._cap_guess()
+    torch.cuda.synchronize()
     sel_bufs = []
     for _ in range(0, cfg.heads, hc):
         from dynamic_block_sparse_amd.path import Selection
@@ -598,7 +605,7 @@ def main():
                                   torch.empty(hc, dtype=torch.int64, device="cuda"), cap, None))
     # the calls run one after another on one stream, so one workspace serves them all
     ws_sizes = {"zone": P.prism_workspace_size(P.OP_ZONE_SHAPES, cfg.N, 1, cfg.heads * cfg.d, 0, 0),
-                "sel": P.prism_workspace_size(P.OP_SELECT, cfg.N, hc, cfg.d, nb, cap),
+                "sel": P.prism_workspace_size(P.OP_SELECT, cfg.N, hc, cfg.d, nb, 0),
                 "fwd": P.prism_workspace_size(P.OP_ATTN_FWD, cfg.N, hc, cfg.d, nb, cap),
                 "bwd": P.prism_workspace_size(P.OP_ATTN_BWD, cfg.N, hc, cfg.d, nb, cap)}
     ws_all = torch.empty(max(ws_sizes.values()), dtype=torch.uint8, device="cuda")
@@ -651,6 +658,14 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = wall / args.steps * 1e3
+    short = [int(s.total.max().item()) for s in sel_bufs if int(s.total.max().item()) > cap]
+    if short:
+        raise RuntimeError(f"a head's selection needed {max(short)} CSR entries, above the sized capacity {cap}")
+    # device memory the step holds: inputs, block-major copies, outputs, the
+    # selections and the shared workspace (what torch has allocated)
+    memory = {"allocated_gb": round(torch.cuda.memory_allocated() / 1e9, 2),
+              "workspace_gb": round(ws_all.numel() / 1e9, 3),
+              "csr_entries_per_head": cap}
     acc = {s: 0.0 for s in stages}
     for ev in evs:
         acc["shapes"] += ev[0].elapsed_time(ev[1])
@@ -698,6 +713,7 @@ def main():
         "stage_ms": {s: round(v, 3) for s, v in stage_ms.items()},
         "stage_gbs_algorithmic": stage_gbs,
         "roofline": roofline,
+        "device_memory": memory,
     }
     if not args.no_next_rows:
         result["next_rows"] = {"f1_audio_norm_map": measure_norm_map(cfg),

@@ -61,15 +61,15 @@ struct SelectWs {
     float* logits;
     int32_t* row_count;
     uint32_t* row_thr;
-    int32_t* row_jlim;
+    int32_t* row_tie;
 };
 SelectWs carve_select(Carver& c, int64_t heads, int64_t d, int64_t nb) {
     SelectWs w;
     w.pooled = c.take<double>(2 * heads * nb * d);
-    w.logits = c.take<float>(heads * nb * nb);
+    w.logits = c.take<float>(prism::score_group_heads(static_cast<int>(heads), static_cast<int>(nb)) * nb * nb);
     w.row_count = c.take<int32_t>(heads * nb);
     w.row_thr = c.take<uint32_t>(heads * nb);
-    w.row_jlim = c.take<int32_t>(heads * nb);
+    w.row_tie = c.take<int32_t>(heads * nb);
     return w;
 }
 
@@ -78,19 +78,20 @@ struct SubSelectWs {
     float* logits;
     int32_t* row_count;
     uint32_t* row_thr;
-    int32_t* row_jlim;
+    int32_t* row_tie;
     prism::SubblockWs sub;
 };
 SubSelectWs carve_select_sub(Carver& c, int64_t N, int64_t heads, int64_t d, int64_t nb) {
     SubSelectWs w;
     const int64_t nr = N / 64;
-    w.logits = c.take<float>(heads * nb * nb);
+    const int64_t hg = prism::subblock_group_heads(static_cast<int>(heads), nr, static_cast<int>(nb));
+    w.logits = c.take<float>(hg * nb * nb);
     w.row_count = c.take<int32_t>(heads * nb);
     w.row_thr = c.take<uint32_t>(heads * nb);
-    w.row_jlim = c.take<int32_t>(heads * nb);
+    w.row_tie = c.take<int32_t>(heads * nb);
     w.sub.run_offs = c.take<int32_t>(nr + 1);
     w.sub.run_pooled = c.take<double>(2 * heads * nr * d);
-    w.sub.run_scores = c.take<double>(heads * nr * nr);
+    w.sub.run_scores = c.take<double>(hg * nr * nr);
     return w;
 }
 
@@ -624,8 +625,8 @@ prism_status prism_select(const void* q, const void* k, prism_dtype dt, int64_t 
     SelectWs w = carve_select(c, heads, d, nb);
     float* L = logits ? logits : w.logits;
     return hip_status(prism::launch_select(q, k, dt == PRISM_BF16, heads, d, ld, hs, block_offsets, nb, top_k, top_p,
-                                           scale, sel_offsets, sel_idx, cap, sel_total, L, w.pooled, w.row_count,
-                                           w.row_thr, w.row_jlim, stream),
+                                           scale, sel_offsets, sel_idx, cap, sel_total, L, logits != nullptr, w.pooled,
+                                           w.row_count, w.row_thr, w.row_tie, stream),
                       "select launch");
 }
 
@@ -653,7 +654,8 @@ prism_status prism_select_subblock(const void* q, const void* k, prism_dtype dt,
     float* L = logits ? logits : w.logits;
     return hip_status(prism::launch_select_subblock(q, k, dt == PRISM_BF16, heads, d, ld, hs, N, block_offsets, nb,
                                                     top_k, top_p, scale, sel_offsets, sel_idx, cap, sel_total, L,
-                                                    w.sub, w.row_count, w.row_thr, w.row_jlim, stream),
+                                                    logits != nullptr, w.sub, w.row_count, w.row_thr, w.row_tie,
+                                                    stream),
                       "sub-block select launch");
 }
 

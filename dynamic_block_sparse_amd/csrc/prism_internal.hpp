@@ -24,23 +24,32 @@ hipError_t launch_block_permute_heads(const void* x, void* y, int elem_bytes, in
                                       int64_t x_hs, int64_t y_ld, int64_t y_hs, const uint8_t* zone_shape, ZoneGrid g,
                                       int64_t N, int inverse, hipStream_t s);
 
+// The selection scores heads in groups: the fp32 score matrices of one group
+// ([g, nb, nb]) are written and then read back by the selection, so a group is
+// sized to stay within the 256 MB memory-side (Infinity) cache of the MI355X
+// (one head at 2K: 6924^2 scores = 192 MB), and no [heads, nb, nb] matrix is
+// kept.  logits_all: the caller's buffer holds every head's scores instead.
+constexpr int64_t kScoreGroupBytes = int64_t(256) << 20;
+int64_t score_group_heads(int heads, int nb);
+int64_t subblock_group_heads(int heads, int64_t nr, int nb);
+
 hipError_t launch_select(const void* q, const void* k, bool bf16, int heads, int d, int64_t ld, int64_t hs,
                          const int32_t* offs, int nb, int top_k, double top_p, float scale, int32_t* sel_offsets,
-                         int32_t* sel_idx, int64_t cap, int64_t* sel_total, float* logits, double* pooled,
-                         int32_t* row_count, uint32_t* row_thr, int32_t* row_jlim, hipStream_t s);
+                         int32_t* sel_idx, int64_t cap, int64_t* sel_total, float* logits, bool logits_all,
+                         double* pooled, int32_t* row_count, uint32_t* row_thr, int32_t* row_tie, hipStream_t s);
 
 // Sub-block scoring: the runs (64-token pieces) of the N tokens, their float64
 // means of Q and K, and their pairwise float64 scores.
 struct SubblockWs {
     int32_t* run_offs;     // [N/64 + 1]
     double* run_pooled;    // [2, heads, N/64, d]
-    double* run_scores;    // [heads, N/64, N/64]
+    double* run_scores;    // [g, N/64, N/64]: one head group (subblock_group_heads)
 };
 hipError_t launch_select_subblock(const void* q, const void* k, bool bf16, int heads, int d, int64_t ld, int64_t hs,
                                   int64_t N, const int32_t* offs, int nb, int top_k, double top_p, float scale,
                                   int32_t* sel_offsets, int32_t* sel_idx, int64_t cap, int64_t* sel_total,
-                                  float* logits, const SubblockWs& w, int32_t* row_count, uint32_t* row_thr,
-                                  int32_t* row_jlim, hipStream_t s);
+                                  float* logits, bool logits_all, const SubblockWs& w, int32_t* row_count,
+                                  uint32_t* row_thr, int32_t* row_tie, hipStream_t s);
 
 // rowmask (NULL: every query block) keeps query block i when
 // (rowmask[h*nb + i] != 0) == want

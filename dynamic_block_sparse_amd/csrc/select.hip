@@ -14,10 +14,11 @@
 //   select_reg_kernel    per row (up to 16384 blocks): the row's order-
 //                        preserving 32-bit score keys and their softmax masses
 //                        (float64 exp, as 2^-48 fixed-point integers) are held
-//                        in registers; a binary search over the key space,
-//                        each step one block-wide (count, mass) reduction,
-//                        finds the boundary of the first max(k, n_p) ranked
-//                        blocks; ties at the boundary are resolved by index.
+//                        in registers; a (count, mass) histogram over 256
+//                        score buckets finds the bucket of the boundary of the
+//                        first max(k, n_p) ranked blocks, and a binary search
+//                        over that bucket's keys finds the boundary; ties at
+//                        it are resolved by index.
 //                        No sort: the union of the two prefixes is one prefix
 //                        of the ranking, so only its boundary matters.
 //   select_count_kernel  the same result for longer rows, keys in LDS, by a
@@ -114,7 +115,8 @@ typedef double d4_t __attribute__((ext_vector_type(4)));
 constexpr int kLGroup = 8;
 template <int D, typename TOut>
 __global__ void __launch_bounds__(256, 2)
-logits_kernel(const double* __restrict__ pooled, int nb, int heads, double scale, TOut* __restrict__ logits) {
+logits_kernel(const double* __restrict__ pq, const double* __restrict__ pk, int nb, double scale,
+              TOut* __restrict__ logits) {
     __shared__ double Qs[kLC][kLT + 2];
     __shared__ double Ks[kLC][kLT + 2];
     const int nt = (nb + kLT - 1) / kLT;
@@ -129,8 +131,8 @@ logits_kernel(const double* __restrict__ pooled, int nb, int heads, double scale
     const int ti = first + (u % per_group) % gsize;
     const int tj = (u % per_group) / gsize;
     const int i0 = ti * kLT, j0 = tj * kLT;
-    const double* __restrict__ Qb = pooled + static_cast<int64_t>(h) * nb * D;
-    const double* __restrict__ Kb = pooled + (static_cast<int64_t>(heads) + h) * nb * D;
+    const double* __restrict__ Qb = pq + static_cast<int64_t>(h) * nb * D;
+    const double* __restrict__ Kb = pk + static_cast<int64_t>(h) * nb * D;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
     const int wi = wave >> 1, wj = wave & 1;
@@ -259,6 +261,9 @@ __device__ __forceinline__ uint64_t mass_fixed(uint32_t key, double M) {
 }
 
 constexpr int kSelThreads = 256;
+constexpr int kBuckets = kSelThreads;   // score buckets of select_reg_kernel
+constexpr float kBucketSpan = 40.0f;    // their span below the row maximum at most:
+                                        // mass below max - 34.7 rounds to 0 (2^-48 units)
 
 // One workgroup per (row i, head h).  The row's keys live in LDS; the boundary
 // key of the kept prefix is found by a 4-pass radix select (8-bit digits, most
@@ -268,7 +273,7 @@ constexpr int kSelThreads = 256;
 //   count >= max(k, 1)  and  mass >= p * Z.
 __global__ void __launch_bounds__(kSelThreads)
 select_count_kernel(const float* __restrict__ logits, int nb, int top_k, double top_p, int32_t* __restrict__ row_count,
-                    uint32_t* __restrict__ row_thr, int32_t* __restrict__ row_jlim) {
+                    uint32_t* __restrict__ row_thr, int32_t* __restrict__ row_tie) {
     extern __shared__ uint32_t skey[];                 // nb keys
     __shared__ uint32_t hcnt[256];
     __shared__ unsigned long long hmass[256];
@@ -299,11 +304,11 @@ select_count_kernel(const float* __restrict__ logits, int nb, int top_k, double 
 
     int count;
     uint32_t thr;
-    int jlim;
+    int tie;
     if (!(nb >= kk && static_cast<double>(z) >= target)) {
         count = nb;                            // no prefix qualifies: keep every block
         thr = 0u;
-        jlim = -1;
+        tie = 0;
     } else {
         uint32_t prefix = 0, cabove = 0;
         uint64_t mabove = 0;
@@ -417,25 +422,12 @@ select_count_kernel(const float* __restrict__ logits, int nb, int top_k, double 
             acc += eb;
         } while (m < ceq && !(cabove + m >= static_cast<uint32_t>(kk) && static_cast<double>(acc) >= target));
         count = static_cast<int>(cabove + m);
-        if (m == ceq) {
-            jlim = nb;
-        } else {
-            // index of the m-th tie in ascending index order (rare: equal scores)
-            jlim = nb;
-            if (threadIdx.x == 0) {
-                uint32_t seen = 0;
-                for (int j = 0; j < nb; ++j)
-                    if (skey[j] == thr && ++seen == m) {
-                        jlim = j;
-                        break;
-                    }
-            }
-        }
+        tie = static_cast<int>(m);   // the first m ties in index order (select_write_kernel)
     }
     if (threadIdx.x == 0) {
         row_count[row] = count;
         row_thr[row] = thr;
-        row_jlim[row] = jlim;
+        row_tie[row] = tie;
     }
 }
 
@@ -530,14 +522,14 @@ __device__ __forceinline__ unsigned long long block_sum_m(unsigned long long m,
 // One workgroup per (row i, head h); thread t holds blocks t + 256 e, e < E.
 // The kept prefix is {key > u} plus the first ties of key u in index order,
 // where u is the largest key value with count(key >= u) >= max(k, 1) and
-// mass(key >= u) >= p * Z.  Both sums only grow as u falls, so u is found by
-// bisection: first on the count alone (u <= tk, the max(k, 1)-th largest
-// key), then, only for rows whose top max(k, 1) blocks hold less than p Z, on
-// the mass below tk.
+// mass(key >= u) >= p * Z.  Both sums only grow as u falls: a histogram over
+// score buckets finds the bucket that holds u, and a bisection over that
+// bucket's keys alone finds u.
+// (Registers capped so that four workgroups share a CU up to E = 32.)
 template <int E>
-__global__ void __launch_bounds__(kSelThreads)
+__global__ void __launch_bounds__(kSelThreads, E <= 32 ? 4 : 2)
 select_reg_kernel(const float* __restrict__ logits, int nb, int top_k, double top_p, int32_t* __restrict__ row_count,
-                  uint32_t* __restrict__ row_thr, int32_t* __restrict__ row_jlim) {
+                  uint32_t* __restrict__ row_thr, int32_t* __restrict__ row_tie) {
     __shared__ uint32_t red32[kSelThreads / kWave];
     __shared__ unsigned long long red64[kSelThreads / kWave];
     __shared__ uint32_t rc[2][kSelThreads / kWave];
@@ -545,11 +537,16 @@ select_reg_kernel(const float* __restrict__ logits, int nb, int top_k, double to
     __shared__ uint32_t ckey[kSelThreads];            // compacted undecided keys
     __shared__ unsigned long long cms[kSelThreads];   // and their masses
     __shared__ uint32_t ccnt, cres;
+    __shared__ uint32_t hcnt[kBuckets];               // per score bucket: keys
+    __shared__ unsigned long long hmass[kBuckets];    // and their mass
+    __shared__ uint32_t s_bc, s_bn;
+    __shared__ unsigned long long s_bm;
     const int i = blockIdx.x, h = blockIdx.y;
     const int64_t row = static_cast<int64_t>(h) * nb + i;
     const float* __restrict__ L = logits + row * nb;
     uint32_t key[E];
-    unsigned long long ms[E];
+    hcnt[threadIdx.x] = 0u;   // kBuckets == kSelThreads: thread t owns bucket t
+    hmass[threadIdx.x] = 0ull;
     uint32_t kmax = 0, nkmin = 0;   // nkmin = ~(smallest key)
 #pragma unroll
     for (int e = 0; e < E; ++e) {
@@ -562,21 +559,37 @@ select_reg_kernel(const float* __restrict__ logits, int nb, int top_k, double to
     kmax = block_max(kmax, red32);
     const uint32_t kmin = ~block_max(nkmin, red32);
     const double M = static_cast<double>(key_score(kmax));
+    // Score buckets counted down from the maximum, of width span /
+    // (kBuckets - 1), span = min(max - min, kBucketSpan); the last bucket also
+    // takes everything deeper.  A bucket is an interval of keys (the map only
+    // falls as the score grows).  Each key's mass goes to Z and to its
+    // bucket's (count, mass); the masses are not kept.
+    const float smax = key_score(kmax);
+    const float span = fminf(smax - key_score(kmin), kBucketSpan);
+    const float inv = span > 0.0f ? static_cast<float>(kBuckets - 1) / span : 0.0f;
+    auto bucket_of = [&](uint32_t kv) -> int {
+        const float t = (smax - key_score(kv)) * inv;
+        return t < static_cast<float>(kBuckets - 1) ? static_cast<int>(t) : kBuckets - 1;
+    };
     unsigned long long z = 0;
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-        ms[e] = key[e] ? mass_fixed(key[e], M) : 0ull;
-        z += ms[e];
-    }
-    z = block_sum(z, red64);
+    for (int e = 0; e < E; ++e)
+        if (key[e]) {
+            const unsigned long long m = mass_fixed(key[e], M);
+            const int b = bucket_of(key[e]);
+            z += m;
+            atomicAdd(&hcnt[b], 1u);
+            if (m) atomicAdd(&hmass[b], m);
+        }
+    z = block_sum(z, red64);   // its barriers also complete the histogram
     const double target = top_p * static_cast<double>(z);
     const uint32_t kk = top_k > 1 ? static_cast<uint32_t>(top_k) : 1u;
-    int count, jlim;
+    int count, tie;
     uint32_t thr;
     if (!(static_cast<uint32_t>(nb) >= kk && static_cast<double>(z) >= target)) {
         count = nb;                    // no prefix qualifies: keep every block
         thr = 0u;
-        jlim = -1;
+        tie = 0;
     } else {
         int slot = 0;
         // Largest u in [lo, hi) whose suffix (keys >= u) satisfies the count
@@ -591,13 +604,11 @@ select_reg_kernel(const float* __restrict__ logits, int nb, int top_k, double to
             __syncthreads();
 #pragma unroll
             for (int e = 0; e < E; ++e)
-                if (key[e] >= lo && key[e] < hi) {
-                    const uint32_t at = atomicAdd(&ccnt, 1u);
-                    ckey[at] = key[e];
-                    cms[at] = ms[e];
-                }
+                if (key[e] >= lo && key[e] < hi) ckey[atomicAdd(&ccnt, 1u)] = key[e];
             __syncthreads();
             if (threadIdx.x < kWave) {
+                // the candidates' masses are evaluated here, CPL per lane (not
+                // in the compaction, whose per-key branches a whole wave runs)
                 constexpr int CPL = kSelThreads / kWave;   // candidates per lane
                 const uint32_t n = ccnt;
                 uint32_t ck[CPL];
@@ -606,7 +617,7 @@ select_reg_kernel(const float* __restrict__ logits, int nb, int top_k, double to
                 for (int x = 0; x < CPL; ++x) {
                     const uint32_t j = threadIdx.x + kWave * x;
                     ck[x] = j < n ? ckey[j] : 0u;   // key 0 lies below every finite score's key
-                    cm[x] = j < n ? cms[j] : 0ull;
+                    cm[x] = (j < n && !by_count) ? mass_fixed(ck[x], M) : 0ull;
                 }
                 while (hi - lo > 1u) {
                     const uint32_t mid = lo + (hi - lo) / 2u;
@@ -647,12 +658,15 @@ select_reg_kernel(const float* __restrict__ logits, int nb, int top_k, double to
                     c = block_sum_c(c, rc, slot);
                     ok = c >= kk;
                 } else {
+                    // the mass at or above hi is m_hi; the masses of the keys in
+                    // [mid, hi) are evaluated again
 #pragma unroll
                     for (int e = 0; e < E; ++e) {
                         c += key[e] >= mid ? 1u : 0u;
-                        m += key[e] >= mid ? ms[e] : 0ull;
+                        if (key[e] >= mid && key[e] < hi) m += mass_fixed(key[e], M);
                     }
                     block_sum_cm(c, m, rc, rm, slot);
+                    m += m_hi;
                     ok = static_cast<double>(m) >= target;
                 }
                 if (ok) {
@@ -666,35 +680,116 @@ select_reg_kernel(const float* __restrict__ logits, int nb, int top_k, double to
             }
             return lo;
         };
-        // 1) tk = the largest key with count(key >= tk) >= kk: count condition
-        //    (all nb keys lie at or above kmin, none above kmax)
-        uint32_t lo = search(kmin, kmax + 1u, static_cast<uint32_t>(nb), 0u, 0ull, true);
-        // 2) if the blocks at or above tk already hold p Z, the boundary is tk;
-        // otherwise it lies below tk, where the count condition always holds,
-        //    and the mass condition finds the largest u with mass(key >= u) >= p Z
-        uint32_t ck_ = 0;
-        unsigned long long mk = 0;
+        // The boundary's bucket: the count and the mass of keys at or above a
+        // bucket's lowest key are prefix sums over the buckets from the top.
+        // The boundary u = min(u_count, u_mass) lies in the bucket b* where
+        // the later of the two conditions first holds; keys in earlier buckets
+        // are kept, keys in later ones are not, and the bisection runs only
+        // over the keys of b* (search() starts with the counts at its ends).
+        // inclusive prefix over the buckets: a wave scan, then the totals of
+        // the waves below
+        const int lane = threadIdx.x & (kWave - 1);
+        const int wid = threadIdx.x / kWave;
+        const uint32_t own_c = hcnt[threadIdx.x];
+        const unsigned long long own_m = hmass[threadIdx.x];
+        uint32_t pc = own_c;
+        unsigned long long pm = own_m;
 #pragma unroll
-        for (int e = 0; e < E; ++e) {
-            ck_ += key[e] >= lo ? 1u : 0u;
-            mk += key[e] >= lo ? ms[e] : 0ull;
+        for (int off = 1; off < kWave; off <<= 1) {
+            const uint32_t c = __shfl_up(pc, off, kWave);
+            const unsigned long long m = __shfl_up(pm, off, kWave);
+            if (lane >= off) {
+                pc += c;
+                pm += m;
+            }
         }
-        block_sum_cm(ck_, mk, rc, rm, slot);
-        if (!(static_cast<double>(mk) >= target))   // holds at kmin (all of Z), fails at tk
-            lo = search(kmin, lo, static_cast<uint32_t>(nb), ck_, mk, false);
+        if (lane == kWave - 1) {
+            rc[slot][wid] = pc;
+            rm[slot][wid] = pm;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int w = 0; w < kSelThreads / kWave; ++w)
+            if (w < wid) {
+                pc += rc[slot][w];
+                pm += rm[slot][w];
+            }
+        slot ^= 1;
+        // first bucket meeting each condition = the number of buckets that
+        // miss it (both only become true along the buckets, and both hold at
+        // the last bucket, which ends the row)
+        uint32_t miss_c = pc >= kk ? 0u : 1u;
+        unsigned long long miss_m = static_cast<double>(pm) >= target ? 0ull : 1ull;
+        block_sum_cm(miss_c, miss_m, rc, rm, slot);
+        const int b_c = static_cast<int>(miss_c), b_m = static_cast<int>(miss_m);
+        const int bs = b_c > b_m ? b_c : b_m;
+        if (static_cast<int>(threadIdx.x) == bs) {
+            s_bc = pc - own_c;   // count and mass of the keys above the bucket
+            s_bm = pm - own_m;
+            s_bn = own_c;
+        }
+        // the bucket's lowest and highest keys
+        uint32_t bmax = 0u, bnmin = 0u;
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+            if (key[e] && bucket_of(key[e]) == bs) {
+                bmax = key[e] > bmax ? key[e] : bmax;
+                bnmin = ~key[e] > bnmin ? ~key[e] : bnmin;
+            }
+        bmax = block_max(bmax, red32);
+        bnmin = block_max(bnmin, red32);   // its barriers also publish s_bc, s_bm, s_bn
+        const uint32_t blo = ~bnmin, bhi = bmax + 1u;
+        const uint32_t c_above = s_bc, n_b = s_bn;
+        const unsigned long long m_above = s_bm;
+        uint32_t lo = 0xFFFFFFFFu;
+        if (b_c == bs) lo = search(blo, bhi, c_above + n_b, c_above, m_above, true);
+        if (b_m == bs) {
+            const uint32_t um = search(blo, bhi, c_above + n_b, c_above, m_above, false);
+            lo = um < lo ? um : lo;
+        }
         thr = lo;
-        // blocks strictly above the boundary key, and the ties at it
+        // blocks strictly above the boundary key, and the ties at it.  The
+        // keys above b* hold m_above; the masses of the keys of b* above thr
+        // are evaluated again, by wave 0 on the compacted keys when they fit.
         uint32_t cabove = 0, ceq = 0;
-        unsigned long long mabove = 0;
 #pragma unroll
         for (int e = 0; e < E; ++e) {
             cabove += key[e] > thr ? 1u : 0u;
-            mabove += key[e] > thr ? ms[e] : 0ull;
             ceq += key[e] == thr ? 1u : 0u;
         }
-        block_sum_cm(cabove, mabove, rc, rm, slot);
-        unsigned long long dummy = 0;
-        block_sum_cm(ceq, dummy, rc, rm, slot);
+        {
+            unsigned long long c64 = ceq;
+            block_sum_cm(cabove, c64, rc, rm, slot);
+            ceq = static_cast<uint32_t>(c64);
+        }
+        unsigned long long mabove = 0;
+        if (cabove - c_above <= static_cast<uint32_t>(kSelThreads)) {
+            if (threadIdx.x == 0) ccnt = 0u;
+            __syncthreads();
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                if (key[e] > thr && key[e] < bhi) ckey[atomicAdd(&ccnt, 1u)] = key[e];
+            __syncthreads();
+            if (threadIdx.x < kWave) {
+                const uint32_t n = ccnt;
+                unsigned long long m = 0;
+#pragma unroll
+                for (int x = 0; x < kSelThreads / kWave; ++x) {
+                    const uint32_t j = threadIdx.x + kWave * x;
+                    m += j < n ? mass_fixed(ckey[j], M) : 0ull;
+                }
+                m = wave_sum_dpp(m);
+                if (threadIdx.x == 0) cms[0] = m;
+            }
+            __syncthreads();
+            mabove = cms[0];
+        } else {
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                if (key[e] > thr && key[e] < bhi) mabove += mass_fixed(key[e], M);
+            mabove = block_sum_m(mabove, rm, slot);
+        }
+        mabove += m_above;
         const uint64_t eb = mass_fixed(thr, M);
         uint32_t m = 0;
         uint64_t acc = mabove;
@@ -703,21 +798,12 @@ select_reg_kernel(const float* __restrict__ logits, int nb, int top_k, double to
             acc += eb;
         } while (m < ceq && !(cabove + m >= kk && static_cast<double>(acc) >= target));
         count = static_cast<int>(cabove + m);
-        jlim = nb;
-        if (m < ceq && threadIdx.x == 0) {
-            // index of the m-th tie in ascending index order (rare: equal scores)
-            uint32_t seen = 0;
-            for (int j = 0; j < nb; ++j)
-                if (score_key(L[j]) == thr && ++seen == m) {
-                    jlim = j;
-                    break;
-                }
-        }
+        tie = static_cast<int>(m);   // the first m ties in index order (select_write_kernel)
     }
     if (threadIdx.x == 0) {
         row_count[row] = count;
         row_thr[row] = thr;
-        row_jlim[row] = jlim;
+        row_tie[row] = tie;
     }
 }
 
@@ -756,27 +842,32 @@ csr_scan_kernel(const int32_t* __restrict__ counts, int n, int32_t* __restrict__
 // The row is taken kWriteChunks chunks of NW*64 keys at a time: each thread
 // has that many independent loads in flight, and one barrier per pass orders
 // the chunks (the per-wave counts are double-buffered, so the next pass can
-// write its counts while a slower wave still reads this pass's).
+// write its counts while a slower wave still reads this pass's).  A block is
+// kept if its key is above the row's boundary key, or equal to it and among
+// the first `tie` such blocks in index order; the ties' ranks come from the
+// same per-wave counts.
 constexpr int kWriteChunks = 4;
 template <int NW>
 __global__ void __launch_bounds__(NW * 64)
 select_write_kernel(const float* __restrict__ logits, int nb, const uint32_t* __restrict__ row_thr,
-                    const int32_t* __restrict__ row_jlim, const int32_t* __restrict__ sel_offsets,
+                    const int32_t* __restrict__ row_tie, const int32_t* __restrict__ sel_offsets,
                     int32_t* __restrict__ sel_idx, int64_t cap) {
     constexpr int NT = NW * 64;
     constexpr int U = kWriteChunks;
-    __shared__ int sc[2][U * NW];
+    __shared__ int sg[2][U * NW];   // keys above the boundary, per chunk and wave
+    __shared__ int st[2][U * NW];   // keys equal to it
     const int i = blockIdx.x, h = blockIdx.y;
     const int64_t row = static_cast<int64_t>(h) * nb + i;
     const float* __restrict__ L = logits + row * nb;
     const uint32_t thr = row_thr[row];
-    const int jlim = row_jlim[row];
+    const int tie = row_tie[row];
     int64_t pos = sel_offsets[static_cast<int64_t>(h) * (nb + 1) + i];
     int32_t* __restrict__ out = sel_idx + static_cast<int64_t>(h) * cap;
     const int lane = threadIdx.x & (kWave - 1);
     const int wid = threadIdx.x / kWave;
     const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));   // lanes under this one
     int buf = 0;
+    int tbase = 0;   // ties in earlier passes
     for (int base = 0; base < nb; base += U * NT) {
         float v[U];
 #pragma unroll
@@ -784,38 +875,49 @@ select_write_kernel(const float* __restrict__ logits, int nb, const uint32_t* __
             const int j = base + u * NT + static_cast<int>(threadIdx.x);
             v[u] = j < nb ? L[j] : 0.0f;
         }
-        bool f[U];
-        int before[U];
+        bool g[U], t[U];
+        uint64_t bt[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int j = base + u * NT + static_cast<int>(threadIdx.x);
-            f[u] = false;
-            if (j < nb) {
-                const uint32_t kk = score_key(v[u]);
-                f[u] = kk > thr || (kk == thr && j <= jlim);
+            const uint32_t kk = score_key(v[u]);
+            g[u] = j < nb && kk > thr;
+            t[u] = j < nb && kk == thr;
+            bt[u] = __ballot(t[u]);
+            const uint64_t bg = __ballot(g[u]);
+            if (lane == 0) {
+                sg[buf][u * NW + wid] = __popcll(bg);
+                st[buf][u * NW + wid] = __popcll(bt[u]);
             }
-            const uint64_t bal = __ballot(f[u]);
-            before[u] = __popcll(bal & below);
-            if (lane == 0) sc[buf][u * NW + wid] = __popcll(bal);
         }
         __syncthreads();
         // chunk u of wave w starts after every chunk before u and, inside u,
-        // after the waves below w
-        int acc = 0, woff[U];
+        // after the waves below w; of the ties of (u, w), those ranked below
+        // `tie` in the row are kept
+        int acc = 0, tacc = tbase, woff[U], toff[U];
 #pragma unroll
         for (int u = 0; u < U; ++u)
 #pragma unroll
             for (int w = 0; w < NW; ++w) {
-                if (w == wid) woff[u] = acc;
-                acc += sc[buf][u * NW + w];
+                const int ng = sg[buf][u * NW + w], nt = st[buf][u * NW + w];
+                if (w == wid) {
+                    woff[u] = acc;
+                    toff[u] = tacc;
+                }
+                acc += ng + min(max(tie - tacc, 0), nt);
+                tacc += nt;
             }
 #pragma unroll
-        for (int u = 0; u < U; ++u)
-            if (f[u]) {
-                const int64_t p = pos + woff[u] + before[u];
+        for (int u = 0; u < U; ++u) {
+            const bool f = g[u] || (t[u] && toff[u] + __popcll(bt[u] & below) < tie);
+            const int before = __popcll(__ballot(f) & below);
+            if (f) {
+                const int64_t p = pos + woff[u] + before;
                 if (p < cap) out[p] = base + u * NT + static_cast<int>(threadIdx.x);
             }
+        }
         pos += acc;
+        tbase = tacc;
         buf ^= 1;
     }
 }
@@ -1049,23 +1151,26 @@ hipError_t launch_pool(const void* q, const void* k, bool bf16, int heads, int d
     return hipGetLastError();
 }
 
+// scores of `heads` heads whose pooled means of Q and K start at pq and pk
+// (n x d doubles per head)
 template <typename TOut>
-hipError_t launch_scores(const double* pooled, int n, int heads, int d, float scale, TOut* out, hipStream_t s) {
+hipError_t launch_scores(const double* pq, const double* pk, int n, int heads, int d, float scale, TOut* out,
+                         hipStream_t s) {
     const int nt = (n + kLT - 1) / kLT;
     const dim3 lg(static_cast<unsigned>(nt * nt * heads));
     if (d == 128)
-        hipLaunchKernelGGL((logits_kernel<128, TOut>), lg, dim3(256), 0, s, pooled, n, heads,
-                           static_cast<double>(scale), out);
+        hipLaunchKernelGGL((logits_kernel<128, TOut>), lg, dim3(256), 0, s, pq, pk, n, static_cast<double>(scale),
+                           out);
     else
-        hipLaunchKernelGGL((logits_kernel<64, TOut>), lg, dim3(256), 0, s, pooled, n, heads,
-                           static_cast<double>(scale), out);
+        hipLaunchKernelGGL((logits_kernel<64, TOut>), lg, dim3(256), 0, s, pq, pk, n, static_cast<double>(scale),
+                           out);
     return hipGetLastError();
 }
 
 // the selection proper, from the fp32 scores of every row
 hipError_t select_rows(const float* logits, int heads, int nb, int top_k, double top_p, int32_t* sel_offsets,
                        int32_t* sel_idx, int64_t cap, int64_t* sel_total, int32_t* row_count, uint32_t* row_thr,
-                       int32_t* row_jlim, hipStream_t s) {
+                       int32_t* row_tie, hipStream_t s) {
     const dim3 rg(nb, heads);
     // PRISM_SELECT_RADIX=1 forces the LDS radix kernel (used by the tests to
     // compare the two kernels on rows of any length)
@@ -1075,17 +1180,17 @@ hipError_t select_rows(const float* logits, int heads, int nb, int top_k, double
     if (!radix && nb <= 16 * kSelThreads) {
         if (nb <= 8 * kSelThreads)
             hipLaunchKernelGGL(select_reg_kernel<8>, rg, dim3(kSelThreads), 0, s, logits, nb, top_k, top_p, row_count,
-                               row_thr, row_jlim);
+                               row_thr, row_tie);
         else
             hipLaunchKernelGGL(select_reg_kernel<16>, rg, dim3(kSelThreads), 0, s, logits, nb, top_k, top_p,
-                               row_count, row_thr, row_jlim);
+                               row_count, row_thr, row_tie);
     } else if (!radix && nb <= 64 * kSelThreads) {
         if (nb <= 32 * kSelThreads)
             hipLaunchKernelGGL(select_reg_kernel<32>, rg, dim3(kSelThreads), 0, s, logits, nb, top_k, top_p,
-                               row_count, row_thr, row_jlim);
+                               row_count, row_thr, row_tie);
         else
             hipLaunchKernelGGL(select_reg_kernel<64>, rg, dim3(kSelThreads), 0, s, logits, nb, top_k, top_p,
-                               row_count, row_thr, row_jlim);
+                               row_count, row_thr, row_tie);
     } else {
         const size_t lds = static_cast<size_t>(nb) * sizeof(uint32_t);
         if (lds > 48 * 1024) {
@@ -1094,37 +1199,67 @@ hipError_t select_rows(const float* logits, int heads, int nb, int top_k, double
             if (e != hipSuccess) return e;
         }
         hipLaunchKernelGGL(select_count_kernel, rg, dim3(kSelThreads), lds, s, logits, nb, top_k, top_p, row_count,
-                           row_thr, row_jlim);
+                           row_thr, row_tie);
     }
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(csr_scan_kernel, dim3(heads), dim3(1024), 0, s, row_count, nb, sel_offsets, sel_total);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(select_write_kernel<4>, rg, dim3(256), 0, s, logits, nb, row_thr, row_jlim, sel_offsets,
+    hipLaunchKernelGGL(select_write_kernel<4>, rg, dim3(256), 0, s, logits, nb, row_thr, row_tie, sel_offsets,
                        sel_idx, cap);
     return hipGetLastError();
 }
 
 }  // namespace
 
+// PRISM_SCORE_GROUP_BYTES overrides the group budget (the tests force groups
+// of one head on small grids); the workspace size and the launches read it
+// alike, so it must not change between the two
+int64_t score_group_budget() {
+    const char* ev = std::getenv("PRISM_SCORE_GROUP_BYTES");
+    const long long v = ev ? std::atoll(ev) : 0;
+    return v > 0 ? static_cast<int64_t>(v) : kScoreGroupBytes;
+}
+
+int64_t score_group_heads(int heads, int nb) {
+    const int64_t per_head = static_cast<int64_t>(nb) * nb * static_cast<int64_t>(sizeof(float));
+    return std::max<int64_t>(1, std::min<int64_t>(heads, score_group_budget() / std::max<int64_t>(per_head, 1)));
+}
+
 hipError_t launch_select(const void* q, const void* k, bool bf16, int heads, int d, int64_t ld, int64_t hs,
                          const int32_t* offs, int nb, int top_k, double top_p, float scale, int32_t* sel_offsets,
-                         int32_t* sel_idx, int64_t cap, int64_t* sel_total, float* logits, double* pooled,
-                         int32_t* row_count, uint32_t* row_thr, int32_t* row_jlim, hipStream_t s) {
+                         int32_t* sel_idx, int64_t cap, int64_t* sel_total, float* logits, bool logits_all,
+                         double* pooled, int32_t* row_count, uint32_t* row_thr, int32_t* row_tie, hipStream_t s) {
     hipError_t e = launch_pool(q, k, bf16, heads, d, ld, hs, offs, nb, pooled, s);
     if (e != hipSuccess) return e;
-    e = launch_scores<float>(pooled, nb, heads, d, scale, logits, s);
-    if (e != hipSuccess) return e;
-    return select_rows(logits, heads, nb, top_k, top_p, sel_offsets, sel_idx, cap, sel_total, row_count, row_thr,
-                       row_jlim, s);
+    // heads in groups whose scores fit kScoreGroupBytes; the group's score
+    // buffer is reused unless the caller asked for every head's scores
+    const int64_t hg = logits_all ? heads : score_group_heads(heads, nb);
+    const int64_t nb2 = static_cast<int64_t>(nb) * nb;
+    for (int64_t h0 = 0; h0 < heads; h0 += hg) {
+        const int g = static_cast<int>(std::min<int64_t>(hg, heads - h0));
+        float* L = logits_all ? logits + h0 * nb2 : logits;
+        e = launch_scores<float>(pooled + h0 * nb * d, pooled + (heads + h0) * nb * d, nb, g, d, scale, L, s);
+        if (e != hipSuccess) return e;
+        e = select_rows(L, g, nb, top_k, top_p, sel_offsets + h0 * (nb + 1), sel_idx + h0 * cap, cap, sel_total + h0,
+                        row_count + h0 * nb, row_thr + h0 * nb, row_tie + h0 * nb, s);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+int64_t subblock_group_heads(int heads, int64_t nr, int nb) {
+    const int64_t per_head = nr * nr * static_cast<int64_t>(sizeof(double)) +
+                             static_cast<int64_t>(nb) * nb * static_cast<int64_t>(sizeof(float));
+    return std::max<int64_t>(1, std::min<int64_t>(heads, score_group_budget() / std::max<int64_t>(per_head, 1)));
 }
 
 hipError_t launch_select_subblock(const void* q, const void* k, bool bf16, int heads, int d, int64_t ld, int64_t hs,
                                   int64_t N, const int32_t* offs, int nb, int top_k, double top_p, float scale,
                                   int32_t* sel_offsets, int32_t* sel_idx, int64_t cap, int64_t* sel_total,
-                                  float* logits, const SubblockWs& w, int32_t* row_count, uint32_t* row_thr,
-                                  int32_t* row_jlim, hipStream_t s) {
+                                  float* logits, bool logits_all, const SubblockWs& w, int32_t* row_count,
+                                  uint32_t* row_thr, int32_t* row_tie, hipStream_t s) {
     const int64_t nr = N / 64;
     hipLaunchKernelGGL(run_offsets_kernel, dim3(static_cast<unsigned>((nr + 1 + 255) / 256)), dim3(256), 0, s,
                        w.run_offs, nr);
@@ -1132,13 +1267,24 @@ hipError_t launch_select_subblock(const void* q, const void* k, bool bf16, int h
     if (e != hipSuccess) return e;
     e = launch_pool(q, k, bf16, heads, d, ld, hs, w.run_offs, static_cast<int>(nr), w.run_pooled, s);
     if (e != hipSuccess) return e;
-    e = launch_scores<double>(w.run_pooled, static_cast<int>(nr), heads, d, scale, w.run_scores, s);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(subblock_reduce_kernel, dim3(nb, heads), dim3(256), 0, s, w.run_scores, nr, offs, nb, logits);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    return select_rows(logits, heads, nb, top_k, top_p, sel_offsets, sel_idx, cap, sel_total, row_count, row_thr,
-                       row_jlim, s);
+    // heads in groups, as in launch_select: the run-pair scores and the block
+    // scores of one group at a time
+    const int64_t hg = subblock_group_heads(heads, nr, nb);
+    const int64_t nb2 = static_cast<int64_t>(nb) * nb;
+    for (int64_t h0 = 0; h0 < heads; h0 += hg) {
+        const int g = static_cast<int>(std::min<int64_t>(hg, heads - h0));
+        float* L = logits_all ? logits + h0 * nb2 : logits;
+        e = launch_scores<double>(w.run_pooled + h0 * nr * d, w.run_pooled + (heads + h0) * nr * d,
+                                  static_cast<int>(nr), g, d, scale, w.run_scores, s);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(subblock_reduce_kernel, dim3(nb, g), dim3(256), 0, s, w.run_scores, nr, offs, nb, L);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        e = select_rows(L, g, nb, top_k, top_p, sel_offsets + h0 * (nb + 1), sel_idx + h0 * cap, cap, sel_total + h0,
+                        row_count + h0 * nb, row_thr + h0 * nb, row_tie + h0 * nb, s);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 // zeroes n counters with a kernel (not a memset node, so that a captured

@@ -80,6 +80,7 @@ class PrismPath:
         self.nb_dev = torch.empty(1, dtype=torch.int32, device=self.device)
         self.zone_stats = torch.empty(self.nZ * P.ZS_STRIDE, dtype=torch.float64, device=self.device)
         self.nb = None
+        self._cap_seen = 0   # largest per-head selection count seen (CSR sizing)
         self._reuse = None   # selections of the last fresh step, for step(..., reuse=True)
         if zone_order not in ("raster", "hilbert"):
             raise ValueError("zone_order must be 'raster' or 'hilbert'")
@@ -98,6 +99,7 @@ class PrismPath:
         self.nb = P.prism_zone_shapes(self.T, self.H, self.W, v, C, v.stride(0), a, self.zone_shape,
                                       self.block_offsets, self.nb_dev, ws, prm=self.prm, zone_stats=self.zone_stats,
                                       zone_order=self.zone_order)
+        self._cap_seen = 0
         return self.nb
 
     def block_major_like(self, x):
@@ -128,26 +130,41 @@ class PrismPath:
                                   out.stride(0), 1 if inverse else 0, zone_order=self.zone_order)
         return out
 
-    def _cap(self):
-        return self.nb * self.nb
+    def _cap_guess(self):
+        """First CSR capacity per head to try: the largest count seen so far on
+        this path, else 4 k entries per row (at most nb * nb)."""
+        if self._cap_seen:
+            return self._cap_seen
+        return min(self.nb * self.nb, 4 * max(self.top_k, 1) * self.nb)
 
     def select(self, qp, kp, h0=0, want_logits=False, scoring=None, cap=None):
         """scoring: "block" (pooled block scores, prism_select) or "subblock"
         (prism_select_subblock); default the path's own.  cap: CSR capacity per
-        head (default nb * nb, which never truncates)."""
+        head.  Default: sized from the counts, i.e. a first guess, and one more
+        call with the largest per-head count when the guess was short (nb * nb
+        never truncates)."""
         scoring = scoring or self.scoring
         nb, hc = self.nb, self.hc
-        cap = self._cap() if cap is None else int(cap)
+        fixed = cap is not None
+        cap = int(cap) if fixed else self._cap_guess()
         offsets = torch.empty((hc, nb + 1), dtype=torch.int32, device=self.device)
-        idx = torch.empty((hc, cap), dtype=torch.int32, device=self.device)
         total = torch.empty(hc, dtype=torch.int64, device=self.device)
         logits = torch.empty((hc, nb, nb), dtype=torch.float32, device=self.device) if want_logits else None
         op, fn = (P.OP_SELECT, P.prism_select) if scoring == "block" else (P.OP_SELECT_SUB, P.prism_select_subblock)
-        ws = torch.empty(P.prism_workspace_size(op, self.N, hc, self.d, nb, cap), dtype=torch.uint8,
+        ws = torch.empty(P.prism_workspace_size(op, self.N, hc, self.d, nb, 0), dtype=torch.uint8,
                          device=self.device)
         q, k = qp[:, h0:h0 + hc], kp[:, h0:h0 + hc]
-        fn(q, k, self.N, hc, self.d, q.stride(0), q.stride(1), self.block_offsets, nb, self.top_k, self.top_p,
-           self.scale, offsets, idx, cap, total, ws, logits=logits)
+        while True:
+            idx = torch.empty((hc, cap), dtype=torch.int32, device=self.device)
+            fn(q, k, self.N, hc, self.d, q.stride(0), q.stride(1), self.block_offsets, nb, self.top_k, self.top_p,
+               self.scale, offsets, idx, cap, total, ws, logits=logits)
+            if fixed:
+                break
+            need = int(total.max().item())
+            self._cap_seen = max(self._cap_seen, need)
+            if need <= cap:
+                break
+            cap = need
         return Selection(offsets, idx, total, cap, logits)
 
     def raster_layout(self, x):

@@ -37,11 +37,19 @@
  *     (PRISM_E_ARG otherwise) and nb <= 32768 (PRISM_E_UNSUPPORTED above: the
  *     longest selection row, 32768 fp32 keys, is held in one workgroup's LDS).
  *     A 128 x 128 x 128 grid of 64-token blocks reaches the limit exactly.
- *   - Two environment variables switch to alternative kernels with the same
- *     results, for tests: PRISM_SELECT_RADIX=1 makes prism_select use its LDS
- *     radix-select kernel at every row length (by default it is used only for
- *     rows of more than 16384 blocks); PRISM_ATTN_SIMT=1 makes the bf16
- *     attention calls use the vector-ALU kernels instead of the MFMA ones.
+ *   - Environment variables that switch to alternative kernels or schedules
+ *     with the same results, for tests: PRISM_SELECT_RADIX=1 makes
+ *     prism_select use its LDS radix-select kernel at every row length (by
+ *     default it is used only for rows of more than 16384 blocks);
+ *     PRISM_ATTN_SIMT=1 makes the bf16 attention calls use the vector-ALU
+ *     kernels instead of the MFMA ones; PRISM_SCORE_GROUP_BYTES=n sets the
+ *     per-group budget of the selection's score matrices (default 256 MB);
+ *     PRISM_SPLIT_T, PRISM_SPLIT_W, PRISM_SPLIT_GROUP and PRISM_SPLIT_SLOTS
+ *     set the key-range split of long selected lists (first threshold in key
+ *     tiles, 0 = never split; range width in blocks; heads per launch group;
+ *     partial slots per 64-token tile).  Workspace sizes read the same
+ *     variables, so they must not change between prism_workspace_size and
+ *     the call.
  *   - Block-major order: zones in raster order (m = (zt*nH + zh)*nW + zw, 512
  *     positions each); inside a zone, its blocks in raster order over the block
  *     grid; inside a block, tokens in raster (t, h, w) order.  Raster token
@@ -236,11 +244,20 @@ prism_status prism_block_permute_heads(int32_t T, int32_t H, int32_t W, const ui
  *                  sel_idx[h*cap + sel_offsets[h*(nb+1) + i] ...
  *                  h*cap + sel_offsets[h*(nb+1) + i + 1] - 1]
  *   sel_idx        out [heads * cap] int32 key-block indices, ascending per row
- *   cap            capacity per head (nb*nb never truncates)
+ *   cap            capacity per head (nb*nb never truncates).  A caller that
+ *                  sizes it from the counts passes a guess, reads sel_total,
+ *                  and calls again with cap >= max(sel_total) if it was short
+ *                  (sel_offsets and sel_total are complete either way).
  *   sel_total      out device [heads] int64: entries head h needed; a value
  *                  above cap means that head's list was truncated at cap
  *                  (its CSR must then not be used)
- *   logits         optional out [heads * nb * nb] fp32: the pooled scores
+ *   logits         optional out [heads * nb * nb] fp32: the pooled scores.
+ *                  NULL: the scores are computed one group of heads at a
+ *                  time in the workspace, each group's [g, nb, nb] matrices
+ *                  within 256 MB (the MI355X's memory-side cache), and no
+ *                  matrix of every head is kept.
+ *   ws, ws_bytes   prism_workspace_size(PRISM_OP_SELECT, N, heads, d, nb, 0)
+ *                  bytes (independent of cap)
  *
  * Each block is pooled by its float64 mean; its score with key block j is
  * scale * (Q_bar_i . K_bar_j) evaluated in float64 and rounded once to fp32.
@@ -274,8 +291,9 @@ prism_status prism_select(const void* q, const void* k, prism_dtype dt,
  *
  *   N              a multiple of 64
  *   ws, ws_bytes   prism_workspace_size(PRISM_OP_SELECT_SUB, N, heads, d, nb, 0)
- *                  bytes: the run-pair scores take heads * (N/64)^2 doubles
- *                  (16.3 GB for 24 heads of 589,824 tokens)
+ *                  bytes: the run-pair scores of one group of heads at a time,
+ *                  g * (N/64)^2 doubles, g as many heads as fit 256 MB with
+ *                  their block scores, at least one (680 MB at 589,824 tokens)
  * Status: as prism_select, plus PRISM_E_ARG when N is not a multiple of 64.
  */
 prism_status prism_select_subblock(const void* q, const void* k, prism_dtype dt,

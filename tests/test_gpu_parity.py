@@ -217,6 +217,60 @@ def test_selection_kernels_agree(idx, monkeypatch):
         assert torch.equal(a.idx[h, :t], b.idx[h, :t])
 
 
+@pytest.mark.parametrize("idx", [1, 2, 7], ids=lambda i: SMALL[i].name)
+def test_selection_by_head_groups(idx, monkeypatch):
+    """prism_select scores the heads in groups that fit the score budget; a
+    budget of one byte forces groups of one head.  The CSR must be identical,
+    with and without the caller's full score buffer, and so must the
+    sub-block variant's."""
+    cfg = SMALL[idx]
+    print(f"case {cfg.name}", flush=True)
+    x = make_inputs(cfg, device="cuda")
+    path = _path(cfg)
+    path.shapes(x["v"], x["a"])
+    qp, kp = path.permute(x["q"]), path.permute(x["k"])
+    cap = path.nb * path.nb
+    ref = {s: path.select(qp, kp, cap=cap, want_logits=True, scoring=s) for s in ("block", "subblock")}
+    monkeypatch.setenv("PRISM_SCORE_GROUP_BYTES", "1")
+    for scoring in ("block", "subblock"):
+        for want in (False, True):
+            got = path.select(qp, kp, cap=cap, want_logits=want, scoring=scoring)
+            torch.cuda.synchronize()
+            a = ref[scoring]
+            assert torch.equal(a.offsets, got.offsets), (scoring, want)
+            assert torch.equal(a.total, got.total), (scoring, want)
+            for h in range(cfg.heads):
+                t = int(a.total[h])
+                assert torch.equal(a.idx[h, :t], got.idx[h, :t]), (scoring, want, h)
+            if want:
+                assert torch.equal(a.logits, got.logits), scoring
+
+
+@pytest.mark.parametrize("idx", [2, 7], ids=lambda i: SMALL[i].name)
+def test_csr_capacity_from_counts(idx):
+    """Without an explicit cap, path.select sizes the CSR from the counts: a
+    short first guess is followed by one call at the largest count, and the
+    CSR equals the one made with the never-truncating nb * nb."""
+    cfg = SMALL[idx]
+    print(f"case {cfg.name}", flush=True)
+    x = make_inputs(cfg, device="cuda")
+    path = _path(cfg)
+    path.shapes(x["v"], x["a"])
+    qp, kp = path.permute(x["q"]), path.permute(x["k"])
+    full = path.select(qp, kp, cap=path.nb * path.nb)
+    path._cap_seen = 1                       # a guess of one entry per head: always short here
+    sized = path.select(qp, kp)
+    torch.cuda.synchronize()
+    need = int(full.total.max())
+    assert need > 1
+    assert sized.cap == need
+    assert torch.equal(full.offsets, sized.offsets)
+    assert torch.equal(full.total, sized.total)
+    for h in range(cfg.heads):
+        t = int(full.total[h])
+        assert torch.equal(full.idx[h, :t], sized.idx[h, :t])
+
+
 @pytest.mark.parametrize("idx", [1, 2], ids=lambda i: SMALL[i].name)
 def test_vector_alu_attention_in_bf16(idx, monkeypatch):
     """PRISM_ATTN_SIMT=1 runs the bf16 attention on the vector-ALU kernels; they
