@@ -78,7 +78,33 @@ def parse():
     ap.add_argument("--flat-ratio", type=float, default=0.5,
                     help="flat ratio of the routed-forward measurement (next row f3)")
     ap.add_argument("--profile", metavar="DIR", help="run the rocprofv3 passes and write summaries into DIR")
+    ap.add_argument("--calibrate", action="store_true",
+                    help="only run the two counter calibration kernels once (the profile passes use this)")
     return ap.parse_args()
+
+
+def calibrate(cfg):
+    """The two kernels the HBM counters are calibrated on, one launch each, on
+    one tensor of the workload's size ([N, heads, d]): the permutation of a
+    raster tensor into block-major order (streaming reads and writes) and a
+    torch gather of its 64-row tiles in random order (16 KB runs, as the
+    attention kernels load them).  Each reads and writes the tensor once."""
+    from dynamic_block_sparse_amd.path import PrismPath
+    from workloads.synth import make_inputs
+    x = make_inputs(cfg, device="cuda", tensors=("v",))
+    path = PrismPath(cfg.T, cfg.H, cfg.W, cfg.heads, cfg.d, cfg.top_k, cfg.top_p, 1.0)
+    path.shapes(x["v"], x["a"])
+    t = path.block_major_like(x["v"])
+    torch.cuda.synchronize()
+    path.permute(x["v"], out=t)
+    tiles = x["v"].reshape(-1, 64 * cfg.d)              # [N * heads / 64, 64 rows of one head]
+    idx = torch.randperm(tiles.shape[0], device="cuda")
+    torch.cuda.synchronize()
+    g = torch.index_select(tiles, 0, idx)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration_bytes_each_way": int(x["v"].numel() * x["v"].element_size()),
+                      "gather_rows": int(g.shape[0]), "gather_row_bytes": int(g.shape[1] * g.element_size())}),
+          flush=True)
 
 
 def source_hash():
@@ -245,6 +271,31 @@ def profile(args):
         fh.write(f"prism_sparse_attn_bwd call (its kernels' average durations x launches): {bwd_ns / 1e6:.3f} ms\n")
         if bench_line:
             fh.write(f"bench stage_ms of the same run (HIP events): {json.dumps(bench_line.get('stage_ms'))}\n")
+    # calibration: both counters over the two calibration kernels (one launch
+    # each, a process of their own)
+    import workloads.synth as synth
+    cfg = synth.CONFIGS[args.config]
+    es = 2 if cfg.dtype == "bf16" else 4
+    copy_bytes = cfg.N * cfg.heads * cfg.d * es   # each calibration kernel reads and writes one whole tensor
+    cal_regex = "permute_heads|gather|index_select"
+    cal = {}
+    cal_cmds = {}
+    for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
+        d = os.path.join(raw, "cal_" + ctr.lower())
+        cmd = ["rocprofv3", "--pmc", ctr, "--kernel-include-regex", cal_regex, "--output-format", "csv", "-d", d,
+               "-o", "cal", "--", sys.executable, "-u", os.path.abspath(__file__), "--config", args.config,
+               "--calibrate"]
+        cal_cmds[ctr] = (f"rocprofv3 --pmc {ctr} --kernel-include-regex '{cal_regex}' --output-format csv -d {rel(d)} "
+                         f"-o cal -- python bench.py --config {args.config} --calibrate")
+        _run(cmd, d + ".log", 300)
+        rows_ = _counter_rows(d)
+        ip = [i for i, ((_, k), _) in enumerate(rows_) if "permute_heads" in k]
+        # the calibration gather: every gather launch after the permutation
+        # (torch may split it; the input generation's own gathers come before)
+        gath = [v for (_, k), v in rows_[ip[-1] + 1:] if "gather" in k or "index_select" in k] if ip else []
+        if not ip or not gath:
+            sys.exit("[profile] the calibration run did not record both calibration kernels")
+        cal[ctr] = {"permute": copy_bytes / (1024.0 * rows_[ip[-1]][1]), "gather": copy_bytes / (1024.0 * sum(gath))}
     # counters: one pass each
     res = {}
     pcmds = {}
@@ -254,42 +305,62 @@ def profile(args):
                              "-d", d, "-o", ctr.lower()], 1, 0)
         pcmds[ctr] = show.replace(d, rel(d)).replace(PMC_REGEX, "'" + PMC_REGEX + "'")
         _run(cmd, d + ".log", 300)
-        res[ctr] = _counter_rows(d)
-    import workloads.synth as synth
-    cfg = synth.CONFIGS[args.config]
-    es = 2 if cfg.dtype == "bf16" else 4
-    copy_bytes = cfg.N * cfg.heads * cfg.d * es   # one permute launch reads and writes one whole tensor
-    scale = {}
-    for ctr, rows_ in res.items():
-        vals = [v for (_, k), v in rows_ if "permute_heads" in k]
-        if not vals:
-            sys.exit("[profile] no permutation kernel in the counter pass: nothing to calibrate against")
-        scale[ctr] = copy_bytes / (1024.0 * (sum(vals) / len(vals)))
-    # the backward call: the dispatches from attn_bwd_dot through attn_dkdv
-    per_call = {}
+        rows_ = _counter_rows(d)
+        # the timed step's dispatches: from its zone statistics on (the set-up
+        # before it also computes the shapes and a sizing selection)
+        first = max(i for i, ((_, k), _) in enumerate(rows_) if "zone_profile" in k)
+        res[ctr] = rows_[first:]
+    # the scale of each counter: algorithmic / counted bytes on the permutation
+    # kernel; the gather's factor is recorded beside it as a check
+    scale = {ctr: cal[ctr]["permute"] for ctr in cal}
+
+    def call_range(seq, first, last, after=None):
+        """dispatches of one call: from the last `first` kernel (or, with
+        `after`, the one following the last `after` kernel before it) through
+        the last `last` kernel"""
+        end = max(i for i, (k, _) in enumerate(seq) if last in k)
+        if after is None:
+            start = max(i for i, (k, _) in enumerate(seq[:end + 1]) if first in k)
+        else:
+            start = max(i for i, (k, _) in enumerate(seq[:end + 1]) if after in k) + 1
+        return seq[start:end + 1]
+
+    calls = {"bwd": {}, "fwd": {}}
     for ctr, rows_ in res.items():
         seq = [(k, v) for (_, k), v in rows_]
-        start = max(i for i, (k, _) in enumerate(seq) if "attn_bwd_dot" in k)
-        end = max(i for i, (k, _) in enumerate(seq) if "attn_dkdv" in k)
-        per_call[ctr] = [(_short(k), v) for k, v in seq[start:end + 1]]
-    fetch = sum(v for _, v in per_call["FETCH_SIZE"]) * 1024 * scale["FETCH_SIZE"]
-    write = sum(v for _, v in per_call["WRITE_SIZE"]) * 1024 * scale["WRITE_SIZE"]
-    with open(os.path.join(out, f"attn_bwd_{args.config}_traffic.txt"), "w") as fh:
-        fh.write(f"# HBM-side traffic of one prism_sparse_attn_bwd call, {args.config} workload, from rocprofv3 counters\n")
-        for ctr, show in pcmds.items():
-            fh.write(f"# {ctr} pass: {show}\n")
-        fh.write(f"# made by: python bench.py --profile {out} --config {args.config}\n")
-        fh.write(f"# calibration: a permute launch (prism_block_permute_heads) moves {copy_bytes} bytes each way;\n"
-                 f"# the counters (KiB per dispatch) are scaled by algorithmic/counted on that copy kernel\n\n")
-        for ctr in res:
-            fh.write(f"scale_{ctr.lower()}: {scale[ctr]:.4f}\n")
-        for ctr, items in per_call.items():
-            for k, v in items:
-                fh.write(f"  {ctr} {k}: {v:.0f} KiB\n")
-        fh.write(f"fetch_bytes_per_call: {fetch:.6g}\n")
-        fh.write(f"write_bytes_per_call: {write:.6g}\n")
-        fh.write(f"bytes_per_call: {fetch + write:.6g}\n")
-        fh.write(f"source_sha256: {source_hash()}\n")
+        calls["bwd"][ctr] = [(_short(k), v) for k, v in call_range(seq, "attn_bwd_dot", "attn_dkdv")]
+        # the forward call: everything after the selection's last CSR write up
+        # to the forward's last attention kernel
+        fwd_last = "attn_fwd_combine" if any("attn_fwd_combine" in k for k, _ in seq) else "attn_fwd_mfma"
+        calls["fwd"][ctr] = [(_short(k), v) for k, v in call_range(seq, None, fwd_last, after="select_write")]
+    fetch = write = 0.0
+    for which, per_call in calls.items():
+        f_b = sum(v for _, v in per_call["FETCH_SIZE"]) * 1024 * scale["FETCH_SIZE"]
+        w_b = sum(v for _, v in per_call["WRITE_SIZE"]) * 1024 * scale["WRITE_SIZE"]
+        if which == "bwd":
+            fetch, write = f_b, w_b
+        api = "prism_sparse_attn_bwd" if which == "bwd" else "prism_sparse_attn_fwd"
+        with open(os.path.join(out, f"attn_{which}_{args.config}_traffic.txt"), "w") as fh:
+            fh.write(f"# HBM-side traffic of one {api} call, {args.config} workload, from rocprofv3 counters\n")
+            for ctr, show in pcmds.items():
+                fh.write(f"# {ctr} pass: {show}\n")
+            for ctr, show in cal_cmds.items():
+                fh.write(f"# {ctr} calibration pass: {show}\n")
+            fh.write(f"# made by: python bench.py --profile {out} --config {args.config}\n")
+            fh.write(f"# calibration: each calibration kernel reads and writes {copy_bytes} bytes (one tensor); the\n"
+                     f"# counters (KiB per dispatch) are scaled by algorithmic/counted on the permutation kernel\n"
+                     f"# (streaming); a gather of the tensor's 16 KB tiles in random order, the attention kernels'\n"
+                     f"# access pattern, gives the check factor beside it\n\n")
+            for ctr in cal:
+                fh.write(f"scale_{ctr.lower()}: {scale[ctr]:.4f}\n")
+                fh.write(f"check_scale_{ctr.lower()}_gather: {cal[ctr]['gather']:.4f}\n")
+            for ctr, items in per_call.items():
+                for k, v in items:
+                    fh.write(f"  {ctr} {k}: {v:.0f} KiB\n")
+            fh.write(f"fetch_bytes_per_call: {f_b:.6g}\n")
+            fh.write(f"write_bytes_per_call: {w_b:.6g}\n")
+            fh.write(f"bytes_per_call: {f_b + w_b:.6g}\n")
+            fh.write(f"source_sha256: {source_hash()}\n")
     # the bandwidth-bound stages from the same two passes: bytes per dispatch,
     # counted (scaled as above) against algorithmic
     nb_run = int(bench_line.get("config", {}).get("blocks", 0)) if bench_line else 0
@@ -297,7 +368,7 @@ def profile(args):
     stage_alg = {"zone_profile": ("zone statistics: read V, the a map", cfg.N * C * es + 4 * cfg.N),
                  "permute_heads": ("permutation of one tensor: read + write", 2 * cfg.N * C * es),
                  "pool_kernel": ("block means: read Q and K", 2 * cfg.N * C * es),
-                 "logits_kernel": ("scores: write fp32 [heads, NB, NB]", cfg.heads * nb_run * nb_run * 4),
+                 "logits_kernel": ("scores: write fp32 [NB, NB] per head", cfg.heads * nb_run * nb_run * 4),
                  "select_reg": ("selection: read the scores", cfg.heads * nb_run * nb_run * 4),
                  "select_write": ("CSR write: read the scores", cfg.heads * nb_run * nb_run * 4)}
     with open(os.path.join(out, f"stages_{args.config}_traffic.txt"), "w") as fh:
@@ -307,6 +378,8 @@ def profile(args):
             fh.write(f"# {ctr} pass: {show}\n")
         fh.write(f"# made by: python bench.py --profile {out} --config {args.config}\n")
         fh.write("# bytes per dispatch: the counters (KiB) scaled as in the attention traffic summary\n\n")
+        fh.write("# per call of the stage: the kernel's dispatches of one step summed (the permutation: per tensor;\n"
+                 "# the scores and the selection run one launch per head group)\n\n")
         fh.write(f"{'kernel':28s} {'dispatches':>10s} {'fetch_GB':>10s} {'write_GB':>10s} {'algorithmic_GB':>15s} "
                  f"{'counted/alg':>12s}  work\n")
         for key, (what, alg_b) in stage_alg.items():
@@ -314,8 +387,9 @@ def profile(args):
             w_v = [v for (_, k), v in res["WRITE_SIZE"] if key in k]
             if not f_v or not w_v:
                 continue
-            fb = sum(f_v) / len(f_v) * 1024 * scale["FETCH_SIZE"]
-            wb = sum(w_v) / len(w_v) * 1024 * scale["WRITE_SIZE"]
+            per = len(f_v) if key == "permute_heads" else 1   # the permutation: the average launch (one tensor)
+            fb = sum(f_v) / per * 1024 * scale["FETCH_SIZE"]
+            wb = sum(w_v) / per * 1024 * scale["WRITE_SIZE"]
             ratio = (fb + wb) / alg_b if alg_b else float("nan")
             fh.write(f"{key:28s} {len(f_v):10d} {fb / 1e9:10.3f} {wb / 1e9:10.3f} {alg_b / 1e9:15.3f} {ratio:12.3f}  "
                      f"{what}\n")
@@ -571,6 +645,9 @@ def main():
     from dynamic_block_sparse_amd.path import PrismPath
 
     cfg = CONFIGS[args.config]
+    if args.calibrate:
+        calibrate(cfg)
+        return
     print(f"[bench] generating {cfg.name} inputs", file=sys.stderr, flush=True)
     x = make_inputs(cfg, device="cuda")
     torch.cuda.synchronize()
