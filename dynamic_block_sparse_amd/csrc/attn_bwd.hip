@@ -398,14 +398,9 @@ attn_dkdv_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
             for (int g = 0; g < 4; ++g) pex[64 * g] = float4{x[4 * g], x[4 * g + 1], x[4 * g + 2], x[4 * g + 3]};
         };
         auto accumulate = [&](const f32x16_t& x, int mr) {   // acc += tb^T x over the half's 32 rows
+            const u32x4_t bx[2] = {pack_kstep(x, 0), pack_kstep(x, 1)};
             __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-            for (int k2 = 0; k2 < 2; ++k2) {
-                const u32x4_t bx = pack_kstep(x, k2);
-#pragma unroll
-                for (int m = 0; m < DM; ++m)
-                    acc[m] = mfma32(tr_operand<D>(tb, 32 * mr + 16 * k2, 32 * m, lane), bx, acc[m]);
-            }
+            tr_accumulate<D, 2>(tb, 32 * mr, bx, acc, lane);
             __builtin_amdgcn_s_setprio(0);
         };
         if (role == 0) {

@@ -174,6 +174,28 @@ __device__ __forceinline__ u32x4_t tr_operand(const uint16_t* tile, int base, in
     return u32x4_t{a.x, a.y, b.x, b.y};
 }
 
+// acc[m] += tile^T(rows row0 + 16 ks .. +15, columns 32 m .. +31) b[ks] for
+// ks < KST and m < D / 32, in (ks, m) order: the DM accumulators are
+// independent chains, and the transposed operands are read AHEAD products
+// ahead of their MFMA (a schedule barrier keeps that order, as in
+// rows_x_ksteps; 4 VGPRs per product read ahead).
+template <int D, int KST, int AHEAD = 4>
+__device__ __forceinline__ void tr_accumulate(const uint16_t* tile, int row0, const u32x4_t (&b)[KST],
+                                              f32x16_t (&acc)[D / 32], int lane) {
+    constexpr int DM = D / 32, N = KST * DM, kAhead = AHEAD;
+    u32x4_t a[kAhead];
+#pragma unroll
+    for (int i = 0; i < kAhead && i < N; ++i) a[i] = tr_operand<D>(tile, row0 + 16 * (i / DM), 32 * (i % DM), lane);
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        u32x4_t nx;
+        if (i + kAhead < N) nx = tr_operand<D>(tile, row0 + 16 * ((i + kAhead) / DM), 32 * ((i + kAhead) % DM), lane);
+        acc[i % DM] = mfma32(a[i % kAhead], b[i / DM], acc[i % DM]);
+        if (i + kAhead < N) a[i % kAhead] = nx;
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
 // Per-lane byte offsets for loading a 64-row tile (token stride ld elements)
 // into a swizzled LDS tile, shared by the NW waves of the workgroup: wave w
 // issues instructions w, w + NW, ...; one instruction fills 1 KB of LDS

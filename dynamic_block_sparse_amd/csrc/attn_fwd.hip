@@ -135,11 +135,7 @@ __device__ __forceinline__ void fwd_pass(const uint16_t* __restrict__ q, const u
             for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
                 for (int w = 0; w < 4; ++w) lrnd = sum_bf16_pair(pb[ks][w], lrnd);
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-                for (int m = 0; m < DM; ++m)
-                    st.oacc[m] = mfma32(tr_operand<D>(vt, 16 * ks, 32 * m, lane), pb[ks], st.oacc[m]);
+            tr_accumulate<D, 4>(vt, 0, pb, st.oacc, lane);
             dma_join();                    // K(tn) landed; every wave is done with V(t)
             if (tn < 0) break;
             dma.load(vbuf, vh_ + static_cast<int64_t>(tn) * ld, wave);
