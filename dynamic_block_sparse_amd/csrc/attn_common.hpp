@@ -34,8 +34,6 @@
 // lane fetching the global chunk its LDS slot holds, so that the loads overlap
 // the compute of this or another resident workgroup.
 #pragma once
-#include <type_traits>
-
 #include "prism_device.hpp"
 #include "prism_internal.hpp"
 
@@ -265,11 +263,9 @@ struct TileCursor {
 };
 
 // Double-buffered walk over the tiles of `cur`: tile t+1 is loaded into
-// buffer b^1 while tile t, in buffer b, is used.  The loop is unrolled over the
-// two buffers and passes b as a std::integral_constant, so that the callee's
-// LDS addresses are compile-time offsets.  (The dK/dV kernel; the forward and
-// dQ kernels keep one tile of each operand and a second resident workgroup per
-// SIMD instead, loading by phase.)
+// buffer b^1 while tile t, in buffer b, is used.  (The dK/dV kernel; the
+// forward and dQ kernels keep one tile of each operand and a second resident
+// workgroup per SIMD instead, loading by phase.)
 template <class Issue, class Compute>
 __device__ __forceinline__ void tile_pipeline(TileCursor& cur, Issue&& issue, Compute&& compute) {
     int t = cur.next();
