@@ -3,6 +3,8 @@
 // Built with MFMA accumulators in ordinary VGPRs (see build.py): the kernel
 // fits in 256 VGPRs that way and was measured faster than with accumulator
 // registers.
+#include <cstdlib>
+
 #include "attn_common.hpp"
 #include "attn_split.hpp"
 
@@ -55,7 +57,7 @@ struct FwdState {
 
 // One pass of the workgroup's query tile (rows p0 .. p0+63 of head h) over the
 // key tiles of selected entries e0 .. e1-1 of `si`.
-template <int D>
+template <int D, int NW = 2>
 __device__ __forceinline__ void fwd_pass(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kh_,
                                          const uint16_t* __restrict__ vh_, int64_t ld, int64_t hs, int h, int64_t p0,
                                          const int32_t* __restrict__ offs, const int32_t* __restrict__ si, int e0,
@@ -79,9 +81,9 @@ __device__ __forceinline__ void fwd_pass(const uint16_t* __restrict__ q, const u
         for (int x = 0; x < 16; ++x) st.oacc[m][x] = 0.0f;
     float mrow = -INFINITY, lrow = 0.0f, lrnd = 0.0f;
 
-    TileDma<D, 2> dma;
+    TileDma<D, NW> dma;
     dma.init(ld, wave, lane);
-    constexpr int PER = TileDma<D, 2>::PER;
+    constexpr int PER = TileDma<D, NW>::PER;
     TileCursor cur;
     cur.init(si, offs, e0, e1);
     int t = cur.next();
@@ -174,13 +176,19 @@ __device__ __forceinline__ void fwd_store(const FwdState<D>& st, uint16_t* __res
     if (hl == 0) lse[static_cast<int64_t>(h) * N + row] = (st.mrow + __log2f(lt)) * kLn2;
 }
 
-template <int D>
-__global__ void __launch_bounds__(128, 2)
+// NW = 2: one 64-row tile per workgroup.  NW = 4: two sibling tiles (tiles
+// 2u and 2u + 1 of one block, which share the block's selected list) per
+// workgroup, waves 2 and 3 taking the second: every K and V tile is loaded
+// once for 128 rows, and each wave runs the same loop as with NW = 2.  With
+// `pairs` set the NW = 2 launch leaves the paired tiles to the NW = 4 one.
+template <int D, int NW>
+__global__ void __launch_bounds__(64 * NW, 2)
 attn_fwd_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
                      uint16_t* __restrict__ o, float* __restrict__ lse, int64_t N, int64_t ld, int64_t hs,
                      const int32_t* __restrict__ offs, int nb, const int32_t* __restrict__ sel_off,
                      const int32_t* __restrict__ sel_idx, int64_t cap, const int32_t* __restrict__ order,
-                     const uint8_t* __restrict__ skip, const RowMap om, float scale_log2, uint16_t* __restrict__ ores) {
+                     const uint8_t* __restrict__ skip, const RowMap om, float scale_log2, uint16_t* __restrict__ ores,
+                     int pairs) {
     __shared__ uint16_t kbuf[64 * D], vbuf[64 * D];
     const int ntiles = static_cast<int>(N / 64);
     const int wg = xcd_remap(blockIdx.x);
@@ -188,12 +196,16 @@ attn_fwd_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     const int64_t p0 = static_cast<int64_t>(tile_of(order, wg, ntiles)) * 64;
     const int i = find_block(offs, nb, p0);
     if (skip && skip[static_cast<int64_t>(h) * nb + i]) return;   // split into chunks, or routed to another path
+    const int nt = (offs[i + 1] - offs[i]) >> 6;
+    const int t = static_cast<int>((p0 - offs[i]) >> 6);
+    const bool paired = (t | 1) < nt;   // tile t has a sibling tile t ^ 1
+    if (NW == 4 ? (!paired || (t & 1)) : (pairs && paired)) return;
     const int32_t* __restrict__ so = sel_off + static_cast<int64_t>(h) * (nb + 1);
     const int e0 = so[i];
     const int e1 = static_cast<int>(min(static_cast<int64_t>(so[i + 1]), cap));
     FwdState<D> st;
-    fwd_pass<D>(q, k + h * hs, v + h * hs, ld, hs, h, p0, offs, sel_idx + static_cast<int64_t>(h) * cap, e0, e1, kbuf,
-                vbuf, scale_log2, st);
+    fwd_pass<D, NW>(q, k + h * hs, v + h * hs, ld, hs, h, p0, offs, sel_idx + static_cast<int64_t>(h) * cap, e0, e1,
+                    kbuf, vbuf, scale_log2, st);
     fwd_store<D>(st, o, ores, lse, om, N, h, p0);
 }
 
@@ -287,6 +299,12 @@ attn_fwd_combine_kernel(uint16_t* __restrict__ o, float* __restrict__ lse, uint1
 
 // ---------------------------------------------------------------- launchers
 
+// Sibling tiles in one workgroup: off by default (PRISM_FWD_PAIRS=1 turns it
+// on).  Measured at 2K: forward 58.3-58.9 ms with pairs against 57.3 ms
+// without, outputs bit-identical; the shared loads do not pay for the
+// four-wave barriers.
+constexpr int kFwdPairs = 0;
+
 hipError_t launch_attn_fwd_mfma(const void* q, const void* k, const void* v, void* o, float* lse, int64_t N, int heads,
                                 int d, int64_t ld, int64_t hs, const int32_t* offs, int nb, const int32_t* so,
                                 const int32_t* si, int64_t cap, const int32_t* order, const uint8_t* skip,
@@ -298,12 +316,22 @@ hipError_t launch_attn_fwd_mfma(const void* q, const void* k, const void* v, voi
     const uint16_t* V = static_cast<const uint16_t*>(v);
     uint16_t* O = static_cast<uint16_t*>(o);
     uint16_t* R = static_cast<uint16_t*>(ores);
+    const char* ev = std::getenv("PRISM_FWD_PAIRS");
+    const int pairs = ev ? (ev[0] == '1') : kFwdPairs;
     if (d == 128)
-        hipLaunchKernelGGL(attn_fwd_mfma_kernel<128>, grid, dim3(128), 0, s, Q, K, V, O, lse, N, ld, hs, offs, nb, so,
-                           si, cap, order, skip, om, sl2, R);
+        hipLaunchKernelGGL((attn_fwd_mfma_kernel<128, 2>), grid, dim3(128), 0, s, Q, K, V, O, lse, N, ld, hs, offs, nb,
+                           so, si, cap, order, skip, om, sl2, R, pairs);
     else
-        hipLaunchKernelGGL(attn_fwd_mfma_kernel<64>, grid, dim3(128), 0, s, Q, K, V, O, lse, N, ld, hs, offs, nb, so,
-                           si, cap, order, skip, om, sl2, R);
+        hipLaunchKernelGGL((attn_fwd_mfma_kernel<64, 2>), grid, dim3(128), 0, s, Q, K, V, O, lse, N, ld, hs, offs, nb,
+                           so, si, cap, order, skip, om, sl2, R, pairs);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || !pairs) return e;
+    if (d == 128)
+        hipLaunchKernelGGL((attn_fwd_mfma_kernel<128, 4>), grid, dim3(256), 0, s, Q, K, V, O, lse, N, ld, hs, offs, nb,
+                           so, si, cap, order, skip, om, sl2, R, pairs);
+    else
+        hipLaunchKernelGGL((attn_fwd_mfma_kernel<64, 4>), grid, dim3(256), 0, s, Q, K, V, O, lse, N, ld, hs, offs, nb,
+                           so, si, cap, order, skip, om, sl2, R, pairs);
     return hipGetLastError();
 }
 

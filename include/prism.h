@@ -44,6 +44,8 @@
  *     PRISM_ATTN_SIMT=1 makes the bf16 attention calls use the vector-ALU
  *     kernels instead of the MFMA ones; PRISM_SCORE_GROUP_BYTES=n sets the
  *     per-group budget of the selection's score matrices (default 256 MB);
+ *     PRISM_FWD_PAIRS=1 runs the two 64-row tiles of a 128- or 256-token
+ *     block in one forward workgroup over their shared list (bit-identical);
  *     PRISM_SPLIT_T, PRISM_SPLIT_W, PRISM_SPLIT_GROUP and PRISM_SPLIT_SLOTS
  *     set the key-range split of long selected lists (first threshold in key
  *     tiles, 0 = never split; range width in blocks; heads per launch group;

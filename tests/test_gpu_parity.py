@@ -217,6 +217,37 @@ def test_selection_kernels_agree(idx, monkeypatch):
         assert torch.equal(a.idx[h, :t], b.idx[h, :t])
 
 
+PAIRS_D64 = custom("s_pairs_d64", T=16, H=16, W=16, heads=2, d=64, dtype="bf16", top_k=3, top_p=0.9,
+                   kinds=(("static", 0.5), ("smooth", 0.5)), sigma={"static": 1e-3, "smooth": 0.3}, seed=21)
+
+
+@pytest.mark.parametrize("cfg", [SMALL[1], SMALL[7], PAIRS_D64], ids=lambda c: c.name)
+def test_forward_sibling_tiles_bit_identical(cfg, monkeypatch):
+    """The forward runs the two 64-row tiles of a 128- or 256-token block in
+    one workgroup over their shared selected list (PRISM_FWD_PAIRS=1) or one
+    tile per workgroup (0, the default); each row's arithmetic is the same,
+    so O, its residual and lse must be identical bit for bit."""
+    print(f"case {cfg.name}", flush=True)
+    x = make_inputs(cfg, device="cuda")
+    path = _path(cfg)
+    path.shapes(x["v"], x["a"])
+    sizes = np.diff(path.block_offsets.cpu().numpy())
+    assert (sizes >= 128).any(), "the grid needs blocks of more than one tile"
+    qp, kp, vp = path.permute(x["q"]), path.permute(x["k"]), path.permute(x["v"])
+    sel = path.select(qp, kp)
+    outs = {}
+    for flag in ("1", "0"):
+        monkeypatch.setenv("PRISM_FWD_PAIRS", flag)
+        ores = path.residual_like(path.block_major_like(qp)) if cfg.dtype == "bf16" else None
+        o, lse = path.forward(qp, kp, vp, sel, ores=ores)
+        torch.cuda.synchronize()
+        outs[flag] = (o.clone(), lse.clone(), None if ores is None else ores.clone())
+    assert torch.equal(outs["1"][0], outs["0"][0])
+    assert torch.equal(outs["1"][1], outs["0"][1])
+    if outs["1"][2] is not None:
+        assert torch.equal(outs["1"][2], outs["0"][2])
+
+
 @pytest.mark.parametrize("idx", [1, 2, 7], ids=lambda i: SMALL[i].name)
 def test_selection_by_head_groups(idx, monkeypatch):
     """prism_select scores the heads in groups that fit the score budget; a
