@@ -139,7 +139,9 @@ OrderWs carve_order(Carver& c, int64_t N, int64_t heads, int64_t nb) {
 // group with the same per-group buffers (tile order, split plan, partials).
 // Rows with more than T0 key tiles (or the lowest multiple 2^k T0 whose items
 // fit the slot capacity, `slots` per query tile of the group) are split into
-// key ranges of W blocks.  The environment may override the four for
+// key ranges of W blocks.  (At 2K one slot per tile runs as fast as two and
+// needs 7.6 GB of partials instead of 15.2; groups of 8 or 12 heads took 4-11 ms
+// more per step.)  The environment may override the four for
 // experiments (PRISM_SPLIT_W, PRISM_SPLIT_T: 0 turns the split off,
 // PRISM_SPLIT_GROUP, PRISM_SPLIT_SLOTS); the workspace size and the calls read
 // the same values.
@@ -154,7 +156,7 @@ int env_int(const char* name, int dflt, int lo, int hi) {
 }
 SplitParams split_params() {
     return SplitParams{env_int("PRISM_SPLIT_W", 128, 1, 1 << 15), env_int("PRISM_SPLIT_T", 256, 0, 1 << 20),
-                       env_int("PRISM_SPLIT_GROUP", 64, 1, 1 << 10), env_int("PRISM_SPLIT_SLOTS", 2, 1, 1 << 10)};
+                       env_int("PRISM_SPLIT_GROUP", 64, 1, 1 << 10), env_int("PRISM_SPLIT_SLOTS", 1, 1, 1 << 10)};
 }
 int64_t group_heads(int64_t heads, const SplitParams& sp) { return std::min<int64_t>(heads, sp.group); }
 // partial-slot capacity of one group, a multiple of 8
