@@ -79,6 +79,25 @@ __device__ __forceinline__ float sum_bf16_pair(uint32_t w, float acc) {
 // which is what the softmax wants for scores far below the row maximum
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// max(a, b, c) in one v_max3_f32 on the raw values.  fmaxf keeps IEEE NaN
+// semantics, so the compiler first canonicalises every MFMA result with a
+// v_max_f32 x, x of its own (two instructions per value instead of half of
+// one); the scores here are never NaN, and the maximum is the same.
+__device__ __forceinline__ float max3_raw(float a, float b, float c) {
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+
+// max of x and the x of lane ^ 32 (never NaN), through v_permlane32_swap (a register
+// exchange between the two 32-lane halves, no LDS round trip): with both
+// operands x, one result holds the lower half's values in both halves and the
+// other the upper half's
+__device__ __forceinline__ float max_across_halves(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return max3_raw(__uint_as_float(r[0]), __uint_as_float(r[1]), __uint_as_float(r[1]));
+}
+
 // B operand of k-step s2 built from C-tile registers 8*s2 .. 8*s2+7
 __device__ __forceinline__ u32x4_t pack_kstep(const f32x16_t& x, int s2) {
     return u32x4_t{pack2(x[8 * s2 + 0], x[8 * s2 + 1]), pack2(x[8 * s2 + 2], x[8 * s2 + 3]),

@@ -104,10 +104,15 @@ __device__ __forceinline__ void fwd_pass(const uint16_t* __restrict__ q, const u
             dma_join();                    // V(t) landed; every wave is done with K(t)
             const int tn = cur.next();
             if (tn >= 0) dma.load(kbuf, kh_ + static_cast<int64_t>(tn) * ld, wave);
-            float mx = -INFINITY;
+            // four independent chains of v_max3 over the 32 raw scores
+            float mq[4] = {s0[0], s0[1], s0[2], s0[3]};
 #pragma unroll
-            for (int x = 0; x < 16; ++x) mx = fmaxf(mx, fmaxf(s0[x], s1[x]));
-            mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * scale_log2;
+            for (int x = 0; x < 16; ++x) {
+                const int c = x & 3;
+                mq[c] = x < 4 ? max3_raw(mq[c], s1[x], s1[x]) : max3_raw(mq[c], s0[x], s1[x]);
+            }
+            float mx = max3_raw(max3_raw(mq[0], mq[1], mq[2]), mq[3], mq[3]);
+            mx = max_across_halves(mx) * scale_log2;
             if (__any(mx > mrow + 8.0f)) {
                 const float mnew = fmaxf(mrow, mx);
                 const float alpha = fast_exp2(mrow - mnew);
