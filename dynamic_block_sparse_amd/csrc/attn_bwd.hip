@@ -268,9 +268,9 @@ attn_dq_combine_kernel(uint16_t* __restrict__ dq, float* __restrict__ Dq, int64_
 // and the MFMA work is the same 16 d-step products per row half as with one
 // wave doing both.  The query tile is processed in two 32-row halves so that
 // the P exchange needs 4 KB per key half:
-//   A  role 0: S, P(0) -> LDS, P(1)            role 1: dP
+//   A  role 0: S, P(0) -> LDS                  role 1: dP
 //   -- barrier
-//   B  role 0: dV += P(0)                      role 1: dS(0), dK += dS(0)
+//   B  role 0: dV += P(0), P(1)                role 1: dS(0), dK += dS(0)
 //   -- barrier (role 1 has read P(0))
 //      role 0: P(1) -> LDS
 //   -- barrier
@@ -406,11 +406,11 @@ attn_dkdv_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
         if (role == 0) {
             softmax(x0, 0);
             publish(x0);
-            softmax(x1, 1);
         }
         __syncthreads();
         if (role) dsoft(x0);
         accumulate(x0, 0);
+        if (role == 0) softmax(x1, 1);   // under the dV products just issued
         __syncthreads();   // role 1 has read P of half 0
         if (role == 0) publish(x1);
         __syncthreads();
