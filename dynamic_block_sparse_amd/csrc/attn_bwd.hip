@@ -346,22 +346,27 @@ attn_dkdv_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
         if (wave == 0) dma4(lh + t, loff, lds_addr(lbuf[b]));
         else if (wave == 1) dma4(dh + t, loff, lds_addr(dbuf[b]));
     };
-    // The buffer index is a template constant, so LDS addresses are
-    // loop-invariant lane offsets plus immediates.
+    // b, the buffer of the current tile, alternates at run time (an unrolled
+    // pair of iterations with constant buffers does not fit the registers).
     auto compute = [&](int b) {
-        const uint16_t* rb = role ? obuf[b] : qbuf[b];   // row operand: Q for S, dO for dP
         const uint16_t* tb = role ? qbuf[b] : obuf[b];   // transposed operand: dO^T for dV, Q^T for dK
         const float* dt = dbuf[b];
         const float* l2 = l2buf[kh];
-        if (role == 0) l2buf[kh][lane] = lbuf[b][lane] * kLog2e;   // read back by this wave only
+        const float lraw = role == 0 ? lbuf[b][lane] : 0.0f;   // read now, used after the products
         // S (role 0) or D - dP (role 1) of both row halves: register x of half
         // mr holds query row 32*mr + 8*(x/4) + 4*hl + x%4 against key col of
         // the wave's half (two independent MFMA chains, LDS reads two steps
-        // ahead)
+        // ahead).  Each role has its own chain, so role 0's first products
+        // take the MFMA's zero operand instead of 32 register moves, and its
+        // lse read is consumed only after the products are issued.
         f32x16_t x0, x1;
         if (role == 0) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) x0[i] = x1[i] = 0.0f;
+            __builtin_amdgcn_s_setprio(1);
+            rows_x_ksteps<D>(qbuf[b], col, hl, kv, x0, x1);
+            __builtin_amdgcn_s_setprio(0);
+            l2buf[kh][lane] = lraw * kLog2e;   // read back by this wave only
         } else {
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
@@ -370,10 +375,10 @@ attn_dkdv_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
                 x0[4 * g] = d0.x, x0[4 * g + 1] = d0.y, x0[4 * g + 2] = d0.z, x0[4 * g + 3] = d0.w;
                 x1[4 * g] = d1.x, x1[4 * g + 1] = d1.y, x1[4 * g + 2] = d1.z, x1[4 * g + 3] = d1.w;
             }
+            __builtin_amdgcn_s_setprio(1);
+            rows_x_ksteps<D>(obuf[b], col, hl, kv, x0, x1);
+            __builtin_amdgcn_s_setprio(0);
         }
-        __builtin_amdgcn_s_setprio(1);
-        rows_x_ksteps<D>(rb, col, hl, kv, x0, x1);
-        __builtin_amdgcn_s_setprio(0);
         auto softmax = [&](f32x16_t& x, int mr) {   // S -> P (role 0)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
