@@ -219,7 +219,13 @@ def _counter_rows(root):
 
 
 def _short(name):
+    name = name.replace("(anonymous namespace)::", "")
     return re.sub(r"\(.*", "", name).replace("void ", "").replace("prism::", "")
+
+
+def _ours(name):
+    """A kernel of libprism (namespace prism), as opposed to torch's."""
+    return re.match(r"(void )?prism::", name) is not None
 
 
 def profile(args):
@@ -233,6 +239,9 @@ def profile(args):
     me = [sys.executable, "-u", os.path.abspath(__file__), "--config", args.config, "--no-cpu-baseline",
           "--no-next-rows"]
     rel = lambda p: os.path.relpath(p, ROOT)
+    # library switches in effect (the child processes inherit them)
+    env = " ".join(f"{k}={v}" for k, v in sorted(os.environ.items()) if k.startswith("PRISM_"))
+    made_by = (env + " " if env else "") + f"python bench.py --profile {out} --config {args.config}"
 
     def cmd_for(prof, steps, warmup):
         run = ["--steps", str(steps), "--warmup", str(warmup)]
@@ -253,12 +262,12 @@ def profile(args):
     with open(os.path.join(out, f"attn_{args.config}_kernel_stats.txt"), "w") as fh:
         fh.write(f"# rocprofv3 kernel statistics, {args.config} workload, 4 steps (1 warm-up)\n")
         fh.write("# command: " + tshow + "\n")
-        fh.write(f"# made by: python bench.py --profile {out} --config {args.config}\n\n")
+        fh.write(f"# made by: {made_by}\n\n")
         fh.write(f"{'kernel':62s} {'calls':>6s} {'avg_ms':>10s} {'total_ms':>10s} {'pct':>6s}\n")
         other = [0, 0.0, 0.0]
         for r in rows:
             name = _short(r["Name"])
-            if not name.strip() or name.startswith(("at::", "rocprim::", "__amd_rocclr")):
+            if not _ours(r["Name"]):
                 other[0] += int(r["Calls"])
                 other[1] += float(r["TotalDurationNs"])
                 other[2] += float(r["Percentage"])
@@ -346,7 +355,7 @@ def profile(args):
                 fh.write(f"# {ctr} pass: {show}\n")
             for ctr, show in cal_cmds.items():
                 fh.write(f"# {ctr} calibration pass: {show}\n")
-            fh.write(f"# made by: python bench.py --profile {out} --config {args.config}\n")
+            fh.write(f"# made by: {made_by}\n")
             fh.write(f"# calibration: each calibration kernel reads and writes {copy_bytes} bytes (one tensor); the\n"
                      f"# counters (KiB per dispatch) are scaled by algorithmic/counted on the permutation kernel\n"
                      f"# (streaming); a gather of the tensor's 16 KB tiles in random order, the attention kernels'\n"
@@ -376,7 +385,7 @@ def profile(args):
                  f"passes\n")
         for ctr, show in pcmds.items():
             fh.write(f"# {ctr} pass: {show}\n")
-        fh.write(f"# made by: python bench.py --profile {out} --config {args.config}\n")
+        fh.write(f"# made by: {made_by}\n")
         fh.write("# bytes per dispatch: the counters (KiB) scaled as in the attention traffic summary\n\n")
         fh.write("# per call of the stage: the kernel's dispatches of one step summed (the permutation: per tensor;\n"
                  "# the scores and the selection run one launch per head group)\n\n")
@@ -416,7 +425,7 @@ def profile(args):
         fh.write(f"# rocprofv3 counters of the attention kernels, {args.config} workload, one step\n")
         for g, show in shows.items():
             fh.write(f"# {g} pass: {show}\n")
-        fh.write(f"# made by: python bench.py --profile {out} --config {args.config}\n\n")
+        fh.write(f"# made by: {made_by}\n\n")
         kernels = sorted({k for k, _ in vals})
         for k in kernels:
             m = {c: sum(v.values()) / len(v) for (kk, c), v in vals.items() if kk == k}
