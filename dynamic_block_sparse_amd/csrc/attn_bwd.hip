@@ -285,18 +285,16 @@ attn_dq_combine_kernel(uint16_t* __restrict__ dq, float* __restrict__ Dq, int64_
 template <int D>
 __global__ void __launch_bounds__(256, 2)
 attn_dkdv_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-                      const uint16_t* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ Dq,
+                      const uint16_t* __restrict__ dout, const float* __restrict__ lse2, const float* __restrict__ Dq,
                       uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, int64_t N, int64_t ld, int64_t hs,
                       const int32_t* __restrict__ offs, int nb, const int32_t* __restrict__ tr_off,
                       const int32_t* __restrict__ tr_idx, int64_t cap, const float* __restrict__ dkbar,
                       const float* __restrict__ dvbar, const RowMap om, float scale_log2, float scale) {
-    // Q and dO tiles, lse (natural log) and D = rowsum(dO * O) of their rows
+    // Q and dO tiles, lse log2(e) and D = rowsum(dO * O) of their rows
     __shared__ uint16_t qbuf[2][64 * D], obuf[2][64 * D];
     __shared__ float lbuf[2][64], dbuf[2][64];
     // P of one 32-row half per key half: [key half][register group][lane][4]
     __shared__ float pbuf[2][4][64][4];
-    // each role-0 wave's copy of the tile's lse, times log2(e)
-    __shared__ float l2buf[2][64];
     const int ntiles = static_cast<int>(N / 64);
     const int wg = xcd_remap(blockIdx.x);
     const int h = wg / ntiles;
@@ -333,7 +331,7 @@ attn_dkdv_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
         for (int x = 0; x < 16; ++x) acc[m][x] = 0.0f;
     const uint16_t* __restrict__ qh_ = q + h * hs;
     const uint16_t* __restrict__ oh_ = dout + h * hs;
-    const float* __restrict__ lh = lse + static_cast<int64_t>(h) * N;
+    const float* __restrict__ lh = lse2 + static_cast<int64_t>(h) * N;
     const float* __restrict__ dh = Dq + static_cast<int64_t>(h) * N;
     float4* __restrict__ pex = reinterpret_cast<float4*>(&pbuf[kh][0][0][0]) + lane;
 
@@ -351,22 +349,24 @@ attn_dkdv_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
     auto compute = [&](int b) {
         const uint16_t* tb = role ? qbuf[b] : obuf[b];   // transposed operand: dO^T for dV, Q^T for dK
         const float* dt = dbuf[b];
-        const float* l2 = l2buf[kh];
-        const float lraw = role == 0 ? lbuf[b][lane] : 0.0f;   // read now, used after the products
+        const float* l2 = lbuf[b];
         // S (role 0) or D - dP (role 1) of both row halves: register x of half
         // mr holds query row 32*mr + 8*(x/4) + 4*hl + x%4 against key col of
         // the wave's half (two independent MFMA chains, LDS reads two steps
         // ahead).  Each role has its own chain, so role 0's first products
-        // take the MFMA's zero operand instead of 32 register moves, and its
-        // lse read is consumed only after the products are issued.
+        // take the MFMA's zero operand instead of 32 register moves.
         f32x16_t x0, x1;
+        float4 lreg[2][4];   // role 0: the rows' lse log2(e), read before the products
         if (role == 0) {
+#pragma unroll
+            for (int mr = 0; mr < 2; ++mr)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) lreg[mr][g] = *reinterpret_cast<const float4*>(&l2[32 * mr + 8 * g + 4 * hl]);
 #pragma unroll
             for (int i = 0; i < 16; ++i) x0[i] = x1[i] = 0.0f;
             __builtin_amdgcn_s_setprio(1);
             rows_x_ksteps<D>(qbuf[b], col, hl, kv, x0, x1);
             __builtin_amdgcn_s_setprio(0);
-            l2buf[kh][lane] = lraw * kLog2e;   // read back by this wave only
         } else {
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
@@ -382,7 +382,7 @@ attn_dkdv_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
         auto softmax = [&](f32x16_t& x, int mr) {   // S -> P (role 0)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const float4 l4 = *reinterpret_cast<const float4*>(&l2[32 * mr + 8 * g + 4 * hl]);
+                const float4 l4 = lreg[mr][g];
                 const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
 #pragma unroll
                 for (int r = 0; r < 4; ++r) x[4 * g + r] = fast_exp2(fmaf(x[4 * g + r], scale_log2, -lv[r]));
@@ -497,7 +497,7 @@ hipError_t launch_attn_dq_split(const void* q, const void* k, const void* v, con
     return hipGetLastError();
 }
 
-hipError_t launch_attn_dkdv_mfma(const void* q, const void* k, const void* v, const void* dout, const float* lse,
+hipError_t launch_attn_dkdv_mfma(const void* q, const void* k, const void* v, const void* dout, const float* lse2,
                                  const float* Dq, void* dk, void* dv, int64_t N, int heads, int d, int64_t ld,
                                  int64_t hs, const int32_t* offs, int nb, const int32_t* to, const int32_t* ti,
                                  int64_t cap, const RouteGrad* rg, const RowMap& om, float scale, hipStream_t s) {
@@ -512,10 +512,10 @@ hipError_t launch_attn_dkdv_mfma(const void* q, const void* k, const void* v, co
     uint16_t* dK = static_cast<uint16_t*>(dk);
     uint16_t* dV = static_cast<uint16_t*>(dv);
     if (d == 128)
-        hipLaunchKernelGGL(attn_dkdv_mfma_kernel<128>, grid, dim3(256), 0, s, Q, K, V, O, lse, Dq, dK, dV, N, ld, hs,
+        hipLaunchKernelGGL(attn_dkdv_mfma_kernel<128>, grid, dim3(256), 0, s, Q, K, V, O, lse2, Dq, dK, dV, N, ld, hs,
                            offs, nb, to, ti, cap, dkb, dvb, om, sl2, scale);
     else
-        hipLaunchKernelGGL(attn_dkdv_mfma_kernel<64>, grid, dim3(256), 0, s, Q, K, V, O, lse, Dq, dK, dV, N, ld, hs,
+        hipLaunchKernelGGL(attn_dkdv_mfma_kernel<64>, grid, dim3(256), 0, s, Q, K, V, O, lse2, Dq, dK, dV, N, ld, hs,
                            offs, nb, to, ti, cap, dkb, dvb, om, sl2, scale);
     return hipGetLastError();
 }

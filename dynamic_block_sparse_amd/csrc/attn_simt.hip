@@ -112,12 +112,15 @@ attn_fwd_simt_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* 
     lse[static_cast<int64_t>(h) * N + p] = m + __logf(l);
 }
 
-// Dq[h][p] = sum_c dO[p,h,c] * O[p,h,c].  LPR lanes share a row, each with 16
-// bytes of O and of dO (EPV elements); a workgroup covers 64 rows of one head.
+// Dq[h][p] = sum_c dO[p,h,c] * O[p,h,c], and lse2[h][p] = lse[h][p] log2(e) (the
+// base-2 form that the dK/dV kernel loads per tile).  LPR lanes share a row,
+// each with 16 bytes of O and of dO (EPV elements); a workgroup covers 64 rows
+// of one head.
 template <typename T, int D>
 __global__ void __launch_bounds__(256)
 attn_bwd_dot_kernel(const T* __restrict__ o, const T* __restrict__ dout, int64_t N, int heads, int64_t ld, int64_t hs,
-                    const RowMap om, float* __restrict__ Dq, const T* __restrict__ ores) {
+                    const RowMap om, float* __restrict__ Dq, const T* __restrict__ ores, const float* __restrict__ lse,
+                    float* __restrict__ lse2) {
     constexpr int EPV = 16 / static_cast<int>(sizeof(T));
     constexpr int LPR = D / EPV;            // lanes per row (power of two, <= 64)
     constexpr int RPI = 256 / LPR;          // rows per workgroup step
@@ -151,7 +154,10 @@ attn_bwd_dot_kernel(const T* __restrict__ o, const T* __restrict__ dout, int64_t
         }
 #pragma unroll
         for (int off = LPR / 2; off >= 1; off >>= 1) s += __shfl_xor(s, off, kWave);
-        if (p < N && sub == 0) Dq[static_cast<int64_t>(h) * N + p] = s;
+        if (p < N && sub == 0) {
+            Dq[static_cast<int64_t>(h) * N + p] = s;
+            if (lse2) lse2[static_cast<int64_t>(h) * N + p] = lse[static_cast<int64_t>(h) * N + p] * kLog2e;
+        }
     }
 }
 
@@ -312,20 +318,22 @@ hipError_t launch_attn_fwd_simt(const void* q, const void* k, const void* v, voi
 
 template <typename T, int D>
 static hipError_t dot_launch(const void* o, const void* dout, int64_t N, int heads, int64_t ld, int64_t hs,
-                             const RowMap& om, float* Dq, const void* ores, hipStream_t s) {
+                             const RowMap& om, float* Dq, const void* ores, const float* lse, float* lse2,
+                             hipStream_t s) {
     hipLaunchKernelGGL((attn_bwd_dot_kernel<T, D>), dim3(static_cast<unsigned>((N + 63) / 64), heads), dim3(256), 0, s,
                        static_cast<const T*>(o), static_cast<const T*>(dout), N, heads, ld, hs, om, Dq,
-                       static_cast<const T*>(ores));
+                       static_cast<const T*>(ores), lse, lse2);
     return hipGetLastError();
 }
 
 hipError_t launch_bwd_dot(const void* o, const void* dout, bool bf16, int64_t N, int heads, int d, int64_t ld,
-                          int64_t hs, const RowMap& om, float* Dq, const void* ores, hipStream_t s) {
+                          int64_t hs, const RowMap& om, float* Dq, const void* ores, const float* lse, float* lse2,
+                          hipStream_t s) {
     if (bf16)
-        return d == 128 ? dot_launch<uint16_t, 128>(o, dout, N, heads, ld, hs, om, Dq, ores, s)
-                        : dot_launch<uint16_t, 64>(o, dout, N, heads, ld, hs, om, Dq, ores, s);
-    return d == 128 ? dot_launch<float, 128>(o, dout, N, heads, ld, hs, om, Dq, nullptr, s)
-                    : dot_launch<float, 64>(o, dout, N, heads, ld, hs, om, Dq, nullptr, s);
+        return d == 128 ? dot_launch<uint16_t, 128>(o, dout, N, heads, ld, hs, om, Dq, ores, lse, lse2, s)
+                        : dot_launch<uint16_t, 64>(o, dout, N, heads, ld, hs, om, Dq, ores, lse, lse2, s);
+    return d == 128 ? dot_launch<float, 128>(o, dout, N, heads, ld, hs, om, Dq, nullptr, lse, lse2, s)
+                    : dot_launch<float, 64>(o, dout, N, heads, ld, hs, om, Dq, nullptr, lse, lse2, s);
 }
 
 template <typename T, int D>

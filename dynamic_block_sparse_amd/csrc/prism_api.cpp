@@ -97,6 +97,7 @@ SubSelectWs carve_select_sub(Carver& c, int64_t N, int64_t heads, int64_t d, int
 
 struct BwdWs {
     float* Dq;
+    float* lse2;       // lse * log2(e), for dK/dV
     int32_t* tcount;
     int32_t* tr_offsets;
     int32_t* tr_idx;
@@ -109,6 +110,7 @@ struct BwdWs {
 BwdWs carve_bwd(Carver& c, int64_t N, int64_t heads, int64_t hg, int64_t nb, int64_t cap) {
     BwdWs w;
     w.Dq = c.take<float>(heads * N);
+    w.lse2 = c.take<float>(heads * N);
     w.tcount = c.take<int32_t>(heads * nb);
     w.tr_offsets = c.take<int32_t>(heads * (nb + 1));
     w.tr_idx = c.take<int32_t>(heads * cap);
@@ -893,7 +895,7 @@ prism_status exact_bwd(const void* q, const void* k, const void* v, const void* 
             if (st != PRISM_OK) return st;
         }
     }
-    return hip_status(prism::launch_attn_dkdv_mfma(q, k, v, dout, lse, w.Dq, dk, dv, N, heads, d, ld, hs,
+    return hip_status(prism::launch_attn_dkdv_mfma(q, k, v, dout, w.lse2, w.Dq, dk, dv, N, heads, d, ld, hs,
                                                    block_offsets, nb, w.tr_offsets, w.tr_idx, cap, rg, om, scale,
                                                    stream),
                       "dK/dV launch");
@@ -918,7 +920,8 @@ prism_status prism_sparse_attn_bwd(const void* q, const void* k, const void* v, 
         return fail(PRISM_E_WORKSPACE, "backward needs %zu workspace bytes, got %zu", need, ws ? ws_bytes : 0);
     Carver c(ws);
     BwdWs w = carve_bwd(c, N, heads, group_heads(heads, split_params()), nb, cap);
-    st = hip_status(prism::launch_bwd_dot(o, dout, dt == PRISM_BF16, N, heads, d, ld, hs, om, w.Dq, o_res, stream),
+    st = hip_status(prism::launch_bwd_dot(o, dout, dt == PRISM_BF16, N, heads, d, ld, hs, om, w.Dq, o_res, lse, w.lse2,
+                                          stream),
                     "backward dot launch");
     if (st != PRISM_OK) return st;
     st = hip_status(prism::launch_transpose_csr(sel_offsets, sel_idx, nb, heads, cap, w.tcount, w.tr_offsets, w.tr_idx,
@@ -949,7 +952,7 @@ prism_status prism_routed_attn_bwd(const void* q, const void* k, const void* v, 
     const bool bf16 = dt == PRISM_BF16;
     prism::RowMap om;
     row_map(nullptr, dt, N, ld, hs, om);
-    st = hip_status(prism::launch_bwd_dot(o, dout, bf16, N, heads, d, ld, hs, om, w.Dq, o_res, stream),
+    st = hip_status(prism::launch_bwd_dot(o, dout, bf16, N, heads, d, ld, hs, om, w.Dq, o_res, lse, w.lse2, stream),
                     "backward dot launch");
     if (st != PRISM_OK) return st;
     // key block -> sharp query blocks (exact dK/dV) and -> flat query blocks (block-mean gradients)

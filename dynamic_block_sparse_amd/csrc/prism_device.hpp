@@ -10,6 +10,7 @@ namespace prism {
 constexpr int kWave = 64;
 constexpr int kZone = 8;
 constexpr int kZoneTokens = 512;
+constexpr float kLog2e = 1.4426950408889634f;   // log2(e), for exp(x) = exp2(x log2(e))
 
 // Candidate block shapes (b_T, b_H, b_W), 16 entries: every box with edges in
 // {2, 4, 8} and volume 64, 128 or 256, by volume then lexicographically.  The

@@ -75,8 +75,10 @@ hipError_t launch_attn_fwd_mfma(const void* q, const void* k, const void* v, voi
                                 const int32_t* si, int64_t cap, const int32_t* order, const uint8_t* skip,
                                 const RowMap& om, float scale, void* ores, hipStream_t s);
 
+// row dots D = rowsum(dO * O) into Dq and, when lse2 is set, lse * log2(e) into lse2
 hipError_t launch_bwd_dot(const void* o, const void* dout, bool bf16, int64_t N, int heads, int d, int64_t ld,
-                          int64_t hs, const RowMap& om, float* Dq, const void* ores, hipStream_t s);
+                          int64_t hs, const RowMap& om, float* Dq, const void* ores, const float* lse, float* lse2,
+                          hipStream_t s);
 
 // dQ of one group of heads (pointers at the group's first head): the tile
 // kernel over the tiles not marked in `skip`, then, for a split plan, its
@@ -91,7 +93,8 @@ hipError_t launch_attn_dq_split(const void* q, const void* k, const void* v, con
                                 float* Dq, void* dq, int64_t N, int heads, int d, int64_t ld, int64_t hs,
                                 const int32_t* offs, int nb, const int32_t* si, int64_t cap, const SplitView& sv,
                                 const RowMap& om, float scale, hipStream_t s);
-hipError_t launch_attn_dkdv_mfma(const void* q, const void* k, const void* v, const void* dout, const float* lse,
+// lse2: lse * log2(e) (launch_bwd_dot)
+hipError_t launch_attn_dkdv_mfma(const void* q, const void* k, const void* v, const void* dout, const float* lse2,
                                  const float* Dq, void* dk, void* dv, int64_t N, int heads, int d, int64_t ld,
                                  int64_t hs, const int32_t* offs, int nb, const int32_t* to, const int32_t* ti,
                                  int64_t cap, const RouteGrad* rg, const RowMap& om, float scale, hipStream_t s);

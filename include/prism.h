@@ -382,7 +382,8 @@ prism_status prism_sparse_attn_fwd(const void* q, const void* k, const void* v, 
  *   io             NULL or the raster placement of o, dq, dk and dv (checks as in
  *                  prism_sparse_attn_fwd)
  *   ws, ws_bytes   prism_workspace_size(PRISM_OP_ATTN_BWD, ...) bytes: row sums,
- *                  the transposed selection and the dQ tile visiting order
+ *                  lse in base 2, the transposed selection and the dQ tile
+ *                  visiting order
  * Deterministic: every output element is accumulated in a fixed order.
  */
 prism_status prism_sparse_attn_bwd(const void* q, const void* k, const void* v, const void* o,
