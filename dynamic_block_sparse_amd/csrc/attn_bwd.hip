@@ -35,10 +35,11 @@ namespace prism {
 // double-buffers its Q and dO tiles.
 //
 // dQ takes its query tiles in the visiting order built by launch_tile_order
-// (grouped by first selected key block).  dK/dV keeps raster order: grouping
-// its key tiles by the first query block that selects them was measured 1.6%
-// slower at 2K, where neighbouring key tiles already share most of their
-// query tiles in L2.
+// (grouped by first selected key block).  dK/dV keeps raster order inside a
+// head: grouping its key tiles by the first query block that selects them was
+// measured 1.6% slower at 2K, where neighbouring key tiles already share most
+// of their query tiles in L2.  Its heads are visited in a work-balanced order
+// (head_order_kernel, below).
 
 template <int D>
 struct DqState {
@@ -288,8 +289,9 @@ attn_dkdv_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
                       const uint16_t* __restrict__ dout, const float* __restrict__ lse2, const float* __restrict__ Dq,
                       uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, int64_t N, int64_t ld, int64_t hs,
                       const int32_t* __restrict__ offs, int nb, const int32_t* __restrict__ tr_off,
-                      const int32_t* __restrict__ tr_idx, int64_t cap, const float* __restrict__ dkbar,
-                      const float* __restrict__ dvbar, const RowMap om, float scale_log2, float scale) {
+                      const int32_t* __restrict__ tr_idx, int64_t cap, const int32_t* __restrict__ horder,
+                      const float* __restrict__ dkbar, const float* __restrict__ dvbar, const RowMap om,
+                      float scale_log2, float scale) {
     // Q and dO tiles, lse log2(e) and D = rowsum(dO * O) of their rows
     __shared__ uint16_t qbuf[2][64 * D], obuf[2][64 * D];
     __shared__ float lbuf[2][64], dbuf[2][64];
@@ -297,7 +299,7 @@ attn_dkdv_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
     __shared__ float pbuf[2][4][64][4];
     const int ntiles = static_cast<int>(N / 64);
     const int wg = xcd_remap(blockIdx.x);
-    const int h = wg / ntiles;
+    const int h = horder[wg / ntiles];   // head order of the launch (balanced across XCDs)
     const int64_t k0 = static_cast<int64_t>(wg % ntiles) * 64;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -446,7 +448,76 @@ attn_dkdv_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
         }
 }
 
+// ---------------------------------------------------------------- head order of the dK/dV launch
+//
+// Workgroups are dealt to the 8 XCDs in contiguous ranges of (head, key tile),
+// so with H heads an XCD runs H/8 whole heads.  A head's dK/dV work is its
+// count of (query tile, key tile) pairs, which Top-p makes uneven across heads
+// (diffuse heads select thousands of blocks per row; reading guide, xyznot.com
+// paper 2610.05416, "Các ý tưởng cốt lõi"): at 2K the 24 heads range from
+// 0.56x to 1.47x of the mean, and the XCD holding the heaviest three finishes
+// last.  The launch therefore visits heads in an order whose consecutive runs
+// of H/8 heads carry about equal work: heaviest head first into the lightest
+// run that still has room.  Each head's tiles and sums are unchanged, so the
+// outputs do not depend on the order.
+
+// cost[h] += tiles(j) * sum of tiles(i) over the query blocks i of key block
+// j's transposed list: one wave per (key block, head)
+__global__ void __launch_bounds__(64)
+head_cost_kernel(const int32_t* __restrict__ tr_off, const int32_t* __restrict__ tr_idx, const int32_t* __restrict__ offs,
+                 int nb, int64_t cap, unsigned long long* __restrict__ cost) {
+    const int j = blockIdx.x, h = blockIdx.y;
+    const int32_t* __restrict__ to = tr_off + static_cast<int64_t>(h) * (nb + 1);
+    const int32_t* __restrict__ ti = tr_idx + static_cast<int64_t>(h) * cap;
+    const int64_t e1 = min(static_cast<int64_t>(to[j + 1]), cap);
+    unsigned long long s = 0;
+    for (int64_t e = to[j] + threadIdx.x; e < e1; e += 64) {
+        const int i = ti[e];
+        s += static_cast<unsigned long long>((offs[i + 1] - offs[i]) >> 6);
+    }
+    s = wave_sum(s);
+    if (threadIdx.x == 0 && s) atomicAdd(&cost[h], s * static_cast<unsigned long long>((offs[j + 1] - offs[j]) >> 6));
+}
+
+// order[slot] = head; runs of H/8 slots are the XCDs' shares.  Identity when H
+// is not a multiple of 8 (ranges would straddle heads) or outside [16, 256].
+__global__ void __launch_bounds__(64)
+head_order_kernel(const unsigned long long* __restrict__ cost, int heads, int32_t* __restrict__ order) {
+    const bool balance = heads % 8 == 0 && heads >= 16 && heads <= 256;
+    if (!balance) {
+        for (int x = threadIdx.x; x < heads; x += 64) order[x] = x;
+        return;
+    }
+    if (threadIdx.x != 0) return;
+    const int per = heads / 8;
+    unsigned long long load[8] = {};
+    int fill[8] = {};
+    uint64_t taken[4] = {};   // heads picked so far (heads <= 256)
+    for (int n = 0; n < heads; ++n) {
+        int best = -1;   // heaviest head not yet placed, the lower index on ties
+        for (int x = 0; x < heads; ++x)
+            if (!((taken[x >> 6] >> (x & 63)) & 1) && (best < 0 || cost[x] > cost[best])) best = x;
+        taken[best >> 6] |= uint64_t{1} << (best & 63);
+        int bin = -1;    // lightest run with room, the lower index on ties
+        for (int b = 0; b < 8; ++b)
+            if (fill[b] < per && (bin < 0 || load[b] < load[bin])) bin = b;
+        order[bin * per + fill[bin]] = best;
+        ++fill[bin];
+        load[bin] += cost[best];
+    }
+}
+
 // ---------------------------------------------------------------- launcher
+
+hipError_t launch_head_order(const int32_t* tr_off, const int32_t* tr_idx, const int32_t* offs, int nb, int heads,
+                             int64_t cap, unsigned long long* cost, int32_t* order, hipStream_t s) {
+    hipError_t e = fill_zero(reinterpret_cast<int32_t*>(cost), 2 * static_cast<int64_t>(heads), s);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(head_cost_kernel, dim3(nb, heads), dim3(64), 0, s, tr_off, tr_idx, offs, nb, cap, cost);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(head_order_kernel, dim3(1), dim3(64), 0, s, cost, heads, order);
+    return hipGetLastError();
+}
 
 hipError_t launch_attn_dq_mfma(const void* q, const void* k, const void* v, const void* dout, const float* lse,
                               float* Dq, void* dq, int64_t N, int heads, int d, int64_t ld, int64_t hs,
@@ -500,7 +571,8 @@ hipError_t launch_attn_dq_split(const void* q, const void* k, const void* v, con
 hipError_t launch_attn_dkdv_mfma(const void* q, const void* k, const void* v, const void* dout, const float* lse2,
                                  const float* Dq, void* dk, void* dv, int64_t N, int heads, int d, int64_t ld,
                                  int64_t hs, const int32_t* offs, int nb, const int32_t* to, const int32_t* ti,
-                                 int64_t cap, const RouteGrad* rg, const RowMap& om, float scale, hipStream_t s) {
+                                 int64_t cap, const int32_t* horder, const RouteGrad* rg, const RowMap& om, float scale,
+                                 hipStream_t s) {
     const float* dkb = rg ? rg->dkbar : nullptr;
     const float* dvb = rg ? rg->dvbar : nullptr;
     const dim3 grid(static_cast<unsigned>(N / 64 * heads));
@@ -513,10 +585,10 @@ hipError_t launch_attn_dkdv_mfma(const void* q, const void* k, const void* v, co
     uint16_t* dV = static_cast<uint16_t*>(dv);
     if (d == 128)
         hipLaunchKernelGGL(attn_dkdv_mfma_kernel<128>, grid, dim3(256), 0, s, Q, K, V, O, lse2, Dq, dK, dV, N, ld, hs,
-                           offs, nb, to, ti, cap, dkb, dvb, om, sl2, scale);
+                           offs, nb, to, ti, cap, horder, dkb, dvb, om, sl2, scale);
     else
         hipLaunchKernelGGL(attn_dkdv_mfma_kernel<64>, grid, dim3(256), 0, s, Q, K, V, O, lse2, Dq, dK, dV, N, ld, hs,
-                           offs, nb, to, ti, cap, dkb, dvb, om, sl2, scale);
+                           offs, nb, to, ti, cap, horder, dkb, dvb, om, sl2, scale);
     return hipGetLastError();
 }
 

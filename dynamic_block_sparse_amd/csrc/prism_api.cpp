@@ -105,6 +105,8 @@ struct BwdWs {
     int32_t* obucket;  // bucket counts of the tile order
     int32_t* ostart;   // bucket starts of the tile order
     int32_t* qorder;   // dQ tile order
+    unsigned long long* hcost;   // per-head pair counts of the dK/dV launch
+    int32_t* horder;             // its head order
 };
 // `hg` heads share the per-group buffers (the dQ tile order), all heads the rest
 BwdWs carve_bwd(Carver& c, int64_t N, int64_t heads, int64_t hg, int64_t nb, int64_t cap) {
@@ -119,6 +121,8 @@ BwdWs carve_bwd(Carver& c, int64_t N, int64_t heads, int64_t hg, int64_t nb, int
     w.obucket = c.take<int32_t>(units * nb);
     w.ostart = c.take<int32_t>(units * (nb + 1));
     w.qorder = c.take<int32_t>(2 * hg * (N / 64));
+    w.hcost = c.take<unsigned long long>(heads);
+    w.horder = c.take<int32_t>(heads);
     return w;
 }
 
@@ -895,9 +899,13 @@ prism_status exact_bwd(const void* q, const void* k, const void* v, const void* 
             if (st != PRISM_OK) return st;
         }
     }
+    prism_status st = hip_status(prism::launch_head_order(w.tr_offsets, w.tr_idx, block_offsets, nb, heads, cap,
+                                                          w.hcost, w.horder, stream),
+                                 "dK/dV head order launch");
+    if (st != PRISM_OK) return st;
     return hip_status(prism::launch_attn_dkdv_mfma(q, k, v, dout, w.lse2, w.Dq, dk, dv, N, heads, d, ld, hs,
-                                                   block_offsets, nb, w.tr_offsets, w.tr_idx, cap, rg, om, scale,
-                                                   stream),
+                                                   block_offsets, nb, w.tr_offsets, w.tr_idx, cap, w.horder, rg, om,
+                                                   scale, stream),
                       "dK/dV launch");
 }
 

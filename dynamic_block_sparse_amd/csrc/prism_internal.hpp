@@ -97,7 +97,14 @@ hipError_t launch_attn_dq_split(const void* q, const void* k, const void* v, con
 hipError_t launch_attn_dkdv_mfma(const void* q, const void* k, const void* v, const void* dout, const float* lse2,
                                  const float* Dq, void* dk, void* dv, int64_t N, int heads, int d, int64_t ld,
                                  int64_t hs, const int32_t* offs, int nb, const int32_t* to, const int32_t* ti,
-                                 int64_t cap, const RouteGrad* rg, const RowMap& om, float scale, hipStream_t s);
+                                 int64_t cap, const int32_t* horder, const RouteGrad* rg, const RowMap& om, float scale,
+                                 hipStream_t s);
+// The dK/dV launch's head order (order[slot] = head, `heads` entries): runs of
+// heads/8 consecutive slots, one per XCD, balanced by each head's count of
+// (query tile, key tile) pairs from the transposed CSR; cost holds `heads`
+// 64-bit counters.
+hipError_t launch_head_order(const int32_t* tr_off, const int32_t* tr_idx, const int32_t* offs, int nb, int heads,
+                             int64_t cap, unsigned long long* cost, int32_t* order, hipStream_t s);
 
 hipError_t launch_attn_bwd_simt(const void* q, const void* k, const void* v, const void* dout, const float* lse,
                                 const float* Dq, void* dq, void* dk, void* dv, bool bf16, int64_t N, int heads, int d,

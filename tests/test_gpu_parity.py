@@ -165,6 +165,39 @@ def test_small_determinism():
                            b.view(torch.uint8) if b.dtype != torch.int32 else b)
 
 
+def test_backward_head_order_is_invisible():
+    """With 16 heads the dK/dV launch visits heads in a work-balanced order
+    (runs of 2 heads per XCD).  Heads whose queries are scaled differently
+    select different numbers of blocks, so that order is not the identity.
+    One call over all heads must give, bit for bit, what one call per head
+    gives (where the order is trivially the identity), and every head must
+    match the oracle."""
+    cfg = custom("s_16_heads", T=8, H=16, W=16, heads=16, d=64, dtype="bf16", top_k=2, top_p=0.9,
+                 kinds=(("smooth", 0.5), ("noisy", 0.5)), sigma={"smooth": 0.1, "noisy": 1.0}, beta=2.0, seed=19)
+    x = make_inputs(cfg, device="cuda")
+    # query gains from diffuse (0.2) to sharp (3): per-head selections differ in size
+    gain = torch.linspace(0.2, 3.0, cfg.heads, device="cuda").to(x["q"].dtype)
+    x["q"] = (x["q"] * gain[None, :, None]).contiguous()
+    runs = []
+    for hc in (cfg.heads, 1):
+        path = _path(cfg, hc=hc)
+        out = path.step(x["q"], x["k"], x["v"], x["a"], x["do"])
+        torch.cuda.synchronize()
+        runs.append(out)
+    tot = torch.cat([s.total for s in runs[0]["selections"]]).double()
+    assert float(tot.max() / tot.min()) > 2.0, tot.tolist()
+    for n in ("o", "dq", "dk", "dv"):
+        assert torch.equal(runs[0][n].view(torch.uint16), runs[1][n].view(torch.uint16)), n
+    ref = _oracle_full(cfg, x)
+    pi = ref["pi"]
+    for h, hr in enumerate(ref["heads"]):
+        att = hr["att"]
+        assert_close(_np(runs[0]["o"][:, h]), orc.to_raster(att["O"], pi), cfg.dtype, f"O h{h}")
+        for g, name in (("dq", "dQ"), ("dk", "dK"), ("dv", "dV")):
+            assert_close(_np(runs[0][g][:, h]), orc.to_raster(att[name], pi), cfg.dtype, f"{name} h{h}",
+                         grad=True, terms=orc.to_raster(att["t" + name[1]], pi))
+
+
 @pytest.mark.parametrize("idx", [0, 1], ids=["f32", "bf16"])
 def test_zone_statistics_both_load_paths(idx):
     """The zone statistics kernel loads V rows with 16-byte direct LDS loads when
