@@ -42,7 +42,7 @@ def grad_bar(want, dtype, terms=None):
     return bar
 
 
-def assert_close(got, want, dtype, what, grad=False, terms=None):
+def assert_close(got, want, dtype, what, grad=False, terms=None, log=print):
     """O is a convex combination of V rows, so its bar is absolute.  Gradients
     take grad_bar() element by element, and a mean-abs bar scaled by
     max(1, mean |reference|), plus (with terms) twice the mean standard
@@ -64,14 +64,14 @@ def assert_close(got, want, dtype, what, grad=False, terms=None):
     strict = ""
     if grad and terms is not None:
         strict = f" strict-bar worst {float((err / grad_bar(want, dtype)).max()):.3f}"
-    print(f"{what}: max-abs {err.max():.3e} mean-abs {err.mean():.3e} (bar {mean_bar:.2e}) "
+    log(f"{what}: max-abs {err.max():.3e} mean-abs {err.mean():.3e} (bar {mean_bar:.2e}) "
           f"worst err/bar {ratio[w]:.3f} (err {err[w]:.3e}, |ref| {abs(want[w]):.3e}, bar {bar[w]:.3e}){strict} "
-          f"max|ref| {np.abs(want).max():.3e} over-{mx:g} {int((err > mx).sum())} of {err.size}", flush=True)
+          f"max|ref| {np.abs(want).max():.3e} over-{mx:g} {int((err > mx).sum())} of {err.size}")
     assert ratio[w] <= 1.0, f"{what}: error {err[w]} > bar {bar[w]} at {w} (ref {want[w]})"
     assert err.mean() <= mean_bar, f"{what}: mean-abs {err.mean()} > {mean_bar}"
 
 
-def check_gradient_sums(dk, dv, do, dtype, what):
+def check_gradient_sums(dk, dv, do, dtype, what, log=None):
     """Whole-tensor identities of the masked-softmax gradient, one head at a
     time: every row of dS sums to zero, so the sum of dK over all keys is 0
     for each channel; every row of P sums to one, so the sum of dV over all
@@ -79,7 +79,9 @@ def check_gradient_sums(dk, dv, do, dtype, what):
     stored outputs.  Bar: the per-element gradient bar b_t of each summed
     element (grad_bar at the element's own magnitude), with the element errors
     taken as independent and at most b_t (variance at most b_t^2 / 3 each), at
-    six standard deviations: 6 sqrt(sum_t b_t^2 / 3) per channel."""
+    six standard deviations: 6 sqrt(sum_t b_t^2 / 3) per channel.  log, if
+    given, receives one line with the worst ratio over all heads."""
+    worst = {}
     for h in range(dk.shape[1]):
         k = dk[:, h, :].double()
         v = dv[:, h, :].double()
@@ -92,3 +94,7 @@ def check_gradient_sums(dk, dv, do, dtype, what):
             print(f"{what} head {h} {name}: max |sum| {float(x.abs().max()):.3e}, worst sum/bar {ratio:.3f}",
                   flush=True)
             assert ratio <= 1.0, f"{what} head {h}: {name} {float(x.abs().max())} exceeds its bar"
+            worst[name] = max(worst.get(name, 0.0), ratio)
+    if log is not None:
+        log(f"{what}: gradient sums over {dk.shape[1]} heads, worst sum/bar " +
+            ", ".join(f"{n} {r:.3f}" for n, r in worst.items()))

@@ -438,7 +438,7 @@ def test_full_size_sampled(name, progress):
     for t in (op,) + (grads or ()):
         assert bool(torch.isfinite(t[:, :nh]).all())
     if cfg.backward:
-        check_gradient_sums(grads[1][:, :nh], grads[2][:, :nh], xs["do"], cfg.dtype, name)
+        check_gradient_sums(grads[1][:, :nh], grads[2][:, :nh], xs["do"], cfg.dtype, name, log=progress)
         progress(f"case {name}: gradient sums of all {nh} heads within their bars")
     pi_t = torch.from_numpy(pi).cuda()
     bm = lambda t, a, b, h: _np(t[pi_t[a:b], h, :])   # block-major rows a..b-1 of a raster output
@@ -544,7 +544,8 @@ def test_full_size_sampled(name, progress):
                 got = np.concatenate([p[0] for p in pairs])
                 want = np.concatenate([p[1] for p in pairs])
                 terms = np.concatenate([p[2] for p in pairs]) if k != "O" else None
-                assert_close(got, want, cfg.dtype, f"{name} head {h} {k}", grad=(k != "O"), terms=terms)
+                assert_close(got, want, cfg.dtype, f"{name} head {h} {k}", grad=(k != "O"), terms=terms,
+                             log=progress)
 
 
 def _users_of_keys(co, ci, nb):
